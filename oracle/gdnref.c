@@ -1,0 +1,219 @@
+/*
+ * gdnref.c -- plain fp64 CPU oracle for the Gated DeltaNet forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark load this file's library.  It shares no code,
+ * header, table or helper with the GPU library: it is written from the pages'
+ * definitions, slowly and obviously, token by token, in double precision.
+ *
+ * Sources (the pages are named by title and section):
+ *  - "Source notes" (NextTransformer methods page), section "Linear
+ *    attention", rows deltanet / kda / gdn: the gated delta-rule state update
+ *    with a scalar per-head decay applied before the delta update (gdn), a
+ *    per-key-channel decay applied before the delta update (kda), the read
+ *    y = q^T S after the write (deltanet), causal conv + SiLU and
+ *    L2-normalised q/k (deltanet, kda).
+ *  - same page, section "Backend and numerical limits": query scale is 1; an
+ *    FP64 recurrent scan is the correctness reference.
+ *  - "Frontier model atlas", entries 03 and 08 (Gated DeltaNet): four-token
+ *    causal convolution in front of the state update; 16 key heads shared by
+ *    48 value heads.
+ *
+ * Orientation.  The pages write the state as a K x V matrix S with read
+ * y = q^T S.  Here the state of one (batch, value head) is its transpose,
+ * a dv x dk matrix (row i = value channel, column j = key channel), so that
+ * the read is o_t = S_t q_t.  Both orientations give the same numbers.
+ *
+ * Readings where the pages leave a step open (all are listed in the design
+ * notes of the repository):
+ *  - decay first, then the prediction uses the decayed state:
+ *        S <- alpha_t S          (kda: S <- S diag(alpha_t))
+ *        p  = S k_t
+ *        S <- S + beta_t (v_t - p) k_t^T
+ *        o_t = S q_t             (read after the write, scale 1)
+ *  - alpha_t = exp(g_t) with g_t the natural-log decay handed in;
+ *  - value head h reads key/query head h / (Hv / Hk) (consecutive grouping);
+ *  - conv: depthwise, 4 taps, no bias, zero history before t = 0, tap 3
+ *    multiplies the current token; SiLU after the conv; q and k are then
+ *    divided by sqrt(sum z^2 + eps) per (token, head).
+ *
+ * Inputs are float arrays whose values are the exact stored values (bf16 and
+ * fp16 widen to float exactly); every operation is carried out in double.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Recurrence                                                               */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int B, T, Hk, Hv, dk, dv, per_channel_gate;
+  const float *q, *k, *v, *g, *beta, *S0;
+  const double *S0d; /* used instead of S0 when set */
+  int nsel;
+  const int *sel_b, *sel_h;
+  double *o, *S_T;
+  int next; /* next chain index to take (guarded by mu) */
+  pthread_mutex_t mu;
+} rec_job;
+
+/* One (batch b, value head h) chain over all T tokens. */
+static void rec_chain(const rec_job *J, int n, double *S) {
+  const int b = J->sel_b[n], h = J->sel_h[n];
+  const int dk = J->dk, dv = J->dv, T = J->T;
+  const int kh = h / (J->Hv / J->Hk); /* key/query head read by value head h */
+  double *o = J->o + (size_t)n * T * dv;
+  int i, j, t;
+
+  if (J->S0d) {
+    memcpy(S, J->S0d + ((size_t)b * J->Hv + h) * dv * dk, sizeof(double) * dv * dk);
+  } else if (J->S0) {
+    const float *s0 = J->S0 + ((size_t)b * J->Hv + h) * dv * dk;
+    for (i = 0; i < dv * dk; ++i) S[i] = (double)s0[i];
+  } else {
+    memset(S, 0, sizeof(double) * dv * dk);
+  }
+
+  for (t = 0; t < T; ++t) {
+    const size_t bt = (size_t)b * T + t;
+    const float *qt = J->q + (bt * J->Hk + kh) * dk;
+    const float *kt = J->k + (bt * J->Hk + kh) * dk;
+    const float *vt = J->v + (bt * J->Hv + h) * dv;
+    const double beta = (double)J->beta[bt * J->Hv + h];
+
+    /* decay before the delta update */
+    if (J->per_channel_gate) {
+      const float *gt = J->g + (bt * J->Hv + h) * dk;
+      for (j = 0; j < dk; ++j) {
+        const double a = exp((double)gt[j]);
+        for (i = 0; i < dv; ++i) S[(size_t)i * dk + j] *= a;
+      }
+    } else {
+      const double a = exp((double)J->g[bt * J->Hv + h]);
+      for (i = 0; i < dv * dk; ++i) S[i] *= a;
+    }
+
+    /* delta update: S <- S + beta (v - S k) k^T */
+    for (i = 0; i < dv; ++i) {
+      double *row = S + (size_t)i * dk;
+      double p = 0.0;
+      for (j = 0; j < dk; ++j) p += row[j] * (double)kt[j];
+      const double u = beta * ((double)vt[i] - p);
+      for (j = 0; j < dk; ++j) row[j] += u * (double)kt[j];
+    }
+
+    /* read after the write, scale 1 */
+    for (i = 0; i < dv; ++i) {
+      const double *row = S + (size_t)i * dk;
+      double acc = 0.0;
+      for (j = 0; j < dk; ++j) acc += row[j] * (double)qt[j];
+      o[(size_t)t * dv + i] = acc;
+    }
+  }
+  memcpy(J->S_T + (size_t)n * dv * dk, S, sizeof(double) * dv * dk);
+}
+
+static void *rec_worker(void *arg) {
+  rec_job *J = (rec_job *)arg;
+  double *S = (double *)malloc(sizeof(double) * (size_t)J->dv * J->dk);
+  if (!S) return NULL;
+  for (;;) {
+    pthread_mutex_lock(&J->mu);
+    const int n = J->next++;
+    pthread_mutex_unlock(&J->mu);
+    if (n >= J->nsel) break;
+    rec_chain(J, n, S);
+  }
+  free(S);
+  return NULL;
+}
+
+/*
+ * gdnref_recurrent: token-by-token recurrence for the selected chains.
+ *
+ *   q, k  [B,T,Hk,dk]   v [B,T,Hv,dv]
+ *   g     [B,T,Hv] (per_channel_gate = 0) or [B,T,Hv,dk] (= 1), natural log
+ *   beta  [B,T,Hv]
+ *   S0    [B,Hv,dv,dk] or NULL (zeros); float, or double when s0_double
+ *   sel_b, sel_h [nsel]: the (batch, value head) chains to run
+ *   o     [nsel,T,dv] (double, out)     S_T [nsel,dv,dk] (double, out)
+ *
+ * A decode step is this function with T = 1.  Returns 0, or -1 on a bad
+ * argument.
+ */
+int gdnref_recurrent(int B, int T, int Hk, int Hv, int dk, int dv,
+                     int per_channel_gate, const float *q, const float *k,
+                     const float *v, const float *g, const float *beta,
+                     const void *S0, int s0_double, int nsel, const int *sel_b,
+                     const int *sel_h, double *o, double *S_T, int nthreads) {
+  int n, t;
+  if (B <= 0 || T < 0 || Hk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0) return -1;
+  if (Hv % Hk != 0 || nsel < 0 || !q || !k || !v || !g || !beta || !o || !S_T)
+    return -1;
+  for (n = 0; n < nsel; ++n)
+    if (sel_b[n] < 0 || sel_b[n] >= B || sel_h[n] < 0 || sel_h[n] >= Hv)
+      return -1;
+  rec_job J;
+  J.B = B; J.T = T; J.Hk = Hk; J.Hv = Hv; J.dk = dk; J.dv = dv;
+  J.per_channel_gate = per_channel_gate;
+  J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta;
+  J.S0 = s0_double ? NULL : (const float *)S0;
+  J.S0d = s0_double ? (const double *)S0 : NULL;
+  J.nsel = nsel; J.sel_b = sel_b; J.sel_h = sel_h; J.o = o; J.S_T = S_T;
+  J.next = 0;
+  pthread_mutex_init(&J.mu, NULL);
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > nsel) nthreads = nsel > 0 ? nsel : 1;
+  pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * nthreads);
+  int started = 0;
+  for (t = 0; th && t + 1 < nthreads; ++t)
+    if (pthread_create(&th[started], NULL, rec_worker, &J) == 0) ++started;
+  rec_worker(&J); /* the calling thread works too */
+  for (t = 0; t < started; ++t) pthread_join(th[t], NULL);
+  free(th);
+  pthread_mutex_destroy(&J.mu);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Prologue: 4-tap causal depthwise conv, SiLU, optional L2 normalisation   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * gdnref_conv_silu: x [B,T,H,d] -> y [B,T,H,d] (double).
+ *   w [H*d][4] (tap 3 multiplies token t, tap 0 multiplies token t-3; zero
+ *   history before t = 0);  y = z * sigmoid(z) with z the conv output;
+ *   if l2norm, every (b,t,h) row of y is divided by sqrt(sum y^2 + eps).
+ */
+int gdnref_conv_silu(int B, int T, int H, int d, const float *x,
+                     const float *w, int l2norm, double eps, double *y) {
+  int b, t, h, c, j;
+  if (B <= 0 || T < 0 || H <= 0 || d <= 0 || !x || !w || !y) return -1;
+  for (b = 0; b < B; ++b)
+    for (t = 0; t < T; ++t)
+      for (h = 0; h < H; ++h) {
+        double *yr = y + (((size_t)b * T + t) * H + h) * d;
+        for (c = 0; c < d; ++c) {
+          const int ch = h * d + c;
+          double z = 0.0;
+          for (j = 0; j < 4; ++j) {
+            const int ts = t - 3 + j;
+            if (ts < 0) continue;
+            z += (double)w[(size_t)ch * 4 + j] *
+                 (double)x[(((size_t)b * T + ts) * H + h) * d + c];
+          }
+          yr[c] = z / (1.0 + exp(-z));
+        }
+        if (l2norm) {
+          double ss = 0.0;
+          for (c = 0; c < d; ++c) ss += yr[c] * yr[c];
+          const double inv = 1.0 / sqrt(ss + eps);
+          for (c = 0; c < d; ++c) yr[c] *= inv;
+        }
+      }
+  return 0;
+}
