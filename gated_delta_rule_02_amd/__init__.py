@@ -1,0 +1,195 @@
+"""Gated DeltaNet forward pass on AMD Instinct MI355X (gfx950).
+
+Python binding of ``libgdn.so`` (the C ABI of ``include/gdn.h``).  This module
+only marshals arguments: it checks that tensors are contiguous device tensors
+of the expected shapes, passes their device pointers and the current HIP
+stream to the library, and turns a non-zero status into ``GdnError``.  Every
+step of the computation runs in the library's HIP kernels; there is no
+fallback of any kind.  PyTorch provides device memory and streams.
+
+Entry points (same names as the C functions):
+  prologue(xq, xk, xv, conv_w, out_dtype, eps) -> (q, k, v)
+  fwd_chunked(q, k, v, g, beta, S0, chunk) -> (o, S_T)
+  decode_step(q, k, v, g, beta, S) -> o          (S updated in place)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdn.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "gdn.h")
+
+F32, BF16, F16 = 0, 1, 2
+GATE_HEAD, GATE_KEY_CHANNEL = 0, 1
+STATUS = {0: "GDN_OK", 1: "GDN_E_ARG", 2: "GDN_E_SHAPE", 3: "GDN_E_UNSUPPORTED",
+          4: "GDN_E_ALIGN", 5: "GDN_E_WORKSPACE", 6: "GDN_E_HIP"}
+
+_DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+
+
+class GdnDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "T", "Hk", "Hv", "dk", "dv", "chunk", "qkv_dtype", "gate_dtype", "gate")]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (STATUS.get(status, status), message))
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libgdn.so is not built: run __graft_entry__.build() "
+                               "(or python gated_delta_rule_02_amd/_build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        D = ctypes.POINTER(GdnDesc)
+        L.gdn_prologue.argtypes = [D, I, P, P, P, P, ctypes.c_float, P, P, P, P]
+        L.gdn_prologue.restype = I
+        L.gdn_fwd_workspace_bytes.argtypes = [D]
+        L.gdn_fwd_workspace_bytes.restype = S
+        L.gdn_fwd_chunked.argtypes = [D, P, P, P, P, P, P, P, P, P, S, P]
+        L.gdn_fwd_chunked.restype = I
+        L.gdn_decode_step.argtypes = [D, P, P, P, P, P, P, P, P]
+        L.gdn_decode_step.restype = I
+        L.gdn_status_str.argtypes = [I]
+        L.gdn_status_str.restype = ctypes.c_char_p
+        L.gdn_last_error.argtypes = []
+        L.gdn_last_error.restype = ctypes.c_char_p
+        L.gdn_version.argtypes = []
+        L.gdn_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/gdn.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(gdn_[a-z_]+)\s*\(", text, flags=re.M)
+
+
+def check(status: int) -> None:
+    if status != 0:
+        raise GdnError(status, lib().gdn_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(name, t, shape=None, dtypes=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s" % (name, t.dtype))
+    return t
+
+
+def make_desc(B, T, Hk, Hv, dk, dv, chunk, qkv_dtype, gate_dtype, gate) -> GdnDesc:
+    return GdnDesc(B, T, Hk, Hv, dk, dv, chunk, qkv_dtype, gate_dtype, gate)
+
+
+def prologue(xq, xk, xv, conv_w, out_dtype=torch.float16, eps=1e-6, stream=None):
+    """4-tap causal conv + SiLU over q|k|v, then L2 normalisation of q and k rows.
+
+    xq, xk [B,T,Hk,dk], xv [B,T,Hv,dv] (bf16 or fp32); conv_w fp32
+    [2*Hk*dk + Hv*dv, 4].  Returns new tensors q, k, v in out_dtype.
+    """
+    B, T, Hk, dk = xq.shape
+    Hv, dv = xv.shape[2], xv.shape[3]
+    _dev("xq", xq, (B, T, Hk, dk))
+    _dev("xk", xk, (B, T, Hk, dk), (xq.dtype,))
+    _dev("xv", xv, (B, T, Hv, dv), (xq.dtype,))
+    _dev("conv_w", conv_w, (2 * Hk * dk + Hv * dv, 4), (torch.float32,))
+    q = torch.empty((B, T, Hk, dk), dtype=out_dtype, device=xq.device)
+    k = torch.empty_like(q)
+    v = torch.empty((B, T, Hv, dv), dtype=out_dtype, device=xq.device)
+    d = make_desc(B, T, Hk, Hv, dk, dv, 64, _DTYPE_CODE[out_dtype], F32, GATE_HEAD)
+    check(lib().gdn_prologue(ctypes.byref(d), _DTYPE_CODE[xq.dtype], _ptr(xq), _ptr(xk), _ptr(xv),
+                             _ptr(conv_w), float(eps), _ptr(q), _ptr(k), _ptr(v), _stream(stream)))
+    return q, k, v
+
+
+def _gate_kind(g, B, T, Hv, dk):
+    if tuple(g.shape) == (B, T, Hv):
+        return GATE_HEAD
+    if tuple(g.shape) == (B, T, Hv, dk):
+        return GATE_KEY_CHANNEL
+    raise ValueError("g must be [B,T,Hv] or [B,T,Hv,dk], got %s" % (tuple(g.shape),))
+
+
+def fwd_chunked(q, k, v, g, beta, S0=None, chunk=64, o=None, S_T=None, stream=None):
+    """Chunked forward over T tokens.  q, k [B,T,Hk,dk]; v [B,T,Hv,dv];
+    g [B,T,Hv] or [B,T,Hv,dk]; beta [B,T,Hv]; S0 fp32 [B,Hv,dv,dk] or None.
+    Returns (o fp32 [B,T,Hv,dv], S_T fp32 [B,Hv,dv,dk]); S_T may be S0."""
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    _dev("q", q)
+    _dev("k", k, q.shape, (q.dtype,))
+    _dev("v", v, (B, T, Hv, dv), (q.dtype,))
+    gate = _gate_kind(_dev("g", g), B, T, Hv, dk)
+    _dev("beta", beta, (B, T, Hv), (g.dtype,))
+    if S0 is not None:
+        _dev("S0", S0, (B, Hv, dv, dk), (torch.float32,))
+    if o is None:
+        o = torch.empty((B, T, Hv, dv), dtype=torch.float32, device=q.device)
+    if S_T is None:
+        S_T = torch.empty((B, Hv, dv, dk), dtype=torch.float32, device=q.device)
+    _dev("o", o, (B, T, Hv, dv), (torch.float32,))
+    _dev("S_T", S_T, (B, Hv, dv, dk), (torch.float32,))
+    d = make_desc(B, T, Hk, Hv, dk, dv, chunk, _DTYPE_CODE[q.dtype], _DTYPE_CODE[g.dtype], gate)
+    L = lib()
+    ws_bytes = L.gdn_fwd_workspace_bytes(ctypes.byref(d))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    check(L.gdn_fwd_chunked(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                            _ptr(S0), _ptr(o), _ptr(S_T), _ptr(ws), ws_bytes, _stream(stream)))
+    return o, S_T
+
+
+def decode_step(q, k, v, g, beta, S, o=None, stream=None):
+    """One token per sequence.  q, k [B,Hk,dk]; v [B,Hv,dv]; g [B,Hv] or
+    [B,Hv,dk]; beta [B,Hv]; S fp32 [B,Hv,dv,dk] updated in place.
+    Returns o fp32 [B,Hv,dv]."""
+    B, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    _dev("q", q)
+    _dev("k", k, q.shape, (q.dtype,))
+    _dev("v", v, (B, Hv, dv), (q.dtype,))
+    _dev("g", g)
+    if tuple(g.shape) == (B, Hv):
+        gate = GATE_HEAD
+    elif tuple(g.shape) == (B, Hv, dk):
+        gate = GATE_KEY_CHANNEL
+    else:
+        raise ValueError("g must be [B,Hv] or [B,Hv,dk]")
+    _dev("beta", beta, (B, Hv), (g.dtype,))
+    _dev("S", S, (B, Hv, dv, dk), (torch.float32,))
+    if o is None:
+        o = torch.empty((B, Hv, dv), dtype=torch.float32, device=q.device)
+    _dev("o", o, (B, Hv, dv), (torch.float32,))
+    d = make_desc(B, 1, Hk, Hv, dk, dv, 64, _DTYPE_CODE[q.dtype], _DTYPE_CODE[g.dtype], gate)
+    check(lib().gdn_decode_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                _ptr(S), _ptr(o), _stream(stream)))
+    return o

@@ -1,0 +1,257 @@
+// gdn_api.cpp -- the C ABI declared in include/gdn.h: argument validation on
+// the host (before anything is enqueued) and dispatch to the kernel launchers.
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "gdn_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdn_status fail(gdn_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+gdn_status ok() {
+  g_last_error.clear();
+  return GDN_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool is_dtype(int32_t t) { return t == GDN_F32 || t == GDN_BF16 || t == GDN_F16; }
+
+size_t dsize(int32_t t) { return t == GDN_F32 ? 4 : 2; }
+
+bool pow2_16_128(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+Range range(const void *p, size_t bytes) {
+  return Range{(uintptr_t)p, (uintptr_t)p + bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Checks common to every entry point; fills the launcher's shape.
+gdn_status check_desc(const gdn_desc *d, gdn::Shape *sh) {
+  if (!d) return fail(GDN_E_ARG, "desc is NULL");
+  if (d->B < 1 || d->T < 1 || d->Hk < 1 || d->Hv < 1 || d->dk < 1 || d->dv < 1)
+    return fail(GDN_E_ARG, "B, T, Hk, Hv, dk, dv must be >= 1 (got %d %d %d %d %d %d)", d->B,
+                d->T, d->Hk, d->Hv, d->dk, d->dv);
+  if (!is_dtype(d->qkv_dtype) || !is_dtype(d->gate_dtype))
+    return fail(GDN_E_ARG, "unknown dtype (qkv %d, gate %d)", d->qkv_dtype, d->gate_dtype);
+  if (d->gate != GDN_GATE_HEAD && d->gate != GDN_GATE_KEY_CHANNEL)
+    return fail(GDN_E_ARG, "unknown gate kind %d", d->gate);
+  if (d->Hv % d->Hk != 0)
+    return fail(GDN_E_SHAPE, "Hv (%d) must be a multiple of Hk (%d)", d->Hv, d->Hk);
+  if (d->B > 65535 || d->Hv > 65535)
+    return fail(GDN_E_UNSUPPORTED, "B and Hv must be <= 65535");
+  // element counts must stay far from 64-bit overflow and kernel index limits
+  const double n_big = (double)d->B * d->T * (double)(d->Hv > d->Hk ? d->Hv : d->Hk) *
+                       (d->dv > d->dk ? d->dv : d->dk);
+  if (n_big > 1e13) return fail(GDN_E_UNSUPPORTED, "problem too large");
+  if ((double)d->B * ((d->T + 63) / 64) > 2147483647.0)
+    return fail(GDN_E_UNSUPPORTED, "B * T too large");
+  sh->B = d->B;
+  sh->T = d->T;
+  sh->Hk = d->Hk;
+  sh->Hv = d->Hv;
+  sh->dk = d->dk;
+  sh->dv = d->dv;
+  sh->chunk = d->chunk;
+  sh->qkv = (gdn::DType)d->qkv_dtype;
+  sh->gate_t = (gdn::DType)d->gate_dtype;
+  sh->key_gate = d->gate == GDN_GATE_KEY_CHANNEL;
+  return GDN_OK;
+}
+
+gdn_status check_ptrs(const char *const *names, const void *const *ptrs, int n) {
+  for (int i = 0; i < n; ++i) {
+    if (!ptrs[i]) return fail(GDN_E_ARG, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(GDN_E_ALIGN, "%s is not 16-byte aligned", names[i]);
+  }
+  return GDN_OK;
+}
+
+gdn_status launched(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(GDN_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gdn_version(void) { return "gdn-gfx950 0.1.0"; }
+
+const char *gdn_status_str(gdn_status s) {
+  switch (s) {
+    case GDN_OK: return "ok";
+    case GDN_E_ARG: return "invalid argument";
+    case GDN_E_SHAPE: return "inconsistent shapes";
+    case GDN_E_UNSUPPORTED: return "unsupported configuration";
+    case GDN_E_ALIGN: return "misaligned pointer";
+    case GDN_E_WORKSPACE: return "workspace too small";
+    case GDN_E_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char *gdn_last_error(void) { return g_last_error.c_str(); }
+
+gdn_status gdn_prologue(const gdn_desc *d, int32_t x_dtype, const void *xq, const void *xk,
+                        const void *xv, const float *conv_w, float eps, void *q, void *k, void *v,
+                        void *stream) {
+  gdn::Shape sh;
+  gdn_status st = check_desc(d, &sh);
+  if (st != GDN_OK) return st;
+  if (x_dtype != GDN_BF16 && x_dtype != GDN_F32)
+    return fail(x_dtype == GDN_F16 ? GDN_E_UNSUPPORTED : GDN_E_ARG,
+                "prologue inputs must be bf16 or fp32 (got dtype %d)", x_dtype);
+  if (!pow2_16_128(d->dk) || !pow2_16_128(d->dv))
+    return fail(GDN_E_UNSUPPORTED, "prologue supports dk, dv in {16,32,64,128} (got %d, %d)",
+                d->dk, d->dv);
+  if (!(eps >= 0.f) || eps > 1.f) return fail(GDN_E_ARG, "eps must be in [0, 1]");
+  const char *names[] = {"xq", "xk", "xv", "conv_w", "q", "k", "v"};
+  const void *ptrs[] = {xq, xk, xv, conv_w, q, k, v};
+  if ((st = check_ptrs(names, ptrs, 7)) != GDN_OK) return st;
+  const size_t nqk = (size_t)d->B * d->T * d->Hk * d->dk, nv = (size_t)d->B * d->T * d->Hv * d->dv;
+  const size_t xs = dsize(x_dtype), ys = dsize(d->qkv_dtype);
+  const Range outs[] = {range(q, nqk * ys), range(k, nqk * ys), range(v, nv * ys)};
+  const Range ins[] = {range(xq, nqk * xs), range(xk, nqk * xs), range(xv, nv * xs),
+                       range(conv_w, (2 * (size_t)d->Hk * d->dk + (size_t)d->Hv * d->dv) * 16)};
+  for (const Range &a : outs)
+    for (const Range &b : ins)
+      if (overlap(a, b)) return fail(GDN_E_ARG, "prologue outputs must not overlap its inputs");
+  if (overlap(outs[0], outs[1]) || overlap(outs[0], outs[2]) || overlap(outs[1], outs[2]))
+    return fail(GDN_E_ARG, "prologue outputs must not overlap each other");
+
+  hipStream_t s = (hipStream_t)stream;
+  const gdn::DType xt = (gdn::DType)x_dtype, yt = sh.qkv;
+  const size_t nw_q = (size_t)d->Hk * d->dk;
+  hipError_t e = gdn::launch_prologue(xq, xt, conv_w, q, yt, d->B, d->T, d->Hk, d->dk, true, eps, s);
+  if (e == hipSuccess)
+    e = gdn::launch_prologue(xk, xt, conv_w + 4 * nw_q, k, yt, d->B, d->T, d->Hk, d->dk, true, eps,
+                             s);
+  if (e == hipSuccess)
+    e = gdn::launch_prologue(xv, xt, conv_w + 8 * nw_q, v, yt, d->B, d->T, d->Hv, d->dv, false, eps,
+                             s);
+  return launched(e, "prologue launch");
+}
+
+size_t gdn_fwd_workspace_bytes(const gdn_desc *d) {
+  (void)d;
+  return 0;
+}
+
+gdn_status gdn_fwd_chunked(const gdn_desc *d, const void *q, const void *k, const void *v,
+                           const void *g, const void *beta, const float *S0, float *o, float *S_T,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  gdn::Shape sh;
+  gdn_status st = check_desc(d, &sh);
+  if (st != GDN_OK) return st;
+  (void)workspace;
+  (void)workspace_bytes;  // no workspace is needed (gdn_fwd_workspace_bytes returns 0)
+
+  const bool fp32_mode = d->qkv_dtype == GDN_F32 && d->gate_dtype == GDN_F32;
+  const bool mc_mode = (d->qkv_dtype == GDN_BF16 || d->qkv_dtype == GDN_F16) &&
+                       (d->gate_dtype == GDN_BF16 || d->gate_dtype == GDN_F32);
+  if (!fp32_mode && !mc_mode)
+    return fail(GDN_E_UNSUPPORTED,
+                "dtype combination not built (qkv %d, gate %d): use fp32/fp32, or bf16|fp16 with "
+                "bf16|fp32 gates",
+                d->qkv_dtype, d->gate_dtype);
+  bool use_mfma = false;
+  if (mc_mode && !sh.key_gate) {
+    if (d->dk != 128 || d->dv != 128 || d->chunk != 64)
+      return fail(GDN_E_UNSUPPORTED,
+                  "matrix-core mode supports dk = dv = 128 and chunk = 64 (got %d, %d, %d)", d->dk,
+                  d->dv, d->chunk);
+    use_mfma = true;
+  } else {
+    if (!pow2_16_128(d->dk) || !pow2_16_128(d->dv))
+      return fail(GDN_E_UNSUPPORTED, "dk, dv must be in {16,32,64,128} (got %d, %d)", d->dk, d->dv);
+    if (d->chunk != 16 && d->chunk != 32 && d->chunk != 64)
+      return fail(GDN_E_UNSUPPORTED, "chunk must be 16, 32 or 64 (got %d)", d->chunk);
+    if (fp32_mode && d->chunk * d->dk > 4096)
+      return fail(GDN_E_UNSUPPORTED, "fp32 mode needs chunk * dk <= 4096 (got %d * %d)", d->chunk,
+                  d->dk);
+  }
+
+  const char *names[] = {"q", "k", "v", "g", "beta", "o", "S_T"};
+  const void *ptrs[] = {q, k, v, g, beta, o, S_T};
+  if ((st = check_ptrs(names, ptrs, 7)) != GDN_OK) return st;
+  if (S0 && !aligned16(S0)) return fail(GDN_E_ALIGN, "S0 is not 16-byte aligned");
+
+  const size_t bt = (size_t)d->B * d->T;
+  const size_t qs = dsize(d->qkv_dtype), gs = dsize(d->gate_dtype);
+  const size_t state_bytes = (size_t)d->B * d->Hv * d->dv * d->dk * 4;
+  const Range ro = range(o, bt * d->Hv * d->dv * 4);
+  const Range rst = range(S_T, state_bytes);
+  const Range ins[] = {range(q, bt * d->Hk * d->dk * qs), range(k, bt * d->Hk * d->dk * qs),
+                       range(v, bt * d->Hv * d->dv * qs),
+                       range(g, bt * d->Hv * (sh.key_gate ? d->dk : 1) * gs),
+                       range(beta, bt * d->Hv * gs)};
+  for (const Range &r : ins) {
+    if (overlap(ro, r)) return fail(GDN_E_ARG, "o must not overlap an input");
+    if (overlap(rst, r)) return fail(GDN_E_ARG, "S_T must not overlap q, k, v, g or beta");
+  }
+  if (overlap(ro, rst)) return fail(GDN_E_ARG, "o must not overlap S_T");
+  if (S0) {
+    const Range rs0 = range(S0, state_bytes);
+    if (overlap(ro, rs0)) return fail(GDN_E_ARG, "o must not overlap S0");
+    if ((const void *)S0 != (const void *)S_T && overlap(rst, rs0))
+      return fail(GDN_E_ARG, "S_T must be S0 itself or not overlap it");
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = use_mfma ? gdn::launch_chunk_mfma(sh, q, k, v, g, beta, S0, o, S_T, s)
+                          : gdn::launch_chunk_f32(sh, q, k, v, g, beta, S0, o, S_T, s);
+  return launched(e, "chunked forward launch");
+}
+
+gdn_status gdn_decode_step(const gdn_desc *d, const void *q, const void *k, const void *v,
+                           const void *g, const void *beta, float *S, float *o, void *stream) {
+  gdn::Shape sh;
+  gdn_status st = check_desc(d, &sh);
+  if (st != GDN_OK) return st;
+  if (d->T != 1) return fail(GDN_E_SHAPE, "decode step needs T == 1 (got %d)", d->T);
+  if (!pow2_16_128(d->dk))
+    return fail(GDN_E_UNSUPPORTED, "decode supports dk in {16,32,64,128} (got %d)", d->dk);
+  if (d->dv % 16 != 0 || d->dv > 1024)
+    return fail(GDN_E_UNSUPPORTED, "decode supports dv a multiple of 16, <= 1024 (got %d)", d->dv);
+  if (d->gate_dtype == GDN_F16)
+    return fail(GDN_E_UNSUPPORTED, "decode gates must be fp32 or bf16");
+  const char *names[] = {"q", "k", "v", "g", "beta", "S", "o"};
+  const void *ptrs[] = {q, k, v, g, beta, S, o};
+  if ((st = check_ptrs(names, ptrs, 7)) != GDN_OK) return st;
+  const size_t qs = dsize(d->qkv_dtype), gs = dsize(d->gate_dtype);
+  const Range rS = range(S, (size_t)d->B * d->Hv * d->dv * d->dk * 4);
+  const Range ro = range(o, (size_t)d->B * d->Hv * d->dv * 4);
+  const Range ins[] = {range(q, (size_t)d->B * d->Hk * d->dk * qs),
+                       range(k, (size_t)d->B * d->Hk * d->dk * qs),
+                       range(v, (size_t)d->B * d->Hv * d->dv * qs),
+                       range(g, (size_t)d->B * d->Hv * (sh.key_gate ? d->dk : 1) * gs),
+                       range(beta, (size_t)d->B * d->Hv * gs)};
+  for (const Range &r : ins)
+    if (overlap(rS, r) || overlap(ro, r)) return fail(GDN_E_ARG, "S and o must not overlap inputs");
+  if (overlap(rS, ro)) return fail(GDN_E_ARG, "S and o must not overlap");
+  return launched(gdn::launch_decode(sh, q, k, v, g, beta, S, o, (hipStream_t)stream),
+                  "decode launch");
+}
+
+}  // extern "C"

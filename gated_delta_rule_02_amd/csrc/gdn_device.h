@@ -1,0 +1,90 @@
+// gdn_device.h -- device helpers shared by the gfx950 kernels: storage types,
+// exact widening to fp32, round-to-nearest-even narrowing, 16-byte vector
+// loads, and wave-level sums over aligned lane groups.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Storage types.  bf16 is carried as its 16-bit pattern.
+struct bf16_t {
+  uint16_t bits;
+};
+using f16_t = _Float16;
+
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(f16_t x) { return (float)x; }
+__device__ __forceinline__ float to_f32(bf16_t x) {
+  return __uint_as_float((uint32_t)x.bits << 16);
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ f16_t from_f32<f16_t>(float x) { return (f16_t)x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
+  // round to nearest even (inputs are finite)
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  bf16_t r;
+  r.bits = (uint16_t)(u >> 16);
+  return r;
+}
+
+// Load 8 consecutive elements (16-byte aligned for 2-byte types, 32-byte for
+// fp32) and widen to fp32.
+__device__ __forceinline__ void load8(const float *p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4 *>(p);
+  const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void load8(const f16_t *p, float (&x)[8]) {
+  const half8 h = *reinterpret_cast<const half8 *>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = (float)h[i];
+}
+__device__ __forceinline__ void load8(const bf16_t *p, float (&x)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4 *>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+// Narrow 8 fp32 values and store them (16-byte aligned for 2-byte types).
+__device__ __forceinline__ void store8(float *p, const float (&x)[8]) {
+  *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  *reinterpret_cast<float4 *>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+}
+__device__ __forceinline__ void store8(f16_t *p, const float (&x)[8]) {
+  half8 h;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = (f16_t)x[i];
+  *reinterpret_cast<half8 *>(p) = h;
+}
+__device__ __forceinline__ void store8(bf16_t *p, const float (&x)[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = (uint32_t)from_f32<bf16_t>(x[2 * i]).bits |
+           ((uint32_t)from_f32<bf16_t>(x[2 * i + 1]).bits << 16);
+  *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Sum over an aligned group of G lanes (G a power of two <= 64); every lane
+// of the group receives the total.
+template <int G> __device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int m = G / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+}  // namespace gdn

@@ -1,0 +1,40 @@
+// gdn_launch.h -- host launchers of the gfx950 kernels.  Called by gdn_api.cpp
+// after the arguments have been validated; each returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+enum class DType : int { F32 = 0, BF16 = 1, F16 = 2 };
+
+struct Shape {
+  int B, T, Hk, Hv, dk, dv, chunk;
+  DType qkv, gate_t;
+  bool key_gate;
+};
+
+// Prologue: conv + SiLU (+ L2) over one tensor [B,T,H,d].
+hipError_t launch_prologue(const void *x, DType xt, const float *w, void *y, DType yt, int B, int T,
+                           int H, int d, bool l2, float eps, hipStream_t s);
+
+// One decode step, state in place.
+hipError_t launch_decode(const Shape &sh, const void *q, const void *k, const void *v,
+                         const void *g, const void *beta, float *S, float *o, hipStream_t s);
+
+// Chunked forward with fp32 arithmetic (any supported dtype in, fp32 math).
+hipError_t launch_chunk_f32(const Shape &sh, const void *q, const void *k, const void *v,
+                            const void *g, const void *beta, const float *S0, float *o,
+                            float *ST, hipStream_t s);
+
+// Chunked forward on the fp16 matrix cores (dk = dv = 128, chunk 64, head gate).
+hipError_t launch_chunk_mfma(const Shape &sh, const void *q, const void *k, const void *v,
+                             const void *g, const void *beta, const float *S0, float *o,
+                             float *ST, hipStream_t s);
+
+// Internal chunk length the fp32 kernels use for a requested chunk and dk.
+int chunk_f32_internal(int chunk, int dk);
+
+}  // namespace gdn

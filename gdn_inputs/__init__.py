@@ -189,3 +189,41 @@ def make_decode_token(wl: Workload, step: int) -> dict:
     }
     out["beta"], out["g"] = make_gates(wl, (B,), extra)
     return out
+
+
+def to_torch(t, device="cuda"):
+    """Upload a stored tensor (Tensor, or a float32 ndarray) as a contiguous torch tensor
+    with the same bits (bfloat16 or float32)."""
+    import torch
+    if isinstance(t, Tensor):
+        if t.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(t.data).view(np.int16)).view(torch.bfloat16).to(device)
+        return torch.from_numpy(np.ascontiguousarray(t.data)).to(device)
+    return torch.from_numpy(np.ascontiguousarray(t, dtype=np.float32)).to(device)
+
+
+def decode_tokens_device(wl: Workload, steps: int, device="cuda", first_step: int = 0):
+    """Fresh tokens for `steps` decode steps drawn on the device (fast path for the
+    1000-step workload): q, k [steps,B,Hk,dk] unit rows, v [steps,B,Hv,dv] ~ N(0,1),
+    beta = sigmoid(N(0,1)), g = logsigmoid(N(g_mu,1)), all rounded to bf16 (or kept fp32).
+    Step s uses torch.Generator seeded with (seed, 1 + s) mixed into one 64-bit word;
+    the same seeds give the same tokens on the same device type."""
+    import torch
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    B = wl.B
+    outs = {n: [] for n in ("q", "k", "v", "beta", "g")}
+    gen = torch.Generator(device=device)
+    for s in range(first_step, first_step + steps):
+        gen.manual_seed((wl.seed * 1_000_003 + 1 + s) & 0x7FFFFFFFFFFFFFFF)
+        q = torch.randn((B, wl.Hk, wl.dk), generator=gen, device=device, dtype=torch.float32)
+        k = torch.randn((B, wl.Hk, wl.dk), generator=gen, device=device, dtype=torch.float32)
+        v = torch.randn((B, wl.Hv, wl.dv), generator=gen, device=device, dtype=torch.float32)
+        bx = torch.randn((B, wl.Hv), generator=gen, device=device, dtype=torch.float32)
+        gshape = (B, wl.Hv) if wl.gate == "head" else (B, wl.Hv, wl.dk)
+        gx = torch.randn(gshape, generator=gen, device=device, dtype=torch.float32) + wl.g_mu
+        outs["q"].append((q / q.norm(dim=-1, keepdim=True)).to(dt))
+        outs["k"].append((k / k.norm(dim=-1, keepdim=True)).to(dt))
+        outs["v"].append(v.to(dt))
+        outs["beta"].append(torch.sigmoid(bx).to(dt))
+        outs["g"].append(torch.nn.functional.logsigmoid(gx).to(dt))
+    return {n: torch.stack(x).contiguous() for n, x in outs.items()}

@@ -1,0 +1,175 @@
+/*
+ * gdn.h -- C ABI of the Gated DeltaNet forward library for AMD Instinct MI355X
+ * (gfx950).  Every operation runs as hand-written HIP kernels on the caller's
+ * stream; the library never allocates or frees device memory.
+ *
+ * The method (the pages are cited by title and section):
+ *   "Source notes" (NextTransformer methods), section "Linear attention",
+ *   row gdn: per (batch, value head) a state S updated token by token with a
+ *   scalar decay applied before the delta update; row kda: the same with a
+ *   per-key-channel decay; row deltanet: causal conv + SiLU and L2-normalised
+ *   q/k in front, read y = q^T S after the write.  Section "Backend and
+ *   numerical limits": query scale 1; fp32 carry and accumulation.
+ *   "Frontier model atlas", entries 03 and 08 (Gated DeltaNet): four-token
+ *   causal convolution; 16 key heads shared by 48 value heads.
+ *
+ * Here the state of one (batch b, value head h) is S in R^{dv x dk} (the
+ * transpose of the pages' K x V state), and for t = 1..T
+ *
+ *     S_t = alpha_t S_{t-1} + beta_t (v_t - alpha_t S_{t-1} k_t) k_t^T
+ *         = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = S_t q_t
+ *
+ * with alpha_t = exp(g_t) (g is the natural-log decay), key/query head
+ * h / (Hv / Hk) for value head h, and, for the per-key-channel gate,
+ * alpha_t S_{t-1} replaced by S_{t-1} diag(exp(g_t)).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers marked "device" are device pointers, caller-owned, contiguous,
+ *    16-byte aligned; they are read-only unless marked out / in-out.
+ *  - Layouts are token-major: q, k [B,T,Hk,dk]; v [B,T,Hv,dv];
+ *    g [B,T,Hv] (head gate) or [B,T,Hv,dk] (key-channel gate);
+ *    beta [B,T,Hv]; o [B,T,Hv,dv]; states [B,Hv,dv,dk] fp32, dk contiguous.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *    asynchronous: they enqueue kernels and return; nothing synchronises.
+ *  - Errors: arguments are validated first, on the host, before anything is
+ *    enqueued; an invalid call returns a non-zero status and writes nothing.
+ *    A failed launch returns GDN_E_HIP.  A fault inside a kernel surfaces at
+ *    the caller's next synchronisation.  gdn_last_error() gives a message
+ *    for the last failing call on the calling thread.
+ *  - The library keeps no state between calls except that per-thread message.
+ *    Calls on different streams may run concurrently.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_E_ARG = 1,         /* null pointer, non-positive size, unknown enum value */
+  GDN_E_SHAPE = 2,       /* inconsistent shapes, e.g. Hv not a multiple of Hk */
+  GDN_E_UNSUPPORTED = 3, /* valid but not built: head dim, chunk, dtype combination */
+  GDN_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  GDN_E_WORKSPACE = 5,   /* workspace smaller than gdn_fwd_workspace_bytes() */
+  GDN_E_HIP = 6          /* a HIP launch failed */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1, GDN_F16 = 2 } gdn_dtype;
+
+typedef enum {
+  GDN_GATE_HEAD = 0,       /* g [B,T,Hv]: one decay per (token, value head) */
+  GDN_GATE_KEY_CHANNEL = 1 /* g [B,T,Hv,dk]: one decay per key channel */
+} gdn_gate;
+
+/* Problem description shared by all entry points. */
+typedef struct gdn_desc {
+  int32_t B;          /* batch (independent sequences), >= 1 */
+  int32_t T;          /* tokens per sequence, >= 1 (1 for gdn_decode_step) */
+  int32_t Hk;         /* key/query heads, >= 1 */
+  int32_t Hv;         /* value heads, a multiple of Hk */
+  int32_t dk;         /* key head dim */
+  int32_t dv;         /* value head dim */
+  int32_t chunk;      /* tokens per chunk of gdn_fwd_chunked (a tuning choice; the
+                         result does not depend on it beyond rounding) */
+  int32_t qkv_dtype;  /* gdn_dtype of q, k, v (and of the prologue's outputs) */
+  int32_t gate_dtype; /* gdn_dtype of g and beta */
+  int32_t gate;       /* gdn_gate */
+} gdn_desc;
+
+/*
+ * gdn_prologue -- 4-tap causal depthwise convolution, SiLU, and L2
+ * normalisation of q and k ("Source notes", Linear attention, rows deltanet
+ * and kda: causal conv + SiLU, L2-normalised Q/K; "Frontier model atlas"
+ * entries 03/08: four-token causal convolution).
+ *
+ * For every channel c of the concatenation (q | k | v) and token t:
+ *     y_t = sum_{j=0..3} conv_w[c][j] * x_{t-3+j}   (x_{t'} = 0 for t' < 0)
+ *     z_t = y_t * sigmoid(y_t)
+ * then each (token, head) row of q and of k is divided by
+ * sqrt(sum z^2 + eps).  Tap 3 multiplies the current token.  There is no
+ * bias and no carry between calls (every sequence starts from zeros).
+ *
+ *   xq, xk  device [B,T,Hk,dk]  x_dtype (GDN_BF16 or GDN_F32)
+ *   xv      device [B,T,Hv,dv]  x_dtype
+ *   conv_w  device fp32 [Hk*dk (q) + Hk*dk (k) + Hv*dv (v)][4]
+ *   q, k    device out [B,T,Hk,dk]  d->qkv_dtype (GDN_F16, GDN_BF16 or GDN_F32)
+ *   v       device out [B,T,Hv,dv]  d->qkv_dtype
+ * Supported: dk, dv in {16, 32, 64, 128}.  d->chunk, gate and gate_dtype are
+ * not used.  Outputs must not alias inputs.
+ */
+gdn_status gdn_prologue(const gdn_desc *d, int32_t x_dtype, const void *xq,
+                        const void *xk, const void *xv, const float *conv_w,
+                        float eps, void *q, void *k, void *v, void *stream);
+
+/* Workspace bytes gdn_fwd_chunked needs for `d` (0 = none; pass NULL). */
+size_t gdn_fwd_workspace_bytes(const gdn_desc *d);
+
+/*
+ * gdn_fwd_chunked -- the forward pass over T tokens from an entering state,
+ * computed chunk by chunk (chunkwise-exact form; the attention-sink study page,
+ * "SinkProbe", states that the chunkwise and token-by-token forms agree).
+ *
+ *   q, k   device [B,T,Hk,dk]  qkv_dtype      v device [B,T,Hv,dv] qkv_dtype
+ *   g      device [B,T,Hv] or [B,T,Hv,dk] (per d->gate)  gate_dtype, natural log, < 0
+ *   beta   device [B,T,Hv]  gate_dtype, in [0, 1]
+ *   S0     device fp32 [B,Hv,dv,dk], or NULL for a zero entering state
+ *   o      device out fp32 [B,T,Hv,dv]
+ *   S_T    device out fp32 [B,Hv,dv,dk]: the state after token T; may be the
+ *          same pointer as S0 (updated in place), must not overlap it otherwise
+ *   workspace, workspace_bytes: at least gdn_fwd_workspace_bytes(d) bytes
+ *
+ * Supported combinations:
+ *  - fp32 mode (qkv_dtype = gate_dtype = GDN_F32): fp32 arithmetic throughout;
+ *    dk, dv in {16, 32, 64, 128}; chunk in {16, 32, 64} with
+ *    chunk * dk <= 4096; either gate.
+ *  - matrix-core mode (qkv_dtype GDN_BF16 or GDN_F16; gate_dtype GDN_BF16 or
+ *    GDN_F32): dk = dv = 128, chunk = 64, head gate.  Products run on the
+ *    gfx950 fp16 matrix cores with fp32 accumulation; the state is carried in
+ *    fp32.  The key-channel gate in this mode runs the fp32 kernels.
+ * o must not alias any input.
+ */
+gdn_status gdn_fwd_chunked(const gdn_desc *d, const void *q, const void *k,
+                           const void *v, const void *g, const void *beta,
+                           const float *S0, float *o, float *S_T,
+                           void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/*
+ * gdn_decode_step -- one token per sequence: the recurrence above with T = 1,
+ * the state updated in place.  For state row i (old values S_i, decayed
+ * row D_i = alpha S_i, or S_i o alpha for the key-channel gate):
+ *     u_i = beta (v_i - D_i . k);   S_i <- D_i + u_i k;   o_i = D_i . q + u_i (k . q)
+ *
+ *   d->T must be 1; d->chunk is not used.
+ *   q, k   device [B,Hk,dk] qkv_dtype (GDN_F32, GDN_BF16 or GDN_F16)
+ *   v      device [B,Hv,dv] qkv_dtype
+ *   g      device [B,Hv] or [B,Hv,dk]  gate_dtype (GDN_F32 or GDN_BF16)
+ *   beta   device [B,Hv] gate_dtype
+ *   S      device in-out fp32 [B,Hv,dv,dk]
+ *   o      device out fp32 [B,Hv,dv]
+ * Supported: dk in {16, 32, 64, 128}; dv a multiple of 16, <= 1024.
+ */
+gdn_status gdn_decode_step(const gdn_desc *d, const void *q, const void *k,
+                           const void *v, const void *g, const void *beta,
+                           float *S, float *o, void *stream);
+
+/* Static text for a status code. */
+const char *gdn_status_str(gdn_status s);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char *gdn_last_error(void);
+
+/* Library version string. */
+const char *gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,114 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, and rejects invalid calls with the documented status before touching
+the device.  No call here reaches a kernel launch."""
+import ctypes
+
+import pytest
+
+import gated_delta_rule_02_amd as gdn
+
+FAKE = 1 << 20          # a 16-byte aligned non-null address; never dereferenced by these calls
+
+
+@pytest.fixture(scope="module")
+def L():
+    return gdn.lib()
+
+
+def test_exports_every_header_function(L):
+    names = gdn.header_functions()
+    assert set(names) >= {"gdn_prologue", "gdn_fwd_chunked", "gdn_decode_step",
+                          "gdn_fwd_workspace_bytes", "gdn_status_str", "gdn_last_error", "gdn_version"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in range(7):
+        assert L.gdn_status_str(code)
+    assert L.gdn_version().startswith(b"gdn-gfx950")
+
+
+def desc(**kw):
+    base = dict(B=2, T=100, Hk=2, Hv=6, dk=128, dv=128, chunk=64, qkv_dtype=gdn.BF16,
+                gate_dtype=gdn.BF16, gate=gdn.GATE_HEAD)
+    base.update(kw)
+    return gdn.GdnDesc(**base)
+
+
+def fwd(L, d, ptrs=None, S0=None):
+    p = [FAKE + i * (1 << 32) for i in range(7)] if ptrs is None else ptrs
+    P = ctypes.c_void_p
+    return L.gdn_fwd_chunked(ctypes.byref(d), *[P(x) for x in p[:5]], P(S0), P(p[5]), P(p[6]),
+                             None, 0, None)
+
+
+def dec(L, d, ptrs=None):
+    p = [FAKE + i * (1 << 32) for i in range(7)] if ptrs is None else ptrs
+    return L.gdn_decode_step(ctypes.byref(d), *[ctypes.c_void_p(x) for x in p], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 1), (dict(T=0), 1), (dict(Hk=0), 1), (dict(dk=-1), 1),
+    (dict(qkv_dtype=7), 1), (dict(gate=3), 1),
+    (dict(Hv=5), 2),                                     # Hv % Hk != 0
+    (dict(dk=64), 3), (dict(chunk=32), 3),               # matrix-core mode: d 128, chunk 64 only
+    (dict(qkv_dtype=gdn.F32, gate_dtype=gdn.BF16), 3),    # unbuilt dtype mix
+    (dict(qkv_dtype=gdn.F32, gate_dtype=gdn.F32, dk=100, dv=100), 3),
+    (dict(qkv_dtype=gdn.F32, gate_dtype=gdn.F32, chunk=64), 3),   # fp32 mode: chunk * dk <= 4096
+    (dict(qkv_dtype=gdn.F32, gate_dtype=gdn.F32, chunk=48, dk=16, dv=16), 3),
+])
+def test_fwd_rejects(L, kw, status):
+    assert fwd(L, desc(**kw)) == status
+    assert L.gdn_last_error()
+
+
+def test_fwd_rejects_null_and_misaligned(L):
+    p = [FAKE + i * (1 << 32) for i in range(7)]
+    for i in range(7):
+        bad = list(p)
+        bad[i] = 0
+        assert fwd(L, desc(), bad) == 1
+        bad[i] = p[i] + 8
+        assert fwd(L, desc(), bad) == 4
+    assert fwd(L, desc(), p, S0=FAKE + 7 * (1 << 32) + 4) == 4
+
+
+def test_fwd_rejects_overlaps(L):
+    p = [FAKE + i * (1 << 32) for i in range(7)]
+    o_on_v = list(p)
+    o_on_v[5] = p[2] + 1024                              # o inside v
+    assert fwd(L, desc(), o_on_v) == 1
+    st_partial = list(p)
+    assert fwd(L, desc(), st_partial, S0=p[6] + 4096) == 1   # S_T partly overlapping S0
+
+
+def test_decode_rejects(L):
+    assert dec(L, desc(T=2)) == 2
+    assert dec(L, desc(T=1, dk=48)) == 3
+    assert dec(L, desc(T=1, dv=40)) == 3
+    assert dec(L, desc(T=1, gate_dtype=gdn.F16)) == 3
+    p = [FAKE + i * (1 << 32) for i in range(7)]
+    p[5] = 0
+    assert dec(L, desc(T=1), p) == 1
+
+
+def test_prologue_rejects(L):
+    d = desc()
+    P = ctypes.c_void_p
+    ptrs = [P(FAKE + i * (1 << 32)) for i in range(7)]
+    assert L.gdn_prologue(ctypes.byref(d), gdn.F16, *ptrs[:4], 1e-6, *ptrs[4:], None) == 3
+    assert L.gdn_prologue(ctypes.byref(d), 9, *ptrs[:4], 1e-6, *ptrs[4:], None) == 1
+    assert L.gdn_prologue(ctypes.byref(desc(dk=96)), gdn.BF16, *ptrs[:4], 1e-6, *ptrs[4:], None) == 3
+    assert L.gdn_prologue(ctypes.byref(d), gdn.BF16, *ptrs[:4], -1.0, *ptrs[4:], None) == 1
+    out_on_in = list(ptrs)
+    out_on_in[4] = ptrs[0]                               # q written over xq
+    assert L.gdn_prologue(ctypes.byref(d), gdn.BF16, *out_on_in[:4], 1e-6, *out_on_in[4:], None) == 1
+
+
+def test_workspace_query(L):
+    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc())) == 0
+
+
+def test_null_desc(L):
+    assert L.gdn_fwd_chunked(None, *([None] * 9), 0, None) == 1

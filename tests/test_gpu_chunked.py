@@ -1,0 +1,165 @@
+"""Chunked forward on the GPU vs the fp64 oracle (token-by-token recurrence)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_02_amd as gdn
+import oracle
+from gdn_inputs import (KDA_PREFILL, LONG_PREFILL, PREFILL_CONV, TINY_F32, make_decode_token,
+                        make_prefill, to_torch)
+from parity import check
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print("[case] " + msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    gdn.lib()
+
+
+def gpu_inputs(inp):
+    return [to_torch(inp[n]) for n in ("q", "k", "v", "g", "beta")]
+
+
+def oracle_inputs(inp):
+    return [inp[n].f32() for n in ("q", "k", "v", "g", "beta")]
+
+
+def run_case(wl, label, S0_alias=False):
+    inp = make_prefill(wl)
+    say("%s: B=%d T=%d Hk=%d Hv=%d d=%d/%d C=%d %s gate=%s S0=%s" %
+        (label, wl.B, wl.T, wl.Hk, wl.Hv, wl.dk, wl.dv, wl.chunk, wl.dtype, wl.gate, wl.s0_std))
+    args = gpu_inputs(inp)
+    S0 = None if inp["S0"] is None else to_torch(inp["S0"])
+    o = torch.full((wl.B, wl.T, wl.Hv, wl.dv), float("nan"), device="cuda")   # unwritten -> NaN
+    ST = S0 if (S0_alias and S0 is not None) else torch.full((wl.B, wl.Hv, wl.dv, wl.dk), float("nan"),
+                                                               device="cuda")
+    o, ST = gdn.fwd_chunked(*args, S0=S0, chunk=wl.chunk, o=o, S_T=ST)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.recurrent_full(*oracle_inputs(inp), inp["S0"])
+    return check("f32" if wl.dtype == "f32" else "bf16", o.cpu().numpy(), o_ref, ST.cpu().numpy(),
+                 S_ref, label)
+
+
+# ---------------------------------------------------------------- fp32 mode
+@pytest.mark.parametrize("T", [64, 1, 15, 17, 50])
+@pytest.mark.parametrize("gate", ["head", "key"])
+def test_tiny_fp32(T, gate):
+    run_case(TINY_F32.with_(T=T, gate=gate), "tiny fp32 T=%d %s" % (T, gate))
+
+
+def test_tiny_fp32_variants():
+    run_case(TINY_F32.with_(s0_std=0.5, B=3, Hk=1, Hv=4), "tiny fp32 S0 grouped heads")
+    run_case(TINY_F32.with_(s0_std=0.5, T=40), "tiny fp32 S_T aliases S0", S0_alias=True)
+    run_case(TINY_F32.with_(dk=64, dv=32, chunk=64, T=130), "fp32 d64/32 C64")
+    run_case(TINY_F32.with_(dk=128, dv=128, chunk=32, T=70, Hk=1, Hv=2), "fp32 d128 C32")
+
+
+def test_tiny_then_decode_fp32():
+    """The tiny workload: prefill on the GPU, then one decode step from the GPU's final state,
+    against the oracle's prefill of T + 1 tokens."""
+    wl = TINY_F32
+    inp = make_prefill(wl)
+    say("tiny fp32 prefill + decode")
+    o, ST = gdn.fwd_chunked(*gpu_inputs(inp), chunk=wl.chunk)
+    tok = make_decode_token(wl, 0)
+    od = gdn.decode_step(*(to_torch(tok[n]) for n in ("q", "k", "v", "g", "beta")), ST)
+    torch.cuda.synchronize()
+    cat = lambda n: np.concatenate([inp[n].f32(), tok[n].f32()[:, None]], axis=1)
+    o_ref, S_ref = oracle.recurrent_full(cat("q"), cat("k"), cat("v"), cat("g"), cat("beta"))
+    check("f32", o.cpu().numpy(), o_ref[:, :wl.T], None, None, "tiny prefill")
+    check("f32", od.cpu().numpy(), o_ref[:, wl.T], ST.cpu().numpy(), S_ref, "tiny decode after prefill")
+
+
+# ---------------------------------------------------------------- bf16 inputs, fp32 state
+SMALL = LONG_PREFILL.with_(B=2, T=200, Hk=2, Hv=6)
+
+
+@pytest.mark.parametrize("T", [200, 1, 63, 65, 64])
+def test_bf16_small(T):
+    run_case(SMALL.with_(T=T), "bf16 small T=%d" % T)
+
+
+def test_bf16_small_variants():
+    run_case(SMALL.with_(s0_std=0.0, g_mu=2.0), "bf16 small S0=0 fast decay")
+    run_case(SMALL.with_(T=130), "bf16 S_T aliases S0", S0_alias=True)
+    run_case(SMALL.with_(Hk=6, Hv=6, T=100), "bf16 no grouping")
+    run_case(KDA_PREFILL.with_(B=1, T=150, Hk=2, Hv=2), "bf16 key gate small")
+
+
+def test_bf16_conv_small():
+    """Conv workload, reduced: GPU prologue -> GPU chunked vs oracle prologue -> oracle recurrence."""
+    wl = PREFILL_CONV.with_(B=1, T=300, Hk=2, Hv=6)
+    inp = make_prefill(wl)
+    say("bf16 conv small")
+    q, k, v = gdn.prologue(*(to_torch(inp[n]) for n in ("xq", "xk", "xv")), to_torch(inp["conv_w"]),
+                           out_dtype=torch.float16)
+    o, ST = gdn.fwd_chunked(q, k, v, to_torch(inp["g"]), to_torch(inp["beta"]), chunk=wl.chunk)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.prologue(inp["xq"].f32(), inp["xk"].f32(), inp["xv"].f32(), inp["conv_w"])
+    o_ref, S_ref = oracle.recurrent_full(rq, rk, rv, inp["g"].f32(), inp["beta"].f32())
+    check("bf16", o.cpu().numpy(), o_ref, ST.cpu().numpy(), S_ref, "conv small")
+
+
+def test_deterministic():
+    inp = make_prefill(SMALL)
+    say("determinism")
+    a = gdn.fwd_chunked(*gpu_inputs(inp), S0=to_torch(inp["S0"]))
+    b = gdn.fwd_chunked(*gpu_inputs(inp), S0=to_torch(inp["S0"]))
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------- full sizes, sampled chains
+def sampled(wl, chains, label, conv=False):
+    inp = make_prefill(wl)
+    say("%s full size, chains %s" % (label, chains))
+    if conv:
+        q, k, v = gdn.prologue(*(to_torch(inp[n]) for n in ("xq", "xk", "xv")),
+                               to_torch(inp["conv_w"]), out_dtype=torch.float16)
+        args = [q, k, v, to_torch(inp["g"]), to_torch(inp["beta"])]
+    else:
+        args = gpu_inputs(inp)
+    S0 = None if inp["S0"] is None else to_torch(inp["S0"])
+    o, ST = gdn.fwd_chunked(*args, S0=S0, chunk=wl.chunk)
+    torch.cuda.synchronize()
+    grp = wl.Hv // wl.Hk
+    for (b, h) in chains:
+        kh = h // grp
+        if conv:
+            d = wl.dk
+            nq = wl.Hk * d
+            w = inp["conv_w"]
+            sl = lambda x, hh: np.ascontiguousarray(x.f32()[b:b + 1, :, hh:hh + 1])
+            qr = oracle.conv_silu(sl(inp["xq"], kh), w[kh * d:(kh + 1) * d], True)
+            kr = oracle.conv_silu(sl(inp["xk"], kh), w[nq + kh * d: nq + (kh + 1) * d], True)
+            vr = oracle.conv_silu(sl(inp["xv"], h), w[2 * nq + h * d: 2 * nq + (h + 1) * d], False)
+        else:
+            qr = inp["q"].f32()[b:b + 1, :, kh:kh + 1]
+            kr = inp["k"].f32()[b:b + 1, :, kh:kh + 1]
+            vr = inp["v"].f32()[b:b + 1, :, h:h + 1]
+        gr = inp["g"].f32()[b:b + 1, :, h:h + 1]
+        br = inp["beta"].f32()[b:b + 1, :, h:h + 1]
+        s0 = None if inp["S0"] is None else inp["S0"][b:b + 1, h:h + 1]
+        o_ref, S_ref = oracle.recurrent(qr, kr, vr, gr, br, s0)
+        check("bf16", o[b, :, h].cpu().numpy(), o_ref[0], ST[b, h].cpu().numpy(), S_ref[0],
+              "%s chain (%d,%d)" % (label, b, h))
+
+
+def test_full_prefill_conv_sampled():
+    sampled(PREFILL_CONV, [(0, 0), (1, 20), (3, 47)], "prefill+conv", conv=True)
+
+
+def test_full_long_prefill_sampled():
+    sampled(LONG_PREFILL, [(0, 0), (0, 29)], "long prefill")
+
+
+def test_full_key_gate_sampled():
+    sampled(KDA_PREFILL, [(0, 0), (1, 31)], "key gate")

@@ -1,0 +1,122 @@
+"""Decode step on the GPU vs the fp64 oracle (the recurrence with T = 1, state carried)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_02_amd as gdn
+import oracle
+from gdn_inputs import (BATCHED_DECODE, TINY_F32, decode_tokens_device, make_decode_token,
+                        make_prefill, make_state, to_torch)
+from parity import check
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print("[case] " + msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    gdn.lib()
+
+
+def stack_steps(tokens):
+    """List of per-step dicts of Tensor [B,...] -> float32 arrays [B,steps,...] for the oracle."""
+    out = {}
+    for n in ("q", "k", "v", "g", "beta"):
+        out[n] = np.stack([t[n].f32() for t in tokens], axis=1)
+    return out
+
+
+def run_gpu_steps(tokens, S):
+    os_ = []
+    for t in tokens:
+        o = gdn.decode_step(*(to_torch(t[n]) for n in ("q", "k", "v", "g", "beta")), S)
+        os_.append(o)
+    torch.cuda.synchronize()
+    return torch.stack(os_, dim=1).cpu().numpy()
+
+
+@pytest.mark.parametrize("gate", ["head", "key"])
+def test_decode_tiny_fp32(gate):
+    """One fp32 decode step from the state a 64-token prefill left (the tiny workload)."""
+    wl = TINY_F32.with_(gate=gate)
+    say("decode tiny fp32 gate=%s" % gate)
+    inp = make_prefill(wl)
+    _, ST = oracle.recurrent_full(inp["q"].f32(), inp["k"].f32(), inp["v"].f32(), inp["g"].f32(),
+                                  inp["beta"].f32(), None)
+    S_in = ST.astype(np.float32)                       # an input: the oracle's state, rounded to fp32
+    tok = make_decode_token(wl, 0)
+    S = to_torch(S_in)
+    o = run_gpu_steps([tok], S)
+    r = stack_steps([tok])
+    o_ref, S_ref = oracle.recurrent_full(r["q"], r["k"], r["v"], r["g"], r["beta"], S_in)
+    check("f32", o, o_ref, S.cpu().numpy(), S_ref, "decode tiny fp32 %s" % gate)
+
+
+@pytest.mark.parametrize("gate,qdt", [("head", "bf16"), ("key", "bf16"), ("head", "f32")])
+def test_decode_steps_small(gate, qdt):
+    """20 consecutive steps, B = 4, 16 key / 48 value heads, state carried on the GPU."""
+    wl = BATCHED_DECODE.with_(B=4, gate=gate, dtype=qdt)
+    say("decode small 20 steps gate=%s dtype=%s" % (gate, qdt))
+    S0 = make_state(wl)
+    toks = [make_decode_token(wl, s) for s in range(20)]
+    S = to_torch(S0)
+    o = run_gpu_steps(toks, S)
+    r = stack_steps(toks)
+    o_ref, S_ref = oracle.recurrent_full(r["q"], r["k"], r["v"], r["g"], r["beta"], S0)
+    mode = "f32" if qdt == "f32" else "bf16"
+    check(mode, o, o_ref, S.cpu().numpy(), S_ref, "decode small %s %s" % (gate, qdt))
+    if qdt == "bf16":                                   # fp32 state arithmetic: far inside the bar
+        check("f32", o, o_ref, S.cpu().numpy(), S_ref, "decode small %s %s (fp32 bar)" % (gate, qdt))
+
+
+def test_decode_full_batch_sampled():
+    """The batched-decode workload at full size (B = 256, 16/48 heads, d 128): 200 steps on
+    the GPU, oracle replay of sampled chains; o compared at steps 1, 10, 100, 200 and S at the end."""
+    wl = BATCHED_DECODE
+    steps = 200
+    say("decode full batch B=256 steps=%d" % steps)
+    S0 = make_state(wl)
+    toks = decode_tokens_device(wl, steps)
+    S = to_torch(S0)
+    o_all = []
+    for s in range(steps):
+        o_all.append(gdn.decode_step(toks["q"][s], toks["k"][s], toks["v"][s], toks["g"][s],
+                                     toks["beta"][s], S))
+    torch.cuda.synchronize()
+    chains = [(0, 0), (17, 5), (101, 31), (200, 47), (255, 46), (128, 24)]
+    grp = wl.Hv // wl.Hk
+    for (b, h) in chains:
+        kh = h // grp
+        f = lambda x: x.float().cpu().numpy()
+        q = f(toks["q"][:, b, kh])[None, :, None]
+        k = f(toks["k"][:, b, kh])[None, :, None]
+        v = f(toks["v"][:, b, h])[None, :, None]
+        g = f(toks["g"][:, b, h])[None, :, None]
+        beta = f(toks["beta"][:, b, h])[None, :, None]
+        o_ref, S_ref = oracle.recurrent(q, k, v, g, beta, S0[b:b + 1, h:h + 1])
+        o = np.stack([o_all[s][b, h].cpu().numpy() for s in range(steps)])
+        idx = [0, 9, 99, 199]
+        check("bf16", o[idx], o_ref[0][idx], S[b, h].cpu().numpy(), S_ref[0],
+              "decode full chain (%d,%d)" % (b, h))
+        check("f32", o[idx], o_ref[0][idx], S[b, h].cpu().numpy(), S_ref[0],
+              "decode full chain (%d,%d) fp32 bar" % (b, h))
+
+
+def test_decode_deterministic_and_in_place():
+    wl = BATCHED_DECODE.with_(B=8)
+    say("decode determinism")
+    S0 = make_state(wl)
+    tok = make_decode_token(wl, 3)
+    args = [to_torch(tok[n]) for n in ("q", "k", "v", "g", "beta")]
+    S1, S2 = to_torch(S0), to_torch(S0)
+    o1 = gdn.decode_step(*args, S1)
+    o2 = gdn.decode_step(*args, S2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    assert not torch.equal(S1, to_torch(S0))
