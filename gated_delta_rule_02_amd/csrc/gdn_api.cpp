@@ -87,6 +87,13 @@ gdn_status check_ptrs(const char *const *names, const void *const *ptrs, int n) 
   return GDN_OK;
 }
 
+// The matrix-core path: 16-bit q/k/v, head gate, dk = dv = 128, chunk 64.
+bool uses_matrix_cores(const gdn_desc *d) {
+  const bool mc_mode = (d->qkv_dtype == GDN_BF16 || d->qkv_dtype == GDN_F16) &&
+                       (d->gate_dtype == GDN_BF16 || d->gate_dtype == GDN_F32);
+  return mc_mode && d->gate == GDN_GATE_HEAD && d->dk == 128 && d->dv == 128 && d->chunk == 64;
+}
+
 gdn_status launched(hipError_t e, const char *what) {
   if (e != hipSuccess) return fail(GDN_E_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
@@ -154,8 +161,12 @@ gdn_status gdn_prologue(const gdn_desc *d, int32_t x_dtype, const void *xq, cons
 }
 
 size_t gdn_fwd_workspace_bytes(const gdn_desc *d) {
-  (void)d;
-  return 0;
+  gdn::Shape sh;
+  const std::string saved = g_last_error;  // a query does not change the last error
+  const gdn_status st = check_desc(d, &sh);
+  g_last_error = saved;
+  if (st != GDN_OK) return 0;
+  return uses_matrix_cores(d) ? gdn::chunk_mfma_workspace(sh) : 0;
 }
 
 gdn_status gdn_fwd_chunked(const gdn_desc *d, const void *q, const void *k, const void *v,
@@ -164,9 +175,6 @@ gdn_status gdn_fwd_chunked(const gdn_desc *d, const void *q, const void *k, cons
   gdn::Shape sh;
   gdn_status st = check_desc(d, &sh);
   if (st != GDN_OK) return st;
-  (void)workspace;
-  (void)workspace_bytes;  // no workspace is needed (gdn_fwd_workspace_bytes returns 0)
-
   const bool fp32_mode = d->qkv_dtype == GDN_F32 && d->gate_dtype == GDN_F32;
   const bool mc_mode = (d->qkv_dtype == GDN_BF16 || d->qkv_dtype == GDN_F16) &&
                        (d->gate_dtype == GDN_BF16 || d->gate_dtype == GDN_F32);
@@ -218,8 +226,21 @@ gdn_status gdn_fwd_chunked(const gdn_desc *d, const void *q, const void *k, cons
       return fail(GDN_E_ARG, "S_T must be S0 itself or not overlap it");
   }
 
+  if (use_mfma) {
+    const size_t need = gdn::chunk_mfma_workspace(sh);
+    if (workspace_bytes < need)
+      return fail(GDN_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    if (!workspace) return fail(GDN_E_ARG, "workspace is NULL");
+    if (!aligned16(workspace)) return fail(GDN_E_ALIGN, "workspace is not 16-byte aligned");
+    const Range rw = range(workspace, need);
+    for (const Range &r : ins)
+      if (overlap(rw, r)) return fail(GDN_E_ARG, "workspace must not overlap an input");
+    if (overlap(rw, ro) || overlap(rw, rst) || (S0 && overlap(rw, range(S0, state_bytes))))
+      return fail(GDN_E_ARG, "workspace must not overlap o, S0 or S_T");
+  }
+
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = use_mfma ? gdn::launch_chunk_mfma(sh, q, k, v, g, beta, S0, o, S_T, s)
+  hipError_t e = use_mfma ? gdn::launch_chunk_mfma(sh, q, k, v, g, beta, S0, o, S_T, workspace, s)
                           : gdn::launch_chunk_f32(sh, q, k, v, g, beta, S0, o, S_T, s);
   return launched(e, "chunked forward launch");
 }

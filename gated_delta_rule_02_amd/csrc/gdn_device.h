@@ -79,6 +79,15 @@ __device__ __forceinline__ void store8(bf16_t *p, const float (&x)[8]) {
   *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Workgroup barrier for hand-offs through LDS only: waits for this wave's
+// LDS operations, then for the other waves.  Unlike __syncthreads(), it does
+// not drain the wave's outstanding global loads and stores, so prefetches and
+// output stores stay in flight across it.  Use it only where no other wave
+// reads global memory this wave wrote.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Sum over an aligned group of G lanes (G a power of two <= 64); every lane
 // of the group receives the total.
 template <int G> __device__ __forceinline__ float group_sum(float x) {

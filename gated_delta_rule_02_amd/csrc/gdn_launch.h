@@ -29,10 +29,12 @@ hipError_t launch_chunk_f32(const Shape &sh, const void *q, const void *k, const
                             const void *g, const void *beta, const float *S0, float *o,
                             float *ST, hipStream_t s);
 
-// Chunked forward on the fp16 matrix cores (dk = dv = 128, chunk 64, head gate).
+// Chunked forward on the fp16 matrix cores (dk = dv = 128, chunk 64, head
+// gate).  `ws` holds chunk_mfma_workspace(sh) bytes (16-byte aligned).
 hipError_t launch_chunk_mfma(const Shape &sh, const void *q, const void *k, const void *v,
                              const void *g, const void *beta, const float *S0, float *o,
-                             float *ST, hipStream_t s);
+                             float *ST, void *ws, hipStream_t s);
+size_t chunk_mfma_workspace(const Shape &sh);
 
 // Internal chunk length the fp32 kernels use for a requested chunk and dk.
 int chunk_f32_internal(int chunk, int dk);

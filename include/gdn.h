@@ -107,7 +107,13 @@ gdn_status gdn_prologue(const gdn_desc *d, int32_t x_dtype, const void *xq,
                         const void *xk, const void *xv, const float *conv_w,
                         float eps, void *q, void *k, void *v, void *stream);
 
-/* Workspace bytes gdn_fwd_chunked needs for `d` (0 = none; pass NULL). */
+/*
+ * Device workspace bytes gdn_fwd_chunked needs for `d` (0 = none; then the
+ * workspace pointer may be NULL).  The matrix-core path keeps the per-chunk
+ * triangular inverses there: 6144 bytes per (batch, value head, chunk).
+ * Returns 0 for an invalid description.  The caller owns the workspace; it
+ * is scratch between calls and must not be shared by concurrent calls.
+ */
 size_t gdn_fwd_workspace_bytes(const gdn_desc *d);
 
 /*
@@ -122,7 +128,9 @@ size_t gdn_fwd_workspace_bytes(const gdn_desc *d);
  *   o      device out fp32 [B,T,Hv,dv]
  *   S_T    device out fp32 [B,Hv,dv,dk]: the state after token T; may be the
  *          same pointer as S0 (updated in place), must not overlap it otherwise
- *   workspace, workspace_bytes: at least gdn_fwd_workspace_bytes(d) bytes
+ *   workspace   device scratch of at least gdn_fwd_workspace_bytes(d) bytes,
+ *               16-byte aligned, not overlapping any other argument
+ *               (GDN_E_WORKSPACE if too small)
  *
  * Supported combinations:
  *  - fp32 mode (qkv_dtype = gate_dtype = GDN_F32): fp32 arithmetic throughout;

@@ -107,7 +107,26 @@ def test_prologue_rejects(L):
 
 
 def test_workspace_query(L):
-    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc())) == 0
+    # matrix-core path: 6144 bytes per (batch, value head, 64-token chunk)
+    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc())) == 2 * 6 * 2 * 6144
+    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(T=1))) == 2 * 6 * 1 * 6144
+    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(gate=gdn.GATE_KEY_CHANNEL))) == 0
+    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(qkv_dtype=gdn.F32, gate_dtype=gdn.F32, chunk=32))) == 0
+    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(Hv=5))) == 0       # invalid description
+    assert L.gdn_fwd_workspace_bytes(None) == 0
+
+
+def test_workspace_checked_before_launch(L):
+    d = desc()
+    need = L.gdn_fwd_workspace_bytes(ctypes.byref(d))
+    P = ctypes.c_void_p
+    p = [FAKE + i * (1 << 32) for i in range(8)]
+    args = [P(x) for x in p[:5]] + [None, P(p[5]), P(p[6])]
+    assert L.gdn_fwd_chunked(ctypes.byref(d), *args, None, 0, None) == 5
+    assert L.gdn_fwd_chunked(ctypes.byref(d), *args, P(p[7]), need - 16, None) == 5
+    assert L.gdn_fwd_chunked(ctypes.byref(d), *args, None, need, None) == 1
+    assert L.gdn_fwd_chunked(ctypes.byref(d), *args, P(p[7] + 8), need, None) == 4
+    assert L.gdn_fwd_chunked(ctypes.byref(d), *args, P(p[2]), need, None) == 1   # on top of v
 
 
 def test_null_desc(L):
