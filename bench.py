@@ -1,0 +1,261 @@
+"""Throughput benchmark of the Gated DeltaNet forward hot path on one MI355X.
+
+One step = the whole hot path over one batch of the conv-prologue prefill
+workload (B 4, T 4096, 16 key / 48 value heads, d 128, chunk 64, bf16
+inputs): 4-tap conv + SiLU + L2 prologue -> chunked prefill (fp16 matrix
+cores, fp32 state) -> one decode step from the final state on a fresh token.
+`value` is prefill tokens/s of that step (B*T / step time).  Inputs are
+seeded synthetic data resident in HBM before the timed region.
+
+Also reported on the same line (each timed with HIP events on the stream the
+kernels run on):
+  roofline      the dominant kernel (the chunked forward: prep + sequential
+                launches) against the dense fp16 matrix-core peak;
+  kernels       prologue and decode against the HBM peak;
+  decode        steps/s of the batched-decode workload (B 256, 1000 steps);
+  cpu_baseline  the fp64 oracle on the host cores on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+       python bench.py --calibrate-copy   (a plain 1 GiB device copy, five times: the
+                                          reference for scaling rocprofv3 HBM byte counters)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, GB/s
+PEAK_F16_TFLOPS = 2500.0         # MI355X dense fp16/bf16 matrix cores, TFLOP/s
+FLOPS_PER_TOKEN_HEAD = 180224    # algorithmic prefill flops per (token, value head) at C 64, d 128
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "chunk_fwd_prefill_conv_B4_T4096_pmc.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "gated_delta_rule_02_amd", "csrc", "chunk_mfma.hip")
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch of the chunked forward from the committed rocprofv3
+    summary, or None when the kernel source changed since it was taken."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    fields = dict(line.split("=", 1) for line in text.splitlines() if "=" in line and not line.startswith("#"))
+    if fields.get("kernel_source_sha256_16", "").strip() != source_hash(KERNEL_SOURCE):
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_events(fn, reps, stream):
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps / 1e3   # seconds per call
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the forward pass here runs on a single MI355X "
+              "(no multi-GPU path is built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_02_amd as gdn
+    from gdn_inputs import BATCHED_DECODE, PREFILL_CONV, decode_tokens_device, make_decode_token, \
+        make_prefill, make_state, to_torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)      # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_each_way": src.numel() * 4, "copies": 5}), flush=True)
+        return
+    stream = torch.cuda.current_stream()
+    gdn.lib()
+
+    # ------------------------------------------------------------------ inputs
+    wl = PREFILL_CONV
+    B, T, Hk, Hv, dk, dv, C = wl.B, wl.T, wl.Hk, wl.Hv, wl.dk, wl.dv, wl.chunk
+    log("generating inputs: %s" % wl.name)
+    inp = make_prefill(wl)
+    xq, xk, xv = (to_torch(inp[n], dev) for n in ("xq", "xk", "xv"))
+    w = to_torch(inp["conv_w"], dev)
+    g, beta = to_torch(inp["g"], dev), to_torch(inp["beta"], dev)
+    tok = make_decode_token(wl, 0)
+    dq, dk_, dv_, dg, db = (to_torch(tok[n], dev) for n in ("q", "k", "v", "g", "beta"))
+    q = torch.empty((B, T, Hk, dk), dtype=torch.float16, device=dev)
+    k = torch.empty_like(q)
+    v = torch.empty((B, T, Hv, dv), dtype=torch.float16, device=dev)
+    o = torch.empty((B, T, Hv, dv), dtype=torch.float32, device=dev)
+    ST = torch.empty((B, Hv, dv, dk), dtype=torch.float32, device=dev)
+    od = torch.empty((B, Hv, dv), dtype=torch.float32, device=dev)
+    L = gdn.lib()
+    desc = gdn.make_desc(B, T, Hk, Hv, dk, dv, C, gdn.F16, gdn.BF16, gdn.GATE_HEAD)
+    ws = torch.empty(L.gdn_fwd_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    import ctypes
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    pdesc = gdn.make_desc(B, T, Hk, Hv, dk, dv, C, gdn.F16, gdn.F32, gdn.GATE_HEAD)
+    ddesc = gdn.make_desc(B, 1, Hk, Hv, dk, dv, C, gdn.BF16, gdn.BF16, gdn.GATE_HEAD)
+    s_ptr = ctypes.c_void_p(stream.cuda_stream)
+
+    def prologue():
+        gdn.check(L.gdn_prologue(ctypes.byref(pdesc), gdn.BF16, P(xq), P(xk), P(xv), P(w), 1e-6,
+                                 P(q), P(k), P(v), s_ptr))
+
+    def chunked():
+        gdn.check(L.gdn_fwd_chunked(ctypes.byref(desc), P(q), P(k), P(v), P(g), P(beta), None,
+                                    P(o), P(ST), P(ws), ws.numel(), s_ptr))
+
+    def decode():
+        gdn.check(L.gdn_decode_step(ctypes.byref(ddesc), P(dq), P(dk_), P(dv_), P(dg), P(db), P(ST),
+                                    P(od), s_ptr))
+
+    def step():
+        prologue()
+        chunked()
+        decode()
+
+    # ------------------------------------------------------------------ timed steps
+    log("warmup %d, timed %d steps" % (args.warmup, args.steps))
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / args.steps
+    tokens_per_s = B * T / t_step
+    log("step %.1f us -> %.3e tokens/s" % (t_step * 1e6, tokens_per_s))
+
+    # ------------------------------------------------------------------ per-kernel (HIP events)
+    reps = max(5, args.steps)
+    t_pro = time_events(prologue, reps, stream)
+    t_chk = time_events(chunked, reps, stream)
+    bytes_pro = (2 * B * T * Hk * dk + B * T * Hv * dv) * (2 + 2) + w.numel() * 4
+    bytes_chk = (2 * B * T * Hk * dk + B * T * Hv * dv) * 2 + 2 * B * T * Hv * 2 \
+        + B * T * Hv * dv * 4 + B * Hv * dv * dk * 4
+    flops_chk = FLOPS_PER_TOKEN_HEAD * B * T * Hv
+    achieved = flops_chk / t_chk / 1e12
+    traffic = read_traffic()
+    log("prologue %.1f us (%.0f GB/s); chunked %.1f us (%.1f TFLOP/s, %.0f GB/s algorithmic)" %
+        (t_pro * 1e6, bytes_pro / t_pro / 1e9, t_chk * 1e6, achieved, bytes_chk / t_chk / 1e9))
+
+    # ------------------------------------------------------------------ batched decode workload
+    dwl = BATCHED_DECODE
+    nsteps = args.decode_steps
+    log("decode workload: %s, %d steps" % (dwl.name, nsteps))
+    S_init = to_torch(make_state(dwl), dev)
+    S = S_init.clone()
+    toks = decode_tokens_device(dwl, nsteps, dev)
+    od2 = torch.empty((dwl.B, dwl.Hv, dwl.dv), dtype=torch.float32, device=dev)
+    d3 = gdn.make_desc(dwl.B, 1, dwl.Hk, dwl.Hv, dwl.dk, dwl.dv, 64, gdn.BF16, gdn.BF16, gdn.GATE_HEAD)
+    tq, tk, tv, tg, tb = (toks[n] for n in ("q", "k", "v", "g", "beta"))
+
+    def decode_run():
+        for s in range(nsteps):
+            gdn.check(L.gdn_decode_step(ctypes.byref(d3), P(tq[s]), P(tk[s]), P(tv[s]), P(tg[s]),
+                                        P(tb[s]), P(S), P(od2), s_ptr))
+
+    decode_run()                                   # warm-up pass
+    S.copy_(S_init)
+    torch.cuda.synchronize()
+    t_dec = time_events(decode_run, 1, stream) / nsteps
+    bytes_dec = 2 * S.numel() * 4 + od2.numel() * 4 + (2 * dwl.B * dwl.Hk * dwl.dk + dwl.B * dwl.Hv * dwl.dv) * 2 \
+        + 2 * dwl.B * dwl.Hv * 2
+    log("decode %.1f us/step, %.0f steps/s, %.0f GB/s" % (t_dec * 1e6, 1 / t_dec, bytes_dec / t_dec / 1e9))
+    del toks, S, S_init
+
+    # ------------------------------------------------------------------ CPU baseline (oracle)
+    import oracle
+    nthreads = min(os.cpu_count() or 1, 16)
+    sample_b = [0, 1]
+    log("cpu baseline: fp64 oracle, prologue + recurrence for batch elements %s (%d chains), %d threads" %
+        (sample_b, len(sample_b) * Hv, nthreads))
+    t0 = time.perf_counter()
+    xs = lambda n: np.ascontiguousarray(inp[n].f32()[sample_b])
+    rq, rk, rv = oracle.prologue(xs("xq"), xs("xk"), xs("xv"), inp["conv_w"])
+    oracle.recurrent(rq, rk, rv, xs("g"), xs("beta"), None,
+                     [(b, h) for b in range(len(sample_b)) for h in range(Hv)], nthreads=nthreads)
+    t_cpu = time.perf_counter() - t0
+    cpu_tokens_per_s = len(sample_b) * T / t_cpu
+    log("cpu baseline %.1f s -> %.3e tokens/s" % (t_cpu, cpu_tokens_per_s))
+
+    line = {
+        "metric": "GDN fwd prefill tokens/s + decode steps/s on 1 GPU; % of MFMA/HBM roofline",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "precision": "bf16 inputs; fp16 matrix-core operands; fp32 accumulation, state and output",
+        "data": "synthetic",
+        "config": {"workload": "prefill with conv prologue, then one decode step", "B": B, "T": T,
+                   "Hk": Hk, "Hv": Hv, "dk": dk, "dv": dv, "chunk": C, "gate": "per value head",
+                   "step": "prologue + chunked prefill + 1 decode step"},
+        "roofline": {"kernel": "chunked forward (chunk_prep + chunk_seq launches)", "bound": "mfma",
+                     "achieved": achieved, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_F16_TFLOPS, "traffic": traffic,
+                     "algorithmic_bytes": bytes_chk, "us_per_launch": t_chk * 1e6,
+                     "hbm_frac_algorithmic": bytes_chk / t_chk / 1e9 / PEAK_HBM_GBS},
+        "kernels": {
+            "prologue": {"bound": "hbm", "achieved": bytes_pro / t_pro / 1e9, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": bytes_pro / t_pro / 1e9 / PEAK_HBM_GBS,
+                         "us_per_launch": t_pro * 1e6},
+            "decode": {"bound": "hbm", "achieved": bytes_dec / t_dec / 1e9, "peak": PEAK_HBM_GBS,
+                       "unit": "GB/s", "frac": bytes_dec / t_dec / 1e9 / PEAK_HBM_GBS,
+                       "us_per_launch": t_dec * 1e6},
+        },
+        "decode": {"workload": "batched decode: B 256, 16/48 heads, d 128, fp32 state, %d steps" % nsteps,
+                   "steps_per_s": 1.0 / t_dec, "tokens_per_s": dwl.B / t_dec},
+        "cpu_baseline": {"value": cpu_tokens_per_s, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+                         "sample": "fp64 prologue + token recurrence for batch elements 0-1 of the same "
+                                   "workload (96 of 192 chains, all 4096 tokens)",
+                         "seconds": t_cpu},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
