@@ -25,34 +25,37 @@
 // triangular inverse has fp32 16 x 16 diagonal blocks and fp16-MFMA
 // off-diagonal blocks, and the state is carried in fp32 accumulators.
 //
+// Fragments.  A 16x16x32 MFMA only needs its A and B operands to agree on the
+// order of the 32 contraction indices a lane group holds.  Here lane group g
+// (lanes 16 g .. 16 g + 15) of step kk holds the indices
+//     kset(g, kk) = {32 kk + 4 g + e, 32 kk + 16 + 4 g + e : e = 0..3},
+// which are exactly the rows an accumulator tile pair (16 rows each) leaves in
+// that lane group.  So an MFMA result can feed the next MFMA as an operand
+// without leaving the lane that computed it.
+//
 // Two kernels.
-//  * chunk_prep (every chunk in parallel): for one (batch, key head, chunk)
-//    G = K K^T once, then for each value head of the group A and
-//    T = (I + A)^{-1}: the 16 x 16 diagonal blocks by forward substitution in
-//    fp32 (wave w -> block w), the off-diagonal blocks column by column with
-//    16x16x16 MFMAs (wave w -> column w), T_RS = -T_RR sum_M A_RM T_MS.  T is
-//    written to the workspace as the six MFMA A-operand fragments the
-//    sequential kernel consumes (6 KB per chunk and value head).
-//  * chunk_seq (the chunks of one sequence in order): one 256-thread
-//    workgroup owns DVS = 32 rows of the state of one (batch, value head)
-//    (rows evolve independently) and keeps them in fp32 accumulators.  Per
-//    chunk only the state-dependent products remain on its path:
-//      phase 1  K S^T -> X^T (LDS);  S Q^T (the read, kept transposed so a
-//               lane holds 4 adjacent value channels of one token);
-//               (Q K^T)^T tiles -> decayed, masked P kept in registers
-//      phase 2  N = T X  -> N^T, (diag(e^{gamma_n-gamma}) N)^T (LDS)
-//      phase 3  O^T = Gamma (S Q^T) + N^T P^T -> HBM (16-byte stores);
-//               S = Gamma_n S + N^T diag(..) K  (K columns read from LDS)
-//    P never touches LDS: the MFMA only needs A and B to agree on the order
-//    of the contraction index, so the P fragment packs the two (Q K^T)^T
-//    tiles of a 32-wide step as {4 g..4 g+3, 16+4 g..16+4 g+3} and N^T is
-//    read in the same order.  Q and T go straight from memory into MFMA
-//    registers.  LDS is 46 KB.  Blocks are numbered so that the 4 slices and
-//    the value heads sharing a key head land on one XCD (shared K/Q and the
-//    64-byte V rows then hit in its L2).  The next chunk's loads are issued
-//    into registers during the current chunk and land in LDS at its end;
-//    the workgroup barriers wait for LDS traffic only, so those loads and the
-//    output stores stay in flight across them.
+//  * chunk_prep (every chunk in parallel), per (batch, key head, chunk):
+//    G = K K^T and P0 = masked Q K^T once; then per value head of the group
+//    A and T = (I + A)^{-1} (16 x 16 diagonal blocks by forward substitution
+//    in fp32, wave w -> block w; off-diagonal blocks column by column with
+//    16x16x16 MFMAs, wave w -> column w: T_RS = -T_RR sum_M A_RM T_MS).  T (per
+//    value head) and P0 (per key head) go to the workspace as 64 x 64
+//    lower-triangular matrices in fragment order: six 1 KB fragments each,
+//    lane (g, l) of fragment (R, kk) holding row 16 R + l at columns kset(g, kk).
+//  * chunk_seq (the chunks of one sequence in order): a 256-thread workgroup
+//    owns 4 * DW value rows of the state of one (batch, value head); wave w
+//    owns DW of them (rows evolve independently) for all 64 rows of a chunk,
+//    in fp32 accumulators.  Its whole chain stays in registers:
+//        S (fp32) -> S fragments (fp16)                    [no data movement]
+//        X = beta V - beta Gamma K S^T                     (K from LDS)
+//        N = T X,  N~ = diag(e^{gamma_n - gamma}) N        (T from memory)
+//        O^T = Gamma (S Q^T) + N^T (L o P0)^T -> HBM       (Q from LDS, P0 from memory)
+//        S^T <- Gamma_n S^T + K^T N~                       (K columns from LDS)
+//    so the four waves share only the chunk's K, Q, V tiles and gate scalars,
+//    double-buffered in LDS: one barrier per chunk.  The next chunk's raw
+//    loads (and its T and P0 fragments) are issued at the top of a chunk and
+//    land at its end.  Blocks are numbered so that workgroups sharing a key
+//    head run on one XCD (shared K, Q and P0 then hit in its L2).
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -61,17 +64,13 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int DK = 128, DV = 128, C = 64;
-constexpr int DVS = 32;             // state rows per sequential workgroup
-constexpr int NS = DV / DVS;        // slices per head
-constexpr int NI = DVS / 16;        // 16-wide value tiles per slice
-constexpr int NFRAG = 6;            // T fragments per chunk: (R,kk) = (0,0),(1,0),(2,0),(2,1),(3,0),(3,1)
-constexpr size_t T_BYTES = NFRAG * 64 * 16;   // per (chunk, value head)
+constexpr int NFRAG = 6;                      // fragments (R, kk): (0,0),(1,0),(2,0),(2,1),(3,0),(3,1)
+constexpr size_t FRAGS_BYTES = NFRAG * 64 * 16;   // one 64 x 64 lower-triangular matrix
 
 // LDS strides (elements)
-constexpr int KST = DK + 8;         // sK, sS rows (fp16)
-constexpr int CST = C + 8;          // sT, sAo, sXt, sNt, sNd rows (fp16)
-constexpr int VST = DVS + 8;        // sV rows (fp16)
-constexpr int DST = 17;             // sAd rows (fp32)
+constexpr int KST = DK + 8;                   // K, Q rows (fp16)
+constexpr int CST = C + 8;                    // 64 x 64 fp16 matrices
+constexpr int DST = 17;                       // fp32 16 x 16 diagonal blocks
 
 __device__ __forceinline__ float4v mfma32(half8 a, half8 b, float4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -94,6 +93,21 @@ __device__ __forceinline__ half8 to_half8(uint4 u, f16_t) { return __builtin_bit
 
 __device__ __forceinline__ int frag_index(int R, int kk) { return R < 2 ? R : 2 * R - 2 + kk; }
 
+// One row of a row-major fp16 matrix at the columns kset(g4, kk).
+__device__ __forceinline__ half8 perm_row(const _Float16 *M, int st, int row, int kk, int g4) {
+  const _Float16 *p = M + row * st + 32 * kk + 4 * g4;
+  const half4 lo = *reinterpret_cast<const half4 *>(p);
+  const half4 hi = *reinterpret_cast<const half4 *>(p + 16);
+  return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Two accumulator tiles (rows 16 (2 kk) + 4 g4 + ii and 16 (2 kk + 1) + 4 g4 + ii)
+// packed as one fragment in kset order.
+__device__ __forceinline__ half8 pack_pair(float4v a, float4v b) {
+  return half8{(_Float16)a[0], (_Float16)a[1], (_Float16)a[2], (_Float16)a[3],
+               (_Float16)b[0], (_Float16)b[1], (_Float16)b[2], (_Float16)b[3]};
+}
+
 // Inclusive prefix of the chunk's log decay (wave 0: lane = token) and the
 // per-token scalars: gamma, Gamma = e^gamma, beta, beta Gamma, e^{gamma_n - gamma}.
 __device__ __forceinline__ void chunk_scalars(float g, float beta, float *sc, int lane) {
@@ -113,22 +127,26 @@ __device__ __forceinline__ void chunk_scalars(float g, float beta, float *sc, in
 }
 
 // ============================================================================
-// chunk_prep: T = (I + A)^{-1} per (chunk, value head)
+// chunk_prep: P0 per (chunk, key head), T = (I + A)^{-1} per (chunk, value head)
 // ============================================================================
 constexpr int P_OFF_K = 0;                              // [C][KST] fp16
-constexpr int P_OFF_T = P_OFF_K + C * KST * 2;          // [C][CST] fp16
-constexpr int P_OFF_AO = P_OFF_T + C * CST * 2;         // [C][CST] fp16
+constexpr int P_OFF_Q = P_OFF_K + C * KST * 2;          // [C][KST] fp16
+constexpr int P_OFF_T = P_OFF_Q + C * KST * 2;          // [C][CST] fp16
+constexpr int P_OFF_P = P_OFF_T + C * CST * 2;          // [C][CST] fp16
+constexpr int P_OFF_AO = P_OFF_P + C * CST * 2;         // [C][CST] fp16
 constexpr int P_OFF_AD = P_OFF_AO + C * CST * 2;        // [4][16][DST] fp32
 constexpr int P_OFF_SC = P_OFF_AD + 4 * 16 * DST * 4;   // 5 x [C] fp32
 constexpr int P_SMEM = P_OFF_SC + 5 * C * 4;
 
 template <typename TQ, typename TG>
 __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
-    const TQ *__restrict__ k, const TG *__restrict__ g, const TG *__restrict__ beta,
-    uint4 *__restrict__ Tws, int T, int Hk, int Hv, int nchunks) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[P_SMEM];
+    const TQ *__restrict__ q, const TQ *__restrict__ k, const TG *__restrict__ g,
+    const TG *__restrict__ beta, uint4 *__restrict__ Tws, int T, int Hk, int Hv, int nchunks) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   _Float16 *sK = reinterpret_cast<_Float16 *>(smem + P_OFF_K);
+  _Float16 *sQ = reinterpret_cast<_Float16 *>(smem + P_OFF_Q);
   _Float16 *sT = reinterpret_cast<_Float16 *>(smem + P_OFF_T);
+  _Float16 *sP = reinterpret_cast<_Float16 *>(smem + P_OFF_P);
   _Float16 *sAo = reinterpret_cast<_Float16 *>(smem + P_OFF_AO);
   float *sAd = reinterpret_cast<float *>(smem + P_OFF_AD);
   float *sc = reinterpret_cast<float *>(smem + P_OFF_SC);
@@ -143,45 +161,80 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
   const int t0 = c * C, n = min(C, T - t0);
   const size_t bt0 = (size_t)b * T + t0;
 
-  // K tile (fp16)
+  // K and Q tiles (fp16), rows past the end zero
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int row = (tid >> 4) + 16 * it;
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (row < n) u = *reinterpret_cast<const uint4 *>(k + ((bt0 + row) * Hk + kh) * DK + (tid & 15) * 8);
-    *reinterpret_cast<half8 *>(sK + row * KST + (tid & 15) * 8) = to_half8(u, TQ{});
+    const size_t off = ((bt0 + min(row, n - 1)) * Hk + kh) * DK + (tid & 15) * 8;
+    const uint4 uk = *reinterpret_cast<const uint4 *>(k + off);
+    const uint4 uq = *reinterpret_cast<const uint4 *>(q + off);
+    const half8 hz = {};
+    *reinterpret_cast<half8 *>(sK + row * KST + (tid & 15) * 8) = row < n ? to_half8(uk, TQ{}) : hz;
+    *reinterpret_cast<half8 *>(sQ + row * KST + (tid & 15) * 8) = row < n ? to_half8(uq, TQ{}) : hz;
   }
   lds_barrier();
 
-  // G row w, tiles (w, w - d)
-  float4v accG[4];
+  // G row w (tiles (w, w - d)) and P0 row Rp = 3 - w (tiles (Rp, Rp - d))
+  const int Rp = 3 - w;
+  float4v accG[4], accP[4];
   {
     const _Float16 *kw = sK + (16 * w + ln) * KST + 8 * g4;
-    half8 ak[4];
+    const _Float16 *kp = sK + (16 * Rp + ln) * KST + 8 * g4;
+    half8 ak[4], ap[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) ak[kk] = *reinterpret_cast<const half8 *>(kw + 32 * kk);
+    for (int kk = 0; kk < 4; ++kk) {
+      ak[kk] = *reinterpret_cast<const half8 *>(kw + 32 * kk);
+      ap[kk] = *reinterpret_cast<const half8 *>(sQ + (16 * Rp + ln) * KST + 32 * kk + 8 * g4);
+    }
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      float4v ag = {0.f, 0.f, 0.f, 0.f};
+      float4v ag = {0.f, 0.f, 0.f, 0.f}, apv = {0.f, 0.f, 0.f, 0.f};
       if (d <= w) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           ag = mfma32(ak[kk], *reinterpret_cast<const half8 *>(kw - 16 * d * KST + 32 * kk), ag);
       }
+      if (d <= Rp) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          apv = mfma32(ap[kk], *reinterpret_cast<const half8 *>(kp - 16 * d * KST + 32 * kk), apv);
+      }
       accG[d] = ag;
+      accP[d] = apv;
     }
   }
-
   for (int hv = 0; hv < grp; ++hv) {
     const int h = kh * grp + hv;
-    lds_barrier();  // previous head's T fully written out
+    lds_barrier();  // the previous head's T has been read out
     if (tid < C) {
+      const int row = min(tid, n - 1);
       const bool ok = tid < n;
-      const float gv = ok ? to_f32(g[(bt0 + tid) * Hv + h]) : 0.f;
-      const float bv = ok ? to_f32(beta[(bt0 + tid) * Hv + h]) : 0.f;
+      const float gv = ok ? to_f32(g[(bt0 + row) * Hv + h]) : 0.f;
+      const float bv = ok ? to_f32(beta[(bt0 + row) * Hv + h]) : 0.f;
       chunk_scalars(gv, bv, sc, tid);
     }
     lds_barrier();
+    // P = L o P0 for this head (lower incl. diagonal), fp16; the two upper
+    // blocks the fragments read are zero
+    {
+      const int r0 = 16 * Rp + 4 * g4;
+      _Float16 *pp = sP + r0 * CST + 16 * Rp + ln;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        if (d <= Rp) {
+          const float gs = sGam[16 * (Rp - d) + ln];
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const bool keep = d > 0 || ln <= 4 * g4 + ii;
+            pp[ii * CST - 16 * d] =
+                (_Float16)(keep ? __expf(sGam[r0 + ii] - gs) * accP[d][ii] : 0.f);
+          }
+        }
+      }
+      const int rr = tid >> 4, cc = tid & 15;
+      sP[rr * CST + 16 + cc] = (_Float16)0.f;
+      sP[(32 + rr) * CST + 48 + cc] = (_Float16)0.f;
+    }
     // A: diagonal blocks fp32 (strictly lower), off-diagonal blocks fp16
     {
       const int r0 = 16 * w + 4 * g4;
@@ -209,7 +262,6 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
           }
         }
       }
-      // the upper blocks inside the fragments are zero
       const int rr = tid >> 4, cc = tid & 15;
       sT[rr * CST + 16 + cc] = (_Float16)0.f;
       sT[(32 + rr) * CST + 48 + cc] = (_Float16)0.f;
@@ -271,16 +323,16 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
       }
     }
     lds_barrier();
-    // T as A-operand fragments: wave w writes row block w
     {
-      uint4 *dst = Tws + (((size_t)b * Hv + h) * nchunks + c) * (NFRAG * 64);
+      // T then P for (b, h, chunk): 2 x NFRAG fragments
+      uint4 *dst = Tws + (((size_t)b * Hv + h) * nchunks + c) * (2 * NFRAG * 64);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+      for (int kk = 0; kk < 2; ++kk)
         if (kk == 0 || w >= 2) {
-          const uint4 fr = *reinterpret_cast<const uint4 *>(sT + (16 * w + ln) * CST + 32 * kk + 8 * g4);
-          dst[frag_index(w, kk) * 64 + l] = fr;
+          dst[frag_index(w, kk) * 64 + l] = __builtin_bit_cast(uint4, perm_row(sT, CST, 16 * w + ln, kk, g4));
+          dst[(NFRAG + frag_index(w, kk)) * 64 + l] =
+              __builtin_bit_cast(uint4, perm_row(sP, CST, 16 * w + ln, kk, g4));
         }
-      }
     }
   }
 }
@@ -288,98 +340,43 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
 // ============================================================================
 // chunk_seq: the sequential pass over the chunks of one sequence
 // ============================================================================
-constexpr int S_OFF_K = 0;                              // [C][KST] fp16
-constexpr int S_OFF_S = S_OFF_K + C * KST * 2;          // [DVS][KST] fp16
-constexpr int S_OFF_V = S_OFF_S + DVS * KST * 2;        // [C][VST] fp16
-constexpr int S_OFF_XT = S_OFF_V + C * VST * 2;         // [DVS][CST] fp16
-constexpr int S_OFF_NT = S_OFF_XT + DVS * CST * 2;      // [DVS][CST] fp16
-constexpr int S_OFF_ND = S_OFF_NT + DVS * CST * 2;      // [DVS][CST] fp16
-constexpr int S_OFF_SC = S_OFF_ND + DVS * CST * 2;      // 5 x [C] fp32
-constexpr int S_SMEM = S_OFF_SC + 5 * C * 4;
-static_assert(S_SMEM <= 64 * 1024, "static LDS");
-
-// The next chunk's raw loads.  Every load is unconditional (rows past the end
-// of the sequence re-read its last row) and nothing is converted here, so no
-// instruction needs the data before the chunk is committed: the loads stay in
-// flight through the current chunk's work.
-template <typename TQ, typename TG>
-struct SeqFetch {
-  uint4 k[4], q[4], v, t0, t1;
-  TG g, beta;
-  int n;  // valid rows of the fetched chunk
+template <int NW>
+struct SeqCfg {
+  static constexpr int THREADS = 64 * NW;      // NW waves, 16 value rows of the state each
+  static constexpr int WGC = 16 * NW;          // value rows per workgroup
+  static constexpr int NS = DV / WGC;          // workgroups per (batch, value head)
+  static constexpr int VST = WGC + 8;          // sV row stride
+  static constexpr int NKQ = (C * DK / 8) / THREADS;     // 16-byte K (and Q) pieces per thread
+  static constexpr int NV = (C * WGC / 8) / THREADS;     // 16-byte V pieces per thread
+  static constexpr int NTP = (2 * NFRAG * 64 + THREADS - 1) / THREADS;  // T and P fragment pieces
+  static constexpr int OFF_K = 0;                          // 2 x [C][KST] fp16
+  static constexpr int OFF_Q = OFF_K + 2 * C * KST * 2;    // 2 x [C][KST] fp16
+  static constexpr int OFF_V = OFF_Q + 2 * C * KST * 2;    // 2 x [C][VST] fp16
+  static constexpr int OFF_TP = OFF_V + 2 * C * VST * 2;   // 2 x [2 NFRAG][64] x 16 B
+  static constexpr int OFF_SC = OFF_TP + 2 * 2 * NFRAG * 64 * 16;   // 2 x 5 x [C] fp32
+  static constexpr int SMEM = OFF_SC + 2 * 5 * C * 4;
+  static_assert(SMEM <= 160 * 1024, "LDS");
 };
 
-template <typename TQ, typename TG>
-__device__ __forceinline__ void seq_fetch(SeqFetch<TQ, TG> &f, const TQ *__restrict__ q,
-                                          const TQ *__restrict__ k, const TQ *__restrict__ v,
-                                          const TG *__restrict__ g, const TG *__restrict__ beta,
-                                          const uint4 *__restrict__ Tc, int tid, int w, int l,
-                                          size_t bt0, int n, int Hk, int Hv, int kh, int h, int i0) {
-  f.n = n;
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int row = min((tid >> 4) + 16 * it, n - 1);
-    f.k[it] = *reinterpret_cast<const uint4 *>(k + ((bt0 + row) * Hk + kh) * DK + (tid & 15) * 8);
-  }
-  {
-    // Q fragments of row block w: lane (g4, ln) -> Q[16 w + ln][32 kk + 8 g4 ..]
-    const int row = min(16 * w + (l & 15), n - 1);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      f.q[kk] = *reinterpret_cast<const uint4 *>(q + ((bt0 + row) * Hk + kh) * DK + 32 * kk + 8 * (l >> 4));
-  }
-  {
-    const int row = min(tid >> 2, n - 1);
-    f.v = *reinterpret_cast<const uint4 *>(v + ((bt0 + row) * Hv + h) * DV + i0 + (tid & 3) * 8);
-  }
-  f.t0 = Tc[frag_index(w, 0) * 64 + l];
-  f.t1 = Tc[frag_index(w, w >= 2 ? 1 : 0) * 64 + l];
-  const int row = min(tid & 63, n - 1);
-  f.g = g[(bt0 + row) * Hv + h];
-  f.beta = beta[(bt0 + row) * Hv + h];
-}
+// The next chunk's raw loads.  Nothing is converted here, so no instruction
+// needs the data before the chunk is committed.
+template <typename TQ, typename TG, int NW>
+struct SeqFetch {
+  uint4 k[SeqCfg<NW>::NKQ], q[SeqCfg<NW>::NKQ], v[SeqCfg<NW>::NV], tp[SeqCfg<NW>::NTP];
+  TG g, beta;
+  int n;
+};
 
-// Land a fetched chunk: K and V tiles into LDS (rows past the end as zeros),
-// Q and T fragments into registers, the per-token scalars into LDS.
-template <typename TQ, typename TG>
-__device__ __forceinline__ void seq_commit(const SeqFetch<TQ, TG> &f, _Float16 *sK, _Float16 *sV,
-                                           float *sc, half8 (&qf)[4], half8 (&tf)[2], int tid,
-                                           int w, int l) {
-  const int c8 = (tid & 15) * 8;
-  const half8 hz = {};
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int row = (tid >> 4) + 16 * it;
-    *reinterpret_cast<half8 *>(sK + row * KST + c8) = row < f.n ? to_half8(f.k[it], TQ{}) : hz;
-  }
-  *reinterpret_cast<half8 *>(sV + (tid >> 2) * VST + (tid & 3) * 8) =
-      (tid >> 2) < f.n ? to_half8(f.v, TQ{}) : hz;
-  const bool qok = 16 * w + (l & 15) < f.n;
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) qf[kk] = qok ? to_half8(f.q[kk], TQ{}) : hz;
-  tf[0] = __builtin_bit_cast(half8, f.t0);
-  tf[1] = __builtin_bit_cast(half8, f.t1);
-  if (tid < C) {
-    const bool ok = tid < f.n;
-    chunk_scalars(ok ? to_f32(f.g) : 0.f, ok ? to_f32(f.beta) : 0.f, sc, tid);
-  }
-}
-
-template <typename TQ, typename TG>
-__global__ __launch_bounds__(kThreads, 2) void chunk_seq_kernel(
+template <typename TQ, typename TG, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *__restrict__ v,
-    const TG *__restrict__ g, const TG *__restrict__ beta, const uint4 *__restrict__ Tws,
+    const TG *__restrict__ g, const TG *__restrict__ beta, const uint4 *__restrict__ TPws,
     const float *__restrict__ S0, float *__restrict__ o, float *__restrict__ ST, int T, int Hk,
     int Hv, int ntasks, int nchunks) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[S_SMEM];
-  _Float16 *sK = reinterpret_cast<_Float16 *>(smem + S_OFF_K);
-  _Float16 *sS = reinterpret_cast<_Float16 *>(smem + S_OFF_S);
-  _Float16 *sV = reinterpret_cast<_Float16 *>(smem + S_OFF_V);
-  _Float16 *sXt = reinterpret_cast<_Float16 *>(smem + S_OFF_XT);
-  _Float16 *sNt = reinterpret_cast<_Float16 *>(smem + S_OFF_NT);
-  _Float16 *sNd = reinterpret_cast<_Float16 *>(smem + S_OFF_ND);
-  float *sc = reinterpret_cast<float *>(smem + S_OFF_SC);
-  const float *sGam = sc, *sEg = sc + C, *sB = sc + 2 * C, *sBG = sc + 3 * C, *sDec = sc + 4 * C;
+  using Cfg = SeqCfg<NW>;
+  constexpr int THREADS = Cfg::THREADS, WGC = Cfg::WGC, NS = Cfg::NS, VST = Cfg::VST;
+  constexpr int NKQ = Cfg::NKQ, NV = Cfg::NV, NTP = Cfg::NTP;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   // blocks go round-robin over the 8 XCDs: give each XCD a contiguous task range
   const int bid = blockIdx.x;
@@ -390,216 +387,272 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seq_kernel(
   const int bh = task / NS;  // b * Hv + h
   const int h = bh % Hv, b = bh / Hv;
   const int kh = h / (Hv / Hk);
-  const int i0 = slice * DVS;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, g4 = l >> 4, ln = l & 15;
-  const size_t bT = (size_t)b * T;
-  const uint4 *Tbh = Tws + (size_t)bh * nchunks * (NFRAG * 64);
+  const int ic = w * 16;                  // this wave's first value row within the workgroup
+  const int iw0 = slice * WGC + ic;       // ... within the head
 
-  // entering state: tiles (I, J = 2 w + jj), lane holds S[16 I + 4 g4 + ii][16 J + ln]
-  float4v accS[2][NI];
+  // Per-sequence bases (uniform) and per-thread offsets (fixed for all chunks).
+  const int kq_rs = Hk * DK, v_rs = Hv * DV;        // row strides of q/k and v (elements)
+  const TQ *kb = k + ((size_t)b * T * Hk + kh) * DK;
+  const TQ *qb = q + ((size_t)b * T * Hk + kh) * DK;
+  const TQ *vb = v + ((size_t)b * T * Hv + h) * DV + slice * WGC;
+  const TG *gb = g + (size_t)b * T * Hv + h;
+  const TG *betab = beta + (size_t)b * T * Hv + h;
+  float *ob = o + ((size_t)b * T * Hv + h) * DV + iw0 + 4 * g4;
+  const uint4 *TPbh = TPws + (size_t)bh * nchunks * (2 * NFRAG * 64);
+  int kq_off[NKQ], v_off[NV];
 #pragma unroll
-  for (int jj = 0; jj < 2; ++jj)
+  for (int it = 0; it < NKQ; ++it) {
+    const int e = tid + THREADS * it;
+    kq_off[it] = (e >> 4) * kq_rs + (e & 15) * 8;
+  }
 #pragma unroll
-    for (int I = 0; I < NI; ++I) {
-      const int j = 16 * (2 * w + jj) + ln;
+  for (int it = 0; it < NV; ++it) {
+    const int e = tid + THREADS * it;
+    v_off[it] = (e / (WGC / 8)) * v_rs + (e % (WGC / 8)) * 8;
+  }
+
+  _Float16 *const sKb = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_K);
+  _Float16 *const sQb = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_Q);
+  _Float16 *const sVb = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_V);
+  uint4 *const sTPb = reinterpret_cast<uint4 *>(smem + Cfg::OFF_TP);
+  float *const sScb = reinterpret_cast<float *>(smem + Cfg::OFF_SC);
+
+  // state: tiles J of S^T, lane holds S[iw0 + ln][16 J + 4 g4 + ii]
+  float4v accS[8];
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int il = 16 * I + 4 * g4 + ii;
-        const float s = S0 ? S0[((size_t)bh * DV + i0 + il) * DK + j] : 0.f;
-        accS[jj][I][ii] = s;
-        sS[il * KST + j] = (_Float16)s;
+  for (int J = 0; J < 8; ++J) {
+    float4v s = {0.f, 0.f, 0.f, 0.f};
+    if (S0) {
+      const float4 t4 =
+          *reinterpret_cast<const float4 *>(S0 + ((size_t)bh * DV + iw0 + ln) * DK + 16 * J + 4 * g4);
+      s[0] = t4.x; s[1] = t4.y; s[2] = t4.z; s[3] = t4.w;
+    }
+    accS[J] = s;
+  }
+
+  SeqFetch<TQ, TG, NW> f;
+  auto fetch = [&](int c) {
+    const int n = min(C, T - c * C);
+    f.n = n;
+    const size_t t0 = (size_t)c * C;
+    const TQ *kc = kb + t0 * kq_rs, *qc = qb + t0 * kq_rs, *vc = vb + t0 * v_rs;
+    if (n == C) {
+#pragma unroll
+      for (int it = 0; it < NKQ; ++it) {
+        f.k[it] = *reinterpret_cast<const uint4 *>(kc + kq_off[it]);
+        f.q[it] = *reinterpret_cast<const uint4 *>(qc + kq_off[it]);
+      }
+#pragma unroll
+      for (int it = 0; it < NV; ++it) f.v[it] = *reinterpret_cast<const uint4 *>(vc + v_off[it]);
+    } else {
+      // last chunk: rows past the end of the sequence re-read its last row
+#pragma unroll
+      for (int it = 0; it < NKQ; ++it) {
+        const int e = tid + THREADS * it;
+        const int off = min(e >> 4, n - 1) * kq_rs + (e & 15) * 8;
+        f.k[it] = *reinterpret_cast<const uint4 *>(kc + off);
+        f.q[it] = *reinterpret_cast<const uint4 *>(qc + off);
+      }
+#pragma unroll
+      for (int it = 0; it < NV; ++it) {
+        const int e = tid + THREADS * it;
+        f.v[it] = *reinterpret_cast<const uint4 *>(vc + min(e / (WGC / 8), n - 1) * v_rs +
+                                                   (e % (WGC / 8)) * 8);
       }
     }
+    const uint4 *tpc = TPbh + (size_t)c * (2 * NFRAG * 64);
+#pragma unroll
+    for (int it = 0; it < NTP; ++it) f.tp[it] = tpc[min(tid + THREADS * it, 2 * NFRAG * 64 - 1)];
+    const int row = min(tid & 63, n - 1);
+    f.g = gb[(t0 + row) * Hv];
+    f.beta = betab[(t0 + row) * Hv];
+  };
+  auto commit = [&](int buf) {
+    const half8 hz = {};
+    _Float16 *k_ = sKb + buf * C * KST, *q_ = sQb + buf * C * KST, *v_ = sVb + buf * C * VST;
+    const bool full = f.n == C;
+#pragma unroll
+    for (int it = 0; it < NKQ; ++it) {
+      const int e = tid + THREADS * it;
+      const int row = e >> 4;
+      const bool ok = full || row < f.n;
+      *reinterpret_cast<half8 *>(k_ + row * KST + (e & 15) * 8) = ok ? to_half8(f.k[it], TQ{}) : hz;
+      *reinterpret_cast<half8 *>(q_ + row * KST + (e & 15) * 8) = ok ? to_half8(f.q[it], TQ{}) : hz;
+    }
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+      const int e = tid + THREADS * it;
+      const int row = e / (WGC / 8);
+      *reinterpret_cast<half8 *>(v_ + row * VST + (e % (WGC / 8)) * 8) =
+          full || row < f.n ? to_half8(f.v[it], TQ{}) : hz;
+    }
+#pragma unroll
+    for (int it = 0; it < NTP; ++it) {
+      const int e = tid + THREADS * it;
+      if (e < 2 * NFRAG * 64) sTPb[buf * 2 * NFRAG * 64 + e] = f.tp[it];
+    }
+    if (tid < C) {
+      const bool ok = tid < f.n;
+      chunk_scalars(ok ? to_f32(f.g) : 0.f, ok ? to_f32(f.beta) : 0.f, sScb + buf * 5 * C, tid);
+    }
+  };
 
-  SeqFetch<TQ, TG> f;
-  half8 qf[4];
-  half8 tf[2];
-  seq_fetch(f, q, k, v, g, beta, Tbh, tid, w, l, bT, min(C, T), Hk, Hv, kh, h, i0);
-  seq_commit(f, sK, sV, sc, qf, tf, tid, w, l);
+  fetch(0);
+  commit(0);
   lds_barrier();
 
   for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
     const int t0 = c * C;
-    if (c + 1 < nchunks)
-      seq_fetch(f, q, k, v, g, beta, Tbh + (size_t)(c + 1) * (NFRAG * 64), tid, w, l, bT + t0 + C,
-                min(C, T - t0 - C), Hk, Hv, kh, h, i0);
+    const _Float16 *cK = sKb + buf * C * KST, *cQ = sQb + buf * C * KST, *cV = sVb + buf * C * VST;
+    const uint4 *cT = sTPb + buf * 2 * NFRAG * 64, *cP = cT + NFRAG * 64;
+    const float *sc = sScb + buf * 5 * C;
+    if (c + 1 < nchunks) fetch(c + 1);
 
-    // ================= phase 1
-    float4v accDK[NI], accO[NI], accPt[4];
-    {
-      const _Float16 *kw = sK + (16 * w + ln) * KST + 8 * g4;
-      half8 ak[4];
+    // S fragments (fp16) in kset order over the key channels
+    half8 sf[4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) ak[kk] = *reinterpret_cast<const half8 *>(kw + 32 * kk);
+    for (int kk = 0; kk < 4; ++kk) sf[kk] = pack_pair(accS[2 * kk], accS[2 * kk + 1]);
+
+    // K S^T (rows r = 16 R + 4 g4 + ii, value row ln) and S Q^T (transposed read)
+    float4v accX[4], accO[4];
 #pragma unroll
-      for (int I = 0; I < NI; ++I) {
-        float4v dk_ = {0.f, 0.f, 0.f, 0.f}, so_ = {0.f, 0.f, 0.f, 0.f};
-        const _Float16 *srow = sS + (16 * I + ln) * KST + 8 * g4;
+    for (int R = 0; R < 4; ++R) {
+      half8 kf[4], qf[4];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const half8 s8 = *reinterpret_cast<const half8 *>(srow + 32 * kk);
-          dk_ = mfma32(ak[kk], s8, dk_);   // (K S^T)[16 w + 4 g4 + ii][16 I + ln]
-          so_ = mfma32(s8, qf[kk], so_);   // (S Q^T)[16 I + 4 g4 + ii][16 w + ln]
-        }
-        accDK[I] = dk_;
-        accO[I] = so_;
+      for (int kk = 0; kk < 4; ++kk) {
+        kf[kk] = perm_row(cK, KST, 16 * R + ln, kk, g4);
+        qf[kk] = perm_row(cQ, KST, 16 * R + ln, kk, g4);
       }
-      // (Q K^T)^T tiles (S', w) for S' <= w: lane holds P0[16 w + ln][16 S' + 4 g4 + ii]
+      float4v ax = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int Sp = 0; Sp < 4; ++Sp) {
-        float4v acc = {0.f, 0.f, 0.f, 0.f};
-        if (Sp <= w) {
-          const _Float16 *krow = sK + (16 * Sp + ln) * KST + 8 * g4;
+      for (int kk = 0; kk < 4; ++kk) {
+        ax = mfma32(kf[kk], sf[kk], ax);
+        ao = mfma32(sf[kk], qf[kk], ao);
+      }
+      accX[R] = ax;
+      accO[R] = ao;
+    }
+
+    // X = beta V - beta Gamma (K S^T), as fragments over the chunk rows
+    half8 xf[2];
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
-            acc = mfma32(*reinterpret_cast<const half8 *>(krow + 32 * kk), qf[kk], acc);
-        }
-        accPt[Sp] = acc;
+    for (int R = 0; R < 4; ++R) {
+      const int r0 = 16 * R + 4 * g4;
+      const float4 bb = *reinterpret_cast<const float4 *>(sc + 2 * C + r0);
+      const float4 bg = *reinterpret_cast<const float4 *>(sc + 3 * C + r0);
+      const float bv[4] = {bb.x, bb.y, bb.z, bb.w}, gv[4] = {bg.x, bg.y, bg.z, bg.w};
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        xf[R >> 1][(R & 1) * 4 + ii] =
+            (_Float16)(bv[ii] * (float)cV[(r0 + ii) * VST + ic + ln] - gv[ii] * accX[R][ii]);
+    }
+
+    // N = T X;  N and diag(e^{gamma_n - gamma}) N as fragments over the chunk rows
+    half8 nf[2], ndf[2];
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+      float4v acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma32(__builtin_bit_cast(half8, cT[frag_index(R, 0) * 64 + l]), xf[0], acc);
+      if (R >= 2) acc = mfma32(__builtin_bit_cast(half8, cT[frag_index(R, 1) * 64 + l]), xf[1], acc);
+      const float4 dd = *reinterpret_cast<const float4 *>(sc + 4 * C + 16 * R + 4 * g4);
+      const float dv4[4] = {dd.x, dd.y, dd.z, dd.w};
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        nf[R >> 1][(R & 1) * 4 + ii] = (_Float16)acc[ii];
+        ndf[R >> 1][(R & 1) * 4 + ii] = (_Float16)(acc[ii] * dv4[ii]);
       }
     }
 
-    // ================= epilogue 1: X^T to LDS, O scaled, P in registers
-    half8 pf[2];
-    {
-      const int r0 = 16 * w + 4 * g4;
+    // O^T = Gamma (S Q^T) + N^T P^T:  row r = 16 R + ln of this lane
 #pragma unroll
-      for (int I = 0; I < NI; ++I) {
-        const int il = 16 * I + ln;
-        half4 xv;
+    for (int R = 0; R < 4; ++R) {
+      const int r = 16 * R + ln;
+      const float er = sc[C + r];
+      float4v acc = accO[R];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int r = r0 + ii;
-          xv[ii] = (_Float16)(sB[r] * (float)sV[r * VST + il] - sBG[r] * accDK[I][ii]);
-        }
-        *reinterpret_cast<half4 *>(sXt + il * CST + r0) = xv;
-      }
-      const int rq = 16 * w + ln;        // this lane's token in the read
-      const float gq = sGam[rq], eq = sEg[rq];
-#pragma unroll
-      for (int I = 0; I < NI; ++I)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) accO[I][ii] *= eq;
-#pragma unroll
-      for (int Sp = 0; Sp < 4; ++Sp) {
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int s = 16 * Sp + 4 * g4 + ii;
-          const bool keep = s <= rq;
-          const float p = keep ? __expf(gq - sGam[s]) * accPt[Sp][ii] : 0.f;
-          pf[Sp >> 1][(Sp & 1) * 4 + ii] = (_Float16)p;
-        }
-      }
+      for (int ii = 0; ii < 4; ++ii) acc[ii] *= er;
+      acc = mfma32(nf[0], __builtin_bit_cast(half8, cP[frag_index(R, 0) * 64 + l]), acc);
+      if (R >= 2) acc = mfma32(nf[1], __builtin_bit_cast(half8, cP[frag_index(R, 1) * 64 + l]), acc);
+      if (t0 + r < T)
+        *reinterpret_cast<float4 *>(ob + (size_t)(t0 + r) * v_rs) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
-    lds_barrier();
 
-    // ================= phase 2: N = T X (rows 16 w ..)
+    // S^T <- Gamma_n S^T + K^T N~  (K columns 16 J + ln at the chunk rows kset)
     {
-      const int r0 = 16 * w + 4 * g4;
+      const float gC = sc[C + C - 1];
+      const _Float16 *kcol = cK + (4 * g4) * KST + ln;
 #pragma unroll
-      for (int I = 0; I < NI; ++I) {
-        float4v acc = {0.f, 0.f, 0.f, 0.f};
-        const _Float16 *xrow = sXt + (16 * I + ln) * CST + 8 * g4;
-        acc = mfma32(tf[0], *reinterpret_cast<const half8 *>(xrow), acc);
-        if (w >= 2) acc = mfma32(tf[1], *reinterpret_cast<const half8 *>(xrow + 32), acc);
-        const int il = 16 * I + ln;
-        half4 nv, nd;
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          nv[ii] = (_Float16)acc[ii];
-          nd[ii] = (_Float16)(acc[ii] * sDec[r0 + ii]);
-        }
-        *reinterpret_cast<half4 *>(sNt + il * CST + r0) = nv;
-        *reinterpret_cast<half4 *>(sNd + il * CST + r0) = nd;
-      }
-    }
-    lds_barrier();
-
-    // ================= phase 3: O^T += N^T P^T -> HBM; state update
-    {
-      const int rq = t0 + 16 * w + ln;
-#pragma unroll
-      for (int I = 0; I < NI; ++I) {
-        const _Float16 *nrow = sNt + (16 * I + ln) * CST + 4 * g4;
-        float4v acc = accO[I];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          if (kk == 0 || w >= 2) {
-            const half4 lo = *reinterpret_cast<const half4 *>(nrow + 32 * kk);
-            const half4 hi = *reinterpret_cast<const half4 *>(nrow + 32 * kk + 16);
-            const half8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            acc = mfma32(a, pf[kk], acc);
-          }
-        }
-        if (rq < T)
-          *reinterpret_cast<float4 *>(o + ((bT + rq) * Hv + h) * DV + i0 + 16 * I + 4 * g4) =
-              make_float4(acc[0], acc[1], acc[2], acc[3]);
-      }
-      const float gC = sEg[C - 1];
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int J = 2 * w + jj;
-        half8 kc[2];  // K[32 kk + 8 g4 + j][16 J + ln]
+      for (int J = 0; J < 8; ++J) {
+        half8 kc[2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) kc[kk][j] = sK[(32 * kk + 8 * g4 + j) * KST + 16 * J + ln];
+          for (int e = 0; e < 8; ++e)
+            kc[kk][e] = kcol[(32 * kk + (e >> 2) * 16 + (e & 3)) * KST + 16 * J];
+        float4v acc = accS[J];
 #pragma unroll
-        for (int I = 0; I < NI; ++I) {
-          float4v acc = accS[jj][I];
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) acc[ii] *= gC;
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk)
-            acc = mfma32(*reinterpret_cast<const half8 *>(sNd + (16 * I + ln) * CST + 32 * kk + 8 * g4),
-                         kc[kk], acc);
-          accS[jj][I] = acc;
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) sS[(16 * I + 4 * g4 + ii) * KST + 16 * J + ln] = (_Float16)acc[ii];
-        }
+        for (int ii = 0; ii < 4; ++ii) acc[ii] *= gC;
+        acc = mfma32(kc[0], ndf[0], acc);
+        acc = mfma32(kc[1], ndf[1], acc);
+        accS[J] = acc;
       }
     }
+
+    if (c + 1 < nchunks) commit(buf ^ 1);
     lds_barrier();
-    if (c + 1 < nchunks) {
-      seq_commit(f, sK, sV, sc, qf, tf, tid, w, l);
-      lds_barrier();
-    }
   }
 
   // final state
 #pragma unroll
-  for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-    for (int I = 0; I < NI; ++I) {
-      const int j = 16 * (2 * w + jj) + ln;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-        ST[((size_t)bh * DV + i0 + 16 * I + 4 * g4 + ii) * DK + j] = accS[jj][I][ii];
-    }
+  for (int J = 0; J < 8; ++J)
+    *reinterpret_cast<float4 *>(ST + ((size_t)bh * DV + iw0 + ln) * DK + 16 * J + 4 * g4) =
+        make_float4(accS[J][0], accS[J][1], accS[J][2], accS[J][3]);
+}
+
+template <typename TQ, typename TG, int NW>
+hipError_t launch_seq(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
+                      const void *beta, const uint4 *TPws, const float *S0, float *o, float *ST,
+                      int nchunks, hipStream_t st) {
+  using Cfg = SeqCfg<NW>;
+  auto kern = chunk_seq_kernel<TQ, TG, NW>;
+  hipError_t e =
+      hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::SMEM);
+  if (e != hipSuccess) return e;
+  const int ntasks = sh.B * sh.Hv * Cfg::NS;
+  hipLaunchKernelGGL(kern, dim3(ntasks), dim3(Cfg::THREADS), Cfg::SMEM, st, (const TQ *)q,
+                     (const TQ *)k, (const TQ *)v, (const TG *)g, (const TG *)beta, TPws, S0, o, ST,
+                     sh.T, sh.Hk, sh.Hv, ntasks, nchunks);
+  return hipGetLastError();
 }
 
 template <typename TQ, typename TG>
 hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
                     const void *beta, const float *S0, float *o, float *ST, void *ws, hipStream_t st) {
   const int nchunks = (sh.T + C - 1) / C;
-  hipLaunchKernelGGL((chunk_prep_kernel<TQ, TG>), dim3(nchunks, sh.B * sh.Hk), dim3(kThreads), 0, st,
-                     (const TQ *)k, (const TG *)g, (const TG *)beta, (uint4 *)ws, sh.T, sh.Hk, sh.Hv,
-                     nchunks);
-  hipError_t e = hipGetLastError();
+  uint4 *TPws = (uint4 *)ws;
+  auto prep = chunk_prep_kernel<TQ, TG>;
+  hipError_t e =
+      hipFuncSetAttribute((const void *)prep, hipFuncAttributeMaxDynamicSharedMemorySize, P_SMEM);
   if (e != hipSuccess) return e;
-  const int ntasks = sh.B * sh.Hv * NS;
-  hipLaunchKernelGGL((chunk_seq_kernel<TQ, TG>), dim3(ntasks), dim3(kThreads), 0, st, (const TQ *)q,
-                     (const TQ *)k, (const TQ *)v, (const TG *)g, (const TG *)beta,
-                     (const uint4 *)ws, S0, o, ST, sh.T, sh.Hk, sh.Hv, ntasks, nchunks);
-  return hipGetLastError();
+  hipLaunchKernelGGL(prep, dim3(nchunks, sh.B * sh.Hk), dim3(kThreads), P_SMEM, st, (const TQ *)q,
+                     (const TQ *)k, (const TG *)g, (const TG *)beta, TPws, sh.T, sh.Hk, sh.Hv, nchunks);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // One 8-wave workgroup per head (two waves per SIMD) when that fills the GPU,
+  // else two 4-wave workgroups per head for more parallel chains.
+  if ((long)sh.B * sh.Hv >= 160)
+    return launch_seq<TQ, TG, 8>(sh, q, k, v, g, beta, TPws, S0, o, ST, nchunks, st);
+  return launch_seq<TQ, TG, 4>(sh, q, k, v, g, beta, TPws, S0, o, ST, nchunks, st);
 }
 
 }  // namespace
 
 size_t chunk_mfma_workspace(const Shape &sh) {
   const size_t nchunks = (size_t)(sh.T + C - 1) / C;
-  return (size_t)sh.B * sh.Hv * nchunks * T_BYTES;
+  return (size_t)sh.B * sh.Hv * nchunks * 2 * FRAGS_BYTES;
 }
 
 hipError_t launch_chunk_mfma(const Shape &sh, const void *q, const void *k, const void *v,

@@ -109,8 +109,10 @@ gdn_status gdn_prologue(const gdn_desc *d, int32_t x_dtype, const void *xq,
 
 /*
  * Device workspace bytes gdn_fwd_chunked needs for `d` (0 = none; then the
- * workspace pointer may be NULL).  The matrix-core path keeps the per-chunk
- * triangular inverses there: 6144 bytes per (batch, value head, chunk).
+ * workspace pointer may be NULL).  The matrix-core path keeps two 64 x 64
+ * lower-triangular fp16 matrices per (batch, value head, 64-token chunk)
+ * there, the triangular inverse and the decayed masked q.k products:
+ * 12288 bytes each triple.
  * Returns 0 for an invalid description.  The caller owns the workspace; it
  * is scratch between calls and must not be shared by concurrent calls.
  */

@@ -107,9 +107,9 @@ def test_prologue_rejects(L):
 
 
 def test_workspace_query(L):
-    # matrix-core path: 6144 bytes per (batch, value head, 64-token chunk)
-    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc())) == 2 * 6 * 2 * 6144
-    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(T=1))) == 2 * 6 * 1 * 6144
+    # matrix-core path: 12288 bytes per (batch, value head, 64-token chunk)
+    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc())) == 2 * 6 * 2 * 12288
+    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(T=1))) == 2 * 6 * 1 * 12288
     assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(gate=gdn.GATE_KEY_CHANNEL))) == 0
     assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(qkv_dtype=gdn.F32, gate_dtype=gdn.F32, chunk=32))) == 0
     assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(Hv=5))) == 0       # invalid description
