@@ -147,16 +147,8 @@ gdn_status gdn_prologue(const gdn_desc *d, int32_t x_dtype, const void *xq, cons
   if (overlap(outs[0], outs[1]) || overlap(outs[0], outs[2]) || overlap(outs[1], outs[2]))
     return fail(GDN_E_ARG, "prologue outputs must not overlap each other");
 
-  hipStream_t s = (hipStream_t)stream;
-  const gdn::DType xt = (gdn::DType)x_dtype, yt = sh.qkv;
-  const size_t nw_q = (size_t)d->Hk * d->dk;
-  hipError_t e = gdn::launch_prologue(xq, xt, conv_w, q, yt, d->B, d->T, d->Hk, d->dk, true, eps, s);
-  if (e == hipSuccess)
-    e = gdn::launch_prologue(xk, xt, conv_w + 4 * nw_q, k, yt, d->B, d->T, d->Hk, d->dk, true, eps,
-                             s);
-  if (e == hipSuccess)
-    e = gdn::launch_prologue(xv, xt, conv_w + 8 * nw_q, v, yt, d->B, d->T, d->Hv, d->dv, false, eps,
-                             s);
+  hipError_t e = gdn::launch_prologue(xq, xk, xv, (gdn::DType)x_dtype, conv_w, q, k, v, sh.qkv, d->B,
+                                      d->T, d->Hk, d->Hv, d->dk, d->dv, eps, (hipStream_t)stream);
   return launched(e, "prologue launch");
 }
 

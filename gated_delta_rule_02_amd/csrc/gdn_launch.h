@@ -16,9 +16,11 @@ struct Shape {
   bool key_gate;
 };
 
-// Prologue: conv + SiLU (+ L2) over one tensor [B,T,H,d].
-hipError_t launch_prologue(const void *x, DType xt, const float *w, void *y, DType yt, int B, int T,
-                           int H, int d, bool l2, float eps, hipStream_t s);
+// Prologue: conv + SiLU over q, k, v (L2 over q and k rows); w holds the
+// conv taps of q, then k, then v channels.
+hipError_t launch_prologue(const void *xq, const void *xk, const void *xv, DType xt, const float *w,
+                           void *q, void *k, void *v, DType yt, int B, int T, int Hk, int Hv, int dk,
+                           int dv, float eps, hipStream_t s);
 
 // One decode step, state in place.
 hipError_t launch_decode(const Shape &sh, const void *q, const void *k, const void *v,

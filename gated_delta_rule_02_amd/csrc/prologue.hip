@@ -6,13 +6,12 @@
 //   y_t = w0 x_{t-3} + w1 x_{t-2} + w2 x_{t-1} + w3 x_t      (zero history)
 //   z_t = y_t sigmoid(y_t);   q, k rows: z / sqrt(sum z^2 + eps)
 //
-// HBM-bound: every input element is read once and every output written once.
-// A head row of d channels is held by d/8 lanes, 8 channels each, so one load
-// is 16 bytes (bf16) per lane and the lanes of a wave cover 64/(d/8) adjacent
-// heads of one token: contiguous memory.  Each wave walks a span of tokens,
-// keeping the last three inputs of its channels in registers (the 3-token
-// halo is re-read once per span), and issues the loads of kU tokens before
-// computing them.
+// HBM-bound: every input element is read once (plus a 3-token halo per span)
+// and every output written once.  One launch covers the q, k and v head rows
+// together: a head row of d channels is held by d/8 lanes, 8 channels each,
+// so one load is 16 bytes (bf16) per lane; each lane group walks a span of
+// kSpan tokens of its head row, keeping the last three inputs in registers,
+// and has the loads of kU tokens in flight before computing them.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -20,35 +19,54 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kSpan = 64;  // tokens per wave
-constexpr int kU = 4;      // tokens loaded ahead
+constexpr int kSpan = 32;  // tokens per lane group
+constexpr int kU = 8;      // tokens loaded ahead
 
-template <typename TX, typename TO, int D, bool L2>
-__global__ __launch_bounds__(kThreads) void prologue_kernel(const TX *__restrict__ x,
-                                                            const float *__restrict__ w,
-                                                            TO *__restrict__ y, int T, int H,
-                                                            float eps) {
-  constexpr int LPR = D / 8;               // lanes per head row
-  constexpr int HPB = kThreads / LPR;      // heads per block
-  const int nspan = (T + kSpan - 1) / kSpan;
-  const int b = blockIdx.x / nspan;
-  const int t0 = (blockIdx.x % nspan) * kSpan;
-  const int head = blockIdx.y * HPB + threadIdx.x / LPR;
-  if (head >= H) return;  // whole lane groups leave together
+struct ProTensor {
+  const void *x;
+  const float *w;  // [H*d][4]
+  void *y;
+  int H;
+  bool l2;
+};
+struct ProArgs {
+  ProTensor t[3];
+  int B, T;
+  float eps;
+};
+
+template <typename TX, typename TO, int D>
+__global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
+  constexpr int LPR = D / 8;                 // lanes per head row
+  constexpr int RPB = kThreads / LPR;        // head rows per block
+  const int nspan = (a.T + kSpan - 1) / kSpan;
+  // block -> (span, group of RPB rows of the concatenated q | k | v head list)
+  const int span = blockIdx.x % nspan;
+  const int bg = blockIdx.x / nspan;         // over B * ceil(rows / RPB)
+  const int nrows = a.t[0].H + a.t[1].H + a.t[2].H;
+  const int ngroups = (nrows + RPB - 1) / RPB;
+  const int b = bg / ngroups;
+  const int row = (bg % ngroups) * RPB + threadIdx.x / LPR;
+  if (row >= nrows) return;  // whole lane groups leave together
+  int ti = 0, head = row;
+  if (head >= a.t[0].H) { head -= a.t[0].H; ti = 1; }
+  if (ti == 1 && head >= a.t[1].H) { head -= a.t[1].H; ti = 2; }
+  const ProTensor P = ti == 0 ? a.t[0] : (ti == 1 ? a.t[1] : a.t[2]);
   const int c0 = (threadIdx.x % LPR) * 8;
+  const int t0 = span * kSpan;
 
   float w0[8], w1[8], w2[8], w3[8];
   {
-    const float4 *wp = reinterpret_cast<const float4 *>(w + ((size_t)head * D + c0) * 4);
+    const float4 *wp = reinterpret_cast<const float4 *>(P.w + ((size_t)head * D + c0) * 4);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const float4 t = wp[c];
       w0[c] = t.x; w1[c] = t.y; w2[c] = t.z; w3[c] = t.w;
     }
   }
-  const size_t tok_stride = (size_t)H * D;
-  const TX *xb = x + (size_t)b * T * tok_stride + (size_t)head * D + c0;
-  TO *yb = y + (size_t)b * T * tok_stride + (size_t)head * D + c0;
+  const size_t tok_stride = (size_t)P.H * D;
+  const TX *xb = reinterpret_cast<const TX *>(P.x) + (size_t)b * a.T * tok_stride + (size_t)head * D + c0;
+  TO *yb = reinterpret_cast<TO *>(P.y) + (size_t)b * a.T * tok_stride + (size_t)head * D + c0;
 
   float xm3[8], xm2[8], xm1[8];
 #pragma unroll
@@ -57,18 +75,11 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(const TX *__restrict
   if (t0 >= 2) load8(xb + (size_t)(t0 - 2) * tok_stride, xm2);
   if (t0 >= 1) load8(xb + (size_t)(t0 - 1) * tok_stride, xm1);
 
-  const int t_end = min(T, t0 + kSpan);
+  const int t_end = min(a.T, t0 + kSpan);
   for (int t = t0; t < t_end; t += kU) {
     float xs[kU][8];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      if (t + u < t_end) {
-        load8(xb + (size_t)(t + u) * tok_stride, xs[u]);
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) xs[u][c] = 0.f;
-      }
-    }
+    for (int u = 0; u < kU; ++u) load8(xb + (size_t)min(t + u, t_end - 1) * tok_stride, xs[u]);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       float z[8];
@@ -82,9 +93,9 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(const TX *__restrict
         xm2[c] = xm1[c];
         xm1[c] = xs[u][c];
       }
-      if constexpr (L2) {
+      if (P.l2) {
         ss = group_sum<LPR>(ss);
-        const float inv = rsqrtf(ss + eps);
+        const float inv = rsqrtf(ss + a.eps);
 #pragma unroll
         for (int c = 0; c < 8; ++c) z[c] *= inv;
       }
@@ -94,50 +105,65 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(const TX *__restrict
 }
 
 template <typename TX, typename TO, int D>
-hipError_t launch_d(const void *x, const float *w, void *y, int B, int T, int H, bool l2, float eps,
-                    hipStream_t st) {
-  constexpr int HPB = kThreads / (D / 8);
-  const int nspan = (T + kSpan - 1) / kSpan;
-  dim3 grid(B * nspan, (H + HPB - 1) / HPB);
-  if (l2)
-    hipLaunchKernelGGL((prologue_kernel<TX, TO, D, true>), grid, dim3(kThreads), 0, st,
-                       (const TX *)x, w, (TO *)y, T, H, eps);
-  else
-    hipLaunchKernelGGL((prologue_kernel<TX, TO, D, false>), grid, dim3(kThreads), 0, st,
-                       (const TX *)x, w, (TO *)y, T, H, eps);
+hipError_t launch_d(const ProArgs &a, hipStream_t st) {
+  constexpr int RPB = kThreads / (D / 8);
+  const int nspan = (a.T + kSpan - 1) / kSpan;
+  const int nrows = a.t[0].H + a.t[1].H + a.t[2].H;
+  const long blocks = (long)nspan * a.B * ((nrows + RPB - 1) / RPB);
+  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prologue_kernel<TX, TO, D>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
 template <typename TX, typename TO>
-hipError_t launch_xo(const void *x, const float *w, void *y, int B, int T, int H, int d, bool l2,
-                     float eps, hipStream_t st) {
+hipError_t launch_xo(const ProArgs &a, int d, hipStream_t st) {
   switch (d) {
-    case 16: return launch_d<TX, TO, 16>(x, w, y, B, T, H, l2, eps, st);
-    case 32: return launch_d<TX, TO, 32>(x, w, y, B, T, H, l2, eps, st);
-    case 64: return launch_d<TX, TO, 64>(x, w, y, B, T, H, l2, eps, st);
-    case 128: return launch_d<TX, TO, 128>(x, w, y, B, T, H, l2, eps, st);
+    case 16: return launch_d<TX, TO, 16>(a, st);
+    case 32: return launch_d<TX, TO, 32>(a, st);
+    case 64: return launch_d<TX, TO, 64>(a, st);
+    case 128: return launch_d<TX, TO, 128>(a, st);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename TX>
-hipError_t launch_x(const void *x, const float *w, void *y, DType yt, int B, int T, int H, int d,
-                    bool l2, float eps, hipStream_t st) {
+hipError_t launch_x(const ProArgs &a, DType yt, int d, hipStream_t st) {
   switch (yt) {
-    case DType::F32: return launch_xo<TX, float>(x, w, y, B, T, H, d, l2, eps, st);
-    case DType::BF16: return launch_xo<TX, bf16_t>(x, w, y, B, T, H, d, l2, eps, st);
-    case DType::F16: return launch_xo<TX, f16_t>(x, w, y, B, T, H, d, l2, eps, st);
+    case DType::F32: return launch_xo<TX, float>(a, d, st);
+    case DType::BF16: return launch_xo<TX, bf16_t>(a, d, st);
+    case DType::F16: return launch_xo<TX, f16_t>(a, d, st);
   }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_one(const ProArgs &a, DType xt, DType yt, int d, hipStream_t st) {
+  if (xt == DType::BF16) return launch_x<bf16_t>(a, yt, d, st);
+  if (xt == DType::F32) return launch_x<float>(a, yt, d, st);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_prologue(const void *x, DType xt, const float *w, void *y, DType yt, int B, int T,
-                           int H, int d, bool l2, float eps, hipStream_t st) {
-  if (xt == DType::BF16) return launch_x<bf16_t>(x, w, y, yt, B, T, H, d, l2, eps, st);
-  if (xt == DType::F32) return launch_x<float>(x, w, y, yt, B, T, H, d, l2, eps, st);
-  return hipErrorInvalidValue;
+hipError_t launch_prologue(const void *xq, const void *xk, const void *xv, DType xt, const float *w,
+                           void *q, void *k, void *v, DType yt, int B, int T, int Hk, int Hv, int dk,
+                           int dv, float eps, hipStream_t st) {
+  const size_t nw = (size_t)Hk * dk * 4;   // conv_w rows of q, then of k, then of v
+  ProArgs a;
+  a.B = B;
+  a.T = T;
+  a.eps = eps;
+  a.t[0] = ProTensor{xq, w, q, Hk, true};
+  a.t[1] = ProTensor{xk, w + nw, k, Hk, true};
+  a.t[2] = ProTensor{xv, w + 2 * nw, v, Hv, false};
+  if (dk == dv) return launch_one(a, xt, yt, dk, st);
+  // different head dims: q and k in one launch, v in another
+  ProArgs av = a;
+  a.t[2].H = 0;
+  av.t[0].H = 0;
+  av.t[1].H = 0;
+  hipError_t e = launch_one(a, xt, yt, dk, st);
+  if (e != hipSuccess) return e;
+  return launch_one(av, xt, yt, dv, st);
 }
 
 }  // namespace gdn
