@@ -93,6 +93,17 @@ __device__ __forceinline__ half8 to_half8(uint4 u, f16_t) { return __builtin_bit
 
 __device__ __forceinline__ int frag_index(int R, int kk) { return R < 2 ? R : 2 * R - 2 + kk; }
 
+// LDS transpose read of gfx950 (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, every lane reads 8 bytes (four fp16) and lane j receives element j % 4
+// of the reads of lanes 4 e + j / 4, e = 0..3.  So if lane i of the group reads
+// row r0 + i / 4, columns c0 + 4 (i % 4) .. + 3 of a row-major matrix, lane j
+// receives rows r0 .. r0 + 3 of column c0 + j: a column gather in one read.
+typedef short short4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ half4 lds_read_tr(const _Float16 *p) {
+  return __builtin_bit_cast(
+      half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v *)p));
+}
+
 // One row of a row-major fp16 matrix at the columns kset(g4, kk).
 __device__ __forceinline__ half8 perm_row(const _Float16 *M, int st, int row, int kk, int g4) {
   const _Float16 *p = M + row * st + 32 * kk + 4 * g4;
@@ -129,17 +140,20 @@ __device__ __forceinline__ void chunk_scalars(float g, float beta, float *sc, in
 // ============================================================================
 // chunk_prep: P0 per (chunk, key head), T = (I + A)^{-1} per (chunk, value head)
 // ============================================================================
+// K and Q are only read before the value-head loop (into the G and P0
+// accumulators); the per-head matrices then reuse their space.
 constexpr int P_OFF_K = 0;                              // [C][KST] fp16
 constexpr int P_OFF_Q = P_OFF_K + C * KST * 2;          // [C][KST] fp16
-constexpr int P_OFF_T = P_OFF_Q + C * KST * 2;          // [C][CST] fp16
+constexpr int P_OFF_T = 0;                              // [C][CST] fp16 (over K)
 constexpr int P_OFF_P = P_OFF_T + C * CST * 2;          // [C][CST] fp16
 constexpr int P_OFF_AO = P_OFF_P + C * CST * 2;         // [C][CST] fp16
 constexpr int P_OFF_AD = P_OFF_AO + C * CST * 2;        // [4][16][DST] fp32
-constexpr int P_OFF_SC = P_OFF_AD + 4 * 16 * DST * 4;   // 5 x [C] fp32
+constexpr int P_OFF_SC = P_OFF_Q + C * KST * 2;         // 5 x [C] fp32
 constexpr int P_SMEM = P_OFF_SC + 5 * C * 4;
+static_assert(P_OFF_AD + 4 * 16 * DST * 4 <= P_OFF_SC, "per-head matrices overlap the scalars");
 
 template <typename TQ, typename TG>
-__global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
+__global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TG *__restrict__ g,
     const TG *__restrict__ beta, uint4 *__restrict__ Tws, int T, int Hk, int Hv, int nchunks) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -161,16 +175,31 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
   const int t0 = c * C, n = min(C, T - t0);
   const size_t bt0 = (size_t)b * T + t0;
 
-  // K and Q tiles (fp16), rows past the end zero
+  // gate and beta of the first value head (lane = token); the next head's are
+  // always requested before this head's results are stored, so that waiting
+  // for them never waits for those stores
+  const int hrow = min(tid, n - 1);
+  TG g_nx = g[(bt0 + hrow) * Hv + kh * grp], b_nx = beta[(bt0 + hrow) * Hv + kh * grp];
+
+  // K and Q tiles (fp16), rows past the end zero; all eight loads are in
+  // flight before the first is converted
+  {
+    uint4 uk[4], uq[4];
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int row = (tid >> 4) + 16 * it;
-    const size_t off = ((bt0 + min(row, n - 1)) * Hk + kh) * DK + (tid & 15) * 8;
-    const uint4 uk = *reinterpret_cast<const uint4 *>(k + off);
-    const uint4 uq = *reinterpret_cast<const uint4 *>(q + off);
+    for (int it = 0; it < 4; ++it) {
+      const int row = (tid >> 4) + 16 * it;
+      const size_t off = ((bt0 + min(row, n - 1)) * Hk + kh) * DK + (tid & 15) * 8;
+      uk[it] = *reinterpret_cast<const uint4 *>(k + off);
+      uq[it] = *reinterpret_cast<const uint4 *>(q + off);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     const half8 hz = {};
-    *reinterpret_cast<half8 *>(sK + row * KST + (tid & 15) * 8) = row < n ? to_half8(uk, TQ{}) : hz;
-    *reinterpret_cast<half8 *>(sQ + row * KST + (tid & 15) * 8) = row < n ? to_half8(uq, TQ{}) : hz;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int row = (tid >> 4) + 16 * it;
+      *reinterpret_cast<half8 *>(sK + row * KST + (tid & 15) * 8) = row < n ? to_half8(uk[it], TQ{}) : hz;
+      *reinterpret_cast<half8 *>(sQ + row * KST + (tid & 15) * 8) = row < n ? to_half8(uq[it], TQ{}) : hz;
+    }
   }
   lds_barrier();
 
@@ -205,13 +234,14 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
   }
   for (int hv = 0; hv < grp; ++hv) {
     const int h = kh * grp + hv;
-    lds_barrier();  // the previous head's T has been read out
+    lds_barrier();  // K and Q, or the previous head's T and P, have been read out
     if (tid < C) {
-      const int row = min(tid, n - 1);
       const bool ok = tid < n;
-      const float gv = ok ? to_f32(g[(bt0 + row) * Hv + h]) : 0.f;
-      const float bv = ok ? to_f32(beta[(bt0 + row) * Hv + h]) : 0.f;
-      chunk_scalars(gv, bv, sc, tid);
+      chunk_scalars(ok ? to_f32(g_nx) : 0.f, ok ? to_f32(b_nx) : 0.f, sc, tid);
+    }
+    if (hv + 1 < grp) {
+      g_nx = g[(bt0 + hrow) * Hv + h + 1];
+      b_nx = beta[(bt0 + hrow) * Hv + h + 1];
     }
     lds_barrier();
     // P = L o P0 for this head (lower incl. diagonal), fp16; the two upper
@@ -471,23 +501,40 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
     f.beta = betab[(t0 + row) * Hv];
   };
   auto commit = [&](int buf) {
-    const half8 hz = {};
+    // Nothing of the commit (the conversions of the raw loads above all) may be
+    // scheduled into the chunk's arithmetic: that would wait for the loads there.
+    __builtin_amdgcn_sched_barrier(0);
     _Float16 *k_ = sKb + buf * C * KST, *q_ = sQb + buf * C * KST, *v_ = sVb + buf * C * VST;
-    const bool full = f.n == C;
+    if (f.n == C) {
 #pragma unroll
-    for (int it = 0; it < NKQ; ++it) {
-      const int e = tid + THREADS * it;
-      const int row = e >> 4;
-      const bool ok = full || row < f.n;
-      *reinterpret_cast<half8 *>(k_ + row * KST + (e & 15) * 8) = ok ? to_half8(f.k[it], TQ{}) : hz;
-      *reinterpret_cast<half8 *>(q_ + row * KST + (e & 15) * 8) = ok ? to_half8(f.q[it], TQ{}) : hz;
-    }
+      for (int it = 0; it < NKQ; ++it) {
+        const int e = tid + THREADS * it;
+        *reinterpret_cast<half8 *>(k_ + (e >> 4) * KST + (e & 15) * 8) = to_half8(f.k[it], TQ{});
+        *reinterpret_cast<half8 *>(q_ + (e >> 4) * KST + (e & 15) * 8) = to_half8(f.q[it], TQ{});
+      }
 #pragma unroll
-    for (int it = 0; it < NV; ++it) {
-      const int e = tid + THREADS * it;
-      const int row = e / (WGC / 8);
-      *reinterpret_cast<half8 *>(v_ + row * VST + (e % (WGC / 8)) * 8) =
-          full || row < f.n ? to_half8(f.v[it], TQ{}) : hz;
+      for (int it = 0; it < NV; ++it) {
+        const int e = tid + THREADS * it;
+        *reinterpret_cast<half8 *>(v_ + (e / (WGC / 8)) * VST + (e % (WGC / 8)) * 8) =
+            to_half8(f.v[it], TQ{});
+      }
+    } else {
+      // last chunk of a ragged sequence: rows past its end are zero
+      const half8 hz = {};
+#pragma unroll
+      for (int it = 0; it < NKQ; ++it) {
+        const int e = tid + THREADS * it;
+        const bool ok = (e >> 4) < f.n;
+        *reinterpret_cast<half8 *>(k_ + (e >> 4) * KST + (e & 15) * 8) = ok ? to_half8(f.k[it], TQ{}) : hz;
+        *reinterpret_cast<half8 *>(q_ + (e >> 4) * KST + (e & 15) * 8) = ok ? to_half8(f.q[it], TQ{}) : hz;
+      }
+#pragma unroll
+      for (int it = 0; it < NV; ++it) {
+        const int e = tid + THREADS * it;
+        const int row = e / (WGC / 8);
+        *reinterpret_cast<half8 *>(v_ + row * VST + (e % (WGC / 8)) * 8) =
+            row < f.n ? to_half8(f.v[it], TQ{}) : hz;
+      }
     }
 #pragma unroll
     for (int it = 0; it < NTP; ++it) {
@@ -502,6 +549,11 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
 
   fetch(0);
   commit(0);
+  // Everything loaded so far (S0 and chunk 0) has landed.  Said explicitly,
+  // so that the compiler's wait tracking does not carry these loads into the
+  // loop and wait on later stores for them.  (gfx9 encoding: vmcnt 0,
+  // expcnt 7, lgkmcnt 15.)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   lds_barrier();
 
   for (int c = 0; c < nchunks; ++c) {
@@ -510,6 +562,9 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
     const _Float16 *cK = sKb + buf * C * KST, *cQ = sQb + buf * C * KST, *cV = sVb + buf * C * VST;
     const uint4 *cT = sTPb + buf * 2 * NFRAG * 64, *cP = cT + NFRAG * 64;
     const float *sc = sScb + buf * 5 * C;
+    // transpose-read bases: lane (g4, i) reads row 4 g4 + i / 4, columns 4 (i % 4) .. + 3
+    const _Float16 *kT = cK + (4 * g4 + (ln >> 2)) * KST + 4 * (ln & 3);
+    const _Float16 *vT = cV + (4 * g4 + (ln >> 2)) * VST + ic + 4 * (ln & 3);
     if (c + 1 < nchunks) fetch(c + 1);
 
     // S fragments (fp16) in kset order over the key channels
@@ -538,17 +593,18 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
     }
 
     // X = beta V - beta Gamma (K S^T), as fragments over the chunk rows
+    // (V rows 16 R + 4 g4 .. + 3 at this lane's value column, by transpose reads)
     half8 xf[2];
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
       const int r0 = 16 * R + 4 * g4;
+      const half4 vv = lds_read_tr(vT + 16 * R * VST);
       const float4 bb = *reinterpret_cast<const float4 *>(sc + 2 * C + r0);
       const float4 bg = *reinterpret_cast<const float4 *>(sc + 3 * C + r0);
       const float bv[4] = {bb.x, bb.y, bb.z, bb.w}, gv[4] = {bg.x, bg.y, bg.z, bg.w};
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii)
-        xf[R >> 1][(R & 1) * 4 + ii] =
-            (_Float16)(bv[ii] * (float)cV[(r0 + ii) * VST + ic + ln] - gv[ii] * accX[R][ii]);
+        xf[R >> 1][(R & 1) * 4 + ii] = (_Float16)(bv[ii] * (float)vv[ii] - gv[ii] * accX[R][ii]);
     }
 
     // N = T X;  N and diag(e^{gamma_n - gamma}) N as fragments over the chunk rows
@@ -567,7 +623,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
       }
     }
 
-    // O^T = Gamma (S Q^T) + N^T P^T:  row r = 16 R + ln of this lane
+    // O^T = Gamma (S Q^T) + N^T P^T:  row r = 16 R + ln of this lane (stored after the commit)
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
       const int r = 16 * R + ln;
@@ -577,22 +633,21 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
       for (int ii = 0; ii < 4; ++ii) acc[ii] *= er;
       acc = mfma32(nf[0], __builtin_bit_cast(half8, cP[frag_index(R, 0) * 64 + l]), acc);
       if (R >= 2) acc = mfma32(nf[1], __builtin_bit_cast(half8, cP[frag_index(R, 1) * 64 + l]), acc);
-      if (t0 + r < T)
-        *reinterpret_cast<float4 *>(ob + (size_t)(t0 + r) * v_rs) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      accO[R] = acc;
     }
 
     // S^T <- Gamma_n S^T + K^T N~  (K columns 16 J + ln at the chunk rows kset)
     {
       const float gC = sc[C + C - 1];
-      const _Float16 *kcol = cK + (4 * g4) * KST + ln;
 #pragma unroll
       for (int J = 0; J < 8; ++J) {
         half8 kc[2];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            kc[kk][e] = kcol[(32 * kk + (e >> 2) * 16 + (e & 3)) * KST + 16 * J];
+        for (int kk = 0; kk < 2; ++kk) {
+          const half4 lo = lds_read_tr(kT + 32 * kk * KST + 16 * J);
+          const half4 hi = lds_read_tr(kT + (32 * kk + 16) * KST + 16 * J);
+          kc[kk] = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
         float4v acc = accS[J];
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) acc[ii] *= gC;
@@ -603,6 +658,17 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
     }
 
     if (c + 1 < nchunks) commit(buf ^ 1);
+    // The output stores go out only now.  On this architecture one counter
+    // tracks both loads and stores, and a wait for a load while stores are in
+    // flight also waits for the stores; issued after the commit, they have the
+    // next chunk's arithmetic to complete before its commit waits again.
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+      const int r = 16 * R + ln;
+      if (t0 + r < T)
+        *reinterpret_cast<float4 *>(ob + (size_t)(t0 + r) * v_rs) =
+            make_float4(accO[R][0], accO[R][1], accO[R][2], accO[R][3]);
+    }
     lds_barrier();
   }
 
