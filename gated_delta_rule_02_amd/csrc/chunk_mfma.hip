@@ -56,6 +56,8 @@
 //    loads (and its T and P0 fragments) are issued at the top of a chunk and
 //    land at its end.  Blocks are numbered so that workgroups sharing a key
 //    head run on one XCD (shared K, Q and P0 then hit in its L2).
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -135,6 +137,86 @@ __device__ __forceinline__ void chunk_scalars(float g, float beta, float *sc, in
   sc[2 * C + lane] = beta;
   sc[3 * C + lane] = beta * eg;
   sc[4 * C + lane] = __expf(gC - x);
+}
+
+// T = (I + A)^{-1} for a 64 x 64 unit lower-triangular I + A, then T and P
+// stored as fragments at dst (T first).  On entry the strictly lower 16 x 16
+// diagonal blocks of A are in sAd (fp32), its blocks below the diagonal in
+// sAo (fp16), and sT and sP have zero blocks (0,1) and (2,3) (the fragments
+// read them).  Called by all 256 threads; wave w owns block row w.
+//
+// Diagonal blocks: forward substitution in fp32 (wave w -> block w).  Blocks
+// below: column by column, T_RS = -T_RR sum_M A_RM T_MS, on 16x16x16 MFMAs.
+__device__ __forceinline__ void invert_store(const float *sAd, const _Float16 *sAo, _Float16 *sT,
+                                             const _Float16 *sP, uint4 *__restrict__ dst, int w, int l) {
+  const int g4 = l >> 4, ln = l & 15;
+  lds_barrier();
+  // diagonal blocks of T by forward substitution (wave w -> block w):
+  // lane = (column cc, sub); the lane keeps T[4j + sub][cc], j = 0..3
+  {
+    const int cc = l >> 2, sub = l & 3;
+    const float *Ad = sAd + w * 16 * DST;
+    float t[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t[j] = (4 * j + sub == cc) ? 1.f : 0.f;
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
+      float part = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = 4 * j + sub;
+        if (m < r) part += Ad[r * DST + m] * t[j];
+      }
+      part += __shfl_xor(part, 1, 64);
+      part += __shfl_xor(part, 2, 64);
+      const float val = (r == cc) ? 1.f : -part;
+      if ((r & 3) == sub) t[r >> 2] = val;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sT[(16 * w + 4 * j + sub) * CST + 16 * w + cc] = (_Float16)t[j];
+  }
+  lds_barrier();
+  // off-diagonal blocks, column S = w (waves 0..2); block (S+e, S) = tc[e]
+  if (w < 3) {
+    const int S = w;
+    half4 tc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tc[0][j] = sT[(16 * S + 4 * g4 + j) * CST + 16 * S + ln];
+#pragma unroll
+    for (int e = 1; e < 4; ++e) {
+      if (S + e <= 3) {
+        const int R = S + e;
+        float4v y = {0.f, 0.f, 0.f, 0.f};
+        const _Float16 *arow = sAo + (16 * R + ln) * CST + 16 * S + 4 * g4;
+#pragma unroll
+        for (int f = 0; f < e; ++f)
+          y = mfma16(*reinterpret_cast<const half4 *>(arow + 16 * f), tc[f], y);
+        half4 yb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) yb[j] = (_Float16)y[j];
+        const half4 trr =
+            *reinterpret_cast<const half4 *>(sT + (16 * R + ln) * CST + 16 * R + 4 * g4);
+        const float4v zero = {0.f, 0.f, 0.f, 0.f};
+        const float4v tr = mfma16(trr, yb, zero);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          tc[e][j] = (_Float16)(-tr[j]);
+          sT[(16 * R + 4 * g4 + j) * CST + 16 * S + ln] = tc[e][j];
+        }
+      }
+    }
+  }
+  lds_barrier();
+  {
+    // T then P: 2 x NFRAG fragments
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+      if (kk == 0 || w >= 2) {
+        dst[frag_index(w, kk) * 64 + l] = __builtin_bit_cast(uint4, perm_row(sT, CST, 16 * w + ln, kk, g4));
+        dst[(NFRAG + frag_index(w, kk)) * 64 + l] =
+            __builtin_bit_cast(uint4, perm_row(sP, CST, 16 * w + ln, kk, g4));
+      }
+  }
 }
 
 // ============================================================================
@@ -296,81 +378,25 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
       sT[rr * CST + 16 + cc] = (_Float16)0.f;
       sT[(32 + rr) * CST + 48 + cc] = (_Float16)0.f;
     }
-    lds_barrier();
-    // diagonal blocks of T by forward substitution (wave w -> block w):
-    // lane = (column cc, sub); the lane keeps T[4j + sub][cc], j = 0..3
-    {
-      const int cc = l >> 2, sub = l & 3;
-      const float *Ad = sAd + w * 16 * DST;
-      float t[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) t[j] = (4 * j + sub == cc) ? 1.f : 0.f;
-#pragma unroll
-      for (int r = 1; r < 16; ++r) {
-        float part = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int m = 4 * j + sub;
-          if (m < r) part += Ad[r * DST + m] * t[j];
-        }
-        part += __shfl_xor(part, 1, 64);
-        part += __shfl_xor(part, 2, 64);
-        const float val = (r == cc) ? 1.f : -part;
-        if ((r & 3) == sub) t[r >> 2] = val;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sT[(16 * w + 4 * j + sub) * CST + 16 * w + cc] = (_Float16)t[j];
-    }
-    lds_barrier();
-    // off-diagonal blocks, column S = w (waves 0..2); block (S+e, S) = tc[e]
-    if (w < 3) {
-      const int S = w;
-      half4 tc[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) tc[0][j] = sT[(16 * S + 4 * g4 + j) * CST + 16 * S + ln];
-#pragma unroll
-      for (int e = 1; e < 4; ++e) {
-        if (S + e <= 3) {
-          const int R = S + e;
-          float4v y = {0.f, 0.f, 0.f, 0.f};
-          const _Float16 *arow = sAo + (16 * R + ln) * CST + 16 * S + 4 * g4;
-#pragma unroll
-          for (int f = 0; f < e; ++f)
-            y = mfma16(*reinterpret_cast<const half4 *>(arow + 16 * f), tc[f], y);
-          half4 yb;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) yb[j] = (_Float16)y[j];
-          const half4 trr =
-              *reinterpret_cast<const half4 *>(sT + (16 * R + ln) * CST + 16 * R + 4 * g4);
-          const float4v zero = {0.f, 0.f, 0.f, 0.f};
-          const float4v tr = mfma16(trr, yb, zero);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            tc[e][j] = (_Float16)(-tr[j]);
-            sT[(16 * R + 4 * g4 + j) * CST + 16 * S + ln] = tc[e][j];
-          }
-        }
-      }
-    }
-    lds_barrier();
-    {
-      // T then P for (b, h, chunk): 2 x NFRAG fragments
-      uint4 *dst = Tws + (((size_t)b * Hv + h) * nchunks + c) * (2 * NFRAG * 64);
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        if (kk == 0 || w >= 2) {
-          dst[frag_index(w, kk) * 64 + l] = __builtin_bit_cast(uint4, perm_row(sT, CST, 16 * w + ln, kk, g4));
-          dst[(NFRAG + frag_index(w, kk)) * 64 + l] =
-              __builtin_bit_cast(uint4, perm_row(sP, CST, 16 * w + ln, kk, g4));
-        }
-    }
+    invert_store(sAd, sAo, sT, sP, Tws + (((size_t)b * Hv + h) * nchunks + c) * (2 * NFRAG * 64), w, l);
   }
 }
 
 // ============================================================================
 // chunk_seq: the sequential pass over the chunks of one sequence
 // ============================================================================
-template <int NW>
+// Workspace of the key-channel gate per (batch, value head, chunk), in
+// 16-byte units: T and P fragments; K o e^gamma, Q o e^gamma and
+// K o e^{gamma_n - gamma} (fp16, 64 x 128 row-major, rows past the end of the
+// sequence zero); beta[64] and Gamma_n[128] (fp32).
+constexpr int KDA_KG = 2 * NFRAG * 64;
+constexpr int KDA_QG = KDA_KG + C * DK / 8;
+constexpr int KDA_KD = KDA_QG + C * DK / 8;
+constexpr int KDA_SC = KDA_KD + C * DK / 8;
+constexpr int KDA_NSC = (C + DK) / 4;
+constexpr int KDA_CHUNK_U4 = (KDA_SC + KDA_NSC + 15) / 16 * 16;
+
+template <int NW, bool KDA>
 struct SeqCfg {
   static constexpr int THREADS = 64 * NW;      // NW waves, 16 value rows of the state each
   static constexpr int WGC = 16 * NW;          // value rows per workgroup
@@ -379,31 +405,40 @@ struct SeqCfg {
   static constexpr int NKQ = (C * DK / 8) / THREADS;     // 16-byte K (and Q) pieces per thread
   static constexpr int NV = (C * WGC / 8) / THREADS;     // 16-byte V pieces per thread
   static constexpr int NTP = (2 * NFRAG * 64 + THREADS - 1) / THREADS;  // T and P fragment pieces
+  static constexpr int NSC = KDA ? C + DK : 5 * C;       // fp32 scalars per chunk
+  static constexpr int CHUNK_U4 = KDA ? KDA_CHUNK_U4 : 2 * NFRAG * 64;  // workspace per chunk
   static constexpr int OFF_K = 0;                          // 2 x [C][KST] fp16
   static constexpr int OFF_Q = OFF_K + 2 * C * KST * 2;    // 2 x [C][KST] fp16
-  static constexpr int OFF_V = OFF_Q + 2 * C * KST * 2;    // 2 x [C][VST] fp16
+  static constexpr int OFF_KD = OFF_Q + 2 * C * KST * 2;   // 2 x [C][KST] fp16 (key gate)
+  static constexpr int OFF_V = OFF_KD + (KDA ? 2 * C * KST * 2 : 0);   // 2 x [C][VST] fp16
   static constexpr int OFF_TP = OFF_V + 2 * C * VST * 2;   // 2 x [2 NFRAG][64] x 16 B
-  static constexpr int OFF_SC = OFF_TP + 2 * 2 * NFRAG * 64 * 16;   // 2 x 5 x [C] fp32
-  static constexpr int SMEM = OFF_SC + 2 * 5 * C * 4;
+  static constexpr int OFF_SC = OFF_TP + 2 * 2 * NFRAG * 64 * 16;   // 2 x [NSC] fp32
+  static constexpr int SMEM = OFF_SC + 2 * NSC * 4;
   static_assert(SMEM <= 160 * 1024, "LDS");
 };
 
 // The next chunk's raw loads.  Nothing is converted here, so no instruction
 // needs the data before the chunk is committed.
-template <typename TQ, typename TG, int NW>
+template <typename TQ, typename TG, int NW, bool KDA>
 struct SeqFetch {
-  uint4 k[SeqCfg<NW>::NKQ], q[SeqCfg<NW>::NKQ], v[SeqCfg<NW>::NV], tp[SeqCfg<NW>::NTP];
+  using Cfg = SeqCfg<NW, KDA>;
+  uint4 k[Cfg::NKQ], q[Cfg::NKQ], kd[KDA ? Cfg::NKQ : 1], v[Cfg::NV], tp[Cfg::NTP], sc;
   TG g, beta;
   int n;
 };
 
-template <typename TQ, typename TG, int NW>
+// KDA false: head gate; K, Q, V, g, beta are read from the inputs and T, P
+// from the workspace.  KDA true: key-channel gate; the decayed K, Q, the
+// state-update K, beta and Gamma_n come from the workspace (q, k, g, beta are
+// not read) and the state decays per key channel.
+template <typename TQ, typename TG, int NW, bool KDA>
 __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *__restrict__ v,
-    const TG *__restrict__ g, const TG *__restrict__ beta, const uint4 *__restrict__ TPws,
+    const TG *__restrict__ g, const TG *__restrict__ beta, const uint4 *__restrict__ ws,
     const float *__restrict__ S0, float *__restrict__ o, float *__restrict__ ST, int T, int Hk,
     int Hv, int ntasks, int nchunks) {
-  using Cfg = SeqCfg<NW>;
+  using Cfg = SeqCfg<NW, KDA>;
+  constexpr int NSC = Cfg::NSC;
   constexpr int THREADS = Cfg::THREADS, WGC = Cfg::WGC, NS = Cfg::NS, VST = Cfg::VST;
   constexpr int NKQ = Cfg::NKQ, NV = Cfg::NV, NTP = Cfg::NTP;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -431,7 +466,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
   const TG *gb = g + (size_t)b * T * Hv + h;
   const TG *betab = beta + (size_t)b * T * Hv + h;
   float *ob = o + ((size_t)b * T * Hv + h) * DV + iw0 + 4 * g4;
-  const uint4 *TPbh = TPws + (size_t)bh * nchunks * (2 * NFRAG * 64);
+  const uint4 *wsbh = ws + (size_t)bh * nchunks * Cfg::CHUNK_U4;
   int kq_off[NKQ], v_off[NV];
 #pragma unroll
   for (int it = 0; it < NKQ; ++it) {
@@ -446,6 +481,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
 
   _Float16 *const sKb = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_K);
   _Float16 *const sQb = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_Q);
+  _Float16 *const sKdb = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_KD);
   _Float16 *const sVb = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_V);
   uint4 *const sTPb = reinterpret_cast<uint4 *>(smem + Cfg::OFF_TP);
   float *const sScb = reinterpret_cast<float *>(smem + Cfg::OFF_SC);
@@ -463,28 +499,43 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
     accS[J] = s;
   }
 
-  SeqFetch<TQ, TG, NW> f;
+  SeqFetch<TQ, TG, NW, KDA> f;
   auto fetch = [&](int c) {
     const int n = min(C, T - c * C);
     f.n = n;
     const size_t t0 = (size_t)c * C;
+    const uint4 *wc = wsbh + (size_t)c * Cfg::CHUNK_U4;
     const TQ *kc = kb + t0 * kq_rs, *qc = qb + t0 * kq_rs, *vc = vb + t0 * v_rs;
-    if (n == C) {
+    if constexpr (KDA) {
+      // rows past the end of the sequence are zero in the workspace
 #pragma unroll
       for (int it = 0; it < NKQ; ++it) {
-        f.k[it] = *reinterpret_cast<const uint4 *>(kc + kq_off[it]);
-        f.q[it] = *reinterpret_cast<const uint4 *>(qc + kq_off[it]);
+        const int e = tid + THREADS * it;
+        f.k[it] = wc[KDA_KG + e];
+        f.q[it] = wc[KDA_QG + e];
+        f.kd[it] = wc[KDA_KD + e];
+      }
+    }
+    if (n == C) {
+      if constexpr (!KDA) {
+#pragma unroll
+        for (int it = 0; it < NKQ; ++it) {
+          f.k[it] = *reinterpret_cast<const uint4 *>(kc + kq_off[it]);
+          f.q[it] = *reinterpret_cast<const uint4 *>(qc + kq_off[it]);
+        }
       }
 #pragma unroll
       for (int it = 0; it < NV; ++it) f.v[it] = *reinterpret_cast<const uint4 *>(vc + v_off[it]);
     } else {
       // last chunk: rows past the end of the sequence re-read its last row
+      if constexpr (!KDA) {
 #pragma unroll
-      for (int it = 0; it < NKQ; ++it) {
-        const int e = tid + THREADS * it;
-        const int off = min(e >> 4, n - 1) * kq_rs + (e & 15) * 8;
-        f.k[it] = *reinterpret_cast<const uint4 *>(kc + off);
-        f.q[it] = *reinterpret_cast<const uint4 *>(qc + off);
+        for (int it = 0; it < NKQ; ++it) {
+          const int e = tid + THREADS * it;
+          const int off = min(e >> 4, n - 1) * kq_rs + (e & 15) * 8;
+          f.k[it] = *reinterpret_cast<const uint4 *>(kc + off);
+          f.q[it] = *reinterpret_cast<const uint4 *>(qc + off);
+        }
       }
 #pragma unroll
       for (int it = 0; it < NV; ++it) {
@@ -493,24 +544,42 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
                                                    (e % (WGC / 8)) * 8);
       }
     }
-    const uint4 *tpc = TPbh + (size_t)c * (2 * NFRAG * 64);
 #pragma unroll
-    for (int it = 0; it < NTP; ++it) f.tp[it] = tpc[min(tid + THREADS * it, 2 * NFRAG * 64 - 1)];
-    const int row = min(tid & 63, n - 1);
-    f.g = gb[(t0 + row) * Hv];
-    f.beta = betab[(t0 + row) * Hv];
+    for (int it = 0; it < NTP; ++it) f.tp[it] = wc[min(tid + THREADS * it, 2 * NFRAG * 64 - 1)];
+    if constexpr (KDA) {
+      f.sc = wc[KDA_SC + min(tid, KDA_NSC - 1)];
+    } else {
+      const int row = min(tid & 63, n - 1);
+      f.g = gb[(t0 + row) * Hv];
+      f.beta = betab[(t0 + row) * Hv];
+    }
   };
   auto commit = [&](int buf) {
     // Nothing of the commit (the conversions of the raw loads above all) may be
     // scheduled into the chunk's arithmetic: that would wait for the loads there.
     __builtin_amdgcn_sched_barrier(0);
     _Float16 *k_ = sKb + buf * C * KST, *q_ = sQb + buf * C * KST, *v_ = sVb + buf * C * VST;
-    if (f.n == C) {
+    // K and Q (and the state-update K) are fp16 in the workspace of the key gate
+    using TK = typename std::conditional<KDA, f16_t, TQ>::type;
+    if constexpr (KDA) {
+      _Float16 *kd_ = sKdb + buf * C * KST;
 #pragma unroll
       for (int it = 0; it < NKQ; ++it) {
         const int e = tid + THREADS * it;
-        *reinterpret_cast<half8 *>(k_ + (e >> 4) * KST + (e & 15) * 8) = to_half8(f.k[it], TQ{});
-        *reinterpret_cast<half8 *>(q_ + (e >> 4) * KST + (e & 15) * 8) = to_half8(f.q[it], TQ{});
+        *reinterpret_cast<half8 *>(k_ + (e >> 4) * KST + (e & 15) * 8) = to_half8(f.k[it], f16_t{});
+        *reinterpret_cast<half8 *>(q_ + (e >> 4) * KST + (e & 15) * 8) = to_half8(f.q[it], f16_t{});
+        *reinterpret_cast<half8 *>(kd_ + (e >> 4) * KST + (e & 15) * 8) = to_half8(f.kd[it], f16_t{});
+      }
+      if (tid < KDA_NSC) reinterpret_cast<uint4 *>(sScb + buf * NSC)[tid] = f.sc;
+    }
+    if (f.n == C) {
+      if constexpr (!KDA) {
+#pragma unroll
+        for (int it = 0; it < NKQ; ++it) {
+          const int e = tid + THREADS * it;
+          *reinterpret_cast<half8 *>(k_ + (e >> 4) * KST + (e & 15) * 8) = to_half8(f.k[it], TK{});
+          *reinterpret_cast<half8 *>(q_ + (e >> 4) * KST + (e & 15) * 8) = to_half8(f.q[it], TK{});
+        }
       }
 #pragma unroll
       for (int it = 0; it < NV; ++it) {
@@ -521,12 +590,14 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
     } else {
       // last chunk of a ragged sequence: rows past its end are zero
       const half8 hz = {};
+      if constexpr (!KDA) {
 #pragma unroll
-      for (int it = 0; it < NKQ; ++it) {
-        const int e = tid + THREADS * it;
-        const bool ok = (e >> 4) < f.n;
-        *reinterpret_cast<half8 *>(k_ + (e >> 4) * KST + (e & 15) * 8) = ok ? to_half8(f.k[it], TQ{}) : hz;
-        *reinterpret_cast<half8 *>(q_ + (e >> 4) * KST + (e & 15) * 8) = ok ? to_half8(f.q[it], TQ{}) : hz;
+        for (int it = 0; it < NKQ; ++it) {
+          const int e = tid + THREADS * it;
+          const bool ok = (e >> 4) < f.n;
+          *reinterpret_cast<half8 *>(k_ + (e >> 4) * KST + (e & 15) * 8) = ok ? to_half8(f.k[it], TK{}) : hz;
+          *reinterpret_cast<half8 *>(q_ + (e >> 4) * KST + (e & 15) * 8) = ok ? to_half8(f.q[it], TK{}) : hz;
+        }
       }
 #pragma unroll
       for (int it = 0; it < NV; ++it) {
@@ -541,9 +612,11 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
       const int e = tid + THREADS * it;
       if (e < 2 * NFRAG * 64) sTPb[buf * 2 * NFRAG * 64 + e] = f.tp[it];
     }
-    if (tid < C) {
-      const bool ok = tid < f.n;
-      chunk_scalars(ok ? to_f32(f.g) : 0.f, ok ? to_f32(f.beta) : 0.f, sScb + buf * 5 * C, tid);
+    if constexpr (!KDA) {
+      if (tid < C) {
+        const bool ok = tid < f.n;
+        chunk_scalars(ok ? to_f32(f.g) : 0.f, ok ? to_f32(f.beta) : 0.f, sScb + buf * NSC, tid);
+      }
     }
   };
 
@@ -561,10 +634,12 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
     const int t0 = c * C;
     const _Float16 *cK = sKb + buf * C * KST, *cQ = sQb + buf * C * KST, *cV = sVb + buf * C * VST;
     const uint4 *cT = sTPb + buf * 2 * NFRAG * 64, *cP = cT + NFRAG * 64;
-    const float *sc = sScb + buf * 5 * C;
+    const float *sc = sScb + buf * NSC;
     // transpose-read bases: lane (g4, i) reads row 4 g4 + i / 4, columns 4 (i % 4) .. + 3
     const _Float16 *kT = cK + (4 * g4 + (ln >> 2)) * KST + 4 * (ln & 3);
     const _Float16 *vT = cV + (4 * g4 + (ln >> 2)) * VST + ic + 4 * (ln & 3);
+    // the K whose columns update the state: K itself, or K o e^{gamma_n - gamma} for the key gate
+    const _Float16 *uT = KDA ? sKdb + buf * C * KST + (4 * g4 + (ln >> 2)) * KST + 4 * (ln & 3) : kT;
     if (c + 1 < nchunks) fetch(c + 1);
 
     // S fragments (fp16) in kset order over the key channels
@@ -599,8 +674,9 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
     for (int R = 0; R < 4; ++R) {
       const int r0 = 16 * R + 4 * g4;
       const half4 vv = lds_read_tr(vT + 16 * R * VST);
-      const float4 bb = *reinterpret_cast<const float4 *>(sc + 2 * C + r0);
-      const float4 bg = *reinterpret_cast<const float4 *>(sc + 3 * C + r0);
+      // beta and beta Gamma (key gate: Gamma is inside the decayed K)
+      const float4 bb = *reinterpret_cast<const float4 *>(sc + (KDA ? 0 : 2 * C) + r0);
+      const float4 bg = KDA ? bb : *reinterpret_cast<const float4 *>(sc + 3 * C + r0);
       const float bv[4] = {bb.x, bb.y, bb.z, bb.w}, gv[4] = {bg.x, bg.y, bg.z, bg.w};
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii)
@@ -614,7 +690,8 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
       float4v acc = {0.f, 0.f, 0.f, 0.f};
       acc = mfma32(__builtin_bit_cast(half8, cT[frag_index(R, 0) * 64 + l]), xf[0], acc);
       if (R >= 2) acc = mfma32(__builtin_bit_cast(half8, cT[frag_index(R, 1) * 64 + l]), xf[1], acc);
-      const float4 dd = *reinterpret_cast<const float4 *>(sc + 4 * C + 16 * R + 4 * g4);
+      const float4 dd = KDA ? make_float4(1.f, 1.f, 1.f, 1.f)
+                            : *reinterpret_cast<const float4 *>(sc + 4 * C + 16 * R + 4 * g4);
       const float dv4[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
@@ -627,10 +704,12 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
       const int r = 16 * R + ln;
-      const float er = sc[C + r];
       float4v acc = accO[R];
+      if constexpr (!KDA) {
+        const float er = sc[C + r];
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) acc[ii] *= er;
+        for (int ii = 0; ii < 4; ++ii) acc[ii] *= er;
+      }
       acc = mfma32(nf[0], __builtin_bit_cast(half8, cP[frag_index(R, 0) * 64 + l]), acc);
       if (R >= 2) acc = mfma32(nf[1], __builtin_bit_cast(half8, cP[frag_index(R, 1) * 64 + l]), acc);
       accO[R] = acc;
@@ -638,19 +717,25 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
 
     // S^T <- Gamma_n S^T + K^T N~  (K columns 16 J + ln at the chunk rows kset)
     {
-      const float gC = sc[C + C - 1];
+      const float gC = KDA ? 1.f : sc[C + C - 1];
 #pragma unroll
       for (int J = 0; J < 8; ++J) {
         half8 kc[2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const half4 lo = lds_read_tr(kT + 32 * kk * KST + 16 * J);
-          const half4 hi = lds_read_tr(kT + (32 * kk + 16) * KST + 16 * J);
+          const half4 lo = lds_read_tr(uT + 32 * kk * KST + 16 * J);
+          const half4 hi = lds_read_tr(uT + (32 * kk + 16) * KST + 16 * J);
           kc[kk] = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
         float4v acc = accS[J];
+        if constexpr (KDA) {
+          // per key channel 16 J + 4 g4 + ii
+          const float4 gn = *reinterpret_cast<const float4 *>(sc + C + 16 * J + 4 * g4);
+          acc[0] *= gn.x; acc[1] *= gn.y; acc[2] *= gn.z; acc[3] *= gn.w;
+        } else {
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) acc[ii] *= gC;
+          for (int ii = 0; ii < 4; ++ii) acc[ii] *= gC;
+        }
         acc = mfma32(kc[0], ndf[0], acc);
         acc = mfma32(kc[1], ndf[1], acc);
         accS[J] = acc;
@@ -679,12 +764,12 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
         make_float4(accS[J][0], accS[J][1], accS[J][2], accS[J][3]);
 }
 
-template <typename TQ, typename TG, int NW>
+template <typename TQ, typename TG, int NW, bool KDA>
 hipError_t launch_seq(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
                       const void *beta, const uint4 *TPws, const float *S0, float *o, float *ST,
                       int nchunks, hipStream_t st) {
-  using Cfg = SeqCfg<NW>;
-  auto kern = chunk_seq_kernel<TQ, TG, NW>;
+  using Cfg = SeqCfg<NW, KDA>;
+  auto kern = chunk_seq_kernel<TQ, TG, NW, KDA>;
   hipError_t e =
       hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::SMEM);
   if (e != hipSuccess) return e;
@@ -710,20 +795,306 @@ hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v
   // One 8-wave workgroup per head (two waves per SIMD) when that fills the GPU,
   // else two 4-wave workgroups per head for more parallel chains.
   if ((long)sh.B * sh.Hv >= 160)
-    return launch_seq<TQ, TG, 8>(sh, q, k, v, g, beta, TPws, S0, o, ST, nchunks, st);
-  return launch_seq<TQ, TG, 4>(sh, q, k, v, g, beta, TPws, S0, o, ST, nchunks, st);
+    return launch_seq<TQ, TG, 8, false>(sh, q, k, v, g, beta, TPws, S0, o, ST, nchunks, st);
+  return launch_seq<TQ, TG, 4, false>(sh, q, k, v, g, beta, TPws, S0, o, ST, nchunks, st);
+}
+
+// ============================================================================
+// kda_prep: the state-independent work of the key-channel gate, per
+// (batch, value head, chunk)
+// ============================================================================
+// The decay is a vector per token, so e^{gamma_r - gamma_s} sits inside the
+// sum over key channels of A and P:
+//     A[r][s] = beta_r sum_j k_rj k_sj e^{gamma_rj - gamma_sj}    (s < r)
+//     P[r][s] =        sum_j q_rj k_sj e^{gamma_rj - gamma_sj}    (s <= r)
+// Each block row of 16 rows is a product of decay-scaled K (or Q) and K about
+// a reference token, on the matrix cores (details where A and P are formed).
+constexpr int GST = DK + 4;                              // gamma row stride (fp32)
+constexpr int KP_OFF_K = 0;                              // [C][KST] fp16
+constexpr int KP_OFF_Q = KP_OFF_K + C * KST * 2;         // [C][KST] fp16
+constexpr int KP_OFF_G = KP_OFF_Q + C * KST * 2;         // [C][GST] fp32 (g, then gamma)
+constexpr int KP_OFF_B = KP_OFF_G + C * GST * 4;         // beta [C] fp32
+constexpr int KP_SMEM = KP_OFF_B + C * 4;
+// once A and P are in registers, the matrices of the inverse reuse K and Q
+constexpr int KP_OFF_T = 0;
+constexpr int KP_OFF_P = KP_OFF_T + C * CST * 2;
+constexpr int KP_OFF_AO = KP_OFF_P + C * CST * 2;
+constexpr int KP_OFF_AD = KP_OFF_AO + C * CST * 2;
+static_assert(KP_OFF_AD + 4 * 16 * DST * 4 <= KP_OFF_G, "inverse matrices overlap gamma");
+
+// Eight consecutive channels of row `row` at kset(g4, kk) of a row-major fp32 matrix.
+__device__ __forceinline__ void perm_row_f32(const float *M, int st, int row, int kk, int g4, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4 *>(M + row * st + 32 * kk + 4 * g4);
+  const float4 b = *reinterpret_cast<const float4 *>(M + row * st + 32 * kk + 16 + 4 * g4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+template <typename TQ, typename TG>
+__global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(
+    const TQ *__restrict__ q, const TQ *__restrict__ k, const TG *__restrict__ g,
+    const TG *__restrict__ beta, uint4 *__restrict__ ws, int T, int Hk, int Hv, int nchunks) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  _Float16 *sK = reinterpret_cast<_Float16 *>(smem + KP_OFF_K);
+  _Float16 *sQ = reinterpret_cast<_Float16 *>(smem + KP_OFF_Q);
+  float *sG = reinterpret_cast<float *>(smem + KP_OFF_G);
+  float *sB = reinterpret_cast<float *>(smem + KP_OFF_B);
+  _Float16 *sT = reinterpret_cast<_Float16 *>(smem + KP_OFF_T);
+  _Float16 *sP = reinterpret_cast<_Float16 *>(smem + KP_OFF_P);
+  _Float16 *sAo = reinterpret_cast<_Float16 *>(smem + KP_OFF_AO);
+  float *sAd = reinterpret_cast<float *>(smem + KP_OFF_AD);
+
+  const int c = blockIdx.x, bh = blockIdx.y;  // bh = b * Hv + h
+  const int b = bh / Hv, h = bh % Hv, kh = h / (Hv / Hk);
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, g4 = l >> 4, ln = l & 15;
+  const int t0 = c * C, n = min(C, T - t0);
+  const size_t bt0 = (size_t)b * T + t0;
+  uint4 *wc = ws + ((size_t)bh * nchunks + c) * KDA_CHUNK_U4;
+
+  // K, Q, g and beta of the chunk; rows past the end are zero (so gamma stays flat there)
+  {
+    constexpr int GW = sizeof(TG) == 4 ? 2 : 1;  // 16-byte pieces per 8 gate values
+    uint4 uk[4], uq[4], ug[4][GW];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int row = min((tid >> 4) + 16 * it, n - 1);
+      const size_t off = ((bt0 + row) * Hk + kh) * DK + (tid & 15) * 8;
+      const size_t goff = ((bt0 + row) * Hv + h) * DK + (tid & 15) * 8;
+      uk[it] = *reinterpret_cast<const uint4 *>(k + off);
+      uq[it] = *reinterpret_cast<const uint4 *>(q + off);
+#pragma unroll
+      for (int u = 0; u < GW; ++u) ug[it][u] = *reinterpret_cast<const uint4 *>(g + goff + 4 * u);
+    }
+    const TG braw = beta[(bt0 + min(tid & 63, n - 1)) * Hv + h];
+    __builtin_amdgcn_sched_barrier(0);
+    const half8 hz = {};
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int row = (tid >> 4) + 16 * it;
+      const bool ok = row < n;
+      *reinterpret_cast<half8 *>(sK + row * KST + (tid & 15) * 8) = ok ? to_half8(uk[it], TQ{}) : hz;
+      *reinterpret_cast<half8 *>(sQ + row * KST + (tid & 15) * 8) = ok ? to_half8(uq[it], TQ{}) : hz;
+      float gv[8];
+      if constexpr (sizeof(TG) == 4) {
+        const float4 a = __builtin_bit_cast(float4, ug[it][0]), bq = __builtin_bit_cast(float4, ug[it][1]);
+        gv[0] = a.x; gv[1] = a.y; gv[2] = a.z; gv[3] = a.w;
+        gv[4] = bq.x; gv[5] = bq.y; gv[6] = bq.z; gv[7] = bq.w;
+      } else {
+        const uint32_t wd[4] = {ug[it][0].x, ug[it][0].y, ug[it][0].z, ug[it][0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          gv[2 * i] = __uint_as_float(wd[i] << 16);
+          gv[2 * i + 1] = __uint_as_float(wd[i] & 0xFFFF0000u);
+        }
+      }
+      float *gp = sG + row * GST + (tid & 15) * 8;
+      *reinterpret_cast<float4 *>(gp) = ok ? make_float4(gv[0], gv[1], gv[2], gv[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4 *>(gp + 4) = ok ? make_float4(gv[4], gv[5], gv[6], gv[7]) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (tid < C) sB[tid] = tid < n ? to_f32(braw) : 0.f;
+  }
+  lds_barrier();
+
+  // gamma: inclusive prefix over the rows, per channel (two halves of 32 rows)
+  {
+    const int ch = tid & 127, r0 = (tid >> 7) * 32;
+    float x = 0.f;
+#pragma unroll 8
+    for (int r = r0; r < r0 + 32; ++r) {
+      x += sG[r * GST + ch];
+      sG[r * GST + ch] = x;
+    }
+  }
+  lds_barrier();
+  if (tid >= 128) {
+    const int ch = tid & 127;
+    const float base = sG[31 * GST + ch];
+#pragma unroll 8
+    for (int r = 32; r < 64; ++r) sG[r * GST + ch] += base;
+  }
+  lds_barrier();
+
+  // operands of the sequential pass: K o e^gamma, Q o e^gamma, K o e^{gamma_n - gamma}
+  // (gamma_n = gamma of the chunk's last token); beta; Gamma_n = e^{gamma_n}
+  {
+    const float *gl = sG + (n - 1) * GST;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int e = tid + kThreads * it;
+      const int row = e >> 4, c8 = (e & 15) * 8;
+      const half8 kv = *reinterpret_cast<const half8 *>(sK + row * KST + c8);
+      const half8 qv = *reinterpret_cast<const half8 *>(sQ + row * KST + c8);
+      half8 kg, qg, kd;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float gam = sG[row * GST + c8 + j];
+        const float eg = __expf(gam), ed = __expf(gl[c8 + j] - gam);
+        kg[j] = (_Float16)((float)kv[j] * eg);
+        qg[j] = (_Float16)((float)qv[j] * eg);
+        kd[j] = (_Float16)((float)kv[j] * ed);
+      }
+      wc[KDA_KG + e] = __builtin_bit_cast(uint4, kg);
+      wc[KDA_QG + e] = __builtin_bit_cast(uint4, qg);
+      wc[KDA_KD + e] = __builtin_bit_cast(uint4, kd);
+    }
+    float *wsc = reinterpret_cast<float *>(wc + KDA_SC);
+    if (tid < C) wsc[tid] = sB[tid];
+    if (tid < DK) wsc[C + tid] = __expf(gl[tid]);
+  }
+
+  // A and P for block row R = w (tiles S = 0..R), into registers.  Reference
+  // token p = 16 R (the block row's first): e^{gamma_r - gamma_s} =
+  // e^{gamma_r - gamma_p} e^{gamma_p - gamma_s}.
+  //  * tiles S < R: s < p <= r, so both factors are <= 1; fp16 operands on the
+  //    16x16x32 matrix cores (a factor that underflows belongs to a product
+  //    that is itself that small);
+  //  * tile S = R: e^{gamma_p - gamma_s} >= 1 for s > p, so fp32 operands on
+  //    the 16x16x4 fp32 matrix cores; if a factor would overflow fp32 (a decay
+  //    of e^-80 within 16 tokens), the wave computes that tile term by term.
+  // The lane (g4, ln) holds row 16 R + ln at the channels kset(g4, kk), in
+  // the same order for the fp16 and the fp32 products.
+  const int R = w, p = 16 * R;
+  float4v accA[4], accP[4];
+  {
+    half8 kl[4], ql[4];
+    {
+      float4v ad = {0.f, 0.f, 0.f, 0.f}, pd = {0.f, 0.f, 0.f, 0.f};
+      bool ok = true;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        float gr[8], gp[8];
+        perm_row_f32(sG, GST, 16 * R + ln, kk, g4, gr);
+        perm_row_f32(sG, GST, p, kk, g4, gp);
+        const half8 kv = perm_row(sK, KST, 16 * R + ln, kk, g4);
+        const half8 qv = perm_row(sQ, KST, 16 * R + ln, kk, g4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float f = __expf(gr[e] - gp[e]), fi = __expf(gp[e] - gr[e]);
+          const float kf = (float)kv[e] * f, qf = (float)qv[e] * f, ki = (float)kv[e] * fi;
+          ok = ok && fi <= 1.0e30f;
+          kl[kk][e] = (_Float16)kf;
+          ql[kk][e] = (_Float16)qf;
+          ad = __builtin_amdgcn_mfma_f32_16x16x4f32(kf, ki, ad, 0, 0, 0);
+          pd = __builtin_amdgcn_mfma_f32_16x16x4f32(qf, ki, pd, 0, 0, 0);
+        }
+      }
+      if (__any(!ok)) {
+        // exact diagonal tile: lane (g4, ln) holds r = 16 R + 4 g4 + ii, s = 16 R + ln
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int r = 16 * R + 4 * g4 + ii, s_ = 16 * R + ln;
+          float a = 0.f, pp = 0.f;
+          if (s_ <= r) {
+            for (int j = 0; j < DK; ++j) {
+              const float e = __expf(sG[r * GST + j] - sG[s_ * GST + j]);
+              const float ks = (float)sK[s_ * KST + j];
+              a += (float)sK[r * KST + j] * ks * e;
+              pp += (float)sQ[r * KST + j] * ks * e;
+            }
+          }
+          ad[ii] = a;
+          pd[ii] = pp;
+        }
+      }
+#pragma unroll
+      for (int S = 0; S < 4; ++S) {
+        if (S == R) {
+          accA[S] = ad;
+          accP[S] = pd;
+        }
+      }
+    }
+#pragma unroll
+    for (int S = 0; S < 3; ++S) {
+      if (S < R) {
+        float4v aa = {0.f, 0.f, 0.f, 0.f}, ap = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          float gs[8], gp[8];
+          perm_row_f32(sG, GST, 16 * S + ln, kk, g4, gs);
+          perm_row_f32(sG, GST, p, kk, g4, gp);
+          const half8 kv = perm_row(sK, KST, 16 * S + ln, kk, g4);
+          half8 ks;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ks[e] = (_Float16)((float)kv[e] * __expf(gp[e] - gs[e]));
+          aa = mfma32(kl[kk], ks, aa);
+          ap = mfma32(ql[kk], ks, ap);
+        }
+        accA[S] = aa;
+        accP[S] = ap;
+      }
+    }
+  }
+  lds_barrier();  // K and Q are no longer read: T, P, A take their place
+
+  // A (diagonal blocks fp32 strictly lower, blocks below fp16) and P (lower incl. diagonal)
+  {
+    const int r0 = 16 * R + 4 * g4;
+    float br[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) br[ii] = sB[r0 + ii];
+#pragma unroll
+    for (int S = 0; S < 4; ++S) {
+      if (S > R) continue;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int r = r0 + ii, s_ = 16 * S + ln;
+        if (S == R) {
+          sAd[(R * 16 + 4 * g4 + ii) * DST + ln] = s_ < r ? br[ii] * accA[S][ii] : 0.f;
+          sP[r * CST + s_] = (_Float16)(s_ <= r ? accP[S][ii] : 0.f);
+        } else {
+          sAo[r * CST + s_] = (_Float16)(br[ii] * accA[S][ii]);
+          sP[r * CST + s_] = (_Float16)accP[S][ii];
+        }
+      }
+    }
+    const int rr = tid >> 4, cc = tid & 15;
+    sT[rr * CST + 16 + cc] = (_Float16)0.f;
+    sT[(32 + rr) * CST + 48 + cc] = (_Float16)0.f;
+    sP[rr * CST + 16 + cc] = (_Float16)0.f;
+    sP[(32 + rr) * CST + 48 + cc] = (_Float16)0.f;
+  }
+  invert_store(sAd, sAo, sT, sP, wc, w, l);
+}
+
+template <typename TQ, typename TG>
+hipError_t launch_kda_t(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
+                        const void *beta, const float *S0, float *o, float *ST, void *ws,
+                        hipStream_t st) {
+  const int nchunks = (sh.T + C - 1) / C;
+  uint4 *wsu = (uint4 *)ws;
+  auto prep = kda_prep_kernel<TQ, TG>;
+  hipError_t e =
+      hipFuncSetAttribute((const void *)prep, hipFuncAttributeMaxDynamicSharedMemorySize, KP_SMEM);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(prep, dim3(nchunks, sh.B * sh.Hv), dim3(kThreads), KP_SMEM, st, (const TQ *)q,
+                     (const TQ *)k, (const TG *)g, (const TG *)beta, wsu, sh.T, sh.Hk, sh.Hv, nchunks);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // The decayed K, Q and the state-update K all live in LDS here, so the
+  // sequential pass uses 4-wave workgroups (64 value rows each).
+  return launch_seq<TQ, TG, 4, true>(sh, q, k, v, g, beta, wsu, S0, o, ST, nchunks, st);
 }
 
 }  // namespace
 
 size_t chunk_mfma_workspace(const Shape &sh) {
   const size_t nchunks = (size_t)(sh.T + C - 1) / C;
-  return (size_t)sh.B * sh.Hv * nchunks * 2 * FRAGS_BYTES;
+  const size_t per_chunk = sh.key_gate ? (size_t)KDA_CHUNK_U4 * 16 : 2 * FRAGS_BYTES;
+  return (size_t)sh.B * sh.Hv * nchunks * per_chunk;
 }
 
 hipError_t launch_chunk_mfma(const Shape &sh, const void *q, const void *k, const void *v,
                              const void *g, const void *beta, const float *S0, float *o, float *ST,
                              void *ws, hipStream_t st) {
+  if (sh.key_gate) {
+    if (sh.qkv == DType::BF16)
+      return sh.gate_t == DType::F32
+                 ? launch_kda_t<bf16_t, float>(sh, q, k, v, g, beta, S0, o, ST, ws, st)
+                 : launch_kda_t<bf16_t, bf16_t>(sh, q, k, v, g, beta, S0, o, ST, ws, st);
+    return sh.gate_t == DType::F32 ? launch_kda_t<f16_t, float>(sh, q, k, v, g, beta, S0, o, ST, ws, st)
+                                   : launch_kda_t<f16_t, bf16_t>(sh, q, k, v, g, beta, S0, o, ST, ws, st);
+  }
   if (sh.qkv == DType::BF16)
     return sh.gate_t == DType::F32
                ? launch_t<bf16_t, float>(sh, q, k, v, g, beta, S0, o, ST, ws, st)

@@ -87,11 +87,11 @@ gdn_status check_ptrs(const char *const *names, const void *const *ptrs, int n) 
   return GDN_OK;
 }
 
-// The matrix-core path: 16-bit q/k/v, head gate, dk = dv = 128, chunk 64.
+// The matrix-core path: 16-bit q/k/v, either gate, dk = dv = 128, chunk 64.
 bool uses_matrix_cores(const gdn_desc *d) {
   const bool mc_mode = (d->qkv_dtype == GDN_BF16 || d->qkv_dtype == GDN_F16) &&
                        (d->gate_dtype == GDN_BF16 || d->gate_dtype == GDN_F32);
-  return mc_mode && d->gate == GDN_GATE_HEAD && d->dk == 128 && d->dv == 128 && d->chunk == 64;
+  return mc_mode && d->dk == 128 && d->dv == 128 && d->chunk == 64;
 }
 
 gdn_status launched(hipError_t e, const char *what) {
@@ -175,14 +175,14 @@ gdn_status gdn_fwd_chunked(const gdn_desc *d, const void *q, const void *k, cons
                 "dtype combination not built (qkv %d, gate %d): use fp32/fp32, or bf16|fp16 with "
                 "bf16|fp32 gates",
                 d->qkv_dtype, d->gate_dtype);
-  bool use_mfma = false;
-  if (mc_mode && !sh.key_gate) {
-    if (d->dk != 128 || d->dv != 128 || d->chunk != 64)
-      return fail(GDN_E_UNSUPPORTED,
-                  "matrix-core mode supports dk = dv = 128 and chunk = 64 (got %d, %d, %d)", d->dk,
-                  d->dv, d->chunk);
-    use_mfma = true;
-  } else {
+  // 16-bit inputs run on the matrix cores at dk = dv = 128, chunk 64; the
+  // key-channel gate at other sizes runs on the fp32 vector path.
+  const bool use_mfma = uses_matrix_cores(d);
+  if (mc_mode && !use_mfma && !sh.key_gate)
+    return fail(GDN_E_UNSUPPORTED,
+                "matrix-core mode supports dk = dv = 128 and chunk = 64 (got %d, %d, %d)", d->dk,
+                d->dv, d->chunk);
+  if (!use_mfma) {
     if (!pow2_16_128(d->dk) || !pow2_16_128(d->dv))
       return fail(GDN_E_UNSUPPORTED, "dk, dv must be in {16,32,64,128} (got %d, %d)", d->dk, d->dv);
     if (d->chunk != 16 && d->chunk != 32 && d->chunk != 64)

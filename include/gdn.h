@@ -109,10 +109,12 @@ gdn_status gdn_prologue(const gdn_desc *d, int32_t x_dtype, const void *xq,
 
 /*
  * Device workspace bytes gdn_fwd_chunked needs for `d` (0 = none; then the
- * workspace pointer may be NULL).  The matrix-core path keeps two 64 x 64
- * lower-triangular fp16 matrices per (batch, value head, 64-token chunk)
- * there, the triangular inverse and the decayed masked q.k products:
- * 12288 bytes each triple.
+ * workspace pointer may be NULL).  The matrix-core path (16-bit q/k/v,
+ * dk = dv = 128, chunk 64) keeps per (batch, value head, 64-token chunk):
+ *   head gate: two 64 x 64 lower-triangular fp16 matrices, the triangular
+ *     inverse and the decayed masked q.k products: 12288 bytes;
+ *   key-channel gate: those two, the decayed k, q and the state-update k
+ *     (64 x 128 fp16 each), beta and the chunk's total decay: 62208 bytes.
  * Returns 0 for an invalid description.  The caller owns the workspace; it
  * is scratch between calls and must not be shared by concurrent calls.
  */

@@ -32,11 +32,13 @@ def oracle_inputs(inp):
     return [inp[n].f32() for n in ("q", "k", "v", "g", "beta")]
 
 
-def run_case(wl, label, S0_alias=False):
+def run_case(wl, label, S0_alias=False, gates_f32=False):
     inp = make_prefill(wl)
     say("%s: B=%d T=%d Hk=%d Hv=%d d=%d/%d C=%d %s gate=%s S0=%s" %
         (label, wl.B, wl.T, wl.Hk, wl.Hv, wl.dk, wl.dv, wl.chunk, wl.dtype, wl.gate, wl.s0_std))
     args = gpu_inputs(inp)
+    if gates_f32:      # the same gate values, stored as fp32
+        args[3], args[4] = args[3].float(), args[4].float()
     S0 = None if inp["S0"] is None else to_torch(inp["S0"])
     o = torch.full((wl.B, wl.T, wl.Hv, wl.dv), float("nan"), device="cuda")   # unwritten -> NaN
     ST = S0 if (S0_alias and S0 is not None) else torch.full((wl.B, wl.Hv, wl.dv, wl.dk), float("nan"),
@@ -92,6 +94,28 @@ def test_bf16_small_variants():
     run_case(SMALL.with_(T=130), "bf16 S_T aliases S0", S0_alias=True)
     run_case(SMALL.with_(Hk=6, Hv=6, T=100), "bf16 no grouping")
     run_case(KDA_PREFILL.with_(B=1, T=150, Hk=2, Hv=2), "bf16 key gate small")
+
+
+# ---------------------------------------------------------------- key-channel gate, matrix cores
+KDA_SMALL = KDA_PREFILL.with_(B=2, T=150, Hk=1, Hv=3, s0_std=0.05)
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 150])
+def test_key_gate_small(T):
+    run_case(KDA_SMALL.with_(T=T), "key gate T=%d" % T)
+
+
+def test_key_gate_variants():
+    run_case(KDA_SMALL.with_(T=130), "key gate S_T aliases S0", S0_alias=True)
+    run_case(KDA_SMALL.with_(T=200, g_mu=0.0), "key gate moderate decay")
+    # per-token decay ~ e^-2 per channel: the factored A/P products would leave
+    # the fp16 range, so every block row takes the exact path
+    run_case(KDA_SMALL.with_(T=200, g_mu=-2.0), "key gate strong decay")
+    # ~e^-7 per token: across 16 tokens the fp32 factors of the diagonal
+    # tiles would overflow, so those tiles are computed term by term
+    run_case(KDA_SMALL.with_(T=130, g_mu=-7.0), "key gate extreme decay")
+    run_case(KDA_SMALL.with_(T=100), "key gate fp32 gates", gates_f32=True)
+    run_case(KDA_SMALL.with_(T=100, Hk=3, Hv=3, s0_std=0.0), "key gate no grouping S0=0")
 
 
 def test_bf16_conv_small():
