@@ -13,6 +13,9 @@ kernels run on):
                 launches) against the dense fp16 matrix-core peak;
   kernels       prologue and decode against the HBM peak;
   decode        steps/s of the batched-decode workload (B 256, 1000 steps);
+  workloads     the chunked forward on the long-prefill workload (B 1, T 65536,
+                S0 given, slow decay) and on the per-key-channel-gate workload
+                (B 2, 32 heads, T 8192), tokens/s and fractions of both roofs;
   cpu_baseline  the fp64 oracle on the host cores on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -92,8 +95,8 @@ def main():
     import torch
 
     import gated_delta_rule_02_amd as gdn
-    from gdn_inputs import BATCHED_DECODE, PREFILL_CONV, decode_tokens_device, make_decode_token, \
-        make_prefill, make_state, to_torch
+    from gdn_inputs import BATCHED_DECODE, KDA_PREFILL, LONG_PREFILL, PREFILL_CONV, decode_tokens_device, \
+        make_decode_token, make_prefill, make_state, prefill_device, to_torch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
@@ -202,10 +205,41 @@ def main():
     log("decode %.1f us/step, %.0f steps/s, %.0f GB/s" % (t_dec * 1e6, 1 / t_dec, bytes_dec / t_dec / 1e9))
     del toks, S, S_init
 
+    # ------------------------------------------------------------------ other prefill workloads
+    extra = {}
+    for key, xwl in (("long_prefill", LONG_PREFILL), ("key_gate_prefill", KDA_PREFILL)):
+        log("workload: %s" % xwl.name)
+        xi = prefill_device(xwl, dev)
+        xo = torch.empty((xwl.B, xwl.T, xwl.Hv, xwl.dv), dtype=torch.float32, device=dev)
+        xst = torch.empty((xwl.B, xwl.Hv, xwl.dv, xwl.dk), dtype=torch.float32, device=dev)
+        gate = gdn.GATE_HEAD if xwl.gate == "head" else gdn.GATE_KEY_CHANNEL
+        xd = gdn.make_desc(xwl.B, xwl.T, xwl.Hk, xwl.Hv, xwl.dk, xwl.dv, xwl.chunk, gdn.BF16, gdn.BF16, gate)
+        xws = torch.empty(L.gdn_fwd_workspace_bytes(xd), dtype=torch.uint8, device=dev)
+
+        def xrun(xi=xi, xd=xd, xo=xo, xst=xst, xws=xws):
+            gdn.check(L.gdn_fwd_chunked(ctypes.byref(xd), P(xi["q"]), P(xi["k"]), P(xi["v"]), P(xi["g"]),
+                                        P(xi["beta"]), None if xi["S0"] is None else P(xi["S0"]),
+                                        P(xo), P(xst), P(xws), xws.numel(), s_ptr))
+
+        xrun()
+        torch.cuda.synchronize()
+        tx = time_events(xrun, 5, stream)
+        ntok = xwl.B * xwl.T
+        gdim = xwl.dk if xwl.gate == "key" else 1
+        xbytes = (2 * ntok * xwl.Hk * xwl.dk + ntok * xwl.Hv * xwl.dv + ntok * xwl.Hv * (gdim + 1)) * 2 \
+            + ntok * xwl.Hv * xwl.dv * 4 + (2 if xi["S0"] is not None else 1) * xwl.B * xwl.Hv * xwl.dv * xwl.dk * 4
+        xfl = FLOPS_PER_TOKEN_HEAD * ntok * xwl.Hv
+        extra[key] = {"workload": xwl.name, "us_per_call": tx * 1e6, "tokens_per_s": ntok / tx,
+                      "mfma_tflops": xfl / tx / 1e12, "mfma_frac": xfl / tx / 1e12 / PEAK_F16_TFLOPS,
+                      "hbm_gbs_algorithmic": xbytes / tx / 1e9,
+                      "hbm_frac_algorithmic": xbytes / tx / 1e9 / PEAK_HBM_GBS}
+        log("%s: %.1f us, %.3e tokens/s, %.1f TFLOP/s" % (key, tx * 1e6, ntok / tx, xfl / tx / 1e12))
+        del xi, xo, xst, xws
+
     # ------------------------------------------------------------------ CPU baseline (oracle)
     import oracle
     nthreads = min(os.cpu_count() or 1, 16)
-    sample_b = [0, 1]
+    sample_b = list(range(B))
     log("cpu baseline: fp64 oracle, prologue + recurrence for batch elements %s (%d chains), %d threads" %
         (sample_b, len(sample_b) * Hv, nthreads))
     t0 = time.perf_counter()
@@ -249,9 +283,10 @@ def main():
         },
         "decode": {"workload": "batched decode: B 256, 16/48 heads, d 128, fp32 state, %d steps" % nsteps,
                    "steps_per_s": 1.0 / t_dec, "tokens_per_s": dwl.B / t_dec},
+        "workloads": extra,
         "cpu_baseline": {"value": cpu_tokens_per_s, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
-                         "sample": "fp64 prologue + token recurrence for batch elements 0-1 of the same "
-                                   "workload (96 of 192 chains, all 4096 tokens)",
+                         "sample": "fp64 prologue + token recurrence over the whole prefill workload "
+                                   "(4 x 4096 tokens, all 192 chains); the decode step is not included",
                          "seconds": t_cpu},
     }
     print(json.dumps(line), flush=True)

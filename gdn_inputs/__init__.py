@@ -227,3 +227,32 @@ def decode_tokens_device(wl: Workload, steps: int, device="cuda", first_step: in
         outs["beta"].append(torch.sigmoid(bx).to(dt))
         outs["g"].append(torch.nn.functional.logsigmoid(gx).to(dt))
     return {n: torch.stack(x).contiguous() for n, x in outs.items()}
+
+
+def prefill_device(wl: Workload, device="cuda"):
+    """Inputs of one forward call drawn on the device (fast path for timing the
+    large workloads; the parity tests use make_prefill): q, k [B,T,Hk,dk] unit
+    rows, v [B,T,Hv,dv] ~ N(0,1), beta = sigmoid(N(0,1)), g = logsigmoid(N(g_mu,1))
+    ([B,T,Hv] or [B,T,Hv,dk]), rounded to the workload dtype; S0 ~ N(0, s0_std)
+    fp32 or None.  Seeded with the workload seed on torch's device generator.
+    Workloads with the conv prologue are not covered (their raw inputs differ)."""
+    import torch
+    assert not wl.conv
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device=device)
+    gen.manual_seed((wl.seed * 1_000_003) & 0x7FFFFFFFFFFFFFFF)
+    B, T = wl.B, wl.T
+
+    def unit(shape):
+        x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+        return (x / x.norm(dim=-1, keepdim=True)).to(dt)
+
+    out = {"q": unit((B, T, wl.Hk, wl.dk)), "k": unit((B, T, wl.Hk, wl.dk))}
+    out["v"] = torch.randn((B, T, wl.Hv, wl.dv), generator=gen, device=device, dtype=torch.float32).to(dt)
+    out["beta"] = torch.sigmoid(torch.randn((B, T, wl.Hv), generator=gen, device=device)).to(dt)
+    gshape = (B, T, wl.Hv) if wl.gate == "head" else (B, T, wl.Hv, wl.dk)
+    out["g"] = torch.nn.functional.logsigmoid(
+        torch.randn(gshape, generator=gen, device=device) + wl.g_mu).to(dt)
+    out["S0"] = None if wl.s0_std == 0.0 else \
+        torch.randn((B, wl.Hv, wl.dv, wl.dk), generator=gen, device=device) * wl.s0_std
+    return out
