@@ -10,11 +10,13 @@
 // are reduced from the old row in one pass: the state is read once and written
 // once, which is all the HBM traffic this step needs.
 //
-// Mapping: a row of dk fp32 values is held by dk/8 lanes, 8 values each (two
-// 16-byte loads).  A 256-thread block covers 256/(dk/8) rows per pass and NR
-// passes; every thread issues all NR row loads before any arithmetic so that
-// NR*32 bytes per lane are in flight.  Row dot products are reduced across the
-// dk/8 lanes of the row with xor shuffles.
+// Mapping: a row of dk fp32 values is held by dk/8 lanes, 8 values each: lane
+// j of the row holds columns 4j .. 4j+3 and dk/2 + 4j .. dk/2 + 4j+3, so each
+// of its two 16-byte accesses is part of one contiguous run across the lanes.
+// A 256-thread block covers 256/(dk/8) rows (32 at dk = 128); many small
+// blocks keep enough loads in flight.  The state is streamed with
+// non-temporal loads and stores: it is touched once per step.  Row dot
+// products are reduced across the dk/8 lanes of the row with xor shuffles.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -22,6 +24,28 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
+
+// Four consecutive values widened to fp32.
+__device__ __forceinline__ void load4(const float *p, float *x) {
+  const float4 a = *reinterpret_cast<const float4 *>(p);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+}
+__device__ __forceinline__ void load4(const f16_t *p, float *x) {
+  const half4 h = *reinterpret_cast<const half4 *>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = (float)h[i];
+}
+__device__ __forceinline__ void load4(const bf16_t *p, float *x) {
+  const uint2 u = *reinterpret_cast<const uint2 *>(p);
+  x[0] = __uint_as_float(u.x << 16); x[1] = __uint_as_float(u.x & 0xFFFF0000u);
+  x[2] = __uint_as_float(u.y << 16); x[3] = __uint_as_float(u.y & 0xFFFF0000u);
+}
+// Columns c0 .. c0+3 and DK/2 + c0 .. DK/2 + c0+3 of a row.
+template <int DK, typename T>
+__device__ __forceinline__ void load_cols(const T *row, int c0, float (&x)[8]) {
+  load4(row + c0, x);
+  load4(row + DK / 2 + c0, x + 4);
+}
 
 template <typename TQ, typename TG, bool KEYGATE, int DK, int NR>
 __global__ __launch_bounds__(kThreads) void decode_kernel(
@@ -33,14 +57,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   const int b = blockIdx.z, h = blockIdx.y;
   const int kh = h / (Hv / Hk);
   const int sub = threadIdx.x % LPR;
-  const int c0 = sub * 8;
+  const int c0 = sub * 4;
   const size_t bh = (size_t)b * Hv + h;
 
   float kk[8], qq[8], al[8];
-  load8(k + ((size_t)b * Hk + kh) * DK + c0, kk);
-  load8(q + ((size_t)b * Hk + kh) * DK + c0, qq);
+  load_cols<DK>(k + ((size_t)b * Hk + kh) * DK, c0, kk);
+  load_cols<DK>(q + ((size_t)b * Hk + kh) * DK, c0, qq);
   if constexpr (KEYGATE) {
-    load8(g + bh * DK + c0, al);
+    load_cols<DK>(g + bh * DK, c0, al);
 #pragma unroll
     for (int j = 0; j < 8; ++j) al[j] = __expf(al[j]);
   } else {
@@ -56,15 +80,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
 
   const int row0 = blockIdx.x * (NR * RPP) + threadIdx.x / LPR;
   float *Sbh = S + bh * (size_t)dv * DK;
-  float s[NR][8];
+  float4v s[NR][2];
 #pragma unroll
   for (int p = 0; p < NR; ++p) {
     const int i = row0 + p * RPP;
     if (i < dv) {
-      load8(Sbh + (size_t)i * DK + c0, s[p]);
+      const float *r = Sbh + (size_t)i * DK + c0;
+      s[p][0] = __builtin_nontemporal_load(reinterpret_cast<const float4v *>(r));
+      s[p][1] = __builtin_nontemporal_load(reinterpret_cast<const float4v *>(r + DK / 2));
     } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) s[p][j] = 0.f;
+      s[p][0] = s[p][1] = float4v{0.f, 0.f, 0.f, 0.f};
     }
   }
 #pragma unroll
@@ -73,17 +98,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     float a = 0.f, c = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      s[p][j] *= al[j];
-      a += s[p][j] * kk[j];
-      c += s[p][j] * qq[j];
+      const float x = s[p][j >> 2][j & 3] * al[j];
+      s[p][j >> 2][j & 3] = x;
+      a += x * kk[j];
+      c += x * qq[j];
     }
     a = group_sum<LPR>(a);
     c = group_sum<LPR>(c);
     if (i < dv) {
       const float u = bt * (to_f32(v[bh * dv + i]) - a);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) s[p][j] += u * kk[j];
-      store8(Sbh + (size_t)i * DK + c0, s[p]);
+      for (int j = 0; j < 8; ++j) s[p][j >> 2][j & 3] += u * kk[j];
+      float *r = Sbh + (size_t)i * DK + c0;
+      __builtin_nontemporal_store(s[p][0], reinterpret_cast<float4v *>(r));
+      __builtin_nontemporal_store(s[p][1], reinterpret_cast<float4v *>(r + DK / 2));
       if (sub == 0) o[bh * dv + i] = c + u * kq;
     }
   }
@@ -92,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
 template <typename TQ, typename TG, bool KEYGATE, int DK>
 hipError_t launch_dk(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
                      const void *beta, float *S, float *o, hipStream_t st) {
-  constexpr int NR = 4;
+  constexpr int NR = 1;
   constexpr int rows_per_block = NR * (kThreads / (DK / 8));
   dim3 grid((sh.dv + rows_per_block - 1) / rows_per_block, sh.Hv, sh.B);
   hipLaunchKernelGGL((decode_kernel<TQ, TG, KEYGATE, DK, NR>), grid, dim3(kThreads), 0, st,
