@@ -88,11 +88,24 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// x plus the value of another lane of its 16-lane row, moved by DPP: ctrl is
+// a gfx9 DPP control (quad permutation, row mirror, row half-mirror).
+template <int CTRL> __device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
 // Sum over an aligned group of G lanes (G a power of two <= 64); every lane
-// of the group receives the total.
+// of the group receives the total.  Groups of up to 16 lanes reduce with DPP
+// moves inside the row (quad swaps, then the half-row and row mirrors, each
+// pairing lanes whose partial sums cover disjoint halves); wider groups add
+// cross-row shuffles.
 template <int G> __device__ __forceinline__ float group_sum(float x) {
+  if constexpr (G >= 2) x = dpp_add<0xB1>(x);    // quad_perm [1,0,3,2]
+  if constexpr (G >= 4) x = dpp_add<0x4E>(x);    // quad_perm [2,3,0,1]
+  if constexpr (G >= 8) x = dpp_add<0x141>(x);   // row_half_mirror
+  if constexpr (G >= 16) x = dpp_add<0x140>(x);  // row_mirror
 #pragma unroll
-  for (int m = G / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  for (int m = 16; m < G; m <<= 1) x += __shfl_xor(x, m, 64);
   return x;
 }
 

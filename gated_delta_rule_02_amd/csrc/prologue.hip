@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const float yv = w0[c] * xm3[c] + w1[c] * xm2[c] + w2[c] * xm1[c] + w3[c] * xs[u][c];
-        z[c] = yv / (1.0f + __expf(-yv));
+        z[c] = yv * __builtin_amdgcn_rcpf(1.0f + __expf(-yv));   // SiLU; rcp is exact to 1 ulp
         ss += z[c] * z[c];
         xm3[c] = xm2[c];
         xm2[c] = xm1[c];
