@@ -121,16 +121,11 @@ __device__ __forceinline__ half8 pack_pair(float4v a, float4v b) {
                (_Float16)b[0], (_Float16)b[1], (_Float16)b[2], (_Float16)b[3]};
 }
 
-// Inclusive prefix of the chunk's log decay (wave 0: lane = token) and the
-// per-token scalars: gamma, Gamma = e^gamma, beta, beta Gamma, e^{gamma_n - gamma}.
+// Inclusive prefix of the chunk's log decay (one full wave: lane = token) and
+// the per-token scalars: gamma, Gamma = e^gamma, beta, beta Gamma, e^{gamma_n - gamma}.
 __device__ __forceinline__ void chunk_scalars(float g, float beta, float *sc, int lane) {
-  float x = g;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  const float gC = __shfl(x, 63, 64);
+  const float x = wave_prefix_sum(g);
+  const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
   const float eg = __expf(x);
   sc[0 * C + lane] = x;
   sc[1 * C + lane] = eg;
@@ -167,8 +162,7 @@ __device__ __forceinline__ void invert_store(const float *sAd, const _Float16 *s
         const int m = 4 * j + sub;
         if (m < r) part += Ad[r * DST + m] * t[j];
       }
-      part += __shfl_xor(part, 1, 64);
-      part += __shfl_xor(part, 2, 64);
+      part = group_sum<4>(part);
       const float val = (r == cc) ? 1.f : -part;
       if ((r & 3) == sub) t[r >> 2] = val;
     }
@@ -396,10 +390,10 @@ constexpr int KDA_SC = KDA_KD + C * DK / 8;
 constexpr int KDA_NSC = (C + DK) / 4;
 constexpr int KDA_CHUNK_U4 = (KDA_SC + KDA_NSC + 15) / 16 * 16;
 
-template <int NW, bool KDA>
+template <int NW, int RT, bool KDA>
 struct SeqCfg {
-  static constexpr int THREADS = 64 * NW;      // NW waves, 16 value rows of the state each
-  static constexpr int WGC = 16 * NW;          // value rows per workgroup
+  static constexpr int THREADS = 64 * NW;      // NW waves, 16 RT value rows of the state each
+  static constexpr int WGC = 16 * NW * RT;     // value rows per workgroup
   static constexpr int NS = DV / WGC;          // workgroups per (batch, value head)
   static constexpr int VST = WGC + 8;          // sV row stride
   static constexpr int NKQ = (C * DK / 8) / THREADS;     // 16-byte K (and Q) pieces per thread
@@ -419,9 +413,9 @@ struct SeqCfg {
 
 // The next chunk's raw loads.  Nothing is converted here, so no instruction
 // needs the data before the chunk is committed.
-template <typename TQ, typename TG, int NW, bool KDA>
+template <typename TQ, typename TG, int NW, int RT, bool KDA>
 struct SeqFetch {
-  using Cfg = SeqCfg<NW, KDA>;
+  using Cfg = SeqCfg<NW, RT, KDA>;
   uint4 k[Cfg::NKQ], q[Cfg::NKQ], kd[KDA ? Cfg::NKQ : 1], v[Cfg::NV], tp[Cfg::NTP], sc;
   TG g, beta;
   int n;
@@ -431,13 +425,13 @@ struct SeqFetch {
 // from the workspace.  KDA true: key-channel gate; the decayed K, Q, the
 // state-update K, beta and Gamma_n come from the workspace (q, k, g, beta are
 // not read) and the state decays per key channel.
-template <typename TQ, typename TG, int NW, bool KDA>
+template <typename TQ, typename TG, int NW, int RT, bool KDA>
 __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *__restrict__ v,
     const TG *__restrict__ g, const TG *__restrict__ beta, const uint4 *__restrict__ ws,
     const float *__restrict__ S0, float *__restrict__ o, float *__restrict__ ST, int T, int Hk,
     int Hv, int ntasks, int nchunks) {
-  using Cfg = SeqCfg<NW, KDA>;
+  using Cfg = SeqCfg<NW, RT, KDA>;
   constexpr int NSC = Cfg::NSC;
   constexpr int THREADS = Cfg::THREADS, WGC = Cfg::WGC, NS = Cfg::NS, VST = Cfg::VST;
   constexpr int NKQ = Cfg::NKQ, NV = Cfg::NV, NTP = Cfg::NTP;
@@ -455,7 +449,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, g4 = l >> 4, ln = l & 15;
-  const int ic = w * 16;                  // this wave's first value row within the workgroup
+  const int ic = w * 16 * RT;             // this wave's first value row within the workgroup
   const int iw0 = slice * WGC + ic;       // ... within the head
 
   // Per-sequence bases (uniform) and per-thread offsets (fixed for all chunks).
@@ -486,20 +480,23 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
   uint4 *const sTPb = reinterpret_cast<uint4 *>(smem + Cfg::OFF_TP);
   float *const sScb = reinterpret_cast<float *>(smem + Cfg::OFF_SC);
 
-  // state: tiles J of S^T, lane holds S[iw0 + ln][16 J + 4 g4 + ii]
-  float4v accS[8];
+  // state: row tile t (value rows iw0 + 16 t ..), tiles J of S^T; the lane
+  // holds S[iw0 + 16 t + ln][16 J + 4 g4 + ii]
+  float4v accS[RT][8];
 #pragma unroll
-  for (int J = 0; J < 8; ++J) {
-    float4v s = {0.f, 0.f, 0.f, 0.f};
-    if (S0) {
-      const float4 t4 =
-          *reinterpret_cast<const float4 *>(S0 + ((size_t)bh * DV + iw0 + ln) * DK + 16 * J + 4 * g4);
-      s[0] = t4.x; s[1] = t4.y; s[2] = t4.z; s[3] = t4.w;
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int J = 0; J < 8; ++J) {
+      float4v s = {0.f, 0.f, 0.f, 0.f};
+      if (S0) {
+        const float4 t4 = *reinterpret_cast<const float4 *>(
+            S0 + ((size_t)bh * DV + iw0 + 16 * t + ln) * DK + 16 * J + 4 * g4);
+        s[0] = t4.x; s[1] = t4.y; s[2] = t4.z; s[3] = t4.w;
+      }
+      accS[t][J] = s;
     }
-    accS[J] = s;
-  }
 
-  SeqFetch<TQ, TG, NW, KDA> f;
+  SeqFetch<TQ, TG, NW, RT, KDA> f;
   auto fetch = [&](int c) {
     const int n = min(C, T - c * C);
     f.n = n;
@@ -643,12 +640,15 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
     if (c + 1 < nchunks) fetch(c + 1);
 
     // S fragments (fp16) in kset order over the key channels
-    half8 sf[4];
+    half8 sf[RT][4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) sf[kk] = pack_pair(accS[2 * kk], accS[2 * kk + 1]);
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) sf[t][kk] = pack_pair(accS[t][2 * kk], accS[t][2 * kk + 1]);
 
-    // K S^T (rows r = 16 R + 4 g4 + ii, value row ln) and S Q^T (transposed read)
-    float4v accX[4], accO[4];
+    // K S^T (rows r = 16 R + 4 g4 + ii, value row ln) and S Q^T (transposed read);
+    // each K and Q fragment serves every row tile of the wave
+    float4v accX[RT][4], accO[RT][4];
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
       half8 kf[4], qf[4];
@@ -657,46 +657,57 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
         kf[kk] = perm_row(cK, KST, 16 * R + ln, kk, g4);
         qf[kk] = perm_row(cQ, KST, 16 * R + ln, kk, g4);
       }
-      float4v ax = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        ax = mfma32(kf[kk], sf[kk], ax);
-        ao = mfma32(sf[kk], qf[kk], ao);
+      for (int t = 0; t < RT; ++t) {
+        float4v ax = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          ax = mfma32(kf[kk], sf[t][kk], ax);
+          ao = mfma32(sf[t][kk], qf[kk], ao);
+        }
+        accX[t][R] = ax;
+        accO[t][R] = ao;
       }
-      accX[R] = ax;
-      accO[R] = ao;
     }
 
     // X = beta V - beta Gamma (K S^T), as fragments over the chunk rows
     // (V rows 16 R + 4 g4 .. + 3 at this lane's value column, by transpose reads)
-    half8 xf[2];
+    half8 xf[RT][2];
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
       const int r0 = 16 * R + 4 * g4;
-      const half4 vv = lds_read_tr(vT + 16 * R * VST);
       // beta and beta Gamma (key gate: Gamma is inside the decayed K)
       const float4 bb = *reinterpret_cast<const float4 *>(sc + (KDA ? 0 : 2 * C) + r0);
       const float4 bg = KDA ? bb : *reinterpret_cast<const float4 *>(sc + 3 * C + r0);
       const float bv[4] = {bb.x, bb.y, bb.z, bb.w}, gv[4] = {bg.x, bg.y, bg.z, bg.w};
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-        xf[R >> 1][(R & 1) * 4 + ii] = (_Float16)(bv[ii] * (float)vv[ii] - gv[ii] * accX[R][ii]);
+      for (int t = 0; t < RT; ++t) {
+        const half4 vv = lds_read_tr(vT + 16 * t + 16 * R * VST);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          xf[t][R >> 1][(R & 1) * 4 + ii] = (_Float16)(bv[ii] * (float)vv[ii] - gv[ii] * accX[t][R][ii]);
+      }
     }
 
     // N = T X;  N and diag(e^{gamma_n - gamma}) N as fragments over the chunk rows
-    half8 nf[2], ndf[2];
+    half8 nf[RT][2], ndf[RT][2];
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
-      float4v acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma32(__builtin_bit_cast(half8, cT[frag_index(R, 0) * 64 + l]), xf[0], acc);
-      if (R >= 2) acc = mfma32(__builtin_bit_cast(half8, cT[frag_index(R, 1) * 64 + l]), xf[1], acc);
+      const half8 t0f = __builtin_bit_cast(half8, cT[frag_index(R, 0) * 64 + l]);
+      const half8 t1f = R >= 2 ? __builtin_bit_cast(half8, cT[frag_index(R, 1) * 64 + l]) : half8{};
       const float4 dd = KDA ? make_float4(1.f, 1.f, 1.f, 1.f)
                             : *reinterpret_cast<const float4 *>(sc + 4 * C + 16 * R + 4 * g4);
       const float dv4[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        nf[R >> 1][(R & 1) * 4 + ii] = (_Float16)acc[ii];
-        ndf[R >> 1][(R & 1) * 4 + ii] = (_Float16)(acc[ii] * dv4[ii]);
+      for (int t = 0; t < RT; ++t) {
+        float4v acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma32(t0f, xf[t][0], acc);
+        if (R >= 2) acc = mfma32(t1f, xf[t][1], acc);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          nf[t][R >> 1][(R & 1) * 4 + ii] = (_Float16)acc[ii];
+          ndf[t][R >> 1][(R & 1) * 4 + ii] = (_Float16)(acc[ii] * dv4[ii]);
+        }
       }
     }
 
@@ -704,15 +715,20 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
       const int r = 16 * R + ln;
-      float4v acc = accO[R];
-      if constexpr (!KDA) {
-        const float er = sc[C + r];
+      const float er = KDA ? 1.f : sc[C + r];
+      const half8 p0f = __builtin_bit_cast(half8, cP[frag_index(R, 0) * 64 + l]);
+      const half8 p1f = R >= 2 ? __builtin_bit_cast(half8, cP[frag_index(R, 1) * 64 + l]) : half8{};
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) acc[ii] *= er;
+      for (int t = 0; t < RT; ++t) {
+        float4v acc = accO[t][R];
+        if constexpr (!KDA) {
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) acc[ii] *= er;
+        }
+        acc = mfma32(nf[t][0], p0f, acc);
+        if (R >= 2) acc = mfma32(nf[t][1], p1f, acc);
+        accO[t][R] = acc;
       }
-      acc = mfma32(nf[0], __builtin_bit_cast(half8, cP[frag_index(R, 0) * 64 + l]), acc);
-      if (R >= 2) acc = mfma32(nf[1], __builtin_bit_cast(half8, cP[frag_index(R, 1) * 64 + l]), acc);
-      accO[R] = acc;
     }
 
     // S^T <- Gamma_n S^T + K^T N~  (K columns 16 J + ln at the chunk rows kset)
@@ -727,18 +743,23 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
           const half4 hi = lds_read_tr(uT + (32 * kk + 16) * KST + 16 * J);
           kc[kk] = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
-        float4v acc = accS[J];
+        float sj[4];
         if constexpr (KDA) {
           // per key channel 16 J + 4 g4 + ii
           const float4 gn = *reinterpret_cast<const float4 *>(sc + C + 16 * J + 4 * g4);
-          acc[0] *= gn.x; acc[1] *= gn.y; acc[2] *= gn.z; acc[3] *= gn.w;
+          sj[0] = gn.x; sj[1] = gn.y; sj[2] = gn.z; sj[3] = gn.w;
         } else {
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) acc[ii] *= gC;
+          sj[0] = sj[1] = sj[2] = sj[3] = gC;
         }
-        acc = mfma32(kc[0], ndf[0], acc);
-        acc = mfma32(kc[1], ndf[1], acc);
-        accS[J] = acc;
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          float4v acc = accS[t][J];
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) acc[ii] *= sj[ii];
+          acc = mfma32(kc[0], ndf[t][0], acc);
+          acc = mfma32(kc[1], ndf[t][1], acc);
+          accS[t][J] = acc;
+        }
       }
     }
 
@@ -751,25 +772,29 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
     for (int R = 0; R < 4; ++R) {
       const int r = 16 * R + ln;
       if (t0 + r < T)
-        *reinterpret_cast<float4 *>(ob + (size_t)(t0 + r) * v_rs) =
-            make_float4(accO[R][0], accO[R][1], accO[R][2], accO[R][3]);
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+          *reinterpret_cast<float4 *>(ob + (size_t)(t0 + r) * v_rs + 16 * t) =
+              make_float4(accO[t][R][0], accO[t][R][1], accO[t][R][2], accO[t][R][3]);
     }
     lds_barrier();
   }
 
   // final state
 #pragma unroll
-  for (int J = 0; J < 8; ++J)
-    *reinterpret_cast<float4 *>(ST + ((size_t)bh * DV + iw0 + ln) * DK + 16 * J + 4 * g4) =
-        make_float4(accS[J][0], accS[J][1], accS[J][2], accS[J][3]);
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int J = 0; J < 8; ++J)
+      *reinterpret_cast<float4 *>(ST + ((size_t)bh * DV + iw0 + 16 * t + ln) * DK + 16 * J + 4 * g4) =
+          make_float4(accS[t][J][0], accS[t][J][1], accS[t][J][2], accS[t][J][3]);
 }
 
-template <typename TQ, typename TG, int NW, bool KDA>
+template <typename TQ, typename TG, int NW, int RT, bool KDA>
 hipError_t launch_seq(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
                       const void *beta, const uint4 *TPws, const float *S0, float *o, float *ST,
                       int nchunks, hipStream_t st) {
-  using Cfg = SeqCfg<NW, KDA>;
-  auto kern = chunk_seq_kernel<TQ, TG, NW, KDA>;
+  using Cfg = SeqCfg<NW, RT, KDA>;
+  auto kern = chunk_seq_kernel<TQ, TG, NW, RT, KDA>;
   hipError_t e =
       hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::SMEM);
   if (e != hipSuccess) return e;
@@ -793,10 +818,12 @@ hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v
                      (const TQ *)k, (const TG *)g, (const TG *)beta, TPws, sh.T, sh.Hk, sh.Hv, nchunks);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // One 8-wave workgroup per head (two waves per SIMD) when that fills the GPU,
-  // else two 4-wave workgroups per head for more parallel chains.
+  // else two 4-wave workgroups per head for more parallel chains.  (One wave
+  // per SIMD holding two row tiles, RT = 2, halves the fragment reads from LDS
+  // but measures slower: the two waves per SIMD hide each other's latency.)
   if ((long)sh.B * sh.Hv >= 160)
-    return launch_seq<TQ, TG, 8, false>(sh, q, k, v, g, beta, TPws, S0, o, ST, nchunks, st);
-  return launch_seq<TQ, TG, 4, false>(sh, q, k, v, g, beta, TPws, S0, o, ST, nchunks, st);
+    return launch_seq<TQ, TG, 8, 1, false>(sh, q, k, v, g, beta, TPws, S0, o, ST, nchunks, st);
+  return launch_seq<TQ, TG, 4, 1, false>(sh, q, k, v, g, beta, TPws, S0, o, ST, nchunks, st);
 }
 
 // ============================================================================
@@ -1073,7 +1100,7 @@ hipError_t launch_kda_t(const Shape &sh, const void *q, const void *k, const voi
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // The decayed K, Q and the state-update K all live in LDS here, so the
   // sequential pass uses 4-wave workgroups (64 value rows each).
-  return launch_seq<TQ, TG, 4, true>(sh, q, k, v, g, beta, wsu, S0, o, ST, nchunks, st);
+  return launch_seq<TQ, TG, 4, 1, true>(sh, q, k, v, g, beta, wsu, S0, o, ST, nchunks, st);
 }
 
 }  // namespace

@@ -109,4 +109,21 @@ template <int G> __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave by DPP moves: shifts by
+// 1, 2, 4, 8 within each 16-lane row (lanes shifted in from outside the row
+// add zero), then the last lane of row 0 (row 2) is broadcast into row 1
+// (row 3), and lane 31 into rows 2 and 3.  All lanes must be active.
+template <int CTRL, int ROW_MASK, bool BOUND> __device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, BOUND));
+}
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  x += dpp_mov<0x111, 0xF, true>(x);   // row_shr:1
+  x += dpp_mov<0x112, 0xF, true>(x);   // row_shr:2
+  x += dpp_mov<0x114, 0xF, true>(x);   // row_shr:4
+  x += dpp_mov<0x118, 0xF, true>(x);   // row_shr:8
+  x += dpp_mov<0x142, 0xA, false>(x);  // row_bcast:15 -> rows 1, 3
+  x += dpp_mov<0x143, 0xC, false>(x);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
 }  // namespace gdn
