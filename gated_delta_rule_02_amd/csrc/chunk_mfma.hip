@@ -67,7 +67,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int DK = 128, DV = 128, C = 64;
 constexpr int NFRAG = 6;                      // fragments (R, kk): (0,0),(1,0),(2,0),(2,1),(3,0),(3,1)
-constexpr size_t FRAGS_BYTES = NFRAG * 64 * 16;   // one 64 x 64 lower-triangular matrix
 
 // LDS strides (elements)
 constexpr int KST = DK + 8;                   // K, Q rows (fp16)
@@ -213,6 +212,21 @@ __device__ __forceinline__ void invert_store(const float *sAd, const _Float16 *s
   }
 }
 
+// Workspace of the key-channel gate per (batch, value head, chunk), in
+// 16-byte units: T and P fragments; K o e^gamma, Q o e^gamma and
+// K o e^{gamma_n - gamma} (fp16, 64 x 128 row-major, rows past the end of the
+// sequence zero); beta[64] and Gamma_n[128] (fp32).
+// Workspace of the head gate per (batch, value head, chunk): T and P
+// fragments, then the per-token scalars of chunk_scalars (5 x 64 fp32).
+constexpr int GDN_SC = 2 * NFRAG * 64;
+constexpr int GDN_CHUNK_U4 = GDN_SC + 5 * C / 4;
+constexpr int KDA_KG = 2 * NFRAG * 64;
+constexpr int KDA_QG = KDA_KG + C * DK / 8;
+constexpr int KDA_KD = KDA_QG + C * DK / 8;
+constexpr int KDA_SC = KDA_KD + C * DK / 8;
+constexpr int KDA_NSC = (C + DK) / 4;
+constexpr int KDA_CHUNK_U4 = (KDA_SC + KDA_NSC + 15) / 16 * 16;
+
 // ============================================================================
 // chunk_prep: P0 per (chunk, key head), T = (I + A)^{-1} per (chunk, value head)
 // ============================================================================
@@ -320,6 +334,8 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
       b_nx = beta[(bt0 + hrow) * Hv + h + 1];
     }
     lds_barrier();
+    uint4 *wch = Tws + (((size_t)b * Hv + h) * nchunks + c) * GDN_CHUNK_U4;
+    if (tid < 5 * C / 4) wch[GDN_SC + tid] = reinterpret_cast<const uint4 *>(sc)[tid];
     // P = L o P0 for this head (lower incl. diagonal), fp16; the two upper
     // blocks the fragments read are zero
     {
@@ -372,24 +388,13 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
       sT[rr * CST + 16 + cc] = (_Float16)0.f;
       sT[(32 + rr) * CST + 48 + cc] = (_Float16)0.f;
     }
-    invert_store(sAd, sAo, sT, sP, Tws + (((size_t)b * Hv + h) * nchunks + c) * (2 * NFRAG * 64), w, l);
+    invert_store(sAd, sAo, sT, sP, wch, w, l);
   }
 }
 
 // ============================================================================
 // chunk_seq: the sequential pass over the chunks of one sequence
 // ============================================================================
-// Workspace of the key-channel gate per (batch, value head, chunk), in
-// 16-byte units: T and P fragments; K o e^gamma, Q o e^gamma and
-// K o e^{gamma_n - gamma} (fp16, 64 x 128 row-major, rows past the end of the
-// sequence zero); beta[64] and Gamma_n[128] (fp32).
-constexpr int KDA_KG = 2 * NFRAG * 64;
-constexpr int KDA_QG = KDA_KG + C * DK / 8;
-constexpr int KDA_KD = KDA_QG + C * DK / 8;
-constexpr int KDA_SC = KDA_KD + C * DK / 8;
-constexpr int KDA_NSC = (C + DK) / 4;
-constexpr int KDA_CHUNK_U4 = (KDA_SC + KDA_NSC + 15) / 16 * 16;
-
 template <int NW, int RT, bool KDA>
 struct SeqCfg {
   static constexpr int THREADS = 64 * NW;      // NW waves, 16 RT value rows of the state each
@@ -400,7 +405,8 @@ struct SeqCfg {
   static constexpr int NV = (C * WGC / 8) / THREADS;     // 16-byte V pieces per thread
   static constexpr int NTP = (2 * NFRAG * 64 + THREADS - 1) / THREADS;  // T and P fragment pieces
   static constexpr int NSC = KDA ? C + DK : 5 * C;       // fp32 scalars per chunk
-  static constexpr int CHUNK_U4 = KDA ? KDA_CHUNK_U4 : 2 * NFRAG * 64;  // workspace per chunk
+  static constexpr int SC_U4 = KDA ? KDA_SC : GDN_SC;      // their offset in the chunk's workspace
+  static constexpr int CHUNK_U4 = KDA ? KDA_CHUNK_U4 : GDN_CHUNK_U4;  // workspace per chunk
   static constexpr int OFF_K = 0;                          // 2 x [C][KST] fp16
   static constexpr int OFF_Q = OFF_K + 2 * C * KST * 2;    // 2 x [C][KST] fp16
   static constexpr int OFF_KD = OFF_Q + 2 * C * KST * 2;   // 2 x [C][KST] fp16 (key gate)
@@ -417,7 +423,6 @@ template <typename TQ, typename TG, int NW, int RT, bool KDA>
 struct SeqFetch {
   using Cfg = SeqCfg<NW, RT, KDA>;
   uint4 k[Cfg::NKQ], q[Cfg::NKQ], kd[KDA ? Cfg::NKQ : 1], v[Cfg::NV], tp[Cfg::NTP], sc;
-  TG g, beta;
   int n;
 };
 
@@ -457,8 +462,6 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
   const TQ *kb = k + ((size_t)b * T * Hk + kh) * DK;
   const TQ *qb = q + ((size_t)b * T * Hk + kh) * DK;
   const TQ *vb = v + ((size_t)b * T * Hv + h) * DV + slice * WGC;
-  const TG *gb = g + (size_t)b * T * Hv + h;
-  const TG *betab = beta + (size_t)b * T * Hv + h;
   float *ob = o + ((size_t)b * T * Hv + h) * DV + iw0 + 4 * g4;
   const uint4 *wsbh = ws + (size_t)bh * nchunks * Cfg::CHUNK_U4;
   int kq_off[NKQ], v_off[NV];
@@ -543,13 +546,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
     }
 #pragma unroll
     for (int it = 0; it < NTP; ++it) f.tp[it] = wc[min(tid + THREADS * it, 2 * NFRAG * 64 - 1)];
-    if constexpr (KDA) {
-      f.sc = wc[KDA_SC + min(tid, KDA_NSC - 1)];
-    } else {
-      const int row = min(tid & 63, n - 1);
-      f.g = gb[(t0 + row) * Hv];
-      f.beta = betab[(t0 + row) * Hv];
-    }
+    f.sc = wc[Cfg::SC_U4 + min(tid, NSC / 4 - 1)];
   };
   auto commit = [&](int buf) {
     // Nothing of the commit (the conversions of the raw loads above all) may be
@@ -567,8 +564,8 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
         *reinterpret_cast<half8 *>(q_ + (e >> 4) * KST + (e & 15) * 8) = to_half8(f.q[it], f16_t{});
         *reinterpret_cast<half8 *>(kd_ + (e >> 4) * KST + (e & 15) * 8) = to_half8(f.kd[it], f16_t{});
       }
-      if (tid < KDA_NSC) reinterpret_cast<uint4 *>(sScb + buf * NSC)[tid] = f.sc;
     }
+    if (tid < NSC / 4) reinterpret_cast<uint4 *>(sScb + buf * NSC)[tid] = f.sc;
     if (f.n == C) {
       if constexpr (!KDA) {
 #pragma unroll
@@ -609,12 +606,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
       const int e = tid + THREADS * it;
       if (e < 2 * NFRAG * 64) sTPb[buf * 2 * NFRAG * 64 + e] = f.tp[it];
     }
-    if constexpr (!KDA) {
-      if (tid < C) {
-        const bool ok = tid < f.n;
-        chunk_scalars(ok ? to_f32(f.g) : 0.f, ok ? to_f32(f.beta) : 0.f, sScb + buf * NSC, tid);
-      }
-    }
+
   };
 
   fetch(0);
@@ -1107,7 +1099,7 @@ hipError_t launch_kda_t(const Shape &sh, const void *q, const void *k, const voi
 
 size_t chunk_mfma_workspace(const Shape &sh) {
   const size_t nchunks = (size_t)(sh.T + C - 1) / C;
-  const size_t per_chunk = sh.key_gate ? (size_t)KDA_CHUNK_U4 * 16 : 2 * FRAGS_BYTES;
+  const size_t per_chunk = (size_t)(sh.key_gate ? KDA_CHUNK_U4 : GDN_CHUNK_U4) * 16;
   return (size_t)sh.B * sh.Hv * nchunks * per_chunk;
 }
 

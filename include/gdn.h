@@ -112,7 +112,8 @@ gdn_status gdn_prologue(const gdn_desc *d, int32_t x_dtype, const void *xq,
  * workspace pointer may be NULL).  The matrix-core path (16-bit q/k/v,
  * dk = dv = 128, chunk 64) keeps per (batch, value head, 64-token chunk):
  *   head gate: two 64 x 64 lower-triangular fp16 matrices, the triangular
- *     inverse and the decayed masked q.k products: 12288 bytes;
+ *     inverse and the decayed masked q.k products, and five fp32 values per
+ *     token (cumulative log decay and the factors made from it): 13568 bytes;
  *   key-channel gate: those two, the decayed k, q and the state-update k
  *     (64 x 128 fp16 each), beta and the chunk's total decay: 62208 bytes.
  * Returns 0 for an invalid description.  The caller owns the workspace; it

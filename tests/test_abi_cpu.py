@@ -107,10 +107,10 @@ def test_prologue_rejects(L):
 
 
 def test_workspace_query(L):
-    # matrix-core path: 12288 bytes per (batch, value head, 64-token chunk),
+    # matrix-core path: 13568 bytes per (batch, value head, 64-token chunk),
     # 62208 with the key-channel gate
-    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc())) == 2 * 6 * 2 * 12288
-    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(T=1))) == 2 * 6 * 1 * 12288
+    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc())) == 2 * 6 * 2 * 13568
+    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(T=1))) == 2 * 6 * 1 * 13568
     assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(gate=gdn.GATE_KEY_CHANNEL))) == 2 * 6 * 2 * 62208
     assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(gate=gdn.GATE_KEY_CHANNEL, dk=64, dv=64))) == 0
     assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(qkv_dtype=gdn.F32, gate_dtype=gdn.F32, chunk=32))) == 0
