@@ -104,7 +104,8 @@ def recurrent(q, k, v, g, beta, S0=None, chains=None, nthreads=None):
     o = np.empty((n, T, dv), dtype=np.float64)
     ST = np.empty((n, dv, dk), dtype=np.float64)
     if nthreads is None:
-        nthreads = os.cpu_count() or 1
+        # one GPU's share of the host: OMP_NUM_THREADS when set, at most 16
+        nthreads = min(int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1), 16)
     rc = lib.gdnref_recurrent(B, T, Hk, Hv, dk, dv, per_channel, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                               _ptr(beta), _ptr(S0), s0_double, n, _ptr(sb), _ptr(sh), _ptr(o), _ptr(ST),
                               int(nthreads))

@@ -141,10 +141,12 @@ def test_deterministic():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-# ---------------------------------------------------------------- full sizes, sampled chains
-def sampled(wl, chains, label, conv=False):
+# ---------------------------------------------------------------- full sizes, every chain
+def whole(wl, label, conv=False):
+    """The workload at its full size on the GPU against the oracle over the
+    whole output tensor (every batch element and value head)."""
     inp = make_prefill(wl)
-    say("%s full size, chains %s" % (label, chains))
+    say("%s full size, whole tensor" % label)
     if conv:
         q, k, v = gdn.prologue(*(to_torch(inp[n]) for n in ("xq", "xk", "xv")),
                                to_torch(inp["conv_w"]), out_dtype=torch.float16)
@@ -154,36 +156,23 @@ def sampled(wl, chains, label, conv=False):
     S0 = None if inp["S0"] is None else to_torch(inp["S0"])
     o, ST = gdn.fwd_chunked(*args, S0=S0, chunk=wl.chunk)
     torch.cuda.synchronize()
-    grp = wl.Hv // wl.Hk
-    for (b, h) in chains:
-        kh = h // grp
-        if conv:
-            d = wl.dk
-            nq = wl.Hk * d
-            w = inp["conv_w"]
-            sl = lambda x, hh: np.ascontiguousarray(x.f32()[b:b + 1, :, hh:hh + 1])
-            qr = oracle.conv_silu(sl(inp["xq"], kh), w[kh * d:(kh + 1) * d], True)
-            kr = oracle.conv_silu(sl(inp["xk"], kh), w[nq + kh * d: nq + (kh + 1) * d], True)
-            vr = oracle.conv_silu(sl(inp["xv"], h), w[2 * nq + h * d: 2 * nq + (h + 1) * d], False)
-        else:
-            qr = inp["q"].f32()[b:b + 1, :, kh:kh + 1]
-            kr = inp["k"].f32()[b:b + 1, :, kh:kh + 1]
-            vr = inp["v"].f32()[b:b + 1, :, h:h + 1]
-        gr = inp["g"].f32()[b:b + 1, :, h:h + 1]
-        br = inp["beta"].f32()[b:b + 1, :, h:h + 1]
-        s0 = None if inp["S0"] is None else inp["S0"][b:b + 1, h:h + 1]
-        o_ref, S_ref = oracle.recurrent(qr, kr, vr, gr, br, s0)
-        check("bf16", o[b, :, h].cpu().numpy(), o_ref[0], ST[b, h].cpu().numpy(), S_ref[0],
-              "%s chain (%d,%d)" % (label, b, h))
+    o, ST = o.cpu().numpy(), ST.cpu().numpy()
+    del args
+    if conv:
+        rq, rk, rv = oracle.prologue(inp["xq"].f32(), inp["xk"].f32(), inp["xv"].f32(), inp["conv_w"])
+    else:
+        rq, rk, rv = (inp[n].f32() for n in ("q", "k", "v"))
+    o_ref, S_ref = oracle.recurrent_full(rq, rk, rv, inp["g"].f32(), inp["beta"].f32(), inp["S0"])
+    check("bf16", o, o_ref, ST, S_ref, "%s whole tensor" % label)
 
 
-def test_full_prefill_conv_sampled():
-    sampled(PREFILL_CONV, [(0, 0), (1, 20), (3, 47)], "prefill+conv", conv=True)
+def test_full_prefill_conv():
+    whole(PREFILL_CONV, "prefill+conv", conv=True)
 
 
-def test_full_long_prefill_sampled():
-    sampled(LONG_PREFILL, [(0, 0), (0, 29)], "long prefill")
+def test_full_long_prefill():
+    whole(LONG_PREFILL, "long prefill")
 
 
-def test_full_key_gate_sampled():
-    sampled(KDA_PREFILL, [(0, 0), (1, 31)], "key gate")
+def test_full_key_gate():
+    whole(KDA_PREFILL, "key gate")
