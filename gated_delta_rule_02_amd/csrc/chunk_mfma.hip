@@ -56,7 +56,11 @@
 //    loads (and its T and P0 fragments) are issued at the top of a chunk and
 //    land at its end.  Blocks are numbered so that workgroups sharing a key
 //    head run on one XCD (shared K, Q and P0 then hit in its L2).
+#include <algorithm>
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "gdn_device.h"
 #include "gdn_launch.h"
@@ -245,7 +249,7 @@ static_assert(P_OFF_AD + 4 * 16 * DST * 4 <= P_OFF_SC, "per-head matrices overla
 template <typename TQ, typename TG>
 __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TG *__restrict__ g,
-    const TG *__restrict__ beta, uint4 *__restrict__ Tws, int T, int Hk, int Hv, int nchunks) {
+    const TG *__restrict__ beta, uint4 *__restrict__ Tws, int T, int Hk, int Hv, int nchunks, int c0) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   _Float16 *sK = reinterpret_cast<_Float16 *>(smem + P_OFF_K);
   _Float16 *sQ = reinterpret_cast<_Float16 *>(smem + P_OFF_Q);
@@ -256,20 +260,15 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
   float *sc = reinterpret_cast<float *>(smem + P_OFF_SC);
   const float *sGam = sc;
   const float *sB = sc + 2 * C;
+  float *sGB = reinterpret_cast<float *>(smem + P_SMEM);   // [2][grp][C]: gate, beta per head
 
-  const int c = blockIdx.x;
+  const int c = c0 + blockIdx.x;
   const int b = blockIdx.y / Hk, kh = blockIdx.y % Hk;
   const int grp = Hv / Hk;
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, g4 = l >> 4, ln = l & 15;
   const int t0 = c * C, n = min(C, T - t0);
   const size_t bt0 = (size_t)b * T + t0;
-
-  // gate and beta of the first value head (lane = token); the next head's are
-  // always requested before this head's results are stored, so that waiting
-  // for them never waits for those stores
-  const int hrow = min(tid, n - 1);
-  TG g_nx = g[(bt0 + hrow) * Hv + kh * grp], b_nx = beta[(bt0 + hrow) * Hv + kh * grp];
 
   // K and Q tiles (fp16), rows past the end zero; all eight loads are in
   // flight before the first is converted
@@ -281,6 +280,31 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
       const size_t off = ((bt0 + min(row, n - 1)) * Hk + kh) * DK + (tid & 15) * 8;
       uk[it] = *reinterpret_cast<const uint4 *>(k + off);
       uq[it] = *reinterpret_cast<const uint4 *>(q + off);
+    }
+    // gate and beta of every value head of the group, [head][token] in LDS
+    // past the fixed layout, all requested before anything is stored: one
+    // counter tracks loads and stores, so waiting for a load issued after a
+    // store would also wait for that store.
+    {
+      TG graw[2], braw[2];
+      for (int e0 = 0; e0 < grp * C; e0 += 2 * kThreads) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int e = min(e0 + u * kThreads + tid, grp * C - 1);
+          const int tok = min(e / grp, n - 1), hh = kh * grp + e % grp;
+          graw[u] = g[(bt0 + tok) * Hv + hh];
+          braw[u] = beta[(bt0 + tok) * Hv + hh];
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int e = e0 + u * kThreads + tid;
+          if (e < grp * C) {
+            const int tok = e / grp, hv = e % grp;
+            sGB[hv * C + tok] = tok < n ? to_f32(graw[u]) : 0.f;
+            sGB[(grp + hv) * C + tok] = tok < n ? to_f32(braw[u]) : 0.f;
+          }
+        }
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     const half8 hz = {};
@@ -322,17 +346,14 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
       accP[d] = apv;
     }
   }
+  // All loads so far have landed (nothing is stored yet): said explicitly so
+  // that the head loop does not wait on them again behind its own stores.
+  // (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15.)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   for (int hv = 0; hv < grp; ++hv) {
     const int h = kh * grp + hv;
     lds_barrier();  // K and Q, or the previous head's T and P, have been read out
-    if (tid < C) {
-      const bool ok = tid < n;
-      chunk_scalars(ok ? to_f32(g_nx) : 0.f, ok ? to_f32(b_nx) : 0.f, sc, tid);
-    }
-    if (hv + 1 < grp) {
-      g_nx = g[(bt0 + hrow) * Hv + h + 1];
-      b_nx = beta[(bt0 + hrow) * Hv + h + 1];
-    }
+    if (tid < C) chunk_scalars(sGB[hv * C + tid], sGB[(grp + hv) * C + tid], sc, tid);
     lds_barrier();
     uint4 *wch = Tws + (((size_t)b * Hv + h) * nchunks + c) * GDN_CHUNK_U4;
     if (tid < 5 * C / 4) wch[GDN_SC + tid] = reinterpret_cast<const uint4 *>(sc)[tid];
@@ -435,7 +456,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *__restrict__ v,
     const TG *__restrict__ g, const TG *__restrict__ beta, const uint4 *__restrict__ ws,
     const float *__restrict__ S0, float *__restrict__ o, float *__restrict__ ST, int T, int Hk,
-    int Hv, int ntasks, int nchunks) {
+    int Hv, int ntasks, int nchunks, int c_begin, int c_end) {
   using Cfg = SeqCfg<NW, RT, KDA>;
   constexpr int NSC = Cfg::NSC;
   constexpr int THREADS = Cfg::THREADS, WGC = Cfg::WGC, NS = Cfg::NS, VST = Cfg::VST;
@@ -609,7 +630,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
 
   };
 
-  fetch(0);
+  fetch(c_begin);
   commit(0);
   // Everything loaded so far (S0 and chunk 0) has landed.  Said explicitly,
   // so that the compiler's wait tracking does not carry these loads into the
@@ -618,8 +639,8 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
   __builtin_amdgcn_s_waitcnt(0x0F70);
   lds_barrier();
 
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
+  for (int c = c_begin; c < c_end; ++c) {
+    const int buf = (c - c_begin) & 1;
     const int t0 = c * C;
     const _Float16 *cK = sKb + buf * C * KST, *cQ = sQb + buf * C * KST, *cV = sVb + buf * C * VST;
     const uint4 *cT = sTPb + buf * 2 * NFRAG * 64, *cP = cT + NFRAG * 64;
@@ -629,7 +650,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
     const _Float16 *vT = cV + (4 * g4 + (ln >> 2)) * VST + ic + 4 * (ln & 3);
     // the K whose columns update the state: K itself, or K o e^{gamma_n - gamma} for the key gate
     const _Float16 *uT = KDA ? sKdb + buf * C * KST + (4 * g4 + (ln >> 2)) * KST + 4 * (ln & 3) : kT;
-    if (c + 1 < nchunks) fetch(c + 1);
+    if (c + 1 < c_end) fetch(c + 1);
 
     // S fragments (fp16) in kset order over the key channels
     half8 sf[RT][4];
@@ -755,7 +776,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
       }
     }
 
-    if (c + 1 < nchunks) commit(buf ^ 1);
+    if (c + 1 < c_end) commit(buf ^ 1);
     // The output stores go out only now.  On this architecture one counter
     // tracks both loads and stores, and a wait for a load while stores are in
     // flight also waits for the stores; issued after the commit, they have the
@@ -784,7 +805,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
 template <typename TQ, typename TG, int NW, int RT, bool KDA>
 hipError_t launch_seq(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
                       const void *beta, const uint4 *TPws, const float *S0, float *o, float *ST,
-                      int nchunks, hipStream_t st) {
+                      int nchunks, int c_begin, int c_end, hipStream_t st) {
   using Cfg = SeqCfg<NW, RT, KDA>;
   auto kern = chunk_seq_kernel<TQ, TG, NW, RT, KDA>;
   hipError_t e =
@@ -793,8 +814,93 @@ hipError_t launch_seq(const Shape &sh, const void *q, const void *k, const void 
   const int ntasks = sh.B * sh.Hv * Cfg::NS;
   hipLaunchKernelGGL(kern, dim3(ntasks), dim3(Cfg::THREADS), Cfg::SMEM, st, (const TQ *)q,
                      (const TQ *)k, (const TQ *)v, (const TG *)g, (const TG *)beta, TPws, S0, o, ST,
-                     sh.T, sh.Hk, sh.Hv, ntasks, nchunks);
+                     sh.T, sh.Hk, sh.Hv, ntasks, nchunks, c_begin, c_end);
   return hipGetLastError();
+}
+
+// A side stream and events for one pipelined call, taken from a per-device
+// pool and returned when the call has enqueued its work (the pool grows to
+// the number of concurrent calls).  Streams have the default priority.
+constexpr int kMaxSeg = 8;
+struct SideSlot {
+  hipStream_t stream = nullptr;
+  hipEvent_t ev[kMaxSeg + 1] = {};
+};
+class SidePool {
+ public:
+  static SidePool &get() {
+    static SidePool p;
+    return p;
+  }
+  SideSlot *acquire(int dev) {
+    {
+      std::lock_guard<std::mutex> g(mu_);
+      auto &fl = free_[dev];
+      if (!fl.empty()) {
+        SideSlot *x = fl.back();
+        fl.pop_back();
+        return x;
+      }
+    }
+    SideSlot *x = new SideSlot;
+    bool ok = hipStreamCreateWithFlags(&x->stream, hipStreamNonBlocking) == hipSuccess;
+    for (int i = 0; ok && i <= kMaxSeg; ++i)
+      ok = hipEventCreateWithFlags(&x->ev[i], hipEventDisableTiming) == hipSuccess;
+    if (!ok) {
+      for (auto &e : x->ev)
+        if (e) (void)hipEventDestroy(e);
+      if (x->stream) (void)hipStreamDestroy(x->stream);
+      delete x;
+      return nullptr;
+    }
+    return x;
+  }
+  void release(int dev, SideSlot *x) {
+    std::lock_guard<std::mutex> g(mu_);
+    free_[dev].push_back(x);
+  }
+
+ private:
+  std::mutex mu_;
+  std::map<int, std::vector<SideSlot *>> free_;
+};
+
+// Enqueue the chunked forward, with `overlap` over up to kMaxSeg segments of
+// consecutive chunks: the state-independent launch of segment s + 1 (prep)
+// runs on a side stream while the sequential pass (seq) works through
+// segment s on the caller's stream; segment s + 1 of the pass starts from
+// the state segment s left in S_T.  prep(c_begin, c_end, stream) and
+// seq(c_begin, c_end, S0, stream) enqueue one launch each.  Overlap pays when
+// the pass leaves most compute units idle; when it fills the GPU the two
+// launches only compete for it.
+template <typename PrepFn, typename SeqFn>
+hipError_t pipelined(int nchunks, bool overlap, const float *S0, float *ST, hipStream_t st, PrepFn prep,
+                     SeqFn seq) {
+  const int nseg = overlap ? std::min(kMaxSeg, nchunks / 16) : 1;
+  int dev = 0;
+  SideSlot *side = nullptr;
+  if (nseg > 1 && hipGetDevice(&dev) == hipSuccess) side = SidePool::get().acquire(dev);
+  hipError_t e;
+  if (!side) {
+    if ((e = prep(0, nchunks, st)) != hipSuccess) return e;
+    return seq(0, nchunks, S0, st);
+  }
+  auto bound = [&](int i) { return (int)((long)nchunks * i / nseg); };
+  // the side stream starts once segment 0 is prepared (and so after all the
+  // caller enqueued before), when the pass takes the GPU
+  e = prep(bound(0), bound(1), st);
+  if (e == hipSuccess) e = hipEventRecord(side->ev[0], st);
+  if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->ev[0], 0);
+  for (int i = 1; i < nseg && e == hipSuccess; ++i) {
+    e = prep(bound(i), bound(i + 1), side->stream);
+    if (e == hipSuccess) e = hipEventRecord(side->ev[i], side->stream);
+  }
+  for (int i = 0; i < nseg && e == hipSuccess; ++i) {
+    if (i > 0) e = hipStreamWaitEvent(st, side->ev[i], 0);
+    if (e == hipSuccess) e = seq(bound(i), bound(i + 1), i == 0 ? S0 : ST, st);
+  }
+  SidePool::get().release(dev, side);
+  return e;
 }
 
 template <typename TQ, typename TG>
@@ -802,20 +908,30 @@ hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v
                     const void *beta, const float *S0, float *o, float *ST, void *ws, hipStream_t st) {
   const int nchunks = (sh.T + C - 1) / C;
   uint4 *TPws = (uint4 *)ws;
-  auto prep = chunk_prep_kernel<TQ, TG>;
+  auto prep_k = chunk_prep_kernel<TQ, TG>;
+  // fixed layout, then gate and beta of the group's heads (fp32, 2 x grp x C)
+  const size_t smem = P_SMEM + (size_t)2 * (sh.Hv / sh.Hk) * C * 4;
+  if (smem > 160 * 1024) return hipErrorInvalidValue;
   hipError_t e =
-      hipFuncSetAttribute((const void *)prep, hipFuncAttributeMaxDynamicSharedMemorySize, P_SMEM);
+      hipFuncSetAttribute((const void *)prep_k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(prep, dim3(nchunks, sh.B * sh.Hk), dim3(kThreads), P_SMEM, st, (const TQ *)q,
-                     (const TQ *)k, (const TG *)g, (const TG *)beta, TPws, sh.T, sh.Hk, sh.Hv, nchunks);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  auto prep = [&](int cb, int ce, hipStream_t s) {
+    hipLaunchKernelGGL(prep_k, dim3(ce - cb, sh.B * sh.Hk), dim3(kThreads), smem, s, (const TQ *)q,
+                       (const TQ *)k, (const TG *)g, (const TG *)beta, TPws, sh.T, sh.Hk, sh.Hv,
+                       nchunks, cb);
+    return hipGetLastError();
+  };
   // One 8-wave workgroup per head (two waves per SIMD) when that fills the GPU,
   // else two 4-wave workgroups per head for more parallel chains.  (One wave
   // per SIMD holding two row tiles, RT = 2, halves the fragment reads from LDS
   // but measures slower: the two waves per SIMD hide each other's latency.)
-  if ((long)sh.B * sh.Hv >= 160)
-    return launch_seq<TQ, TG, 8, 1, false>(sh, q, k, v, g, beta, TPws, S0, o, ST, nchunks, st);
-  return launch_seq<TQ, TG, 4, 1, false>(sh, q, k, v, g, beta, TPws, S0, o, ST, nchunks, st);
+  const bool wide = (long)sh.B * sh.Hv >= 160;
+  auto seq = [&](int cb, int ce, const float *s0, hipStream_t s) {
+    return wide ? launch_seq<TQ, TG, 8, 1, false>(sh, q, k, v, g, beta, TPws, s0, o, ST, nchunks, cb, ce, s)
+                : launch_seq<TQ, TG, 4, 1, false>(sh, q, k, v, g, beta, TPws, s0, o, ST, nchunks, cb, ce, s);
+  };
+  // overlap when the pass uses at most half of the 256 compute units
+  return pipelined(nchunks, (long)sh.B * sh.Hv * (wide ? 1 : 2) <= 128, S0, ST, st, prep, seq);
 }
 
 // ============================================================================
@@ -852,7 +968,7 @@ __device__ __forceinline__ void perm_row_f32(const float *M, int st, int row, in
 template <typename TQ, typename TG>
 __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TG *__restrict__ g,
-    const TG *__restrict__ beta, uint4 *__restrict__ ws, int T, int Hk, int Hv, int nchunks) {
+    const TG *__restrict__ beta, uint4 *__restrict__ ws, int T, int Hk, int Hv, int nchunks, int c0) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   _Float16 *sK = reinterpret_cast<_Float16 *>(smem + KP_OFF_K);
   _Float16 *sQ = reinterpret_cast<_Float16 *>(smem + KP_OFF_Q);
@@ -863,7 +979,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(
   _Float16 *sAo = reinterpret_cast<_Float16 *>(smem + KP_OFF_AO);
   float *sAd = reinterpret_cast<float *>(smem + KP_OFF_AD);
 
-  const int c = blockIdx.x, bh = blockIdx.y;  // bh = b * Hv + h
+  const int c = c0 + blockIdx.x, bh = blockIdx.y;  // bh = b * Hv + h
   const int b = bh / Hv, h = bh % Hv, kh = h / (Hv / Hk);
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, g4 = l >> 4, ln = l & 15;
@@ -1083,16 +1199,22 @@ hipError_t launch_kda_t(const Shape &sh, const void *q, const void *k, const voi
                         hipStream_t st) {
   const int nchunks = (sh.T + C - 1) / C;
   uint4 *wsu = (uint4 *)ws;
-  auto prep = kda_prep_kernel<TQ, TG>;
+  auto prep_k = kda_prep_kernel<TQ, TG>;
   hipError_t e =
-      hipFuncSetAttribute((const void *)prep, hipFuncAttributeMaxDynamicSharedMemorySize, KP_SMEM);
+      hipFuncSetAttribute((const void *)prep_k, hipFuncAttributeMaxDynamicSharedMemorySize, KP_SMEM);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(prep, dim3(nchunks, sh.B * sh.Hv), dim3(kThreads), KP_SMEM, st, (const TQ *)q,
-                     (const TQ *)k, (const TG *)g, (const TG *)beta, wsu, sh.T, sh.Hk, sh.Hv, nchunks);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  auto prep = [&](int cb, int ce, hipStream_t s) {
+    hipLaunchKernelGGL(prep_k, dim3(ce - cb, sh.B * sh.Hv), dim3(kThreads), KP_SMEM, s, (const TQ *)q,
+                       (const TQ *)k, (const TG *)g, (const TG *)beta, wsu, sh.T, sh.Hk, sh.Hv,
+                       nchunks, cb);
+    return hipGetLastError();
+  };
   // The decayed K, Q and the state-update K all live in LDS here, so the
   // sequential pass uses 4-wave workgroups (64 value rows each).
-  return launch_seq<TQ, TG, 4, 1, true>(sh, q, k, v, g, beta, wsu, S0, o, ST, nchunks, st);
+  auto seq = [&](int cb, int ce, const float *s0, hipStream_t s) {
+    return launch_seq<TQ, TG, 4, 1, true>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks, cb, ce, s);
+  };
+  return pipelined(nchunks, (long)sh.B * sh.Hv * 2 <= 128, S0, ST, st, prep, seq);
 }
 
 }  // namespace

@@ -37,8 +37,12 @@
  *    A failed launch returns GDN_E_HIP.  A fault inside a kernel surfaces at
  *    the caller's next synchronisation.  gdn_last_error() gives a message
  *    for the last failing call on the calling thread.
- *  - The library keeps no state between calls except that per-thread message.
- *    Calls on different streams may run concurrently.
+ *  - The library keeps no state between calls except that per-thread message
+ *    and, per device, a pool of internal streams and events: a chunked call
+ *    may run part of its work on one of them, ordered by events with the
+ *    caller's stream (a fork and join, also under stream capture).  The pool
+ *    holds one entry per concurrently running call and lives until the
+ *    process ends.  Calls on different streams may run concurrently.
  */
 #ifndef GDN_H_
 #define GDN_H_
