@@ -176,3 +176,38 @@ def test_full_long_prefill():
 
 def test_full_key_gate():
     whole(KDA_PREFILL, "key gate")
+
+
+# ---------------------------------------------------------------- stream capture
+def test_graph_capture_segmented():
+    """A configuration that runs as two overlapped segments (side stream) is
+    captured into a graph and replayed several times, with eager work between
+    the replays; every replay equals the eager call, which matches the oracle."""
+    wl = LONG_PREFILL.with_(B=1, T=64 * 33 + 17, Hk=2, Hv=6)
+    inp = make_prefill(wl)
+    say("graph capture: B=1 T=%d Hk=2 Hv=6 (two segments)" % wl.T)
+    args = gpu_inputs(inp)
+    S0 = to_torch(inp["S0"])
+    o_e, S_e = gdn.fwd_chunked(*args, S0=S0, chunk=64)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.recurrent_full(*oracle_inputs(inp), inp["S0"])
+    check("bf16", o_e.cpu().numpy(), o_ref, S_e.cpu().numpy(), S_ref, "graph capture eager")
+    o = torch.full_like(o_e, float("nan"))
+    ST = torch.full_like(S_e, float("nan"))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):           # warm the allocator outside the capture
+        gdn.fwd_chunked(*args, S0=S0, chunk=64, o=o, S_T=ST)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gdn.fwd_chunked(*args, S0=S0, chunk=64, o=o, S_T=ST)
+    for rep in range(3):
+        o.fill_(float("nan"))
+        ST.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda").sum()   # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        assert torch.equal(o, o_e) and torch.equal(ST, S_e), "replay %d differs from the eager call" % rep
