@@ -520,8 +520,9 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
       accS[t][J] = s;
     }
 
-  SeqFetch<TQ, TG, NW, RT, KDA> f;
-  auto fetch = [&](int c) {
+  using Fetch = SeqFetch<TQ, TG, NW, RT, KDA>;
+  Fetch fa, fb;   // the next two chunks' raw loads (prefetch distance 2)
+  auto fetch = [&](Fetch &f, int c) {
     const int n = min(C, T - c * C);
     f.n = n;
     const size_t t0 = (size_t)c * C;
@@ -569,7 +570,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
     for (int it = 0; it < NTP; ++it) f.tp[it] = wc[min(tid + THREADS * it, 2 * NFRAG * 64 - 1)];
     f.sc = wc[Cfg::SC_U4 + min(tid, NSC / 4 - 1)];
   };
-  auto commit = [&](int buf) {
+  auto commit = [&](const Fetch &f, int buf) {
     // Nothing of the commit (the conversions of the raw loads above all) may be
     // scheduled into the chunk's arithmetic: that would wait for the loads there.
     __builtin_amdgcn_sched_barrier(0);
@@ -630,16 +631,22 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
 
   };
 
-  fetch(c_begin);
-  commit(0);
-  // Everything loaded so far (S0 and chunk 0) has landed.  Said explicitly,
-  // so that the compiler's wait tracking does not carry these loads into the
-  // loop and wait on later stores for them.  (gfx9 encoding: vmcnt 0,
-  // expcnt 7, lgkmcnt 15.)
+  fetch(fa, c_begin);
+  commit(fa, 0);
+  // Everything loaded so far (S0 and the first chunk) has landed.  Said
+  // explicitly, so that the compiler's wait tracking does not carry these
+  // loads into the loop and wait on later stores for them.  (gfx9 encoding:
+  // vmcnt 0, expcnt 7, lgkmcnt 15.)
   __builtin_amdgcn_s_waitcnt(0x0F70);
+  fetch(fb, min(c_begin + 1, c_end - 1));
   lds_barrier();
 
-  for (int c = c_begin; c < c_end; ++c) {
+  // One chunk: compute chunk c from LDS buffer (c - c_begin) & 1, load chunk
+  // c + 2 into fn (fn's previous chunk is already in LDS), and commit chunk
+  // c + 1, loaded one chunk earlier, from fc into the other buffer.  The load
+  // is unconditional (a repeated chunk near the end) so that the number of
+  // loads in flight, which every wait counts, is the same on every path.
+  auto step = [&](int c, Fetch &fn, const Fetch &fc) {
     const int buf = (c - c_begin) & 1;
     const int t0 = c * C;
     const _Float16 *cK = sKb + buf * C * KST, *cQ = sQb + buf * C * KST, *cV = sVb + buf * C * VST;
@@ -650,7 +657,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
     const _Float16 *vT = cV + (4 * g4 + (ln >> 2)) * VST + ic + 4 * (ln & 3);
     // the K whose columns update the state: K itself, or K o e^{gamma_n - gamma} for the key gate
     const _Float16 *uT = KDA ? sKdb + buf * C * KST + (4 * g4 + (ln >> 2)) * KST + 4 * (ln & 3) : kT;
-    if (c + 1 < c_end) fetch(c + 1);
+    fetch(fn, min(c + 2, c_end - 1));
 
     // S fragments (fp16) in kset order over the key channels
     half8 sf[RT][4];
@@ -776,7 +783,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
       }
     }
 
-    if (c + 1 < c_end) commit(buf ^ 1);
+    if (c + 1 < c_end) commit(fc, buf ^ 1);
     // The output stores go out only now.  On this architecture one counter
     // tracks both loads and stores, and a wait for a load while stores are in
     // flight also waits for the stores; issued after the commit, they have the
@@ -791,6 +798,10 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
               make_float4(accO[t][R][0], accO[t][R][1], accO[t][R][2], accO[t][R][3]);
     }
     lds_barrier();
+  };
+  for (int c = c_begin; c < c_end; c += 2) {
+    step(c, fa, fb);
+    if (c + 1 < c_end) step(c + 1, fb, fa);
   }
 
   // final state
