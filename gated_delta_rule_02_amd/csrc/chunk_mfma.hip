@@ -522,13 +522,15 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
 
   using Fetch = SeqFetch<TQ, TG, NW, RT, KDA>;
   Fetch fa, fb;   // the next two chunks' raw loads (prefetch distance 2)
-  auto fetch = [&](Fetch &f, int c) {
+  // part 0: K and Q (and the key gate's state-update K); part 1: V, the T
+  // and P fragments and the scalars; part 2: both
+  auto fetch = [&](Fetch &f, int c, int part) {
     const int n = min(C, T - c * C);
     f.n = n;
     const size_t t0 = (size_t)c * C;
     const uint4 *wc = wsbh + (size_t)c * Cfg::CHUNK_U4;
     const TQ *kc = kb + t0 * kq_rs, *qc = qb + t0 * kq_rs, *vc = vb + t0 * v_rs;
-    if constexpr (KDA) {
+    if (KDA && part != 1) {
       // rows past the end of the sequence are zero in the workspace
 #pragma unroll
       for (int it = 0; it < NKQ; ++it) {
@@ -539,18 +541,20 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
       }
     }
     if (n == C) {
-      if constexpr (!KDA) {
+      if (!KDA && part != 1) {
 #pragma unroll
         for (int it = 0; it < NKQ; ++it) {
           f.k[it] = *reinterpret_cast<const uint4 *>(kc + kq_off[it]);
           f.q[it] = *reinterpret_cast<const uint4 *>(qc + kq_off[it]);
         }
       }
+      if (part != 0) {
 #pragma unroll
-      for (int it = 0; it < NV; ++it) f.v[it] = *reinterpret_cast<const uint4 *>(vc + v_off[it]);
+        for (int it = 0; it < NV; ++it) f.v[it] = *reinterpret_cast<const uint4 *>(vc + v_off[it]);
+      }
     } else {
       // last chunk: rows past the end of the sequence re-read its last row
-      if constexpr (!KDA) {
+      if (!KDA && part != 1) {
 #pragma unroll
         for (int it = 0; it < NKQ; ++it) {
           const int e = tid + THREADS * it;
@@ -559,16 +563,20 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
           f.q[it] = *reinterpret_cast<const uint4 *>(qc + off);
         }
       }
+      if (part != 0) {
 #pragma unroll
-      for (int it = 0; it < NV; ++it) {
-        const int e = tid + THREADS * it;
-        f.v[it] = *reinterpret_cast<const uint4 *>(vc + min(e / (WGC / 8), n - 1) * v_rs +
-                                                   (e % (WGC / 8)) * 8);
+        for (int it = 0; it < NV; ++it) {
+          const int e = tid + THREADS * it;
+          f.v[it] = *reinterpret_cast<const uint4 *>(vc + min(e / (WGC / 8), n - 1) * v_rs +
+                                                     (e % (WGC / 8)) * 8);
+        }
       }
     }
+    if (part != 0) {
 #pragma unroll
-    for (int it = 0; it < NTP; ++it) f.tp[it] = wc[min(tid + THREADS * it, 2 * NFRAG * 64 - 1)];
-    f.sc = wc[Cfg::SC_U4 + min(tid, NSC / 4 - 1)];
+      for (int it = 0; it < NTP; ++it) f.tp[it] = wc[min(tid + THREADS * it, 2 * NFRAG * 64 - 1)];
+      f.sc = wc[Cfg::SC_U4 + min(tid, NSC / 4 - 1)];
+    }
   };
   auto commit = [&](const Fetch &f, int buf) {
     // Nothing of the commit (the conversions of the raw loads above all) may be
@@ -631,14 +639,14 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
 
   };
 
-  fetch(fa, c_begin);
+  fetch(fa, c_begin, 2);
   commit(fa, 0);
   // Everything loaded so far (S0 and the first chunk) has landed.  Said
   // explicitly, so that the compiler's wait tracking does not carry these
   // loads into the loop and wait on later stores for them.  (gfx9 encoding:
   // vmcnt 0, expcnt 7, lgkmcnt 15.)
   __builtin_amdgcn_s_waitcnt(0x0F70);
-  fetch(fb, min(c_begin + 1, c_end - 1));
+  fetch(fb, min(c_begin + 1, c_end - 1), 2);
   lds_barrier();
 
   // One chunk: compute chunk c from LDS buffer (c - c_begin) & 1, load chunk
@@ -657,7 +665,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
     const _Float16 *vT = cV + (4 * g4 + (ln >> 2)) * VST + ic + 4 * (ln & 3);
     // the K whose columns update the state: K itself, or K o e^{gamma_n - gamma} for the key gate
     const _Float16 *uT = KDA ? sKdb + buf * C * KST + (4 * g4 + (ln >> 2)) * KST + 4 * (ln & 3) : kT;
-    fetch(fn, min(c + 2, c_end - 1));
+    fetch(fn, min(c + 2, c_end - 1), 2);
 
     // S fragments (fp16) in kset order over the key channels
     half8 sf[RT][4];

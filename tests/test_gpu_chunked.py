@@ -93,6 +93,10 @@ def test_bf16_small_variants():
     run_case(SMALL.with_(s0_std=0.0, g_mu=2.0), "bf16 small S0=0 fast decay")
     run_case(SMALL.with_(T=130), "bf16 S_T aliases S0", S0_alias=True)
     run_case(SMALL.with_(Hk=6, Hv=6, T=100), "bf16 no grouping")
+    # wide groups: the prep kernel stages the gates of every value head of a
+    # key head (one pass over them at 8 heads, two at 16)
+    run_case(SMALL.with_(B=1, Hk=1, Hv=8, T=150), "bf16 group of 8")
+    run_case(SMALL.with_(B=1, Hk=2, Hv=32, T=90), "bf16 group of 16")
     run_case(KDA_PREFILL.with_(B=1, T=150, Hk=2, Hv=2), "bf16 key gate small")
 
 
