@@ -416,15 +416,21 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
 // ============================================================================
 // chunk_seq: the sequential pass over the chunks of one sequence
 // ============================================================================
-template <int NW, int RT, bool KDA>
+// NW compute waves hold the state, 16 RT value rows each.  LW = 0: every wave
+// also loads the next chunks and writes them to LDS.  LW > 0: LW more waves
+// do all of that instead, so the compute waves issue no loads at all (their
+// only memory traffic is LDS reads and the output stores).
+template <int NW, int RT, bool KDA, int LW>
 struct SeqCfg {
-  static constexpr int THREADS = 64 * NW;      // NW waves, 16 RT value rows of the state each
+  static constexpr int CT = 64 * NW;           // compute threads
+  static constexpr int THREADS = 64 * (NW + LW);
+  static constexpr int LT = LW ? 64 * LW : CT; // threads that load
   static constexpr int WGC = 16 * NW * RT;     // value rows per workgroup
   static constexpr int NS = DV / WGC;          // workgroups per (batch, value head)
   static constexpr int VST = WGC + 8;          // sV row stride
-  static constexpr int NKQ = (C * DK / 8) / THREADS;     // 16-byte K (and Q) pieces per thread
-  static constexpr int NV = (C * WGC / 8) / THREADS;     // 16-byte V pieces per thread
-  static constexpr int NTP = (2 * NFRAG * 64 + THREADS - 1) / THREADS;  // T and P fragment pieces
+  static constexpr int NKQ = (C * DK / 8) / LT;     // 16-byte K (and Q) pieces per loading thread
+  static constexpr int NV = (C * WGC / 8) / LT;     // 16-byte V pieces per loading thread
+  static constexpr int NTP = (2 * NFRAG * 64 + LT - 1) / LT;  // T and P fragment pieces
   static constexpr int NSC = KDA ? C + DK : 5 * C;       // fp32 scalars per chunk
   static constexpr int SC_U4 = KDA ? KDA_SC : GDN_SC;      // their offset in the chunk's workspace
   static constexpr int CHUNK_U4 = KDA ? KDA_CHUNK_U4 : GDN_CHUNK_U4;  // workspace per chunk
@@ -436,13 +442,15 @@ struct SeqCfg {
   static constexpr int OFF_SC = OFF_TP + 2 * 2 * NFRAG * 64 * 16;   // 2 x [NSC] fp32
   static constexpr int SMEM = OFF_SC + 2 * NSC * 4;
   static_assert(SMEM <= 160 * 1024, "LDS");
+  static_assert((C * DK / 8) % LT == 0 && (C * WGC / 8) % LT == 0, "loads per thread");
+  static_assert(LT >= NSC / 4, "one scalar piece per loading thread");
 };
 
 // The next chunk's raw loads.  Nothing is converted here, so no instruction
 // needs the data before the chunk is committed.
-template <typename TQ, typename TG, int NW, int RT, bool KDA>
+template <typename TQ, typename TG, int NW, int RT, bool KDA, int LW>
 struct SeqFetch {
-  using Cfg = SeqCfg<NW, RT, KDA>;
+  using Cfg = SeqCfg<NW, RT, KDA, LW>;
   uint4 k[Cfg::NKQ], q[Cfg::NKQ], kd[KDA ? Cfg::NKQ : 1], v[Cfg::NV], tp[Cfg::NTP], sc;
   int n;
 };
@@ -451,15 +459,15 @@ struct SeqFetch {
 // from the workspace.  KDA true: key-channel gate; the decayed K, Q, the
 // state-update K, beta and Gamma_n come from the workspace (q, k, g, beta are
 // not read) and the state decays per key channel.
-template <typename TQ, typename TG, int NW, int RT, bool KDA>
-__global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
+template <typename TQ, typename TG, int NW, int RT, bool KDA, int LW>
+__global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *__restrict__ v,
     const TG *__restrict__ g, const TG *__restrict__ beta, const uint4 *__restrict__ ws,
     const float *__restrict__ S0, float *__restrict__ o, float *__restrict__ ST, int T, int Hk,
     int Hv, int ntasks, int nchunks, int c_begin, int c_end) {
-  using Cfg = SeqCfg<NW, RT, KDA>;
+  using Cfg = SeqCfg<NW, RT, KDA, LW>;
   constexpr int NSC = Cfg::NSC;
-  constexpr int THREADS = Cfg::THREADS, WGC = Cfg::WGC, NS = Cfg::NS, VST = Cfg::VST;
+  constexpr int LT = Cfg::LT, WGC = Cfg::WGC, NS = Cfg::NS, VST = Cfg::VST;
   constexpr int NKQ = Cfg::NKQ, NV = Cfg::NV, NTP = Cfg::NTP;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
@@ -474,28 +482,16 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
   const int kh = h / (Hv / Hk);
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, g4 = l >> 4, ln = l & 15;
-  const int ic = w * 16 * RT;             // this wave's first value row within the workgroup
-  const int iw0 = slice * WGC + ic;       // ... within the head
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
+  const int l = tid & 63, g4 = l >> 4, ln = l & 15;
+  const int ltid = LW ? tid - Cfg::CT : tid;                 // index among the loading threads
 
-  // Per-sequence bases (uniform) and per-thread offsets (fixed for all chunks).
+  // Per-sequence bases (uniform) and per-thread load offsets (fixed for all chunks).
   const int kq_rs = Hk * DK, v_rs = Hv * DV;        // row strides of q/k and v (elements)
   const TQ *kb = k + ((size_t)b * T * Hk + kh) * DK;
   const TQ *qb = q + ((size_t)b * T * Hk + kh) * DK;
   const TQ *vb = v + ((size_t)b * T * Hv + h) * DV + slice * WGC;
-  float *ob = o + ((size_t)b * T * Hv + h) * DV + iw0 + 4 * g4;
   const uint4 *wsbh = ws + (size_t)bh * nchunks * Cfg::CHUNK_U4;
-  int kq_off[NKQ], v_off[NV];
-#pragma unroll
-  for (int it = 0; it < NKQ; ++it) {
-    const int e = tid + THREADS * it;
-    kq_off[it] = (e >> 4) * kq_rs + (e & 15) * 8;
-  }
-#pragma unroll
-  for (int it = 0; it < NV; ++it) {
-    const int e = tid + THREADS * it;
-    v_off[it] = (e / (WGC / 8)) * v_rs + (e % (WGC / 8)) * 8;
-  }
 
   _Float16 *const sKb = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_K);
   _Float16 *const sQb = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_Q);
@@ -503,6 +499,107 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
   _Float16 *const sVb = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_V);
   uint4 *const sTPb = reinterpret_cast<uint4 *>(smem + Cfg::OFF_TP);
   float *const sScb = reinterpret_cast<float *>(smem + Cfg::OFF_SC);
+
+  using Fetch = SeqFetch<TQ, TG, NW, RT, KDA, LW>;
+  // part 0: K and Q (and the key gate's state-update K); part 1: V, the T
+  // and P fragments and the scalars; part 2: both
+  auto fetch = [&](Fetch &f, int c, int part) {
+    const int n = min(C, T - c * C);
+    f.n = n;
+    const size_t t0 = (size_t)c * C;
+    const uint4 *wc = wsbh + (size_t)c * Cfg::CHUNK_U4;
+    const TQ *kc = kb + t0 * kq_rs, *qc = qb + t0 * kq_rs, *vc = vb + t0 * v_rs;
+    if (KDA && part != 1) {
+      // rows past the end of the sequence are zero in the workspace
+#pragma unroll
+      for (int it = 0; it < NKQ; ++it) {
+        const int e = ltid + LT * it;
+        f.k[it] = wc[KDA_KG + e];
+        f.q[it] = wc[KDA_QG + e];
+        f.kd[it] = wc[KDA_KD + e];
+      }
+    }
+    // rows past the end of the sequence (last chunk) re-read its last row
+#pragma unroll
+    for (int it = 0; it < NKQ; ++it) {
+      const int e = ltid + LT * it;
+      const int off = min(e >> 4, n - 1) * kq_rs + (e & 15) * 8;
+      if (!KDA && part != 1) {
+        f.k[it] = *reinterpret_cast<const uint4 *>(kc + off);
+        f.q[it] = *reinterpret_cast<const uint4 *>(qc + off);
+      }
+    }
+    if (part != 0) {
+#pragma unroll
+      for (int it = 0; it < NV; ++it) {
+        const int e = ltid + LT * it;
+        f.v[it] = *reinterpret_cast<const uint4 *>(vc + min(e / (WGC / 8), n - 1) * v_rs +
+                                                   (e % (WGC / 8)) * 8);
+      }
+#pragma unroll
+      for (int it = 0; it < NTP; ++it) f.tp[it] = wc[min(ltid + LT * it, 2 * NFRAG * 64 - 1)];
+      f.sc = wc[Cfg::SC_U4 + min(ltid, NSC / 4 - 1)];
+    }
+  };
+  auto commit = [&](const Fetch &f, int buf) {
+    // Nothing of the commit (the conversions of the raw loads above all) may be
+    // scheduled into the chunk's arithmetic: that would wait for the loads there.
+    __builtin_amdgcn_sched_barrier(0);
+    _Float16 *k_ = sKb + buf * C * KST, *q_ = sQb + buf * C * KST, *v_ = sVb + buf * C * VST;
+    // K and Q (and the state-update K) are fp16 in the workspace of the key gate
+    using TK = typename std::conditional<KDA, f16_t, TQ>::type;
+    const half8 hz = {};
+    if (ltid < NSC / 4) reinterpret_cast<uint4 *>(sScb + buf * NSC)[ltid] = f.sc;
+#pragma unroll
+    for (int it = 0; it < NKQ; ++it) {
+      const int e = ltid + LT * it;
+      // last chunk of a ragged sequence: rows past its end are zero
+      const bool ok = KDA || (e >> 4) < f.n;
+      const int off = (e >> 4) * KST + (e & 15) * 8;
+      *reinterpret_cast<half8 *>(k_ + off) = ok ? to_half8(f.k[it], TK{}) : hz;
+      *reinterpret_cast<half8 *>(q_ + off) = ok ? to_half8(f.q[it], TK{}) : hz;
+      if constexpr (KDA) *reinterpret_cast<half8 *>(sKdb + buf * C * KST + off) = to_half8(f.kd[it], f16_t{});
+    }
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+      const int e = ltid + LT * it;
+      const int row = e / (WGC / 8);
+      *reinterpret_cast<half8 *>(v_ + row * VST + (e % (WGC / 8)) * 8) =
+          row < f.n ? to_half8(f.v[it], TQ{}) : hz;
+    }
+#pragma unroll
+    for (int it = 0; it < NTP; ++it) {
+      const int e = ltid + LT * it;
+      if (e < 2 * NFRAG * 64) sTPb[buf * 2 * NFRAG * 64 + e] = f.tp[it];
+    }
+  };
+
+  if (LW > 0 && w >= NW) {
+    // Loading waves: chunk c + 2 is loaded while chunk c is computed, and
+    // chunk c + 1, loaded one chunk earlier, is written to the other LDS
+    // buffer.  These waves issue no stores, so each wait for a chunk's loads
+    // is exact.  The loads are unconditional (a repeated chunk near the end),
+    // and the barriers match the compute waves' one per chunk.
+    Fetch fa, fb;
+    fetch(fa, c_begin, 2);
+    commit(fa, 0);
+    fetch(fb, min(c_begin + 1, c_end - 1), 2);
+    lds_barrier();
+    auto lstep = [&](int c, Fetch &fn, const Fetch &fc) {
+      fetch(fn, min(c + 2, c_end - 1), 2);
+      if (c + 1 < c_end) commit(fc, ((c - c_begin) & 1) ^ 1);
+      lds_barrier();
+    };
+    for (int c = c_begin; c < c_end; c += 2) {
+      lstep(c, fa, fb);
+      if (c + 1 < c_end) lstep(c + 1, fb, fa);
+    }
+    return;
+  }
+
+  const int ic = w * 16 * RT;             // this wave's first value row within the workgroup
+  const int iw0 = slice * WGC + ic;       // ... within the head
+  float *ob = o + ((size_t)b * T * Hv + h) * DV + iw0 + 4 * g4;
 
   // state: row tile t (value rows iw0 + 16 t ..), tiles J of S^T; the lane
   // holds S[iw0 + 16 t + ln][16 J + 4 g4 + ii]
@@ -520,143 +617,11 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
       accS[t][J] = s;
     }
 
-  using Fetch = SeqFetch<TQ, TG, NW, RT, KDA>;
-  Fetch fa, fb;   // the next two chunks' raw loads (prefetch distance 2)
-  // part 0: K and Q (and the key gate's state-update K); part 1: V, the T
-  // and P fragments and the scalars; part 2: both
-  auto fetch = [&](Fetch &f, int c, int part) {
-    const int n = min(C, T - c * C);
-    f.n = n;
-    const size_t t0 = (size_t)c * C;
-    const uint4 *wc = wsbh + (size_t)c * Cfg::CHUNK_U4;
-    const TQ *kc = kb + t0 * kq_rs, *qc = qb + t0 * kq_rs, *vc = vb + t0 * v_rs;
-    if (KDA && part != 1) {
-      // rows past the end of the sequence are zero in the workspace
-#pragma unroll
-      for (int it = 0; it < NKQ; ++it) {
-        const int e = tid + THREADS * it;
-        f.k[it] = wc[KDA_KG + e];
-        f.q[it] = wc[KDA_QG + e];
-        f.kd[it] = wc[KDA_KD + e];
-      }
-    }
-    if (n == C) {
-      if (!KDA && part != 1) {
-#pragma unroll
-        for (int it = 0; it < NKQ; ++it) {
-          f.k[it] = *reinterpret_cast<const uint4 *>(kc + kq_off[it]);
-          f.q[it] = *reinterpret_cast<const uint4 *>(qc + kq_off[it]);
-        }
-      }
-      if (part != 0) {
-#pragma unroll
-        for (int it = 0; it < NV; ++it) f.v[it] = *reinterpret_cast<const uint4 *>(vc + v_off[it]);
-      }
-    } else {
-      // last chunk: rows past the end of the sequence re-read its last row
-      if (!KDA && part != 1) {
-#pragma unroll
-        for (int it = 0; it < NKQ; ++it) {
-          const int e = tid + THREADS * it;
-          const int off = min(e >> 4, n - 1) * kq_rs + (e & 15) * 8;
-          f.k[it] = *reinterpret_cast<const uint4 *>(kc + off);
-          f.q[it] = *reinterpret_cast<const uint4 *>(qc + off);
-        }
-      }
-      if (part != 0) {
-#pragma unroll
-        for (int it = 0; it < NV; ++it) {
-          const int e = tid + THREADS * it;
-          f.v[it] = *reinterpret_cast<const uint4 *>(vc + min(e / (WGC / 8), n - 1) * v_rs +
-                                                     (e % (WGC / 8)) * 8);
-        }
-      }
-    }
-    if (part != 0) {
-#pragma unroll
-      for (int it = 0; it < NTP; ++it) f.tp[it] = wc[min(tid + THREADS * it, 2 * NFRAG * 64 - 1)];
-      f.sc = wc[Cfg::SC_U4 + min(tid, NSC / 4 - 1)];
-    }
-  };
-  auto commit = [&](const Fetch &f, int buf) {
-    // Nothing of the commit (the conversions of the raw loads above all) may be
-    // scheduled into the chunk's arithmetic: that would wait for the loads there.
-    __builtin_amdgcn_sched_barrier(0);
-    _Float16 *k_ = sKb + buf * C * KST, *q_ = sQb + buf * C * KST, *v_ = sVb + buf * C * VST;
-    // K and Q (and the state-update K) are fp16 in the workspace of the key gate
-    using TK = typename std::conditional<KDA, f16_t, TQ>::type;
-    if constexpr (KDA) {
-      _Float16 *kd_ = sKdb + buf * C * KST;
-#pragma unroll
-      for (int it = 0; it < NKQ; ++it) {
-        const int e = tid + THREADS * it;
-        *reinterpret_cast<half8 *>(k_ + (e >> 4) * KST + (e & 15) * 8) = to_half8(f.k[it], f16_t{});
-        *reinterpret_cast<half8 *>(q_ + (e >> 4) * KST + (e & 15) * 8) = to_half8(f.q[it], f16_t{});
-        *reinterpret_cast<half8 *>(kd_ + (e >> 4) * KST + (e & 15) * 8) = to_half8(f.kd[it], f16_t{});
-      }
-    }
-    if (tid < NSC / 4) reinterpret_cast<uint4 *>(sScb + buf * NSC)[tid] = f.sc;
-    if (f.n == C) {
-      if constexpr (!KDA) {
-#pragma unroll
-        for (int it = 0; it < NKQ; ++it) {
-          const int e = tid + THREADS * it;
-          *reinterpret_cast<half8 *>(k_ + (e >> 4) * KST + (e & 15) * 8) = to_half8(f.k[it], TK{});
-          *reinterpret_cast<half8 *>(q_ + (e >> 4) * KST + (e & 15) * 8) = to_half8(f.q[it], TK{});
-        }
-      }
-#pragma unroll
-      for (int it = 0; it < NV; ++it) {
-        const int e = tid + THREADS * it;
-        *reinterpret_cast<half8 *>(v_ + (e / (WGC / 8)) * VST + (e % (WGC / 8)) * 8) =
-            to_half8(f.v[it], TQ{});
-      }
-    } else {
-      // last chunk of a ragged sequence: rows past its end are zero
-      const half8 hz = {};
-      if constexpr (!KDA) {
-#pragma unroll
-        for (int it = 0; it < NKQ; ++it) {
-          const int e = tid + THREADS * it;
-          const bool ok = (e >> 4) < f.n;
-          *reinterpret_cast<half8 *>(k_ + (e >> 4) * KST + (e & 15) * 8) = ok ? to_half8(f.k[it], TK{}) : hz;
-          *reinterpret_cast<half8 *>(q_ + (e >> 4) * KST + (e & 15) * 8) = ok ? to_half8(f.q[it], TK{}) : hz;
-        }
-      }
-#pragma unroll
-      for (int it = 0; it < NV; ++it) {
-        const int e = tid + THREADS * it;
-        const int row = e / (WGC / 8);
-        *reinterpret_cast<half8 *>(v_ + row * VST + (e % (WGC / 8)) * 8) =
-            row < f.n ? to_half8(f.v[it], TQ{}) : hz;
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < NTP; ++it) {
-      const int e = tid + THREADS * it;
-      if (e < 2 * NFRAG * 64) sTPb[buf * 2 * NFRAG * 64 + e] = f.tp[it];
-    }
-
-  };
-
-  fetch(fa, c_begin, 2);
-  commit(fa, 0);
-  // Everything loaded so far (S0 and the first chunk) has landed.  Said
-  // explicitly, so that the compiler's wait tracking does not carry these
-  // loads into the loop and wait on later stores for them.  (gfx9 encoding:
-  // vmcnt 0, expcnt 7, lgkmcnt 15.)
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  fetch(fb, min(c_begin + 1, c_end - 1), 2);
-  lds_barrier();
-
-  // One chunk: compute chunk c from LDS buffer (c - c_begin) & 1, load chunk
-  // c + 2 into fn (fn's previous chunk is already in LDS), and commit chunk
-  // c + 1, loaded one chunk earlier, from fc into the other buffer.  The load
-  // is unconditional (a repeated chunk near the end) so that the number of
-  // loads in flight, which every wait counts, is the same on every path.
-  auto step = [&](int c, Fetch &fn, const Fetch &fc) {
+  // The arithmetic of chunk c, from LDS buffer (c - c_begin) & 1: the state
+  // moves on to the chunk's end and accO gets the chunk's outputs O^T.
+  float4v accO[RT][4];
+  auto compute = [&](int c) {
     const int buf = (c - c_begin) & 1;
-    const int t0 = c * C;
     const _Float16 *cK = sKb + buf * C * KST, *cQ = sQb + buf * C * KST, *cV = sVb + buf * C * VST;
     const uint4 *cT = sTPb + buf * 2 * NFRAG * 64, *cP = cT + NFRAG * 64;
     const float *sc = sScb + buf * NSC;
@@ -665,7 +630,6 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
     const _Float16 *vT = cV + (4 * g4 + (ln >> 2)) * VST + ic + 4 * (ln & 3);
     // the K whose columns update the state: K itself, or K o e^{gamma_n - gamma} for the key gate
     const _Float16 *uT = KDA ? sKdb + buf * C * KST + (4 * g4 + (ln >> 2)) * KST + 4 * (ln & 3) : kT;
-    fetch(fn, min(c + 2, c_end - 1), 2);
 
     // S fragments (fp16) in kset order over the key channels
     half8 sf[RT][4];
@@ -676,7 +640,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
 
     // K S^T (rows r = 16 R + 4 g4 + ii, value row ln) and S Q^T (transposed read);
     // each K and Q fragment serves every row tile of the wave
-    float4v accX[RT][4], accO[RT][4];
+    float4v accX[RT][4];
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
       half8 kf[4], qf[4];
@@ -739,7 +703,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
       }
     }
 
-    // O^T = Gamma (S Q^T) + N^T P^T:  row r = 16 R + ln of this lane (stored after the commit)
+    // O^T = Gamma (S Q^T) + N^T P^T:  row r = 16 R + ln of this lane
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
       const int r = 16 * R + ln;
@@ -790,12 +754,9 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
         }
       }
     }
-
-    if (c + 1 < c_end) commit(fc, buf ^ 1);
-    // The output stores go out only now.  On this architecture one counter
-    // tracks both loads and stores, and a wait for a load while stores are in
-    // flight also waits for the stores; issued after the commit, they have the
-    // next chunk's arithmetic to complete before its commit waits again.
+  };
+  auto store_o = [&](int c) {
+    const int t0 = c * C;
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
       const int r = 16 * R + ln;
@@ -805,11 +766,49 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
           *reinterpret_cast<float4 *>(ob + (size_t)(t0 + r) * v_rs + 16 * t) =
               make_float4(accO[t][R][0], accO[t][R][1], accO[t][R][2], accO[t][R][3]);
     }
-    lds_barrier();
   };
-  for (int c = c_begin; c < c_end; c += 2) {
-    step(c, fa, fb);
-    if (c + 1 < c_end) step(c + 1, fb, fa);
+
+  if constexpr (LW > 0) {
+    // Compute waves: no loads after the entering state, so the output stores
+    // never hold up a wait.
+    lds_barrier();
+    for (int c = c_begin; c < c_end; ++c) {
+      compute(c);
+      store_o(c);
+      lds_barrier();
+    }
+  } else {
+    Fetch fa, fb;   // the next two chunks' raw loads (prefetch distance 2)
+    fetch(fa, c_begin, 2);
+    commit(fa, 0);
+    // Everything loaded so far (S0 and the first chunk) has landed.  Said
+    // explicitly, so that the compiler's wait tracking does not carry these
+    // loads into the loop and wait on later stores for them.  (gfx9 encoding:
+    // vmcnt 0, expcnt 7, lgkmcnt 15.)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    fetch(fb, min(c_begin + 1, c_end - 1), 2);
+    lds_barrier();
+
+    // One chunk: compute chunk c, load chunk c + 2 into fn (fn's previous
+    // chunk is already in LDS), and commit chunk c + 1, loaded one chunk
+    // earlier, from fc into the other buffer.  The load is unconditional (a
+    // repeated chunk near the end) so that the number of loads in flight,
+    // which every wait counts, is the same on every path.
+    auto step = [&](int c, Fetch &fn, const Fetch &fc) {
+      fetch(fn, min(c + 2, c_end - 1), 2);
+      compute(c);
+      if (c + 1 < c_end) commit(fc, ((c - c_begin) & 1) ^ 1);
+      // The output stores go out only now.  On this architecture one counter
+      // tracks both loads and stores, and a wait for a load while stores are
+      // in flight also waits for the stores; issued after the commit, they
+      // have the next chunk's arithmetic to complete before its commit waits.
+      store_o(c);
+      lds_barrier();
+    };
+    for (int c = c_begin; c < c_end; c += 2) {
+      step(c, fa, fb);
+      if (c + 1 < c_end) step(c + 1, fb, fa);
+    }
   }
 
   // final state
@@ -821,12 +820,12 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_seq_kernel(
           make_float4(accS[t][J][0], accS[t][J][1], accS[t][J][2], accS[t][J][3]);
 }
 
-template <typename TQ, typename TG, int NW, int RT, bool KDA>
+template <typename TQ, typename TG, int NW, int RT, bool KDA, int LW>
 hipError_t launch_seq(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
                       const void *beta, const uint4 *TPws, const float *S0, float *o, float *ST,
                       int nchunks, int c_begin, int c_end, hipStream_t st) {
-  using Cfg = SeqCfg<NW, RT, KDA>;
-  auto kern = chunk_seq_kernel<TQ, TG, NW, RT, KDA>;
+  using Cfg = SeqCfg<NW, RT, KDA, LW>;
+  auto kern = chunk_seq_kernel<TQ, TG, NW, RT, KDA, LW>;
   hipError_t e =
       hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::SMEM);
   if (e != hipSuccess) return e;
@@ -946,8 +945,8 @@ hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v
   // but measures slower: the two waves per SIMD hide each other's latency.)
   const bool wide = (long)sh.B * sh.Hv >= 160;
   auto seq = [&](int cb, int ce, const float *s0, hipStream_t s) {
-    return wide ? launch_seq<TQ, TG, 8, 1, false>(sh, q, k, v, g, beta, TPws, s0, o, ST, nchunks, cb, ce, s)
-                : launch_seq<TQ, TG, 4, 1, false>(sh, q, k, v, g, beta, TPws, s0, o, ST, nchunks, cb, ce, s);
+    return wide ? launch_seq<TQ, TG, 8, 1, false, 4>(sh, q, k, v, g, beta, TPws, s0, o, ST, nchunks, cb, ce, s)
+                : launch_seq<TQ, TG, 4, 1, false, 4>(sh, q, k, v, g, beta, TPws, s0, o, ST, nchunks, cb, ce, s);
   };
   // overlap when the pass uses at most half of the 256 compute units
   return pipelined(nchunks, (long)sh.B * sh.Hv * (wide ? 1 : 2) <= 128, S0, ST, st, prep, seq);
@@ -1231,7 +1230,7 @@ hipError_t launch_kda_t(const Shape &sh, const void *q, const void *k, const voi
   // The decayed K, Q and the state-update K all live in LDS here, so the
   // sequential pass uses 4-wave workgroups (64 value rows each).
   auto seq = [&](int cb, int ce, const float *s0, hipStream_t s) {
-    return launch_seq<TQ, TG, 4, 1, true>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks, cb, ce, s);
+    return launch_seq<TQ, TG, 4, 1, true, 4>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks, cb, ce, s);
   };
   return pipelined(nchunks, (long)sh.B * sh.Hv * 2 <= 128, S0, ST, st, prep, seq);
 }
