@@ -38,24 +38,26 @@
 //    G = K K^T and P0 = masked Q K^T once; then per value head of the group
 //    A and T = (I + A)^{-1} (16 x 16 diagonal blocks by forward substitution
 //    in fp32, wave w -> block w; off-diagonal blocks column by column with
-//    16x16x16 MFMAs, wave w -> column w: T_RS = -T_RR sum_M A_RM T_MS).  T (per
-//    value head) and P0 (per key head) go to the workspace as 64 x 64
+//    16x16x16 MFMAs, wave w -> column w: T_RS = -T_RR sum_M A_RM T_MS), and
+//    P = L o P0.  T and P (per value head) go to the workspace as 64 x 64
 //    lower-triangular matrices in fragment order: six 1 KB fragments each,
 //    lane (g, l) of fragment (R, kk) holding row 16 R + l at columns kset(g, kk).
-//  * chunk_seq (the chunks of one sequence in order): a 256-thread workgroup
-//    owns 4 * DW value rows of the state of one (batch, value head); wave w
-//    owns DW of them (rows evolve independently) for all 64 rows of a chunk,
-//    in fp32 accumulators.  Its whole chain stays in registers:
+//  * chunk_seq (the chunks of one sequence in order): a workgroup owns 32,
+//    64 or 128 value rows of the state of one (batch, value head); each of
+//    its compute waves owns 16 or 32 of them (rows evolve independently) for
+//    all 64 rows of a chunk, in fp32 accumulators.  Its whole chain stays in
+//    registers:
 //        S (fp32) -> S fragments (fp16)                    [no data movement]
 //        X = beta V - beta Gamma K S^T                     (K from LDS)
-//        N = T X,  N~ = diag(e^{gamma_n - gamma}) N        (T from memory)
-//        O^T = Gamma (S Q^T) + N^T (L o P0)^T -> HBM       (Q from LDS, P0 from memory)
+//        N = T X,  N~ = diag(e^{gamma_n - gamma}) N        (T from LDS)
+//        O^T = Gamma (S Q^T) + N^T P^T -> HBM              (Q, P from LDS)
 //        S^T <- Gamma_n S^T + K^T N~                       (K columns from LDS)
-//    so the four waves share only the chunk's K, Q, V tiles and gate scalars,
-//    double-buffered in LDS: one barrier per chunk.  The next chunk's raw
-//    loads (and its T and P0 fragments) are issued at the top of a chunk and
-//    land at its end.  Blocks are numbered so that workgroups sharing a key
-//    head run on one XCD (shared K, Q and P0 then hit in its L2).
+//    so the compute waves share only the chunk's K, Q, V tiles, T, P and
+//    gate scalars, double-buffered in LDS: one barrier per chunk.  Four
+//    more waves (one per SIMD) do all the loading: chunk c + 2 is fetched
+//    and chunk c + 1 written to LDS while chunk c is computed.  Blocks are
+//    numbered so that workgroups sharing a key head run on one XCD (shared
+//    K and Q then hit in its L2).
 #include <algorithm>
 #include <map>
 #include <mutex>
@@ -232,7 +234,7 @@ constexpr int KDA_NSC = (C + DK) / 4;
 constexpr int KDA_CHUNK_U4 = (KDA_SC + KDA_NSC + 15) / 16 * 16;
 
 // ============================================================================
-// chunk_prep: P0 per (chunk, key head), T = (I + A)^{-1} per (chunk, value head)
+// chunk_prep: per (chunk, key head) P0 = masked Q K^T; per (chunk, value head) T = (I + A)^{-1}, P = L o P0
 // ============================================================================
 // K and Q are only read before the value-head loop (into the G and P0
 // accumulators); the per-head matrices then reuse their space.
@@ -416,15 +418,15 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
 // ============================================================================
 // chunk_seq: the sequential pass over the chunks of one sequence
 // ============================================================================
-// NW compute waves hold the state, 16 RT value rows each.  LW = 0: every wave
-// also loads the next chunks and writes them to LDS.  LW > 0: LW more waves
-// do all of that instead, so the compute waves issue no loads at all (their
-// only memory traffic is LDS reads and the output stores).
+// NW compute waves hold the state, 16 RT value rows each; LW more waves load
+// the next chunks and write them to LDS, so the compute waves issue no loads
+// at all (their only memory traffic is LDS reads and the output stores, and
+// a wait for a load never waits for stores).
 template <int NW, int RT, bool KDA, int LW>
 struct SeqCfg {
   static constexpr int CT = 64 * NW;           // compute threads
   static constexpr int THREADS = 64 * (NW + LW);
-  static constexpr int LT = LW ? 64 * LW : CT; // threads that load
+  static constexpr int LT = 64 * LW;           // loading threads
   static constexpr int WGC = 16 * NW * RT;     // value rows per workgroup
   static constexpr int NS = DV / WGC;          // workgroups per (batch, value head)
   static constexpr int VST = WGC + 8;          // sV row stride
@@ -443,7 +445,7 @@ struct SeqCfg {
   static constexpr int SMEM = OFF_SC + 2 * NSC * 4;
   static_assert(SMEM <= 160 * 1024, "LDS");
   static_assert((C * DK / 8) % LT == 0 && (C * WGC / 8) % LT == 0, "loads per thread");
-  static_assert(LT >= NSC / 4, "one scalar piece per loading thread");
+  static_assert(LW > 0 && LT >= NSC / 4, "one scalar piece per loading thread");
 };
 
 // The next chunk's raw loads.  Nothing is converted here, so no instruction
@@ -484,7 +486,7 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
   const int l = tid & 63, g4 = l >> 4, ln = l & 15;
-  const int ltid = LW ? tid - Cfg::CT : tid;                 // index among the loading threads
+  const int ltid = tid - Cfg::CT;                           // index among the loading threads
 
   // Per-sequence bases (uniform) and per-thread load offsets (fixed for all chunks).
   const int kq_rs = Hk * DK, v_rs = Hv * DV;        // row strides of q/k and v (elements)
@@ -542,8 +544,7 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
     }
   };
   auto commit = [&](const Fetch &f, int buf) {
-    // Nothing of the commit (the conversions of the raw loads above all) may be
-    // scheduled into the chunk's arithmetic: that would wait for the loads there.
+    // The loads issued before the commit stay ahead of its conversions.
     __builtin_amdgcn_sched_barrier(0);
     _Float16 *k_ = sKb + buf * C * KST, *q_ = sQb + buf * C * KST, *v_ = sVb + buf * C * VST;
     // K and Q (and the state-update K) are fp16 in the workspace of the key gate
@@ -574,7 +575,7 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
     }
   };
 
-  if (LW > 0 && w >= NW) {
+  if (w >= NW) {
     // Loading waves: chunk c + 2 is loaded while chunk c is computed, and
     // chunk c + 1, loaded one chunk earlier, is written to the other LDS
     // buffer.  These waves issue no stores, so each wait for a chunk's loads
@@ -768,47 +769,13 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
     }
   };
 
-  if constexpr (LW > 0) {
-    // Compute waves: no loads after the entering state, so the output stores
-    // never hold up a wait.
+  // No loads after the entering state, so the output stores never hold up a
+  // wait.
+  lds_barrier();
+  for (int c = c_begin; c < c_end; ++c) {
+    compute(c);
+    store_o(c);
     lds_barrier();
-    for (int c = c_begin; c < c_end; ++c) {
-      compute(c);
-      store_o(c);
-      lds_barrier();
-    }
-  } else {
-    Fetch fa, fb;   // the next two chunks' raw loads (prefetch distance 2)
-    fetch(fa, c_begin, 2);
-    commit(fa, 0);
-    // Everything loaded so far (S0 and the first chunk) has landed.  Said
-    // explicitly, so that the compiler's wait tracking does not carry these
-    // loads into the loop and wait on later stores for them.  (gfx9 encoding:
-    // vmcnt 0, expcnt 7, lgkmcnt 15.)
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    fetch(fb, min(c_begin + 1, c_end - 1), 2);
-    lds_barrier();
-
-    // One chunk: compute chunk c, load chunk c + 2 into fn (fn's previous
-    // chunk is already in LDS), and commit chunk c + 1, loaded one chunk
-    // earlier, from fc into the other buffer.  The load is unconditional (a
-    // repeated chunk near the end) so that the number of loads in flight,
-    // which every wait counts, is the same on every path.
-    auto step = [&](int c, Fetch &fn, const Fetch &fc) {
-      fetch(fn, min(c + 2, c_end - 1), 2);
-      compute(c);
-      if (c + 1 < c_end) commit(fc, ((c - c_begin) & 1) ^ 1);
-      // The output stores go out only now.  On this architecture one counter
-      // tracks both loads and stores, and a wait for a load while stores are
-      // in flight also waits for the stores; issued after the commit, they
-      // have the next chunk's arithmetic to complete before its commit waits.
-      store_o(c);
-      lds_barrier();
-    };
-    for (int c = c_begin; c < c_end; c += 2) {
-      step(c, fa, fb);
-      if (c + 1 < c_end) step(c + 1, fb, fa);
-    }
   }
 
   // final state
@@ -921,6 +888,11 @@ hipError_t pipelined(int nchunks, bool overlap, const float *S0, float *ST, hipS
   return e;
 }
 
+// Overlap the preparation of later segments with the sequential pass when
+// the pass leaves room on the GPU: few sequences, each long (the pass then
+// has at most 192 workgroups).
+inline bool seq_overlap(long heads) { return heads <= 48; }
+
 template <typename TQ, typename TG>
 hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
                     const void *beta, const float *S0, float *o, float *ST, void *ws, hipStream_t st) {
@@ -939,17 +911,19 @@ hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v
                        nchunks, cb);
     return hipGetLastError();
   };
-  // One 8-wave workgroup per head (two waves per SIMD) when that fills the GPU,
-  // else two 4-wave workgroups per head for more parallel chains.  (One wave
-  // per SIMD holding two row tiles, RT = 2, halves the fragment reads from LDS
-  // but measures slower: the two waves per SIMD hide each other's latency.)
-  const bool wide = (long)sh.B * sh.Hv >= 160;
+  // Workgroups of the sequential pass: as few per head as keep every one of
+  // them resident (one per compute unit).  128 value rows: four compute waves
+  // holding two row tiles each (a K or Q fragment read from LDS then serves
+  // two tiles); 64 and 32 rows: one row tile per compute wave.
+  const long heads = (long)sh.B * sh.Hv;
   auto seq = [&](int cb, int ce, const float *s0, hipStream_t s) {
-    return wide ? launch_seq<TQ, TG, 8, 1, false, 4>(sh, q, k, v, g, beta, TPws, s0, o, ST, nchunks, cb, ce, s)
-                : launch_seq<TQ, TG, 4, 1, false, 4>(sh, q, k, v, g, beta, TPws, s0, o, ST, nchunks, cb, ce, s);
+    if (heads > 128)
+      return launch_seq<TQ, TG, 4, 2, false, 4>(sh, q, k, v, g, beta, TPws, s0, o, ST, nchunks, cb, ce, s);
+    if (heads > 64)
+      return launch_seq<TQ, TG, 4, 1, false, 4>(sh, q, k, v, g, beta, TPws, s0, o, ST, nchunks, cb, ce, s);
+    return launch_seq<TQ, TG, 2, 1, false, 4>(sh, q, k, v, g, beta, TPws, s0, o, ST, nchunks, cb, ce, s);
   };
-  // overlap when the pass uses at most half of the 256 compute units
-  return pipelined(nchunks, (long)sh.B * sh.Hv * (wide ? 1 : 2) <= 128, S0, ST, st, prep, seq);
+  return pipelined(nchunks, seq_overlap(heads), S0, ST, st, prep, seq);
 }
 
 // ============================================================================
@@ -1227,12 +1201,15 @@ hipError_t launch_kda_t(const Shape &sh, const void *q, const void *k, const voi
                        nchunks, cb);
     return hipGetLastError();
   };
-  // The decayed K, Q and the state-update K all live in LDS here, so the
-  // sequential pass uses 4-wave workgroups (64 value rows each).
+  // The decayed K, Q and the state-update K all live in LDS here, so a
+  // workgroup of the sequential pass holds at most 64 value rows.
+  const long heads = (long)sh.B * sh.Hv;
   auto seq = [&](int cb, int ce, const float *s0, hipStream_t s) {
-    return launch_seq<TQ, TG, 4, 1, true, 4>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks, cb, ce, s);
+    if (heads > 64)
+      return launch_seq<TQ, TG, 4, 1, true, 4>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks, cb, ce, s);
+    return launch_seq<TQ, TG, 2, 1, true, 4>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks, cb, ce, s);
   };
-  return pipelined(nchunks, (long)sh.B * sh.Hv * 2 <= 128, S0, ST, st, prep, seq);
+  return pipelined(nchunks, seq_overlap(heads), S0, ST, st, prep, seq);
 }
 
 }  // namespace

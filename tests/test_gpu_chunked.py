@@ -100,6 +100,18 @@ def test_bf16_small_variants():
     run_case(KDA_PREFILL.with_(B=1, T=150, Hk=2, Hv=2), "bf16 key gate small")
 
 
+# The sequential pass sizes its workgroups by the number of (batch, value
+# head) pairs: 32 value rows up to 64 pairs, 64 rows up to 128, 128 above.
+@pytest.mark.parametrize("B,Hk,Hv", [(2, 8, 32), (3, 8, 40), (3, 16, 48)])
+def test_bf16_workgroup_shapes(B, Hk, Hv):
+    run_case(SMALL.with_(B=B, Hk=Hk, Hv=Hv, T=130), "bf16 %d sequences x %d heads" % (B, Hv))
+
+
+@pytest.mark.parametrize("B,H", [(2, 32), (3, 30)])
+def test_key_gate_workgroup_shapes(B, H):
+    run_case(KDA_PREFILL.with_(B=B, T=100, Hk=H, Hv=H), "key gate %d sequences x %d heads" % (B, H))
+
+
 # ---------------------------------------------------------------- key-channel gate, matrix cores
 KDA_SMALL = KDA_PREFILL.with_(B=2, T=150, Hk=1, Hv=3, s0_std=0.05)
 
