@@ -10,6 +10,7 @@ fallback of any kind.  PyTorch provides device memory and streams.
 Entry points (same names as the C functions):
   prologue(xq, xk, xv, conv_w, out_dtype, eps) -> (q, k, v)
   fwd_chunked(q, k, v, g, beta, S0, chunk) -> (o, S_T)
+  fwd_chunked_conv(xq, xk, xv, conv_w, g, beta, S0, qkv_dtype, eps, chunk) -> (o, S_T)
   decode_step(q, k, v, g, beta, S) -> o          (S updated in place)
 """
 from __future__ import annotations
@@ -62,6 +63,10 @@ def lib() -> ctypes.CDLL:
         L.gdn_fwd_workspace_bytes.restype = S
         L.gdn_fwd_chunked.argtypes = [D, P, P, P, P, P, P, P, P, P, S, P]
         L.gdn_fwd_chunked.restype = I
+        L.gdn_fwd_conv_workspace_bytes.argtypes = [D, I]
+        L.gdn_fwd_conv_workspace_bytes.restype = S
+        L.gdn_fwd_chunked_conv.argtypes = [D, I, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, S, P]
+        L.gdn_fwd_chunked_conv.restype = I
         L.gdn_decode_step.argtypes = [D, P, P, P, P, P, P, P, P]
         L.gdn_decode_step.restype = I
         L.gdn_status_str.argtypes = [I]
@@ -165,6 +170,37 @@ def fwd_chunked(q, k, v, g, beta, S0=None, chunk=64, o=None, S_T=None, stream=No
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
     check(L.gdn_fwd_chunked(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                             _ptr(S0), _ptr(o), _ptr(S_T), _ptr(ws), ws_bytes, _stream(stream)))
+    return o, S_T
+
+
+def fwd_chunked_conv(xq, xk, xv, conv_w, g, beta, S0=None, qkv_dtype=torch.float16, eps=1e-6,
+                     chunk=64, o=None, S_T=None, stream=None):
+    """prologue(xq, xk, xv, conv_w, qkv_dtype, eps) then fwd_chunked, in one call
+    (q, k, v are not returned).  Returns (o, S_T)."""
+    B, T, Hk, dk = xq.shape
+    Hv, dv = xv.shape[2], xv.shape[3]
+    _dev("xq", xq, (B, T, Hk, dk))
+    _dev("xk", xk, (B, T, Hk, dk), (xq.dtype,))
+    _dev("xv", xv, (B, T, Hv, dv), (xq.dtype,))
+    _dev("conv_w", conv_w, (2 * Hk * dk + Hv * dv, 4), (torch.float32,))
+    gate = _gate_kind(_dev("g", g), B, T, Hv, dk)
+    _dev("beta", beta, (B, T, Hv), (g.dtype,))
+    if S0 is not None:
+        _dev("S0", S0, (B, Hv, dv, dk), (torch.float32,))
+    if o is None:
+        o = torch.empty((B, T, Hv, dv), dtype=torch.float32, device=xq.device)
+    if S_T is None:
+        S_T = torch.empty((B, Hv, dv, dk), dtype=torch.float32, device=xq.device)
+    _dev("o", o, (B, T, Hv, dv), (torch.float32,))
+    _dev("S_T", S_T, (B, Hv, dv, dk), (torch.float32,))
+    d = make_desc(B, T, Hk, Hv, dk, dv, chunk, _DTYPE_CODE[qkv_dtype], _DTYPE_CODE[g.dtype], gate)
+    L = lib()
+    xt = _DTYPE_CODE[xq.dtype]
+    ws_bytes = L.gdn_fwd_conv_workspace_bytes(ctypes.byref(d), xt)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=xq.device) if ws_bytes else None
+    check(L.gdn_fwd_chunked_conv(ctypes.byref(d), xt, _ptr(xq), _ptr(xk), _ptr(xv), _ptr(conv_w),
+                                 float(eps), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T),
+                                 _ptr(ws), ws_bytes, _stream(stream)))
     return o, S_T
 
 

@@ -98,6 +98,40 @@ __device__ __forceinline__ half8 to_half8(uint4 u, bf16_t) {
 }
 __device__ __forceinline__ half8 to_half8(uint4 u, f16_t) { return __builtin_bit_cast(half8, u); }
 
+// Eight fp32 values narrowed to a 16-bit type, as stored to memory.
+__device__ __forceinline__ uint4 pack8(const float (&x)[8], f16_t) {
+  half8 h;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = (f16_t)x[i];
+  return __builtin_bit_cast(uint4, h);
+}
+__device__ __forceinline__ uint4 pack8(const float (&x)[8], bf16_t) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = (uint32_t)from_f32<bf16_t>(x[2 * i]).bits | ((uint32_t)from_f32<bf16_t>(x[2 * i + 1]).bits << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+// Eight bf16 values of a 16-byte piece, widened (row zero when `zero`).
+__device__ __forceinline__ void unpack8(uint4 u, bool zero, float (&x)[8]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = zero ? 0.f : __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = zero ? 0.f : __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+// Raw inputs of the convolution prologue when it runs inside the chunked
+// forward: the prep kernel convolves q and k (and writes them out for the
+// sequential pass), the sequential pass convolves v as it loads it.
+struct ConvIn {
+  const bf16_t *xq, *xk, *xv;   // raw q, k [B,T,Hk,dk] and v [B,T,Hv,dv]
+  const float *wq, *wk, *wv;    // their taps, [channels][4]
+  void *q, *k;                  // q and k after the prologue, qkv dtype [B,T,Hk,dk]
+  float eps;
+};
+
 __device__ __forceinline__ int frag_index(int R, int kk) { return R < 2 ? R : 2 * R - 2 + kk; }
 
 // LDS transpose read of gfx950 (ds_read_b64_tr_b16).  Within each group of 16
@@ -248,10 +282,14 @@ constexpr int P_OFF_SC = P_OFF_Q + C * KST * 2;         // 5 x [C] fp32
 constexpr int P_SMEM = P_OFF_SC + 5 * C * 4;
 static_assert(P_OFF_AD + 4 * 16 * DST * 4 <= P_OFF_SC, "per-head matrices overlap the scalars");
 
-template <typename TQ, typename TG>
-__global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
+// CONV: q and k are computed here from the raw inputs of cv (convolution,
+// SiLU, L2 normalisation) and written to cv.q and cv.k for the sequential
+// pass; the q and k arguments are not read.
+template <typename TQ, typename TG, bool CONV>
+__global__ __launch_bounds__(kThreads, CONV ? 2 : 4) void chunk_prep_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TG *__restrict__ g,
-    const TG *__restrict__ beta, uint4 *__restrict__ Tws, int T, int Hk, int Hv, int nchunks, int c0) {
+    const TG *__restrict__ beta, uint4 *__restrict__ Tws, int T, int Hk, int Hv, int nchunks, int c0,
+    ConvIn cv) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   _Float16 *sK = reinterpret_cast<_Float16 *>(smem + P_OFF_K);
   _Float16 *sQ = reinterpret_cast<_Float16 *>(smem + P_OFF_Q);
@@ -272,16 +310,41 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
   const int t0 = c * C, n = min(C, T - t0);
   const size_t bt0 = (size_t)b * T + t0;
 
-  // K and Q tiles (fp16), rows past the end zero; all eight loads are in
-  // flight before the first is converted
+  // CONV: this lane's rows of K and Q in the qkv type, stored to cv.k, cv.q
+  // once the loads have all landed
+  uint4 ky[CONV ? 4 : 1], qy[CONV ? 4 : 1];
+  const int rb = tid >> 4, ch = (tid & 15) * 8;
+  // K and Q tiles (fp16), rows past the end zero; all loads are in flight
+  // before the first is converted.  CONV: lane group rb = tid / 16 makes rows
+  // 4 rb .. 4 rb + 3 from the raw rows 4 rb - 3 .. 4 rb + 3 (zero before the
+  // sequence start) at the lane's 8 channels.
   {
-    uint4 uk[4], uq[4];
+    constexpr int NL = CONV ? 7 : 4;
+    uint4 uk[NL], uq[NL];
+    float wk[CONV ? 4 : 1][8], wq[CONV ? 4 : 1][8];
+    if constexpr (CONV) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int row = (tid >> 4) + 16 * it;
-      const size_t off = ((bt0 + min(row, n - 1)) * Hk + kh) * DK + (tid & 15) * 8;
-      uk[it] = *reinterpret_cast<const uint4 *>(k + off);
-      uq[it] = *reinterpret_cast<const uint4 *>(q + off);
+      for (int j = 0; j < 7; ++j) {
+        const int tt = min(max(t0 + 4 * rb - 3 + j, 0), T - 1);
+        const size_t off = (((size_t)b * T + tt) * Hk + kh) * DK + ch;
+        uk[j] = *reinterpret_cast<const uint4 *>(cv.xk + off);
+        uq[j] = *reinterpret_cast<const uint4 *>(cv.xq + off);
+      }
+#pragma unroll
+      for (int c8 = 0; c8 < 8; ++c8) {
+        const float4 a = *reinterpret_cast<const float4 *>(cv.wk + ((size_t)kh * DK + ch + c8) * 4);
+        const float4 bq = *reinterpret_cast<const float4 *>(cv.wq + ((size_t)kh * DK + ch + c8) * 4);
+        wk[0][c8] = a.x; wk[1][c8] = a.y; wk[2][c8] = a.z; wk[3][c8] = a.w;
+        wq[0][c8] = bq.x; wq[1][c8] = bq.y; wq[2][c8] = bq.z; wq[3][c8] = bq.w;
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int row = (tid >> 4) + 16 * it;
+        const size_t off = ((bt0 + min(row, n - 1)) * Hk + kh) * DK + ch;
+        uk[it] = *reinterpret_cast<const uint4 *>(k + off);
+        uq[it] = *reinterpret_cast<const uint4 *>(q + off);
+      }
     }
     // gate and beta of every value head of the group, [head][token] in LDS
     // past the fixed layout, all requested before anything is stored: one
@@ -310,11 +373,32 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);
     const half8 hz = {};
+    if constexpr (CONV) {
+      // the prologue's arithmetic, rounded to the qkv type as it stores it
+      auto conv_rows = [&](const uint4 (&x)[7], const float (&w)[4][8], _Float16 *sX, uint4 (&y)[4]) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int row = (tid >> 4) + 16 * it;
-      *reinterpret_cast<half8 *>(sK + row * KST + (tid & 15) * 8) = row < n ? to_half8(uk[it], TQ{}) : hz;
-      *reinterpret_cast<half8 *>(sQ + row * KST + (tid & 15) * 8) = row < n ? to_half8(uq[it], TQ{}) : hz;
+        for (int it = 0; it < 4; ++it) {
+          const int row = 4 * rb + it;
+          float x3[8], x2[8], x1[8], x0[8], z[8];
+          unpack8(x[it], t0 + row - 3 < 0, x3);
+          unpack8(x[it + 1], t0 + row - 2 < 0, x2);
+          unpack8(x[it + 2], t0 + row - 1 < 0, x1);
+          unpack8(x[it + 3], false, x0);
+          const float ss = conv_silu8(w[0], w[1], w[2], w[3], x3, x2, x1, x0, z);
+          l2_scale8<16>(z, ss, cv.eps);
+          y[it] = pack8(z, TQ{});
+          *reinterpret_cast<half8 *>(sX + row * KST + ch) = row < n ? to_half8(y[it], TQ{}) : hz;
+        }
+      };
+      conv_rows(uk, wk, sK, ky);
+      conv_rows(uq, wq, sQ, qy);
+    } else {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int row = (tid >> 4) + 16 * it;
+        *reinterpret_cast<half8 *>(sK + row * KST + ch) = row < n ? to_half8(uk[it], TQ{}) : hz;
+        *reinterpret_cast<half8 *>(sQ + row * KST + ch) = row < n ? to_half8(uq[it], TQ{}) : hz;
+      }
     }
   }
   lds_barrier();
@@ -352,6 +436,17 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
   // that the head loop does not wait on them again behind its own stores.
   // (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15.)
   __builtin_amdgcn_s_waitcnt(0x0F70);
+  if constexpr (CONV) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int row = 4 * rb + it;
+      if (row < n) {
+        const size_t off = ((bt0 + row) * Hk + kh) * DK + ch;
+        *reinterpret_cast<uint4 *>(reinterpret_cast<TQ *>(cv.k) + off) = ky[it];
+        *reinterpret_cast<uint4 *>(reinterpret_cast<TQ *>(cv.q) + off) = qy[it];
+      }
+    }
+  }
   for (int hv = 0; hv < grp; ++hv) {
     const int h = kh * grp + hv;
     lds_barrier();  // K and Q, or the previous head's T and P, have been read out
@@ -442,7 +537,8 @@ struct SeqCfg {
   static constexpr int OFF_V = OFF_KD + (KDA ? 2 * C * KST * 2 : 0);   // 2 x [C][VST] fp16
   static constexpr int OFF_TP = OFF_V + 2 * C * VST * 2;   // 2 x [2 NFRAG][64] x 16 B
   static constexpr int OFF_SC = OFF_TP + 2 * 2 * NFRAG * 64 * 16;   // 2 x [NSC] fp32
-  static constexpr int SMEM = OFF_SC + 2 * NSC * 4;
+  static constexpr int OFF_W = OFF_SC + 2 * NSC * 4;       // [WGC][4] fp32 (v taps, convolution)
+  static constexpr int SMEM = OFF_W + WGC * 16;
   static_assert(SMEM <= 160 * 1024, "LDS");
   static_assert((C * DK / 8) % LT == 0 && (C * WGC / 8) % LT == 0, "loads per thread");
   static_assert(LW > 0 && LT >= NSC / 4, "one scalar piece per loading thread");
@@ -450,23 +546,25 @@ struct SeqCfg {
 
 // The next chunk's raw loads.  Nothing is converted here, so no instruction
 // needs the data before the chunk is committed.
-template <typename TQ, typename TG, int NW, int RT, bool KDA, int LW>
+// CONV: the raw v rows of the lane's NV output rows and the three before.
+template <typename TQ, typename TG, int NW, int RT, bool KDA, int LW, bool CONV>
 struct SeqFetch {
   using Cfg = SeqCfg<NW, RT, KDA, LW>;
-  uint4 k[Cfg::NKQ], q[Cfg::NKQ], kd[KDA ? Cfg::NKQ : 1], v[Cfg::NV], tp[Cfg::NTP], sc;
-  int n;
+  uint4 k[Cfg::NKQ], q[Cfg::NKQ], kd[KDA ? Cfg::NKQ : 1], v[CONV ? Cfg::NV + 3 : Cfg::NV], tp[Cfg::NTP], sc;
+  int n, t0;
 };
 
 // KDA false: head gate; K, Q, V, g, beta are read from the inputs and T, P
 // from the workspace.  KDA true: key-channel gate; the decayed K, Q, the
 // state-update K, beta and Gamma_n come from the workspace (q, k, g, beta are
-// not read) and the state decays per key channel.
-template <typename TQ, typename TG, int NW, int RT, bool KDA, int LW>
+// not read) and the state decays per key channel.  CONV: v is computed from
+// the raw rows cv.xv as it is loaded (convolution and SiLU); v is not read.
+template <typename TQ, typename TG, int NW, int RT, bool KDA, int LW, bool CONV>
 __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *__restrict__ v,
     const TG *__restrict__ g, const TG *__restrict__ beta, const uint4 *__restrict__ ws,
     const float *__restrict__ S0, float *__restrict__ o, float *__restrict__ ST, int T, int Hk,
-    int Hv, int ntasks, int nchunks, int c_begin, int c_end) {
+    int Hv, int ntasks, int nchunks, int c_begin, int c_end, ConvIn cv) {
   using Cfg = SeqCfg<NW, RT, KDA, LW>;
   constexpr int NSC = Cfg::NSC;
   constexpr int LT = Cfg::LT, WGC = Cfg::WGC, NS = Cfg::NS, VST = Cfg::VST;
@@ -501,17 +599,23 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
   _Float16 *const sVb = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_V);
   uint4 *const sTPb = reinterpret_cast<uint4 *>(smem + Cfg::OFF_TP);
   float *const sScb = reinterpret_cast<float *>(smem + Cfg::OFF_SC);
+  float4 *const sW = reinterpret_cast<float4 *>(smem + Cfg::OFF_W);
 
-  using Fetch = SeqFetch<TQ, TG, NW, RT, KDA, LW>;
-  // part 0: K and Q (and the key gate's state-update K); part 1: V, the T
-  // and P fragments and the scalars; part 2: both
+  using Fetch = SeqFetch<TQ, TG, NW, RT, KDA, LW, CONV>;
+  // CONV: loading thread -> value channels 8 ch8 .. + 7 of the slice at the
+  // chunk rows NV rb .. NV rb + NV - 1 (a row's channels on consecutive lanes)
+  const int vrb = ltid / (WGC / 8), vch8 = ltid % (WGC / 8);
+  const bf16_t *xvb = cv.xv + ((size_t)b * T * Hv + h) * DV + slice * WGC + vch8 * 8;
+  // parts: K and Q (and the key gate's state-update K), V, and the T and P
+  // fragments with the scalars
+  constexpr int FKQ = 1, FV = 2, FTP = 4, FALL = 7;
   auto fetch = [&](Fetch &f, int c, int part) {
     const int n = min(C, T - c * C);
     f.n = n;
     const size_t t0 = (size_t)c * C;
     const uint4 *wc = wsbh + (size_t)c * Cfg::CHUNK_U4;
     const TQ *kc = kb + t0 * kq_rs, *qc = qb + t0 * kq_rs, *vc = vb + t0 * v_rs;
-    if (KDA && part != 1) {
+    if (KDA && (part & FKQ)) {
       // rows past the end of the sequence are zero in the workspace
 #pragma unroll
       for (int it = 0; it < NKQ; ++it) {
@@ -526,18 +630,29 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
     for (int it = 0; it < NKQ; ++it) {
       const int e = ltid + LT * it;
       const int off = min(e >> 4, n - 1) * kq_rs + (e & 15) * 8;
-      if (!KDA && part != 1) {
+      if (!KDA && (part & FKQ)) {
         f.k[it] = *reinterpret_cast<const uint4 *>(kc + off);
         f.q[it] = *reinterpret_cast<const uint4 *>(qc + off);
       }
     }
-    if (part != 0) {
+    f.t0 = (int)t0;
+    if (part & FV) {
+      if constexpr (CONV) {
 #pragma unroll
-      for (int it = 0; it < NV; ++it) {
-        const int e = ltid + LT * it;
-        f.v[it] = *reinterpret_cast<const uint4 *>(vc + min(e / (WGC / 8), n - 1) * v_rs +
-                                                   (e % (WGC / 8)) * 8);
+        for (int j = 0; j < NV + 3; ++j) {
+          const int tt = min(max((int)t0 + NV * vrb - 3 + j, 0), T - 1);
+          f.v[j] = *reinterpret_cast<const uint4 *>(xvb + (size_t)tt * v_rs);
+        }
+      } else {
+#pragma unroll
+        for (int it = 0; it < NV; ++it) {
+          const int e = ltid + LT * it;
+          f.v[it] = *reinterpret_cast<const uint4 *>(vc + min(e / (WGC / 8), n - 1) * v_rs +
+                                                     (e % (WGC / 8)) * 8);
+        }
       }
+    }
+    if (part & FTP) {
 #pragma unroll
       for (int it = 0; it < NTP; ++it) f.tp[it] = wc[min(ltid + LT * it, 2 * NFRAG * 64 - 1)];
       f.sc = wc[Cfg::SC_U4 + min(ltid, NSC / 4 - 1)];
@@ -562,16 +677,41 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
       if constexpr (KDA) *reinterpret_cast<half8 *>(sKdb + buf * C * KST + off) = to_half8(f.kd[it], f16_t{});
     }
 #pragma unroll
-    for (int it = 0; it < NV; ++it) {
-      const int e = ltid + LT * it;
-      const int row = e / (WGC / 8);
-      *reinterpret_cast<half8 *>(v_ + row * VST + (e % (WGC / 8)) * 8) =
-          row < f.n ? to_half8(f.v[it], TQ{}) : hz;
-    }
-#pragma unroll
     for (int it = 0; it < NTP; ++it) {
       const int e = ltid + LT * it;
       if (e < 2 * NFRAG * 64) sTPb[buf * 2 * NFRAG * 64 + e] = f.tp[it];
+    }
+    if constexpr (CONV) {
+      // the prologue's arithmetic, rounded to the qkv type as it stores it;
+      // the taps of the lane's 8 channels come from LDS.  Everything else is
+      // written first, so that its registers are free during the arithmetic.
+      __builtin_amdgcn_sched_barrier(0);
+      float wv[4][8];
+#pragma unroll
+      for (int c8 = 0; c8 < 8; ++c8) {
+        const float4 t4 = sW[vch8 * 8 + c8];
+        wv[0][c8] = t4.x; wv[1][c8] = t4.y; wv[2][c8] = t4.z; wv[3][c8] = t4.w;
+      }
+#pragma unroll
+      for (int it = 0; it < NV; ++it) {
+        const int row = NV * vrb + it;
+        float x3[8], x2[8], x1[8], x0[8], z[8];
+        unpack8(f.v[it], f.t0 + row - 3 < 0, x3);
+        unpack8(f.v[it + 1], f.t0 + row - 2 < 0, x2);
+        unpack8(f.v[it + 2], f.t0 + row - 1 < 0, x1);
+        unpack8(f.v[it + 3], false, x0);
+        (void)conv_silu8(wv[0], wv[1], wv[2], wv[3], x3, x2, x1, x0, z);
+        *reinterpret_cast<half8 *>(v_ + row * VST + vch8 * 8) =
+            row < f.n ? to_half8(pack8(z, TQ{}), TQ{}) : hz;
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < NV; ++it) {
+        const int e = ltid + LT * it;
+        const int row = e / (WGC / 8);
+        *reinterpret_cast<half8 *>(v_ + row * VST + (e % (WGC / 8)) * 8) =
+            row < f.n ? to_half8(f.v[it], TQ{}) : hz;
+      }
     }
   };
 
@@ -582,12 +722,25 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
     // is exact.  The loads are unconditional (a repeated chunk near the end),
     // and the barriers match the compute waves' one per chunk.
     Fetch fa, fb;
-    fetch(fa, c_begin, 2);
+    fetch(fa, c_begin, FALL);
+    if constexpr (CONV) {
+      // the taps of the lane's 8 channels, read back by every commit: each
+      // lane writes the taps it reads (lanes sharing channels write the same
+      // values), so no other wave is waited for
+#pragma unroll
+      for (int c8 = 0; c8 < 8; ++c8)
+        sW[vch8 * 8 + c8] =
+            *reinterpret_cast<const float4 *>(cv.wv + ((size_t)h * DV + slice * WGC + vch8 * 8 + c8) * 4);
+    }
     commit(fa, 0);
-    fetch(fb, min(c_begin + 1, c_end - 1), 2);
+    // CONV: the raw v rows (with the three before each lane's rows) are
+    // fetched one chunk ahead only, first thing in the chunk; two chunks of
+    // them would not fit in the registers beside everything else.
+    fetch(fb, min(c_begin + 1, c_end - 1), CONV ? FKQ | FTP : FALL);
     lds_barrier();
-    auto lstep = [&](int c, Fetch &fn, const Fetch &fc) {
-      fetch(fn, min(c + 2, c_end - 1), 2);
+    auto lstep = [&](int c, Fetch &fn, Fetch &fc) {
+      if constexpr (CONV) fetch(fc, min(c + 1, c_end - 1), FV);
+      fetch(fn, min(c + 2, c_end - 1), CONV ? FKQ | FTP : FALL);
       if (c + 1 < c_end) commit(fc, ((c - c_begin) & 1) ^ 1);
       lds_barrier();
     };
@@ -787,19 +940,19 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
           make_float4(accS[t][J][0], accS[t][J][1], accS[t][J][2], accS[t][J][3]);
 }
 
-template <typename TQ, typename TG, int NW, int RT, bool KDA, int LW>
+template <typename TQ, typename TG, int NW, int RT, bool KDA, int LW, bool CONV = false>
 hipError_t launch_seq(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
                       const void *beta, const uint4 *TPws, const float *S0, float *o, float *ST,
-                      int nchunks, int c_begin, int c_end, hipStream_t st) {
+                      int nchunks, int c_begin, int c_end, hipStream_t st, const ConvIn &cv = ConvIn{}) {
   using Cfg = SeqCfg<NW, RT, KDA, LW>;
-  auto kern = chunk_seq_kernel<TQ, TG, NW, RT, KDA, LW>;
+  auto kern = chunk_seq_kernel<TQ, TG, NW, RT, KDA, LW, CONV>;
   hipError_t e =
       hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::SMEM);
   if (e != hipSuccess) return e;
   const int ntasks = sh.B * sh.Hv * Cfg::NS;
   hipLaunchKernelGGL(kern, dim3(ntasks), dim3(Cfg::THREADS), Cfg::SMEM, st, (const TQ *)q,
                      (const TQ *)k, (const TQ *)v, (const TG *)g, (const TG *)beta, TPws, S0, o, ST,
-                     sh.T, sh.Hk, sh.Hv, ntasks, nchunks, c_begin, c_end);
+                     sh.T, sh.Hk, sh.Hv, ntasks, nchunks, c_begin, c_end, cv);
   return hipGetLastError();
 }
 
@@ -893,12 +1046,16 @@ hipError_t pipelined(int nchunks, bool overlap, const float *S0, float *ST, hipS
 // has at most 192 workgroups).
 inline bool seq_overlap(long heads) { return heads <= 48; }
 
-template <typename TQ, typename TG>
+// CONV: the convolution prologue runs inside: the prep kernel makes q and k
+// (into cv.q, cv.k, which the sequential pass then reads) and the
+// sequential pass makes v; the q, k, v arguments are not read.
+template <typename TQ, typename TG, bool CONV>
 hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
-                    const void *beta, const float *S0, float *o, float *ST, void *ws, hipStream_t st) {
+                    const void *beta, const float *S0, float *o, float *ST, void *ws, hipStream_t st,
+                    const ConvIn &cv) {
   const int nchunks = (sh.T + C - 1) / C;
   uint4 *TPws = (uint4 *)ws;
-  auto prep_k = chunk_prep_kernel<TQ, TG>;
+  auto prep_k = chunk_prep_kernel<TQ, TG, CONV>;
   // fixed layout, then gate and beta of the group's heads (fp32, 2 x grp x C)
   const size_t smem = P_SMEM + (size_t)2 * (sh.Hv / sh.Hk) * C * 4;
   if (smem > 160 * 1024) return hipErrorInvalidValue;
@@ -908,9 +1065,10 @@ hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v
   auto prep = [&](int cb, int ce, hipStream_t s) {
     hipLaunchKernelGGL(prep_k, dim3(ce - cb, sh.B * sh.Hk), dim3(kThreads), smem, s, (const TQ *)q,
                        (const TQ *)k, (const TG *)g, (const TG *)beta, TPws, sh.T, sh.Hk, sh.Hv,
-                       nchunks, cb);
+                       nchunks, cb, cv);
     return hipGetLastError();
   };
+  const void *qs = CONV ? cv.q : q, *ks = CONV ? cv.k : k;
   // Workgroups of the sequential pass: as few per head as keep every one of
   // them resident (one per compute unit).  128 value rows: four compute waves
   // holding two row tiles each (a K or Q fragment read from LDS then serves
@@ -918,10 +1076,13 @@ hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v
   const long heads = (long)sh.B * sh.Hv;
   auto seq = [&](int cb, int ce, const float *s0, hipStream_t s) {
     if (heads > 128)
-      return launch_seq<TQ, TG, 4, 2, false, 4>(sh, q, k, v, g, beta, TPws, s0, o, ST, nchunks, cb, ce, s);
+      return launch_seq<TQ, TG, 4, 2, false, 4, CONV>(sh, qs, ks, v, g, beta, TPws, s0, o, ST, nchunks, cb,
+                                                      ce, s, cv);
     if (heads > 64)
-      return launch_seq<TQ, TG, 4, 1, false, 4>(sh, q, k, v, g, beta, TPws, s0, o, ST, nchunks, cb, ce, s);
-    return launch_seq<TQ, TG, 2, 1, false, 4>(sh, q, k, v, g, beta, TPws, s0, o, ST, nchunks, cb, ce, s);
+      return launch_seq<TQ, TG, 4, 1, false, 4, CONV>(sh, qs, ks, v, g, beta, TPws, s0, o, ST, nchunks, cb,
+                                                      ce, s, cv);
+    return launch_seq<TQ, TG, 2, 1, false, 4, CONV>(sh, qs, ks, v, g, beta, TPws, s0, o, ST, nchunks, cb,
+                                                    ce, s, cv);
   };
   return pipelined(nchunks, seq_overlap(heads), S0, ST, st, prep, seq);
 }
@@ -1231,12 +1392,43 @@ hipError_t launch_chunk_mfma(const Shape &sh, const void *q, const void *k, cons
     return sh.gate_t == DType::F32 ? launch_kda_t<f16_t, float>(sh, q, k, v, g, beta, S0, o, ST, ws, st)
                                    : launch_kda_t<f16_t, bf16_t>(sh, q, k, v, g, beta, S0, o, ST, ws, st);
   }
+  const ConvIn none{};
   if (sh.qkv == DType::BF16)
     return sh.gate_t == DType::F32
-               ? launch_t<bf16_t, float>(sh, q, k, v, g, beta, S0, o, ST, ws, st)
-               : launch_t<bf16_t, bf16_t>(sh, q, k, v, g, beta, S0, o, ST, ws, st);
-  return sh.gate_t == DType::F32 ? launch_t<f16_t, float>(sh, q, k, v, g, beta, S0, o, ST, ws, st)
-                                 : launch_t<f16_t, bf16_t>(sh, q, k, v, g, beta, S0, o, ST, ws, st);
+               ? launch_t<bf16_t, float, false>(sh, q, k, v, g, beta, S0, o, ST, ws, st, none)
+               : launch_t<bf16_t, bf16_t, false>(sh, q, k, v, g, beta, S0, o, ST, ws, st, none);
+  return sh.gate_t == DType::F32
+             ? launch_t<f16_t, float, false>(sh, q, k, v, g, beta, S0, o, ST, ws, st, none)
+             : launch_t<f16_t, bf16_t, false>(sh, q, k, v, g, beta, S0, o, ST, ws, st, none);
+}
+
+hipError_t launch_chunk_mfma_conv(const Shape &sh, const void *xq, const void *xk, const void *xv,
+                                  const float *conv_w, float eps, const void *g, const void *beta,
+                                  const float *S0, float *o, float *ST, void *ws, hipStream_t st) {
+  // workspace: the chunk matrices, then q and k after the prologue
+  const size_t nqk = (size_t)sh.B * sh.T * sh.Hk * DK;
+  char *base = (char *)ws;
+  ConvIn cv;
+  cv.xq = (const bf16_t *)xq;
+  cv.xk = (const bf16_t *)xk;
+  cv.xv = (const bf16_t *)xv;
+  cv.wq = conv_w;
+  cv.wk = conv_w + (size_t)sh.Hk * DK * 4;
+  cv.wv = conv_w + (size_t)2 * sh.Hk * DK * 4;
+  cv.q = base + chunk_mfma_workspace(sh);
+  cv.k = (char *)cv.q + nqk * 2;
+  cv.eps = eps;
+  if (sh.qkv == DType::BF16)
+    return sh.gate_t == DType::F32
+               ? launch_t<bf16_t, float, true>(sh, nullptr, nullptr, nullptr, g, beta, S0, o, ST, ws, st, cv)
+               : launch_t<bf16_t, bf16_t, true>(sh, nullptr, nullptr, nullptr, g, beta, S0, o, ST, ws, st, cv);
+  return sh.gate_t == DType::F32
+             ? launch_t<f16_t, float, true>(sh, nullptr, nullptr, nullptr, g, beta, S0, o, ST, ws, st, cv)
+             : launch_t<f16_t, bf16_t, true>(sh, nullptr, nullptr, nullptr, g, beta, S0, o, ST, ws, st, cv);
+}
+
+size_t chunk_mfma_conv_workspace(const Shape &sh) {
+  return chunk_mfma_workspace(sh) + (size_t)2 * sh.B * sh.T * sh.Hk * DK * 2;
 }
 
 }  // namespace gdn

@@ -94,6 +94,8 @@ bool uses_matrix_cores(const gdn_desc *d) {
   return mc_mode && d->dk == 128 && d->dv == 128 && d->chunk == 64;
 }
 
+gdn_status check_prologue_args(const gdn_desc *d, int32_t x_dtype, float eps);
+
 gdn_status launched(hipError_t e, const char *what) {
   if (e != hipSuccess) return fail(GDN_E_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
@@ -126,13 +128,7 @@ gdn_status gdn_prologue(const gdn_desc *d, int32_t x_dtype, const void *xq, cons
   gdn::Shape sh;
   gdn_status st = check_desc(d, &sh);
   if (st != GDN_OK) return st;
-  if (x_dtype != GDN_BF16 && x_dtype != GDN_F32)
-    return fail(x_dtype == GDN_F16 ? GDN_E_UNSUPPORTED : GDN_E_ARG,
-                "prologue inputs must be bf16 or fp32 (got dtype %d)", x_dtype);
-  if (!pow2_16_128(d->dk) || !pow2_16_128(d->dv))
-    return fail(GDN_E_UNSUPPORTED, "prologue supports dk, dv in {16,32,64,128} (got %d, %d)",
-                d->dk, d->dv);
-  if (!(eps >= 0.f) || eps > 1.f) return fail(GDN_E_ARG, "eps must be in [0, 1]");
+  if ((st = check_prologue_args(d, x_dtype, eps)) != GDN_OK) return st;
   const char *names[] = {"xq", "xk", "xv", "conv_w", "q", "k", "v"};
   const void *ptrs[] = {xq, xk, xv, conv_w, q, k, v};
   if ((st = check_ptrs(names, ptrs, 7)) != GDN_OK) return st;
@@ -161,11 +157,14 @@ size_t gdn_fwd_workspace_bytes(const gdn_desc *d) {
   return uses_matrix_cores(d) ? gdn::chunk_mfma_workspace(sh) : 0;
 }
 
-gdn_status gdn_fwd_chunked(const gdn_desc *d, const void *q, const void *k, const void *v,
-                           const void *g, const void *beta, const float *S0, float *o, float *S_T,
-                           void *workspace, size_t workspace_bytes, void *stream) {
-  gdn::Shape sh;
-  gdn_status st = check_desc(d, &sh);
+}  // extern "C"
+
+namespace {
+
+// Everything gdn_fwd_chunked checks, without launching.  `ws_need` is the
+// workspace the chosen kernels need (the caller checks the one it passes).
+gdn_status check_chunked(const gdn_desc *d, gdn::Shape *sh, bool *use_mfma_out) {
+  gdn_status st = check_desc(d, sh);
   if (st != GDN_OK) return st;
   const bool fp32_mode = d->qkv_dtype == GDN_F32 && d->gate_dtype == GDN_F32;
   const bool mc_mode = (d->qkv_dtype == GDN_BF16 || d->qkv_dtype == GDN_F16) &&
@@ -178,7 +177,7 @@ gdn_status gdn_fwd_chunked(const gdn_desc *d, const void *q, const void *k, cons
   // 16-bit inputs run on the matrix cores at dk = dv = 128, chunk 64; the
   // key-channel gate at other sizes runs on the fp32 vector path.
   const bool use_mfma = uses_matrix_cores(d);
-  if (mc_mode && !use_mfma && !sh.key_gate)
+  if (mc_mode && !use_mfma && !sh->key_gate)
     return fail(GDN_E_UNSUPPORTED,
                 "matrix-core mode supports dk = dv = 128 and chunk = 64 (got %d, %d, %d)", d->dk,
                 d->dv, d->chunk);
@@ -191,24 +190,30 @@ gdn_status gdn_fwd_chunked(const gdn_desc *d, const void *q, const void *k, cons
       return fail(GDN_E_UNSUPPORTED, "fp32 mode needs chunk * dk <= 4096 (got %d * %d)", d->chunk,
                   d->dk);
   }
+  *use_mfma_out = use_mfma;
+  return GDN_OK;
+}
 
-  const char *names[] = {"q", "k", "v", "g", "beta", "o", "S_T"};
-  const void *ptrs[] = {q, k, v, g, beta, o, S_T};
-  if ((st = check_ptrs(names, ptrs, 7)) != GDN_OK) return st;
+// Pointer checks of the chunked forward: ins are the ranges of q, k, v (or
+// the raw inputs and taps of the convolution), g and beta.
+gdn_status check_chunked_ptrs(const gdn_desc *d, const gdn::Shape &sh, const Range *ins, int nins,
+                              const void *g, const void *beta, const float *S0, float *o,
+                              float *S_T) {
+  const char *names[] = {"g", "beta", "o", "S_T"};
+  const void *ptrs[] = {g, beta, o, S_T};
+  gdn_status st = check_ptrs(names, ptrs, 4);
+  if (st != GDN_OK) return st;
   if (S0 && !aligned16(S0)) return fail(GDN_E_ALIGN, "S0 is not 16-byte aligned");
-
   const size_t bt = (size_t)d->B * d->T;
-  const size_t qs = dsize(d->qkv_dtype), gs = dsize(d->gate_dtype);
+  const size_t gs = dsize(d->gate_dtype);
   const size_t state_bytes = (size_t)d->B * d->Hv * d->dv * d->dk * 4;
   const Range ro = range(o, bt * d->Hv * d->dv * 4);
   const Range rst = range(S_T, state_bytes);
-  const Range ins[] = {range(q, bt * d->Hk * d->dk * qs), range(k, bt * d->Hk * d->dk * qs),
-                       range(v, bt * d->Hv * d->dv * qs),
-                       range(g, bt * d->Hv * (sh.key_gate ? d->dk : 1) * gs),
-                       range(beta, bt * d->Hv * gs)};
-  for (const Range &r : ins) {
+  const Range rg = range(g, bt * d->Hv * (sh.key_gate ? d->dk : 1) * gs), rb = range(beta, bt * d->Hv * gs);
+  for (int i = 0; i < nins + 2; ++i) {
+    const Range &r = i < nins ? ins[i] : (i == nins ? rg : rb);
     if (overlap(ro, r)) return fail(GDN_E_ARG, "o must not overlap an input");
-    if (overlap(rst, r)) return fail(GDN_E_ARG, "S_T must not overlap q, k, v, g or beta");
+    if (overlap(rst, r)) return fail(GDN_E_ARG, "S_T must not overlap an input other than S0");
   }
   if (overlap(ro, rst)) return fail(GDN_E_ARG, "o must not overlap S_T");
   if (S0) {
@@ -217,23 +222,137 @@ gdn_status gdn_fwd_chunked(const gdn_desc *d, const void *q, const void *k, cons
     if ((const void *)S0 != (const void *)S_T && overlap(rst, rs0))
       return fail(GDN_E_ARG, "S_T must be S0 itself or not overlap it");
   }
+  return GDN_OK;
+}
 
-  if (use_mfma) {
-    const size_t need = gdn::chunk_mfma_workspace(sh);
-    if (workspace_bytes < need)
-      return fail(GDN_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
-    if (!workspace) return fail(GDN_E_ARG, "workspace is NULL");
-    if (!aligned16(workspace)) return fail(GDN_E_ALIGN, "workspace is not 16-byte aligned");
-    const Range rw = range(workspace, need);
-    for (const Range &r : ins)
-      if (overlap(rw, r)) return fail(GDN_E_ARG, "workspace must not overlap an input");
-    if (overlap(rw, ro) || overlap(rw, rst) || (S0 && overlap(rw, range(S0, state_bytes))))
-      return fail(GDN_E_ARG, "workspace must not overlap o, S0 or S_T");
-  }
+// The caller's workspace: large enough, aligned, and apart from every other
+// argument.
+gdn_status check_workspace(const gdn_desc *d, void *workspace, size_t workspace_bytes, size_t need,
+                           const Range *ins, int nins, const void *g, const void *beta,
+                           const float *S0, float *o, float *S_T, bool key_gate) {
+  if (workspace_bytes < need)
+    return fail(GDN_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  if (need == 0) return GDN_OK;
+  if (!workspace) return fail(GDN_E_ARG, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(GDN_E_ALIGN, "workspace is not 16-byte aligned");
+  const size_t bt = (size_t)d->B * d->T, gs = dsize(d->gate_dtype);
+  const size_t state_bytes = (size_t)d->B * d->Hv * d->dv * d->dk * 4;
+  const Range rw = range(workspace, need);
+  for (int i = 0; i < nins; ++i)
+    if (overlap(rw, ins[i])) return fail(GDN_E_ARG, "workspace must not overlap an input");
+  if (overlap(rw, range(g, bt * d->Hv * (key_gate ? d->dk : 1) * gs)) ||
+      overlap(rw, range(beta, bt * d->Hv * gs)))
+    return fail(GDN_E_ARG, "workspace must not overlap an input");
+  if (overlap(rw, range(o, bt * d->Hv * d->dv * 4)) || overlap(rw, range(S_T, state_bytes)) ||
+      (S0 && overlap(rw, range(S0, state_bytes))))
+    return fail(GDN_E_ARG, "workspace must not overlap o, S0 or S_T");
+  return GDN_OK;
+}
+
+// Everything gdn_prologue checks about its dtypes, sizes and eps.
+gdn_status check_prologue_args(const gdn_desc *d, int32_t x_dtype, float eps) {
+  if (x_dtype != GDN_BF16 && x_dtype != GDN_F32)
+    return fail(x_dtype == GDN_F16 ? GDN_E_UNSUPPORTED : GDN_E_ARG,
+                "prologue inputs must be bf16 or fp32 (got dtype %d)", x_dtype);
+  if (!pow2_16_128(d->dk) || !pow2_16_128(d->dv))
+    return fail(GDN_E_UNSUPPORTED, "prologue supports dk, dv in {16,32,64,128} (got %d, %d)",
+                d->dk, d->dv);
+  if (!(eps >= 0.f) || eps > 1.f) return fail(GDN_E_ARG, "eps must be in [0, 1]");
+  return GDN_OK;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// The convolution runs inside the chunked kernels for bf16 raw inputs on
+// the matrix-core path with the per-head gate; otherwise the prologue
+// writes q, k, v into the workspace first.
+bool conv_fused(const gdn_desc *d, const gdn::Shape &sh, bool use_mfma, int32_t x_dtype) {
+  return use_mfma && !sh.key_gate && x_dtype == GDN_BF16;
+}
+
+size_t conv_workspace(const gdn_desc *d, const gdn::Shape &sh, bool use_mfma, int32_t x_dtype) {
+  if (conv_fused(d, sh, use_mfma, x_dtype)) return gdn::chunk_mfma_conv_workspace(sh);
+  const size_t ys = dsize(d->qkv_dtype);
+  const size_t nqk = (size_t)d->B * d->T * d->Hk * d->dk, nv = (size_t)d->B * d->T * d->Hv * d->dv;
+  return 2 * round256(nqk * ys) + round256(nv * ys) + (use_mfma ? gdn::chunk_mfma_workspace(sh) : 0);
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_fwd_chunked(const gdn_desc *d, const void *q, const void *k, const void *v,
+                           const void *g, const void *beta, const float *S0, float *o, float *S_T,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  gdn::Shape sh;
+  bool use_mfma = false;
+  gdn_status st = check_chunked(d, &sh, &use_mfma);
+  if (st != GDN_OK) return st;
+  const char *names[] = {"q", "k", "v"};
+  const void *ptrs[] = {q, k, v};
+  if ((st = check_ptrs(names, ptrs, 3)) != GDN_OK) return st;
+  const size_t bt = (size_t)d->B * d->T, qs = dsize(d->qkv_dtype);
+  const Range ins[] = {range(q, bt * d->Hk * d->dk * qs), range(k, bt * d->Hk * d->dk * qs),
+                       range(v, bt * d->Hv * d->dv * qs)};
+  if ((st = check_chunked_ptrs(d, sh, ins, 3, g, beta, S0, o, S_T)) != GDN_OK) return st;
+  const size_t need = use_mfma ? gdn::chunk_mfma_workspace(sh) : 0;
+  if ((st = check_workspace(d, workspace, workspace_bytes, need, ins, 3, g, beta, S0, o, S_T,
+                            sh.key_gate)) != GDN_OK)
+    return st;
 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = use_mfma ? gdn::launch_chunk_mfma(sh, q, k, v, g, beta, S0, o, S_T, workspace, s)
                           : gdn::launch_chunk_f32(sh, q, k, v, g, beta, S0, o, S_T, s);
+  return launched(e, "chunked forward launch");
+}
+
+size_t gdn_fwd_conv_workspace_bytes(const gdn_desc *d, int32_t x_dtype) {
+  gdn::Shape sh;
+  bool use_mfma = false;
+  const std::string saved = g_last_error;  // a query does not change the last error
+  gdn_status st = check_chunked(d, &sh, &use_mfma);
+  if (st == GDN_OK) st = check_prologue_args(d, x_dtype, 0.f);
+  g_last_error = saved;
+  if (st != GDN_OK) return 0;
+  return conv_workspace(d, sh, use_mfma, x_dtype);
+}
+
+gdn_status gdn_fwd_chunked_conv(const gdn_desc *d, int32_t x_dtype, const void *xq, const void *xk,
+                                const void *xv, const float *conv_w, float eps, const void *g,
+                                const void *beta, const float *S0, float *o, float *S_T,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+  gdn::Shape sh;
+  bool use_mfma = false;
+  gdn_status st = check_chunked(d, &sh, &use_mfma);
+  if (st != GDN_OK) return st;
+  if ((st = check_prologue_args(d, x_dtype, eps)) != GDN_OK) return st;
+  const char *names[] = {"xq", "xk", "xv", "conv_w"};
+  const void *ptrs[] = {xq, xk, xv, conv_w};
+  if ((st = check_ptrs(names, ptrs, 4)) != GDN_OK) return st;
+  const size_t nqk = (size_t)d->B * d->T * d->Hk * d->dk, nv = (size_t)d->B * d->T * d->Hv * d->dv;
+  const size_t xs = dsize(x_dtype);
+  const Range ins[] = {range(xq, nqk * xs), range(xk, nqk * xs), range(xv, nv * xs),
+                       range(conv_w, (2 * (size_t)d->Hk * d->dk + (size_t)d->Hv * d->dv) * 16)};
+  if ((st = check_chunked_ptrs(d, sh, ins, 4, g, beta, S0, o, S_T)) != GDN_OK) return st;
+  const size_t need = conv_workspace(d, sh, use_mfma, x_dtype);
+  if ((st = check_workspace(d, workspace, workspace_bytes, need, ins, 4, g, beta, S0, o, S_T,
+                            sh.key_gate)) != GDN_OK)
+    return st;
+
+  hipStream_t s = (hipStream_t)stream;
+  if (conv_fused(d, sh, use_mfma, x_dtype))
+    return launched(gdn::launch_chunk_mfma_conv(sh, xq, xk, xv, conv_w, eps, g, beta, S0, o, S_T,
+                                                workspace, s),
+                    "chunked forward with convolution launch");
+  // the prologue into the workspace, then the chunked forward
+  const size_t ys = dsize(d->qkv_dtype);
+  char *q = (char *)workspace, *k = q + round256(nqk * ys), *v = k + round256(nqk * ys);
+  char *rest = v + round256(nv * ys);
+  hipError_t e = gdn::launch_prologue(xq, xk, xv, (gdn::DType)x_dtype, conv_w, q, k, v, sh.qkv, d->B,
+                                      d->T, d->Hk, d->Hv, d->dk, d->dv, eps, s);
+  if (e != hipSuccess) return launched(e, "prologue launch");
+  e = use_mfma ? gdn::launch_chunk_mfma(sh, q, k, v, g, beta, S0, o, S_T, rest, s)
+               : gdn::launch_chunk_f32(sh, q, k, v, g, beta, S0, o, S_T, s);
   return launched(e, "chunked forward launch");
 }
 

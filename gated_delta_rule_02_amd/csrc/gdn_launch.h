@@ -38,6 +38,14 @@ hipError_t launch_chunk_mfma(const Shape &sh, const void *q, const void *k, cons
                              float *ST, void *ws, hipStream_t s);
 size_t chunk_mfma_workspace(const Shape &sh);
 
+// The same with the convolution prologue inside (bf16 raw inputs, head
+// gate): equal to launch_prologue into q, k, v of sh.qkv followed by
+// launch_chunk_mfma.  `ws` holds chunk_mfma_conv_workspace(sh) bytes.
+hipError_t launch_chunk_mfma_conv(const Shape &sh, const void *xq, const void *xk, const void *xv,
+                                  const float *conv_w, float eps, const void *g, const void *beta,
+                                  const float *S0, float *o, float *ST, void *ws, hipStream_t s);
+size_t chunk_mfma_conv_workspace(const Shape &sh);
+
 // Internal chunk length the fp32 kernels use for a requested chunk and dk.
 int chunk_f32_internal(int chunk, int dk);
 

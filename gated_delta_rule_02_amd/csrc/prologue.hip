@@ -83,22 +83,14 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       float z[8];
-      float ss = 0.f;
+      const float ss = conv_silu8(w0, w1, w2, w3, xm3, xm2, xm1, xs[u], z);
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const float yv = w0[c] * xm3[c] + w1[c] * xm2[c] + w2[c] * xm1[c] + w3[c] * xs[u][c];
-        z[c] = yv * __builtin_amdgcn_rcpf(1.0f + __expf(-yv));   // SiLU; rcp is exact to 1 ulp
-        ss += z[c] * z[c];
         xm3[c] = xm2[c];
         xm2[c] = xm1[c];
         xm1[c] = xs[u][c];
       }
-      if (P.l2) {
-        ss = group_sum<LPR>(ss);
-        const float inv = rsqrtf(ss + a.eps);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) z[c] *= inv;
-      }
+      if (P.l2) l2_scale8<LPR>(z, ss, a.eps);
       if (t + u < t_end) store8(yb + (size_t)(t + u) * tok_stride, z);
     }
   }

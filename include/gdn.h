@@ -158,6 +158,31 @@ gdn_status gdn_fwd_chunked(const gdn_desc *d, const void *q, const void *k,
                            void *stream);
 
 /*
+ * gdn_fwd_chunked_conv -- the prologue and the chunked forward in one call:
+ * the same results as gdn_prologue(d, x_dtype, xq, xk, xv, conv_w, eps) into
+ * q, k, v of d->qkv_dtype followed by gdn_fwd_chunked(d, q, k, v, g, beta,
+ * S0) (the same arithmetic and roundings), without q, k, v as arguments.
+ * For bf16 raw inputs on the matrix-core path with the per-head gate the
+ * convolution runs inside the chunked kernels: q and k are made once per
+ * (chunk, key head) and kept in the workspace, v is made as the sequential
+ * pass loads it, so v never goes through memory.  Any other supported
+ * combination runs the prologue into the workspace first.
+ *
+ *   x_dtype, xq, xk, xv, conv_w, eps   as for gdn_prologue
+ *   g, beta, S0, o, S_T                as for gdn_fwd_chunked
+ *   workspace   device scratch of at least gdn_fwd_conv_workspace_bytes(d,
+ *               x_dtype) bytes, 16-byte aligned, not overlapping any other
+ *               argument (GDN_E_WORKSPACE if too small)
+ * Supported: what both gdn_prologue and gdn_fwd_chunked support for d.
+ */
+size_t gdn_fwd_conv_workspace_bytes(const gdn_desc *d, int32_t x_dtype);
+gdn_status gdn_fwd_chunked_conv(const gdn_desc *d, int32_t x_dtype, const void *xq,
+                                const void *xk, const void *xv, const float *conv_w,
+                                float eps, const void *g, const void *beta,
+                                const float *S0, float *o, float *S_T, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/*
  * gdn_decode_step -- one token per sequence: the recurrence above with T = 1,
  * the state updated in place.  For state row i (old values S_i, decayed
  * row D_i = alpha S_i, or S_i o alpha for the key-channel gate):
