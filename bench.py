@@ -4,13 +4,17 @@ One step = the whole hot path over one batch of the conv-prologue prefill
 workload (B 4, T 4096, 16 key / 48 value heads, d 128, chunk 64, bf16
 inputs): 4-tap conv + SiLU + L2 prologue -> chunked prefill (fp16 matrix
 cores, fp32 state) -> one decode step from the final state on a fresh token.
+The prologue runs inside the chunked kernels (gdn_fwd_chunked_conv, the same
+results as gdn_prologue followed by gdn_fwd_chunked); the two separate calls
+are timed too and reported under "workloads".
 `value` is prefill tokens/s of that step (B*T / step time).  Inputs are
 seeded synthetic data resident in HBM before the timed region.
 
 Also reported on the same line (each timed with HIP events on the stream the
 kernels run on):
-  roofline      the dominant kernel (the chunked forward: prep + sequential
-                launches) against the dense fp16 matrix-core peak;
+  roofline      the dominant kernel (the chunked forward with the prologue
+                inside: prep + sequential launches) against the dense fp16
+                matrix-core peak;
   kernels       prologue and decode against the HBM peak;
   decode        steps/s of the batched-decode workload (B 256, 1000 steps);
   workloads     the chunked forward on the long-prefill workload (B 1, T 65536,
@@ -131,6 +135,7 @@ def main():
     L = gdn.lib()
     desc = gdn.make_desc(B, T, Hk, Hv, dk, dv, C, gdn.F16, gdn.BF16, gdn.GATE_HEAD)
     ws = torch.empty(L.gdn_fwd_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    cws = torch.empty(L.gdn_fwd_conv_workspace_bytes(desc, gdn.BF16), dtype=torch.uint8, device=dev)
     import ctypes
     P = lambda t: ctypes.c_void_p(t.data_ptr())
     pdesc = gdn.make_desc(B, T, Hk, Hv, dk, dv, C, gdn.F16, gdn.F32, gdn.GATE_HEAD)
@@ -145,13 +150,16 @@ def main():
         gdn.check(L.gdn_fwd_chunked(ctypes.byref(desc), P(q), P(k), P(v), P(g), P(beta), None,
                                     P(o), P(ST), P(ws), ws.numel(), s_ptr))
 
+    def fused():
+        gdn.check(L.gdn_fwd_chunked_conv(ctypes.byref(desc), gdn.BF16, P(xq), P(xk), P(xv), P(w), 1e-6,
+                                         P(g), P(beta), None, P(o), P(ST), P(cws), cws.numel(), s_ptr))
+
     def decode():
         gdn.check(L.gdn_decode_step(ctypes.byref(ddesc), P(dq), P(dk_), P(dv_), P(dg), P(db), P(ST),
                                     P(od), s_ptr))
 
     def step():
-        prologue()
-        chunked()
+        fused()
         decode()
 
     # ------------------------------------------------------------------ timed steps
@@ -169,16 +177,20 @@ def main():
 
     # ------------------------------------------------------------------ per-kernel (HIP events)
     reps = max(5, args.steps)
+    t_fus = time_events(fused, reps, stream)
     t_pro = time_events(prologue, reps, stream)
     t_chk = time_events(chunked, reps, stream)
     bytes_pro = (2 * B * T * Hk * dk + B * T * Hv * dv) * (2 + 2) + w.numel() * 4
+    # the same bytes whether q, k, v or the raw inputs are read (both 2 bytes each)
     bytes_chk = (2 * B * T * Hk * dk + B * T * Hv * dv) * 2 + 2 * B * T * Hv * 2 \
         + B * T * Hv * dv * 4 + B * Hv * dv * dk * 4
+    bytes_fus = bytes_chk + w.numel() * 4
     flops_chk = FLOPS_PER_TOKEN_HEAD * B * T * Hv
-    achieved = flops_chk / t_chk / 1e12
+    achieved = flops_chk / t_fus / 1e12
     traffic = read_traffic()
-    log("prologue %.1f us (%.0f GB/s); chunked %.1f us (%.1f TFLOP/s, %.0f GB/s algorithmic)" %
-        (t_pro * 1e6, bytes_pro / t_pro / 1e9, t_chk * 1e6, achieved, bytes_chk / t_chk / 1e9))
+    log("chunked with prologue inside %.1f us (%.1f TFLOP/s, %.0f GB/s algorithmic); separately: "
+        "prologue %.1f us (%.0f GB/s) + chunked %.1f us" %
+        (t_fus * 1e6, achieved, bytes_fus / t_fus / 1e9, t_pro * 1e6, bytes_pro / t_pro / 1e9, t_chk * 1e6))
 
     # ------------------------------------------------------------------ batched decode workload
     dwl = BATCHED_DECODE
@@ -206,7 +218,11 @@ def main():
     del toks, S, S_init
 
     # ------------------------------------------------------------------ other prefill workloads
-    extra = {}
+    extra = {"prefill_conv_two_calls": {
+        "workload": wl.name + ", gdn_prologue then gdn_fwd_chunked",
+        "us_per_call": (t_pro + t_chk) * 1e6, "tokens_per_s": B * T / (t_pro + t_chk),
+        "prologue_us": t_pro * 1e6, "chunked_us": t_chk * 1e6,
+        "chunked_mfma_frac": flops_chk / t_chk / 1e12 / PEAK_F16_TFLOPS}}
     for key, xwl in (("long_prefill", LONG_PREFILL), ("key_gate_prefill", KDA_PREFILL)):
         log("workload: %s" % xwl.name)
         xi = prefill_device(xwl, dev)
@@ -267,12 +283,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": "prefill with conv prologue, then one decode step", "B": B, "T": T,
                    "Hk": Hk, "Hv": Hv, "dk": dk, "dv": dv, "chunk": C, "gate": "per value head",
-                   "step": "prologue + chunked prefill + 1 decode step"},
-        "roofline": {"kernel": "chunked forward (chunk_prep + chunk_seq launches)", "bound": "mfma",
-                     "achieved": achieved, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                   "step": "chunked prefill with the conv prologue inside (gdn_fwd_chunked_conv) "
+                           "+ 1 decode step"},
+        "roofline": {"kernel": "chunked forward with the prologue inside (chunk_prep + chunk_seq launches)",
+                     "bound": "mfma", "achieved": achieved, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_F16_TFLOPS, "traffic": traffic,
-                     "algorithmic_bytes": bytes_chk, "us_per_launch": t_chk * 1e6,
-                     "hbm_frac_algorithmic": bytes_chk / t_chk / 1e9 / PEAK_HBM_GBS},
+                     "algorithmic_bytes": bytes_fus, "us_per_launch": t_fus * 1e6,
+                     "hbm_frac_algorithmic": bytes_fus / t_fus / 1e9 / PEAK_HBM_GBS},
         "kernels": {
             "prologue": {"bound": "hbm", "achieved": bytes_pro / t_pro / 1e9, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": bytes_pro / t_pro / 1e9 / PEAK_HBM_GBS,
