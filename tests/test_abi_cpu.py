@@ -133,3 +133,38 @@ def test_workspace_checked_before_launch(L):
 
 def test_null_desc(L):
     assert L.gdn_fwd_chunked(None, *([None] * 9), 0, None) == 1
+
+
+def test_conv_workspace_query(L):
+    d = desc()                       # B 2, 6 value heads, 2 chunks, matrix-core path
+    ws = L.gdn_fwd_workspace_bytes(ctypes.byref(d))
+    B, T, Hk, Hv = d.B, d.T, d.Hk, d.Hv
+    # fused (bf16 raw inputs): the chunk matrices, then q and k after the prologue
+    assert L.gdn_fwd_conv_workspace_bytes(ctypes.byref(d), gdn.BF16) == ws + 2 * B * T * Hk * 128 * 2
+    # fp32 raw inputs: q, k, v buffers (256-byte rounded) and the chunk matrices
+    r = lambda x: (x + 255) // 256 * 256
+    nqk, nv = B * T * Hk * 128 * 2, B * T * Hv * 128 * 2
+    assert L.gdn_fwd_conv_workspace_bytes(ctypes.byref(d), gdn.F32) == 2 * r(nqk) + r(nv) + ws
+    assert L.gdn_fwd_conv_workspace_bytes(ctypes.byref(d), gdn.F16) == 0    # raw fp16 is not supported
+    assert L.gdn_fwd_conv_workspace_bytes(ctypes.byref(desc(Hv=5)), gdn.BF16) == 0
+
+
+def test_conv_rejects_before_launch(L):
+    d = desc()
+    need = L.gdn_fwd_conv_workspace_bytes(ctypes.byref(d), gdn.BF16)
+    P = ctypes.c_void_p
+    p = [P(FAKE + i * (1 << 32)) for i in range(10)]
+    # xq, xk, xv, conv_w | g, beta | S0 | o, S_T | workspace
+    call = lambda dd, xt, ptrs, eps=1e-6, ws=p[9], nbytes=need: L.gdn_fwd_chunked_conv(
+        ctypes.byref(dd), xt, *ptrs[:4], eps, *ptrs[4:6], None, *ptrs[6:8], ws, nbytes, None)
+    assert call(d, gdn.F16, p) == 3                      # raw fp16
+    assert call(d, gdn.BF16, p, eps=-1.0) == 1
+    assert call(d, gdn.BF16, p, nbytes=need - 16) == 5
+    assert call(d, gdn.BF16, p, ws=None) == 1
+    bad = list(p)
+    bad[6] = p[2]                                        # o written over xv
+    assert call(d, gdn.BF16, bad) == 1
+    bad = list(p)
+    bad[0] = P(FAKE + 8)
+    assert call(d, gdn.BF16, bad) == 4                   # misaligned xq
+    assert call(desc(Hv=5), gdn.BF16, p) == 2
