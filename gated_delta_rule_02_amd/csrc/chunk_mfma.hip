@@ -286,7 +286,7 @@ static_assert(P_OFF_AD + 4 * 16 * DST * 4 <= P_OFF_SC, "per-head matrices overla
 // SiLU, L2 normalisation) and written to cv.q and cv.k for the sequential
 // pass; the q and k arguments are not read.
 template <typename TQ, typename TG, bool CONV>
-__global__ __launch_bounds__(kThreads, CONV ? 2 : 4) void chunk_prep_kernel(
+__global__ __launch_bounds__(kThreads, (CONV && std::is_same<TQ, bf16_t>::value) ? 3 : 4) void chunk_prep_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TG *__restrict__ g,
     const TG *__restrict__ beta, uint4 *__restrict__ Tws, int T, int Hk, int Hv, int nchunks, int c0,
     ConvIn cv) {
@@ -301,6 +301,8 @@ __global__ __launch_bounds__(kThreads, CONV ? 2 : 4) void chunk_prep_kernel(
   const float *sGam = sc;
   const float *sB = sc + 2 * C;
   float *sGB = reinterpret_cast<float *>(smem + P_SMEM);   // [2][grp][C]: gate, beta per head
+  // CONV: the convolution taps of k, then q, for the key head (after sGB)
+  float4 *sTap = reinterpret_cast<float4 *>(smem + P_SMEM + (size_t)2 * (Hv / Hk) * C * 4);
 
   const int c = c0 + blockIdx.x;
   const int b = blockIdx.y / Hk, kh = blockIdx.y % Hk;
@@ -321,7 +323,6 @@ __global__ __launch_bounds__(kThreads, CONV ? 2 : 4) void chunk_prep_kernel(
   {
     constexpr int NL = CONV ? 7 : 4;
     uint4 uk[NL], uq[NL];
-    float wk[CONV ? 4 : 1][8], wq[CONV ? 4 : 1][8];
     if constexpr (CONV) {
 #pragma unroll
       for (int j = 0; j < 7; ++j) {
@@ -330,13 +331,8 @@ __global__ __launch_bounds__(kThreads, CONV ? 2 : 4) void chunk_prep_kernel(
         uk[j] = *reinterpret_cast<const uint4 *>(cv.xk + off);
         uq[j] = *reinterpret_cast<const uint4 *>(cv.xq + off);
       }
-#pragma unroll
-      for (int c8 = 0; c8 < 8; ++c8) {
-        const float4 a = *reinterpret_cast<const float4 *>(cv.wk + ((size_t)kh * DK + ch + c8) * 4);
-        const float4 bq = *reinterpret_cast<const float4 *>(cv.wq + ((size_t)kh * DK + ch + c8) * 4);
-        wk[0][c8] = a.x; wk[1][c8] = a.y; wk[2][c8] = a.z; wk[3][c8] = a.w;
-        wq[0][c8] = bq.x; wq[1][c8] = bq.y; wq[2][c8] = bq.z; wq[3][c8] = bq.w;
-      }
+      // the taps of k (threads 0..127) and q (128..255), one channel each
+      sTap[tid] = *reinterpret_cast<const float4 *>((tid < DK ? cv.wk : cv.wq) + ((size_t)kh * DK + (tid & (DK - 1))) * 4);
     } else {
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
@@ -374,8 +370,15 @@ __global__ __launch_bounds__(kThreads, CONV ? 2 : 4) void chunk_prep_kernel(
     __builtin_amdgcn_sched_barrier(0);
     const half8 hz = {};
     if constexpr (CONV) {
+      lds_barrier();   // the taps are in LDS
       // the prologue's arithmetic, rounded to the qkv type as it stores it
-      auto conv_rows = [&](const uint4 (&x)[7], const float (&w)[4][8], _Float16 *sX, uint4 (&y)[4]) {
+      auto conv_rows = [&](const uint4 (&x)[7], const float4 *taps, _Float16 *sX, uint4 (&y)[4]) {
+        float w[4][8];
+#pragma unroll
+        for (int c8 = 0; c8 < 8; ++c8) {
+          const float4 t4 = taps[ch + c8];
+          w[0][c8] = t4.x; w[1][c8] = t4.y; w[2][c8] = t4.z; w[3][c8] = t4.w;
+        }
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
           const int row = 4 * rb + it;
@@ -390,8 +393,8 @@ __global__ __launch_bounds__(kThreads, CONV ? 2 : 4) void chunk_prep_kernel(
           *reinterpret_cast<half8 *>(sX + row * KST + ch) = row < n ? to_half8(y[it], TQ{}) : hz;
         }
       };
-      conv_rows(uk, wk, sK, ky);
-      conv_rows(uq, wq, sQ, qy);
+      conv_rows(uk, sTap, sK, ky);
+      conv_rows(uq, sTap + DK, sQ, qy);
     } else {
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
@@ -1056,8 +1059,9 @@ hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v
   const int nchunks = (sh.T + C - 1) / C;
   uint4 *TPws = (uint4 *)ws;
   auto prep_k = chunk_prep_kernel<TQ, TG, CONV>;
-  // fixed layout, then gate and beta of the group's heads (fp32, 2 x grp x C)
-  const size_t smem = P_SMEM + (size_t)2 * (sh.Hv / sh.Hk) * C * 4;
+  // fixed layout, then gate and beta of the group's heads (fp32, 2 x grp x C),
+  // then (CONV) the taps of k and q
+  const size_t smem = P_SMEM + (size_t)2 * (sh.Hv / sh.Hk) * C * 4 + (CONV ? 2 * DK * 16 : 0);
   if (smem > 160 * 1024) return hipErrorInvalidValue;
   hipError_t e =
       hipFuncSetAttribute((const void *)prep_k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
