@@ -25,6 +25,8 @@ kernels run on):
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --calibrate-copy   (a plain 1 GiB device copy, five times: the
                                           reference for scaling rocprofv3 HBM byte counters)
+       python bench.py --profile-steps N  (N steps only, no JSON line: the program that
+                                          hardware-counter passes profile)
 """
 from __future__ import annotations
 
@@ -89,6 +91,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--profile-steps", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the forward pass here runs on a single MI355X "
@@ -161,6 +164,13 @@ def main():
     def step():
         fused()
         decode()
+
+    if args.profile_steps > 0:
+        for _ in range(args.profile_steps):
+            step()
+        torch.cuda.synchronize()
+        log("%d profile steps done" % args.profile_steps)
+        return
 
     # ------------------------------------------------------------------ timed steps
     log("warmup %d, timed %d steps" % (args.warmup, args.steps))

@@ -92,3 +92,38 @@ def test_fused_vs_oracle():
 
 def test_fused_full_size_equals_two_calls():
     fused_vs_two_calls(PREFILL_CONV, "prefill with conv, full size")
+
+
+def test_fused_graph_capture_segmented():
+    """The fused call in a configuration that runs as two overlapped segments
+    (side stream), captured into a graph and replayed with eager work between
+    the replays: every replay equals the eager call."""
+    wl = PREFILL_CONV.with_(B=1, T=64 * 33 + 17, Hk=2, Hv=6)
+    inp = make_prefill(wl)
+    say("conv graph capture: B=1 T=%d Hk=2 Hv=6 (two segments)" % wl.T)
+    xs, w = raw(inp)
+    g, beta = to_torch(inp["g"]), to_torch(inp["beta"])
+    o_e, S_e = gdn.fwd_chunked_conv(*xs, w, g, beta, chunk=64)
+    q, k, v = gdn.prologue(*xs, w, out_dtype=torch.float16)
+    o_2, S_2 = gdn.fwd_chunked(q, k, v, g, beta, chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(o_e, o_2) and torch.equal(S_e, S_2)
+    o = torch.full_like(o_e, float("nan"))
+    ST = torch.full_like(S_e, float("nan"))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):           # warm the allocator outside the capture
+        gdn.fwd_chunked_conv(*xs, w, g, beta, chunk=64, o=o, S_T=ST)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gdn.fwd_chunked_conv(*xs, w, g, beta, chunk=64, o=o, S_T=ST)
+    for rep in range(3):
+        o.fill_(float("nan"))
+        ST.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda").sum()   # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        assert torch.equal(o, o_e) and torch.equal(ST, S_e), "replay %d differs from the eager call" % rep
