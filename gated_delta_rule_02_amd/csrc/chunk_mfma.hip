@@ -695,15 +695,16 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
         const float4 t4 = sW[vch8 * 8 + c8];
         wv[0][c8] = t4.x; wv[1][c8] = t4.y; wv[2][c8] = t4.z; wv[3][c8] = t4.w;
       }
+      // the raw rows NV rb - 3 .. NV rb + NV - 1, widened once; only the first
+      // three can lie before the sequence start (zero there)
+      float x[NV + 3][8];
+#pragma unroll
+      for (int j = 0; j < NV + 3; ++j) unpack8(f.v[j], j < 3 && f.t0 + NV * vrb - 3 + j < 0, x[j]);
 #pragma unroll
       for (int it = 0; it < NV; ++it) {
         const int row = NV * vrb + it;
-        float x3[8], x2[8], x1[8], x0[8], z[8];
-        unpack8(f.v[it], f.t0 + row - 3 < 0, x3);
-        unpack8(f.v[it + 1], f.t0 + row - 2 < 0, x2);
-        unpack8(f.v[it + 2], f.t0 + row - 1 < 0, x1);
-        unpack8(f.v[it + 3], false, x0);
-        (void)conv_silu8(wv[0], wv[1], wv[2], wv[3], x3, x2, x1, x0, z);
+        float z[8];
+        (void)conv_silu8(wv[0], wv[1], wv[2], wv[3], x[it], x[it + 1], x[it + 2], x[it + 3], z);
         *reinterpret_cast<half8 *>(v_ + row * VST + vch8 * 8) =
             row < f.n ? to_half8(pack8(z, TQ{}), TQ{}) : hz;
       }
