@@ -271,16 +271,22 @@ constexpr int KDA_CHUNK_U4 = (KDA_SC + KDA_NSC + 15) / 16 * 16;
 // chunk_prep: per (chunk, key head) P0 = masked Q K^T; per (chunk, value head) T = (I + A)^{-1}, P = L o P0
 // ============================================================================
 // K and Q are only read before the value-head loop (into the G and P0
-// accumulators); the per-head matrices then reuse their space.
+// accumulators); the per-head matrices then reuse their space.  After them:
+// the gate and beta of the group's heads (2 x grp x C fp32), then the five
+// per-token scalars of the current head, which (convolution) first hold the
+// taps of k and q: the two are never live together.
 constexpr int P_OFF_K = 0;                              // [C][KST] fp16
 constexpr int P_OFF_Q = P_OFF_K + C * KST * 2;          // [C][KST] fp16
 constexpr int P_OFF_T = 0;                              // [C][CST] fp16 (over K)
 constexpr int P_OFF_P = P_OFF_T + C * CST * 2;          // [C][CST] fp16
 constexpr int P_OFF_AO = P_OFF_P + C * CST * 2;         // [C][CST] fp16
 constexpr int P_OFF_AD = P_OFF_AO + C * CST * 2;        // [4][16][DST] fp32
-constexpr int P_OFF_SC = P_OFF_Q + C * KST * 2;         // 5 x [C] fp32
-constexpr int P_SMEM = P_OFF_SC + 5 * C * 4;
-static_assert(P_OFF_AD + 4 * 16 * DST * 4 <= P_OFF_SC, "per-head matrices overlap the scalars");
+constexpr int P_OFF_GB = P_OFF_Q + C * KST * 2;         // then 2 x grp x C fp32
+constexpr int P_SC_BYTES = 5 * C * 4, P_TAP_BYTES = 2 * DK * 16;
+static_assert(P_OFF_AD + 4 * 16 * DST * 4 <= P_OFF_GB, "per-head matrices overlap the gates");
+inline size_t prep_smem(int grp, bool conv) {
+  return P_OFF_GB + (size_t)2 * grp * C * 4 + (conv ? P_TAP_BYTES : P_SC_BYTES);
+}
 
 // CONV: q and k are computed here from the raw inputs of cv (convolution,
 // SiLU, L2 normalisation) and written to cv.q and cv.k for the sequential
@@ -297,12 +303,11 @@ __global__ __launch_bounds__(kThreads, (CONV && std::is_same<TQ, bf16_t>::value)
   _Float16 *sP = reinterpret_cast<_Float16 *>(smem + P_OFF_P);
   _Float16 *sAo = reinterpret_cast<_Float16 *>(smem + P_OFF_AO);
   float *sAd = reinterpret_cast<float *>(smem + P_OFF_AD);
-  float *sc = reinterpret_cast<float *>(smem + P_OFF_SC);
+  float *sGB = reinterpret_cast<float *>(smem + P_OFF_GB);   // [2][grp][C]: gate, beta per head
+  float *sc = sGB + 2 * (Hv / Hk) * C;
   const float *sGam = sc;
   const float *sB = sc + 2 * C;
-  float *sGB = reinterpret_cast<float *>(smem + P_SMEM);   // [2][grp][C]: gate, beta per head
-  // CONV: the convolution taps of k, then q, for the key head (after sGB)
-  float4 *sTap = reinterpret_cast<float4 *>(smem + P_SMEM + (size_t)2 * (Hv / Hk) * C * 4);
+  float4 *sTap = reinterpret_cast<float4 *>(sc);   // CONV: taps of k, then q (before the head loop)
 
   const int c = c0 + blockIdx.x;
   const int b = blockIdx.y / Hk, kh = blockIdx.y % Hk;
@@ -1060,9 +1065,7 @@ hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v
   const int nchunks = (sh.T + C - 1) / C;
   uint4 *TPws = (uint4 *)ws;
   auto prep_k = chunk_prep_kernel<TQ, TG, CONV>;
-  // fixed layout, then gate and beta of the group's heads (fp32, 2 x grp x C),
-  // then (CONV) the taps of k and q
-  const size_t smem = P_SMEM + (size_t)2 * (sh.Hv / sh.Hk) * C * 4 + (CONV ? 2 * DK * 16 : 0);
+  const size_t smem = prep_smem(sh.Hv / sh.Hk, CONV);
   if (smem > 160 * 1024) return hipErrorInvalidValue;
   hipError_t e =
       hipFuncSetAttribute((const void *)prep_k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
