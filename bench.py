@@ -225,7 +225,22 @@ def main():
     bytes_dec = 2 * S.numel() * 4 + od2.numel() * 4 + (2 * dwl.B * dwl.Hk * dwl.dk + dwl.B * dwl.Hv * dwl.dv) * 2 \
         + 2 * dwl.B * dwl.Hv * 2
     log("decode %.1f us/step, %.0f steps/s, %.0f GB/s" % (t_dec * 1e6, 1 / t_dec, bytes_dec / t_dec / 1e9))
-    del toks, S, S_init
+    # the same loop captured into one HIP graph (1000 kernel nodes); its final
+    # state and last output must equal the eager loop's
+    S_eager, o_eager = S.clone(), od2.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cap = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for st in range(nsteps):
+            gdn.check(L.gdn_decode_step(ctypes.byref(d3), P(tq[st]), P(tk[st]), P(tv[st]), P(tg[st]),
+                                        P(tb[st]), P(S), P(od2), cap))
+    S.copy_(S_init)
+    torch.cuda.synchronize()
+    t_dec_graph = time_events(graph.replay, 1, stream) / nsteps
+    graph_equal = bool(torch.equal(S, S_eager) and torch.equal(od2, o_eager))
+    log("decode as one graph %.1f us/step (final state %s the eager loop's)" %
+        (t_dec_graph * 1e6, "equals" if graph_equal else "DIFFERS FROM"))
+    del toks, S, S_init, S_eager, graph
 
     # ------------------------------------------------------------------ other prefill workloads
     extra = {"prefill_conv_two_calls": {
@@ -309,7 +324,8 @@ def main():
                        "us_per_launch": t_dec * 1e6},
         },
         "decode": {"workload": "batched decode: B 256, 16/48 heads, d 128, fp32 state, %d steps" % nsteps,
-                   "steps_per_s": 1.0 / t_dec, "tokens_per_s": dwl.B / t_dec},
+                   "steps_per_s": 1.0 / t_dec, "tokens_per_s": dwl.B / t_dec,
+                   "graph_steps_per_s": 1.0 / t_dec_graph, "graph_equals_eager": graph_equal},
         "workloads": extra,
         "cpu_baseline": {"value": cpu_tokens_per_s, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
                          "sample": "fp64 prologue + token recurrence over the whole prefill workload "

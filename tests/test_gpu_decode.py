@@ -120,3 +120,45 @@ def test_decode_deterministic_and_in_place():
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
     assert not torch.equal(S1, to_torch(S0))
+
+
+def test_decode_loop_graph_capture():
+    """A loop of decode steps captured into one graph (the state carried in
+    place from step to step) and replayed several times from a reset state,
+    with eager work between replays: every replay equals the eager loop."""
+    wl = BATCHED_DECODE.with_(B=16)
+    steps = 12
+    say("decode loop graph capture: B=%d, %d steps" % (wl.B, steps))
+    S_init = to_torch(make_state(wl))
+    toks = [make_decode_token(wl, s) for s in range(steps)]
+    args = [[to_torch(t[n]) for n in ("q", "k", "v", "g", "beta")] for t in toks]
+    S = S_init.clone()
+    o = torch.empty((wl.B, wl.Hv, wl.dv), device="cuda")
+    outs = torch.empty((steps, wl.B, wl.Hv, wl.dv), device="cuda")
+
+    def loop():
+        for s in range(steps):
+            gdn.decode_step(*args[s], S, o=o)
+            outs[s].copy_(o)
+
+    loop()
+    torch.cuda.synchronize()
+    S_e, outs_e = S.clone(), outs.clone()
+    graph = torch.cuda.CUDAGraph()
+    S.copy_(S_init)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):        # warm-up on a side stream before capture
+        loop()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        loop()
+    for rep in range(3):
+        S.copy_(S_init)
+        outs.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        assert torch.equal(S, S_e) and torch.equal(outs, outs_e), "replay %d differs" % rep
