@@ -72,6 +72,17 @@ def read_traffic():
         return None
 
 
+def host_cpu():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def time_events(fn, reps, stream):
     import torch
     e0 = torch.cuda.Event(enable_timing=True)
@@ -330,7 +341,7 @@ def main():
         "cpu_baseline": {"value": cpu_tokens_per_s, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
                          "sample": "fp64 prologue + token recurrence over the whole prefill workload "
                                    "(4 x 4096 tokens, all 192 chains); the decode step is not included",
-                         "seconds": t_cpu},
+                         "seconds": t_cpu, "host_cpu": host_cpu(), "host_logical_cpus": os.cpu_count()},
     }
     print(json.dumps(line), flush=True)
 
