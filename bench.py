@@ -44,16 +44,20 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, GB/s
 PEAK_F16_TFLOPS = 2500.0         # MI355X dense fp16/bf16 matrix cores, TFLOP/s
 FLOPS_PER_TOKEN_HEAD = 180224    # algorithmic prefill flops per (token, value head) at C 64, d 128
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "chunk_fwd_prefill_conv_B4_T4096_pmc.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "gated_delta_rule_02_amd", "csrc", "chunk_mfma.hip")
+# the sources the chunked kernels are compiled from
+KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_02_amd", "csrc", f) for f in ("chunk_mfma.hip", "gdn_device.h")]
 
 
 def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic():
@@ -64,7 +68,7 @@ def read_traffic():
     except OSError:
         return None
     fields = dict(line.split("=", 1) for line in text.splitlines() if "=" in line and not line.startswith("#"))
-    if fields.get("kernel_source_sha256_16", "").strip() != source_hash(KERNEL_SOURCE):
+    if fields.get("kernel_source_sha256_16", "").strip() != source_hash(KERNEL_SOURCES):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -83,6 +87,18 @@ def host_cpu():
     return None
 
 
+def warm_up(fn, seconds=0.03):
+    """Call fn until `seconds` of wall time have passed (at least twice), so
+    that the GPU's clocks have come up before a timed region."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while n < 2 or time.perf_counter() - t0 < seconds:
+        fn()
+        torch.cuda.synchronize()
+        n += 1
+
+
 def time_events(fn, reps, stream):
     import torch
     e0 = torch.cuda.Event(enable_timing=True)
@@ -98,8 +114,10 @@ def time_events(fn, reps, stream):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # the GPU's clocks take some milliseconds of load to come up from idle: the
+    # default warm-up runs about 20 ms of steps, the timed region about 70 ms
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=0)
@@ -273,9 +291,8 @@ def main():
                                         P(xi["beta"]), None if xi["S0"] is None else P(xi["S0"]),
                                         P(xo), P(xst), P(xws), xws.numel(), s_ptr))
 
-        xrun()
-        torch.cuda.synchronize()
-        tx = time_events(xrun, 5, stream)
+        warm_up(xrun)
+        tx = time_events(xrun, 10, stream)
         ntok = xwl.B * xwl.T
         gdim = xwl.dk if xwl.gate == "key" else 1
         xbytes = (2 * ntok * xwl.Hk * xwl.dk + ntok * xwl.Hv * xwl.dv + ntok * xwl.Hv * (gdim + 1)) * 2 \

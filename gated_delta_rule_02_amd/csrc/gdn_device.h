@@ -109,13 +109,23 @@ template <int G> __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// x as computed in fp32.  The empty asm statement emits nothing; it only hides
+// how x was made, so that the compiler cannot merge that operation with a
+// narrowing conversion that follows (a mixed-precision fma rounds once where
+// a product and a conversion round twice).  Every kernel then narrows the
+// value the same way.
+__device__ __forceinline__ float fp32_value(float x) {
+  asm("" : "+v"(x));
+  return x;
+}
+
 // Causal 4-tap depthwise convolution and SiLU of 8 channels at one token:
 // x3, x2, x1 hold the inputs 3, 2 and 1 tokens back, x0 the current token's,
 // w0..w3 the taps (w3 multiplies the current token).  Writes z = y sigmoid(y)
 // and returns the sum of z^2 over the 8 channels.  Every kernel that applies
-// the convolution calls this one function, and every multiply-add in it is
-// an explicit fma (the compiler may not choose which products to fuse), so
-// they all round identically.
+// the convolution calls this one function, every multiply-add in it is an
+// explicit fma (the compiler may not choose which products to fuse) and z
+// leaves it as an fp32 value, so they all round identically.
 __device__ __forceinline__ float conv_silu8(const float (&w0)[8], const float (&w1)[8],
                                             const float (&w2)[8], const float (&w3)[8],
                                             const float (&x3)[8], const float (&x2)[8],
@@ -125,7 +135,7 @@ __device__ __forceinline__ float conv_silu8(const float (&w0)[8], const float (&
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     const float yv = __builtin_fmaf(w3[c], x0[c], __builtin_fmaf(w2[c], x1[c], __builtin_fmaf(w1[c], x2[c], w0[c] * x3[c])));
-    z[c] = yv * __builtin_amdgcn_rcpf(1.0f + __expf(-yv));   // SiLU; rcp is exact to 1 ulp
+    z[c] = fp32_value(yv * __builtin_amdgcn_rcpf(1.0f + __expf(-yv)));   // SiLU; rcp is exact to 1 ulp
     ss = __builtin_fmaf(z[c], z[c], ss);
   }
   return ss;
@@ -138,7 +148,7 @@ __device__ __forceinline__ void l2_scale8(float (&z)[8], float ss, float eps) {
   ss = group_sum<G>(ss);
   const float inv = rsqrtf(ss + eps);
 #pragma unroll
-  for (int c = 0; c < 8; ++c) z[c] *= inv;
+  for (int c = 0; c < 8; ++c) z[c] = fp32_value(z[c] * inv);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave by DPP moves: shifts by
