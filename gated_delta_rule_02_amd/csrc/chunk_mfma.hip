@@ -55,9 +55,10 @@
 //    so the compute waves share only the chunk's K, Q, V tiles, T, P and
 //    gate scalars, double-buffered in LDS: one barrier per chunk.  Four
 //    more waves (one per SIMD) do all the loading: chunk c + 2 is fetched
-//    and chunk c + 1 written to LDS while chunk c is computed.  Blocks are
-//    numbered so that workgroups sharing a key head run on one XCD (shared
-//    K and Q then hit in its L2).
+//    and chunk c + 1 written to LDS while chunk c is computed (with the
+//    prologue inside and fp16 q, k: K and Q of chunk c + 1 go straight from
+//    global memory to LDS instead).  Blocks are numbered so that workgroups
+//    sharing a key head run on one XCD (shared K and Q then hit in its L2).
 #include <algorithm>
 #include <map>
 #include <mutex>
@@ -543,14 +544,47 @@ struct SeqCfg {
   static constexpr int OFF_Q = OFF_K + 2 * C * KST * 2;    // 2 x [C][KST] fp16
   static constexpr int OFF_KD = OFF_Q + 2 * C * KST * 2;   // 2 x [C][KST] fp16 (key gate)
   static constexpr int OFF_V = OFF_KD + (KDA ? 2 * C * KST * 2 : 0);   // 2 x [C][VST] fp16
-  static constexpr int OFF_TP = OFF_V + 2 * C * VST * 2;   // 2 x [2 NFRAG][64] x 16 B
-  static constexpr int OFF_SC = OFF_TP + 2 * 2 * NFRAG * 64 * 16;   // 2 x [NSC] fp32
-  static constexpr int OFF_W = OFF_SC + 2 * NSC * 4;       // [WGC][4] fp32 (v taps, convolution)
+  static constexpr int TPS_U4 = 2 * NFRAG * 64 + NSC / 4;  // T, P fragments, then the scalars (16 B units)
+  static constexpr int OFF_TP = OFF_V + 2 * C * VST * 2;   // 2 x [TPS_U4] x 16 B
+  static constexpr int OFF_W = OFF_TP + 2 * TPS_U4 * 16;   // [WGC][4] fp32 (v taps, convolution)
   static constexpr int SMEM = OFF_W + WGC * 16;
   static_assert(SMEM <= 160 * 1024, "LDS");
   static_assert((C * DK / 8) % LT == 0 && (C * WGC / 8) % LT == 0, "loads per thread");
   static_assert(LW > 0 && LT >= NSC / 4, "one scalar piece per loading thread");
+  static_assert(NSC % 4 == 0 && (C * (KST / 8)) % 64 == 0, "16-byte pieces");
 };
+
+// Wave load g of a chunk's K and Q tiles straight into LDS (g < NK: K, then
+// Q): 64 pieces of 16 bytes, KP to a tile row of KST halves (the last piece
+// of a row is padding, which repeats the row's first).  Rows past n repeat
+// row n - 1.  Returns this lane's source, the wave's LDS destination, the
+// lane's row and its piece in the row (-1: padding).  Everything is selected
+// as a value (a function of the arguments), so that no variable has to stay
+// in memory for the choice.
+template <typename TQ>
+struct TilePiece {
+  const TQ *src;
+  _Float16 *dst;
+  int row, pc;
+};
+template <int NK, int KP, typename TQ>
+__device__ __forceinline__ TilePiece<TQ> tile_piece(int g, int n, size_t t0, int lane, const TQ *kb,
+                                                    const TQ *qb, int rs, _Float16 *tk, _Float16 *tq) {
+  const bool isK = g < NK;
+  const int i = isK ? g : g - NK;
+  const int e = 64 * i + lane;
+  const int row = e / KP, pc = e - row * KP;
+  return TilePiece<TQ>{(isK ? kb : qb) + (t0 + min(row, n - 1)) * rs + (pc < KP - 1 ? 8 * pc : 0),
+                       (isK ? tk : tq) + 8 * 64 * i, row, pc < KP - 1 ? pc : -1};
+}
+
+// One 16-byte piece per lane from global memory straight into LDS (the
+// gfx950 global_load_lds_dwordx4): lane i of the wave writes its piece to
+// dst + 16 i, dst being the same for the whole wave.  The wave's load counter
+// covers the write to LDS.
+__device__ __forceinline__ void lds_load16(const void *src, void *dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+}
 
 // The next chunk's raw loads.  Nothing is converted here, so no instruction
 // needs the data before the chunk is committed.
@@ -605,11 +639,13 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
   _Float16 *const sQb = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_Q);
   _Float16 *const sKdb = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_KD);
   _Float16 *const sVb = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_V);
-  uint4 *const sTPb = reinterpret_cast<uint4 *>(smem + Cfg::OFF_TP);
-  float *const sScb = reinterpret_cast<float *>(smem + Cfg::OFF_SC);
+  uint4 *const sTPb = reinterpret_cast<uint4 *>(smem + Cfg::OFF_TP);   // buffer b at b TPS_U4
+  constexpr int TPS_U4 = Cfg::TPS_U4, SC_AT = 2 * NFRAG * 64;   // the scalars follow T and P
   float4 *const sW = reinterpret_cast<float4 *>(smem + Cfg::OFF_W);
 
   using Fetch = SeqFetch<TQ, TG, NW, RT, KDA, LW, CONV>;
+  // fp16 q, k, v need no conversion: they are loaded straight into LDS
+  constexpr bool DMA = CONV && !KDA && std::is_same<TQ, f16_t>::value;
   // CONV: loading thread -> value channels 8 ch8 .. + 7 of the slice at the
   // chunk rows NV rb .. NV rb + NV - 1 (a row's channels on consecutive lanes)
   const int vrb = ltid / (WGC / 8), vch8 = ltid % (WGC / 8);
@@ -666,6 +702,24 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
       f.sc = wc[Cfg::SC_U4 + min(ltid, NSC / 4 - 1)];
     }
   };
+  // CONV: v of the lane's rows from the raw rows of f, with the prologue's
+  // arithmetic, rounded to the qkv type as it stores it, into the V tile v_
+  // (rows past the sequence end zero).  wv: the taps of the lane's channels.
+  auto conv_v = [&](const Fetch &f, _Float16 *v_, const float (&wv)[4][8]) __attribute__((always_inline)) {
+    // the raw rows NV rb - 3 .. NV rb + NV - 1, widened once; only the first
+    // three can lie before the sequence start (zero there)
+    float x[NV + 3][8];
+#pragma unroll
+    for (int j = 0; j < NV + 3; ++j) unpack8(f.v[j], j < 3 && f.t0 + NV * vrb - 3 + j < 0, x[j]);
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+      const int row = NV * vrb + it;
+      float z[8];
+      (void)conv_silu8(wv[0], wv[1], wv[2], wv[3], x[it], x[it + 1], x[it + 2], x[it + 3], z);
+      *reinterpret_cast<half8 *>(v_ + row * VST + vch8 * 8) =
+          row < f.n ? to_half8(pack8(z, TQ{}), TQ{}) : half8{};
+    }
+  };
   auto commit = [&](const Fetch &f, int buf) {
     // The loads issued before the commit stay ahead of its conversions.
     __builtin_amdgcn_sched_barrier(0);
@@ -673,7 +727,7 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
     // K and Q (and the state-update K) are fp16 in the workspace of the key gate
     using TK = typename std::conditional<KDA, f16_t, TQ>::type;
     const half8 hz = {};
-    if (ltid < NSC / 4) reinterpret_cast<uint4 *>(sScb + buf * NSC)[ltid] = f.sc;
+    if (ltid < NSC / 4) sTPb[buf * TPS_U4 + SC_AT + ltid] = f.sc;
 #pragma unroll
     for (int it = 0; it < NKQ; ++it) {
       const int e = ltid + LT * it;
@@ -687,10 +741,9 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
 #pragma unroll
     for (int it = 0; it < NTP; ++it) {
       const int e = ltid + LT * it;
-      if (e < 2 * NFRAG * 64) sTPb[buf * 2 * NFRAG * 64 + e] = f.tp[it];
+      if (e < 2 * NFRAG * 64) sTPb[buf * TPS_U4 + e] = f.tp[it];
     }
     if constexpr (CONV) {
-      // the prologue's arithmetic, rounded to the qkv type as it stores it;
       // the taps of the lane's 8 channels come from LDS.  Everything else is
       // written first, so that its registers are free during the arithmetic.
       __builtin_amdgcn_sched_barrier(0);
@@ -700,19 +753,7 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
         const float4 t4 = sW[vch8 * 8 + c8];
         wv[0][c8] = t4.x; wv[1][c8] = t4.y; wv[2][c8] = t4.z; wv[3][c8] = t4.w;
       }
-      // the raw rows NV rb - 3 .. NV rb + NV - 1, widened once; only the first
-      // three can lie before the sequence start (zero there)
-      float x[NV + 3][8];
-#pragma unroll
-      for (int j = 0; j < NV + 3; ++j) unpack8(f.v[j], j < 3 && f.t0 + NV * vrb - 3 + j < 0, x[j]);
-#pragma unroll
-      for (int it = 0; it < NV; ++it) {
-        const int row = NV * vrb + it;
-        float z[8];
-        (void)conv_silu8(wv[0], wv[1], wv[2], wv[3], x[it], x[it + 1], x[it + 2], x[it + 3], z);
-        *reinterpret_cast<half8 *>(v_ + row * VST + vch8 * 8) =
-            row < f.n ? to_half8(pack8(z, TQ{}), TQ{}) : hz;
-      }
+      conv_v(f, v_, wv);
     } else {
 #pragma unroll
       for (int it = 0; it < NV; ++it) {
@@ -724,6 +765,73 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
     }
   };
 
+  if (w >= NW && DMA) {
+    // Loading waves, the prologue inside with fp16 q and k: K and Q of chunk
+    // c + 1 go from global memory straight into the other LDS buffer while
+    // chunk c is computed (they need no conversion), and the raw v rows with
+    // the T and P fragments and the scalars of chunk c + 1, fetched into
+    // registers one chunk earlier (fa, fb alternate), are convolved and
+    // written there meanwhile.  Each wave waits for its own loads before the
+    // barrier that hands the buffer over.
+    const int lw = w - NW;
+    // NK wave loads a tile; wave lw issues loads lw, lw + LW, .., NPER of
+    // them, the last ones repeating one of its own (so every wave issues the
+    // same number and its waits have a fixed count).  Rows past n repeat
+    // row n - 1 (in bounds) and are zeroed once they have landed, each wave
+    // over the pieces it loaded itself.
+    constexpr int KP = KST / 8, NK = C * KP / 64, NTOT = 2 * NK, NPER = (NTOT + LW - 1) / LW;
+    static_assert(NTOT >= LW, "loads per wave");
+    float wv[4][8];
+#pragma unroll
+    for (int c8 = 0; c8 < 8; ++c8) {
+      const float4 t4 =
+          *reinterpret_cast<const float4 *>(cv.wv + ((size_t)h * DV + slice * WGC + vch8 * 8 + c8) * 4);
+      wv[0][c8] = t4.x; wv[1][c8] = t4.y; wv[2][c8] = t4.z; wv[3][c8] = t4.w;
+    }
+    Fetch fa, fb;
+    auto piece = [&](int j, int n, size_t t0, int buf) __attribute__((always_inline)) {
+      int g = lw + LW * j;
+      if (g >= NTOT) g -= LW;
+      return tile_piece<NK, KP>(g, n, t0, l, kb, qb, kq_rs, sKb + buf * C * KST, sQb + buf * C * KST);
+    };
+    auto load_chunk = [&](int c, int buf, const Fetch &fcur, Fetch &fnext) __attribute__((always_inline)) {
+      const int n = min(C, T - c * C);
+      const size_t t0 = (size_t)c * C;
+      fetch(fnext, min(c + 1, c_end - 1), FV | FTP);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < NPER; ++j) {
+        const auto pt = piece(j, n, t0, buf);
+        lds_load16(pt.src, pt.dst);
+      }
+      conv_v(fcur, sVb + buf * C * VST, wv);
+#pragma unroll
+      for (int it = 0; it < NTP; ++it) {
+        const int e = ltid + LT * it;
+        if (e < 2 * NFRAG * 64) sTPb[buf * TPS_U4 + e] = fcur.tp[it];
+      }
+      if (ltid < NSC / 4) sTPb[buf * TPS_U4 + SC_AT + ltid] = fcur.sc;
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt 0: this wave's K and Q pieces are in LDS
+      if (n < C) {
+        for (int j = 0; j < NPER; ++j) {
+          const auto pt = piece(j, n, t0, buf);
+          if (pt.row >= n && pt.pc >= 0) *reinterpret_cast<half8 *>(pt.dst + 8 * l) = half8{};
+        }
+      }
+    };
+    fetch(fa, c_begin, FV | FTP);
+    load_chunk(c_begin, 0, fa, fb);
+    lds_barrier();
+    for (int c = c_begin; c < c_end; c += 2) {
+      if (c + 1 < c_end) load_chunk(c + 1, 1, fb, fa);
+      lds_barrier();
+      if (c + 1 < c_end) {
+        if (c + 2 < c_end) load_chunk(c + 2, 0, fa, fb);
+        lds_barrier();
+      }
+    }
+    return;
+  }
   if (w >= NW) {
     // Loading waves: chunk c + 2 is loaded while chunk c is computed, and
     // chunk c + 1, loaded one chunk earlier, is written to the other LDS
@@ -786,8 +894,8 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
   auto compute = [&](int c) {
     const int buf = (c - c_begin) & 1;
     const _Float16 *cK = sKb + buf * C * KST, *cQ = sQb + buf * C * KST, *cV = sVb + buf * C * VST;
-    const uint4 *cT = sTPb + buf * 2 * NFRAG * 64, *cP = cT + NFRAG * 64;
-    const float *sc = sScb + buf * NSC;
+    const uint4 *cT = sTPb + buf * TPS_U4, *cP = cT + NFRAG * 64;
+    const float *sc = reinterpret_cast<const float *>(cT + SC_AT);
     // transpose-read bases: lane (g4, i) reads row 4 g4 + i / 4, columns 4 (i % 4) .. + 3
     const _Float16 *kT = cK + (4 * g4 + (ln >> 2)) * KST + 4 * (ln & 3);
     const _Float16 *vT = cV + (4 * g4 + (ln >> 2)) * VST + ic + 4 * (ln & 3);
