@@ -10,8 +10,9 @@
 // and every output written once.  One launch covers the q, k and v head rows
 // together: a head row of d channels is held by d/8 lanes, 8 channels each,
 // so one load is 16 bytes (bf16) per lane; each lane group walks a span of
-// kSpan tokens of its head row, keeping the last three inputs in registers,
-// and has the loads of kU tokens in flight before computing them.
+// kSpan tokens of its head row, keeping the last three inputs in registers;
+// the loads of the next kU tokens are in flight while the current ones are
+// computed and stored.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -19,8 +20,8 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kSpan = 32;  // tokens per lane group
-constexpr int kU = 8;      // tokens loaded ahead
+constexpr int kSpan = 16;  // tokens per lane group
+constexpr int kU = 4;      // tokens loaded ahead
 
 struct ProTensor {
   const void *x;
@@ -34,6 +35,33 @@ struct ProArgs {
   int B, T;
   float eps;
 };
+
+// Eight input channels as loaded (16 bytes of bf16, 32 of fp32), widened
+// only where they are used, so that a load in flight holds no conversion.
+template <typename TX>
+struct Raw8 {
+  uint4 v[sizeof(TX) / 2];
+};
+template <typename TX>
+__device__ __forceinline__ Raw8<TX> load_raw8(const TX *p) {
+  Raw8<TX> r;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(TX) / 2); ++i) r.v[i] = reinterpret_cast<const uint4 *>(p)[i];
+  return r;
+}
+__device__ __forceinline__ void widen8(const Raw8<bf16_t> &r, float (&x)[8]) {
+  const uint32_t w[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void widen8(const Raw8<float> &r, float (&x)[8]) {
+  const uint32_t w[8] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w, r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = __uint_as_float(w[i]);
+}
 
 template <typename TX, typename TO, int D>
 __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
@@ -69,6 +97,44 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
   TO *yb = reinterpret_cast<TO *>(P.y) + (size_t)b * a.T * tok_stride + (size_t)head * D + c0;
 
   float xm3[8], xm2[8], xm1[8];
+  if (t0 >= 3 && t0 + kSpan <= a.T) {
+    // A whole span with its whole history: the loads of the next kU tokens
+    // are issued before the current ones are computed and stored, and every
+    // store is unconditional, so each wait is for loads alone (one counter
+    // tracks loads and stores in issue order).
+    widen8(load_raw8(xb + (size_t)(t0 - 3) * tok_stride), xm3);
+    widen8(load_raw8(xb + (size_t)(t0 - 2) * tok_stride), xm2);
+    widen8(load_raw8(xb + (size_t)(t0 - 1) * tok_stride), xm1);
+    Raw8<TX> cur[kU], nxt[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) cur[u] = load_raw8(xb + (size_t)(t0 + u) * tok_stride);
+#pragma unroll
+    for (int it = 0; it < kSpan / kU; ++it) {
+      const int t = t0 + it * kU;
+      if (it + 1 < kSpan / kU) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) nxt[u] = load_raw8(xb + (size_t)(t + kU + u) * tok_stride);
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        float x0[8], z[8];
+        widen8(cur[u], x0);
+        const float ss = conv_silu8(w0, w1, w2, w3, xm3, xm2, xm1, x0, z);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          xm3[c] = xm2[c];
+          xm2[c] = xm1[c];
+          xm1[c] = x0[c];
+        }
+        if (P.l2) l2_scale8<LPR>(z, ss, a.eps);
+        store8(yb + (size_t)(t + u) * tok_stride, z);
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) cur[u] = nxt[u];
+    }
+    return;
+  }
+  // the first span of a sequence, or its last when it is cut short
 #pragma unroll
   for (int c = 0; c < 8; ++c) xm3[c] = xm2[c] = xm1[c] = 0.f;
   if (t0 >= 3) load8(xb + (size_t)(t0 - 3) * tok_stride, xm3);
