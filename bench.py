@@ -342,7 +342,9 @@ def main():
                      "bound": "mfma", "achieved": achieved, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_F16_TFLOPS, "traffic": traffic,
                      "algorithmic_bytes": bytes_fus, "us_per_launch": t_fus * 1e6,
-                     "hbm_frac_algorithmic": bytes_fus / t_fus / 1e9 / PEAK_HBM_GBS},
+                     "hbm_frac_algorithmic": bytes_fus / t_fus / 1e9 / PEAK_HBM_GBS,
+                     # the bytes the kernels actually move (rocprofv3 counters), per second, against the HBM peak
+                     "hbm_frac_traffic": None if traffic is None else traffic / t_fus / 1e9 / PEAK_HBM_GBS},
         "kernels": {
             "prologue": {"bound": "hbm", "achieved": bytes_pro / t_pro / 1e9, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": bytes_pro / t_pro / 1e9 / PEAK_HBM_GBS,
