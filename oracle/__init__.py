@@ -5,8 +5,8 @@ baseline leg of ``bench.py`` are the only callers.  The GPU library never
 imports, links or runs anything here, and nothing here imports the GPU
 library.
 
-``gdnref.c`` holds the token-by-token recurrence and the conv/SiLU/L2
-prologue, compiled with gcc into ``libgdnref.so`` and called through ctypes.
+``gdnref.c`` holds the token-by-token recurrence, the conv/SiLU/L2
+prologue and the gated output norm that follows the state read, compiled with gcc into ``libgdnref.so`` and called through ctypes.
 ``chunked.py`` holds a second, chunk-parallel formulation in NumPy that is used
 only to pin the recurrence (the two must agree to 1e-10).
 
@@ -51,6 +51,8 @@ def _load():
         lib.gdnref_recurrent.restype = I
         lib.gdnref_conv_silu.argtypes = [I, I, I, I, P, P, I, ctypes.c_double, P]
         lib.gdnref_conv_silu.restype = I
+        lib.gdnref_output_gate.argtypes = [ctypes.c_long, I, P, P, P, ctypes.c_double, P]
+        lib.gdnref_output_gate.restype = I
         _lib = lib
     return _lib
 
@@ -155,3 +157,24 @@ def prologue(xq, xk, xv, w, eps=1e-6):
     k = conv_silu(xk, w[nq:2 * nq], True, eps)
     v = conv_silu(xv, w[2 * nq:2 * nq + Hv * dv], False, eps)
     return q, k, v
+
+
+def output_gate(o, z, gain, eps):
+    """Gated output norm: every row of o over its last axis (d channels),
+    y = o / sqrt(mean(o^2) + eps) * gain * z * sigmoid(z).
+
+    o: [..., d] (taken as float64), z: same shape (float32 values as stored),
+    gain: [d].  Returns float64 of o's shape.
+    """
+    lib = _load()
+    o = np.ascontiguousarray(np.asarray(o, dtype=np.float64))
+    z = _f32(z)
+    gain = _f32(gain)
+    d = o.shape[-1]
+    if z.shape != o.shape or gain.shape != (d,):
+        raise ValueError("z must match o and gain must be [d]")
+    y = np.empty(o.shape, dtype=np.float64)
+    rc = lib.gdnref_output_gate(int(o.size // d), d, _ptr(o), _ptr(z), _ptr(gain), float(eps), _ptr(y))
+    if rc != 0:
+        raise ValueError("gdnref_output_gate rejected its arguments")
+    return y

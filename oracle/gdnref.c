@@ -217,3 +217,38 @@ int gdnref_conv_silu(int B, int T, int H, int d, const float *x,
       }
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Gated output norm after the state read                                   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * gdnref_output_gate: o [rows][d] (double), z [rows][d], gain [d] -> y [rows][d].
+ *   "Source notes", section "Linear attention", row gdn: the read-out of the
+ *   state is RMS-normalised, multiplied by a learned gain and by a SiLU gate.
+ *   "Adopt vs. port", entry burn-rmsnorm: the RMS norm divides a vector by the
+ *   square root of the mean of its squares plus eps, then multiplies it by the
+ *   gain, element by element.
+ * One row per (batch, token, value head), normalised over its d channels; one
+ * gain vector for every row; the SiLU gate is z sigmoid(z):
+ *     y_c = o_c / sqrt((1/d) sum_c' o_c'^2 + eps) * gain_c * z_c / (1 + e^{-z_c})
+ */
+int gdnref_output_gate(long rows, int d, const double *o, const float *z,
+                       const float *gain, double eps, double *y) {
+  long r;
+  int c;
+  if (rows < 0 || d <= 0 || eps < 0.0 || !o || !z || !gain || !y) return -1;
+  for (r = 0; r < rows; ++r) {
+    const double *orow = o + (size_t)r * d;
+    const float *zrow = z + (size_t)r * d;
+    double *yrow = y + (size_t)r * d;
+    double ss = 0.0;
+    for (c = 0; c < d; ++c) ss += orow[c] * orow[c];
+    const double inv = 1.0 / sqrt(ss / d + eps);
+    for (c = 0; c < d; ++c) {
+      const double zc = (double)zrow[c];
+      yrow[c] = orow[c] * inv * (double)gain[c] * (zc / (1.0 + exp(-zc)));
+    }
+  }
+  return 0;
+}

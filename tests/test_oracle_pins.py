@@ -291,3 +291,86 @@ def test_oracle_rejects_bad_shapes():
     q, k, v, g, beta, S0 = rand_problem(12, Hk=2, Hv=3)
     with pytest.raises(ValueError):
         oracle.recurrent(q, k, v, g, beta, S0)
+
+
+# --------------------------------------------------------------------------
+# Gated output norm: library routines, unit RMS rows, per-row scale, eps
+# --------------------------------------------------------------------------
+def _gate_problem(seed, shape=(2, 5, 3, 8)):
+    r = np.random.default_rng(seed)
+    o = r.standard_normal(shape)
+    z = r.standard_normal(shape).astype(np.float32)
+    gain = (1.0 + 0.3 * r.standard_normal(shape[-1])).astype(np.float32)
+    return o, z, gain
+
+
+def test_output_gate_matches_torch_rms_norm_and_silu():
+    # the whole operation is two library routines: torch's RMS norm (mean of
+    # squares over the last axis, eps inside the root, then the weight) and SiLU
+    import torch
+    import torch.nn.functional as F
+    o, z, gain = _gate_problem(21)
+    for eps in (0.0, 1e-5, 0.7):
+        y = oracle.output_gate(o, z, gain, eps)
+        ot = torch.from_numpy(o)
+        ref = F.rms_norm(ot, (o.shape[-1],), torch.from_numpy(gain.astype(np.float64)), eps) * \
+            F.silu(torch.from_numpy(z.astype(np.float64)))
+        np.testing.assert_allclose(y, ref.numpy(), rtol=1e-13, atol=1e-15)
+
+
+def test_output_gate_rows_have_unit_rms():
+    # with eps = 0 every row divided by its gate and gain has mean square 1
+    o, z, gain = _gate_problem(22)
+    z = np.where(np.abs(z) < 0.1, np.float32(0.5), z)          # keep the gate away from 0
+    y = oracle.output_gate(o, z, gain, 0.0)
+    zz = z.astype(np.float64)
+    ohat = y / (gain.astype(np.float64) * zz / (1 + np.exp(-zz)))
+    np.testing.assert_allclose(np.mean(ohat * ohat, axis=-1), 1.0, rtol=1e-12)
+    # and points the way o does
+    assert np.all(np.sign(ohat) == np.sign(o))
+
+
+def test_output_gate_scale_per_row():
+    # eps = 0: each (batch, token, head) row is normalised on its own, so a
+    # positive factor per row changes nothing and a negative one flips the sign
+    o, z, gain = _gate_problem(23)
+    r = np.random.default_rng(24)
+    f = r.uniform(0.01, 100.0, o.shape[:-1] + (1,)) * r.choice([-1.0, 1.0], o.shape[:-1] + (1,))
+    y = oracle.output_gate(o, z, gain, 0.0)
+    y2 = oracle.output_gate(o * f, z, gain, 0.0)
+    np.testing.assert_allclose(y2, y * np.sign(f), rtol=1e-12, atol=1e-15)
+
+
+def test_output_gate_constant_rows_closed_form():
+    # a row of d equal values a: o / rms = a / sqrt(a^2 + eps); with z large
+    # the gate is z itself (sigmoid(40) = 1 in double), with z = 0 it is 0
+    d = 16
+    a = np.array([0.01, -0.02, 3.0])
+    o = np.repeat(a[:, None], d, axis=1)
+    gain = np.linspace(0.5, 2.0, d).astype(np.float32)
+    eps = 1e-4
+    z = np.full(o.shape, 40.0, np.float32)
+    y = oracle.output_gate(o, z, gain, eps)
+    expect = (a / np.sqrt(a * a + eps))[:, None] * gain.astype(np.float64)[None, :] * 40.0
+    np.testing.assert_allclose(y, expect, rtol=1e-14)
+    assert np.all(oracle.output_gate(o, np.zeros(o.shape, np.float32), gain, eps) == 0.0)
+
+
+def test_output_gate_gain_is_per_channel():
+    # a one-hot gain keeps exactly its channel in every row
+    o, z, gain = _gate_problem(25)
+    j = 5
+    e = np.zeros(o.shape[-1], np.float32)
+    e[j] = 1.0
+    y = oracle.output_gate(o, z, e, 1e-5)
+    assert np.all(np.delete(y, j, axis=-1) == 0.0)
+    full = oracle.output_gate(o, z, np.ones_like(e), 1e-5)
+    np.testing.assert_array_equal(y[..., j], full[..., j])
+
+
+def test_output_gate_rejects_bad_shapes():
+    o, z, gain = _gate_problem(26)
+    with pytest.raises(ValueError):
+        oracle.output_gate(o, z[..., :-1], gain, 1e-5)
+    with pytest.raises(ValueError):
+        oracle.output_gate(o, z, gain[:-1], 1e-5)
