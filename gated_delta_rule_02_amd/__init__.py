@@ -12,6 +12,8 @@ Entry points (same names as the C functions):
   fwd_chunked(q, k, v, g, beta, S0, chunk) -> (o, S_T)
   fwd_chunked_conv(xq, xk, xv, conv_w, g, beta, S0, qkv_dtype, eps, chunk) -> (o, S_T)
   decode_step(q, k, v, g, beta, S) -> o          (S updated in place)
+  output_gate(o, z, gain, eps, out_dtype) -> y
+  fwd_chunked_conv_gated(xq, xk, xv, conv_w, g, beta, z, gain, S0, ...) -> (y, S_T)
 """
 from __future__ import annotations
 
@@ -67,6 +69,13 @@ def lib() -> ctypes.CDLL:
         L.gdn_fwd_conv_workspace_bytes.restype = S
         L.gdn_fwd_chunked_conv.argtypes = [D, I, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, S, P]
         L.gdn_fwd_chunked_conv.restype = I
+        L.gdn_output_gate.argtypes = [D, P, I, P, P, ctypes.c_float, I, P, P]
+        L.gdn_output_gate.restype = I
+        L.gdn_fwd_gated_workspace_bytes.argtypes = [D, I, I]
+        L.gdn_fwd_gated_workspace_bytes.restype = S
+        L.gdn_fwd_chunked_conv_gated.argtypes = [D, I, P, P, P, P, ctypes.c_float, P, P, P, P, P,
+                                                 ctypes.c_float, I, P, P, P, S, P]
+        L.gdn_fwd_chunked_conv_gated.restype = I
         L.gdn_decode_step.argtypes = [D, P, P, P, P, P, P, P, P]
         L.gdn_decode_step.restype = I
         L.gdn_status_str.argtypes = [I]
@@ -202,6 +211,58 @@ def fwd_chunked_conv(xq, xk, xv, conv_w, g, beta, S0=None, qkv_dtype=torch.float
                                  float(eps), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T),
                                  _ptr(ws), ws_bytes, _stream(stream)))
     return o, S_T
+
+
+def output_gate(o, z, gain, eps=1e-5, out_dtype=torch.bfloat16, y=None, stream=None):
+    """Gated output norm of every (token, value head) row of o (fp32 [B,T,Hv,dv]):
+    y = o / sqrt(mean(o^2) + eps) * gain * silu(z).  z [B,T,Hv,dv] (fp32, bf16
+    or fp16), gain fp32 [dv].  Returns y in out_dtype."""
+    B, T, Hv, dv = o.shape
+    _dev("o", o, None, (torch.float32,))
+    _dev("z", z, o.shape, tuple(_DTYPE_CODE))
+    _dev("gain", gain, (dv,), (torch.float32,))
+    if y is None:
+        y = torch.empty(o.shape, dtype=out_dtype, device=o.device)
+    _dev("y", y, o.shape, tuple(_DTYPE_CODE))
+    d = make_desc(B, T, 1, Hv, 16, dv, 64, F32, F32, GATE_HEAD)
+    check(lib().gdn_output_gate(ctypes.byref(d), _ptr(o), _DTYPE_CODE[z.dtype], _ptr(z), _ptr(gain),
+                                float(eps), _DTYPE_CODE[y.dtype], _ptr(y), _stream(stream)))
+    return y
+
+
+def fwd_chunked_conv_gated(xq, xk, xv, conv_w, g, beta, z, gain, S0=None, qkv_dtype=torch.float16,
+                           eps=1e-6, norm_eps=1e-5, out_dtype=torch.bfloat16, chunk=64, y=None,
+                           S_T=None, stream=None):
+    """fwd_chunked_conv followed by output_gate(o, z, gain, norm_eps) in one call
+    (o is not returned).  z [B,T,Hv,dv] in the raw inputs' dtype.  Returns (y, S_T)."""
+    B, T, Hk, dk = xq.shape
+    Hv, dv = xv.shape[2], xv.shape[3]
+    _dev("xq", xq, (B, T, Hk, dk))
+    _dev("xk", xk, (B, T, Hk, dk), (xq.dtype,))
+    _dev("xv", xv, (B, T, Hv, dv), (xq.dtype,))
+    _dev("conv_w", conv_w, (2 * Hk * dk + Hv * dv, 4), (torch.float32,))
+    gate = _gate_kind(_dev("g", g), B, T, Hv, dk)
+    _dev("beta", beta, (B, T, Hv), (g.dtype,))
+    _dev("z", z, (B, T, Hv, dv), (xq.dtype,))
+    _dev("gain", gain, (dv,), (torch.float32,))
+    if S0 is not None:
+        _dev("S0", S0, (B, Hv, dv, dk), (torch.float32,))
+    if y is None:
+        y = torch.empty((B, T, Hv, dv), dtype=out_dtype, device=xq.device)
+    if S_T is None:
+        S_T = torch.empty((B, Hv, dv, dk), dtype=torch.float32, device=xq.device)
+    _dev("y", y, (B, T, Hv, dv), tuple(_DTYPE_CODE))
+    _dev("S_T", S_T, (B, Hv, dv, dk), (torch.float32,))
+    d = make_desc(B, T, Hk, Hv, dk, dv, chunk, _DTYPE_CODE[qkv_dtype], _DTYPE_CODE[g.dtype], gate)
+    L = lib()
+    xt = _DTYPE_CODE[xq.dtype]
+    ws_bytes = L.gdn_fwd_gated_workspace_bytes(ctypes.byref(d), xt, _DTYPE_CODE[y.dtype])
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=xq.device) if ws_bytes else None
+    check(L.gdn_fwd_chunked_conv_gated(ctypes.byref(d), xt, _ptr(xq), _ptr(xk), _ptr(xv), _ptr(conv_w),
+                                       float(eps), _ptr(g), _ptr(beta), _ptr(S0), _ptr(z), _ptr(gain),
+                                       float(norm_eps), _DTYPE_CODE[y.dtype], _ptr(y), _ptr(S_T),
+                                       _ptr(ws), ws_bytes, _stream(stream)))
+    return y, S_T
 
 
 def decode_step(q, k, v, g, beta, S, o=None, stream=None):

@@ -548,6 +548,9 @@ struct SeqCfg {
   static constexpr int OFF_TP = OFF_V + 2 * C * VST * 2;   // 2 x [TPS_U4] x 16 B
   static constexpr int OFF_W = OFF_TP + 2 * TPS_U4 * 16;   // [WGC][4] fp32 (v taps, convolution)
   static constexpr int SMEM = OFF_W + WGC * 16;
+  // with the output gate: the row sums of squares of two chunks, [2][C][NW] fp32
+  static constexpr int OFF_SS = SMEM;
+  static constexpr int SMEM_GATE = OFF_SS + 2 * C * NW * 4;
   static_assert(SMEM <= 160 * 1024, "LDS");
   static_assert((C * DK / 8) % LT == 0 && (C * WGC / 8) % LT == 0, "loads per thread");
   static_assert(LW > 0 && LT >= NSC / 4, "one scalar piece per loading thread");
@@ -601,12 +604,14 @@ struct SeqFetch {
 // state-update K, beta and Gamma_n come from the workspace (q, k, g, beta are
 // not read) and the state decays per key channel.  CONV: v is computed from
 // the raw rows cv.xv as it is loaded (convolution and SiLU); v is not read.
-template <typename TQ, typename TG, int NW, int RT, bool KDA, int LW, bool CONV>
+// GATE (a whole value head per workgroup): the gated output norm is applied
+// to the chunk's outputs and y is written instead of o (which is not used).
+template <typename TQ, typename TG, int NW, int RT, bool KDA, int LW, bool CONV, bool GATE>
 __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *__restrict__ v,
     const TG *__restrict__ g, const TG *__restrict__ beta, const uint4 *__restrict__ ws,
     const float *__restrict__ S0, float *__restrict__ o, float *__restrict__ ST, int T, int Hk,
-    int Hv, int ntasks, int nchunks, int c_begin, int c_end, ConvIn cv) {
+    int Hv, int ntasks, int nchunks, int c_begin, int c_end, ConvIn cv, GateArgs ga) {
   using Cfg = SeqCfg<NW, RT, KDA, LW>;
   constexpr int NSC = Cfg::NSC;
   constexpr int LT = Cfg::LT, WGC = Cfg::WGC, NS = Cfg::NS, VST = Cfg::VST;
@@ -870,7 +875,7 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
 
   const int ic = w * 16 * RT;             // this wave's first value row within the workgroup
   const int iw0 = slice * WGC + ic;       // ... within the head
-  float *ob = o + ((size_t)b * T * Hv + h) * DV + iw0 + 4 * g4;
+  float *ob = GATE ? nullptr : o + ((size_t)b * T * Hv + h) * DV + iw0 + 4 * g4;
 
   // state: row tile t (value rows iw0 + 16 t ..), tiles J of S^T; the lane
   // holds S[iw0 + 16 t + ln][16 J + 4 g4 + ii]
@@ -888,10 +893,32 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
       accS[t][J] = s;
     }
 
+  // The gated output norm: the row sums of squares of a chunk's outputs are
+  // combined over the compute waves through LDS (written before the chunk's
+  // barrier, read after it), so the outputs of chunk c are normalised and
+  // stored just after that barrier.  The lane's gain values are loaded with
+  // the entering state and its z values at the start of each chunk (rows
+  // past the end of the sequence re-read the last one).
+  static_assert(!GATE || (NS == 1 && RT == 2 && NW == 4 && !KDA), "the gate needs a whole value head");
+  float gw[RT][4];
+  const bf16_t *zb = nullptr;
+  // z and y move as 16 bytes per lane: lanes of lane groups g4 and g4 ^ 1
+  // hold the 8 rows 8 (g4 >> 1) .. + 7 of a tile for one token each (row
+  // block 2 p + (g4 & 1)), exchanged with __shfl_xor(., 16)
+  const bool godd = g4 & 1;
+  const size_t yoff = ((size_t)b * T * Hv + h) * DV + iw0 + 8 * (g4 >> 1);
+  if constexpr (GATE) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t) load4(ga.gain + iw0 + 16 * t + 4 * g4, gw[t]);
+    zb = (const bf16_t *)ga.z + yoff;
+  }
+  uint4 zl[RT][2];   // z of a chunk as loaded: [tile][row block pair]
+  uint2 yp[RT][4];   // y of a chunk, 16-bit, this lane's 4 rows per (tile, row block)
+
   // The arithmetic of chunk c, from LDS buffer (c - c_begin) & 1: the state
   // moves on to the chunk's end and accO gets the chunk's outputs O^T.
   float4v accO[RT][4];
-  auto compute = [&](int c) {
+  auto compute = [&](int c, auto &&mid) {
     const int buf = (c - c_begin) & 1;
     const _Float16 *cK = sKb + buf * C * KST, *cQ = sQb + buf * C * KST, *cV = sVb + buf * C * VST;
     const uint4 *cT = sTPb + buf * TPS_U4, *cP = cT + NFRAG * 64;
@@ -932,6 +959,8 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
         accO[t][R] = ao;
       }
     }
+
+    mid();
 
     // X = beta V - beta Gamma (K S^T), as fragments over the chunk rows
     // (V rows 16 R + 4 g4 .. + 3 at this lane's value column, by transpose reads)
@@ -1039,14 +1068,110 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
     }
   };
 
-  // No loads after the entering state, so the output stores never hold up a
-  // wait.
+  // the wave's partial row sums of squares of the chunk's outputs (over its
+  // 32 value rows: the lane's 8 in order, then lane groups g4 ^ 1 and g4 ^ 2)
+  auto gate_partials = [&](int c) {
+    float *ss = reinterpret_cast<float *>(smem + Cfg::OFF_SS) + ((c - c_begin) & 1) * C * NW;
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+      const float x[8] = {accO[0][R][0], accO[0][R][1], accO[0][R][2], accO[0][R][3],
+                          accO[1][R][0], accO[1][R][1], accO[1][R][2], accO[1][R][3]};
+      float p = gate_sumsq8(x);
+      p = p + __shfl_xor(p, 16, 64);
+      p = p + __shfl_xor(p, 32, 64);
+      if (g4 == 0) ss[(16 * R + ln) * NW + w] = p;
+    }
+  };
+  // after the barrier: the row sums over the waves (in wave order), then y
+  // of chunk c as 16-bit values in yp.  The z loads were issued half a chunk
+  // earlier; one wait for all of them here (for the compiler, a wait for a
+  // load issued after a store would also wait for that store).
+  auto gate_finish = [&](int c) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    // this lane's 4 rows of z per (tile, row block): keep one half of each
+    // load, take the other from the partner lane
+    uint2 zr[RT][4];
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const uint4 v = zl[t][p];
+        const uint2 keep = godd ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y);
+        const uint2 send = godd ? make_uint2(v.x, v.y) : make_uint2(v.z, v.w);
+        const uint2 recv = make_uint2(__shfl_xor(send.x, 16, 64), __shfl_xor(send.y, 16, 64));
+        zr[t][2 * p] = godd ? recv : keep;
+        zr[t][2 * p + 1] = godd ? keep : recv;
+      }
+    const float4 *ss = reinterpret_cast<const float4 *>(smem + Cfg::OFF_SS) + ((c - c_begin) & 1) * C;
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+      const float4 pw = ss[16 * R + ln];
+      const float inv = gate_inv_rms<DV>(((pw.x + pw.y) + pw.z) + pw.w, ga.eps);
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const uint2 u = zr[t][R];
+        const float zz[4] = {__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                             __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u)};
+        float yv[4];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) yv[ii] = gate_apply(accO[t][R][ii], inv, gw[t][ii], zz[ii]);
+        yp[t][R] = ga.yt == DType::BF16 ? pack4_bf16(yv) : pack4_f16(yv);
+      }
+    }
+  };
+  // the stores of chunk c's y (issued in the middle of the next chunk's
+  // arithmetic, away from the loading waves' burst of loads after the
+  // barrier), then the z loads of chunk c + 1 (rows past the end of the
+  // sequence re-read the last one)
+  auto gate_emit = [&](int c) {
+    const int t0 = c * C;
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const uint2 a = yp[t][2 * p], bq = yp[t][2 * p + 1];
+        const uint2 send = godd ? a : bq;
+        const uint2 recv = make_uint2(__shfl_xor(send.x, 16, 64), __shfl_xor(send.y, 16, 64));
+        const uint4 out = godd ? make_uint4(recv.x, recv.y, bq.x, bq.y) : make_uint4(a.x, a.y, recv.x, recv.y);
+        const int tok = t0 + 16 * (2 * p + godd) + ln;
+        if (tok < T) *reinterpret_cast<uint4 *>((uint16_t *)ga.y + yoff + (size_t)tok * v_rs + 16 * t) = out;
+      }
+  };
+  auto gate_load_z = [&](int c) {
+    const int t0 = c * C;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const size_t tt = (size_t)min(t0 + 16 * (2 * p + godd) + ln, T - 1);
+#pragma unroll
+      for (int t = 0; t < RT; ++t) zl[t][p] = *reinterpret_cast<const uint4 *>(zb + tt * v_rs + 16 * t);
+    }
+  };
+
+  // No loads after the entering state but the gate's z values (whose wait
+  // comes a whole chunk after the previous output stores), so the output
+  // stores never hold up a wait.  With the gate, the entering state and the
+  // gain are waited for here: otherwise the compiler's wait for them inside
+  // the loop (the loop merges the first iteration with the later ones) would
+  // also wait for the previous chunk's output stores.
+  if constexpr (GATE) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   lds_barrier();
   for (int c = c_begin; c < c_end; ++c) {
-    compute(c);
-    store_o(c);
+    compute(c, [&] {
+      if constexpr (GATE) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (c > c_begin) gate_emit(c - 1);
+        gate_load_z(c);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    });
+    if constexpr (GATE)
+      gate_partials(c);
+    else
+      store_o(c);
     lds_barrier();
+    if constexpr (GATE) gate_finish(c);
   }
+  if constexpr (GATE) gate_emit(c_end - 1);
 
   // final state
 #pragma unroll
@@ -1057,19 +1182,21 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
           make_float4(accS[t][J][0], accS[t][J][1], accS[t][J][2], accS[t][J][3]);
 }
 
-template <typename TQ, typename TG, int NW, int RT, bool KDA, int LW, bool CONV = false>
+template <typename TQ, typename TG, int NW, int RT, bool KDA, int LW, bool CONV = false, bool GATE = false>
 hipError_t launch_seq(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
                       const void *beta, const uint4 *TPws, const float *S0, float *o, float *ST,
-                      int nchunks, int c_begin, int c_end, hipStream_t st, const ConvIn &cv = ConvIn{}) {
+                      int nchunks, int c_begin, int c_end, hipStream_t st, const ConvIn &cv = ConvIn{},
+                      const GateArgs &ga = GateArgs{}) {
   using Cfg = SeqCfg<NW, RT, KDA, LW>;
-  auto kern = chunk_seq_kernel<TQ, TG, NW, RT, KDA, LW, CONV>;
-  hipError_t e =
-      hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::SMEM);
+  constexpr int smem = GATE ? Cfg::SMEM_GATE : Cfg::SMEM;
+  static_assert(smem <= 160 * 1024, "LDS");
+  auto kern = chunk_seq_kernel<TQ, TG, NW, RT, KDA, LW, CONV, GATE>;
+  hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   if (e != hipSuccess) return e;
   const int ntasks = sh.B * sh.Hv * Cfg::NS;
-  hipLaunchKernelGGL(kern, dim3(ntasks), dim3(Cfg::THREADS), Cfg::SMEM, st, (const TQ *)q,
-                     (const TQ *)k, (const TQ *)v, (const TG *)g, (const TG *)beta, TPws, S0, o, ST,
-                     sh.T, sh.Hk, sh.Hv, ntasks, nchunks, c_begin, c_end, cv);
+  hipLaunchKernelGGL(kern, dim3(ntasks), dim3(Cfg::THREADS), smem, st, (const TQ *)q, (const TQ *)k,
+                     (const TQ *)v, (const TG *)g, (const TG *)beta, TPws, S0, o, ST, sh.T, sh.Hk, sh.Hv,
+                     ntasks, nchunks, c_begin, c_end, cv, ga);
   return hipGetLastError();
 }
 
@@ -1169,7 +1296,7 @@ inline bool seq_overlap(long heads) { return heads <= 48; }
 template <typename TQ, typename TG, bool CONV>
 hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
                     const void *beta, const float *S0, float *o, float *ST, void *ws, hipStream_t st,
-                    const ConvIn &cv) {
+                    const ConvIn &cv, const GateArgs *gate = nullptr) {
   const int nchunks = (sh.T + C - 1) / C;
   uint4 *TPws = (uint4 *)ws;
   auto prep_k = chunk_prep_kernel<TQ, TG, CONV>;
@@ -1191,6 +1318,10 @@ hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v
   // two tiles); 64 and 32 rows: one row tile per compute wave.
   const long heads = (long)sh.B * sh.Hv;
   auto seq = [&](int cb, int ce, const float *s0, hipStream_t s) {
+    if constexpr (CONV)
+      if (gate)
+        return launch_seq<TQ, TG, 4, 2, false, 4, CONV, true>(sh, qs, ks, v, g, beta, TPws, s0, nullptr, ST,
+                                                              nchunks, cb, ce, s, cv, *gate);
     if (heads > 128)
       return launch_seq<TQ, TG, 4, 2, false, 4, CONV>(sh, qs, ks, v, g, beta, TPws, s0, o, ST, nchunks, cb,
                                                       ce, s, cv);
@@ -1518,9 +1649,13 @@ hipError_t launch_chunk_mfma(const Shape &sh, const void *q, const void *k, cons
              : launch_t<f16_t, bf16_t, false>(sh, q, k, v, g, beta, S0, o, ST, ws, st, none);
 }
 
+bool chunk_mfma_gate_inside(const Shape &sh) { return !sh.key_gate && (long)sh.B * sh.Hv > 128; }
+
 hipError_t launch_chunk_mfma_conv(const Shape &sh, const void *xq, const void *xk, const void *xv,
                                   const float *conv_w, float eps, const void *g, const void *beta,
-                                  const float *S0, float *o, float *ST, void *ws, hipStream_t st) {
+                                  const float *S0, float *o, float *ST, void *ws, hipStream_t st,
+                                  const GateArgs *gate) {
+  if (gate && (!chunk_mfma_gate_inside(sh) || gate->yt == DType::F32)) return hipErrorInvalidValue;
   // workspace: the chunk matrices, then q and k after the prologue
   const size_t nqk = (size_t)sh.B * sh.T * sh.Hk * DK;
   char *base = (char *)ws;
@@ -1536,11 +1671,12 @@ hipError_t launch_chunk_mfma_conv(const Shape &sh, const void *xq, const void *x
   cv.eps = eps;
   if (sh.qkv == DType::BF16)
     return sh.gate_t == DType::F32
-               ? launch_t<bf16_t, float, true>(sh, nullptr, nullptr, nullptr, g, beta, S0, o, ST, ws, st, cv)
-               : launch_t<bf16_t, bf16_t, true>(sh, nullptr, nullptr, nullptr, g, beta, S0, o, ST, ws, st, cv);
+               ? launch_t<bf16_t, float, true>(sh, nullptr, nullptr, nullptr, g, beta, S0, o, ST, ws, st, cv, gate)
+               : launch_t<bf16_t, bf16_t, true>(sh, nullptr, nullptr, nullptr, g, beta, S0, o, ST, ws, st, cv,
+                                                gate);
   return sh.gate_t == DType::F32
-             ? launch_t<f16_t, float, true>(sh, nullptr, nullptr, nullptr, g, beta, S0, o, ST, ws, st, cv)
-             : launch_t<f16_t, bf16_t, true>(sh, nullptr, nullptr, nullptr, g, beta, S0, o, ST, ws, st, cv);
+             ? launch_t<f16_t, float, true>(sh, nullptr, nullptr, nullptr, g, beta, S0, o, ST, ws, st, cv, gate)
+             : launch_t<f16_t, bf16_t, true>(sh, nullptr, nullptr, nullptr, g, beta, S0, o, ST, ws, st, cv, gate);
 }
 
 size_t chunk_mfma_conv_workspace(const Shape &sh) {

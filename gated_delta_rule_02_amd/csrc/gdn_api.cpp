@@ -197,8 +197,8 @@ gdn_status check_chunked(const gdn_desc *d, gdn::Shape *sh, bool *use_mfma_out) 
 // Pointer checks of the chunked forward: ins are the ranges of q, k, v (or
 // the raw inputs and taps of the convolution), g and beta.
 gdn_status check_chunked_ptrs(const gdn_desc *d, const gdn::Shape &sh, const Range *ins, int nins,
-                              const void *g, const void *beta, const float *S0, float *o,
-                              float *S_T) {
+                              const void *g, const void *beta, const float *S0, const void *o,
+                              float *S_T, size_t o_bytes = 0) {
   const char *names[] = {"g", "beta", "o", "S_T"};
   const void *ptrs[] = {g, beta, o, S_T};
   gdn_status st = check_ptrs(names, ptrs, 4);
@@ -207,7 +207,7 @@ gdn_status check_chunked_ptrs(const gdn_desc *d, const gdn::Shape &sh, const Ran
   const size_t bt = (size_t)d->B * d->T;
   const size_t gs = dsize(d->gate_dtype);
   const size_t state_bytes = (size_t)d->B * d->Hv * d->dv * d->dk * 4;
-  const Range ro = range(o, bt * d->Hv * d->dv * 4);
+  const Range ro = range(o, o_bytes ? o_bytes : bt * d->Hv * d->dv * 4);
   const Range rst = range(S_T, state_bytes);
   const Range rg = range(g, bt * d->Hv * (sh.key_gate ? d->dk : 1) * gs), rb = range(beta, bt * d->Hv * gs);
   for (int i = 0; i < nins + 2; ++i) {
@@ -229,7 +229,8 @@ gdn_status check_chunked_ptrs(const gdn_desc *d, const gdn::Shape &sh, const Ran
 // argument.
 gdn_status check_workspace(const gdn_desc *d, void *workspace, size_t workspace_bytes, size_t need,
                            const Range *ins, int nins, const void *g, const void *beta,
-                           const float *S0, float *o, float *S_T, bool key_gate) {
+                           const float *S0, const void *o, float *S_T, bool key_gate,
+                           size_t o_bytes = 0) {
   if (workspace_bytes < need)
     return fail(GDN_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
   if (need == 0) return GDN_OK;
@@ -243,7 +244,8 @@ gdn_status check_workspace(const gdn_desc *d, void *workspace, size_t workspace_
   if (overlap(rw, range(g, bt * d->Hv * (key_gate ? d->dk : 1) * gs)) ||
       overlap(rw, range(beta, bt * d->Hv * gs)))
     return fail(GDN_E_ARG, "workspace must not overlap an input");
-  if (overlap(rw, range(o, bt * d->Hv * d->dv * 4)) || overlap(rw, range(S_T, state_bytes)) ||
+  if (overlap(rw, range(o, o_bytes ? o_bytes : bt * d->Hv * d->dv * 4)) ||
+      overlap(rw, range(S_T, state_bytes)) ||
       (S0 && overlap(rw, range(S0, state_bytes))))
     return fail(GDN_E_ARG, "workspace must not overlap o, S0 or S_T");
   return GDN_OK;
@@ -275,6 +277,53 @@ size_t conv_workspace(const gdn_desc *d, const gdn::Shape &sh, bool use_mfma, in
   const size_t ys = dsize(d->qkv_dtype);
   const size_t nqk = (size_t)d->B * d->T * d->Hk * d->dk, nv = (size_t)d->B * d->T * d->Hv * d->dv;
   return 2 * round256(nqk * ys) + round256(nv * ys) + (use_mfma ? gdn::chunk_mfma_workspace(sh) : 0);
+}
+
+// The prologue and the chunked forward after validation (the workspace holds
+// conv_workspace(d, sh, use_mfma, x_dtype) bytes).
+gdn_status run_chunked_conv(const gdn_desc *d, const gdn::Shape &sh, bool use_mfma, int32_t x_dtype,
+                            const void *xq, const void *xk, const void *xv, const float *conv_w,
+                            float eps, const void *g, const void *beta, const float *S0, float *o,
+                            float *S_T, void *workspace, hipStream_t s) {
+  if (conv_fused(d, sh, use_mfma, x_dtype))
+    return launched(gdn::launch_chunk_mfma_conv(sh, xq, xk, xv, conv_w, eps, g, beta, S0, o, S_T,
+                                                workspace, s),
+                    "chunked forward with convolution launch");
+  // the prologue into the workspace, then the chunked forward
+  const size_t nqk = (size_t)d->B * d->T * d->Hk * d->dk, nv = (size_t)d->B * d->T * d->Hv * d->dv;
+  const size_t ys = dsize(d->qkv_dtype);
+  char *q = (char *)workspace, *k = q + round256(nqk * ys), *v = k + round256(nqk * ys);
+  char *rest = v + round256(nv * ys);
+  hipError_t e = gdn::launch_prologue(xq, xk, xv, (gdn::DType)x_dtype, conv_w, q, k, v, sh.qkv, d->B,
+                                      d->T, d->Hk, d->Hv, d->dk, d->dv, eps, s);
+  if (e != hipSuccess) return launched(e, "prologue launch");
+  e = use_mfma ? gdn::launch_chunk_mfma(sh, q, k, v, g, beta, S0, o, S_T, rest, s)
+               : gdn::launch_chunk_f32(sh, q, k, v, g, beta, S0, o, S_T, s);
+  return launched(e, "chunked forward launch");
+}
+
+// The gated output norm inside the sequential pass: the prologue runs inside
+// the chunked kernels, a workgroup holds a whole value head and y is 16-bit.
+bool gate_inside(const gdn_desc *d, const gdn::Shape &sh, bool use_mfma, int32_t x_dtype,
+                 int32_t y_dtype) {
+  return conv_fused(d, sh, use_mfma, x_dtype) && gdn::chunk_mfma_gate_inside(sh) && y_dtype != GDN_F32;
+}
+
+size_t gated_workspace(const gdn_desc *d, const gdn::Shape &sh, bool use_mfma, int32_t x_dtype,
+                       int32_t y_dtype) {
+  if (gate_inside(d, sh, use_mfma, x_dtype, y_dtype)) return gdn::chunk_mfma_conv_workspace(sh);
+  return round256(conv_workspace(d, sh, use_mfma, x_dtype)) +
+         (size_t)d->B * d->T * d->Hv * d->dv * 4;   // then o
+}
+
+// Everything the gate checks about its sizes, dtypes and eps.
+gdn_status check_gate_args(const gdn_desc *d, int32_t z_dtype, int32_t y_dtype, float eps) {
+  if (!is_dtype(z_dtype) || !is_dtype(y_dtype))
+    return fail(GDN_E_ARG, "unknown dtype (z %d, y %d)", z_dtype, y_dtype);
+  if (!pow2_16_128(d->dv))
+    return fail(GDN_E_UNSUPPORTED, "the output gate supports dv in {16,32,64,128} (got %d)", d->dv);
+  if (!(eps >= 0.f) || eps > 1.f) return fail(GDN_E_ARG, "norm eps must be in [0, 1]");
+  return GDN_OK;
 }
 
 }  // namespace
@@ -339,21 +388,83 @@ gdn_status gdn_fwd_chunked_conv(const gdn_desc *d, int32_t x_dtype, const void *
                             sh.key_gate)) != GDN_OK)
     return st;
 
+  return run_chunked_conv(d, sh, use_mfma, x_dtype, xq, xk, xv, conv_w, eps, g, beta, S0, o, S_T,
+                          workspace, (hipStream_t)stream);
+}
+
+gdn_status gdn_output_gate(const gdn_desc *d, const float *o, int32_t z_dtype, const void *z,
+                           const float *gain, float eps, int32_t y_dtype, void *y, void *stream) {
+  gdn::Shape sh;
+  gdn_status st = check_desc(d, &sh);
+  if (st != GDN_OK) return st;
+  if ((st = check_gate_args(d, z_dtype, y_dtype, eps)) != GDN_OK) return st;
+  const char *names[] = {"o", "z", "gain", "y"};
+  const void *ptrs[] = {o, z, gain, y};
+  if ((st = check_ptrs(names, ptrs, 4)) != GDN_OK) return st;
+  const size_t n = (size_t)d->B * d->T * d->Hv * d->dv;
+  const Range ry = range(y, n * dsize(y_dtype));
+  if (overlap(ry, range(o, n * 4)) || overlap(ry, range(z, n * dsize(z_dtype))) ||
+      overlap(ry, range(gain, (size_t)d->dv * 4)))
+    return fail(GDN_E_ARG, "y must not overlap o, z or gain");
+  return launched(gdn::launch_output_gate(o, z, (gdn::DType)z_dtype, gain, eps, y, (gdn::DType)y_dtype,
+                                          (long)d->B * d->T * d->Hv, d->dv, (hipStream_t)stream),
+                  "output gate launch");
+}
+
+size_t gdn_fwd_gated_workspace_bytes(const gdn_desc *d, int32_t x_dtype, int32_t y_dtype) {
+  gdn::Shape sh;
+  bool use_mfma = false;
+  const std::string saved = g_last_error;  // a query does not change the last error
+  gdn_status st = check_chunked(d, &sh, &use_mfma);
+  if (st == GDN_OK) st = check_prologue_args(d, x_dtype, 0.f);
+  if (st == GDN_OK) st = check_gate_args(d, x_dtype, y_dtype, 0.f);
+  g_last_error = saved;
+  if (st != GDN_OK) return 0;
+  return gated_workspace(d, sh, use_mfma, x_dtype, y_dtype);
+}
+
+gdn_status gdn_fwd_chunked_conv_gated(const gdn_desc *d, int32_t x_dtype, const void *xq,
+                                      const void *xk, const void *xv, const float *conv_w, float eps,
+                                      const void *g, const void *beta, const float *S0,
+                                      const void *z, const float *gain, float norm_eps,
+                                      int32_t y_dtype, void *y, float *S_T, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+  gdn::Shape sh;
+  bool use_mfma = false;
+  gdn_status st = check_chunked(d, &sh, &use_mfma);
+  if (st != GDN_OK) return st;
+  if ((st = check_prologue_args(d, x_dtype, eps)) != GDN_OK) return st;
+  if ((st = check_gate_args(d, x_dtype, y_dtype, norm_eps)) != GDN_OK) return st;
+  const char *names[] = {"xq", "xk", "xv", "conv_w", "z", "gain"};
+  const void *ptrs[] = {xq, xk, xv, conv_w, z, gain};
+  if ((st = check_ptrs(names, ptrs, 6)) != GDN_OK) return st;
+  const size_t nqk = (size_t)d->B * d->T * d->Hk * d->dk, nv = (size_t)d->B * d->T * d->Hv * d->dv;
+  const size_t xs = dsize(x_dtype);
+  const Range ins[] = {range(xq, nqk * xs), range(xk, nqk * xs), range(xv, nv * xs),
+                       range(conv_w, (2 * (size_t)d->Hk * d->dk + (size_t)d->Hv * d->dv) * 16),
+                       range(z, nv * xs), range(gain, (size_t)d->dv * 4)};
+  const size_t y_bytes = nv * dsize(y_dtype);
+  if ((st = check_chunked_ptrs(d, sh, ins, 6, g, beta, S0, y, S_T, y_bytes)) != GDN_OK) return st;
+  const size_t need = gated_workspace(d, sh, use_mfma, x_dtype, y_dtype);
+  if ((st = check_workspace(d, workspace, workspace_bytes, need, ins, 6, g, beta, S0, y, S_T,
+                            sh.key_gate, y_bytes)) != GDN_OK)
+    return st;
+
   hipStream_t s = (hipStream_t)stream;
-  if (conv_fused(d, sh, use_mfma, x_dtype))
-    return launched(gdn::launch_chunk_mfma_conv(sh, xq, xk, xv, conv_w, eps, g, beta, S0, o, S_T,
-                                                workspace, s),
-                    "chunked forward with convolution launch");
-  // the prologue into the workspace, then the chunked forward
-  const size_t ys = dsize(d->qkv_dtype);
-  char *q = (char *)workspace, *k = q + round256(nqk * ys), *v = k + round256(nqk * ys);
-  char *rest = v + round256(nv * ys);
-  hipError_t e = gdn::launch_prologue(xq, xk, xv, (gdn::DType)x_dtype, conv_w, q, k, v, sh.qkv, d->B,
-                                      d->T, d->Hk, d->Hv, d->dk, d->dv, eps, s);
-  if (e != hipSuccess) return launched(e, "prologue launch");
-  e = use_mfma ? gdn::launch_chunk_mfma(sh, q, k, v, g, beta, S0, o, S_T, rest, s)
-               : gdn::launch_chunk_f32(sh, q, k, v, g, beta, S0, o, S_T, s);
-  return launched(e, "chunked forward launch");
+  if (gate_inside(d, sh, use_mfma, x_dtype, y_dtype)) {
+    const gdn::GateArgs ga{z, gain, norm_eps, y, (gdn::DType)y_dtype};
+    return launched(gdn::launch_chunk_mfma_conv(sh, xq, xk, xv, conv_w, eps, g, beta, S0, nullptr, S_T,
+                                                workspace, s, &ga),
+                    "gated chunked forward launch");
+  }
+  // o into the workspace after what the forward uses, then the gate
+  float *o = (float *)((char *)workspace + round256(conv_workspace(d, sh, use_mfma, x_dtype)));
+  if ((st = run_chunked_conv(d, sh, use_mfma, x_dtype, xq, xk, xv, conv_w, eps, g, beta, S0, o, S_T,
+                             workspace, s)) != GDN_OK)
+    return st;
+  return launched(gdn::launch_output_gate(o, z, (gdn::DType)x_dtype, gain, norm_eps, y,
+                                          (gdn::DType)y_dtype, (long)d->B * d->T * d->Hv, d->dv, s),
+                  "output gate launch");
 }
 
 gdn_status gdn_decode_step(const gdn_desc *d, const void *q, const void *k, const void *v,

@@ -1,6 +1,7 @@
 // gdn_device.h -- device helpers shared by the gfx950 kernels: storage types,
-// exact widening to fp32, round-to-nearest-even narrowing, 16-byte vector
-// loads, and wave-level sums over aligned lane groups.
+// exact widening to fp32, round-to-nearest-even narrowing, vector loads and
+// stores, wave-level sums over aligned lane groups, and the arithmetic of the
+// convolution and of the gated output norm.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -149,6 +150,77 @@ __device__ __forceinline__ void l2_scale8(float (&z)[8], float ss, float eps) {
   const float inv = rsqrtf(ss + eps);
 #pragma unroll
   for (int c = 0; c < 8; ++c) z[c] = fp32_value(z[c] * inv);
+}
+
+// The gated output norm y = o / sqrt(mean(o^2) + eps) * gain * z sigmoid(z)
+// over a row of DV channels, in the steps every kernel that applies it
+// shares, so that they all round identically:
+//  - gate_sumsq8: the sum of squares of 8 of the row's values, in a fixed
+//    order (the caller combines such partial sums over lanes and waves in a
+//    fixed tree);
+//  - gate_inv_rms: 1 / sqrt(sum / DV + eps) from the row's sum of squares;
+//  - gate_apply: ((o * inv) * gain) * silu(z), as an fp32 value.
+__device__ __forceinline__ float gate_sumsq8(const float (&x)[8]) {
+  float s = x[0] * x[0];
+#pragma unroll
+  for (int c = 1; c < 8; ++c) s = __builtin_fmaf(x[c], x[c], s);
+  return s;
+}
+template <int DV> __device__ __forceinline__ float gate_inv_rms(float ss, float eps) {
+  return rsqrtf(fp32_value(__builtin_fmaf(ss, 1.0f / DV, eps)));
+}
+__device__ __forceinline__ float gate_apply(float o, float inv, float gain, float z) {
+  const float s = fp32_value(z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)));   // SiLU
+  return fp32_value(fp32_value(fp32_value(o * inv) * gain) * s);
+}
+
+// Narrow 4 fp32 values and store them (16-byte aligned for fp32, 8-byte for
+// 2-byte types).
+__device__ __forceinline__ void store4(float *p, const float (&x)[4]) {
+  *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void store4(f16_t *p, const float (&x)[4]) {
+  half4 h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) h[i] = (f16_t)x[i];
+  *reinterpret_cast<half4 *>(p) = h;
+}
+__device__ __forceinline__ void store4(bf16_t *p, const float (&x)[4]) {
+  uint32_t w[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    w[i] = (uint32_t)from_f32<bf16_t>(x[2 * i]).bits |
+           ((uint32_t)from_f32<bf16_t>(x[2 * i + 1]).bits << 16);
+  *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
+}
+
+// 4 fp32 values as 4 bf16 or fp16 (round to nearest even) in 8 bytes.
+__device__ __forceinline__ uint2 pack4_bf16(const float (&x)[4]) {
+  return make_uint2((uint32_t)from_f32<bf16_t>(x[0]).bits | ((uint32_t)from_f32<bf16_t>(x[1]).bits << 16),
+                    (uint32_t)from_f32<bf16_t>(x[2]).bits | ((uint32_t)from_f32<bf16_t>(x[3]).bits << 16));
+}
+__device__ __forceinline__ uint2 pack4_f16(const float (&x)[4]) {
+  const half4 h = {(f16_t)x[0], (f16_t)x[1], (f16_t)x[2], (f16_t)x[3]};
+  return __builtin_bit_cast(uint2, h);
+}
+
+// Load 4 consecutive elements (8-byte aligned for 2-byte types, 16-byte for
+// fp32) and widen to fp32.
+__device__ __forceinline__ void load4(const float *p, float (&x)[4]) {
+  const float4 a = *reinterpret_cast<const float4 *>(p);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+}
+__device__ __forceinline__ void load4(const f16_t *p, float (&x)[4]) {
+  const half4 h = *reinterpret_cast<const half4 *>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = (float)h[i];
+}
+__device__ __forceinline__ void load4(const bf16_t *p, float (&x)[4]) {
+  const uint2 u = *reinterpret_cast<const uint2 *>(p);
+  x[0] = __uint_as_float(u.x << 16);
+  x[1] = __uint_as_float(u.x & 0xFFFF0000u);
+  x[2] = __uint_as_float(u.y << 16);
+  x[3] = __uint_as_float(u.y & 0xFFFF0000u);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave by DPP moves: shifts by

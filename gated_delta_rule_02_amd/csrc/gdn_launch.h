@@ -16,6 +16,18 @@ struct Shape {
   bool key_gate;
 };
 
+// The gate's arguments for the chunked forward with the prologue inside,
+// which applies it inside the sequential pass when chunk_mfma_gate_inside(sh)
+// and y is 16-bit (z is bf16, like the raw inputs).
+struct GateArgs {
+  const void *z;
+  const float *gain;
+  float eps;
+  void *y;
+  DType yt;
+};
+bool chunk_mfma_gate_inside(const Shape &sh);
+
 // Prologue: conv + SiLU over q, k, v (L2 over q and k rows); w holds the
 // conv taps of q, then k, then v channels.
 hipError_t launch_prologue(const void *xq, const void *xk, const void *xv, DType xt, const float *w,
@@ -41,10 +53,18 @@ size_t chunk_mfma_workspace(const Shape &sh);
 // The same with the convolution prologue inside (bf16 raw inputs, head
 // gate): equal to launch_prologue into q, k, v of sh.qkv followed by
 // launch_chunk_mfma.  `ws` holds chunk_mfma_conv_workspace(sh) bytes.
+// With `gate` (only where chunk_mfma_gate_inside(sh)), the gated output
+// norm is applied in the sequential pass and y written instead of o.
 hipError_t launch_chunk_mfma_conv(const Shape &sh, const void *xq, const void *xk, const void *xv,
                                   const float *conv_w, float eps, const void *g, const void *beta,
-                                  const float *S0, float *o, float *ST, void *ws, hipStream_t s);
+                                  const float *S0, float *o, float *ST, void *ws, hipStream_t s,
+                                  const GateArgs *gate = nullptr);
 size_t chunk_mfma_conv_workspace(const Shape &sh);
+
+// The gated output norm over `rows` rows of dv channels: o fp32 -> y of yt,
+// z of zt (same layout as o), gain fp32 [dv].  dv in {16, 32, 64, 128}.
+hipError_t launch_output_gate(const float *o, const void *z, DType zt, const float *gain, float eps,
+                              void *y, DType yt, long rows, int dv, hipStream_t s);
 
 // Internal chunk length the fp32 kernels use for a requested chunk and dk.
 int chunk_f32_internal(int chunk, int dk);

@@ -9,7 +9,8 @@ exactly to float32, to the oracle.
 
 Seeds: every tensor has its own stream,
 ``numpy.random.Generator(PCG64(SeedSequence([workload_seed, *extra, stream])))``
-with streams q=0, k=1, v=2, beta=3, g=4, conv_w=5, S0=6, in that order.
+with streams q=0, k=1, v=2, beta=3, g=4, conv_w=5, S0=6, in that order, and
+z=7, gain=8 for the output gate that follows the forward pass.
 Normals are drawn in float64 for small tensors and in float32 for tensors of
 10**7 elements or more (then widened for the transforms).
 """
@@ -20,7 +21,7 @@ from typing import Optional
 
 import numpy as np
 
-STREAM = {"q": 0, "k": 1, "v": 2, "beta": 3, "g": 4, "conv_w": 5, "S0": 6}
+STREAM = {"q": 0, "k": 1, "v": 2, "beta": 3, "g": 4, "conv_w": 5, "S0": 6, "z": 7, "gain": 8}
 BIG = 10 ** 7
 
 
@@ -175,6 +176,16 @@ def make_state(wl: Workload) -> Optional[np.ndarray]:
         return None
     return np.ascontiguousarray(normal(rng(wl.seed, "S0"), (wl.B, wl.Hv, wl.dv, wl.dk), std=wl.s0_std),
                                 dtype=np.float32)
+
+
+def make_gate_inputs(wl: Workload) -> dict:
+    """Inputs of the gated output norm after the forward pass: the gate
+    z ~ N(0,1) [B,T,Hv,dv] in the workload dtype (like the raw projections),
+    and one gain vector 1 + N(0, 0.1) [dv] float32 (a learned gain near its
+    initial value of one), plus the norm's eps = 1e-5."""
+    z = store(normal(rng(wl.seed, "z"), (wl.B, wl.T, wl.Hv, wl.dv)), wl.dtype)
+    gain = np.ascontiguousarray(1.0 + normal(rng(wl.seed, "gain"), (wl.dv,), std=0.1), dtype=np.float32)
+    return {"z": z, "gain": gain, "norm_eps": 1e-5}
 
 
 def make_decode_token(wl: Workload, step: int) -> dict:

@@ -183,6 +183,58 @@ gdn_status gdn_fwd_chunked_conv(const gdn_desc *d, int32_t x_dtype, const void *
                                 size_t workspace_bytes, void *stream);
 
 /*
+ * gdn_output_gate -- the gated output norm that follows the state read in a
+ * Gated DeltaNet layer ("Source notes", Linear attention, row gdn: the
+ * read-out is RMS-normalised, scaled by a learned gain and multiplied by a
+ * SiLU gate; "Adopt vs. port", entry burn-rmsnorm, for the RMS norm: divide
+ * by the square root of the mean of squares plus eps, multiply by the gain).
+ * For every (batch, token, value head) row of dv channels:
+ *     y_c = o_c / sqrt((1/dv) sum_c' o_c'^2 + eps) * gain_c * z_c sigmoid(z_c)
+ *
+ *   o      device fp32 [B,T,Hv,dv] (as gdn_fwd_chunked writes it)
+ *   z      device [B,T,Hv,dv] z_dtype (GDN_F32, GDN_BF16 or GDN_F16): the gate
+ *   gain   device fp32 [dv], the same for every value head
+ *   eps    in [0, 1]
+ *   y      device out [B,T,Hv,dv] y_dtype (GDN_F32, GDN_BF16 or GDN_F16),
+ *          rounded to nearest even; must not overlap o, z or gain
+ * d->Hk, dk, chunk, the dtypes and the gate kind must form a valid
+ * description but are not used.  Supported: dv in {16, 32, 64, 128}.
+ */
+gdn_status gdn_output_gate(const gdn_desc *d, const float *o, int32_t z_dtype,
+                           const void *z, const float *gain, float eps,
+                           int32_t y_dtype, void *y, void *stream);
+
+/*
+ * gdn_fwd_chunked_conv_gated -- gdn_fwd_chunked_conv followed by
+ * gdn_output_gate, without o as an argument: the same results (the same
+ * arithmetic, roundings and order of the row sums) as
+ *     gdn_fwd_chunked_conv(d, x_dtype, xq, xk, xv, conv_w, eps, g, beta, S0, o, S_T)
+ *     gdn_output_gate(d, o, x_dtype, z, gain, norm_eps, y_dtype, y).
+ * When the convolution runs inside the chunked kernels (bf16 raw inputs,
+ * matrix-core path, per-head gate), B * Hv > 128 (a workgroup of the
+ * sequential pass then holds a whole value head) and y is 16-bit, the gate
+ * is applied there and o never goes through memory; otherwise o is kept in
+ * the workspace and the gate runs after the forward.
+ *
+ *   x_dtype, xq, xk, xv, conv_w, eps   as for gdn_fwd_chunked_conv
+ *   g, beta, S0, S_T                   as for gdn_fwd_chunked
+ *   z      device [B,T,Hv,dv] x_dtype (the gate, like the raw projections)
+ *   gain, norm_eps, y_dtype, y         as gain, eps, y_dtype, y of gdn_output_gate;
+ *          y must not overlap any other argument
+ *   workspace   device scratch of at least gdn_fwd_gated_workspace_bytes(d,
+ *               x_dtype, y_dtype) bytes, 16-byte aligned, not overlapping any other
+ *               argument (GDN_E_WORKSPACE if too small)
+ * Supported: what gdn_fwd_chunked_conv and gdn_output_gate support for d.
+ */
+size_t gdn_fwd_gated_workspace_bytes(const gdn_desc *d, int32_t x_dtype, int32_t y_dtype);
+gdn_status gdn_fwd_chunked_conv_gated(const gdn_desc *d, int32_t x_dtype, const void *xq,
+                                      const void *xk, const void *xv, const float *conv_w,
+                                      float eps, const void *g, const void *beta,
+                                      const float *S0, const void *z, const float *gain,
+                                      float norm_eps, int32_t y_dtype, void *y, float *S_T,
+                                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * gdn_decode_step -- one token per sequence: the recurrence above with T = 1,
  * the state updated in place.  For state row i (old values S_i, decayed
  * row D_i = alpha S_i, or S_i o alpha for the key-channel gate):

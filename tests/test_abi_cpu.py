@@ -168,3 +168,76 @@ def test_conv_rejects_before_launch(L):
     bad[0] = P(FAKE + 8)
     assert call(d, gdn.BF16, bad) == 4                   # misaligned xq
     assert call(desc(Hv=5), gdn.BF16, p) == 2
+
+
+def test_gated_workspace_query(L):
+    r = lambda x: (x + 255) // 256 * 256
+    # B * Hv = 12 <= 128: the gate runs after the forward, o kept in the workspace
+    d = desc()
+    conv = L.gdn_fwd_conv_workspace_bytes(ctypes.byref(d), gdn.BF16)
+    o_bytes = d.B * d.T * d.Hv * 128 * 4
+    assert L.gdn_fwd_gated_workspace_bytes(ctypes.byref(d), gdn.BF16, gdn.BF16) == r(conv) + o_bytes
+    # B * Hv = 192 > 128 with bf16 raw inputs and 16-bit y: the gate runs
+    # inside the sequential pass
+    d = desc(B=4, Hk=16, Hv=48)
+    inside = L.gdn_fwd_conv_workspace_bytes(ctypes.byref(d), gdn.BF16)
+    assert L.gdn_fwd_gated_workspace_bytes(ctypes.byref(d), gdn.BF16, gdn.BF16) == inside
+    assert L.gdn_fwd_gated_workspace_bytes(ctypes.byref(d), gdn.BF16, gdn.F16) == inside
+    o_bytes = d.B * d.T * d.Hv * 128 * 4
+    assert L.gdn_fwd_gated_workspace_bytes(ctypes.byref(d), gdn.BF16, gdn.F32) == r(inside) + o_bytes
+    # fp32 raw inputs never take the fused form
+    conv = L.gdn_fwd_conv_workspace_bytes(ctypes.byref(d), gdn.F32)
+    assert L.gdn_fwd_gated_workspace_bytes(ctypes.byref(d), gdn.F32, gdn.BF16) == r(conv) + o_bytes
+    assert L.gdn_fwd_gated_workspace_bytes(ctypes.byref(desc(Hv=5)), gdn.BF16, gdn.BF16) == 0
+    assert L.gdn_fwd_gated_workspace_bytes(ctypes.byref(d), gdn.BF16, 9) == 0
+    assert L.gdn_fwd_gated_workspace_bytes(ctypes.byref(desc(gate=gdn.GATE_KEY_CHANNEL, dk=64, dv=48,
+                                                             qkv_dtype=gdn.F32, gate_dtype=gdn.F32,
+                                                             chunk=16)), gdn.F32, gdn.F32) == 0   # dv 48
+
+
+def test_output_gate_rejects(L):
+    P = ctypes.c_void_p
+    p = [P(FAKE + i * (1 << 32)) for i in range(4)]      # o, z, gain, y
+    call = lambda dd, ptrs, zt=gdn.BF16, yt=gdn.BF16, eps=1e-5: L.gdn_output_gate(
+        ctypes.byref(dd), ptrs[0], zt, ptrs[1], ptrs[2], eps, yt, ptrs[3], None)
+    assert call(desc(dv=48), p) == 3                     # dv not in {16, 32, 64, 128}
+    assert call(desc(), p, zt=5) == 1
+    assert call(desc(), p, yt=-1) == 1
+    assert call(desc(), p, eps=-1.0) == 1
+    assert call(desc(), p, eps=float("nan")) == 1
+    assert call(desc(Hv=5), p) == 2
+    for i in range(4):
+        bad = list(p)
+        bad[i] = None
+        assert call(desc(), bad) == 1
+        bad[i] = P(p[i].value + 8)
+        assert call(desc(), bad) == 4
+    bad = list(p)
+    bad[3] = P(p[0].value + 4096)                        # y written over o
+    assert call(desc(), bad) == 1
+    assert L.gdn_last_error()
+
+
+def test_gated_rejects_before_launch(L):
+    d = desc(B=4, Hk=16, Hv=48)
+    need = L.gdn_fwd_gated_workspace_bytes(ctypes.byref(d), gdn.BF16, gdn.BF16)
+    P = ctypes.c_void_p
+    p = [P(FAKE + i * (1 << 36)) for i in range(11)]
+    # xq, xk, xv, conv_w | g, beta | z, gain | y, S_T | workspace
+    call = lambda dd, ptrs, xt=gdn.BF16, yt=gdn.BF16, neps=1e-5, ws=p[10], nbytes=need: \
+        L.gdn_fwd_chunked_conv_gated(ctypes.byref(dd), xt, *ptrs[:4], 1e-6, *ptrs[4:6], None,
+                                     *ptrs[6:8], neps, yt, *ptrs[8:10], ws, nbytes, None)
+    assert call(d, p, xt=gdn.F16) == 3                   # raw fp16
+    assert call(d, p, yt=4) == 1
+    assert call(d, p, neps=2.0) == 1
+    assert call(d, p, nbytes=need - 16) == 5
+    assert call(d, p, ws=None) == 1
+    for i, code in ((6, 1), (7, 1)):                     # z, gain missing
+        bad = list(p)
+        bad[i] = None
+        assert call(d, bad) == code
+    bad = list(p)
+    bad[8] = P(p[6].value + 256)                         # y written over z
+    assert call(d, bad) == 1
+    assert call(d, p, ws=P(p[8].value + 256)) == 1      # workspace over y
+    assert call(desc(B=4, Hk=16, Hv=48, dv=64), p) == 3  # matrix-core mode needs dv 128
