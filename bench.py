@@ -20,6 +20,10 @@ kernels run on):
   workloads     the chunked forward on the long-prefill workload (B 1, T 65536,
                 S0 given, slow decay) and on the per-key-channel-gate workload
                 (B 2, 32 heads, T 8192), tokens/s and fractions of both roofs;
+                and the step's prefill followed by the gated output norm (RMS
+                norm x gain x SiLU gate, bf16 out): inside the sequential pass
+                (gdn_fwd_chunked_conv_gated) against the forward followed by
+                gdn_output_gate;
   cpu_baseline  the fp64 oracle on the host cores on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -132,7 +136,7 @@ def main():
 
     import gated_delta_rule_02_amd as gdn
     from gdn_inputs import BATCHED_DECODE, KDA_PREFILL, LONG_PREFILL, PREFILL_CONV, decode_tokens_device, \
-        make_decode_token, make_prefill, make_state, prefill_device, to_torch
+        make_decode_token, make_gate_inputs, make_prefill, make_state, prefill_device, to_torch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
@@ -277,6 +281,43 @@ def main():
         "us_per_call": (t_pro + t_chk) * 1e6, "tokens_per_s": B * T / (t_pro + t_chk),
         "prologue_us": t_pro * 1e6, "chunked_us": t_chk * 1e6,
         "chunked_mfma_frac": flops_chk / t_chk / 1e12 / PEAK_F16_TFLOPS}}
+    # the gated output norm after the step's prefill: inside the sequential
+    # pass, and as the forward followed by the standalone gate
+    log("workload: %s, then the gated output norm" % wl.name)
+    gi = make_gate_inputs(wl)
+    z, gain = to_torch(gi["z"], dev), to_torch(gi["gain"], dev)
+    y = torch.empty((B, T, Hv, dv), dtype=torch.bfloat16, device=dev)
+    gws = torch.empty(L.gdn_fwd_gated_workspace_bytes(desc, gdn.BF16, gdn.BF16), dtype=torch.uint8, device=dev)
+    neps = gi["norm_eps"]
+
+    def gated():
+        gdn.check(L.gdn_fwd_chunked_conv_gated(ctypes.byref(desc), gdn.BF16, P(xq), P(xk), P(xv), P(w), 1e-6,
+                                               P(g), P(beta), None, P(z), P(gain), neps, gdn.BF16, P(y),
+                                               P(ST), P(gws), gws.numel(), s_ptr))
+
+    def gate_alone():
+        gdn.check(L.gdn_output_gate(ctypes.byref(desc), P(o), gdn.BF16, P(z), P(gain), neps, gdn.BF16, P(y),
+                                    s_ptr))
+
+    warm_up(gated)
+    t_gated = time_events(gated, 20, stream)
+    warm_up(gate_alone)
+    t_gate = time_events(gate_alone, 20, stream)
+    bytes_gate = B * T * Hv * dv * (4 + 2 + 2) + dv * 4
+    # the forward's algorithmic bytes with y (bf16) read as z and written in place of o (fp32)
+    bytes_gated = bytes_fus - B * T * Hv * dv * 4 + B * T * Hv * dv * (2 + 2) + dv * 4
+    extra["prefill_conv_gated"] = {
+        "workload": wl.name + ", then y = RMSNorm(o) * gain * SiLU(z), bf16 y",
+        "us_per_call": t_gated * 1e6, "tokens_per_s": B * T / t_gated,
+        "mfma_frac": flops_chk / t_gated / 1e12 / PEAK_F16_TFLOPS,
+        "hbm_frac_algorithmic": bytes_gated / t_gated / 1e9 / PEAK_HBM_GBS,
+        "two_calls_us": (t_fus + t_gate) * 1e6, "gate_alone_us": t_gate * 1e6,
+        "gate_alone_hbm_gbs": bytes_gate / t_gate / 1e9,
+        "gate_alone_hbm_frac": bytes_gate / t_gate / 1e9 / PEAK_HBM_GBS}
+    log("gated: %.1f us inside the pass; forward + gate %.1f + %.1f us (gate %.0f GB/s)" %
+        (t_gated * 1e6, t_fus * 1e6, t_gate * 1e6, bytes_gate / t_gate / 1e9))
+    del z, gain, y, gws
+
     for key, xwl in (("long_prefill", LONG_PREFILL), ("key_gate_prefill", KDA_PREFILL)):
         log("workload: %s" % xwl.name)
         xi = prefill_device(xwl, dev)

@@ -29,11 +29,9 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ f16_t from_f32<f16_t>(float x) { return (f16_t)x; }
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
-  // round to nearest even (inputs are finite)
-  uint32_t u = __float_as_uint(x);
-  u += 0x7FFFu + ((u >> 16) & 1u);
+  // round to nearest even (the gfx950 conversion instruction)
   bf16_t r;
-  r.bits = (uint16_t)(u >> 16);
+  r.bits = __builtin_bit_cast(uint16_t, (__bf16)x);
   return r;
 }
 
