@@ -13,6 +13,8 @@ Entry points (same names as the C functions):
   fwd_chunked_conv(xq, xk, xv, conv_w, g, beta, S0, qkv_dtype, eps, chunk) -> (o, S_T)
   decode_step(q, k, v, g, beta, S) -> o          (S updated in place)
   output_gate(o, z, gain, eps, out_dtype) -> y
+  prologue_varlen, fwd_chunked_varlen, fwd_chunked_conv_varlen: packed sequences
+      of different lengths (token tensors [1,T,...], cu_seqlens int32 [N+1])
   fwd_chunked_conv_gated(xq, xk, xv, conv_w, g, beta, z, gain, S0, ...) -> (y, S_T)
 """
 from __future__ import annotations
@@ -69,6 +71,16 @@ def lib() -> ctypes.CDLL:
         L.gdn_fwd_conv_workspace_bytes.restype = S
         L.gdn_fwd_chunked_conv.argtypes = [D, I, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, S, P]
         L.gdn_fwd_chunked_conv.restype = I
+        L.gdn_prologue_varlen.argtypes = [D, P, I, P, P, P, P, ctypes.c_float, P, P, P, P]
+        L.gdn_prologue_varlen.restype = I
+        L.gdn_fwd_varlen_workspace_bytes.argtypes = [D]
+        L.gdn_fwd_varlen_workspace_bytes.restype = S
+        L.gdn_fwd_chunked_varlen.argtypes = [D, P, P, P, P, P, P, P, P, P, P, S, P]
+        L.gdn_fwd_chunked_varlen.restype = I
+        L.gdn_fwd_conv_varlen_workspace_bytes.argtypes = [D, I]
+        L.gdn_fwd_conv_varlen_workspace_bytes.restype = S
+        L.gdn_fwd_chunked_conv_varlen.argtypes = [D, P, I, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, S, P]
+        L.gdn_fwd_chunked_conv_varlen.restype = I
         L.gdn_output_gate.argtypes = [D, P, I, P, P, ctypes.c_float, I, P, P]
         L.gdn_output_gate.restype = I
         L.gdn_fwd_gated_workspace_bytes.argtypes = [D, I, I]
@@ -263,6 +275,94 @@ def fwd_chunked_conv_gated(xq, xk, xv, conv_w, g, beta, z, gain, S0=None, qkv_dt
                                        float(norm_eps), _DTYPE_CODE[y.dtype], _ptr(y), _ptr(S_T),
                                        _ptr(ws), ws_bytes, _stream(stream)))
     return y, S_T
+
+
+def _offsets(cu_seqlens, T):
+    _dev("cu_seqlens", cu_seqlens, None, (torch.int32,))
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be int32 [N+1] with N >= 1")
+    return cu_seqlens.numel() - 1
+
+
+def prologue_varlen(xq, xk, xv, conv_w, cu_seqlens, out_dtype=torch.float16, eps=1e-6, stream=None):
+    """prologue over packed sequences: xq, xk [1,T,Hk,dk], xv [1,T,Hv,dv];
+    the convolution history is zero before each sequence's first token."""
+    _, T, Hk, dk = xq.shape
+    Hv, dv = xv.shape[2], xv.shape[3]
+    N = _offsets(cu_seqlens, T)
+    _dev("xq", xq, (1, T, Hk, dk))
+    _dev("xk", xk, (1, T, Hk, dk), (xq.dtype,))
+    _dev("xv", xv, (1, T, Hv, dv), (xq.dtype,))
+    _dev("conv_w", conv_w, (2 * Hk * dk + Hv * dv, 4), (torch.float32,))
+    q = torch.empty((1, T, Hk, dk), dtype=out_dtype, device=xq.device)
+    k = torch.empty_like(q)
+    v = torch.empty((1, T, Hv, dv), dtype=out_dtype, device=xq.device)
+    d = make_desc(N, T, Hk, Hv, dk, dv, 64, _DTYPE_CODE[out_dtype], F32, GATE_HEAD)
+    check(lib().gdn_prologue_varlen(ctypes.byref(d), _ptr(cu_seqlens), _DTYPE_CODE[xq.dtype], _ptr(xq),
+                                    _ptr(xk), _ptr(xv), _ptr(conv_w), float(eps), _ptr(q), _ptr(k), _ptr(v),
+                                    _stream(stream)))
+    return q, k, v
+
+
+def fwd_chunked_varlen(q, k, v, g, beta, cu_seqlens, S0=None, chunk=64, o=None, S_T=None, stream=None):
+    """fwd_chunked over packed sequences: q, k [1,T,Hk,dk]; v [1,T,Hv,dv];
+    g [1,T,Hv] or [1,T,Hv,dk]; beta [1,T,Hv]; cu_seqlens int32 [N+1];
+    S0 fp32 [N,Hv,dv,dk] or None.  Returns (o [1,T,Hv,dv], S_T [N,Hv,dv,dk])."""
+    _, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    N = _offsets(cu_seqlens, T)
+    _dev("q", q, (1, T, Hk, dk))
+    _dev("k", k, q.shape, (q.dtype,))
+    _dev("v", v, (1, T, Hv, dv), (q.dtype,))
+    gate = _gate_kind(_dev("g", g), 1, T, Hv, dk)
+    _dev("beta", beta, (1, T, Hv), (g.dtype,))
+    if S0 is not None:
+        _dev("S0", S0, (N, Hv, dv, dk), (torch.float32,))
+    if o is None:
+        o = torch.empty((1, T, Hv, dv), dtype=torch.float32, device=q.device)
+    if S_T is None:
+        S_T = torch.empty((N, Hv, dv, dk), dtype=torch.float32, device=q.device)
+    _dev("o", o, (1, T, Hv, dv), (torch.float32,))
+    _dev("S_T", S_T, (N, Hv, dv, dk), (torch.float32,))
+    d = make_desc(N, T, Hk, Hv, dk, dv, chunk, _DTYPE_CODE[q.dtype], _DTYPE_CODE[g.dtype], gate)
+    L = lib()
+    ws_bytes = L.gdn_fwd_varlen_workspace_bytes(ctypes.byref(d))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    check(L.gdn_fwd_chunked_varlen(ctypes.byref(d), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                   _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T), _ptr(ws), ws_bytes,
+                                   _stream(stream)))
+    return o, S_T
+
+
+def fwd_chunked_conv_varlen(xq, xk, xv, conv_w, g, beta, cu_seqlens, S0=None, qkv_dtype=torch.float16,
+                            eps=1e-6, chunk=64, o=None, S_T=None, stream=None):
+    """prologue_varlen then fwd_chunked_varlen in one call.  Returns (o, S_T)."""
+    _, T, Hk, dk = xq.shape
+    Hv, dv = xv.shape[2], xv.shape[3]
+    N = _offsets(cu_seqlens, T)
+    _dev("xq", xq, (1, T, Hk, dk))
+    _dev("xk", xk, (1, T, Hk, dk), (xq.dtype,))
+    _dev("xv", xv, (1, T, Hv, dv), (xq.dtype,))
+    _dev("conv_w", conv_w, (2 * Hk * dk + Hv * dv, 4), (torch.float32,))
+    gate = _gate_kind(_dev("g", g), 1, T, Hv, dk)
+    _dev("beta", beta, (1, T, Hv), (g.dtype,))
+    if S0 is not None:
+        _dev("S0", S0, (N, Hv, dv, dk), (torch.float32,))
+    if o is None:
+        o = torch.empty((1, T, Hv, dv), dtype=torch.float32, device=xq.device)
+    if S_T is None:
+        S_T = torch.empty((N, Hv, dv, dk), dtype=torch.float32, device=xq.device)
+    _dev("o", o, (1, T, Hv, dv), (torch.float32,))
+    _dev("S_T", S_T, (N, Hv, dv, dk), (torch.float32,))
+    d = make_desc(N, T, Hk, Hv, dk, dv, chunk, _DTYPE_CODE[qkv_dtype], _DTYPE_CODE[g.dtype], gate)
+    L = lib()
+    xt = _DTYPE_CODE[xq.dtype]
+    ws_bytes = L.gdn_fwd_conv_varlen_workspace_bytes(ctypes.byref(d), xt)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=xq.device) if ws_bytes else None
+    check(L.gdn_fwd_chunked_conv_varlen(ctypes.byref(d), _ptr(cu_seqlens), xt, _ptr(xq), _ptr(xk), _ptr(xv),
+                                        _ptr(conv_w), float(eps), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
+                                        _ptr(S_T), _ptr(ws), ws_bytes, _stream(stream)))
+    return o, S_T
 
 
 def decode_step(q, k, v, g, beta, S, o=None, stream=None):

@@ -50,7 +50,7 @@ template <typename TQ, typename TG, bool KEYGATE, int DK, int DVS, int C>
 __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *__restrict__ v,
     const TG *__restrict__ g, const TG *__restrict__ beta, const float *__restrict__ S0,
-    float *__restrict__ o, float *__restrict__ ST, int T, int Hk, int Hv, int dv) {
+    float *__restrict__ o, float *__restrict__ ST, int Tall, int Hk, int Hv, int dv, Seqs sq) {
   using L = F32Smem<DK, DVS, C, KEYGATE>;
   constexpr int KP = L::KP, VP = L::VP, CP = L::CP;
   extern __shared__ float smem[];
@@ -71,6 +71,8 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(
   const int b = blockIdx.z, h = blockIdx.y, i0 = blockIdx.x * DVS;
   const int kh = h / (Hv / Hk);
   const size_t bh = (size_t)b * Hv + h;
+  int start, T;   // the sequence's first token and length
+  seq_bounds(sq, b, Tall, start, T);
 
   for (int e = tid; e < DVS * DK; e += kThreads) {
     const int i = e / DK, j = e % DK;
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(
     // padded rows inert) ----
     for (int e = tid; e < C * DK; e += kThreads) {
       const int r = e / DK, j = e % DK;
-      const size_t t = (size_t)b * T + c0 + r;
+      const size_t t = (size_t)start + c0 + r;
       const bool ok = r < n;
       sK[r * KP + j] = ok ? to_f32(k[(t * Hk + kh) * DK + j]) : 0.f;
       sQ[r * KP + j] = ok ? to_f32(q[(t * Hk + kh) * DK + j]) : 0.f;
@@ -92,11 +94,11 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(
     }
     for (int e = tid; e < C * DVS; e += kThreads) {
       const int r = e / DVS, i = e % DVS;
-      const size_t t = (size_t)b * T + c0 + r;
+      const size_t t = (size_t)start + c0 + r;
       sV[r * VP + i] = r < n ? to_f32(v[(t * Hv + h) * dv + i0 + i]) : 0.f;
     }
     for (int r = tid; r < C; r += kThreads) {
-      const size_t t = (size_t)b * T + c0 + r;
+      const size_t t = (size_t)start + c0 + r;
       sBeta[r] = r < n ? to_f32(beta[t * Hv + h]) : 0.f;
       if constexpr (!KEYGATE) sGam[r] = r < n ? to_f32(g[t * Hv + h]) : 0.f;
     }
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(
       if (r < n) {
         float acc = sO[r * VP + i];
         for (int s = 0; s <= r; ++s) acc += sP[r * CP + s] * sX[s * VP + i];
-        o[(((size_t)b * T + c0 + r) * Hv + h) * dv + i0 + i] = acc;
+        o[(((size_t)start + c0 + r) * Hv + h) * dv + i0 + i] = acc;
       }
     }
     // ---- state update (reads only N, K and the decay tables) ----
@@ -220,7 +222,7 @@ hipError_t launch_cfg(const Shape &sh, const void *q, const void *k, const void 
   dim3 grid(sh.dv / DVS, sh.Hv, sh.B);
   hipLaunchKernelGGL(kern, grid, dim3(kThreads), smem, st, (const TQ *)q, (const TQ *)k,
                      (const TQ *)v, (const TG *)g, (const TG *)beta, S0, o, ST, sh.T, sh.Hk, sh.Hv,
-                     sh.dv);
+                     sh.dv, Seqs{sh.cu, sh.B});
   return hipGetLastError();
 }
 

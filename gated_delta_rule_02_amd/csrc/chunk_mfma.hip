@@ -133,6 +133,13 @@ struct ConvIn {
   float eps;
 };
 
+// Workspace index of chunk 0 of (sequence b, value head h): per (b, h) runs of
+// nchunks chunks, or, for packed sequences, per value head runs of nchunks
+// slots (the sequence's chunks from slot start / C + b).
+__device__ __forceinline__ size_t ws_chain(const Seqs &sq, int b, int h, int Hv, int nchunks, int start) {
+  return sq.cu ? (size_t)h * nchunks + start / C + b : ((size_t)b * Hv + h) * nchunks;
+}
+
 __device__ __forceinline__ int frag_index(int R, int kk) { return R < 2 ? R : 2 * R - 2 + kk; }
 
 // LDS transpose read of gfx950 (ds_read_b64_tr_b16).  Within each group of 16
@@ -295,8 +302,8 @@ inline size_t prep_smem(int grp, bool conv) {
 template <typename TQ, typename TG, bool CONV>
 __global__ __launch_bounds__(kThreads, (CONV && std::is_same<TQ, bf16_t>::value) ? 3 : 4) void chunk_prep_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TG *__restrict__ g,
-    const TG *__restrict__ beta, uint4 *__restrict__ Tws, int T, int Hk, int Hv, int nchunks, int c0,
-    ConvIn cv) {
+    const TG *__restrict__ beta, uint4 *__restrict__ Tws, int Tall, int Hk, int Hv, int nchunks, int c0,
+    ConvIn cv, Seqs sq) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   _Float16 *sK = reinterpret_cast<_Float16 *>(smem + P_OFF_K);
   _Float16 *sQ = reinterpret_cast<_Float16 *>(smem + P_OFF_Q);
@@ -310,13 +317,23 @@ __global__ __launch_bounds__(kThreads, (CONV && std::is_same<TQ, bf16_t>::value)
   const float *sB = sc + 2 * C;
   float4 *sTap = reinterpret_cast<float4 *>(sc);   // CONV: taps of k, then q (before the head loop)
 
-  const int c = c0 + blockIdx.x;
-  const int b = blockIdx.y / Hk, kh = blockIdx.y % Hk;
+  // block -> (chunk c of sequence b, key head kh); packed sequences: blockIdx.x
+  // is a chunk slot (nchunks = the slot count)
+  const int kh = blockIdx.y % Hk;
+  int c, b, start, T;
+  if (sq.cu) {
+    b = seq_of_slot<C>(sq, Tall, blockIdx.x, c, start, T);
+    if (b < 0) return;
+  } else {
+    c = c0 + blockIdx.x;
+    b = blockIdx.y / Hk;
+    seq_bounds(sq, b, Tall, start, T);
+  }
   const int grp = Hv / Hk;
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, g4 = l >> 4, ln = l & 15;
   const int t0 = c * C, n = min(C, T - t0);
-  const size_t bt0 = (size_t)b * T + t0;
+  const size_t bt0 = (size_t)start + t0;
 
   // CONV: this lane's rows of K and Q in the qkv type, stored to cv.k, cv.q
   // once the loads have all landed
@@ -333,7 +350,7 @@ __global__ __launch_bounds__(kThreads, (CONV && std::is_same<TQ, bf16_t>::value)
 #pragma unroll
       for (int j = 0; j < 7; ++j) {
         const int tt = min(max(t0 + 4 * rb - 3 + j, 0), T - 1);
-        const size_t off = (((size_t)b * T + tt) * Hk + kh) * DK + ch;
+        const size_t off = (((size_t)start + tt) * Hk + kh) * DK + ch;
         uk[j] = *reinterpret_cast<const uint4 *>(cv.xk + off);
         uq[j] = *reinterpret_cast<const uint4 *>(cv.xq + off);
       }
@@ -461,7 +478,7 @@ __global__ __launch_bounds__(kThreads, (CONV && std::is_same<TQ, bf16_t>::value)
     lds_barrier();  // K and Q, or the previous head's T and P, have been read out
     if (tid < C) chunk_scalars(sGB[hv * C + tid], sGB[(grp + hv) * C + tid], sc, tid);
     lds_barrier();
-    uint4 *wch = Tws + (((size_t)b * Hv + h) * nchunks + c) * GDN_CHUNK_U4;
+    uint4 *wch = Tws + (ws_chain(sq, b, h, Hv, nchunks, start) + c) * GDN_CHUNK_U4;
     if (tid < 5 * C / 4) wch[GDN_SC + tid] = reinterpret_cast<const uint4 *>(sc)[tid];
     // P = L o P0 for this head (lower incl. diagonal), fp16; the two upper
     // blocks the fragments read are zero
@@ -610,8 +627,8 @@ template <typename TQ, typename TG, int NW, int RT, bool KDA, int LW, bool CONV,
 __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *__restrict__ v,
     const TG *__restrict__ g, const TG *__restrict__ beta, const uint4 *__restrict__ ws,
-    const float *__restrict__ S0, float *__restrict__ o, float *__restrict__ ST, int T, int Hk,
-    int Hv, int ntasks, int nchunks, int c_begin, int c_end, ConvIn cv, GateArgs ga) {
+    const float *__restrict__ S0, float *__restrict__ o, float *__restrict__ ST, int Tall, int Hk,
+    int Hv, int ntasks, int nchunks, int c_begin, int c_end, ConvIn cv, GateArgs ga, Seqs sq) {
   using Cfg = SeqCfg<NW, RT, KDA, LW>;
   constexpr int NSC = Cfg::NSC;
   constexpr int LT = Cfg::LT, WGC = Cfg::WGC, NS = Cfg::NS, VST = Cfg::VST;
@@ -627,6 +644,20 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
   const int bh = task / NS;  // b * Hv + h
   const int h = bh % Hv, b = bh / Hv;
   const int kh = h / (Hv / Hk);
+  int start, T;   // the sequence's first token and length
+  seq_bounds(sq, b, Tall, start, T);
+  if (sq.cu) {    // packed sequences: all of the sequence's chunks
+    c_begin = 0;
+    c_end = (T + C - 1) / C;
+  }
+  if (c_begin >= c_end) {   // an empty sequence: the state passes through
+    if (threadIdx.x < Cfg::CT)
+      for (int e = threadIdx.x; e < WGC * DK; e += Cfg::CT) {
+        const size_t at = ((size_t)bh * DV + slice * WGC + e / DK) * DK + e % DK;
+        ST[at] = S0 ? S0[at] : 0.f;
+      }
+    return;
+  }
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
@@ -635,10 +666,10 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
 
   // Per-sequence bases (uniform) and per-thread load offsets (fixed for all chunks).
   const int kq_rs = Hk * DK, v_rs = Hv * DV;        // row strides of q/k and v (elements)
-  const TQ *kb = k + ((size_t)b * T * Hk + kh) * DK;
-  const TQ *qb = q + ((size_t)b * T * Hk + kh) * DK;
-  const TQ *vb = v + ((size_t)b * T * Hv + h) * DV + slice * WGC;
-  const uint4 *wsbh = ws + (size_t)bh * nchunks * Cfg::CHUNK_U4;
+  const TQ *kb = k + ((size_t)start * Hk + kh) * DK;
+  const TQ *qb = q + ((size_t)start * Hk + kh) * DK;
+  const TQ *vb = v + ((size_t)start * Hv + h) * DV + slice * WGC;
+  const uint4 *wsbh = ws + ws_chain(sq, b, h, Hv, nchunks, start) * Cfg::CHUNK_U4;
 
   _Float16 *const sKb = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_K);
   _Float16 *const sQb = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_Q);
@@ -654,7 +685,7 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
   // CONV: loading thread -> value channels 8 ch8 .. + 7 of the slice at the
   // chunk rows NV rb .. NV rb + NV - 1 (a row's channels on consecutive lanes)
   const int vrb = ltid / (WGC / 8), vch8 = ltid % (WGC / 8);
-  const bf16_t *xvb = cv.xv + ((size_t)b * T * Hv + h) * DV + slice * WGC + vch8 * 8;
+  const bf16_t *xvb = cv.xv + ((size_t)start * Hv + h) * DV + slice * WGC + vch8 * 8;
   // parts: K and Q (and the key gate's state-update K), V, and the T and P
   // fragments with the scalars
   constexpr int FKQ = 1, FV = 2, FTP = 4, FALL = 7;
@@ -875,7 +906,7 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
 
   const int ic = w * 16 * RT;             // this wave's first value row within the workgroup
   const int iw0 = slice * WGC + ic;       // ... within the head
-  float *ob = GATE ? nullptr : o + ((size_t)b * T * Hv + h) * DV + iw0 + 4 * g4;
+  float *ob = GATE ? nullptr : o + ((size_t)start * Hv + h) * DV + iw0 + 4 * g4;
 
   // state: row tile t (value rows iw0 + 16 t ..), tiles J of S^T; the lane
   // holds S[iw0 + 16 t + ln][16 J + 4 g4 + ii]
@@ -906,7 +937,7 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
   // hold the 8 rows 8 (g4 >> 1) .. + 7 of a tile for one token each (row
   // block 2 p + (g4 & 1)), exchanged with __shfl_xor(., 16)
   const bool godd = g4 & 1;
-  const size_t yoff = ((size_t)b * T * Hv + h) * DV + iw0 + 8 * (g4 >> 1);
+  const size_t yoff = ((size_t)start * Hv + h) * DV + iw0 + 8 * (g4 >> 1);
   if constexpr (GATE) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) load4(ga.gain + iw0 + 16 * t + 4 * g4, gw[t]);
@@ -1196,7 +1227,7 @@ hipError_t launch_seq(const Shape &sh, const void *q, const void *k, const void 
   const int ntasks = sh.B * sh.Hv * Cfg::NS;
   hipLaunchKernelGGL(kern, dim3(ntasks), dim3(Cfg::THREADS), smem, st, (const TQ *)q, (const TQ *)k,
                      (const TQ *)v, (const TG *)g, (const TG *)beta, TPws, S0, o, ST, sh.T, sh.Hk, sh.Hv,
-                     ntasks, nchunks, c_begin, c_end, cv, ga);
+                     ntasks, nchunks, c_begin, c_end, cv, ga, Seqs{sh.cu, sh.B});
   return hipGetLastError();
 }
 
@@ -1285,6 +1316,14 @@ hipError_t pipelined(int nchunks, bool overlap, const float *S0, float *ST, hipS
   return e;
 }
 
+// Chunks per (sequence, value head) in the workspace: ceil(T / C); for packed
+// sequences, chunk slots per value head.
+inline int chunks_per_chain(const Shape &sh) {
+  return sh.packed ? packed_slots(sh.T, sh.B, C) : (sh.T + C - 1) / C;
+}
+// Tokens of all the sequences of a call.
+inline size_t tokens(const Shape &sh) { return sh.packed ? (size_t)sh.T : (size_t)sh.B * sh.T; }
+
 // Overlap the preparation of later segments with the sequential pass when
 // the pass leaves room on the GPU: few sequences, each long (the pass then
 // has at most 192 workgroups).
@@ -1297,7 +1336,8 @@ template <typename TQ, typename TG, bool CONV>
 hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
                     const void *beta, const float *S0, float *o, float *ST, void *ws, hipStream_t st,
                     const ConvIn &cv, const GateArgs *gate = nullptr) {
-  const int nchunks = (sh.T + C - 1) / C;
+  // chunks per (sequence, value head), or chunk slots per value head (packed sequences)
+  const int nchunks = chunks_per_chain(sh);
   uint4 *TPws = (uint4 *)ws;
   auto prep_k = chunk_prep_kernel<TQ, TG, CONV>;
   const size_t smem = prep_smem(sh.Hv / sh.Hk, CONV);
@@ -1306,9 +1346,9 @@ hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v
       hipFuncSetAttribute((const void *)prep_k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
   auto prep = [&](int cb, int ce, hipStream_t s) {
-    hipLaunchKernelGGL(prep_k, dim3(ce - cb, sh.B * sh.Hk), dim3(kThreads), smem, s, (const TQ *)q,
-                       (const TQ *)k, (const TG *)g, (const TG *)beta, TPws, sh.T, sh.Hk, sh.Hv,
-                       nchunks, cb, cv);
+    const dim3 grid = sh.packed ? dim3(nchunks, sh.Hk) : dim3(ce - cb, sh.B * sh.Hk);
+    hipLaunchKernelGGL(prep_k, grid, dim3(kThreads), smem, s, (const TQ *)q, (const TQ *)k, (const TG *)g,
+                       (const TG *)beta, TPws, sh.T, sh.Hk, sh.Hv, nchunks, cb, cv, Seqs{sh.cu, sh.B});
     return hipGetLastError();
   };
   const void *qs = CONV ? cv.q : q, *ks = CONV ? cv.k : k;
@@ -1331,7 +1371,7 @@ hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v
     return launch_seq<TQ, TG, 2, 1, false, 4, CONV>(sh, qs, ks, v, g, beta, TPws, s0, o, ST, nchunks, cb,
                                                     ce, s, cv);
   };
-  return pipelined(nchunks, seq_overlap(heads), S0, ST, st, prep, seq);
+  return pipelined(nchunks, !sh.packed && seq_overlap(heads), S0, ST, st, prep, seq);
 }
 
 // ============================================================================
@@ -1368,7 +1408,8 @@ __device__ __forceinline__ void perm_row_f32(const float *M, int st, int row, in
 template <typename TQ, typename TG>
 __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TG *__restrict__ g,
-    const TG *__restrict__ beta, uint4 *__restrict__ ws, int T, int Hk, int Hv, int nchunks, int c0) {
+    const TG *__restrict__ beta, uint4 *__restrict__ ws, int Tall, int Hk, int Hv, int nchunks, int c0,
+    Seqs sq) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   _Float16 *sK = reinterpret_cast<_Float16 *>(smem + KP_OFF_K);
   _Float16 *sQ = reinterpret_cast<_Float16 *>(smem + KP_OFF_Q);
@@ -1379,13 +1420,23 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(
   _Float16 *sAo = reinterpret_cast<_Float16 *>(smem + KP_OFF_AO);
   float *sAd = reinterpret_cast<float *>(smem + KP_OFF_AD);
 
-  const int c = c0 + blockIdx.x, bh = blockIdx.y;  // bh = b * Hv + h
-  const int b = bh / Hv, h = bh % Hv, kh = h / (Hv / Hk);
+  // block -> (chunk c of sequence b, value head h); packed sequences: blockIdx.x
+  // is a chunk slot (nchunks = the slot count)
+  const int h = blockIdx.y % Hv, kh = h / (Hv / Hk);
+  int c, b, start, T;
+  if (sq.cu) {
+    b = seq_of_slot<C>(sq, Tall, blockIdx.x, c, start, T);
+    if (b < 0) return;
+  } else {
+    c = c0 + blockIdx.x;
+    b = blockIdx.y / Hv;
+    seq_bounds(sq, b, Tall, start, T);
+  }
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, g4 = l >> 4, ln = l & 15;
   const int t0 = c * C, n = min(C, T - t0);
-  const size_t bt0 = (size_t)b * T + t0;
-  uint4 *wc = ws + ((size_t)bh * nchunks + c) * KDA_CHUNK_U4;
+  const size_t bt0 = (size_t)start + t0;
+  uint4 *wc = ws + (ws_chain(sq, b, h, Hv, nchunks, start) + c) * KDA_CHUNK_U4;
 
   // K, Q, g and beta of the chunk; rows past the end are zero (so gamma stays flat there)
   {
@@ -1597,16 +1648,16 @@ template <typename TQ, typename TG>
 hipError_t launch_kda_t(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
                         const void *beta, const float *S0, float *o, float *ST, void *ws,
                         hipStream_t st) {
-  const int nchunks = (sh.T + C - 1) / C;
+  const int nchunks = chunks_per_chain(sh);
   uint4 *wsu = (uint4 *)ws;
   auto prep_k = kda_prep_kernel<TQ, TG>;
   hipError_t e =
       hipFuncSetAttribute((const void *)prep_k, hipFuncAttributeMaxDynamicSharedMemorySize, KP_SMEM);
   if (e != hipSuccess) return e;
   auto prep = [&](int cb, int ce, hipStream_t s) {
-    hipLaunchKernelGGL(prep_k, dim3(ce - cb, sh.B * sh.Hv), dim3(kThreads), KP_SMEM, s, (const TQ *)q,
-                       (const TQ *)k, (const TG *)g, (const TG *)beta, wsu, sh.T, sh.Hk, sh.Hv,
-                       nchunks, cb);
+    const dim3 grid = sh.packed ? dim3(nchunks, sh.Hv) : dim3(ce - cb, sh.B * sh.Hv);
+    hipLaunchKernelGGL(prep_k, grid, dim3(kThreads), KP_SMEM, s, (const TQ *)q, (const TQ *)k, (const TG *)g,
+                       (const TG *)beta, wsu, sh.T, sh.Hk, sh.Hv, nchunks, cb, Seqs{sh.cu, sh.B});
     return hipGetLastError();
   };
   // The decayed K, Q and the state-update K all live in LDS here, so a
@@ -1617,15 +1668,14 @@ hipError_t launch_kda_t(const Shape &sh, const void *q, const void *k, const voi
       return launch_seq<TQ, TG, 4, 1, true, 4>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks, cb, ce, s);
     return launch_seq<TQ, TG, 2, 1, true, 4>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks, cb, ce, s);
   };
-  return pipelined(nchunks, seq_overlap(heads), S0, ST, st, prep, seq);
+  return pipelined(nchunks, !sh.packed && seq_overlap(heads), S0, ST, st, prep, seq);
 }
 
 }  // namespace
 
 size_t chunk_mfma_workspace(const Shape &sh) {
-  const size_t nchunks = (size_t)(sh.T + C - 1) / C;
   const size_t per_chunk = (size_t)(sh.key_gate ? KDA_CHUNK_U4 : GDN_CHUNK_U4) * 16;
-  return (size_t)sh.B * sh.Hv * nchunks * per_chunk;
+  return (size_t)(sh.packed ? 1 : sh.B) * sh.Hv * chunks_per_chain(sh) * per_chunk;
 }
 
 hipError_t launch_chunk_mfma(const Shape &sh, const void *q, const void *k, const void *v,
@@ -1657,7 +1707,7 @@ hipError_t launch_chunk_mfma_conv(const Shape &sh, const void *xq, const void *x
                                   const GateArgs *gate) {
   if (gate && (!chunk_mfma_gate_inside(sh) || gate->yt == DType::F32)) return hipErrorInvalidValue;
   // workspace: the chunk matrices, then q and k after the prologue
-  const size_t nqk = (size_t)sh.B * sh.T * sh.Hk * DK;
+  const size_t nqk = tokens(sh) * sh.Hk * DK;
   char *base = (char *)ws;
   ConvIn cv;
   cv.xq = (const bf16_t *)xq;
@@ -1680,7 +1730,7 @@ hipError_t launch_chunk_mfma_conv(const Shape &sh, const void *xq, const void *x
 }
 
 size_t chunk_mfma_conv_workspace(const Shape &sh) {
-  return chunk_mfma_workspace(sh) + (size_t)2 * sh.B * sh.T * sh.Hk * DK * 2;
+  return chunk_mfma_workspace(sh) + (size_t)2 * tokens(sh) * sh.Hk * DK * 2;
 }
 
 }  // namespace gdn

@@ -46,8 +46,12 @@ Range range(const void *p, size_t bytes) {
 }
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
-// Checks common to every entry point; fills the launcher's shape.
-gdn_status check_desc(const gdn_desc *d, gdn::Shape *sh) {
+// Tokens of all the sequences: B x T, or T for packed sequences.
+size_t ntok(const gdn_desc *d, bool packed) { return packed ? (size_t)d->T : (size_t)d->B * d->T; }
+
+// Checks common to every entry point; fills the launcher's shape.  packed: B
+// sequences packed into T tokens.
+gdn_status check_desc(const gdn_desc *d, gdn::Shape *sh, bool packed = false) {
   if (!d) return fail(GDN_E_ARG, "desc is NULL");
   if (d->B < 1 || d->T < 1 || d->Hk < 1 || d->Hv < 1 || d->dk < 1 || d->dv < 1)
     return fail(GDN_E_ARG, "B, T, Hk, Hv, dk, dv must be >= 1 (got %d %d %d %d %d %d)", d->B,
@@ -64,7 +68,7 @@ gdn_status check_desc(const gdn_desc *d, gdn::Shape *sh) {
   const double n_big = (double)d->B * d->T * (double)(d->Hv > d->Hk ? d->Hv : d->Hk) *
                        (d->dv > d->dk ? d->dv : d->dk);
   if (n_big > 1e13) return fail(GDN_E_UNSUPPORTED, "problem too large");
-  if ((double)d->B * ((d->T + 63) / 64) > 2147483647.0)
+  if (!packed && (double)d->B * d->T > 2147483647.0)
     return fail(GDN_E_UNSUPPORTED, "B * T too large");
   sh->B = d->B;
   sh->T = d->T;
@@ -76,6 +80,15 @@ gdn_status check_desc(const gdn_desc *d, gdn::Shape *sh) {
   sh->qkv = (gdn::DType)d->qkv_dtype;
   sh->gate_t = (gdn::DType)d->gate_dtype;
   sh->key_gate = d->gate == GDN_GATE_KEY_CHANNEL;
+  sh->packed = packed;
+  return GDN_OK;
+}
+
+// The offsets of packed sequences: present and 4-byte aligned (their values
+// are read on the device only).
+gdn_status check_offsets(const int32_t *cu) {
+  if (!cu) return fail(GDN_E_ARG, "cu_seqlens is NULL");
+  if (((uintptr_t)cu & 3u) != 0) return fail(GDN_E_ALIGN, "cu_seqlens is not 4-byte aligned");
   return GDN_OK;
 }
 
@@ -122,19 +135,28 @@ const char *gdn_status_str(gdn_status s) {
 
 const char *gdn_last_error(void) { return g_last_error.c_str(); }
 
-gdn_status gdn_prologue(const gdn_desc *d, int32_t x_dtype, const void *xq, const void *xk,
-                        const void *xv, const float *conv_w, float eps, void *q, void *k, void *v,
-                        void *stream) {
+}  // extern "C"
+
+namespace {
+
+gdn_status prologue_impl(const gdn_desc *d, const int32_t *cu, int32_t x_dtype, const void *xq,
+                         const void *xk, const void *xv, const float *conv_w, float eps, void *q,
+                         void *k, void *v, void *stream) {
+  const bool packed = cu != nullptr;
   gdn::Shape sh;
-  gdn_status st = check_desc(d, &sh);
+  gdn_status st = check_desc(d, &sh, packed);
   if (st != GDN_OK) return st;
   if ((st = check_prologue_args(d, x_dtype, eps)) != GDN_OK) return st;
   const char *names[] = {"xq", "xk", "xv", "conv_w", "q", "k", "v"};
   const void *ptrs[] = {xq, xk, xv, conv_w, q, k, v};
   if ((st = check_ptrs(names, ptrs, 7)) != GDN_OK) return st;
-  const size_t nqk = (size_t)d->B * d->T * d->Hk * d->dk, nv = (size_t)d->B * d->T * d->Hv * d->dv;
+  const size_t nqk = ntok(d, packed) * d->Hk * d->dk, nv = ntok(d, packed) * d->Hv * d->dv;
   const size_t xs = dsize(x_dtype), ys = dsize(d->qkv_dtype);
   const Range outs[] = {range(q, nqk * ys), range(k, nqk * ys), range(v, nv * ys)};
+  if (packed)
+    for (const Range &a : outs)
+      if (overlap(a, range(cu, ((size_t)d->B + 1) * 4)))
+        return fail(GDN_E_ARG, "prologue outputs must not overlap cu_seqlens");
   const Range ins[] = {range(xq, nqk * xs), range(xk, nqk * xs), range(xv, nv * xs),
                        range(conv_w, (2 * (size_t)d->Hk * d->dk + (size_t)d->Hv * d->dv) * 16)};
   for (const Range &a : outs)
@@ -144,8 +166,26 @@ gdn_status gdn_prologue(const gdn_desc *d, int32_t x_dtype, const void *xq, cons
     return fail(GDN_E_ARG, "prologue outputs must not overlap each other");
 
   hipError_t e = gdn::launch_prologue(xq, xk, xv, (gdn::DType)x_dtype, conv_w, q, k, v, sh.qkv, d->B,
-                                      d->T, d->Hk, d->Hv, d->dk, d->dv, eps, (hipStream_t)stream);
+                                      d->T, d->Hk, d->Hv, d->dk, d->dv, eps, (hipStream_t)stream, cu);
   return launched(e, "prologue launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_prologue(const gdn_desc *d, int32_t x_dtype, const void *xq, const void *xk,
+                        const void *xv, const float *conv_w, float eps, void *q, void *k, void *v,
+                        void *stream) {
+  return prologue_impl(d, nullptr, x_dtype, xq, xk, xv, conv_w, eps, q, k, v, stream);
+}
+
+gdn_status gdn_prologue_varlen(const gdn_desc *d, const int32_t *cu_seqlens, int32_t x_dtype,
+                               const void *xq, const void *xk, const void *xv, const float *conv_w,
+                               float eps, void *q, void *k, void *v, void *stream) {
+  const gdn_status st = check_offsets(cu_seqlens);
+  if (st != GDN_OK) return st;
+  return prologue_impl(d, cu_seqlens, x_dtype, xq, xk, xv, conv_w, eps, q, k, v, stream);
 }
 
 size_t gdn_fwd_workspace_bytes(const gdn_desc *d) {
@@ -157,14 +197,23 @@ size_t gdn_fwd_workspace_bytes(const gdn_desc *d) {
   return uses_matrix_cores(d) ? gdn::chunk_mfma_workspace(sh) : 0;
 }
 
+size_t gdn_fwd_varlen_workspace_bytes(const gdn_desc *d) {
+  gdn::Shape sh;
+  const std::string saved = g_last_error;
+  const gdn_status st = check_desc(d, &sh, true);
+  g_last_error = saved;
+  if (st != GDN_OK) return 0;
+  return uses_matrix_cores(d) ? gdn::chunk_mfma_workspace(sh) : 0;
+}
+
 }  // extern "C"
 
 namespace {
 
 // Everything gdn_fwd_chunked checks, without launching.  `ws_need` is the
 // workspace the chosen kernels need (the caller checks the one it passes).
-gdn_status check_chunked(const gdn_desc *d, gdn::Shape *sh, bool *use_mfma_out) {
-  gdn_status st = check_desc(d, sh);
+gdn_status check_chunked(const gdn_desc *d, gdn::Shape *sh, bool *use_mfma_out, bool packed = false) {
+  gdn_status st = check_desc(d, sh, packed);
   if (st != GDN_OK) return st;
   const bool fp32_mode = d->qkv_dtype == GDN_F32 && d->gate_dtype == GDN_F32;
   const bool mc_mode = (d->qkv_dtype == GDN_BF16 || d->qkv_dtype == GDN_F16) &&
@@ -199,12 +248,13 @@ gdn_status check_chunked(const gdn_desc *d, gdn::Shape *sh, bool *use_mfma_out) 
 gdn_status check_chunked_ptrs(const gdn_desc *d, const gdn::Shape &sh, const Range *ins, int nins,
                               const void *g, const void *beta, const float *S0, const void *o,
                               float *S_T, size_t o_bytes = 0) {
+  const bool packed = sh.packed;
   const char *names[] = {"g", "beta", "o", "S_T"};
   const void *ptrs[] = {g, beta, o, S_T};
   gdn_status st = check_ptrs(names, ptrs, 4);
   if (st != GDN_OK) return st;
   if (S0 && !aligned16(S0)) return fail(GDN_E_ALIGN, "S0 is not 16-byte aligned");
-  const size_t bt = (size_t)d->B * d->T;
+  const size_t bt = ntok(d, packed);
   const size_t gs = dsize(d->gate_dtype);
   const size_t state_bytes = (size_t)d->B * d->Hv * d->dv * d->dk * 4;
   const Range ro = range(o, o_bytes ? o_bytes : bt * d->Hv * d->dv * 4);
@@ -230,13 +280,13 @@ gdn_status check_chunked_ptrs(const gdn_desc *d, const gdn::Shape &sh, const Ran
 gdn_status check_workspace(const gdn_desc *d, void *workspace, size_t workspace_bytes, size_t need,
                            const Range *ins, int nins, const void *g, const void *beta,
                            const float *S0, const void *o, float *S_T, bool key_gate,
-                           size_t o_bytes = 0) {
+                           size_t o_bytes = 0, bool packed = false) {
   if (workspace_bytes < need)
     return fail(GDN_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
   if (need == 0) return GDN_OK;
   if (!workspace) return fail(GDN_E_ARG, "workspace is NULL");
   if (!aligned16(workspace)) return fail(GDN_E_ALIGN, "workspace is not 16-byte aligned");
-  const size_t bt = (size_t)d->B * d->T, gs = dsize(d->gate_dtype);
+  const size_t bt = ntok(d, packed), gs = dsize(d->gate_dtype);
   const size_t state_bytes = (size_t)d->B * d->Hv * d->dv * d->dk * 4;
   const Range rw = range(workspace, need);
   for (int i = 0; i < nins; ++i)
@@ -275,7 +325,7 @@ bool conv_fused(const gdn_desc *d, const gdn::Shape &sh, bool use_mfma, int32_t 
 size_t conv_workspace(const gdn_desc *d, const gdn::Shape &sh, bool use_mfma, int32_t x_dtype) {
   if (conv_fused(d, sh, use_mfma, x_dtype)) return gdn::chunk_mfma_conv_workspace(sh);
   const size_t ys = dsize(d->qkv_dtype);
-  const size_t nqk = (size_t)d->B * d->T * d->Hk * d->dk, nv = (size_t)d->B * d->T * d->Hv * d->dv;
+  const size_t nqk = ntok(d, sh.packed) * d->Hk * d->dk, nv = ntok(d, sh.packed) * d->Hv * d->dv;
   return 2 * round256(nqk * ys) + round256(nv * ys) + (use_mfma ? gdn::chunk_mfma_workspace(sh) : 0);
 }
 
@@ -290,12 +340,12 @@ gdn_status run_chunked_conv(const gdn_desc *d, const gdn::Shape &sh, bool use_mf
                                                 workspace, s),
                     "chunked forward with convolution launch");
   // the prologue into the workspace, then the chunked forward
-  const size_t nqk = (size_t)d->B * d->T * d->Hk * d->dk, nv = (size_t)d->B * d->T * d->Hv * d->dv;
+  const size_t nqk = ntok(d, sh.packed) * d->Hk * d->dk, nv = ntok(d, sh.packed) * d->Hv * d->dv;
   const size_t ys = dsize(d->qkv_dtype);
   char *q = (char *)workspace, *k = q + round256(nqk * ys), *v = k + round256(nqk * ys);
   char *rest = v + round256(nv * ys);
   hipError_t e = gdn::launch_prologue(xq, xk, xv, (gdn::DType)x_dtype, conv_w, q, k, v, sh.qkv, d->B,
-                                      d->T, d->Hk, d->Hv, d->dk, d->dv, eps, s);
+                                      d->T, d->Hk, d->Hv, d->dk, d->dv, eps, s, sh.cu);
   if (e != hipSuccess) return launched(e, "prologue launch");
   e = use_mfma ? gdn::launch_chunk_mfma(sh, q, k, v, g, beta, S0, o, S_T, rest, s)
                : gdn::launch_chunk_f32(sh, q, k, v, g, beta, S0, o, S_T, s);
@@ -328,31 +378,85 @@ gdn_status check_gate_args(const gdn_desc *d, int32_t z_dtype, int32_t y_dtype, 
 
 }  // namespace
 
+namespace {
+
+// gdn_fwd_chunked and its packed-sequence form (cu: device offsets, or null).
+gdn_status chunked_impl(const gdn_desc *d, const int32_t *cu, const void *q, const void *k, const void *v,
+                        const void *g, const void *beta, const float *S0, float *o, float *S_T,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  const bool packed = cu != nullptr;
+  gdn::Shape sh;
+  bool use_mfma = false;
+  gdn_status st = check_chunked(d, &sh, &use_mfma, packed);
+  if (st != GDN_OK) return st;
+  const char *names[] = {"q", "k", "v"};
+  const void *ptrs[] = {q, k, v};
+  if ((st = check_ptrs(names, ptrs, 3)) != GDN_OK) return st;
+  const size_t bt = ntok(d, packed), qs = dsize(d->qkv_dtype);
+  const Range ins[] = {range(q, bt * d->Hk * d->dk * qs), range(k, bt * d->Hk * d->dk * qs),
+                       range(v, bt * d->Hv * d->dv * qs), range(cu, ((size_t)d->B + 1) * 4)};
+  const int nins = packed ? 4 : 3;
+  if ((st = check_chunked_ptrs(d, sh, ins, nins, g, beta, S0, o, S_T)) != GDN_OK) return st;
+  const size_t need = use_mfma ? gdn::chunk_mfma_workspace(sh) : 0;
+  if ((st = check_workspace(d, workspace, workspace_bytes, need, ins, nins, g, beta, S0, o, S_T,
+                            sh.key_gate, 0, packed)) != GDN_OK)
+    return st;
+
+  sh.cu = cu;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = use_mfma ? gdn::launch_chunk_mfma(sh, q, k, v, g, beta, S0, o, S_T, workspace, s)
+                          : gdn::launch_chunk_f32(sh, q, k, v, g, beta, S0, o, S_T, s);
+  return launched(e, "chunked forward launch");
+}
+
+// gdn_fwd_chunked_conv and its packed-sequence form.
+gdn_status chunked_conv_impl(const gdn_desc *d, const int32_t *cu, int32_t x_dtype, const void *xq,
+                             const void *xk, const void *xv, const float *conv_w, float eps,
+                             const void *g, const void *beta, const float *S0, float *o, float *S_T,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+  const bool packed = cu != nullptr;
+  gdn::Shape sh;
+  bool use_mfma = false;
+  gdn_status st = check_chunked(d, &sh, &use_mfma, packed);
+  if (st != GDN_OK) return st;
+  if ((st = check_prologue_args(d, x_dtype, eps)) != GDN_OK) return st;
+  const char *names[] = {"xq", "xk", "xv", "conv_w"};
+  const void *ptrs[] = {xq, xk, xv, conv_w};
+  if ((st = check_ptrs(names, ptrs, 4)) != GDN_OK) return st;
+  const size_t nqk = ntok(d, packed) * d->Hk * d->dk, nv = ntok(d, packed) * d->Hv * d->dv;
+  const size_t xs = dsize(x_dtype);
+  const Range ins[] = {range(xq, nqk * xs), range(xk, nqk * xs), range(xv, nv * xs),
+                       range(conv_w, (2 * (size_t)d->Hk * d->dk + (size_t)d->Hv * d->dv) * 16),
+                       range(cu, ((size_t)d->B + 1) * 4)};
+  const int nins = packed ? 5 : 4;
+  if ((st = check_chunked_ptrs(d, sh, ins, nins, g, beta, S0, o, S_T)) != GDN_OK) return st;
+  const size_t need = conv_workspace(d, sh, use_mfma, x_dtype);
+  if ((st = check_workspace(d, workspace, workspace_bytes, need, ins, nins, g, beta, S0, o, S_T,
+                            sh.key_gate, 0, packed)) != GDN_OK)
+    return st;
+
+  sh.cu = cu;
+  return run_chunked_conv(d, sh, use_mfma, x_dtype, xq, xk, xv, conv_w, eps, g, beta, S0, o, S_T,
+                          workspace, (hipStream_t)stream);
+}
+
+}  // namespace
+
 extern "C" {
 
 gdn_status gdn_fwd_chunked(const gdn_desc *d, const void *q, const void *k, const void *v,
                            const void *g, const void *beta, const float *S0, float *o, float *S_T,
                            void *workspace, size_t workspace_bytes, void *stream) {
-  gdn::Shape sh;
-  bool use_mfma = false;
-  gdn_status st = check_chunked(d, &sh, &use_mfma);
-  if (st != GDN_OK) return st;
-  const char *names[] = {"q", "k", "v"};
-  const void *ptrs[] = {q, k, v};
-  if ((st = check_ptrs(names, ptrs, 3)) != GDN_OK) return st;
-  const size_t bt = (size_t)d->B * d->T, qs = dsize(d->qkv_dtype);
-  const Range ins[] = {range(q, bt * d->Hk * d->dk * qs), range(k, bt * d->Hk * d->dk * qs),
-                       range(v, bt * d->Hv * d->dv * qs)};
-  if ((st = check_chunked_ptrs(d, sh, ins, 3, g, beta, S0, o, S_T)) != GDN_OK) return st;
-  const size_t need = use_mfma ? gdn::chunk_mfma_workspace(sh) : 0;
-  if ((st = check_workspace(d, workspace, workspace_bytes, need, ins, 3, g, beta, S0, o, S_T,
-                            sh.key_gate)) != GDN_OK)
-    return st;
+  return chunked_impl(d, nullptr, q, k, v, g, beta, S0, o, S_T, workspace, workspace_bytes, stream);
+}
 
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e = use_mfma ? gdn::launch_chunk_mfma(sh, q, k, v, g, beta, S0, o, S_T, workspace, s)
-                          : gdn::launch_chunk_f32(sh, q, k, v, g, beta, S0, o, S_T, s);
-  return launched(e, "chunked forward launch");
+gdn_status gdn_fwd_chunked_varlen(const gdn_desc *d, const int32_t *cu_seqlens, const void *q,
+                                  const void *k, const void *v, const void *g, const void *beta,
+                                  const float *S0, float *o, float *S_T, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+  const gdn_status st = check_offsets(cu_seqlens);
+  if (st != GDN_OK) return st;
+  return chunked_impl(d, cu_seqlens, q, k, v, g, beta, S0, o, S_T, workspace, workspace_bytes, stream);
 }
 
 size_t gdn_fwd_conv_workspace_bytes(const gdn_desc *d, int32_t x_dtype) {
@@ -366,30 +470,34 @@ size_t gdn_fwd_conv_workspace_bytes(const gdn_desc *d, int32_t x_dtype) {
   return conv_workspace(d, sh, use_mfma, x_dtype);
 }
 
+size_t gdn_fwd_conv_varlen_workspace_bytes(const gdn_desc *d, int32_t x_dtype) {
+  gdn::Shape sh;
+  bool use_mfma = false;
+  const std::string saved = g_last_error;
+  gdn_status st = check_chunked(d, &sh, &use_mfma, true);
+  if (st == GDN_OK) st = check_prologue_args(d, x_dtype, 0.f);
+  g_last_error = saved;
+  if (st != GDN_OK) return 0;
+  return conv_workspace(d, sh, use_mfma, x_dtype);
+}
+
 gdn_status gdn_fwd_chunked_conv(const gdn_desc *d, int32_t x_dtype, const void *xq, const void *xk,
                                 const void *xv, const float *conv_w, float eps, const void *g,
                                 const void *beta, const float *S0, float *o, float *S_T,
                                 void *workspace, size_t workspace_bytes, void *stream) {
-  gdn::Shape sh;
-  bool use_mfma = false;
-  gdn_status st = check_chunked(d, &sh, &use_mfma);
-  if (st != GDN_OK) return st;
-  if ((st = check_prologue_args(d, x_dtype, eps)) != GDN_OK) return st;
-  const char *names[] = {"xq", "xk", "xv", "conv_w"};
-  const void *ptrs[] = {xq, xk, xv, conv_w};
-  if ((st = check_ptrs(names, ptrs, 4)) != GDN_OK) return st;
-  const size_t nqk = (size_t)d->B * d->T * d->Hk * d->dk, nv = (size_t)d->B * d->T * d->Hv * d->dv;
-  const size_t xs = dsize(x_dtype);
-  const Range ins[] = {range(xq, nqk * xs), range(xk, nqk * xs), range(xv, nv * xs),
-                       range(conv_w, (2 * (size_t)d->Hk * d->dk + (size_t)d->Hv * d->dv) * 16)};
-  if ((st = check_chunked_ptrs(d, sh, ins, 4, g, beta, S0, o, S_T)) != GDN_OK) return st;
-  const size_t need = conv_workspace(d, sh, use_mfma, x_dtype);
-  if ((st = check_workspace(d, workspace, workspace_bytes, need, ins, 4, g, beta, S0, o, S_T,
-                            sh.key_gate)) != GDN_OK)
-    return st;
+  return chunked_conv_impl(d, nullptr, x_dtype, xq, xk, xv, conv_w, eps, g, beta, S0, o, S_T, workspace,
+                           workspace_bytes, stream);
+}
 
-  return run_chunked_conv(d, sh, use_mfma, x_dtype, xq, xk, xv, conv_w, eps, g, beta, S0, o, S_T,
-                          workspace, (hipStream_t)stream);
+gdn_status gdn_fwd_chunked_conv_varlen(const gdn_desc *d, const int32_t *cu_seqlens, int32_t x_dtype,
+                                       const void *xq, const void *xk, const void *xv,
+                                       const float *conv_w, float eps, const void *g, const void *beta,
+                                       const float *S0, float *o, float *S_T, void *workspace,
+                                       size_t workspace_bytes, void *stream) {
+  const gdn_status st = check_offsets(cu_seqlens);
+  if (st != GDN_OK) return st;
+  return chunked_conv_impl(d, cu_seqlens, x_dtype, xq, xk, xv, conv_w, eps, g, beta, S0, o, S_T,
+                           workspace, workspace_bytes, stream);
 }
 
 gdn_status gdn_output_gate(const gdn_desc *d, const float *o, int32_t z_dtype, const void *z,

@@ -78,6 +78,45 @@ __device__ __forceinline__ void store8(bf16_t *p, const float (&x)[8]) {
   *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// The token sequences of a call: B sequences of T tokens each (cu null), or
+// B sequences packed one after another, sequence s being tokens
+// cu[s] .. cu[s + 1] - 1 of the T.  The offsets are read on the device: each
+// is clamped to [0, T] and a sequence whose end precedes its start is empty,
+// so that no access leaves the tensors whatever the offsets hold.
+struct Seqs {
+  const int *cu;
+  int B;
+};
+__device__ __forceinline__ void seq_bounds(const Seqs &sq, int s, int T, int &start, int &len) {
+  if (!sq.cu) {
+    start = s * T;   // B * T < 2^31 (checked on the host)
+    len = T;
+    return;
+  }
+  const int a = min(max(sq.cu[s], 0), T), e = min(max(sq.cu[s + 1], a), T);
+  start = a;
+  len = e - a;
+}
+// Packed sequences keep the work units of G tokens of sequence s in the slots
+// cu[s] / G + s + j, j < ceil(len / G): distinct for valid offsets, and below
+// T / G + B for any.  seq_of_slot gives the sequence of a slot, its unit
+// index and bounds, or -1 when no unit of any sequence is there.
+__host__ __device__ __forceinline__ int packed_slots(int T, int B, int G) { return T / G + B; }
+template <int G>
+__device__ __forceinline__ int seq_of_slot(const Seqs &sq, int T, int slot, int &unit, int &start, int &len) {
+  int lo = 0, hi = sq.B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (min(max(sq.cu[mid], 0), T) / G + mid <= slot)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  seq_bounds(sq, lo, T, start, len);
+  unit = slot - (start / G + lo);
+  return unit >= 0 && unit * G < len ? lo : -1;
+}
+
 // Workgroup barrier for hand-offs through LDS only: waits for this wave's
 // LDS operations, then for the other waves.  Unlike __syncthreads(), it does
 // not drain the wave's outstanding global loads and stores, so prefetches and

@@ -10,10 +10,15 @@ namespace gdn {
 
 enum class DType : int { F32 = 0, BF16 = 1, F16 = 2 };
 
+// B sequences of T tokens each; or (packed) B sequences packed into T
+// tokens, sequence s being tokens cu[s] .. cu[s+1]-1 (cu: device int32
+// [B + 1]; null in a size query).
 struct Shape {
   int B, T, Hk, Hv, dk, dv, chunk;
   DType qkv, gate_t;
   bool key_gate;
+  bool packed = false;
+  const int *cu = nullptr;
 };
 
 // The gate's arguments for the chunked forward with the prologue inside,
@@ -29,10 +34,10 @@ struct GateArgs {
 bool chunk_mfma_gate_inside(const Shape &sh);
 
 // Prologue: conv + SiLU over q, k, v (L2 over q and k rows); w holds the
-// conv taps of q, then k, then v channels.
+// conv taps of q, then k, then v channels.  cu: packed sequences (see Shape).
 hipError_t launch_prologue(const void *xq, const void *xk, const void *xv, DType xt, const float *w,
                            void *q, void *k, void *v, DType yt, int B, int T, int Hk, int Hv, int dk,
-                           int dv, float eps, hipStream_t s);
+                           int dv, float eps, hipStream_t s, const int *cu = nullptr);
 
 // One decode step, state in place.
 hipError_t launch_decode(const Shape &sh, const void *q, const void *k, const void *v,

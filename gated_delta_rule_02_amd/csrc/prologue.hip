@@ -12,7 +12,9 @@
 // so one load is 16 bytes (bf16) per lane; each lane group walks a span of
 // kSpan tokens of its head row, keeping the last three inputs in registers;
 // the loads of the next kU tokens are in flight while the current ones are
-// computed and stored.
+// computed and stored.  Packed sequences of different lengths: a block takes
+// a span of one sequence (the history before a sequence's first token is
+// zero), found from the sequence offsets.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -34,6 +36,7 @@ struct ProArgs {
   ProTensor t[3];
   int B, T;
   float eps;
+  Seqs sq;   // packed sequences (sq.cu), or B sequences of T tokens
 };
 
 // Eight input channels as loaded (16 bytes of bf16, 32 of fp32), widened
@@ -67,13 +70,22 @@ template <typename TX, typename TO, int D>
 __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
   constexpr int LPR = D / 8;                 // lanes per head row
   constexpr int RPB = kThreads / LPR;        // head rows per block
-  const int nspan = (a.T + kSpan - 1) / kSpan;
-  // block -> (span, group of RPB rows of the concatenated q | k | v head list)
-  const int span = blockIdx.x % nspan;
-  const int bg = blockIdx.x / nspan;         // over B * ceil(rows / RPB)
+  // block -> (span, group of RPB rows of the concatenated q | k | v head
+  // list); packed sequences: span slots, each a span of one sequence
+  const int nspan = a.sq.cu ? packed_slots(a.T, a.B, kSpan) : (a.T + kSpan - 1) / kSpan;
+  const int slot = blockIdx.x % nspan;
+  const int bg = blockIdx.x / nspan;         // over B * ceil(rows / RPB), or ceil(rows / RPB)
   const int nrows = a.t[0].H + a.t[1].H + a.t[2].H;
   const int ngroups = (nrows + RPB - 1) / RPB;
-  const int b = bg / ngroups;
+  int b, span, start, T;
+  if (a.sq.cu) {
+    b = seq_of_slot<kSpan>(a.sq, a.T, slot, span, start, T);
+    if (b < 0) return;
+  } else {
+    b = bg / ngroups;
+    span = slot;
+    seq_bounds(a.sq, b, a.T, start, T);
+  }
   const int row = (bg % ngroups) * RPB + threadIdx.x / LPR;
   if (row >= nrows) return;  // whole lane groups leave together
   int ti = 0, head = row;
@@ -93,11 +105,11 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
     }
   }
   const size_t tok_stride = (size_t)P.H * D;
-  const TX *xb = reinterpret_cast<const TX *>(P.x) + (size_t)b * a.T * tok_stride + (size_t)head * D + c0;
-  TO *yb = reinterpret_cast<TO *>(P.y) + (size_t)b * a.T * tok_stride + (size_t)head * D + c0;
+  const TX *xb = reinterpret_cast<const TX *>(P.x) + (size_t)start * tok_stride + (size_t)head * D + c0;
+  TO *yb = reinterpret_cast<TO *>(P.y) + (size_t)start * tok_stride + (size_t)head * D + c0;
 
   float xm3[8], xm2[8], xm1[8];
-  if (t0 >= 3 && t0 + kSpan <= a.T) {
+  if (t0 >= 3 && t0 + kSpan <= T) {
     // A whole span with its whole history: the loads of the next kU tokens
     // are issued before the current ones are computed and stored, and every
     // store is unconditional, so each wait is for loads alone (one counter
@@ -141,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
   if (t0 >= 2) load8(xb + (size_t)(t0 - 2) * tok_stride, xm2);
   if (t0 >= 1) load8(xb + (size_t)(t0 - 1) * tok_stride, xm1);
 
-  const int t_end = min(a.T, t0 + kSpan);
+  const int t_end = min(T, t0 + kSpan);
   for (int t = t0; t < t_end; t += kU) {
     float xs[kU][8];
 #pragma unroll
@@ -165,9 +177,9 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
 template <typename TX, typename TO, int D>
 hipError_t launch_d(const ProArgs &a, hipStream_t st) {
   constexpr int RPB = kThreads / (D / 8);
-  const int nspan = (a.T + kSpan - 1) / kSpan;
+  const int nspan = a.sq.cu ? packed_slots(a.T, a.B, kSpan) : (a.T + kSpan - 1) / kSpan;
   const int nrows = a.t[0].H + a.t[1].H + a.t[2].H;
-  const long blocks = (long)nspan * a.B * ((nrows + RPB - 1) / RPB);
+  const long blocks = (long)nspan * (a.sq.cu ? 1 : a.B) * ((nrows + RPB - 1) / RPB);
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((prologue_kernel<TX, TO, D>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
   return hipGetLastError();
@@ -204,12 +216,13 @@ hipError_t launch_one(const ProArgs &a, DType xt, DType yt, int d, hipStream_t s
 
 hipError_t launch_prologue(const void *xq, const void *xk, const void *xv, DType xt, const float *w,
                            void *q, void *k, void *v, DType yt, int B, int T, int Hk, int Hv, int dk,
-                           int dv, float eps, hipStream_t st) {
+                           int dv, float eps, hipStream_t st, const int *cu) {
   const size_t nw = (size_t)Hk * dk * 4;   // conv_w rows of q, then of k, then of v
   ProArgs a;
   a.B = B;
   a.T = T;
   a.eps = eps;
+  a.sq = Seqs{cu, B};
   a.t[0] = ProTensor{xq, w, q, Hk, true};
   a.t[1] = ProTensor{xk, w + nw, k, Hk, true};
   a.t[2] = ProTensor{xv, w + 2 * nw, v, Hv, false};

@@ -183,6 +183,45 @@ gdn_status gdn_fwd_chunked_conv(const gdn_desc *d, int32_t x_dtype, const void *
                                 size_t workspace_bytes, void *stream);
 
 /*
+ * Packed sequences of different lengths ("_varlen" entry points): the same
+ * operations over B sequences stored one after another along one token axis
+ * of T tokens, sequence s being tokens cu_seqlens[s] .. cu_seqlens[s+1] - 1.
+ * Each sequence is computed on its own, exactly as a call with that sequence
+ * alone would compute it: its own entering state S0[s] (or zero), its own
+ * chunks (a chunk never spans two sequences), convolution history zero before
+ * its first token, its own S_T[s].
+ *
+ *   d->B        the number of sequences (<= 65535); d->T the total tokens
+ *   cu_seqlens  device int32 [B + 1]: 0 = cu[0] <= cu[1] <= ... <= cu[B] = T;
+ *               empty sequences are allowed (their S_T is their S0, or zero)
+ *   token-major tensors (q, k, v, g, beta, o, raw inputs) have the layouts
+ *               above with the batch dimension removed: q [T,Hk,dk], o [T,Hv,dv], ...
+ *   S0, S_T     [B,Hv,dv,dk] as above, one state per sequence
+ * The offsets are read on the device, so the host checks only that the
+ * pointer is present and 4-byte aligned.  Each offset is clamped to [0, T]
+ * and a sequence whose end precedes its start is read as empty: offsets that
+ * break the rule above give unspecified results but no access outside the
+ * arguments.  Supported: what the fixed-length entry point supports; the
+ * workspace sizes are those of the _varlen queries.
+ */
+gdn_status gdn_prologue_varlen(const gdn_desc *d, const int32_t *cu_seqlens, int32_t x_dtype,
+                               const void *xq, const void *xk, const void *xv,
+                               const float *conv_w, float eps, void *q, void *k, void *v,
+                               void *stream);
+size_t gdn_fwd_varlen_workspace_bytes(const gdn_desc *d);
+gdn_status gdn_fwd_chunked_varlen(const gdn_desc *d, const int32_t *cu_seqlens, const void *q,
+                                  const void *k, const void *v, const void *g,
+                                  const void *beta, const float *S0, float *o, float *S_T,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+size_t gdn_fwd_conv_varlen_workspace_bytes(const gdn_desc *d, int32_t x_dtype);
+gdn_status gdn_fwd_chunked_conv_varlen(const gdn_desc *d, const int32_t *cu_seqlens,
+                                       int32_t x_dtype, const void *xq, const void *xk,
+                                       const void *xv, const float *conv_w, float eps,
+                                       const void *g, const void *beta, const float *S0,
+                                       float *o, float *S_T, void *workspace,
+                                       size_t workspace_bytes, void *stream);
+
+/*
  * gdn_output_gate -- the gated output norm that follows the state read in a
  * Gated DeltaNet layer ("Source notes", Linear attention, row gdn: the
  * read-out is RMS-normalised, scaled by a learned gain and multiplied by a

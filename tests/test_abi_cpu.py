@@ -241,3 +241,31 @@ def test_gated_rejects_before_launch(L):
     assert call(d, bad) == 1
     assert call(d, p, ws=P(p[8].value + 256)) == 1      # workspace over y
     assert call(desc(B=4, Hk=16, Hv=48, dv=64), p) == 3  # matrix-core mode needs dv 128
+
+
+def test_varlen_checks(L):
+    P = ctypes.c_void_p
+    d = desc(B=5, T=1000)                                # 5 packed sequences, 1000 tokens in all
+    p = [P(FAKE + i * (1 << 36)) for i in range(12)]
+    cu = P(FAKE + 11 * (1 << 36))
+    need = L.gdn_fwd_varlen_workspace_bytes(ctypes.byref(d))
+    # matrix-core path: chunk slots per value head = T / 64 + B = 20
+    assert need == 6 * (1000 // 64 + 5) * 13568
+    assert L.gdn_fwd_varlen_workspace_bytes(ctypes.byref(desc(B=5, T=1000, Hv=5))) == 0
+    call = lambda dd, cu_, ptrs=p, ws=p[10], nbytes=need: L.gdn_fwd_chunked_varlen(
+        ctypes.byref(dd), cu_, *ptrs[:5], None, *ptrs[5:7], ws, nbytes, None)
+    assert call(d, None) == 1                            # offsets missing
+    assert call(d, P(cu.value + 2)) == 4                 # offsets misaligned
+    assert call(d, cu, nbytes=need - 16) == 5
+    bad = list(p)
+    bad[5] = P(cu.value - 64)                            # o over the offsets
+    assert call(d, cu, bad) == 1
+    assert call(desc(B=5, T=1000, dk=64), cu) == 3
+    # the conv form and the prologue
+    cneed = L.gdn_fwd_conv_varlen_workspace_bytes(ctypes.byref(d), gdn.BF16)
+    assert cneed == need + 2 * 1000 * 2 * 128 * 2        # plus q and k after the prologue
+    assert L.gdn_fwd_chunked_conv_varlen(ctypes.byref(d), None, gdn.BF16, *p[:4], 1e-6, *p[4:6], None,
+                                         *p[6:8], p[10], cneed, None) == 1
+    assert L.gdn_prologue_varlen(ctypes.byref(d), cu, gdn.BF16, *p[:4], 1e-6, P(cu.value), *p[5:7],
+                                 None) == 1              # q written over the offsets
+    assert L.gdn_prologue_varlen(ctypes.byref(d), None, gdn.BF16, *p[:4], 1e-6, *p[4:7], None) == 1
