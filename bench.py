@@ -23,7 +23,8 @@ kernels run on):
                 and the step's prefill followed by the gated output norm (RMS
                 norm x gain x SiLU gate, bf16 out): inside the sequential pass
                 (gdn_fwd_chunked_conv_gated) against the forward followed by
-                gdn_output_gate;
+                gdn_output_gate; and the step's 16 384 tokens as 16 packed
+                sequences of mixed lengths (gdn_fwd_chunked_conv_varlen);
   cpu_baseline  the fp64 oracle on the host cores on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -136,7 +137,7 @@ def main():
 
     import gated_delta_rule_02_amd as gdn
     from gdn_inputs import BATCHED_DECODE, KDA_PREFILL, LONG_PREFILL, PREFILL_CONV, decode_tokens_device, \
-        make_decode_token, make_gate_inputs, make_prefill, make_state, prefill_device, to_torch
+        make_decode_token, make_gate_inputs, make_prefill, make_state, packed_lengths, prefill_device, to_torch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
@@ -273,10 +274,33 @@ def main():
     graph_equal = bool(torch.equal(S, S_eager) and torch.equal(od2, o_eager))
     log("decode as one graph %.1f us/step (final state %s the eager loop's)" %
         (t_dec_graph * 1e6, "equals" if graph_equal else "DIFFERS FROM"))
-    del toks, S, S_init, S_eager, graph
+    # the same steps from raw inputs through the convolution history
+    # (gdn_decode_step_conv: the decode prologue, then the decode step); the
+    # step's tokens serve as the raw inputs
+    cst = torch.zeros((dwl.B, 3, 2 * dwl.Hk * dwl.dk + dwl.Hv * dwl.dv), dtype=torch.bfloat16, device=dev)
+    cws = torch.empty(L.gdn_decode_conv_workspace_bytes(d3), dtype=torch.uint8, device=dev)
+    w_dec = to_torch(np.ascontiguousarray(np.random.default_rng(3).normal(
+        0, 0.5, (2 * dwl.Hk * dwl.dk + dwl.Hv * dwl.dv, 4)), dtype=np.float32), dev)
+
+    def decode_conv_run():
+        for s in range(nsteps):
+            gdn.check(L.gdn_decode_step_conv(ctypes.byref(d3), gdn.BF16, P(tq[s]), P(tk[s]), P(tv[s]), P(w_dec),
+                                             1e-6, P(cst), P(tg[s]), P(tb[s]), P(S), P(od2), P(cws), cws.numel(),
+                                             s_ptr))
+
+    decode_conv_run()
+    S.copy_(S_init)
+    torch.cuda.synchronize()
+    t_dec_conv = time_events(decode_conv_run, 1, stream) / nsteps
+    log("decode from raw inputs (conv history) %.1f us/step" % (t_dec_conv * 1e6))
+    del toks, S, S_init, S_eager, graph, cst, cws
 
     # ------------------------------------------------------------------ other prefill workloads
-    extra = {"prefill_conv_two_calls": {
+    extra = {"decode_from_raw_inputs": {
+        "workload": dwl.name + ", tokens as raw inputs through the 3-token convolution history",
+        "us_per_step": t_dec_conv * 1e6, "steps_per_s": 1 / t_dec_conv,
+        "hbm_frac_algorithmic": bytes_dec / t_dec_conv / 1e9 / PEAK_HBM_GBS},
+        "prefill_conv_two_calls": {
         "workload": wl.name + ", gdn_prologue then gdn_fwd_chunked",
         "us_per_call": (t_pro + t_chk) * 1e6, "tokens_per_s": B * T / (t_pro + t_chk),
         "prologue_us": t_pro * 1e6, "chunked_us": t_chk * 1e6,
@@ -317,6 +341,31 @@ def main():
     log("gated: %.1f us inside the pass; forward + gate %.1f + %.1f us (gate %.0f GB/s)" %
         (t_gated * 1e6, t_fus * 1e6, t_gate * 1e6, bytes_gate / t_gate / 1e9))
     del z, gain, y, gws
+
+    # the step's tokens as packed sequences of mixed lengths (the same inputs,
+    # read as one token axis)
+    lens = packed_lengths(B * T, 16, wl.seed)
+    N = len(lens)
+    log("workload: %d tokens as %d packed sequences, lengths %s" % (B * T, N, lens.tolist()))
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(dev)
+    vdesc = gdn.make_desc(N, B * T, Hk, Hv, dk, dv, C, gdn.F16, gdn.BF16, gdn.GATE_HEAD)
+    vws = torch.empty(L.gdn_fwd_conv_varlen_workspace_bytes(vdesc, gdn.BF16), dtype=torch.uint8, device=dev)
+    vST = torch.empty((N, Hv, dv, dk), dtype=torch.float32, device=dev)
+
+    def varlen():
+        gdn.check(L.gdn_fwd_chunked_conv_varlen(ctypes.byref(vdesc), P(cu), gdn.BF16, P(xq), P(xk), P(xv), P(w),
+                                                1e-6, P(g), P(beta), None, P(o), P(vST), P(vws), vws.numel(),
+                                                s_ptr))
+
+    warm_up(varlen)
+    t_var = time_events(varlen, 20, stream)
+    extra["prefill_conv_varlen"] = {
+        "workload": "%d tokens (16 key / 48 value heads, d 128, C 64, bf16, conv prologue) packed as %d "
+                    "sequences of mixed lengths" % (B * T, N),
+        "lengths": lens.tolist(), "us_per_call": t_var * 1e6, "tokens_per_s": B * T / t_var,
+        "mfma_frac": flops_chk / t_var / 1e12 / PEAK_F16_TFLOPS}
+    log("packed sequences: %.1f us, %.3e tokens/s (longest %d tokens)" % (t_var * 1e6, B * T / t_var, lens.max()))
+    del vws, vST
 
     for key, xwl in (("long_prefill", LONG_PREFILL), ("key_gate_prefill", KDA_PREFILL)):
         log("workload: %s" % xwl.name)

@@ -15,6 +15,8 @@ Entry points (same names as the C functions):
   output_gate(o, z, gain, eps, out_dtype) -> y
   prologue_varlen, fwd_chunked_varlen, fwd_chunked_conv_varlen: packed sequences
       of different lengths (token tensors [1,T,...], cu_seqlens int32 [N+1])
+  conv_state(xq, xk, xv, cu_seqlens=None) -> conv_state [B,3,channels]
+  decode_step_conv(xq, xk, xv, conv_w, conv_state, g, beta, S) -> o   (conv_state, S in place)
   fwd_chunked_conv_gated(xq, xk, xv, conv_w, g, beta, z, gain, S0, ...) -> (y, S_T)
 """
 from __future__ import annotations
@@ -81,6 +83,12 @@ def lib() -> ctypes.CDLL:
         L.gdn_fwd_conv_varlen_workspace_bytes.restype = S
         L.gdn_fwd_chunked_conv_varlen.argtypes = [D, P, I, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, S, P]
         L.gdn_fwd_chunked_conv_varlen.restype = I
+        L.gdn_conv_state.argtypes = [D, P, I, P, P, P, P, P]
+        L.gdn_conv_state.restype = I
+        L.gdn_decode_conv_workspace_bytes.argtypes = [D]
+        L.gdn_decode_conv_workspace_bytes.restype = S
+        L.gdn_decode_step_conv.argtypes = [D, I, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, S, P]
+        L.gdn_decode_step_conv.restype = I
         L.gdn_output_gate.argtypes = [D, P, I, P, P, ctypes.c_float, I, P, P]
         L.gdn_output_gate.restype = I
         L.gdn_fwd_gated_workspace_bytes.argtypes = [D, I, I]
@@ -363,6 +371,52 @@ def fwd_chunked_conv_varlen(xq, xk, xv, conv_w, g, beta, cu_seqlens, S0=None, qk
                                         _ptr(conv_w), float(eps), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
                                         _ptr(S_T), _ptr(ws), ws_bytes, _stream(stream)))
     return o, S_T
+
+
+def conv_state(xq, xk, xv, cu_seqlens=None, stream=None):
+    """The convolution history after each sequence's last token: the raw inputs
+    of its last three tokens (zero before its first), [B,3,2*Hk*dk+Hv*dv] in the
+    raw dtype.  xq, xk [B,T,Hk,dk], xv [B,T,Hv,dv]; or packed sequences
+    ([1,T,...] with cu_seqlens int32 [B+1])."""
+    Bx, T, Hk, dk = xq.shape
+    Hv, dv = xv.shape[2], xv.shape[3]
+    _dev("xq", xq)
+    _dev("xk", xk, xq.shape, (xq.dtype,))
+    _dev("xv", xv, (Bx, T, Hv, dv), (xq.dtype,))
+    B = Bx if cu_seqlens is None else _offsets(cu_seqlens, T)
+    cs = torch.empty((B, 3, 2 * Hk * dk + Hv * dv), dtype=xq.dtype, device=xq.device)
+    d = make_desc(B, T, Hk, Hv, dk, dv, 64, F16, F32, GATE_HEAD)
+    check(lib().gdn_conv_state(ctypes.byref(d), _ptr(cu_seqlens), _DTYPE_CODE[xq.dtype], _ptr(xq), _ptr(xk),
+                               _ptr(xv), _ptr(cs), _stream(stream)))
+    return cs
+
+
+def decode_step_conv(xq, xk, xv, conv_w, conv_st, g, beta, S, qkv_dtype=torch.float16, eps=1e-6, o=None,
+                     stream=None):
+    """One decode step from raw inputs xq, xk [B,Hk,dk], xv [B,Hv,dv] and the
+    convolution history conv_st [B,3,channels] (moved on by one token in place);
+    S updated in place.  Returns o fp32 [B,Hv,dv]."""
+    B, Hk, dk = xq.shape
+    Hv, dv = xv.shape[1], xv.shape[2]
+    _dev("xq", xq)
+    _dev("xk", xk, xq.shape, (xq.dtype,))
+    _dev("xv", xv, (B, Hv, dv), (xq.dtype,))
+    _dev("conv_w", conv_w, (2 * Hk * dk + Hv * dv, 4), (torch.float32,))
+    _dev("conv_state", conv_st, (B, 3, 2 * Hk * dk + Hv * dv), (xq.dtype,))
+    _dev("g", g)
+    gate = GATE_HEAD if tuple(g.shape) == (B, Hv) else GATE_KEY_CHANNEL
+    _dev("beta", beta, (B, Hv), (g.dtype,))
+    _dev("S", S, (B, Hv, dv, dk), (torch.float32,))
+    if o is None:
+        o = torch.empty((B, Hv, dv), dtype=torch.float32, device=xq.device)
+    d = make_desc(B, 1, Hk, Hv, dk, dv, 64, _DTYPE_CODE[qkv_dtype], _DTYPE_CODE[g.dtype], gate)
+    L = lib()
+    ws_bytes = L.gdn_decode_conv_workspace_bytes(ctypes.byref(d))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=xq.device)
+    check(L.gdn_decode_step_conv(ctypes.byref(d), _DTYPE_CODE[xq.dtype], _ptr(xq), _ptr(xk), _ptr(xv),
+                                 _ptr(conv_w), float(eps), _ptr(conv_st), _ptr(g), _ptr(beta), _ptr(S), _ptr(o),
+                                 _ptr(ws), ws_bytes, _stream(stream)))
+    return o
 
 
 def decode_step(q, k, v, g, beta, S, o=None, stream=None):

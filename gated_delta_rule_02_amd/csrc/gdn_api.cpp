@@ -575,6 +575,75 @@ gdn_status gdn_fwd_chunked_conv_gated(const gdn_desc *d, int32_t x_dtype, const 
                   "output gate launch");
 }
 
+size_t gdn_decode_conv_workspace_bytes(const gdn_desc *d) {
+  gdn::Shape sh;
+  const std::string saved = g_last_error;
+  const gdn_status st = check_desc(d, &sh);
+  g_last_error = saved;
+  if (st != GDN_OK) return 0;
+  const size_t qs = dsize(d->qkv_dtype);
+  return 2 * round256((size_t)d->B * d->Hk * d->dk * qs) + round256((size_t)d->B * d->Hv * d->dv * qs);
+}
+
+gdn_status gdn_decode_step_conv(const gdn_desc *d, int32_t x_dtype, const void *xq, const void *xk,
+                                const void *xv, const float *conv_w, float eps, void *conv_state,
+                                const void *g, const void *beta, float *S, float *o, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  gdn::Shape sh;
+  gdn_status st = check_desc(d, &sh);
+  if (st != GDN_OK) return st;
+  if (d->T != 1) return fail(GDN_E_SHAPE, "decode step needs T == 1 (got %d)", d->T);
+  if ((st = check_prologue_args(d, x_dtype, eps)) != GDN_OK) return st;
+  const char *names[] = {"xq", "xk", "xv", "conv_w", "conv_state", "workspace"};
+  const void *ptrs[] = {xq, xk, xv, conv_w, conv_state, workspace};
+  if ((st = check_ptrs(names, ptrs, 6)) != GDN_OK) return st;
+  const size_t need = gdn_decode_conv_workspace_bytes(d);
+  if (workspace_bytes < need)
+    return fail(GDN_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  const size_t xs = dsize(x_dtype), nch = 2 * (size_t)d->Hk * d->dk + (size_t)d->Hv * d->dv;
+  const Range rcs = range(conv_state, (size_t)d->B * 3 * nch * xs), rw = range(workspace, need);
+  const Range ins[] = {range(xq, (size_t)d->B * d->Hk * d->dk * xs), range(xk, (size_t)d->B * d->Hk * d->dk * xs),
+                       range(xv, (size_t)d->B * d->Hv * d->dv * xs), range(conv_w, nch * 16),
+                       range(g, (size_t)d->B * d->Hv * (sh.key_gate ? d->dk : 1) * dsize(d->gate_dtype)),
+                       range(beta, (size_t)d->B * d->Hv * dsize(d->gate_dtype)),
+                       range(S, (size_t)d->B * d->Hv * d->dv * d->dk * 4), range(o, (size_t)d->B * d->Hv * d->dv * 4)};
+  for (const Range &r : ins)
+    if (overlap(rcs, r) || overlap(rw, r))
+      return fail(GDN_E_ARG, "conv_state and the workspace must not overlap another argument");
+  if (overlap(rcs, rw)) return fail(GDN_E_ARG, "conv_state must not overlap the workspace");
+  // q, k, v of the token into the workspace, then the decode step on them
+  const size_t qs = dsize(d->qkv_dtype);
+  char *q = (char *)workspace, *k = q + round256((size_t)d->B * d->Hk * d->dk * qs);
+  char *v = k + round256((size_t)d->B * d->Hk * d->dk * qs);
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = gdn::launch_decode_prologue(xq, xk, xv, (gdn::DType)x_dtype, conv_w, conv_state, q, k, v,
+                                                   sh.qkv, d->B, d->Hk, d->Hv, d->dk, d->dv, eps, s);
+  if (e != hipSuccess) return launched(e, "decode prologue launch");
+  return gdn_decode_step(d, q, k, v, g, beta, S, o, stream);
+}
+
+gdn_status gdn_conv_state(const gdn_desc *d, const int32_t *cu_seqlens, int32_t x_dtype, const void *xq,
+                          const void *xk, const void *xv, void *conv_state, void *stream) {
+  const bool packed = cu_seqlens != nullptr;
+  gdn::Shape sh;
+  gdn_status st = check_desc(d, &sh, packed);
+  if (st != GDN_OK) return st;
+  if ((st = check_prologue_args(d, x_dtype, 0.f)) != GDN_OK) return st;
+  const char *names[] = {"xq", "xk", "xv", "conv_state"};
+  const void *ptrs[] = {xq, xk, xv, conv_state};
+  if ((st = check_ptrs(names, ptrs, 4)) != GDN_OK) return st;
+  if (packed && ((uintptr_t)cu_seqlens & 3u) != 0) return fail(GDN_E_ALIGN, "cu_seqlens is not 4-byte aligned");
+  const size_t xs = dsize(x_dtype), nt = ntok(d, packed);
+  const Range rcs = range(conv_state, (size_t)d->B * 3 * (2 * (size_t)d->Hk * d->dk + (size_t)d->Hv * d->dv) * xs);
+  if (overlap(rcs, range(xq, nt * d->Hk * d->dk * xs)) || overlap(rcs, range(xk, nt * d->Hk * d->dk * xs)) ||
+      overlap(rcs, range(xv, nt * d->Hv * d->dv * xs)) ||
+      (packed && overlap(rcs, range(cu_seqlens, ((size_t)d->B + 1) * 4))))
+    return fail(GDN_E_ARG, "conv_state must not overlap an input");
+  return launched(gdn::launch_conv_state(xq, xk, xv, (gdn::DType)x_dtype, conv_state, d->B, d->T, d->Hk, d->Hv,
+                                         d->dk, d->dv, cu_seqlens, (hipStream_t)stream),
+                  "conv state launch");
+}
+
 gdn_status gdn_decode_step(const gdn_desc *d, const void *q, const void *k, const void *v,
                            const void *g, const void *beta, float *S, float *o, void *stream) {
   gdn::Shape sh;

@@ -39,6 +39,17 @@ hipError_t launch_prologue(const void *xq, const void *xk, const void *xv, DType
                            void *q, void *k, void *v, DType yt, int B, int T, int Hk, int Hv, int dk,
                            int dv, float eps, hipStream_t s, const int *cu = nullptr);
 
+// One token per sequence from raw inputs xq, xk [B,Hk,dk], xv [B,Hv,dv] and
+// the convolution history cs [B][3][2 Hk dk + Hv dv] (raw input type, moved
+// on by one token in place): q, k, v of type yt, as the prologue makes them.
+hipError_t launch_decode_prologue(const void *xq, const void *xk, const void *xv, DType xt, const float *w,
+                                  void *cs, void *q, void *k, void *v, DType yt, int B, int Hk, int Hv,
+                                  int dk, int dv, float eps, hipStream_t s);
+// The convolution history after each sequence's last token (raw inputs of its
+// last three tokens, zero before its first) into cs.
+hipError_t launch_conv_state(const void *xq, const void *xk, const void *xv, DType xt, void *cs, int B,
+                             int T, int Hk, int Hv, int dk, int dv, const int *cu, hipStream_t s);
+
 // One decode step, state in place.
 hipError_t launch_decode(const Shape &sh, const void *q, const void *k, const void *v,
                          const void *g, const void *beta, float *S, float *o, hipStream_t s);

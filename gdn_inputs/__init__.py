@@ -188,6 +188,18 @@ def make_gate_inputs(wl: Workload) -> dict:
     return {"z": z, "gain": gain, "norm_eps": 1e-5}
 
 
+def packed_lengths(total: int, n: int, seed: int) -> np.ndarray:
+    """Lengths of n packed sequences summing to total: a seeded mix of short
+    and long prompts, log-uniform between a quarter and four times the mean
+    length, rescaled to the total, every length at least 1.  int32 [n]."""
+    r = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 99])))
+    mean = total / n
+    raw = np.exp(r.uniform(np.log(mean / 4), np.log(mean * 4), n))
+    lens = np.maximum(1, np.floor(raw / raw.sum() * total)).astype(np.int64)
+    lens[np.argmax(lens)] += total - int(lens.sum())
+    return lens.astype(np.int32)
+
+
 def make_decode_token(wl: Workload, step: int) -> dict:
     """Fresh tokens of decode step `step` (0-based): q, k [B,Hk,dk] unit rows, v [B,Hv,dv] ~ N(0,1),
     beta, g [B,Hv] (or g [B,Hv,dk]).  Seeds [seed, 1 + step, stream]."""

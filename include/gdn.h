@@ -292,6 +292,45 @@ gdn_status gdn_decode_step(const gdn_desc *d, const void *q, const void *k,
                            const void *v, const void *g, const void *beta,
                            float *S, float *o, void *stream);
 
+/*
+ * The convolution history, so that decode continues a prefill with the
+ * convolution prologue ("Source notes", Linear attention, rows deltanet and
+ * kda: causal conv in front of the state update; "Frontier model atlas"
+ * entries 03/08: a four-token causal convolution, so three tokens of
+ * history).  conv_state holds, per sequence, the raw inputs of its last three
+ * tokens, oldest first, for every channel of q | k | v:
+ *     conv_state [B][3][2 Hk dk + Hv dv]  x_dtype, channels in the order of conv_w
+ *
+ * gdn_conv_state -- the history after the last token of each sequence (zero
+ * before a sequence's first token).  With cu_seqlens NULL the raw inputs are
+ * [B,T,...]; otherwise packed sequences as for the _varlen entry points.
+ *   conv_state  device out; must not overlap the inputs
+ * Supported: dk, dv in {16, 32, 64, 128}; x_dtype GDN_BF16 or GDN_F32.
+ */
+gdn_status gdn_conv_state(const gdn_desc *d, const int32_t *cu_seqlens, int32_t x_dtype,
+                          const void *xq, const void *xk, const void *xv, void *conv_state,
+                          void *stream);
+
+/*
+ * gdn_decode_step_conv -- one decode step from raw inputs: q, k, v of the new
+ * token are made exactly as gdn_prologue makes them (the same arithmetic and
+ * rounding to d->qkv_dtype) from conv_state and the token, conv_state moves
+ * on by one token in place, then gdn_decode_step runs on them.
+ *   d->T must be 1.
+ *   xq, xk      device [B,Hk,dk]  x_dtype;  xv device [B,Hv,dv] x_dtype
+ *   conv_w, eps as for gdn_prologue
+ *   conv_state  device in-out [B][3][2 Hk dk + Hv dv] x_dtype
+ *   g, beta, S, o as for gdn_decode_step
+ *   workspace   device scratch of gdn_decode_conv_workspace_bytes(d) bytes
+ *               (q, k, v of the token), 16-byte aligned
+ * Supported: what gdn_prologue and gdn_decode_step support for d.
+ */
+size_t gdn_decode_conv_workspace_bytes(const gdn_desc *d);
+gdn_status gdn_decode_step_conv(const gdn_desc *d, int32_t x_dtype, const void *xq,
+                                const void *xk, const void *xv, const float *conv_w, float eps,
+                                void *conv_state, const void *g, const void *beta, float *S,
+                                float *o, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static text for a status code. */
 const char *gdn_status_str(gdn_status s);
 
