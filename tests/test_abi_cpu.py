@@ -269,3 +269,26 @@ def test_varlen_checks(L):
     assert L.gdn_prologue_varlen(ctypes.byref(d), cu, gdn.BF16, *p[:4], 1e-6, P(cu.value), *p[5:7],
                                  None) == 1              # q written over the offsets
     assert L.gdn_prologue_varlen(ctypes.byref(d), None, gdn.BF16, *p[:4], 1e-6, *p[4:7], None) == 1
+
+
+def test_conv_cache_checks(L):
+    P = ctypes.c_void_p
+    p = [P(FAKE + i * (1 << 36)) for i in range(12)]
+    d = desc(T=1)
+    need = L.gdn_decode_conv_workspace_bytes(ctypes.byref(d))
+    assert need == 2 * 2 * 2 * 128 * 2 + 2 * 6 * 128 * 2   # q, k (B 2, 2 heads) and v (6 heads), bf16
+    # xq, xk, xv, conv_w | conv_state | g, beta, S, o | workspace
+    call = lambda dd, ptrs=p, xt=gdn.BF16, nbytes=need: L.gdn_decode_step_conv(
+        ctypes.byref(dd), xt, *ptrs[:4], 1e-6, ptrs[4], *ptrs[5:9], ptrs[9], nbytes, None)
+    assert call(desc(T=2)) == 2                          # one token per sequence
+    assert call(d, xt=gdn.F16) == 3                      # raw fp16 is not supported
+    assert call(d, nbytes=need - 1) == 5
+    bad = list(p)
+    bad[4] = None
+    assert call(d, bad) == 1                             # conv_state missing
+    bad = list(p)
+    bad[4] = P(p[7].value + 64)                          # conv_state over S
+    assert call(d, bad) == 1
+    assert L.gdn_conv_state(ctypes.byref(desc()), None, gdn.BF16, *p[:3], None, None) == 1
+    assert L.gdn_conv_state(ctypes.byref(desc()), None, gdn.BF16, *p[:3], P(p[1].value + 16), None) == 1
+    assert L.gdn_conv_state(ctypes.byref(desc()), P(p[5].value + 2), gdn.BF16, *p[:3], p[4], None) == 4
