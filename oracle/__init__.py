@@ -5,8 +5,9 @@ baseline leg of ``bench.py`` are the only callers.  The GPU library never
 imports, links or runs anything here, and nothing here imports the GPU
 library.
 
-``gdnref.c`` holds the token-by-token recurrence, the conv/SiLU/L2
-prologue and the gated output norm that follows the state read, compiled with gcc into ``libgdnref.so`` and called through ctypes.
+``gdnref.c`` holds the token-by-token recurrence and its backward (reverse
+mode over the stored state history), the conv/SiLU/L2 prologue and the gated
+output norm that follows the state read, compiled with gcc into ``libgdnref.so`` and called through ctypes.
 ``chunked.py`` holds a second, chunk-parallel formulation in NumPy that is used
 only to pin the recurrence (the two must agree to 1e-10).
 
@@ -53,6 +54,8 @@ def _load():
         lib.gdnref_conv_silu.restype = I
         lib.gdnref_output_gate.argtypes = [ctypes.c_long, I, P, P, P, ctypes.c_double, P]
         lib.gdnref_output_gate.restype = I
+        lib.gdnref_backward.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
+        lib.gdnref_backward.restype = I
         _lib = lib
     return _lib
 
@@ -178,3 +181,29 @@ def output_gate(o, z, gain, eps):
     if rc != 0:
         raise ValueError("gdnref_output_gate rejected its arguments")
     return y
+
+
+def backward(q, k, v, g, beta, S0, dO, dST=None):
+    """Gradients of L = sum <dO, o> + <dST, S_T> with respect to q, k, v, g,
+    beta and S0 (fp64, reverse mode over the stored state history).
+
+    Shapes as for recurrent(); dO [B,T,Hv,dv]; dST [B,Hv,dv,dk] or None; S0
+    [B,Hv,dv,dk] or None.  Returns a dict dq, dk, dv, dg, dbeta, dS0 (float64).
+    """
+    lib = _load()
+    q, k, v, g, beta = (_f32(a) for a in (q, k, v, g, beta))
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    per_channel = 1 if g.ndim == 4 else 0
+    d64 = lambda a: None if a is None else np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    S0, dO, dST = d64(S0), d64(dO), d64(dST)
+    if dO.shape != (B, T, Hv, dv):
+        raise ValueError("dO must be [B,T,Hv,dv]")
+    out = {"dq": np.empty(q.shape), "dk": np.empty(k.shape), "dv": np.empty(v.shape),
+           "dg": np.empty(g.shape), "dbeta": np.empty(beta.shape), "dS0": np.empty((B, Hv, dv, dk))}
+    rc = lib.gdnref_backward(B, T, Hk, Hv, dk, dv, per_channel, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _ptr(S0), _ptr(dO), _ptr(dST), *(_ptr(out[n]) for n in
+                                                             ("dq", "dk", "dv", "dg", "dbeta", "dS0")))
+    if rc != 0:
+        raise ValueError("gdnref_backward rejected its arguments")
+    return out

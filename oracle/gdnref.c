@@ -252,3 +252,139 @@ int gdnref_output_gate(long rows, int d, const double *o, const float *z,
   }
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Backward of the recurrence (first-order, with the state history)         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * gdnref_backward: the gradients of L = sum_t <dO_t, o_t> + <dS_T, S_T> with
+ * respect to every input of gdnref_recurrent, by reverse-mode
+ * differentiation of its steps with the state before every token kept (the
+ * first-order backward with one complete state history that "Source notes",
+ * section "Linear attention", row kda, describes).  Per token t, with
+ * D = alpha S_{t-1} (per-key-channel gate: S_{t-1} diag(alpha)), a = D k,
+ * u = beta (v - a), S_t = D + u k^T, o_t = S_t q, and G the gradient of L
+ * with respect to S_t, in reverse token order:
+ *   G += dO_t q^T;   dq_t = S_t^T dO_t
+ *   du = G k;   dv_t = beta du;   dbeta_t = du . (v - a)
+ *   dk_t = G^T u - beta D^T du
+ *   dD = G - beta du k^T
+ *   dg_t = <dD, D>  (per-key-channel gate: column sums of dD o D)
+ *   G <- alpha dD  (per-key-channel gate: dD diag(alpha)), the gradient for S_{t-1}
+ * and dS0 = G after token 0.  dq and dk of a key head add up over its value
+ * heads.  Inputs as for gdnref_recurrent (S0 double or NULL); dO [B,T,Hv,dv],
+ * dST [B,Hv,dv,dk] or NULL; outputs double: dq, dk [B,T,Hk,dk], dv
+ * [B,T,Hv,dv], dg like g, dbeta [B,T,Hv], dS0 [B,Hv,dv,dk].
+ */
+int gdnref_backward(int B, int T, int Hk, int Hv, int dk, int dv, int per_channel_gate,
+                    const float *q, const float *k, const float *v, const float *g,
+                    const float *beta, const double *S0, const double *dO, const double *dST,
+                    double *dq, double *dkk, double *dvv, double *dg, double *dbeta,
+                    double *dS0) {
+  int b, h, t, i, j;
+  if (B <= 0 || T < 0 || Hk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || Hv % Hk != 0) return -1;
+  if (!q || !k || !v || !g || !beta || !dO || !dq || !dkk || !dvv || !dg || !dbeta || !dS0) return -1;
+  const size_t ss = (size_t)dv * dk;
+  double *hist = (double *)malloc(sizeof(double) * ss * ((size_t)T + 1));
+  double *G = (double *)malloc(sizeof(double) * ss);
+  double *D = (double *)malloc(sizeof(double) * ss);
+  double *St = (double *)malloc(sizeof(double) * ss);
+  double *u = (double *)malloc(sizeof(double) * dv);
+  double *a = (double *)malloc(sizeof(double) * dv);
+  double *du = (double *)malloc(sizeof(double) * dv);
+  double *al = (double *)malloc(sizeof(double) * dk);
+  if (!hist || !G || !D || !St || !u || !a || !du || !al) {
+    free(hist); free(G); free(D); free(St); free(u); free(a); free(du); free(al);
+    return -2;
+  }
+  memset(dq, 0, sizeof(double) * (size_t)B * T * Hk * dk);
+  memset(dkk, 0, sizeof(double) * (size_t)B * T * Hk * dk);
+  for (b = 0; b < B; ++b)
+    for (h = 0; h < Hv; ++h) {
+      const int kh = h / (Hv / Hk);
+      /* forward: hist[t] = the state before token t */
+      if (S0) memcpy(hist, S0 + ((size_t)b * Hv + h) * ss, sizeof(double) * ss);
+      else memset(hist, 0, sizeof(double) * ss);
+      for (t = 0; t < T; ++t) {
+        const size_t bt = (size_t)b * T + t;
+        const float *kt = k + (bt * Hk + kh) * dk;
+        const float *vt = v + (bt * Hv + h) * dv;
+        const double bet = (double)beta[bt * Hv + h];
+        const double *P = hist + (size_t)t * ss;
+        double *N = hist + (size_t)(t + 1) * ss;
+        for (j = 0; j < dk; ++j)
+          al[j] = exp((double)(per_channel_gate ? g[(bt * Hv + h) * dk + j] : g[bt * Hv + h]));
+        for (i = 0; i < dv; ++i) {
+          double p = 0.0;
+          for (j = 0; j < dk; ++j) p += P[(size_t)i * dk + j] * al[j] * (double)kt[j];
+          const double uu = bet * ((double)vt[i] - p);
+          for (j = 0; j < dk; ++j) N[(size_t)i * dk + j] = P[(size_t)i * dk + j] * al[j] + uu * (double)kt[j];
+        }
+      }
+      /* backward */
+      if (dST) memcpy(G, dST + ((size_t)b * Hv + h) * ss, sizeof(double) * ss);
+      else memset(G, 0, sizeof(double) * ss);
+      for (t = T - 1; t >= 0; --t) {
+        const size_t bt = (size_t)b * T + t;
+        const float *qt = q + (bt * Hk + kh) * dk;
+        const float *kt = k + (bt * Hk + kh) * dk;
+        const float *vt = v + (bt * Hv + h) * dv;
+        const double *dOt = dO + (bt * Hv + h) * dv;
+        const double bet = (double)beta[bt * Hv + h];
+        const double *P = hist + (size_t)t * ss;
+        for (j = 0; j < dk; ++j)
+          al[j] = exp((double)(per_channel_gate ? g[(bt * Hv + h) * dk + j] : g[bt * Hv + h]));
+        for (i = 0; i < dv; ++i) {
+          double p = 0.0;
+          for (j = 0; j < dk; ++j) {
+            D[(size_t)i * dk + j] = P[(size_t)i * dk + j] * al[j];
+            p += D[(size_t)i * dk + j] * (double)kt[j];
+          }
+          a[i] = p;
+          u[i] = bet * ((double)vt[i] - p);
+          for (j = 0; j < dk; ++j) St[(size_t)i * dk + j] = D[(size_t)i * dk + j] + u[i] * (double)kt[j];
+        }
+        /* o_t = S_t q */
+        for (i = 0; i < dv; ++i)
+          for (j = 0; j < dk; ++j) G[(size_t)i * dk + j] += dOt[i] * (double)qt[j];
+        double *dqt = dq + (bt * Hk + kh) * dk, *dkt = dkk + (bt * Hk + kh) * dk;
+        for (j = 0; j < dk; ++j) {
+          double s = 0.0;
+          for (i = 0; i < dv; ++i) s += St[(size_t)i * dk + j] * dOt[i];
+          dqt[j] += s;
+        }
+        /* S_t = D + u k^T, u = beta (v - D k) */
+        double db = 0.0;
+        for (i = 0; i < dv; ++i) {
+          double s = 0.0;
+          for (j = 0; j < dk; ++j) s += G[(size_t)i * dk + j] * (double)kt[j];
+          du[i] = s;
+          dvv[(bt * Hv + h) * dv + i] = bet * s;
+          db += s * ((double)vt[i] - a[i]);
+        }
+        dbeta[bt * Hv + h] = db;
+        for (j = 0; j < dk; ++j) {
+          double s = 0.0;
+          for (i = 0; i < dv; ++i) s += G[(size_t)i * dk + j] * u[i] - bet * du[i] * D[(size_t)i * dk + j];
+          dkt[j] += s;
+        }
+        /* dD, the decay's gradient, then the gradient for S_{t-1} */
+        double dgh = 0.0;
+        for (j = 0; j < dk; ++j) {
+          double colsum = 0.0;
+          for (i = 0; i < dv; ++i) {
+            const double dd = G[(size_t)i * dk + j] - bet * du[i] * (double)kt[j];
+            colsum += dd * D[(size_t)i * dk + j];
+            G[(size_t)i * dk + j] = dd * al[j];
+          }
+          if (per_channel_gate) dg[(bt * Hv + h) * dk + j] = colsum;
+          else dgh += colsum;
+        }
+        if (!per_channel_gate) dg[bt * Hv + h] = dgh;
+      }
+      memcpy(dS0 + ((size_t)b * Hv + h) * ss, G, sizeof(double) * ss);
+    }
+  free(hist); free(G); free(D); free(St); free(u); free(a); free(du); free(al);
+  return 0;
+}

@@ -374,3 +374,49 @@ def test_output_gate_rejects_bad_shapes():
         oracle.output_gate(o, z[..., :-1], gain, 1e-5)
     with pytest.raises(ValueError):
         oracle.output_gate(o, z, gain[:-1], 1e-5)
+
+
+# --------------------------------------------------------------------------
+# Backward: central finite differences of the forward oracle, every input
+# --------------------------------------------------------------------------
+def _loss(q, k, v, g, beta, S0, dO, dST):
+    o, ST = oracle.recurrent_full(q, k, v, g, beta, S0)
+    return float(np.sum(o * dO) + np.sum(ST * dST))
+
+
+@pytest.mark.parametrize("gate", ["head", "key"])
+def test_backward_matches_finite_differences(gate):
+    # grouped heads (2 value heads per key head), S0 given, dS_T given
+    q, k, v, g, beta, S0 = rand_problem(31, B=1, T=5, Hk=1, Hv=2, dk=3, dv=2, gate=gate)
+    r = np.random.default_rng(32)
+    dO = r.standard_normal(v.shape)
+    dST = r.standard_normal(S0.shape)
+    grads = oracle.backward(q, k, v, g, beta, S0, dO, dST)
+    inputs = {"q": q, "k": k, "v": v, "g": g, "beta": beta, "S0": S0}
+    for name, x in inputs.items():
+        fd = np.zeros(x.shape)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            if name == "S0":        # the oracle takes S0 in double
+                xp[idx] += 1e-4
+                xm[idx] -= 1e-4
+            else:                   # the others in float32: use the stored values' actual step
+                xp[idx] = np.float32(x[idx] + 1e-3)
+                xm[idx] = np.float32(x[idx] - 1e-3)
+            args = dict(inputs)
+            args[name] = xp
+            lp = _loss(args["q"], args["k"], args["v"], args["g"], args["beta"], args["S0"], dO, dST)
+            args[name] = xm
+            lm = _loss(args["q"], args["k"], args["v"], args["g"], args["beta"], args["S0"], dO, dST)
+            fd[idx] = (lp - lm) / (xp[idx] - xm[idx])
+        np.testing.assert_allclose(grads["d" + name], fd, rtol=2e-5, atol=2e-6, err_msg=name)
+
+
+def test_backward_without_state_gradients():
+    # S0 absent and dS_T absent: the same as zeros
+    q, k, v, g, beta, S0 = rand_problem(33, B=2, T=4, Hk=1, Hv=1, dk=4, dv=3, s0=False)
+    dO = np.random.default_rng(34).standard_normal(v.shape)
+    a = oracle.backward(q, k, v, g, beta, None, dO, None)
+    b = oracle.backward(q, k, v, g, beta, np.zeros((2, 1, 3, 4)), dO, np.zeros((2, 1, 3, 4)))
+    for n in a:
+        np.testing.assert_array_equal(a[n], b[n])
