@@ -17,6 +17,7 @@ Entry points (same names as the C functions):
       of different lengths (token tensors [1,T,...], cu_seqlens int32 [N+1])
   conv_state(xq, xk, xv, cu_seqlens=None) -> conv_state [B,3,channels]
   decode_step_conv(xq, xk, xv, conv_w, conv_state, g, beta, S) -> o   (conv_state, S in place)
+  bwd(q, k, v, g, beta, S0, dO, dS_T) -> dict of dq, dk, dv, dg, dbeta, dS0 (fp32)
   fwd_chunked_conv_gated(xq, xk, xv, conv_w, g, beta, z, gain, S0, ...) -> (y, S_T)
 """
 from __future__ import annotations
@@ -89,6 +90,10 @@ def lib() -> ctypes.CDLL:
         L.gdn_decode_conv_workspace_bytes.restype = S
         L.gdn_decode_step_conv.argtypes = [D, I, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, S, P]
         L.gdn_decode_step_conv.restype = I
+        L.gdn_bwd_workspace_bytes.argtypes = [D]
+        L.gdn_bwd_workspace_bytes.restype = S
+        L.gdn_bwd.argtypes = [D] + [P] * 15 + [S, P]
+        L.gdn_bwd.restype = I
         L.gdn_output_gate.argtypes = [D, P, I, P, P, ctypes.c_float, I, P, P]
         L.gdn_output_gate.restype = I
         L.gdn_fwd_gated_workspace_bytes.argtypes = [D, I, I]
@@ -417,6 +422,33 @@ def decode_step_conv(xq, xk, xv, conv_w, conv_st, g, beta, S, qkv_dtype=torch.fl
                                  _ptr(conv_w), float(eps), _ptr(conv_st), _ptr(g), _ptr(beta), _ptr(S), _ptr(o),
                                  _ptr(ws), ws_bytes, _stream(stream)))
     return o
+
+
+def bwd(q, k, v, g, beta, S0, dO, dS_T=None, stream=None):
+    """Gradients of sum <dO, o> + <dS_T, S_T> with respect to q, k, v, g, beta,
+    S0 (fp32).  Shapes as for fwd_chunked; dO fp32 [B,T,Hv,dv]."""
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    _dev("q", q)
+    _dev("k", k, q.shape, (q.dtype,))
+    _dev("v", v, (B, T, Hv, dv), (q.dtype,))
+    gate = _gate_kind(_dev("g", g), B, T, Hv, dk)
+    _dev("beta", beta, (B, T, Hv), (g.dtype,))
+    _dev("dO", dO, (B, T, Hv, dv), (torch.float32,))
+    for n, x in (("S0", S0), ("dS_T", dS_T)):
+        if x is not None:
+            _dev(n, x, (B, Hv, dv, dk), (torch.float32,))
+    f = lambda shape: torch.empty(shape, dtype=torch.float32, device=q.device)
+    out = {"dq": f(q.shape), "dk": f(q.shape), "dv": f(v.shape), "dg": f(g.shape), "dbeta": f(beta.shape),
+           "dS0": f((B, Hv, dv, dk))}
+    d = make_desc(B, T, Hk, Hv, dk, dv, 64, _DTYPE_CODE[q.dtype], _DTYPE_CODE[g.dtype], gate)
+    L = lib()
+    ws_bytes = L.gdn_bwd_workspace_bytes(ctypes.byref(d))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    check(L.gdn_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(dO),
+                    _ptr(dS_T), *(_ptr(out[n]) for n in ("dq", "dk", "dv", "dg", "dbeta", "dS0")), _ptr(ws),
+                    ws_bytes, _stream(stream)))
+    return out
 
 
 def decode_step(q, k, v, g, beta, S, o=None, stream=None):

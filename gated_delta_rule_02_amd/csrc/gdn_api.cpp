@@ -575,6 +575,63 @@ gdn_status gdn_fwd_chunked_conv_gated(const gdn_desc *d, int32_t x_dtype, const 
                   "output gate launch");
 }
 
+namespace {
+// What the backward checks about the sizes and dtypes of d.
+gdn_status check_bwd(const gdn_desc *d, gdn::Shape *sh) {
+  gdn_status st = check_desc(d, sh);
+  if (st != GDN_OK) return st;
+  if (d->dk != 32 && d->dk != 64 && d->dk != 128)
+    return fail(GDN_E_UNSUPPORTED, "the backward supports dk in {32,64,128} (got %d)", d->dk);
+  if (d->dv % 32 != 0 || d->dv > 1024)
+    return fail(GDN_E_UNSUPPORTED, "the backward supports dv a multiple of 32, <= 1024 (got %d)", d->dv);
+  if (d->gate_dtype == GDN_F16) return fail(GDN_E_UNSUPPORTED, "the backward's gates must be fp32 or bf16");
+  return GDN_OK;
+}
+}  // namespace
+
+size_t gdn_bwd_workspace_bytes(const gdn_desc *d) {
+  gdn::Shape sh;
+  const std::string saved = g_last_error;
+  const gdn_status st = check_bwd(d, &sh);
+  g_last_error = saved;
+  return st == GDN_OK ? gdn::backward_workspace(sh) : 0;
+}
+
+gdn_status gdn_bwd(const gdn_desc *d, const void *q, const void *k, const void *v, const void *g,
+                   const void *beta, const float *S0, const float *dO, const float *dS_T, float *dq,
+                   float *dk, float *dv, float *dg, float *dbeta, float *dS0, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+  gdn::Shape sh;
+  gdn_status st = check_bwd(d, &sh);
+  if (st != GDN_OK) return st;
+  const char *names[] = {"q", "k", "v", "g", "beta", "dO", "dq", "dk", "dv", "dg", "dbeta", "dS0", "workspace"};
+  const void *ptrs[] = {q, k, v, g, beta, dO, dq, dk, dv, dg, dbeta, dS0, workspace};
+  if ((st = check_ptrs(names, ptrs, 13)) != GDN_OK) return st;
+  if ((S0 && !aligned16(S0)) || (dS_T && !aligned16(dS_T)))
+    return fail(GDN_E_ALIGN, "S0 and dS_T must be 16-byte aligned");
+  const size_t need = gdn::backward_workspace(sh);
+  if (workspace_bytes < need)
+    return fail(GDN_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  const size_t bt = (size_t)d->B * d->T, qs = dsize(d->qkv_dtype), gs = dsize(d->gate_dtype);
+  const size_t gdim = sh.key_gate ? d->dk : 1, sb = (size_t)d->B * d->Hv * d->dv * d->dk * 4;
+  const Range ins[] = {range(q, bt * d->Hk * d->dk * qs), range(k, bt * d->Hk * d->dk * qs),
+                       range(v, bt * d->Hv * d->dv * qs), range(g, bt * d->Hv * gdim * gs),
+                       range(beta, bt * d->Hv * gs), range(S0, S0 ? sb : 0), range(dO, bt * d->Hv * d->dv * 4),
+                       range(dS_T, dS_T ? sb : 0)};
+  const Range outs[] = {range(dq, bt * d->Hk * d->dk * 4), range(dk, bt * d->Hk * d->dk * 4),
+                        range(dv, bt * d->Hv * d->dv * 4), range(dg, bt * d->Hv * gdim * 4),
+                        range(dbeta, bt * d->Hv * 4), range(dS0, sb), range(workspace, need)};
+  for (int i = 0; i < 7; ++i) {
+    for (const Range &r : ins)
+      if (overlap(outs[i], r)) return fail(GDN_E_ARG, "outputs and workspace must not overlap the inputs");
+    for (int j = 0; j < i; ++j)
+      if (overlap(outs[i], outs[j])) return fail(GDN_E_ARG, "outputs and workspace must not overlap each other");
+  }
+  return launched(gdn::launch_backward(sh, q, k, v, g, beta, S0, dO, dS_T, dq, dk, dv, dg, dbeta, dS0, workspace,
+                                       (hipStream_t)stream),
+                  "backward launch");
+}
+
 size_t gdn_decode_conv_workspace_bytes(const gdn_desc *d) {
   gdn::Shape sh;
   const std::string saved = g_last_error;

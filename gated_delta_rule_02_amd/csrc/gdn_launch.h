@@ -82,6 +82,14 @@ size_t chunk_mfma_conv_workspace(const Shape &sh);
 hipError_t launch_output_gate(const float *o, const void *z, DType zt, const float *gain, float eps,
                               void *y, DType yt, long rows, int dv, hipStream_t s);
 
+// Backward of the recurrence with one complete state history: dq, dk, dv,
+// dg, dbeta, dS0 (fp32) from dO [B,T,Hv,dv] and dST (or null).  ws holds
+// backward_workspace(sh) bytes.  dk in {32, 64, 128}, dv a multiple of 32.
+size_t backward_workspace(const Shape &sh);
+hipError_t launch_backward(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
+                           const void *beta, const float *S0, const float *dO, const float *dST, float *dq,
+                           float *dk, float *dv, float *dg, float *dbeta, float *dS0, void *ws, hipStream_t st);
+
 // Internal chunk length the fp32 kernels use for a requested chunk and dk.
 int chunk_f32_internal(int chunk, int dk);
 

@@ -331,6 +331,33 @@ gdn_status gdn_decode_step_conv(const gdn_desc *d, int32_t x_dtype, const void *
                                 void *conv_state, const void *g, const void *beta, float *S,
                                 float *o, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * gdn_bwd -- the backward of the recurrence: the gradients of
+ * L = sum_t <dO_t, o_t> + <dS_T, S_T> with respect to q, k, v, g, beta and S0,
+ * by the first-order backward that keeps one complete state history
+ * ("Source notes", Linear attention, row kda).  The forward recurrence is run
+ * again to store the state before every token (fp32, in the workspace), then
+ * the tokens are run backwards; all arithmetic is fp32.
+ *   q, k, v, g, beta, S0   the forward's inputs, as for gdn_fwd_chunked (S0 NULL: zeros)
+ *   dO     device fp32 [B,T,Hv,dv]: the gradient of o
+ *   dS_T   device fp32 [B,Hv,dv,dk] or NULL (zeros): the gradient of S_T
+ *   dq, dk device out fp32 [B,T,Hk,dk] (summed over the value heads of a key head)
+ *   dv     device out fp32 [B,T,Hv,dv]
+ *   dg     device out fp32, g's shape ([B,T,Hv] or [B,T,Hv,dk]), the gradient of g = ln alpha
+ *   dbeta  device out fp32 [B,T,Hv]
+ *   dS0    device out fp32 [B,Hv,dv,dk]
+ *   workspace   device scratch of gdn_bwd_workspace_bytes(d) bytes (the state
+ *               history, B Hv T dv dk fp32, and partial sums), 16-byte aligned
+ * Outputs and workspace must not overlap each other or the inputs.
+ * Supported: dk in {32, 64, 128}; dv a multiple of 32, <= 1024; q, k, v fp32,
+ * bf16 or fp16; g and beta fp32 or bf16; either gate; d->chunk is not used.
+ */
+size_t gdn_bwd_workspace_bytes(const gdn_desc *d);
+gdn_status gdn_bwd(const gdn_desc *d, const void *q, const void *k, const void *v, const void *g,
+                   const void *beta, const float *S0, const float *dO, const float *dS_T, float *dq,
+                   float *dk, float *dv, float *dg, float *dbeta, float *dS0, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
 /* Static text for a status code. */
 const char *gdn_status_str(gdn_status s);
 
