@@ -23,8 +23,10 @@ kernels run on):
                 and the step's prefill followed by the gated output norm (RMS
                 norm x gain x SiLU gate, bf16 out): inside the sequential pass
                 (gdn_fwd_chunked_conv_gated) against the forward followed by
-                gdn_output_gate; and the step's 16 384 tokens as 16 packed
-                sequences of mixed lengths (gdn_fwd_chunked_conv_varlen);
+                gdn_output_gate; the step's 16 384 tokens as 16 packed
+                sequences of mixed lengths (gdn_fwd_chunked_conv_varlen); and
+                the backward of the step's prefill (gdn_bwd, state history in
+                the workspace);
   cpu_baseline  the fp64 oracle on the host cores on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -366,6 +368,35 @@ def main():
         "mfma_frac": flops_chk / t_var / 1e12 / PEAK_F16_TFLOPS}
     log("packed sequences: %.1f us, %.3e tokens/s (longest %d tokens)" % (t_var * 1e6, B * T / t_var, lens.max()))
     del vws, vST
+
+    # the backward of the step's prefill: q, k, v as the prologue makes them,
+    # a random dO, the state history (B Hv T dv dk fp32) in the workspace
+    log("workload: backward of the prefill (state history %.1f GB)" % (B * Hv * T * dv * dk * 4 / 1e9))
+    prologue()
+    dO = torch.randn((B, T, Hv, dv), device=dev)
+    pdesc_bwd = gdn.make_desc(B, T, Hk, Hv, dk, dv, C, gdn.F16, gdn.BF16, gdn.GATE_HEAD)
+    bws = torch.empty(L.gdn_bwd_workspace_bytes(pdesc_bwd), dtype=torch.uint8, device=dev)
+    grads = [torch.empty_like(x, dtype=torch.float32) for x in (q, k, v, g, beta)] + [torch.empty_like(ST)]
+
+    def backward():
+        gdn.check(L.gdn_bwd(ctypes.byref(pdesc_bwd), P(q), P(k), P(v), P(g), P(beta), None, P(dO), None,
+                            *(P(x) for x in grads), P(bws), bws.numel(), s_ptr))
+
+    backward()
+    torch.cuda.synchronize()
+    t_bwd = time_events(backward, 3, stream)
+    hist_bytes = B * Hv * T * dv * dk * 4
+    io_bytes = 2 * ((2 * B * T * Hk * dk + B * T * Hv * dv) * 2 + 2 * B * T * Hv * 2) + B * T * Hv * dv * 4 \
+        + (2 * B * T * Hk * dk + B * T * Hv * dv + 2 * B * T * Hv) * 4 + B * Hv * dv * dk * 4
+    extra["backward"] = {
+        "workload": wl.name + ", backward (dq, dk, dv, dg, dbeta, dS0 fp32) from a random dO",
+        "us_per_call": t_bwd * 1e6, "tokens_per_s": B * T / t_bwd,
+        "hbm_gbs": (2 * hist_bytes + io_bytes) / t_bwd / 1e9,
+        "hbm_frac": (2 * hist_bytes + io_bytes) / t_bwd / 1e9 / PEAK_HBM_GBS,
+        "bytes": 2 * hist_bytes + io_bytes}
+    log("backward: %.2f ms, %.3e tokens/s, %.0f GB/s (history written and read once)" %
+        (t_bwd * 1e3, B * T / t_bwd, (2 * hist_bytes + io_bytes) / t_bwd / 1e9))
+    del bws, grads, dO
 
     for key, xwl in (("long_prefill", LONG_PREFILL), ("key_gate_prefill", KDA_PREFILL)):
         log("workload: %s" % xwl.name)

@@ -292,3 +292,29 @@ def test_conv_cache_checks(L):
     assert L.gdn_conv_state(ctypes.byref(desc()), None, gdn.BF16, *p[:3], None, None) == 1
     assert L.gdn_conv_state(ctypes.byref(desc()), None, gdn.BF16, *p[:3], P(p[1].value + 16), None) == 1
     assert L.gdn_conv_state(ctypes.byref(desc()), P(p[5].value + 2), gdn.BF16, *p[:3], p[4], None) == 4
+
+
+def test_bwd_checks(L):
+    P = ctypes.c_void_p
+    p = [P(FAKE + i * (1 << 36)) for i in range(16)]
+    d = desc(qkv_dtype=gdn.F32, gate_dtype=gdn.F32)
+    need = L.gdn_bwd_workspace_bytes(ctypes.byref(d))
+    # the state history (B Hv T dv dk fp32, 256-byte rounded), then partial sums
+    hist = 2 * 6 * 100 * 128 * 128 * 4
+    assert need == (hist + 255) // 256 * 256 + 2 * 6 * 4 * 100 * (2 * 128 + 2) * 4
+    assert L.gdn_bwd_workspace_bytes(ctypes.byref(desc(dk=16))) == 0
+    assert L.gdn_bwd_workspace_bytes(ctypes.byref(desc(dv=48))) == 0
+    # q, k, v, g, beta | S0 | dO | dS_T | dq, dk, dv, dg, dbeta, dS0 | workspace
+    call = lambda dd, ptrs=p, nbytes=need: L.gdn_bwd(ctypes.byref(dd), *ptrs[:5], None, ptrs[6], None,
+                                                     *ptrs[8:14], ptrs[14], nbytes, None)
+    assert call(desc(gate_dtype=gdn.F16)) == 3
+    assert call(d, nbytes=need - 1) == 5
+    bad = list(p)
+    bad[8] = None
+    assert call(d, bad) == 1                             # dq missing
+    bad = list(p)
+    bad[10] = P(p[2].value + 64)                         # dv over v
+    assert call(d, bad) == 1
+    bad = list(p)
+    bad[14] = P(p[13].value + 4096)                      # workspace over dS0
+    assert call(d, bad) == 1
