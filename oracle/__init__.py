@@ -68,7 +68,7 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def recurrent(q, k, v, g, beta, S0=None, chains=None, nthreads=None):
+def recurrent(q, k, v, g, beta, S0=None, chains=None, nthreads=None, delta=True):
     """Token-by-token fp64 recurrence.
 
     q, k: [B,T,Hk,dk]; v: [B,T,Hv,dv]; g: [B,T,Hv] (per-head decay) or
@@ -78,6 +78,7 @@ def recurrent(q, k, v, g, beta, S0=None, chains=None, nthreads=None):
     arrays holding bf16/fp16/fp32 values).
 
     chains: list of (b, h) pairs to run (default: all, in b-major order).
+    delta=False: the update without the delta correction, S <- decay(S) + beta v k^T.
     Returns (o [n,T,dv] float64, S_T [n,dv,dk] float64) for the chains in order.
     """
     lib = _load()
@@ -111,7 +112,7 @@ def recurrent(q, k, v, g, beta, S0=None, chains=None, nthreads=None):
     if nthreads is None:
         # one GPU's share of the host: OMP_NUM_THREADS when set, at most 16
         nthreads = min(int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1), 16)
-    rc = lib.gdnref_recurrent(B, T, Hk, Hv, dk, dv, per_channel, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+    rc = lib.gdnref_recurrent(B, T, Hk, Hv, dk, dv, per_channel | (0 if delta else 2), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                               _ptr(beta), _ptr(S0), s0_double, n, _ptr(sb), _ptr(sh), _ptr(o), _ptr(ST),
                               int(nthreads))
     if rc != 0:
@@ -119,12 +120,12 @@ def recurrent(q, k, v, g, beta, S0=None, chains=None, nthreads=None):
     return o, ST
 
 
-def recurrent_full(q, k, v, g, beta, S0=None, nthreads=None):
+def recurrent_full(q, k, v, g, beta, S0=None, nthreads=None, delta=True):
     """All chains; returns o [B,T,Hv,dv] and S_T [B,Hv,dv,dk] (float64)."""
     B, T = q.shape[:2]
     Hv, dv = v.shape[2], v.shape[3]
     dk = q.shape[3]
-    o, ST = recurrent(q, k, v, g, beta, S0, None, nthreads)
+    o, ST = recurrent(q, k, v, g, beta, S0, None, nthreads, delta)
     return (o.reshape(B, Hv, T, dv).transpose(0, 2, 1, 3).copy(), ST.reshape(B, Hv, dv, dk))
 
 

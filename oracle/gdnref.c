@@ -51,7 +51,7 @@
 /* ------------------------------------------------------------------------ */
 
 typedef struct {
-  int B, T, Hk, Hv, dk, dv, per_channel_gate;
+  int B, T, Hk, Hv, dk, dv, per_channel_gate, no_delta;
   const float *q, *k, *v, *g, *beta, *S0;
   const double *S0d; /* used instead of S0 when set */
   int nsel;
@@ -97,11 +97,14 @@ static void rec_chain(const rec_job *J, int n, double *S) {
       for (i = 0; i < dv * dk; ++i) S[i] *= a;
     }
 
-    /* delta update: S <- S + beta (v - S k) k^T */
+    /* delta update: S <- S + beta (v - S k) k^T; without the delta
+       correction ("SinkProbe" page, hybrid_nodelta; "Source notes", gla
+       row): S <- S + beta v k^T */
     for (i = 0; i < dv; ++i) {
       double *row = S + (size_t)i * dk;
       double p = 0.0;
-      for (j = 0; j < dk; ++j) p += row[j] * (double)kt[j];
+      if (!J->no_delta)
+        for (j = 0; j < dk; ++j) p += row[j] * (double)kt[j];
       const double u = beta * ((double)vt[i] - p);
       for (j = 0; j < dk; ++j) row[j] += u * (double)kt[j];
     }
@@ -136,7 +139,8 @@ static void *rec_worker(void *arg) {
  * gdnref_recurrent: token-by-token recurrence for the selected chains.
  *
  *   q, k  [B,T,Hk,dk]   v [B,T,Hv,dv]
- *   g     [B,T,Hv] (per_channel_gate = 0) or [B,T,Hv,dk] (= 1), natural log
+ *   g     [B,T,Hv] (bit 0 of gate_flags clear) or [B,T,Hv,dk] (set), natural log;
+ *         bit 1 of gate_flags set: the update without the delta correction
  *   beta  [B,T,Hv]
  *   S0    [B,Hv,dv,dk] or NULL (zeros); float, or double when s0_double
  *   sel_b, sel_h [nsel]: the (batch, value head) chains to run
@@ -146,7 +150,7 @@ static void *rec_worker(void *arg) {
  * argument.
  */
 int gdnref_recurrent(int B, int T, int Hk, int Hv, int dk, int dv,
-                     int per_channel_gate, const float *q, const float *k,
+                     int gate_flags, const float *q, const float *k,
                      const float *v, const float *g, const float *beta,
                      const void *S0, int s0_double, int nsel, const int *sel_b,
                      const int *sel_h, double *o, double *S_T, int nthreads) {
@@ -159,7 +163,8 @@ int gdnref_recurrent(int B, int T, int Hk, int Hv, int dk, int dv,
       return -1;
   rec_job J;
   J.B = B; J.T = T; J.Hk = Hk; J.Hv = Hv; J.dk = dk; J.dv = dv;
-  J.per_channel_gate = per_channel_gate;
+  J.per_channel_gate = gate_flags & 1;
+  J.no_delta = (gate_flags >> 1) & 1;
   J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta;
   J.S0 = s0_double ? NULL : (const float *)S0;
   J.S0d = s0_double ? (const double *)S0 : NULL;

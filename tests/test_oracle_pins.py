@@ -420,3 +420,40 @@ def test_backward_without_state_gradients():
     b = oracle.backward(q, k, v, g, beta, np.zeros((2, 1, 3, 4)), dO, np.zeros((2, 1, 3, 4)))
     for n in a:
         np.testing.assert_array_equal(a[n], b[n])
+
+
+# --------------------------------------------------------------------------
+# Without the delta correction: a plain decayed sum of outer products
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("gate", ["head", "key"])
+def test_no_delta_is_decayed_sum(gate):
+    q, k, v, g, beta, S0 = rand_problem(41, B=2, T=9, Hk=1, Hv=2, dk=4, dv=3, gate=gate)
+    o, ST = oracle.recurrent_full(q, k, v, g, beta, S0, delta=False)
+    B, T, Hv, dv = v.shape
+    dk = q.shape[3]
+    for b in range(B):
+        for h in range(Hv):
+            for t in range(T):
+                # S_t = S0 decayed by every alpha up to t, plus each write decayed by the alphas after it
+                dec = lambda a, z: np.exp(np.sum(g[b, a:z, h], axis=0))   # scalar or [dk]
+                S = S0[b, h] * dec(0, t + 1)
+                for s in range(t + 1):
+                    S = S + beta[b, s, h] * np.outer(v[b, s, h], k[b, s, 0] * dec(s + 1, t + 1))
+                np.testing.assert_allclose(o[b, t, h], S @ q[b, t, 0], rtol=1e-12, atol=1e-13)
+                if t == T - 1:
+                    np.testing.assert_allclose(ST[b, h], S, rtol=1e-12, atol=1e-13)
+
+
+def test_no_delta_accumulates_where_delta_overwrites():
+    # alpha = 1, beta = 1, one key written twice: the delta rule keeps the
+    # second value, the rule without the correction keeps the sum
+    k = np.zeros((1, 2, 1, 4))
+    k[0, :, 0, 1] = 1.0
+    q = k.copy()
+    v = np.array([[[[1.0, 2.0]], [[10.0, -3.0]]]])
+    g = np.zeros((1, 2, 1))
+    beta = np.ones((1, 2, 1))
+    o_d, _ = oracle.recurrent_full(q, k, v, g, beta)
+    o_n, _ = oracle.recurrent_full(q, k, v, g, beta, delta=False)
+    np.testing.assert_array_equal(o_d[0, 1, 0], [10.0, -3.0])
+    np.testing.assert_array_equal(o_n[0, 1, 0], [11.0, -1.0])
