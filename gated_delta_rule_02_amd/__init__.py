@@ -42,7 +42,7 @@ _DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 
 class GdnDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("B", "T", "Hk", "Hv", "dk", "dv", "chunk", "qkv_dtype", "gate_dtype", "gate")]
+                ("B", "T", "Hk", "Hv", "dk", "dv", "chunk", "qkv_dtype", "gate_dtype", "gate", "rule")]
 
 
 class GdnError(RuntimeError):
@@ -146,8 +146,11 @@ def _dev(name, t, shape=None, dtypes=None):
     return t
 
 
-def make_desc(B, T, Hk, Hv, dk, dv, chunk, qkv_dtype, gate_dtype, gate) -> GdnDesc:
-    return GdnDesc(B, T, Hk, Hv, dk, dv, chunk, qkv_dtype, gate_dtype, gate)
+RULE_DELTA, RULE_NO_DELTA = 0, 1
+
+
+def make_desc(B, T, Hk, Hv, dk, dv, chunk, qkv_dtype, gate_dtype, gate, rule=RULE_DELTA) -> GdnDesc:
+    return GdnDesc(B, T, Hk, Hv, dk, dv, chunk, qkv_dtype, gate_dtype, gate, rule)
 
 
 def prologue(xq, xk, xv, conv_w, out_dtype=torch.float16, eps=1e-6, stream=None):
@@ -179,10 +182,11 @@ def _gate_kind(g, B, T, Hv, dk):
     raise ValueError("g must be [B,T,Hv] or [B,T,Hv,dk], got %s" % (tuple(g.shape),))
 
 
-def fwd_chunked(q, k, v, g, beta, S0=None, chunk=64, o=None, S_T=None, stream=None):
+def fwd_chunked(q, k, v, g, beta, S0=None, chunk=64, o=None, S_T=None, stream=None, delta=True):
     """Chunked forward over T tokens.  q, k [B,T,Hk,dk]; v [B,T,Hv,dv];
     g [B,T,Hv] or [B,T,Hv,dk]; beta [B,T,Hv]; S0 fp32 [B,Hv,dv,dk] or None.
-    Returns (o fp32 [B,T,Hv,dv], S_T fp32 [B,Hv,dv,dk]); S_T may be S0."""
+    Returns (o fp32 [B,T,Hv,dv], S_T fp32 [B,Hv,dv,dk]); S_T may be S0.
+    delta=False: the update without the delta correction."""
     B, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
     _dev("q", q)
@@ -198,7 +202,8 @@ def fwd_chunked(q, k, v, g, beta, S0=None, chunk=64, o=None, S_T=None, stream=No
         S_T = torch.empty((B, Hv, dv, dk), dtype=torch.float32, device=q.device)
     _dev("o", o, (B, T, Hv, dv), (torch.float32,))
     _dev("S_T", S_T, (B, Hv, dv, dk), (torch.float32,))
-    d = make_desc(B, T, Hk, Hv, dk, dv, chunk, _DTYPE_CODE[q.dtype], _DTYPE_CODE[g.dtype], gate)
+    d = make_desc(B, T, Hk, Hv, dk, dv, chunk, _DTYPE_CODE[q.dtype], _DTYPE_CODE[g.dtype], gate,
+                  RULE_DELTA if delta else RULE_NO_DELTA)
     L = lib()
     ws_bytes = L.gdn_fwd_workspace_bytes(ctypes.byref(d))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
@@ -208,7 +213,7 @@ def fwd_chunked(q, k, v, g, beta, S0=None, chunk=64, o=None, S_T=None, stream=No
 
 
 def fwd_chunked_conv(xq, xk, xv, conv_w, g, beta, S0=None, qkv_dtype=torch.float16, eps=1e-6,
-                     chunk=64, o=None, S_T=None, stream=None):
+                     chunk=64, o=None, S_T=None, stream=None, delta=True):
     """prologue(xq, xk, xv, conv_w, qkv_dtype, eps) then fwd_chunked, in one call
     (q, k, v are not returned).  Returns (o, S_T)."""
     B, T, Hk, dk = xq.shape
@@ -227,7 +232,8 @@ def fwd_chunked_conv(xq, xk, xv, conv_w, g, beta, S0=None, qkv_dtype=torch.float
         S_T = torch.empty((B, Hv, dv, dk), dtype=torch.float32, device=xq.device)
     _dev("o", o, (B, T, Hv, dv), (torch.float32,))
     _dev("S_T", S_T, (B, Hv, dv, dk), (torch.float32,))
-    d = make_desc(B, T, Hk, Hv, dk, dv, chunk, _DTYPE_CODE[qkv_dtype], _DTYPE_CODE[g.dtype], gate)
+    d = make_desc(B, T, Hk, Hv, dk, dv, chunk, _DTYPE_CODE[qkv_dtype], _DTYPE_CODE[g.dtype], gate,
+                  RULE_DELTA if delta else RULE_NO_DELTA)
     L = lib()
     xt = _DTYPE_CODE[xq.dtype]
     ws_bytes = L.gdn_fwd_conv_workspace_bytes(ctypes.byref(d), xt)
@@ -317,7 +323,8 @@ def prologue_varlen(xq, xk, xv, conv_w, cu_seqlens, out_dtype=torch.float16, eps
     return q, k, v
 
 
-def fwd_chunked_varlen(q, k, v, g, beta, cu_seqlens, S0=None, chunk=64, o=None, S_T=None, stream=None):
+def fwd_chunked_varlen(q, k, v, g, beta, cu_seqlens, S0=None, chunk=64, o=None, S_T=None, stream=None,
+                       delta=True):
     """fwd_chunked over packed sequences: q, k [1,T,Hk,dk]; v [1,T,Hv,dv];
     g [1,T,Hv] or [1,T,Hv,dk]; beta [1,T,Hv]; cu_seqlens int32 [N+1];
     S0 fp32 [N,Hv,dv,dk] or None.  Returns (o [1,T,Hv,dv], S_T [N,Hv,dv,dk])."""
@@ -337,7 +344,8 @@ def fwd_chunked_varlen(q, k, v, g, beta, cu_seqlens, S0=None, chunk=64, o=None, 
         S_T = torch.empty((N, Hv, dv, dk), dtype=torch.float32, device=q.device)
     _dev("o", o, (1, T, Hv, dv), (torch.float32,))
     _dev("S_T", S_T, (N, Hv, dv, dk), (torch.float32,))
-    d = make_desc(N, T, Hk, Hv, dk, dv, chunk, _DTYPE_CODE[q.dtype], _DTYPE_CODE[g.dtype], gate)
+    d = make_desc(N, T, Hk, Hv, dk, dv, chunk, _DTYPE_CODE[q.dtype], _DTYPE_CODE[g.dtype], gate,
+                  RULE_DELTA if delta else RULE_NO_DELTA)
     L = lib()
     ws_bytes = L.gdn_fwd_varlen_workspace_bytes(ctypes.byref(d))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
@@ -451,7 +459,7 @@ def bwd(q, k, v, g, beta, S0, dO, dS_T=None, stream=None):
     return out
 
 
-def decode_step(q, k, v, g, beta, S, o=None, stream=None):
+def decode_step(q, k, v, g, beta, S, o=None, stream=None, delta=True):
     """One token per sequence.  q, k [B,Hk,dk]; v [B,Hv,dv]; g [B,Hv] or
     [B,Hv,dk]; beta [B,Hv]; S fp32 [B,Hv,dv,dk] updated in place.
     Returns o fp32 [B,Hv,dv]."""
@@ -472,7 +480,8 @@ def decode_step(q, k, v, g, beta, S, o=None, stream=None):
     if o is None:
         o = torch.empty((B, Hv, dv), dtype=torch.float32, device=q.device)
     _dev("o", o, (B, Hv, dv), (torch.float32,))
-    d = make_desc(B, 1, Hk, Hv, dk, dv, 64, _DTYPE_CODE[q.dtype], _DTYPE_CODE[g.dtype], gate)
+    d = make_desc(B, 1, Hk, Hv, dk, dv, 64, _DTYPE_CODE[q.dtype], _DTYPE_CODE[g.dtype], gate,
+                  RULE_DELTA if delta else RULE_NO_DELTA)
     check(lib().gdn_decode_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                 _ptr(S), _ptr(o), _stream(stream)))
     return o

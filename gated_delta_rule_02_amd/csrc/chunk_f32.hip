@@ -50,7 +50,7 @@ template <typename TQ, typename TG, bool KEYGATE, int DK, int DVS, int C>
 __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *__restrict__ v,
     const TG *__restrict__ g, const TG *__restrict__ beta, const float *__restrict__ S0,
-    float *__restrict__ o, float *__restrict__ ST, int Tall, int Hk, int Hv, int dv, Seqs sq) {
+    float *__restrict__ o, float *__restrict__ ST, int Tall, int Hk, int Hv, int dv, Seqs sq, int nodelta) {
   using L = F32Smem<DK, DVS, C, KEYGATE>;
   constexpr int KP = L::KP, VP = L::VP, CP = L::CP;
   extern __shared__ float smem[];
@@ -169,12 +169,13 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(
         kx *= sEg[r];
         qx *= sEg[r];
       }
-      sX[r * VP + i] = sBeta[r] * (sV[r * VP + i] - kx);
+      // without the delta correction the chunk's new values are beta V
+      sX[r * VP + i] = sBeta[r] * (sV[r * VP + i] - (nodelta ? 0.f : kx));
       sO[r * VP + i] = qx;
     }
     __syncthreads();
     // ---- N = (I + A)^{-1} X by forward substitution, in place ----
-    for (int i = tid; i < DVS; i += kThreads) {
+    for (int i = tid; i < DVS && !nodelta; i += kThreads) {
       for (int r = 1; r < n; ++r) {
         float acc = sX[r * VP + i];
         for (int s = 0; s < r; ++s) acc -= sA[r * CP + s] * sX[s * VP + i];
@@ -222,7 +223,7 @@ hipError_t launch_cfg(const Shape &sh, const void *q, const void *k, const void 
   dim3 grid(sh.dv / DVS, sh.Hv, sh.B);
   hipLaunchKernelGGL(kern, grid, dim3(kThreads), smem, st, (const TQ *)q, (const TQ *)k,
                      (const TQ *)v, (const TG *)g, (const TG *)beta, S0, o, ST, sh.T, sh.Hk, sh.Hv,
-                     sh.dv, Seqs{sh.cu, sh.B});
+                     sh.dv, Seqs{sh.cu, sh.B}, sh.no_delta ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -623,7 +623,9 @@ struct SeqFetch {
 // the raw rows cv.xv as it is loaded (convolution and SiLU); v is not read.
 // GATE (a whole value head per workgroup): the gated output norm is applied
 // to the chunk's outputs and y is written instead of o (which is not used).
-template <typename TQ, typename TG, int NW, int RT, bool KDA, int LW, bool CONV, bool GATE>
+// ND: the update without the delta correction: X = beta V (no K S^T term) and
+// N = X (the workspace's T is not read).
+template <typename TQ, typename TG, int NW, int RT, bool KDA, int LW, bool CONV, bool GATE, bool ND>
 __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *__restrict__ v,
     const TG *__restrict__ g, const TG *__restrict__ beta, const uint4 *__restrict__ ws,
@@ -983,7 +985,7 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
         float4v ax = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          ax = mfma32(kf[kk], sf[t][kk], ax);
+          if constexpr (!ND) ax = mfma32(kf[kk], sf[t][kk], ax);
           ao = mfma32(sf[t][kk], qf[kk], ao);
         }
         accX[t][R] = ax;
@@ -1008,7 +1010,8 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
         const half4 vv = lds_read_tr(vT + 16 * t + 16 * R * VST);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-          xf[t][R >> 1][(R & 1) * 4 + ii] = (_Float16)(bv[ii] * (float)vv[ii] - gv[ii] * accX[t][R][ii]);
+          xf[t][R >> 1][(R & 1) * 4 + ii] =
+              ND ? (_Float16)(bv[ii] * (float)vv[ii]) : (_Float16)(bv[ii] * (float)vv[ii] - gv[ii] * accX[t][R][ii]);
       }
     }
 
@@ -1024,8 +1027,13 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         float4v acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma32(t0f, xf[t][0], acc);
-        if (R >= 2) acc = mfma32(t1f, xf[t][1], acc);
+        if constexpr (ND) {
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) acc[ii] = (float)xf[t][R >> 1][(R & 1) * 4 + ii];
+        } else {
+          acc = mfma32(t0f, xf[t][0], acc);
+          if (R >= 2) acc = mfma32(t1f, xf[t][1], acc);
+        }
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           nf[t][R >> 1][(R & 1) * 4 + ii] = (_Float16)acc[ii];
@@ -1213,7 +1221,8 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
           make_float4(accS[t][J][0], accS[t][J][1], accS[t][J][2], accS[t][J][3]);
 }
 
-template <typename TQ, typename TG, int NW, int RT, bool KDA, int LW, bool CONV = false, bool GATE = false>
+template <typename TQ, typename TG, int NW, int RT, bool KDA, int LW, bool CONV = false, bool GATE = false,
+          bool ND = false>
 hipError_t launch_seq(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
                       const void *beta, const uint4 *TPws, const float *S0, float *o, float *ST,
                       int nchunks, int c_begin, int c_end, hipStream_t st, const ConvIn &cv = ConvIn{},
@@ -1221,7 +1230,7 @@ hipError_t launch_seq(const Shape &sh, const void *q, const void *k, const void 
   using Cfg = SeqCfg<NW, RT, KDA, LW>;
   constexpr int smem = GATE ? Cfg::SMEM_GATE : Cfg::SMEM;
   static_assert(smem <= 160 * 1024, "LDS");
-  auto kern = chunk_seq_kernel<TQ, TG, NW, RT, KDA, LW, CONV, GATE>;
+  auto kern = chunk_seq_kernel<TQ, TG, NW, RT, KDA, LW, CONV, GATE, ND>;
   hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   if (e != hipSuccess) return e;
   const int ntasks = sh.B * sh.Hv * Cfg::NS;
@@ -1362,6 +1371,17 @@ hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v
       if (gate)
         return launch_seq<TQ, TG, 4, 2, false, 4, CONV, true>(sh, qs, ks, v, g, beta, TPws, s0, nullptr, ST,
                                                               nchunks, cb, ce, s, cv, *gate);
+    if constexpr (!CONV)
+      if (sh.no_delta) {
+        if (heads > 128)
+          return launch_seq<TQ, TG, 4, 2, false, 4, false, false, true>(sh, qs, ks, v, g, beta, TPws, s0, o, ST,
+                                                                        nchunks, cb, ce, s, cv);
+        if (heads > 64)
+          return launch_seq<TQ, TG, 4, 1, false, 4, false, false, true>(sh, qs, ks, v, g, beta, TPws, s0, o, ST,
+                                                                        nchunks, cb, ce, s, cv);
+        return launch_seq<TQ, TG, 2, 1, false, 4, false, false, true>(sh, qs, ks, v, g, beta, TPws, s0, o, ST,
+                                                                      nchunks, cb, ce, s, cv);
+      }
     if (heads > 128)
       return launch_seq<TQ, TG, 4, 2, false, 4, CONV>(sh, qs, ks, v, g, beta, TPws, s0, o, ST, nchunks, cb,
                                                       ce, s, cv);
@@ -1664,6 +1684,13 @@ hipError_t launch_kda_t(const Shape &sh, const void *q, const void *k, const voi
   // workgroup of the sequential pass holds at most 64 value rows.
   const long heads = (long)sh.B * sh.Hv;
   auto seq = [&](int cb, int ce, const float *s0, hipStream_t s) {
+    if (sh.no_delta) {
+      if (heads > 64)
+        return launch_seq<TQ, TG, 4, 1, true, 4, false, false, true>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks,
+                                                                     cb, ce, s);
+      return launch_seq<TQ, TG, 2, 1, true, 4, false, false, true>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks,
+                                                                   cb, ce, s);
+    }
     if (heads > 64)
       return launch_seq<TQ, TG, 4, 1, true, 4>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks, cb, ce, s);
     return launch_seq<TQ, TG, 2, 1, true, 4>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks, cb, ce, s);

@@ -51,7 +51,7 @@ template <typename TQ, typename TG, bool KEYGATE, int DK, int NR>
 __global__ __launch_bounds__(kThreads) void decode_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *__restrict__ v,
     const TG *__restrict__ g, const TG *__restrict__ beta, float *__restrict__ S,
-    float *__restrict__ o, int Hk, int Hv, int dv) {
+    float *__restrict__ o, int Hk, int Hv, int dv, int nodelta) {
   constexpr int LPR = DK / 8;          // lanes per state row
   constexpr int RPP = kThreads / LPR;  // rows per pass
   const int b = blockIdx.z, h = blockIdx.y;
@@ -106,7 +106,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     a = group_sum<LPR>(a);
     c = group_sum<LPR>(c);
     if (i < dv) {
-      const float u = bt * (to_f32(v[bh * dv + i]) - a);
+      // without the delta correction the write is beta v
+      const float u = bt * (to_f32(v[bh * dv + i]) - (nodelta ? 0.f : a));
 #pragma unroll
       for (int j = 0; j < 8; ++j) s[p][j >> 2][j & 3] += u * kk[j];
       float *r = Sbh + (size_t)i * DK + c0;
@@ -125,7 +126,7 @@ hipError_t launch_dk(const Shape &sh, const void *q, const void *k, const void *
   dim3 grid((sh.dv + rows_per_block - 1) / rows_per_block, sh.Hv, sh.B);
   hipLaunchKernelGGL((decode_kernel<TQ, TG, KEYGATE, DK, NR>), grid, dim3(kThreads), 0, st,
                      (const TQ *)q, (const TQ *)k, (const TQ *)v, (const TG *)g, (const TG *)beta, S,
-                     o, sh.Hk, sh.Hv, sh.dv);
+                     o, sh.Hk, sh.Hv, sh.dv, sh.no_delta ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -60,6 +60,8 @@ gdn_status check_desc(const gdn_desc *d, gdn::Shape *sh, bool packed = false) {
     return fail(GDN_E_ARG, "unknown dtype (qkv %d, gate %d)", d->qkv_dtype, d->gate_dtype);
   if (d->gate != GDN_GATE_HEAD && d->gate != GDN_GATE_KEY_CHANNEL)
     return fail(GDN_E_ARG, "unknown gate kind %d", d->gate);
+  if (d->rule != GDN_RULE_DELTA && d->rule != GDN_RULE_NO_DELTA)
+    return fail(GDN_E_ARG, "unknown update rule %d", d->rule);
   if (d->Hv % d->Hk != 0)
     return fail(GDN_E_SHAPE, "Hv (%d) must be a multiple of Hk (%d)", d->Hv, d->Hk);
   if (d->B > 65535 || d->Hv > 65535)
@@ -81,6 +83,7 @@ gdn_status check_desc(const gdn_desc *d, gdn::Shape *sh, bool packed = false) {
   sh->gate_t = (gdn::DType)d->gate_dtype;
   sh->key_gate = d->gate == GDN_GATE_KEY_CHANNEL;
   sh->packed = packed;
+  sh->no_delta = d->rule == GDN_RULE_NO_DELTA;
   return GDN_OK;
 }
 
@@ -319,7 +322,7 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 // the matrix-core path with the per-head gate; otherwise the prologue
 // writes q, k, v into the workspace first.
 bool conv_fused(const gdn_desc *d, const gdn::Shape &sh, bool use_mfma, int32_t x_dtype) {
-  return use_mfma && !sh.key_gate && x_dtype == GDN_BF16;
+  return use_mfma && !sh.key_gate && !sh.no_delta && x_dtype == GDN_BF16;
 }
 
 size_t conv_workspace(const gdn_desc *d, const gdn::Shape &sh, bool use_mfma, int32_t x_dtype) {
@@ -585,6 +588,7 @@ gdn_status check_bwd(const gdn_desc *d, gdn::Shape *sh) {
   if (d->dv % 32 != 0 || d->dv > 1024)
     return fail(GDN_E_UNSUPPORTED, "the backward supports dv a multiple of 32, <= 1024 (got %d)", d->dv);
   if (d->gate_dtype == GDN_F16) return fail(GDN_E_UNSUPPORTED, "the backward's gates must be fp32 or bf16");
+  if (d->rule != GDN_RULE_DELTA) return fail(GDN_E_UNSUPPORTED, "the backward is built for the delta rule only");
   return GDN_OK;
 }
 }  // namespace

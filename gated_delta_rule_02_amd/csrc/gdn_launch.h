@@ -19,6 +19,7 @@ struct Shape {
   bool key_gate;
   bool packed = false;
   const int *cu = nullptr;
+  bool no_delta = false;   // the update without the delta correction
 };
 
 // The gate's arguments for the chunked forward with the prologue inside,

@@ -71,6 +71,14 @@ typedef enum {
   GDN_GATE_KEY_CHANNEL = 1 /* g [B,T,Hv,dk]: one decay per key channel */
 } gdn_gate;
 
+typedef enum {
+  GDN_RULE_DELTA = 0,   /* the gated delta rule above */
+  GDN_RULE_NO_DELTA = 1 /* without the delta correction: S_t = alpha_t S_{t-1} + beta_t v_t k_t^T
+                           (per-key-channel gate: S_{t-1} diag(alpha_t)); the "SinkProbe" page's
+                           hybrid_nodelta layer, the "Source notes" gla row's update.  Supported by
+                           the forward and decode entry points, not by gdn_bwd. */
+} gdn_rule;
+
 /* Problem description shared by all entry points. */
 typedef struct gdn_desc {
   int32_t B;          /* batch (independent sequences), >= 1 */
@@ -84,6 +92,7 @@ typedef struct gdn_desc {
   int32_t qkv_dtype;  /* gdn_dtype of q, k, v (and of the prologue's outputs) */
   int32_t gate_dtype; /* gdn_dtype of g and beta */
   int32_t gate;       /* gdn_gate */
+  int32_t rule;       /* gdn_rule (0, the gated delta rule, when zero-initialised) */
 } gdn_desc;
 
 /*
