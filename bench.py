@@ -26,7 +26,7 @@ kernels run on):
                 gdn_output_gate; the step's 16 384 tokens as 16 packed
                 sequences of mixed lengths (gdn_fwd_chunked_conv_varlen); and
                 the backward of the step's prefill (gdn_bwd, state history in
-                the workspace);
+                the workspace); the same forward without the delta correction;
   cpu_baseline  the fp64 oracle on the host cores on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -226,6 +226,14 @@ def main():
     t_fus = time_events(fused, reps, stream)
     t_pro = time_events(prologue, reps, stream)
     t_chk = time_events(chunked, reps, stream)
+    ndesc = gdn.make_desc(B, T, Hk, Hv, dk, dv, C, gdn.F16, gdn.BF16, gdn.GATE_HEAD, gdn.RULE_NO_DELTA)
+
+    def chunked_nd():
+        gdn.check(L.gdn_fwd_chunked(ctypes.byref(ndesc), P(q), P(k), P(v), P(g), P(beta), None,
+                                    P(o), P(ST), P(ws), ws.numel(), s_ptr))
+
+    warm_up(chunked_nd)
+    t_nd = time_events(chunked_nd, reps, stream)
     bytes_pro = (2 * B * T * Hk * dk + B * T * Hv * dv) * (2 + 2) + w.numel() * 4
     # the same bytes whether q, k, v or the raw inputs are read (both 2 bytes each)
     bytes_chk = (2 * B * T * Hk * dk + B * T * Hv * dv) * 2 + 2 * B * T * Hv * 2 \
@@ -298,7 +306,10 @@ def main():
     del toks, S, S_init, S_eager, graph, cst, cws
 
     # ------------------------------------------------------------------ other prefill workloads
-    extra = {"decode_from_raw_inputs": {
+    extra = {"prefill_no_delta": {
+        "workload": wl.name + ", fp16 q/k/v after the prologue, the update without the delta correction",
+        "us_per_call": t_nd * 1e6, "tokens_per_s": B * T / t_nd, "delta_rule_us": t_chk * 1e6},
+        "decode_from_raw_inputs": {
         "workload": dwl.name + ", tokens as raw inputs through the 3-token convolution history",
         "us_per_step": t_dec_conv * 1e6, "steps_per_s": 1 / t_dec_conv,
         "hbm_frac_algorithmic": bytes_dec / t_dec_conv / 1e9 / PEAK_HBM_GBS},
