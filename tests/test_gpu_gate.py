@@ -182,3 +182,33 @@ def test_gated_after_forward_vs_oracle():
 def test_gated_full_size_vs_oracle_and_two_calls():
     fused_vs_two_calls(PREFILL_CONV, "gated full size")
     gated_vs_oracle(PREFILL_CONV, "gated full size, whole tensor")
+
+
+def test_gated_graph_capture():
+    """The gated call with the gate inside the pass, captured into a graph and
+    replayed with eager work between the replays: every replay equals the
+    eager call."""
+    wl = FUSED.with_(T=100)
+    inp, gi, xs, w, g, beta = gated_inputs(wl)
+    say("gated graph capture: B=%d T=%d Hv=%d" % (wl.B, wl.T, wl.Hv))
+    z, gain = to_torch(gi["z"]), to_torch(gi["gain"])
+    y_e, S_e = gdn.fwd_chunked_conv_gated(*xs, w, g, beta, z, gain, norm_eps=gi["norm_eps"])
+    y = torch.full_like(y_e, float("nan"))
+    ST = torch.full_like(S_e, float("nan"))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):           # warm the allocator outside the capture
+        gdn.fwd_chunked_conv_gated(*xs, w, g, beta, z, gain, norm_eps=gi["norm_eps"], y=y, S_T=ST)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gdn.fwd_chunked_conv_gated(*xs, w, g, beta, z, gain, norm_eps=gi["norm_eps"], y=y, S_T=ST)
+    for rep in range(3):
+        y.fill_(float("nan"))
+        ST.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        assert torch.equal(y, y_e) and torch.equal(ST, S_e), "replay %d differs from the eager call" % rep

@@ -200,3 +200,35 @@ def test_varlen_long_mix_vs_oracle_sampled():
             os_, Ss = oracle.recurrent(q[:, a:e], k[:, a:e], v[:, a:e], g[:, a:e], beta[:, a:e],
                                        S0[s:s + 1].astype(np.float64), chains=[(0, h)])
             check("bf16", o[0, a:e, h], os_[0], ST[s, h], Ss[0], "long mix seq %d head %d" % (s, h))
+
+
+def test_varlen_graph_capture():
+    """Packed sequences with the prologue inside, captured into a graph and
+    replayed with eager work between the replays."""
+    wl = PREFILL_CONV.with_(Hk=2, Hv=6)
+    lens = [70, 0, 130, 1]
+    inp, cu, S0 = packed_case(wl, lens, seed=9, conv=True)
+    say("varlen graph capture: lens %s" % lens)
+    xs = [to_torch(inp[n]) for n in ("xq", "xk", "xv")]
+    w, g, beta = to_torch(inp["conv_w"]), to_torch(inp["g"]), to_torch(inp["beta"])
+    cut, S0t = torch.from_numpy(cu).cuda(), to_torch(S0)
+    o_e, S_e = gdn.fwd_chunked_conv_varlen(*xs, w, g, beta, cut, S0=S0t)
+    o = torch.full_like(o_e, float("nan"))
+    ST = torch.full_like(S_e, float("nan"))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        gdn.fwd_chunked_conv_varlen(*xs, w, g, beta, cut, S0=S0t, o=o, S_T=ST)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gdn.fwd_chunked_conv_varlen(*xs, w, g, beta, cut, S0=S0t, o=o, S_T=ST)
+    for rep in range(3):
+        o.fill_(float("nan"))
+        ST.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        assert torch.equal(o, o_e) and torch.equal(ST, S_e), "replay %d differs from the eager call" % rep
