@@ -637,14 +637,30 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
   constexpr int NKQ = Cfg::NKQ, NV = Cfg::NV, NTP = Cfg::NTP;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
-  // blocks go round-robin over the 8 XCDs: give each XCD a contiguous task range
+  // Blocks go round-robin over the 8 XCDs.  Sequences of one length: each XCD
+  // takes a contiguous task range.  Packed sequences: the tasks of one
+  // (sequence, key head) group stay on one XCD (its value heads share K and
+  // Q in that L2), group j goes to XCD j % 8 and the groups come longest
+  // sequence first, so that every XCD gets an even share of the chunks and
+  // the longest chains start first.
   const int bid = blockIdx.x;
   const int xcd = bid & 7, idx = bid >> 3;
-  const int per = ntasks >> 3, rem = ntasks & 7;
-  const int task = xcd * per + min(xcd, rem) + idx;
-  const int slice = task % NS;
-  const int bh = task / NS;  // b * Hv + h
-  const int h = bh % Hv, b = bh / Hv;
+  int slice, h, b;
+  if (sq.cu) {
+    const int G = Hv / Hk * NS;   // tasks per group
+    const int j = idx / G * 8 + xcd, m = idx % G;
+    if (j >= sq.B * Hk) return;   // the grid rounds the groups up to a multiple of 8
+    b = sq.order ? sq.order[j / Hk] : j / Hk;
+    h = j % Hk * (Hv / Hk) + m / NS;
+    slice = m % NS;
+  } else {
+    const int per = ntasks >> 3, rem = ntasks & 7;
+    const int task = xcd * per + min(xcd, rem) + idx;
+    slice = task % NS;
+    h = task / NS % Hv;
+    b = task / NS / Hv;
+  }
+  const int bh = b * Hv + h;
   const int kh = h / (Hv / Hk);
   int start, T;   // the sequence's first token and length
   seq_bounds(sq, b, Tall, start, T);
@@ -1221,6 +1237,62 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
           make_float4(accS[t][J][0], accS[t][J][1], accS[t][J][2], accS[t][J][3]);
 }
 
+// Chunks per (sequence, value head) in the workspace: ceil(T / C); for packed
+// sequences, chunk slots per value head.
+inline int chunks_per_chain(const Shape &sh) {
+  return sh.packed ? packed_slots(sh.T, sh.B, C) : (sh.T + C - 1) / C;
+}
+// Tokens of all the sequences of a call.
+inline size_t tokens(const Shape &sh) { return sh.packed ? (size_t)sh.T : (size_t)sh.B * sh.T; }
+
+// Packed sequences in order of decreasing chunk count (ties in any order),
+// for the sequential pass: a counting sort in one workgroup, over bins of
+// chunk counts (1023 chunks and more share the first bin).
+constexpr int kOrderBins = 1024;
+__global__ __launch_bounds__(kOrderBins) void seq_order_kernel(Seqs sq, int Tall, int *__restrict__ order) {
+  __shared__ int bin[kOrderBins];
+  __shared__ int wsum[kOrderBins / 64];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  auto key = [&](int s) {
+    int start, len;
+    seq_bounds(sq, s, Tall, start, len);
+    return kOrderBins - 1 - min((len + C - 1) / C, kOrderBins - 1);   // bin 0: the longest
+  };
+  bin[t] = 0;
+  __syncthreads();
+  for (int s = t; s < sq.B; s += kOrderBins) atomicAdd(&bin[key(s)], 1);
+  __syncthreads();
+  const int n = bin[t];   // exclusive prefix sum over the bins: wave scans, then the waves' totals
+  int x = n;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wsum[wv] = x;
+  __syncthreads();
+  for (int i = 0; i < wv; ++i) x += wsum[i];
+  bin[t] = x - n;
+  __syncthreads();
+  for (int s = t; s < sq.B; s += kOrderBins) order[atomicAdd(&bin[key(s)], 1)] = s;
+}
+
+// Bytes of the chunk matrices in the workspace; packed sequences keep their
+// order after them (B ints, rounded up to 256 bytes).
+inline size_t chunk_matrix_bytes(const Shape &sh) {
+  const size_t per_chunk = (size_t)(sh.key_gate ? KDA_CHUNK_U4 : GDN_CHUNK_U4) * 16;
+  return (size_t)(sh.packed ? 1 : sh.B) * sh.Hv * chunks_per_chain(sh) * per_chunk;
+}
+inline size_t order_bytes(const Shape &sh) { return sh.packed ? ((size_t)sh.B * 4 + 255) / 256 * 256 : 0; }
+inline int *seq_order(const Shape &sh, const void *ws) {
+  return sh.packed ? (int *)((char *)ws + chunk_matrix_bytes(sh)) : nullptr;
+}
+hipError_t launch_order(const Shape &sh, void *ws, hipStream_t st) {
+  if (!sh.packed) return hipSuccess;
+  hipLaunchKernelGGL(seq_order_kernel, dim3(1), dim3(kOrderBins), 0, st, Seqs{sh.cu, sh.B}, sh.T,
+                     seq_order(sh, ws));
+  return hipGetLastError();
+}
+
 template <typename TQ, typename TG, int NW, int RT, bool KDA, int LW, bool CONV = false, bool GATE = false,
           bool ND = false>
 hipError_t launch_seq(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
@@ -1234,9 +1306,11 @@ hipError_t launch_seq(const Shape &sh, const void *q, const void *k, const void 
   hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   if (e != hipSuccess) return e;
   const int ntasks = sh.B * sh.Hv * Cfg::NS;
-  hipLaunchKernelGGL(kern, dim3(ntasks), dim3(Cfg::THREADS), smem, st, (const TQ *)q, (const TQ *)k,
+  // packed sequences: (sequence, key head) groups rounded up to a multiple of 8
+  const int grid = sh.packed ? (sh.B * sh.Hk + 7) / 8 * 8 * (sh.Hv / sh.Hk) * Cfg::NS : ntasks;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(Cfg::THREADS), smem, st, (const TQ *)q, (const TQ *)k,
                      (const TQ *)v, (const TG *)g, (const TG *)beta, TPws, S0, o, ST, sh.T, sh.Hk, sh.Hv,
-                     ntasks, nchunks, c_begin, c_end, cv, ga, Seqs{sh.cu, sh.B});
+                     ntasks, nchunks, c_begin, c_end, cv, ga, Seqs{sh.cu, sh.B, seq_order(sh, TPws)});
   return hipGetLastError();
 }
 
@@ -1325,14 +1399,6 @@ hipError_t pipelined(int nchunks, bool overlap, const float *S0, float *ST, hipS
   return e;
 }
 
-// Chunks per (sequence, value head) in the workspace: ceil(T / C); for packed
-// sequences, chunk slots per value head.
-inline int chunks_per_chain(const Shape &sh) {
-  return sh.packed ? packed_slots(sh.T, sh.B, C) : (sh.T + C - 1) / C;
-}
-// Tokens of all the sequences of a call.
-inline size_t tokens(const Shape &sh) { return sh.packed ? (size_t)sh.T : (size_t)sh.B * sh.T; }
-
 // Overlap the preparation of later segments with the sequential pass when
 // the pass leaves room on the GPU: few sequences, each long (the pass then
 // has at most 192 workgroups).
@@ -1391,6 +1457,7 @@ hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v
     return launch_seq<TQ, TG, 2, 1, false, 4, CONV>(sh, qs, ks, v, g, beta, TPws, s0, o, ST, nchunks, cb,
                                                     ce, s, cv);
   };
+  if ((e = launch_order(sh, ws, st)) != hipSuccess) return e;
   return pipelined(nchunks, !sh.packed && seq_overlap(heads), S0, ST, st, prep, seq);
 }
 
@@ -1695,15 +1762,13 @@ hipError_t launch_kda_t(const Shape &sh, const void *q, const void *k, const voi
       return launch_seq<TQ, TG, 4, 1, true, 4>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks, cb, ce, s);
     return launch_seq<TQ, TG, 2, 1, true, 4>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks, cb, ce, s);
   };
+  if ((e = launch_order(sh, ws, st)) != hipSuccess) return e;
   return pipelined(nchunks, !sh.packed && seq_overlap(heads), S0, ST, st, prep, seq);
 }
 
 }  // namespace
 
-size_t chunk_mfma_workspace(const Shape &sh) {
-  const size_t per_chunk = (size_t)(sh.key_gate ? KDA_CHUNK_U4 : GDN_CHUNK_U4) * 16;
-  return (size_t)(sh.packed ? 1 : sh.B) * sh.Hv * chunks_per_chain(sh) * per_chunk;
-}
+size_t chunk_mfma_workspace(const Shape &sh) { return chunk_matrix_bytes(sh) + order_bytes(sh); }
 
 hipError_t launch_chunk_mfma(const Shape &sh, const void *q, const void *k, const void *v,
                              const void *g, const void *beta, const float *S0, float *o, float *ST,

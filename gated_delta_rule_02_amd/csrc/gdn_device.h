@@ -86,6 +86,7 @@ __device__ __forceinline__ void store8(bf16_t *p, const float (&x)[8]) {
 struct Seqs {
   const int *cu;
   int B;
+  const int *order = nullptr;   // the sequences, longest first (sequential pass)
 };
 __device__ __forceinline__ void seq_bounds(const Seqs &sq, int s, int T, int &start, int &len) {
   if (!sq.cu) {

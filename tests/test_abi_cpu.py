@@ -250,7 +250,7 @@ def test_varlen_checks(L):
     cu = P(FAKE + 11 * (1 << 36))
     need = L.gdn_fwd_varlen_workspace_bytes(ctypes.byref(d))
     # matrix-core path: chunk slots per value head = T / 64 + B = 20
-    assert need == 6 * (1000 // 64 + 5) * 13568
+    assert need == 6 * (1000 // 64 + 5) * 13568 + 256   # and the sequence order (5 ints, in 256 bytes)
     assert L.gdn_fwd_varlen_workspace_bytes(ctypes.byref(desc(B=5, T=1000, Hv=5))) == 0
     call = lambda dd, cu_, ptrs=p, ws=p[10], nbytes=need: L.gdn_fwd_chunked_varlen(
         ctypes.byref(dd), cu_, *ptrs[:5], None, *ptrs[5:7], ws, nbytes, None)

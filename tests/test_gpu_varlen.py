@@ -177,6 +177,23 @@ def test_varlen_other_paths_vs_oracle(kind):
     check(mode, o.cpu().numpy(), o_ref, ST.cpu().numpy(), S_ref, "varlen %s" % kind)
 
 
+def test_varlen_many_sequences():
+    """More sequences than the workgroup that orders them (1024 threads), most
+    of them 0 to 3 tokens long (ties everywhere), a few long ones among them,
+    and a group count that is not a multiple of 8."""
+    wl = PREFILL_CONV.with_(Hk=1, Hv=1, conv=False)
+    r = np.random.default_rng(21)
+    lens = r.integers(0, 4, 1101)
+    lens[[3, 700, 1100]] = [300, 129, 64]
+    inp, cu, S0 = packed_case(wl, lens, seed=21)
+    say("varlen: %d sequences, %d tokens" % (len(lens), int(cu[-1])))
+    args = [to_torch(inp[n]) for n in ("q", "k", "v", "g", "beta")]
+    o, ST = gdn.fwd_chunked_varlen(*args, torch.from_numpy(cu).cuda(), S0=to_torch(S0))
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_per_sequence(inp, cu, S0, conv=False)
+    check("bf16", o.cpu().numpy(), o_ref, ST.cpu().numpy(), S_ref, "varlen 1101 sequences")
+
+
 def test_varlen_long_mix_vs_oracle_sampled():
     """A long mix (total 20 000 tokens, 24 sequences) on 128-row workgroups,
     checked on sampled sequences."""
