@@ -211,7 +211,9 @@ gdn_status gdn_fwd_chunked_conv(const gdn_desc *d, int32_t x_dtype, const void *
  * and a sequence whose end precedes its start is read as empty: offsets that
  * break the rule above give unspecified results but no access outside the
  * arguments.  Supported: what the fixed-length entry point supports; the
- * workspace sizes are those of the _varlen queries.
+ * workspace sizes are those of the _varlen queries (beside the chunk
+ * matrices, the workspace holds the sequences' order by chunk count, the
+ * longest first, which only decides the order in which the work is started).
  */
 gdn_status gdn_prologue_varlen(const gdn_desc *d, const int32_t *cu_seqlens, int32_t x_dtype,
                                const void *xq, const void *xk, const void *xv,
