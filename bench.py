@@ -106,16 +106,33 @@ def warm_up(fn, seconds=0.03):
         n += 1
 
 
-def time_events(fn, reps, stream):
+def time_events(fn, reps, stream, repeats=3, warm=0.05):
+    """Seconds per call of fn: `reps` calls between two HIP events recorded on
+    `stream` (the stream the kernels are launched on), after a time-based
+    warm-up; the median over `repeats` such timings."""
     import torch
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        fn()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps / 1e3   # seconds per call
+    warm_up(fn, warm)
+    times = []
+    for _ in range(repeats):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / reps / 1e3)
+    return sorted(times)[len(times) // 2]
+
+
+def git_sha():
+    """The commit of the working tree, or None where there is no git history."""
+    import subprocess
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=10)
+        return r.stdout.strip() or None if r.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError):
+        return None
 
 
 def main():
@@ -209,17 +226,32 @@ def main():
         return
 
     # ------------------------------------------------------------------ timed steps
-    log("warmup %d, timed %d steps" % (args.warmup, args.steps))
+    log("warmup %d, timed %d steps, 3 times" % (args.warmup, args.steps))
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t_step = (time.perf_counter() - t0) / args.steps
+    # the GPU's clocks need some milliseconds of load to come up from idle,
+    # whatever --warmup asks for
+    warm_up(step, 0.1)
+    step_reps = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        step_reps.append((time.perf_counter() - t0) / args.steps)
+    t_step = sorted(step_reps)[1]
     tokens_per_s = B * T / t_step
-    log("step %.1f us -> %.3e tokens/s" % (t_step * 1e6, tokens_per_s))
+    log("step %.1f us (median of %s) -> %.3e tokens/s" %
+        (t_step * 1e6, ", ".join("%.1f" % (x * 1e6) for x in step_reps), tokens_per_s))
+    # the step's outputs, kept for the parity check against the oracle below
+    fused()
+    torch.cuda.synchronize()
+    o_step, ST_step = o.cpu().numpy(), ST.cpu().numpy()
+    decode()
+    torch.cuda.synchronize()
+    od_step = od.cpu().numpy()
 
     # ------------------------------------------------------------------ per-kernel (HIP events)
     reps = max(5, args.steps)
@@ -232,7 +264,6 @@ def main():
         gdn.check(L.gdn_fwd_chunked(ctypes.byref(ndesc), P(q), P(k), P(v), P(g), P(beta), None,
                                     P(o), P(ST), P(ws), ws.numel(), s_ptr))
 
-    warm_up(chunked_nd)
     t_nd = time_events(chunked_nd, reps, stream)
     bytes_pro = (2 * B * T * Hk * dk + B * T * Hv * dv) * (2 + 2) + w.numel() * 4
     # the same bytes whether q, k, v or the raw inputs are read (both 2 bytes each)
@@ -263,9 +294,11 @@ def main():
                                         P(tb[s]), P(S), P(od2), s_ptr))
 
     decode_run()                                   # warm-up pass
-    S.copy_(S_init)
     torch.cuda.synchronize()
-    t_dec = time_events(decode_run, 1, stream) / nsteps
+    t_dec = time_events(decode_run, 1, stream, warm=0) / nsteps
+    S.copy_(S_init)
+    decode_run()                                   # the eager result the graph must reproduce
+    torch.cuda.synchronize()
     bytes_dec = 2 * S.numel() * 4 + od2.numel() * 4 + (2 * dwl.B * dwl.Hk * dwl.dk + dwl.B * dwl.Hv * dwl.dv) * 2 \
         + 2 * dwl.B * dwl.Hv * 2
     log("decode %.1f us/step, %.0f steps/s, %.0f GB/s" % (t_dec * 1e6, 1 / t_dec, bytes_dec / t_dec / 1e9))
@@ -280,8 +313,10 @@ def main():
                                         P(tb[st]), P(S), P(od2), cap))
     S.copy_(S_init)
     torch.cuda.synchronize()
-    t_dec_graph = time_events(graph.replay, 1, stream) / nsteps
+    graph.replay()
+    torch.cuda.synchronize()
     graph_equal = bool(torch.equal(S, S_eager) and torch.equal(od2, o_eager))
+    t_dec_graph = time_events(graph.replay, 1, stream, warm=0) / nsteps
     log("decode as one graph %.1f us/step (final state %s the eager loop's)" %
         (t_dec_graph * 1e6, "equals" if graph_equal else "DIFFERS FROM"))
     # the same steps from raw inputs through the convolution history
@@ -299,11 +334,20 @@ def main():
                                              s_ptr))
 
     decode_conv_run()
-    S.copy_(S_init)
     torch.cuda.synchronize()
-    t_dec_conv = time_events(decode_conv_run, 1, stream) / nsteps
+    t_dec_conv = time_events(decode_conv_run, 1, stream, warm=0) / nsteps
     log("decode from raw inputs (conv history) %.1f us/step" % (t_dec_conv * 1e6))
-    del toks, S, S_init, S_eager, graph, cst, cws
+    # a sample of the decode workload's chains for the oracle's decode rate:
+    # 384 (sequence, value head) chains over the first 100 steps
+    dsel = np.random.default_rng(31).choice(dwl.B * dwl.Hv, 384, replace=False)
+    dsb = torch.from_numpy(dsel // dwl.Hv).to(dev)
+    dsh = torch.from_numpy(dsel % dwl.Hv).to(dev)
+    dsk = dsh // (dwl.Hv // dwl.Hk)
+    ftok = lambda x: x.float().cpu().numpy()
+    dec_sample = {"q": ftok(tq[:100, dsb, dsk]), "k": ftok(tk[:100, dsb, dsk]), "v": ftok(tv[:100, dsb, dsh]),
+                  "g": ftok(tg[:100, dsb, dsh]), "beta": ftok(tb[:100, dsb, dsh]),
+                  "S0": S_init[dsb, dsh].cpu().numpy()}
+    del toks, tq, tk, tv, tg, tb, S, S_init, S_eager, graph, cst, cws
 
     # ------------------------------------------------------------------ other prefill workloads
     extra = {"prefill_no_delta": {
@@ -336,9 +380,7 @@ def main():
         gdn.check(L.gdn_output_gate(ctypes.byref(desc), P(o), gdn.BF16, P(z), P(gain), neps, gdn.BF16, P(y),
                                     s_ptr))
 
-    warm_up(gated)
     t_gated = time_events(gated, 20, stream)
-    warm_up(gate_alone)
     t_gate = time_events(gate_alone, 20, stream)
     bytes_gate = B * T * Hv * dv * (4 + 2 + 2) + dv * 4
     # the forward's algorithmic bytes with y (bf16) read as z and written in place of o (fp32)
@@ -370,7 +412,6 @@ def main():
                                                 1e-6, P(g), P(beta), None, P(o), P(vST), P(vws), vws.numel(),
                                                 s_ptr))
 
-    warm_up(varlen)
     t_var = time_events(varlen, 20, stream)
     extra["prefill_conv_varlen"] = {
         "workload": "%d tokens (16 key / 48 value heads, d 128, C 64, bf16, conv prologue) packed as %d "
@@ -393,9 +434,7 @@ def main():
         gdn.check(L.gdn_bwd(ctypes.byref(pdesc_bwd), P(q), P(k), P(v), P(g), P(beta), None, P(dO), None,
                             *(P(x) for x in grads), P(bws), bws.numel(), s_ptr))
 
-    backward()
-    torch.cuda.synchronize()
-    t_bwd = time_events(backward, 3, stream)
+    t_bwd = time_events(backward, 2, stream, warm=0)
     hist_bytes = B * Hv * T * dv * dk * 4
     io_bytes = 2 * ((2 * B * T * Hk * dk + B * T * Hv * dv) * 2 + 2 * B * T * Hv * 2) + B * T * Hv * dv * 4 \
         + (2 * B * T * Hk * dk + B * T * Hv * dv + 2 * B * T * Hv) * 4 + B * Hv * dv * dk * 4
@@ -423,7 +462,6 @@ def main():
                                         P(xi["beta"]), None if xi["S0"] is None else P(xi["S0"]),
                                         P(xo), P(xst), P(xws), xws.numel(), s_ptr))
 
-        warm_up(xrun)
         tx = time_events(xrun, 10, stream)
         ntok = xwl.B * xwl.T
         gdim = xwl.dk if xwl.gate == "key" else 1
@@ -440,17 +478,40 @@ def main():
     # ------------------------------------------------------------------ CPU baseline (oracle)
     import oracle
     nthreads = min(os.cpu_count() or 1, 16)
-    sample_b = list(range(B))
-    log("cpu baseline: fp64 oracle, prologue + recurrence for batch elements %s (%d chains), %d threads" %
-        (sample_b, len(sample_b) * Hv, nthreads))
+    log("cpu baseline: fp64 oracle, prologue + recurrence over the whole prefill workload (%d chains), "
+        "%d threads" % (B * Hv, nthreads))
     t0 = time.perf_counter()
-    xs = lambda n: np.ascontiguousarray(inp[n].f32()[sample_b])
-    rq, rk, rv = oracle.prologue(xs("xq"), xs("xk"), xs("xv"), inp["conv_w"])
-    oracle.recurrent(rq, rk, rv, xs("g"), xs("beta"), None,
-                     [(b, h) for b in range(len(sample_b)) for h in range(Hv)], nthreads=nthreads)
+    rq, rk, rv = oracle.prologue(inp["xq"].f32(), inp["xk"].f32(), inp["xv"].f32(), inp["conv_w"])
+    o_ref, S_ref = oracle.recurrent_full(rq, rk, rv, inp["g"].f32(), inp["beta"].f32(), nthreads=nthreads)
     t_cpu = time.perf_counter() - t0
-    cpu_tokens_per_s = len(sample_b) * T / t_cpu
+    cpu_tokens_per_s = B * T / t_cpu
     log("cpu baseline %.1f s -> %.3e tokens/s" % (t_cpu, cpu_tokens_per_s))
+    # the same recurrence on one thread, two chains: the rate of one core
+    t0 = time.perf_counter()
+    oracle.recurrent(rq, rk, rv, inp["g"].f32(), inp["beta"].f32(), None, [(0, 0), (0, 1)], nthreads=1)
+    t_one = time.perf_counter() - t0
+    one_thread_tokens_per_s = B * T / (t_one * (B * Hv) / 2)
+    # the decode workload's sampled chains, 100 steps each, scaled to all 12 288 chains
+    ds = dec_sample
+    t0 = time.perf_counter()
+    oracle.recurrent(ds["q"].transpose(1, 0, 2)[:, :, None], ds["k"].transpose(1, 0, 2)[:, :, None],
+                     ds["v"].transpose(1, 0, 2)[:, :, None], ds["g"].T[:, :, None], ds["beta"].T[:, :, None],
+                     ds["S0"][:, None], nthreads=nthreads)
+    t_dcpu = time.perf_counter() - t0
+    cpu_decode_steps_per_s = 100 / (t_dcpu * dwl.B * dwl.Hv / len(ds["S0"]))
+    log("cpu baseline: one thread %.3e tokens/s; decode %.2f steps/s" %
+        (one_thread_tokens_per_s, cpu_decode_steps_per_s))
+    # the timed step's results against the oracle: the prefill's o and S_T,
+    # then the decode step from the oracle's S_T
+    rms_inf = lambda x, r: float(np.max(np.abs(x - r)) / np.sqrt(np.mean(r * r)))
+    rel_inf = lambda x, r: float(np.max(np.abs(x - r)) / np.max(np.abs(r)))
+    od_ref, _ = oracle.recurrent(tok["q"].f32()[:, None], tok["k"].f32()[:, None], tok["v"].f32()[:, None],
+                                 tok["g"].f32()[:, None], tok["beta"].f32()[:, None], S_ref, nthreads=nthreads)
+    step_parity = {"o_max_err_over_rms": rms_inf(o_step, o_ref), "S_T_rel_err": rel_inf(ST_step, S_ref),
+                   "decode_o_max_err_over_rms": rms_inf(od_step, od_ref.reshape(od_step.shape)),
+                   "bars": {"o": 2e-2, "S_T": 1e-2},
+                   "against": "fp64 oracle (prologue + token recurrence) on the step's own inputs"}
+    log("step parity: %s" % step_parity)
 
     line = {
         "metric": "GDN fwd prefill tokens/s + decode steps/s on 1 GPU; % of MFMA/HBM roofline",
@@ -489,10 +550,22 @@ def main():
                    "steps_per_s": 1.0 / t_dec, "tokens_per_s": dwl.B / t_dec,
                    "graph_steps_per_s": 1.0 / t_dec_graph, "graph_equals_eager": graph_equal},
         "workloads": extra,
+        "step_parity": step_parity,
         "cpu_baseline": {"value": cpu_tokens_per_s, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
                          "sample": "fp64 prologue + token recurrence over the whole prefill workload "
                                    "(4 x 4096 tokens, all 192 chains); the decode step is not included",
-                         "seconds": t_cpu, "host_cpu": host_cpu(), "host_logical_cpus": os.cpu_count()},
+                         "seconds": t_cpu, "host_cpu": host_cpu(), "host_logical_cpus": os.cpu_count(),
+                         "one_thread_tokens_per_s": one_thread_tokens_per_s,
+                         "one_thread_sample": "2 of the 192 chains, whole length, scaled to all chains",
+                         "decode_steps_per_s": cpu_decode_steps_per_s,
+                         "decode_sample": "384 of the 12 288 (sequence, value head) chains of the batched "
+                                          "decode workload over its first 100 steps, %d threads, scaled to "
+                                          "all chains" % nthreads},
+        "step_repetitions_ms": [x * 1e3 for x in step_reps],
+        "git_sha": git_sha(),
+        "source_sha16": source_hash(sorted(os.path.join(ROOT, "gated_delta_rule_02_amd", "csrc", f) for f in
+                                           os.listdir(os.path.join(ROOT, "gated_delta_rule_02_amd", "csrc")))
+                                    + [os.path.join(ROOT, "bench.py")]),
     }
     print(json.dumps(line), flush=True)
 

@@ -29,7 +29,9 @@ import re
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libgdn.so")
+# GDN_LIBRARY names another build of the same library (the sanitizer tests load
+# one built with host AddressSanitizer and UBSan)
+LIB_PATH = os.environ.get("GDN_LIBRARY") or os.path.join(HERE, "libgdn.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "gdn.h")
 
 F32, BF16, F16 = 0, 1, 2
@@ -148,6 +150,26 @@ def _dev(name, t, shape=None, dtypes=None):
 
 RULE_DELTA, RULE_NO_DELTA = 0, 1
 
+_poison = False
+
+
+def poison_workspace(on: bool = True) -> None:
+    """Fill every workspace this module allocates with 0xFF bytes before the
+    call (NaN as fp16 and fp32, -1 as int32), so that a kernel that reads
+    workspace memory it has not written first produces NaN instead of stale
+    values.  A testing aid; off by default."""
+    global _poison
+    _poison = bool(on)
+
+
+def _workspace(nbytes, device):
+    if not nbytes:
+        return None
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if _poison:
+        ws.fill_(0xFF)
+    return ws
+
 
 def make_desc(B, T, Hk, Hv, dk, dv, chunk, qkv_dtype, gate_dtype, gate, rule=RULE_DELTA) -> GdnDesc:
     return GdnDesc(B, T, Hk, Hv, dk, dv, chunk, qkv_dtype, gate_dtype, gate, rule)
@@ -206,7 +228,7 @@ def fwd_chunked(q, k, v, g, beta, S0=None, chunk=64, o=None, S_T=None, stream=No
                   RULE_DELTA if delta else RULE_NO_DELTA)
     L = lib()
     ws_bytes = L.gdn_fwd_workspace_bytes(ctypes.byref(d))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    ws = _workspace(ws_bytes, q.device)
     check(L.gdn_fwd_chunked(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                             _ptr(S0), _ptr(o), _ptr(S_T), _ptr(ws), ws_bytes, _stream(stream)))
     return o, S_T
@@ -237,7 +259,7 @@ def fwd_chunked_conv(xq, xk, xv, conv_w, g, beta, S0=None, qkv_dtype=torch.float
     L = lib()
     xt = _DTYPE_CODE[xq.dtype]
     ws_bytes = L.gdn_fwd_conv_workspace_bytes(ctypes.byref(d), xt)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=xq.device) if ws_bytes else None
+    ws = _workspace(ws_bytes, xq.device)
     check(L.gdn_fwd_chunked_conv(ctypes.byref(d), xt, _ptr(xq), _ptr(xk), _ptr(xv), _ptr(conv_w),
                                  float(eps), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T),
                                  _ptr(ws), ws_bytes, _stream(stream)))
@@ -288,7 +310,7 @@ def fwd_chunked_conv_gated(xq, xk, xv, conv_w, g, beta, z, gain, S0=None, qkv_dt
     L = lib()
     xt = _DTYPE_CODE[xq.dtype]
     ws_bytes = L.gdn_fwd_gated_workspace_bytes(ctypes.byref(d), xt, _DTYPE_CODE[y.dtype])
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=xq.device) if ws_bytes else None
+    ws = _workspace(ws_bytes, xq.device)
     check(L.gdn_fwd_chunked_conv_gated(ctypes.byref(d), xt, _ptr(xq), _ptr(xk), _ptr(xv), _ptr(conv_w),
                                        float(eps), _ptr(g), _ptr(beta), _ptr(S0), _ptr(z), _ptr(gain),
                                        float(norm_eps), _DTYPE_CODE[y.dtype], _ptr(y), _ptr(S_T),
@@ -348,7 +370,7 @@ def fwd_chunked_varlen(q, k, v, g, beta, cu_seqlens, S0=None, chunk=64, o=None, 
                   RULE_DELTA if delta else RULE_NO_DELTA)
     L = lib()
     ws_bytes = L.gdn_fwd_varlen_workspace_bytes(ctypes.byref(d))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    ws = _workspace(ws_bytes, q.device)
     check(L.gdn_fwd_chunked_varlen(ctypes.byref(d), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                    _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T), _ptr(ws), ws_bytes,
                                    _stream(stream)))
@@ -379,7 +401,7 @@ def fwd_chunked_conv_varlen(xq, xk, xv, conv_w, g, beta, cu_seqlens, S0=None, qk
     L = lib()
     xt = _DTYPE_CODE[xq.dtype]
     ws_bytes = L.gdn_fwd_conv_varlen_workspace_bytes(ctypes.byref(d), xt)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=xq.device) if ws_bytes else None
+    ws = _workspace(ws_bytes, xq.device)
     check(L.gdn_fwd_chunked_conv_varlen(ctypes.byref(d), _ptr(cu_seqlens), xt, _ptr(xq), _ptr(xk), _ptr(xv),
                                         _ptr(conv_w), float(eps), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
                                         _ptr(S_T), _ptr(ws), ws_bytes, _stream(stream)))
@@ -425,7 +447,7 @@ def decode_step_conv(xq, xk, xv, conv_w, conv_st, g, beta, S, qkv_dtype=torch.fl
     d = make_desc(B, 1, Hk, Hv, dk, dv, 64, _DTYPE_CODE[qkv_dtype], _DTYPE_CODE[g.dtype], gate)
     L = lib()
     ws_bytes = L.gdn_decode_conv_workspace_bytes(ctypes.byref(d))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=xq.device)
+    ws = _workspace(ws_bytes, xq.device)
     check(L.gdn_decode_step_conv(ctypes.byref(d), _DTYPE_CODE[xq.dtype], _ptr(xq), _ptr(xk), _ptr(xv),
                                  _ptr(conv_w), float(eps), _ptr(conv_st), _ptr(g), _ptr(beta), _ptr(S), _ptr(o),
                                  _ptr(ws), ws_bytes, _stream(stream)))
@@ -452,7 +474,7 @@ def bwd(q, k, v, g, beta, S0, dO, dS_T=None, stream=None):
     d = make_desc(B, T, Hk, Hv, dk, dv, 64, _DTYPE_CODE[q.dtype], _DTYPE_CODE[g.dtype], gate)
     L = lib()
     ws_bytes = L.gdn_bwd_workspace_bytes(ctypes.byref(d))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws = _workspace(ws_bytes, q.device)
     check(L.gdn_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(dO),
                     _ptr(dS_T), *(_ptr(out[n]) for n in ("dq", "dk", "dv", "dg", "dbeta", "dS0")), _ptr(ws),
                     ws_bytes, _stream(stream)))

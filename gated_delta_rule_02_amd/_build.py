@@ -56,5 +56,57 @@ def build(jobs: int = 8) -> str:
     return LIB
 
 
+# Host-side sanitizers for the C ABI's validation code: AddressSanitizer and
+# UBSan on the host pass only (device code is built as usual), every finding
+# fatal.
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-sanitize-recover=all",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-g", "-O1"]
+
+
+def build_sanitized(out_dir: str) -> str:
+    """libgdn.so with gdn_api.cpp (argument validation, dispatch) compiled with
+    host AddressSanitizer and UBSan, linked with the regular kernel objects,
+    into out_dir.  Load it with the compiler's ASan runtime preloaded."""
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    for src in sources():
+        if os.path.basename(src) == "gdn_api.cpp":
+            obj = os.path.join(out_dir, "gdn_api_san.o")
+            cmd = [_hipcc(), "-x", "hip", *HIP_FLAGS, *SAN_FLAGS, "-c", src, "-o", obj]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stderr))
+            objs.append(obj)
+        else:
+            obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+            if not os.path.exists(obj) or os.path.getmtime(obj) < os.path.getmtime(src):
+                obj = _compile(src)
+            objs.append(obj)
+    lib = os.path.join(out_dir, "libgdn_san.so")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = [_hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", lib, *objs,
+           "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n%s" % r.stderr)
+    return lib
+
+
+def asan_runtime() -> str:
+    """The host compiler's shared AddressSanitizer runtime (to preload)."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    r = subprocess.run([os.path.join(rocm, "llvm", "bin", "clang"), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        import glob
+        found = glob.glob(os.path.join(rocm, "llvm", "lib", "clang", "*", "lib", "linux",
+                                       "libclang_rt.asan-x86_64.so"))
+        if not found:
+            raise RuntimeError("no clang AddressSanitizer runtime under %s" % rocm)
+        path = found[0]
+    return path
+
+
 if __name__ == "__main__":
     print(build())

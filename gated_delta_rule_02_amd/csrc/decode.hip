@@ -13,7 +13,7 @@
 // Mapping: a row of dk fp32 values is held by dk/8 lanes, 8 values each: lane
 // j of the row holds columns 4j .. 4j+3 and dk/2 + 4j .. dk/2 + 4j+3, so each
 // of its two 16-byte accesses is part of one contiguous run across the lanes.
-// A 256-thread block covers 256/(dk/8) rows (32 at dk = 128); many small
+// A 256-thread block covers 256/(dk/8) rows (16 at dk = 128, 16 lanes a row); many small
 // blocks keep enough loads in flight.  The state is streamed with
 // non-temporal loads and stores: it is touched once per step.  Row dot
 // products are reduced across the dk/8 lanes of the row with xor shuffles.

@@ -60,7 +60,7 @@ hipError_t launch_chunk_f32(const Shape &sh, const void *q, const void *k, const
                             const void *g, const void *beta, const float *S0, float *o,
                             float *ST, hipStream_t s);
 
-// Chunked forward on the fp16 matrix cores (dk = dv = 128, chunk 64, head
+// Chunked forward on the fp16 matrix cores (dk = dv = 128, chunk 64, either
 // gate).  `ws` holds chunk_mfma_workspace(sh) bytes (16-byte aligned).
 hipError_t launch_chunk_mfma(const Shape &sh, const void *q, const void *k, const void *v,
                              const void *g, const void *beta, const float *S0, float *o,

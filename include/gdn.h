@@ -155,9 +155,15 @@ size_t gdn_fwd_workspace_bytes(const gdn_desc *d);
  *    dk, dv in {16, 32, 64, 128}; chunk in {16, 32, 64} with
  *    chunk * dk <= 4096; either gate.
  *  - matrix-core mode (qkv_dtype GDN_BF16 or GDN_F16; gate_dtype GDN_BF16 or
- *    GDN_F32): dk = dv = 128, chunk = 64, head gate.  Products run on the
+ *    GDN_F32): dk = dv = 128, chunk = 64, either gate.  Products run on the
  *    gfx950 fp16 matrix cores with fp32 accumulation; the state is carried in
- *    fp32.  The key-channel gate in this mode runs the fp32 kernels.
+ *    fp32.  Both the per-head and the per-key-channel gate run on the matrix
+ *    cores at these sizes; the fp32 kernels serve only the other sizes (and
+ *    16-bit inputs at them).  Operands are narrowed to fp16, so bf16 inputs
+ *    must lie in fp16's range: a magnitude above 65504 becomes infinite and
+ *    one below 2^-24 becomes zero (q and k are unit rows, and v and the state
+ *    of the workloads here are far inside that range); the call does not
+ *    check the values.
  * o must not alias any input.
  */
 gdn_status gdn_fwd_chunked(const gdn_desc *d, const void *q, const void *k,

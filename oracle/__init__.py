@@ -41,11 +41,27 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def build_sanitized(path: str) -> str:
+    """Compile gdnref.c with AddressSanitizer and UBSan (gcc; every finding
+    aborts) into `path`.  Loaded in place of the plain build when the
+    environment names it in GDNREF_LIBRARY, with gcc's libasan preloaded."""
+    subprocess.run(
+        ["gcc", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+         "-fno-sanitize-recover=all", "-std=c99", "-fPIC", "-shared", "-pthread", "-D_POSIX_C_SOURCE=200112L",
+         "-Wall", "-Werror", "-o", path, _SRC, "-lm"],
+        check=True,
+    )
+    return path
+
+
 def _load():
     global _lib
     if _lib is None:
-        build(force=False)
-        lib = ctypes.CDLL(_LIB)
+        path = os.environ.get("GDNREF_LIBRARY")
+        if not path:
+            build(force=False)
+            path = _LIB
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         I = ctypes.c_int
         lib.gdnref_recurrent.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, I, I, P, P, P, P, I]

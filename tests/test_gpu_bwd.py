@@ -72,3 +72,36 @@ def test_bwd_bf16_grouped():
 
 def test_bwd_bf16_key_gate():
     run_case(KDA_PREFILL.with_(B=1, T=100, Hk=2, Hv=2), "bwd bf16 key gate")
+
+
+def test_bwd_full_heads_long():
+    """The backward at the prefill workload's head shape (16 key / 48 value
+    heads, d 128, bf16 inputs) over T = 1024 tokens, on the GPU for every
+    head; the oracle recomputes the gradients of two sampled key heads (each
+    with its three value heads: a key head's dq and dk depend on no other)."""
+    wl = PREFILL_CONV.with_(B=1, T=1024, conv=False)
+    inp = make_prefill(wl)
+    say("bwd full heads: B=1 T=%d Hk=%d Hv=%d d=128 bf16" % (wl.T, wl.Hk, wl.Hv))
+    r = np.random.default_rng(777)
+    S0 = np.ascontiguousarray(r.normal(0, 0.05, (wl.B, wl.Hv, wl.dv, wl.dk)), dtype=np.float32)
+    dO = np.ascontiguousarray(r.standard_normal((wl.B, wl.T, wl.Hv, wl.dv)), dtype=np.float32)
+    dST = np.ascontiguousarray(r.standard_normal((wl.B, wl.Hv, wl.dv, wl.dk)), dtype=np.float32)
+    args = [to_torch(inp[n]) for n in ("q", "k", "v", "g", "beta")]
+    got = gdn.bwd(*args, to_torch(S0), to_torch(dO), to_torch(dST))
+    torch.cuda.synchronize()
+    got = {n: x.cpu().numpy() for n, x in got.items()}
+    del args
+    grp = wl.Hv // wl.Hk
+    for kh in (0, 11):
+        hs = slice(kh * grp, (kh + 1) * grp)
+        x = {n: inp[n].f32() for n in ("q", "k", "v", "g", "beta")}
+        ref = oracle.backward(x["q"][:, :, kh:kh + 1], x["k"][:, :, kh:kh + 1], x["v"][:, :, hs], x["g"][:, :, hs],
+                              x["beta"][:, :, hs], S0[:, hs].astype(np.float64), dO[:, :, hs], dST[:, hs])
+        mine = {"dq": got["dq"][:, :, kh:kh + 1], "dk": got["dk"][:, :, kh:kh + 1], "dv": got["dv"][:, :, hs],
+                "dg": got["dg"][:, :, hs], "dbeta": got["dbeta"][:, :, hs], "dS0": got["dS0"][:, hs]}
+        for n in ("dq", "dk", "dv", "dg", "dbeta", "dS0"):
+            assert np.all(np.isfinite(mine[n])), "non-finite %s" % n
+            e = rel_inf(mine[n], ref[n])
+            print("[parity] bwd 16/48 T=1024 key head %d %s rel %.3e (bar 1e-4)" % (kh, n, e),
+                  file=sys.stderr, flush=True)
+            assert e <= 1e-4, "key head %d: %s error %.3e" % (kh, n, e)

@@ -186,6 +186,24 @@ def test_full_prefill_conv():
     whole(PREFILL_CONV, "prefill+conv", conv=True)
 
 
+@pytest.mark.parametrize("seed", [101, 102])
+def test_full_prefill_conv_fused_seeds(seed):
+    """The prefill-with-conv workload at full size through the call the
+    benchmark times (the prologue inside the chunked kernels), on two more
+    input seeds, over the whole output tensor: the margin to the bar must not
+    depend on one lucky draw."""
+    wl = PREFILL_CONV.with_(seed=seed)
+    inp = make_prefill(wl)
+    say("prefill+conv fused, seed %d, full size, whole tensor" % seed)
+    o, ST = gdn.fwd_chunked_conv(*(to_torch(inp[n]) for n in ("xq", "xk", "xv")), to_torch(inp["conv_w"]),
+                                 to_torch(inp["g"]), to_torch(inp["beta"]), chunk=wl.chunk)
+    torch.cuda.synchronize()
+    o, ST = o.cpu().numpy(), ST.cpu().numpy()
+    rq, rk, rv = oracle.prologue(inp["xq"].f32(), inp["xk"].f32(), inp["xv"].f32(), inp["conv_w"])
+    o_ref, S_ref = oracle.recurrent_full(rq, rk, rv, inp["g"].f32(), inp["beta"].f32())
+    check("bf16", o, o_ref, ST, S_ref, "prefill+conv fused seed %d whole tensor" % seed)
+
+
 def test_full_long_prefill():
     whole(LONG_PREFILL, "long prefill")
 

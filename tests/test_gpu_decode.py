@@ -76,36 +76,47 @@ def test_decode_steps_small(gate, qdt):
 
 
 def test_decode_full_batch_sampled():
-    """The batched-decode workload at full size (B = 256, 16/48 heads, d 128): 200 steps on
-    the GPU, oracle replay of sampled chains; o compared at steps 1, 10, 100, 200 and S at the end."""
+    """The batched-decode workload at its full size and length: B = 256, 16/48
+    heads, d 128, 1000 consecutive steps on the GPU with the state carried in
+    place.  The oracle replays 48 sampled chains over all 1000 steps; o is
+    compared at steps 1, 10, 100, 200, ..., 1000 and S after step 1000, and
+    the error is logged at every checkpoint to show how it grows."""
     wl = BATCHED_DECODE
-    steps = 200
+    steps = wl.decode_steps
+    assert steps == 1000
     say("decode full batch B=256 steps=%d" % steps)
     S0 = make_state(wl)
     toks = decode_tokens_device(wl, steps)
     S = to_torch(S0)
-    o_all = []
-    for s in range(steps):
-        o_all.append(gdn.decode_step(toks["q"][s], toks["k"][s], toks["v"][s], toks["g"][s],
-                                     toks["beta"][s], S))
-    torch.cuda.synchronize()
-    chains = [(0, 0), (17, 5), (101, 31), (200, 47), (255, 46), (128, 24)]
+    idx = [0, 9] + list(range(99, steps, 100))
     grp = wl.Hv // wl.Hk
-    for (b, h) in chains:
-        kh = h // grp
-        f = lambda x: x.float().cpu().numpy()
-        q = f(toks["q"][:, b, kh])[None, :, None]
-        k = f(toks["k"][:, b, kh])[None, :, None]
-        v = f(toks["v"][:, b, h])[None, :, None]
-        g = f(toks["g"][:, b, h])[None, :, None]
-        beta = f(toks["beta"][:, b, h])[None, :, None]
-        o_ref, S_ref = oracle.recurrent(q, k, v, g, beta, S0[b:b + 1, h:h + 1])
-        o = np.stack([o_all[s][b, h].cpu().numpy() for s in range(steps)])
-        idx = [0, 9, 99, 199]
-        check("bf16", o[idx], o_ref[0][idx], S[b, h].cpu().numpy(), S_ref[0],
-              "decode full chain (%d,%d)" % (b, h))
-        check("f32", o[idx], o_ref[0][idx], S[b, h].cpu().numpy(), S_ref[0],
-              "decode full chain (%d,%d) fp32 bar" % (b, h))
+    r = np.random.default_rng(1000)
+    chains = [(0, 0), (255, 47), (17, 5), (101, 31), (200, 46), (128, 24)] + \
+        [(int(b), int(h)) for b, h in zip(r.integers(0, wl.B, 42), r.integers(0, wl.Hv, 42))]
+    bi = torch.tensor([c[0] for c in chains], device="cuda")
+    hi = torch.tensor([c[1] for c in chains], device="cuda")
+    o_steps = []
+    for s in range(steps):
+        o = gdn.decode_step(toks["q"][s], toks["k"][s], toks["v"][s], toks["g"][s], toks["beta"][s], S)
+        if s in idx:
+            o_steps.append(o[bi, hi])
+    torch.cuda.synchronize()
+    o_gpu = torch.stack(o_steps, 1).cpu().numpy()                 # [chains, checkpoints, dv]
+    S_gpu = S[bi, hi].cpu().numpy()
+    f = lambda x: x.float().cpu().numpy()
+    kh = hi // grp
+    q = f(toks["q"][:, bi, kh]).transpose(1, 0, 2)[:, :, None]     # [chains, steps, 1, dk]
+    k = f(toks["k"][:, bi, kh]).transpose(1, 0, 2)[:, :, None]
+    v = f(toks["v"][:, bi, hi]).transpose(1, 0, 2)[:, :, None]
+    g = f(toks["g"][:, bi, hi]).T[:, :, None]
+    beta = f(toks["beta"][:, bi, hi]).T[:, :, None]
+    S0c = np.stack([S0[b, h] for b, h in chains])[:, None]
+    o_ref, S_ref = oracle.recurrent(q, k, v, g, beta, S0c)           # every chain as its own sequence
+    o_ref = o_ref[:, idx]
+    for j, s in enumerate(idx):
+        check("f32", o_gpu[:, j], o_ref[:, j], None, None, "decode 48 chains, step %d" % (s + 1))
+    check("bf16", o_gpu, o_ref, S_gpu, S_ref, "decode 48 chains, steps 1..1000")
+    check("f32", o_gpu, o_ref, S_gpu, S_ref, "decode 48 chains, steps 1..1000 (fp32 bar)")
 
 
 def test_decode_deterministic_and_in_place():
