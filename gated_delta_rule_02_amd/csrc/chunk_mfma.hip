@@ -106,13 +106,6 @@ __device__ __forceinline__ uint4 pack8(const float (&x)[8], f16_t) {
   for (int i = 0; i < 8; ++i) h[i] = (f16_t)x[i];
   return __builtin_bit_cast(uint4, h);
 }
-__device__ __forceinline__ uint4 pack8(const float (&x)[8], bf16_t) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = (uint32_t)from_f32<bf16_t>(x[2 * i]).bits | ((uint32_t)from_f32<bf16_t>(x[2 * i + 1]).bits << 16);
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
 // Eight bf16 values of a 16-byte piece, widened (row zero when `zero`).
 __device__ __forceinline__ void unpack8(uint4 u, bool zero, float (&x)[8]) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
@@ -181,14 +174,16 @@ __device__ __forceinline__ void chunk_scalars(float g, float beta, float *sc, in
   sc[4 * C + lane] = __expf(gC - x);
 }
 
-// T = (I + A)^{-1} for a 64 x 64 unit lower-triangular I + A, then T and P
-// stored as fragments at dst (T first).  On entry the strictly lower 16 x 16
-// diagonal blocks of A are in sAd (fp32), its blocks below the diagonal in
-// sAo (fp16), and sT and sP have zero blocks (0,1) and (2,3) (the fragments
-// read them).  Called by all 256 threads; wave w owns block row w.
+// T = (I + A)^{-1} for a 64 x 64 unit lower-triangular I + A, then T (and,
+// WITH_P, P after it) stored as fragments at dst.  On entry the strictly
+// lower 16 x 16 diagonal blocks of A are in sAd (fp32), its blocks below the
+// diagonal in sAo (fp16), and sT (and sP) have zero blocks (0,1) and (2,3)
+// (the fragments read them).  Called by all 256 threads; wave w owns block
+// row w.
 //
 // Diagonal blocks: forward substitution in fp32 (wave w -> block w).  Blocks
 // below: column by column, T_RS = -T_RR sum_M A_RM T_MS, on 16x16x16 MFMAs.
+template <bool WITH_P>
 __device__ __forceinline__ void invert_store(const float *sAd, const _Float16 *sAo, _Float16 *sT,
                                              const _Float16 *sP, uint4 *__restrict__ dst, int w, int l) {
   const int g4 = l >> 4, ln = l & 15;
@@ -249,13 +244,14 @@ __device__ __forceinline__ void invert_store(const float *sAd, const _Float16 *s
   }
   lds_barrier();
   {
-    // T then P: 2 x NFRAG fragments
+    // T (then P): NFRAG fragments each
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
       if (kk == 0 || w >= 2) {
         dst[frag_index(w, kk) * 64 + l] = __builtin_bit_cast(uint4, perm_row(sT, CST, 16 * w + ln, kk, g4));
-        dst[(NFRAG + frag_index(w, kk)) * 64 + l] =
-            __builtin_bit_cast(uint4, perm_row(sP, CST, 16 * w + ln, kk, g4));
+        if constexpr (WITH_P)
+          dst[(NFRAG + frag_index(w, kk)) * 64 + l] =
+              __builtin_bit_cast(uint4, perm_row(sP, CST, 16 * w + ln, kk, g4));
       }
   }
 }
@@ -264,9 +260,10 @@ __device__ __forceinline__ void invert_store(const float *sAd, const _Float16 *s
 // 16-byte units: T and P fragments; K o e^gamma, Q o e^gamma and
 // K o e^{gamma_n - gamma} (fp16, 64 x 128 row-major, rows past the end of the
 // sequence zero); beta[64] and Gamma_n[128] (fp32).
-// Workspace of the head gate per (batch, value head, chunk): T and P
-// fragments, then the per-token scalars of chunk_scalars (5 x 64 fp32).
-constexpr int GDN_SC = 2 * NFRAG * 64;
+// Workspace of the head gate per (batch, value head, chunk): T fragments,
+// then the per-token scalars of chunk_scalars (5 x 64 fp32).  (Its P is
+// formed in the sequential pass.)
+constexpr int GDN_SC = NFRAG * 64;
 constexpr int GDN_CHUNK_U4 = GDN_SC + 5 * C / 4;
 constexpr int KDA_KG = 2 * NFRAG * 64;
 constexpr int KDA_QG = KDA_KG + C * DK / 8;
@@ -276,18 +273,18 @@ constexpr int KDA_NSC = (C + DK) / 4;
 constexpr int KDA_CHUNK_U4 = (KDA_SC + KDA_NSC + 15) / 16 * 16;
 
 // ============================================================================
-// chunk_prep: per (chunk, key head) P0 = masked Q K^T; per (chunk, value head) T = (I + A)^{-1}, P = L o P0
+// chunk_prep: per (chunk, key head) G = K K^T; per (chunk, value head) T = (I + A)^{-1}
 // ============================================================================
-// K and Q are only read before the value-head loop (into the G and P0
-// accumulators); the per-head matrices then reuse their space.  After them:
-// the gate and beta of the group's heads (2 x grp x C fp32), then the five
-// per-token scalars of the current head, which (convolution) first hold the
-// taps of k and q: the two are never live together.
+// K is only read before the value-head loop (into the G accumulators); the
+// per-head matrices then reuse its space.  After K and Q (Q: with the
+// convolution, whose q this kernel makes for the sequential pass): the gate
+// and beta of the group's heads (2 x grp x C fp32), then the five per-token
+// scalars of the current head, which (convolution) first hold the taps of k
+// and q: the two are never live together.
 constexpr int P_OFF_K = 0;                              // [C][KST] fp16
 constexpr int P_OFF_Q = P_OFF_K + C * KST * 2;          // [C][KST] fp16
 constexpr int P_OFF_T = 0;                              // [C][CST] fp16 (over K)
-constexpr int P_OFF_P = P_OFF_T + C * CST * 2;          // [C][CST] fp16
-constexpr int P_OFF_AO = P_OFF_P + C * CST * 2;         // [C][CST] fp16
+constexpr int P_OFF_AO = P_OFF_T + C * CST * 2;         // [C][CST] fp16
 constexpr int P_OFF_AD = P_OFF_AO + C * CST * 2;        // [4][16][DST] fp32
 constexpr int P_OFF_GB = P_OFF_Q + C * KST * 2;         // then 2 x grp x C fp32
 constexpr int P_SC_BYTES = 5 * C * 4, P_TAP_BYTES = 2 * DK * 16;
@@ -300,15 +297,13 @@ inline size_t prep_smem(int grp, bool conv) {
 // SiLU, L2 normalisation) and written to cv.q and cv.k for the sequential
 // pass; the q and k arguments are not read.
 template <typename TQ, typename TG, bool CONV>
-__global__ __launch_bounds__(kThreads, (CONV && std::is_same<TQ, bf16_t>::value) ? 3 : 4) void chunk_prep_kernel(
+__global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TG *__restrict__ g,
     const TG *__restrict__ beta, uint4 *__restrict__ Tws, int Tall, int Hk, int Hv, int nchunks, int c0,
     ConvIn cv, Seqs sq) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   _Float16 *sK = reinterpret_cast<_Float16 *>(smem + P_OFF_K);
-  _Float16 *sQ = reinterpret_cast<_Float16 *>(smem + P_OFF_Q);
   _Float16 *sT = reinterpret_cast<_Float16 *>(smem + P_OFF_T);
-  _Float16 *sP = reinterpret_cast<_Float16 *>(smem + P_OFF_P);
   _Float16 *sAo = reinterpret_cast<_Float16 *>(smem + P_OFF_AO);
   float *sAd = reinterpret_cast<float *>(smem + P_OFF_AD);
   float *sGB = reinterpret_cast<float *>(smem + P_OFF_GB);   // [2][grp][C]: gate, beta per head
@@ -339,13 +334,13 @@ __global__ __launch_bounds__(kThreads, (CONV && std::is_same<TQ, bf16_t>::value)
   // once the loads have all landed
   uint4 ky[CONV ? 4 : 1], qy[CONV ? 4 : 1];
   const int rb = tid >> 4, ch = (tid & 15) * 8;
-  // K and Q tiles (fp16), rows past the end zero; all loads are in flight
+  // The K tile (fp16), rows past the end zero; all loads are in flight
   // before the first is converted.  CONV: lane group rb = tid / 16 makes rows
-  // 4 rb .. 4 rb + 3 from the raw rows 4 rb - 3 .. 4 rb + 3 (zero before the
-  // sequence start) at the lane's 8 channels.
+  // 4 rb .. 4 rb + 3 of K and Q from the raw rows 4 rb - 3 .. 4 rb + 3 (zero
+  // before the sequence start) at the lane's 8 channels.
   {
     constexpr int NL = CONV ? 7 : 4;
-    uint4 uk[NL], uq[NL];
+    uint4 uk[NL], uq[CONV ? NL : 1];
     if constexpr (CONV) {
 #pragma unroll
       for (int j = 0; j < 7; ++j) {
@@ -362,7 +357,6 @@ __global__ __launch_bounds__(kThreads, (CONV && std::is_same<TQ, bf16_t>::value)
         const int row = (tid >> 4) + 16 * it;
         const size_t off = ((bt0 + min(row, n - 1)) * Hk + kh) * DK + ch;
         uk[it] = *reinterpret_cast<const uint4 *>(k + off);
-        uq[it] = *reinterpret_cast<const uint4 *>(q + off);
       }
     }
     // gate and beta of every value head of the group, [head][token] in LDS
@@ -417,45 +411,35 @@ __global__ __launch_bounds__(kThreads, (CONV && std::is_same<TQ, bf16_t>::value)
         }
       };
       conv_rows(uk, sTap, sK, ky);
-      conv_rows(uq, sTap + DK, sQ, qy);
+      // q's rows go to LDS too, where nothing reads them: without these
+      // stores the compiler's schedule of this kernel spills registers
+      conv_rows(uq, sTap + DK, reinterpret_cast<_Float16 *>(smem + P_OFF_Q), qy);
     } else {
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const int row = (tid >> 4) + 16 * it;
         *reinterpret_cast<half8 *>(sK + row * KST + ch) = row < n ? to_half8(uk[it], TQ{}) : hz;
-        *reinterpret_cast<half8 *>(sQ + row * KST + ch) = row < n ? to_half8(uq[it], TQ{}) : hz;
       }
     }
   }
   lds_barrier();
 
-  // G row w (tiles (w, w - d)) and P0 row Rp = 3 - w (tiles (Rp, Rp - d))
-  const int Rp = 3 - w;
-  float4v accG[4], accP[4];
+  // G row w (tiles (w, w - d))
+  float4v accG[4];
   {
     const _Float16 *kw = sK + (16 * w + ln) * KST + 8 * g4;
-    const _Float16 *kp = sK + (16 * Rp + ln) * KST + 8 * g4;
-    half8 ak[4], ap[4];
+    half8 ak[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      ak[kk] = *reinterpret_cast<const half8 *>(kw + 32 * kk);
-      ap[kk] = *reinterpret_cast<const half8 *>(sQ + (16 * Rp + ln) * KST + 32 * kk + 8 * g4);
-    }
+    for (int kk = 0; kk < 4; ++kk) ak[kk] = *reinterpret_cast<const half8 *>(kw + 32 * kk);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      float4v ag = {0.f, 0.f, 0.f, 0.f}, apv = {0.f, 0.f, 0.f, 0.f};
+      float4v ag = {0.f, 0.f, 0.f, 0.f};
       if (d <= w) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           ag = mfma32(ak[kk], *reinterpret_cast<const half8 *>(kw - 16 * d * KST + 32 * kk), ag);
       }
-      if (d <= Rp) {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          apv = mfma32(ap[kk], *reinterpret_cast<const half8 *>(kp - 16 * d * KST + 32 * kk), apv);
-      }
       accG[d] = ag;
-      accP[d] = apv;
     }
   }
   // All loads so far have landed (nothing is stored yet): said explicitly so
@@ -475,32 +459,11 @@ __global__ __launch_bounds__(kThreads, (CONV && std::is_same<TQ, bf16_t>::value)
   }
   for (int hv = 0; hv < grp; ++hv) {
     const int h = kh * grp + hv;
-    lds_barrier();  // K and Q, or the previous head's T and P, have been read out
+    lds_barrier();  // K, or the previous head's T, has been read out
     if (tid < C) chunk_scalars(sGB[hv * C + tid], sGB[(grp + hv) * C + tid], sc, tid);
     lds_barrier();
     uint4 *wch = Tws + (ws_chain(sq, b, h, Hv, nchunks, start) + c) * GDN_CHUNK_U4;
     if (tid < 5 * C / 4) wch[GDN_SC + tid] = reinterpret_cast<const uint4 *>(sc)[tid];
-    // P = L o P0 for this head (lower incl. diagonal), fp16; the two upper
-    // blocks the fragments read are zero
-    {
-      const int r0 = 16 * Rp + 4 * g4;
-      _Float16 *pp = sP + r0 * CST + 16 * Rp + ln;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        if (d <= Rp) {
-          const float gs = sGam[16 * (Rp - d) + ln];
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) {
-            const bool keep = d > 0 || ln <= 4 * g4 + ii;
-            pp[ii * CST - 16 * d] =
-                (_Float16)(keep ? __expf(sGam[r0 + ii] - gs) * accP[d][ii] : 0.f);
-          }
-        }
-      }
-      const int rr = tid >> 4, cc = tid & 15;
-      sP[rr * CST + 16 + cc] = (_Float16)0.f;
-      sP[(32 + rr) * CST + 48 + cc] = (_Float16)0.f;
-    }
     // A: diagonal blocks fp32 (strictly lower), off-diagonal blocks fp16
     {
       const int r0 = 16 * w + 4 * g4;
@@ -532,19 +495,36 @@ __global__ __launch_bounds__(kThreads, (CONV && std::is_same<TQ, bf16_t>::value)
       sT[rr * CST + 16 + cc] = (_Float16)0.f;
       sT[(32 + rr) * CST + 48 + cc] = (_Float16)0.f;
     }
-    invert_store(sAd, sAo, sT, sP, wch, w, l);
+    invert_store<false>(sAd, sAo, sT, nullptr, wch, w, l);
   }
 }
 
 // ============================================================================
 // chunk_seq: the sequential pass over the chunks of one sequence
 // ============================================================================
-// NW compute waves hold the state, 16 RT value rows each; LW more waves load
-// the next chunks and write them to LDS, so the compute waves issue no loads
-// at all (their only memory traffic is LDS reads and the output stores, and
-// a wait for a load never waits for stores).
-template <int NW, int RT, bool KDA, int LW>
+// NW compute waves hold the state, 16 RT value rows each; four more waves
+// load the next chunks and write them to LDS, so the compute waves issue no
+// loads at all (their only memory traffic is LDS reads and the output
+// stores, and a wait for a load never waits for stores).
+//
+// Two barriers per chunk c.  Before the first (B1) the loading waves form
+// the chunk's P (the decayed masked Q K^T) from its K and Q and the compute
+// waves read the chunk's V; after it the compute waves read P, and the
+// loading waves write V of chunk c + 1 (before the second barrier, B2), so
+// V and P need one LDS buffer each.  K, Q, T and the per-token scalars of chunk c + 1
+// are written during chunk c into the other of two buffers and are complete
+// at B2.
+//
+// Precision: X, N (as the operand of the output product) and P are each
+// split into an fp16 high part and an fp16 low part (x = hi + lo with
+// |lo| <= 2^-11 |x|), and their products take the three terms
+// hi*hi + lo*hi + hi*lo; with the prologue inside, v keeps its fp32 value the
+// same way (high and low parts in LDS).  An fp16 operand alone rounds each of
+// these to 11 bits, which on the conv-prefill workload costs up to 2e-2 of
+// rms(o) over a whole output tensor; the splits bring that to about 6e-3.
+template <int NW, int RT, bool KDA, bool VLO>
 struct SeqCfg {
+  static constexpr int LW = 4;                 // loading waves
   static constexpr int CT = 64 * NW;           // compute threads
   static constexpr int THREADS = 64 * (NW + LW);
   static constexpr int LT = 64 * LW;           // loading threads
@@ -553,24 +533,28 @@ struct SeqCfg {
   static constexpr int VST = WGC + 8;          // sV row stride
   static constexpr int NKQ = (C * DK / 8) / LT;     // 16-byte K (and Q) pieces per loading thread
   static constexpr int NV = (C * WGC / 8) / LT;     // 16-byte V pieces per loading thread
-  static constexpr int NTP = (2 * NFRAG * 64 + LT - 1) / LT;  // T and P fragment pieces
+  static constexpr int NFR = KDA ? 2 * NFRAG : NFRAG;   // fragments from the workspace: T (key gate: T, P)
+  static constexpr int NTP = (NFR * 64 + LT - 1) / LT;  // their pieces per loading thread
   static constexpr int NSC = KDA ? C + DK : 5 * C;       // fp32 scalars per chunk
   static constexpr int SC_U4 = KDA ? KDA_SC : GDN_SC;      // their offset in the chunk's workspace
   static constexpr int CHUNK_U4 = KDA ? KDA_CHUNK_U4 : GDN_CHUNK_U4;  // workspace per chunk
+  static constexpr int TPS_U4 = NFR * 64 + NSC / 4;        // fragments, then the scalars (16 B units)
   static constexpr int OFF_K = 0;                          // 2 x [C][KST] fp16
   static constexpr int OFF_Q = OFF_K + 2 * C * KST * 2;    // 2 x [C][KST] fp16
   static constexpr int OFF_KD = OFF_Q + 2 * C * KST * 2;   // 2 x [C][KST] fp16 (key gate)
-  static constexpr int OFF_V = OFF_KD + (KDA ? 2 * C * KST * 2 : 0);   // 2 x [C][VST] fp16
-  static constexpr int TPS_U4 = 2 * NFRAG * 64 + NSC / 4;  // T, P fragments, then the scalars (16 B units)
-  static constexpr int OFF_TP = OFF_V + 2 * C * VST * 2;   // 2 x [TPS_U4] x 16 B
-  static constexpr int OFF_W = OFF_TP + 2 * TPS_U4 * 16;   // [WGC][4] fp32 (v taps, convolution)
-  static constexpr int SMEM = OFF_W + WGC * 16;
+  // V (one buffer): [C][VST] fp16; VLO: fp32 and transposed, [WGC][VTS]
+  static constexpr int VTS = C + 4;
+  static constexpr int OFF_V = OFF_KD + (KDA ? 2 * C * KST * 2 : 0);
+  static constexpr int OFF_TP = OFF_V + (VLO ? WGC * VTS * 4 : C * VST * 2);   // 2 x [TPS_U4] x 16 B
+  static constexpr int OFF_P = OFF_TP + 2 * TPS_U4 * 16;   // head gate: P high, then low fragments
+  static constexpr int OFF_W = OFF_P + (KDA ? 0 : 2 * NFRAG * 1024);   // VLO: v taps, [WGC][4] fp32
+  static constexpr int SMEM = OFF_W + (VLO ? WGC * 16 : 0);
   // with the output gate: the row sums of squares of two chunks, [2][C][NW] fp32
   static constexpr int OFF_SS = SMEM;
   static constexpr int SMEM_GATE = OFF_SS + 2 * C * NW * 4;
-  static_assert(SMEM <= 160 * 1024, "LDS");
+  static_assert(SMEM_GATE <= 160 * 1024, "LDS");
   static_assert((C * DK / 8) % LT == 0 && (C * WGC / 8) % LT == 0, "loads per thread");
-  static_assert(LW > 0 && LT >= NSC / 4, "one scalar piece per loading thread");
+  static_assert(LT >= NSC / 4, "one scalar piece per loading thread");
   static_assert(NSC % 4 == 0 && (C * (KST / 8)) % 64 == 0, "16-byte pieces");
 };
 
@@ -606,35 +590,52 @@ __device__ __forceinline__ void lds_load16(const void *src, void *dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
 }
 
-// The next chunk's raw loads.  Nothing is converted here, so no instruction
-// needs the data before the chunk is committed.
-// CONV: the raw v rows of the lane's NV output rows and the three before.
-template <typename TQ, typename TG, int NW, int RT, bool KDA, int LW, bool CONV>
+// A chunk's loads into registers.  Nothing is converted here, so no
+// instruction needs the data before it is committed to LDS.  CONV: the raw v
+// rows of the lane's NV output rows and the three before (K and Q go
+// straight to LDS).
+template <int NW, int RT, bool KDA, bool CONV>
 struct SeqFetch {
-  using Cfg = SeqCfg<NW, RT, KDA, LW>;
-  uint4 k[Cfg::NKQ], q[Cfg::NKQ], kd[KDA ? Cfg::NKQ : 1], v[CONV ? Cfg::NV + 3 : Cfg::NV], tp[Cfg::NTP], sc;
+  using Cfg = SeqCfg<NW, RT, KDA, CONV>;
+  static constexpr int NKQ = CONV ? 1 : Cfg::NKQ;
+  uint4 k[NKQ], q[NKQ], kd[KDA ? Cfg::NKQ : 1], v[CONV ? Cfg::NV + 3 : Cfg::NV], tp[Cfg::NTP], sc;
   int n, t0;
 };
 
-// KDA false: head gate; K, Q, V, g, beta are read from the inputs and T, P
-// from the workspace.  KDA true: key-channel gate; the decayed K, Q, the
-// state-update K, beta and Gamma_n come from the workspace (q, k, g, beta are
-// not read) and the state decays per key channel.  CONV: v is computed from
-// the raw rows cv.xv as it is loaded (convolution and SiLU); v is not read.
-// GATE (a whole value head per workgroup): the gated output norm is applied
-// to the chunk's outputs and y is written instead of o (which is not used).
-// ND: the update without the delta correction: X = beta V (no K S^T term) and
-// N = X (the workspace's T is not read).
-template <typename TQ, typename TG, int NW, int RT, bool KDA, int LW, bool CONV, bool GATE, bool ND>
-__global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
+// fp16 high and low parts of x: x = hi + lo to about 22 bits.
+// The low part is x - hi (exact in fp32) rounded to fp16 by one mixed-precision
+// fma (hi read as fp16, -1 and x as fp32), written out as the instruction:
+// the compiler otherwise widens hi, subtracts and narrows again.
+__device__ __forceinline__ void split16(float x, _Float16 &hi, _Float16 &lo) {
+  hi = (_Float16)x;
+  const uint32_t h = __builtin_bit_cast(uint16_t, hi);
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
+  lo = __builtin_bit_cast(_Float16, (uint16_t)r);
+}
+
+// KDA false: head gate; K, Q, V, g, beta are read from the inputs and T from
+// the workspace, P is formed here.  KDA true: key-channel gate; the decayed
+// K, Q, the state-update K, T, P, beta and Gamma_n come from the workspace
+// (q, k, g, beta are not read) and the state decays per key channel.  CONV:
+// v is computed from the raw rows cv.xv as it is loaded (convolution and
+// SiLU, kept to fp32 as high and low fp16 parts) and K, Q (fp16, after the
+// prologue) go from global memory straight to LDS; v is not read.  GATE (a
+// whole value head per workgroup): the gated output norm is applied to the
+// chunk's outputs and y is written instead of o (which is not used).  ND:
+// the update without the delta correction: N = beta V (no K S^T term, the
+// workspace's T is not read).
+template <typename TQ, typename TG, int NW, int RT, bool KDA, bool CONV, bool GATE, bool ND>
+__global__ __launch_bounds__(64 * (NW + 4), 1) void chunk_seq_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *__restrict__ v,
     const TG *__restrict__ g, const TG *__restrict__ beta, const uint4 *__restrict__ ws,
     const float *__restrict__ S0, float *__restrict__ o, float *__restrict__ ST, int Tall, int Hk,
     int Hv, int ntasks, int nchunks, int c_begin, int c_end, ConvIn cv, GateArgs ga, Seqs sq) {
-  using Cfg = SeqCfg<NW, RT, KDA, LW>;
-  constexpr int NSC = Cfg::NSC;
+  static_assert(!CONV || (std::is_same<TQ, f16_t>::value && !KDA), "the prologue inside: fp16 q, k, head gate");
+  using Cfg = SeqCfg<NW, RT, KDA, CONV>;
+  constexpr int NSC = Cfg::NSC, LW = Cfg::LW;
   constexpr int LT = Cfg::LT, WGC = Cfg::WGC, NS = Cfg::NS, VST = Cfg::VST;
-  constexpr int NKQ = Cfg::NKQ, NV = Cfg::NV, NTP = Cfg::NTP;
+  constexpr int NKQ = Cfg::NKQ, NV = Cfg::NV, NTP = Cfg::NTP, NFR = Cfg::NFR;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   // Blocks go round-robin over the 8 XCDs.  Sequences of one length: each XCD
@@ -692,48 +693,51 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
   _Float16 *const sKb = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_K);
   _Float16 *const sQb = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_Q);
   _Float16 *const sKdb = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_KD);
-  _Float16 *const sVb = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_V);
+  _Float16 *const sV = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_V);
+  float *const sVt = reinterpret_cast<float *>(smem + Cfg::OFF_V);   // CONV: V^T, fp32
   uint4 *const sTPb = reinterpret_cast<uint4 *>(smem + Cfg::OFF_TP);   // buffer b at b TPS_U4
-  constexpr int TPS_U4 = Cfg::TPS_U4, SC_AT = 2 * NFRAG * 64;   // the scalars follow T and P
-  float4 *const sW = reinterpret_cast<float4 *>(smem + Cfg::OFF_W);
+  uint4 *const sPh = reinterpret_cast<uint4 *>(smem + Cfg::OFF_P);     // head gate: P high fragments
+  uint4 *const sPl = sPh + NFRAG * 64;                                  // ... and low
+  constexpr int TPS_U4 = Cfg::TPS_U4, SC_AT = NFR * 64;   // the scalars follow the fragments
 
-  using Fetch = SeqFetch<TQ, TG, NW, RT, KDA, LW, CONV>;
-  // fp16 q, k, v need no conversion: they are loaded straight into LDS
-  constexpr bool DMA = CONV && !KDA && std::is_same<TQ, f16_t>::value;
+  using Fetch = SeqFetch<NW, RT, KDA, CONV>;
   // CONV: loading thread -> value channels 8 ch8 .. + 7 of the slice at the
   // chunk rows NV rb .. NV rb + NV - 1 (a row's channels on consecutive lanes)
   const int vrb = ltid / (WGC / 8), vch8 = ltid % (WGC / 8);
   const bf16_t *xvb = cv.xv + ((size_t)start * Hv + h) * DV + slice * WGC + vch8 * 8;
-  // parts: K and Q (and the key gate's state-update K), V, and the T and P
+  // parts: K and Q (and the key gate's state-update K), V, and the T (and P)
   // fragments with the scalars
   constexpr int FKQ = 1, FV = 2, FTP = 4, FALL = 7;
   auto fetch = [&](Fetch &f, int c, int part) {
     const int n = min(C, T - c * C);
     f.n = n;
     const size_t t0 = (size_t)c * C;
-    const uint4 *wc = wsbh + (size_t)c * Cfg::CHUNK_U4;
-    const TQ *kc = kb + t0 * kq_rs, *qc = qb + t0 * kq_rs, *vc = vb + t0 * v_rs;
-    if (KDA && (part & FKQ)) {
-      // rows past the end of the sequence are zero in the workspace
-#pragma unroll
-      for (int it = 0; it < NKQ; ++it) {
-        const int e = ltid + LT * it;
-        f.k[it] = wc[KDA_KG + e];
-        f.q[it] = wc[KDA_QG + e];
-        f.kd[it] = wc[KDA_KD + e];
-      }
-    }
-    // rows past the end of the sequence (last chunk) re-read its last row
-#pragma unroll
-    for (int it = 0; it < NKQ; ++it) {
-      const int e = ltid + LT * it;
-      const int off = min(e >> 4, n - 1) * kq_rs + (e & 15) * 8;
-      if (!KDA && (part & FKQ)) {
-        f.k[it] = *reinterpret_cast<const uint4 *>(kc + off);
-        f.q[it] = *reinterpret_cast<const uint4 *>(qc + off);
-      }
-    }
     f.t0 = (int)t0;
+    const uint4 *wc = wsbh + (size_t)c * Cfg::CHUNK_U4;
+    if constexpr (!CONV) {
+      if (part & FKQ) {
+        if constexpr (KDA) {
+          // rows past the end of the sequence are zero in the workspace
+#pragma unroll
+          for (int it = 0; it < NKQ; ++it) {
+            const int e = ltid + LT * it;
+            f.k[it] = wc[KDA_KG + e];
+            f.q[it] = wc[KDA_QG + e];
+            f.kd[it] = wc[KDA_KD + e];
+          }
+        } else {
+          // rows past the end of the sequence (last chunk) re-read its last row
+          const TQ *kc = kb + t0 * kq_rs, *qc = qb + t0 * kq_rs;
+#pragma unroll
+          for (int it = 0; it < NKQ; ++it) {
+            const int e = ltid + LT * it;
+            const int off = min(e >> 4, n - 1) * kq_rs + (e & 15) * 8;
+            f.k[it] = *reinterpret_cast<const uint4 *>(kc + off);
+            f.q[it] = *reinterpret_cast<const uint4 *>(qc + off);
+          }
+        }
+      }
+    }
     if (part & FV) {
       if constexpr (CONV) {
 #pragma unroll
@@ -742,6 +746,7 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
           f.v[j] = *reinterpret_cast<const uint4 *>(xvb + (size_t)tt * v_rs);
         }
       } else {
+        const TQ *vc = vb + t0 * v_rs;
 #pragma unroll
         for (int it = 0; it < NV; ++it) {
           const int e = ltid + LT * it;
@@ -752,172 +757,240 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
     }
     if (part & FTP) {
 #pragma unroll
-      for (int it = 0; it < NTP; ++it) f.tp[it] = wc[min(ltid + LT * it, 2 * NFRAG * 64 - 1)];
+      for (int it = 0; it < NTP; ++it) f.tp[it] = wc[min(ltid + LT * it, NFR * 64 - 1)];
       f.sc = wc[Cfg::SC_U4 + min(ltid, NSC / 4 - 1)];
     }
   };
-  // CONV: v of the lane's rows from the raw rows of f, with the prologue's
-  // arithmetic, rounded to the qkv type as it stores it, into the V tile v_
-  // (rows past the sequence end zero).  wv: the taps of the lane's channels.
-  auto conv_v = [&](const Fetch &f, _Float16 *v_, const float (&wv)[4][8]) __attribute__((always_inline)) {
-    // the raw rows NV rb - 3 .. NV rb + NV - 1, widened once; only the first
-    // three can lie before the sequence start (zero there)
-    float x[NV + 3][8];
-#pragma unroll
-    for (int j = 0; j < NV + 3; ++j) unpack8(f.v[j], j < 3 && f.t0 + NV * vrb - 3 + j < 0, x[j]);
-#pragma unroll
-    for (int it = 0; it < NV; ++it) {
-      const int row = NV * vrb + it;
-      float z[8];
-      (void)conv_silu8(wv[0], wv[1], wv[2], wv[3], x[it], x[it + 1], x[it + 2], x[it + 3], z);
-      *reinterpret_cast<half8 *>(v_ + row * VST + vch8 * 8) =
-          row < f.n ? to_half8(pack8(z, TQ{}), TQ{}) : half8{};
-    }
-  };
-  auto commit = [&](const Fetch &f, int buf) {
-    // The loads issued before the commit stay ahead of its conversions.
-    __builtin_amdgcn_sched_barrier(0);
-    _Float16 *k_ = sKb + buf * C * KST, *q_ = sQb + buf * C * KST, *v_ = sVb + buf * C * VST;
-    // K and Q (and the state-update K) are fp16 in the workspace of the key gate
-    using TK = typename std::conditional<KDA, f16_t, TQ>::type;
-    const half8 hz = {};
-    if (ltid < NSC / 4) sTPb[buf * TPS_U4 + SC_AT + ltid] = f.sc;
-#pragma unroll
-    for (int it = 0; it < NKQ; ++it) {
-      const int e = ltid + LT * it;
-      // last chunk of a ragged sequence: rows past its end are zero
-      const bool ok = KDA || (e >> 4) < f.n;
-      const int off = (e >> 4) * KST + (e & 15) * 8;
-      *reinterpret_cast<half8 *>(k_ + off) = ok ? to_half8(f.k[it], TK{}) : hz;
-      *reinterpret_cast<half8 *>(q_ + off) = ok ? to_half8(f.q[it], TK{}) : hz;
-      if constexpr (KDA) *reinterpret_cast<half8 *>(sKdb + buf * C * KST + off) = to_half8(f.kd[it], f16_t{});
-    }
+  // The fragments and scalars of f into T/P buffer `buf`.
+  auto commit_tp = [&](const Fetch &f, int buf) {
 #pragma unroll
     for (int it = 0; it < NTP; ++it) {
       const int e = ltid + LT * it;
-      if (e < 2 * NFRAG * 64) sTPb[buf * TPS_U4 + e] = f.tp[it];
+      if (e < NFR * 64) sTPb[buf * TPS_U4 + e] = f.tp[it];
     }
-    if constexpr (CONV) {
-      // the taps of the lane's 8 channels come from LDS.  Everything else is
-      // written first, so that its registers are free during the arithmetic.
-      __builtin_amdgcn_sched_barrier(0);
-      float wv[4][8];
+    if (ltid < NSC / 4) sTPb[buf * TPS_U4 + SC_AT + ltid] = f.sc;
+  };
+  // K and Q (and the state-update K) of f into buffer `buf` (register path)
+  auto commit_kq = [&](const Fetch &f, int buf) {
+    if constexpr (!CONV) {
+      _Float16 *k_ = sKb + buf * C * KST, *q_ = sQb + buf * C * KST;
+      // K and Q (and the state-update K) are fp16 in the workspace of the key gate
+      using TK = typename std::conditional<KDA, f16_t, TQ>::type;
+      const half8 hz = {};
 #pragma unroll
-      for (int c8 = 0; c8 < 8; ++c8) {
-        const float4 t4 = sW[vch8 * 8 + c8];
-        wv[0][c8] = t4.x; wv[1][c8] = t4.y; wv[2][c8] = t4.z; wv[3][c8] = t4.w;
+      for (int it = 0; it < NKQ; ++it) {
+        const int e = ltid + LT * it;
+        // last chunk of a ragged sequence: rows past its end are zero
+        const bool ok = KDA || (e >> 4) < f.n;
+        const int off = (e >> 4) * KST + (e & 15) * 8;
+        *reinterpret_cast<half8 *>(k_ + off) = ok ? to_half8(f.k[it], TK{}) : hz;
+        *reinterpret_cast<half8 *>(q_ + off) = ok ? to_half8(f.q[it], TK{}) : hz;
+        if constexpr (KDA) *reinterpret_cast<half8 *>(sKdb + buf * C * KST + off) = to_half8(f.kd[it], f16_t{});
       }
-      conv_v(f, v_, wv);
-    } else {
+    }
+  };
+  // V of f into the V buffer (register path; rows past the sequence end zero)
+  auto commit_v = [&](const Fetch &f) {
+    if constexpr (!CONV) {
 #pragma unroll
       for (int it = 0; it < NV; ++it) {
         const int e = ltid + LT * it;
         const int row = e / (WGC / 8);
-        *reinterpret_cast<half8 *>(v_ + row * VST + (e % (WGC / 8)) * 8) =
-            row < f.n ? to_half8(f.v[it], TQ{}) : hz;
+        *reinterpret_cast<half8 *>(sV + row * VST + (e % (WGC / 8)) * 8) =
+            row < f.n ? to_half8(f.v[it], TQ{}) : half8{};
       }
     }
   };
 
-  if (w >= NW && DMA) {
-    // Loading waves, the prologue inside with fp16 q and k: K and Q of chunk
-    // c + 1 go from global memory straight into the other LDS buffer while
-    // chunk c is computed (they need no conversion), and the raw v rows with
-    // the T and P fragments and the scalars of chunk c + 1, fetched into
-    // registers one chunk earlier (fa, fb alternate), are convolved and
-    // written there meanwhile.  Each wave waits for its own loads before the
-    // barrier that hands the buffer over.
-    const int lw = w - NW;
-    // NK wave loads a tile; wave lw issues loads lw, lw + LW, .., NPER of
-    // them, the last ones repeating one of its own (so every wave issues the
-    // same number and its waits have a fixed count).  Rows past n repeat
-    // row n - 1 (in bounds) and are zeroed once they have landed, each wave
-    // over the pieces it loaded itself.
-    constexpr int KP = KST / 8, NK = C * KP / 64, NTOT = 2 * NK, NPER = (NTOT + LW - 1) / LW;
-    static_assert(NTOT >= LW, "loads per wave");
-    float wv[4][8];
+  // The chunk's P = L o Q K^T (head gate), formed by the compute waves before
+  // B1 from the K and Q fragments they read for K S^T and S Q^T: block (R, S),
+  // S <= R, is computed as P^T = K_S Q_R^T, so that lane (g4, ln) holds
+  // P[16 R + ln][16 S + 4 g4 + ii]: four consecutive elements of its own slot
+  // in the fragment (R, S / 2) that the output product reads.  p_store scales
+  // them by the decays, writes their high and low parts, and zeroes the upper
+  // halves of the diagonal fragments (blocks (0, 1) and (2, 3)).
+  auto p_store = [&](int R, int S, float4v acc, const float *sc) __attribute__((always_inline)) {
+    const float gr = sc[16 * R + ln];
+    const float4 gs = *reinterpret_cast<const float4 *>(sc + 16 * S + 4 * g4);
+    const float gsv[4] = {gs.x, gs.y, gs.z, gs.w};
+    half4 ph, pl;
 #pragma unroll
-    for (int c8 = 0; c8 < 8; ++c8) {
-      const float4 t4 =
-          *reinterpret_cast<const float4 *>(cv.wv + ((size_t)h * DV + slice * WGC + vch8 * 8 + c8) * 4);
-      wv[0][c8] = t4.x; wv[1][c8] = t4.y; wv[2][c8] = t4.z; wv[3][c8] = t4.w;
+    for (int ii = 0; ii < 4; ++ii) {
+      const bool keep = S < R || 4 * g4 + ii <= ln;
+      _Float16 hi, lo;
+      split16(keep ? __expf(gr - gsv[ii]) * acc[ii] : 0.f, hi, lo);
+      ph[ii] = hi;
+      pl[ii] = lo;
     }
-    Fetch fa, fb;
-    auto piece = [&](int j, int n, size_t t0, int buf) __attribute__((always_inline)) {
-      int g = lw + LW * j;
-      if (g >= NTOT) g -= LW;
-      return tile_piece<NK, KP>(g, n, t0, l, kb, qb, kq_rs, sKb + buf * C * KST, sQb + buf * C * KST);
-    };
-    auto load_chunk = [&](int c, int buf, const Fetch &fcur, Fetch &fnext) __attribute__((always_inline)) {
-      const int n = min(C, T - c * C);
-      const size_t t0 = (size_t)c * C;
-      fetch(fnext, min(c + 1, c_end - 1), FV | FTP);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < NPER; ++j) {
-        const auto pt = piece(j, n, t0, buf);
-        lds_load16(pt.src, pt.dst);
-      }
-      conv_v(fcur, sVb + buf * C * VST, wv);
-#pragma unroll
-      for (int it = 0; it < NTP; ++it) {
-        const int e = ltid + LT * it;
-        if (e < 2 * NFRAG * 64) sTPb[buf * TPS_U4 + e] = fcur.tp[it];
-      }
-      if (ltid < NSC / 4) sTPb[buf * TPS_U4 + SC_AT + ltid] = fcur.sc;
-      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt 0: this wave's K and Q pieces are in LDS
-      if (n < C) {
-        for (int j = 0; j < NPER; ++j) {
-          const auto pt = piece(j, n, t0, buf);
-          if (pt.row >= n && pt.pc >= 0) *reinterpret_cast<half8 *>(pt.dst + 8 * l) = half8{};
-        }
-      }
-    };
-    fetch(fa, c_begin, FV | FTP);
-    load_chunk(c_begin, 0, fa, fb);
-    lds_barrier();
-    for (int c = c_begin; c < c_end; c += 2) {
-      if (c + 1 < c_end) load_chunk(c + 1, 1, fb, fa);
-      lds_barrier();
-      if (c + 1 < c_end) {
-        if (c + 2 < c_end) load_chunk(c + 2, 0, fa, fb);
-        lds_barrier();
-      }
+    const int at = frag_index(R, S >> 1) * 64 + l;
+    half4 *dh = reinterpret_cast<half4 *>(sPh + at) + (S & 1);
+    half4 *dl = reinterpret_cast<half4 *>(sPl + at) + (S & 1);
+    *dh = ph;
+    *dl = pl;
+    if (S == R && !(R & 1)) {   // the block right of the diagonal in the same fragment
+      dh[1] = half4{};
+      dl[1] = half4{};
     }
-    return;
-  }
+  };
   if (w >= NW) {
-    // Loading waves: chunk c + 2 is loaded while chunk c is computed, and
-    // chunk c + 1, loaded one chunk earlier, is written to the other LDS
-    // buffer.  These waves issue no stores, so each wait for a chunk's loads
-    // is exact.  The loads are unconditional (a repeated chunk near the end),
-    // and the barriers match the compute waves' one per chunk.
-    Fetch fa, fb;
-    fetch(fa, c_begin, FALL);
     if constexpr (CONV) {
-      // the taps of the lane's 8 channels, read back by every commit: each
-      // lane writes the taps it reads (lanes sharing channels write the same
-      // values), so no other wave is waited for
+      // Loading waves, the prologue inside: K and Q (fp16, made by the prep
+      // kernel) of chunk c + 1 go from global memory straight into the other
+      // LDS buffer while chunk c is computed; the raw v rows with the T
+      // fragments and the scalars of chunk c + 1, fetched into registers one
+      // chunk earlier (fa, fb alternate), are convolved before B1 and
+      // written after it.  Each wave waits for its own loads before B2.
+      const int lw = w - NW;
+      // NK wave loads a tile; wave lw issues loads lw, lw + LW, .., NPER of
+      // them, the last ones repeating one of its own (so every wave issues the
+      // same number and its waits have a fixed count).  Rows past n repeat
+      // row n - 1 (in bounds) and are zeroed once they have landed, each wave
+      // over the pieces it loaded itself.
+      constexpr int KP = KST / 8, NK = C * KP / 64, NTOT = 2 * NK, NPER = (NTOT + LW - 1) / LW;
+      static_assert(NTOT >= LW, "loads per wave");
+      // the taps of the lane's 8 channels, read back from LDS by every
+      // convolution: each lane writes the taps it reads (lanes sharing
+      // channels write the same values), so no other wave is waited for
+      float4 *const sW = reinterpret_cast<float4 *>(smem + Cfg::OFF_W);
 #pragma unroll
       for (int c8 = 0; c8 < 8; ++c8)
         sW[vch8 * 8 + c8] =
             *reinterpret_cast<const float4 *>(cv.wv + ((size_t)h * DV + slice * WGC + vch8 * 8 + c8) * 4);
-    }
-    commit(fa, 0);
-    // CONV: the raw v rows (with the three before each lane's rows) are
-    // fetched one chunk ahead only, first thing in the chunk; two chunks of
-    // them would not fit in the registers beside everything else.
-    fetch(fb, min(c_begin + 1, c_end - 1), CONV ? FKQ | FTP : FALL);
-    lds_barrier();
-    auto lstep = [&](int c, Fetch &fn, Fetch &fc) {
-      if constexpr (CONV) fetch(fc, min(c + 1, c_end - 1), FV);
-      fetch(fn, min(c + 2, c_end - 1), CONV ? FKQ | FTP : FALL);
-      if (c + 1 < c_end) commit(fc, ((c - c_begin) & 1) ^ 1);
+      auto piece = [&](int j, int n, size_t t0, int buf) __attribute__((always_inline)) {
+        int gi = lw + LW * j;
+        if (gi >= NTOT) gi -= LW;
+        return tile_piece<NK, KP>(gi, n, t0, l, kb, qb, kq_rs, sKb + buf * C * KST, sQb + buf * C * KST);
+      };
+      auto issue_kq = [&](int c, int buf) __attribute__((always_inline)) {
+        const int n = min(C, T - c * C);
+#pragma unroll
+        for (int j = 0; j < NPER; ++j) {
+          const auto pt = piece(j, n, (size_t)c * C, buf);
+          lds_load16(pt.src, pt.dst);
+        }
+      };
+      // after the wave's loads have landed: zero the rows past a ragged end
+      auto zero_tail = [&](int c, int buf) __attribute__((always_inline)) {
+        const int n = min(C, T - c * C);
+        if (n < C) {
+          for (int j = 0; j < NPER; ++j) {
+            const auto pt = piece(j, n, (size_t)c * C, buf);
+            if (pt.row >= n && pt.pc >= 0) *reinterpret_cast<half8 *>(pt.dst + 8 * l) = half8{};
+          }
+        }
+      };
+      // v of the lane's rows from the raw rows of f, with the prologue's
+      // arithmetic, into z (fp32; rows past the end zero)
+      auto conv_v = [&](const Fetch &f, float (&z)[NV][8]) __attribute__((always_inline)) {
+        float wv[4][8];
+#pragma unroll
+        for (int c8 = 0; c8 < 8; ++c8) {
+          const float4 t4 = sW[vch8 * 8 + c8];
+          wv[0][c8] = t4.x; wv[1][c8] = t4.y; wv[2][c8] = t4.z; wv[3][c8] = t4.w;
+        }
+        float x[NV + 3][8];
+#pragma unroll
+        for (int j = 0; j < NV + 3; ++j) unpack8(f.v[j], j < 3 && f.t0 + NV * vrb - 3 + j < 0, x[j]);
+#pragma unroll
+        for (int it = 0; it < NV; ++it) {
+          const int row = NV * vrb + it;
+          (void)conv_silu8(wv[0], wv[1], wv[2], wv[3], x[it], x[it + 1], x[it + 2], x[it + 3], z[it]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) z[it][e] = row < f.n ? z[it][e] : 0.f;
+        }
+      };
+      // z into the V buffer, transposed: channel-major, the lane's NV
+      // consecutive rows of a channel in one write.  The writes are written
+      // out as instructions: the compiler would otherwise make them wait for
+      // the K, Q loads into LDS issued before them (it cannot tell that they
+      // touch other LDS), which take until the end of the chunk; the loads'
+      // own wait comes before the next barrier, and the writes are complete
+      // at the barrier (its wait for this wave's LDS operations).
+      auto write_v = [&](const float (&z)[NV][8]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          // the LDS address (offset in the workgroup's LDS) of the write
+          const uint32_t dst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float *)(
+              sVt + (vch8 * 8 + e) * Cfg::VTS + NV * vrb);
+          if constexpr (NV == 4) {
+            const float4v x = {z[0][e], z[1][e], z[2][e], z[3][e]};
+            asm volatile("ds_write_b128 %0, %1" ::"v"(dst), "v"(x));
+          }
+          if constexpr (NV == 2) {
+            const float2 x = make_float2(z[0][e], z[1][e]);
+            asm volatile("ds_write_b64 %0, %1" ::"v"(dst), "v"(x));
+          }
+          if constexpr (NV == 1) asm volatile("ds_write_b32 %0, %1" ::"v"(dst), "v"(z[0][e]));
+        }
+      };
+      Fetch fa, fb;
+      // chunk c_begin: everything in LDS before the first barrier
+      fetch(fa, c_begin, FV | FTP);
+      issue_kq(c_begin, 0);
+      fetch(fb, min(c_begin + 1, c_end - 1), FV | FTP);
+      commit_tp(fa, 0);
+      {
+        float z[NV][8];
+        conv_v(fa, z);
+        write_v(z);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt 0: this wave's K and Q pieces are in LDS
+      zero_tail(c_begin, 0);
       lds_barrier();
-    };
-    for (int c = c_begin; c < c_end; c += 2) {
-      lstep(c, fa, fb);
-      if (c + 1 < c_end) lstep(c + 1, fb, fa);
+      // chunk c: fb holds chunk c + 1's registers, fa takes chunk c + 2's
+      auto lstep = [&](int c, Fetch &fn, Fetch &fc) __attribute__((always_inline)) {
+        const int buf = (c + 1 - c_begin) & 1;
+        const bool more = c + 1 < c_end;
+        float z[NV][8];
+        // fc's registers landed during the previous chunk: they are written
+        // out and convolved before new loads are issued, so that no wait for
+        // them covers the new ones
+        if (more) {
+          commit_tp(fc, buf);
+          conv_v(fc, z);
+        }
+        if (more) issue_kq(c + 1, buf);
+        fetch(fn, min(c + 2, c_end - 1), FV | FTP);
+        lds_barrier();   // B1: the compute waves have read V of chunk c
+        if (more) write_v(z);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt 0
+        if (more) zero_tail(c + 1, buf);
+        lds_barrier();   // B2
+      };
+      for (int c = c_begin; c < c_end; c += 2) {
+        lstep(c, fa, fb);
+        if (c + 1 < c_end) lstep(c + 1, fb, fa);
+      }
+    } else {
+      // Loading waves, register path: chunk c + 2 is loaded while chunk c is
+      // computed, and chunk c + 1, loaded one chunk earlier, is written to
+      // the other LDS buffer (K, Q, T, scalars before B1, V after it).  These
+      // waves issue no stores, so each wait for a chunk's loads is exact.
+      Fetch fa, fb;
+      fetch(fa, c_begin, FALL);
+      commit_kq(fa, 0);
+      commit_tp(fa, 0);
+      commit_v(fa);
+      fetch(fb, min(c_begin + 1, c_end - 1), FALL);
+      lds_barrier();
+      auto lstep = [&](int c, Fetch &fn, Fetch &fc) __attribute__((always_inline)) {
+        const int buf = (c + 1 - c_begin) & 1;
+        const bool more = c + 1 < c_end;
+        // fc's registers landed during the previous chunk: write them out
+        // before new loads are issued, so that no wait covers the new ones
+        if (more) {
+          commit_kq(fc, buf);
+          commit_tp(fc, buf);
+        }
+        fetch(fn, min(c + 2, c_end - 1), FALL);
+        lds_barrier();   // B1: the compute waves have read V of chunk c
+        if (more) commit_v(fc);
+        lds_barrier();   // B2
+      };
+      for (int c = c_begin; c < c_end; c += 2) {
+        lstep(c, fa, fb);
+        if (c + 1 < c_end) lstep(c + 1, fb, fa);
+      }
     }
     return;
   }
@@ -944,10 +1017,10 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
 
   // The gated output norm: the row sums of squares of a chunk's outputs are
   // combined over the compute waves through LDS (written before the chunk's
-  // barrier, read after it), so the outputs of chunk c are normalised and
-  // stored just after that barrier.  The lane's gain values are loaded with
-  // the entering state and its z values at the start of each chunk (rows
-  // past the end of the sequence re-read the last one).
+  // last barrier, read after it), so the outputs of chunk c are normalised
+  // and stored just after that barrier.  The lane's gain values are loaded
+  // with the entering state and its z values at the start of each chunk
+  // (rows past the end of the sequence re-read the last one).
   static_assert(!GATE || (NS == 1 && RT == 2 && NW == 4 && !KDA), "the gate needs a whole value head");
   float gw[RT][4];
   const bf16_t *zb = nullptr;
@@ -964,19 +1037,48 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
   uint4 zl[RT][2];   // z of a chunk as loaded: [tile][row block pair]
   uint2 yp[RT][4];   // y of a chunk, 16-bit, this lane's 4 rows per (tile, row block)
 
-  // The arithmetic of chunk c, from LDS buffer (c - c_begin) & 1: the state
-  // moves on to the chunk's end and accO gets the chunk's outputs O^T.
+  // The arithmetic of chunk c before B1 (buffer (c - c_begin) & 1): K S^T and
+  // S Q^T, X, N and the state update; accO gets S Q^T, and nh, nl the high
+  // and low parts of N for the output product after B1.
   float4v accO[RT][4];
-  auto compute = [&](int c, auto &&mid) {
+  half8 nh[RT][2], nl[RT][2];
+  auto compute_a = [&](int c, auto &&mid) {
     const int buf = (c - c_begin) & 1;
-    const _Float16 *cK = sKb + buf * C * KST, *cQ = sQb + buf * C * KST, *cV = sVb + buf * C * VST;
-    const uint4 *cT = sTPb + buf * TPS_U4, *cP = cT + NFRAG * 64;
+    const _Float16 *cK = sKb + buf * C * KST, *cQ = sQb + buf * C * KST;
+    const uint4 *cT = sTPb + buf * TPS_U4;
     const float *sc = reinterpret_cast<const float *>(cT + SC_AT);
     // transpose-read bases: lane (g4, i) reads row 4 g4 + i / 4, columns 4 (i % 4) .. + 3
     const _Float16 *kT = cK + (4 * g4 + (ln >> 2)) * KST + 4 * (ln & 3);
-    const _Float16 *vT = cV + (4 * g4 + (ln >> 2)) * VST + ic + 4 * (ln & 3);
+    const int vto = (4 * g4 + (ln >> 2)) * VST + ic + 4 * (ln & 3);
     // the K whose columns update the state: K itself, or K o e^{gamma_n - gamma} for the key gate
     const _Float16 *uT = KDA ? sKdb + buf * C * KST + (4 * g4 + (ln >> 2)) * KST + 4 * (ln & 3) : kT;
+
+    half8 kk0[4], kk1[4];   // kept K fragments: of row w (and, with two waves, of row w + 2)
+    if constexpr (GATE) {
+      const int R0 = w == 0 ? 1 : w == 1 ? 2 : 3;   // the rows of the off-diagonal blocks (R0.., S = w)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) kk0[kk] = perm_row(cK, KST, 16 * w + ln, kk, g4);
+#pragma unroll
+      for (int R = 1; R < 4; ++R) {
+        if (w < 3 && R >= R0) {
+          float4v a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) a = mfma32(kk0[kk], perm_row(cQ, KST, 16 * R + ln, kk, g4), a);
+          p_store(R, w, a, sc);
+        }
+      }
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        const bool diag = (w == 1 && R == 0) || (w == 2 && R == 1) || (w == 3 && R >= 2);
+        if (diag) {
+          float4v a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+            a = mfma32(perm_row(cK, KST, 16 * R + ln, kk, g4), perm_row(cQ, KST, 16 * R + ln, kk, g4), a);
+          p_store(R, R, a, sc);
+        }
+      }
+    }
 
     // S fragments (fp16) in kset order over the key channels
     half8 sf[RT][4];
@@ -986,7 +1088,15 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
       for (int kk = 0; kk < 4; ++kk) sf[t][kk] = pack_pair(accS[t][2 * kk], accS[t][2 * kk + 1]);
 
     // K S^T (rows r = 16 R + 4 g4 + ii, value row ln) and S Q^T (transposed read);
-    // each K and Q fragment serves every row tile of the wave
+    // each K and Q fragment serves every row tile of the wave.  With them,
+    // the wave's blocks of P (head gate): the block (R, R) from this row's
+    // fragments, and (R, S) for S < R from the K fragments of row S that the
+    // wave kept.  Blocks per wave (as if there were four compute waves;
+    // with two, wave w also takes wave w + 2's): wave 0 keeps K_0 for (1,0)
+    // (2,0) (3,0); wave 1 keeps K_1 for (2,1) (3,1) and makes (0,0); wave 2
+    // keeps K_2 for (3,2) and makes (1,1); wave 3 makes (2,2) (3,3).  (With
+    // the output gate, whose registers leave no room for the kept fragments,
+    // the wave forms the same blocks first, from fragments it reads for them.)
     float4v accX[RT][4];
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
@@ -1007,13 +1117,40 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
         accX[t][R] = ax;
         accO[t][R] = ao;
       }
+      if constexpr (!KDA && !GATE) {
+        // virtual wave vw in [0, 4): this wave's own w, and w + 2 with two waves
+#pragma unroll
+        for (int vw = 0; vw < 4; ++vw) {
+          if (vw % NW != w) continue;
+          half8 (&kp)[4] = vw < NW ? kk0 : kk1;
+          if (vw < 3 && R == vw) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) kp[kk] = kf[kk];
+          }
+          if (vw < 3 && R > vw) {
+            float4v a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) a = mfma32(kp[kk], qf[kk], a);
+            p_store(R, vw, a, sc);
+          }
+          const bool diag = (vw == 1 && R == 0) || (vw == 2 && R == 1) || (vw == 3 && R >= 2);
+          if (diag) {
+            float4v a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) a = mfma32(kf[kk], qf[kk], a);
+            p_store(R, R, a, sc);
+          }
+        }
+      }
     }
 
     mid();
 
-    // X = beta V - beta Gamma (K S^T), as fragments over the chunk rows
-    // (V rows 16 R + 4 g4 .. + 3 at this lane's value column, by transpose reads)
-    half8 xf[RT][2];
+    // X = beta V - beta Gamma (K S^T) as fp32 (V rows 16 R + 4 g4 .. + 3 at
+    // this lane's value column, by transpose reads of the high and low
+    // parts), then its high and low fp16 parts, as fragments over the chunk
+    // rows.  Without the delta correction this is N itself.
+    half8 xh[RT][2], xl[RT][2];
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
       const int r0 = 16 * R + 4 * g4;
@@ -1023,20 +1160,34 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
       const float bv[4] = {bb.x, bb.y, bb.z, bb.w}, gv[4] = {bg.x, bg.y, bg.z, bg.w};
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
-        const half4 vv = lds_read_tr(vT + 16 * t + 16 * R * VST);
+        float vx4[4];
+        if constexpr (CONV) {
+          const float4 vv = *reinterpret_cast<const float4 *>(sVt + (ic + 16 * t + ln) * Cfg::VTS + r0);
+          vx4[0] = vv.x; vx4[1] = vv.y; vx4[2] = vv.z; vx4[3] = vv.w;
+        } else {
+          const half4 vv = lds_read_tr(sV + vto + 16 * t + 16 * R * VST);
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          xf[t][R >> 1][(R & 1) * 4 + ii] =
-              ND ? (_Float16)(bv[ii] * (float)vv[ii]) : (_Float16)(bv[ii] * (float)vv[ii] - gv[ii] * accX[t][R][ii]);
+          for (int ii = 0; ii < 4; ++ii) vx4[ii] = (float)vv[ii];
+        }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const float vx = vx4[ii];
+          const float x = ND ? bv[ii] * vx : bv[ii] * vx - gv[ii] * accX[t][R][ii];
+          _Float16 hi, lo;
+          split16(x, hi, lo);
+          xh[t][R >> 1][(R & 1) * 4 + ii] = hi;
+          xl[t][R >> 1][(R & 1) * 4 + ii] = lo;
+        }
       }
     }
 
-    // N = T X;  N and diag(e^{gamma_n - gamma}) N as fragments over the chunk rows
-    half8 nf[RT][2], ndf[RT][2];
+    // N = T X (from both parts of X), its high and low parts for the output
+    // product and N~ = diag(e^{gamma_n - gamma}) N for the state update
+    half8 ndf[RT][2];
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
-      const half8 t0f = __builtin_bit_cast(half8, cT[frag_index(R, 0) * 64 + l]);
-      const half8 t1f = R >= 2 ? __builtin_bit_cast(half8, cT[frag_index(R, 1) * 64 + l]) : half8{};
+      const half8 t0f = ND ? half8{} : __builtin_bit_cast(half8, cT[frag_index(R, 0) * 64 + l]);
+      const half8 t1f = (ND || R < 2) ? half8{} : __builtin_bit_cast(half8, cT[frag_index(R, 1) * 64 + l]);
       const float4 dd = KDA ? make_float4(1.f, 1.f, 1.f, 1.f)
                             : *reinterpret_cast<const float4 *>(sc + 4 * C + 16 * R + 4 * g4);
       const float dv4[4] = {dd.x, dd.y, dd.z, dd.w};
@@ -1045,36 +1196,24 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
         float4v acc = {0.f, 0.f, 0.f, 0.f};
         if constexpr (ND) {
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) acc[ii] = (float)xf[t][R >> 1][(R & 1) * 4 + ii];
+          for (int ii = 0; ii < 4; ++ii)
+            acc[ii] = (float)xh[t][R >> 1][(R & 1) * 4 + ii] + (float)xl[t][R >> 1][(R & 1) * 4 + ii];
         } else {
-          acc = mfma32(t0f, xf[t][0], acc);
-          if (R >= 2) acc = mfma32(t1f, xf[t][1], acc);
+          acc = mfma32(t0f, xh[t][0], acc);
+          acc = mfma32(t0f, xl[t][0], acc);
+          if (R >= 2) {
+            acc = mfma32(t1f, xh[t][1], acc);
+            acc = mfma32(t1f, xl[t][1], acc);
+          }
         }
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-          nf[t][R >> 1][(R & 1) * 4 + ii] = (_Float16)acc[ii];
+          _Float16 hi, lo;
+          split16(acc[ii], hi, lo);
+          nh[t][R >> 1][(R & 1) * 4 + ii] = hi;
+          nl[t][R >> 1][(R & 1) * 4 + ii] = lo;
           ndf[t][R >> 1][(R & 1) * 4 + ii] = (_Float16)(acc[ii] * dv4[ii]);
         }
-      }
-    }
-
-    // O^T = Gamma (S Q^T) + N^T P^T:  row r = 16 R + ln of this lane
-#pragma unroll
-    for (int R = 0; R < 4; ++R) {
-      const int r = 16 * R + ln;
-      const float er = KDA ? 1.f : sc[C + r];
-      const half8 p0f = __builtin_bit_cast(half8, cP[frag_index(R, 0) * 64 + l]);
-      const half8 p1f = R >= 2 ? __builtin_bit_cast(half8, cP[frag_index(R, 1) * 64 + l]) : half8{};
-#pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        float4v acc = accO[t][R];
-        if constexpr (!KDA) {
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) acc[ii] *= er;
-        }
-        acc = mfma32(nf[t][0], p0f, acc);
-        if (R >= 2) acc = mfma32(nf[t][1], p1f, acc);
-        accO[t][R] = acc;
       }
     }
 
@@ -1110,17 +1249,56 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
       }
     }
   };
-  auto store_o = [&](int c) {
-    const int t0 = c * C;
+
+  // After B1: O^T = Gamma (S Q^T) + N^T P^T with the three terms of the high
+  // and low parts (key gate: P, from the workspace, has one part).  Row
+  // r = 16 R + ln of this lane.
+  auto compute_b = [&](int c, auto &&emit) {
+    const int buf = (c - c_begin) & 1;
+    const uint4 *cT = sTPb + buf * TPS_U4;
+    const float *sc = reinterpret_cast<const float *>(cT + SC_AT);
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
       const int r = 16 * R + ln;
-      if (t0 + r < T)
+      const float er = KDA ? 1.f : sc[C + r];
+      const uint4 *ph = KDA ? cT + NFRAG * 64 : sPh;
+      const half8 p0h = __builtin_bit_cast(half8, ph[frag_index(R, 0) * 64 + l]);
+      const half8 p1h = R >= 2 ? __builtin_bit_cast(half8, ph[frag_index(R, 1) * 64 + l]) : half8{};
+      half8 p0l = {}, p1l = {};
+      if constexpr (!KDA) {
+        p0l = __builtin_bit_cast(half8, sPl[frag_index(R, 0) * 64 + l]);
+        if (R >= 2) p1l = __builtin_bit_cast(half8, sPl[frag_index(R, 1) * 64 + l]);
+      }
 #pragma unroll
-        for (int t = 0; t < RT; ++t)
-          *reinterpret_cast<float4 *>(ob + (size_t)(t0 + r) * v_rs + 16 * t) =
-              make_float4(accO[t][R][0], accO[t][R][1], accO[t][R][2], accO[t][R][3]);
+      for (int t = 0; t < RT; ++t) {
+        float4v acc = accO[t][R];
+        if constexpr (!KDA) {
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) acc[ii] *= er;
+        }
+        acc = mfma32(nh[t][0], p0h, acc);
+        acc = mfma32(nl[t][0], p0h, acc);
+        if constexpr (!KDA) acc = mfma32(nh[t][0], p0l, acc);
+        if (R >= 2) {
+          acc = mfma32(nh[t][1], p1h, acc);
+          acc = mfma32(nl[t][1], p1h, acc);
+          if constexpr (!KDA) acc = mfma32(nh[t][1], p1l, acc);
+        }
+        accO[t][R] = acc;
+      }
+      emit(R);
     }
+  };
+  // the outputs of row block R of chunk c (issued as soon as they are made,
+  // between the products of the next row blocks)
+  auto store_o = [&](int c, int R) {
+    const int t0 = c * C;
+    const int r = 16 * R + ln;
+    if (t0 + r < T)
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+        *reinterpret_cast<float4 *>(ob + (size_t)(t0 + r) * v_rs + 16 * t) =
+            make_float4(accO[t][R][0], accO[t][R][1], accO[t][R][2], accO[t][R][3]);
   };
 
   // the wave's partial row sums of squares of the chunk's outputs (over its
@@ -1137,10 +1315,11 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
       if (g4 == 0) ss[(16 * R + ln) * NW + w] = p;
     }
   };
-  // after the barrier: the row sums over the waves (in wave order), then y
-  // of chunk c as 16-bit values in yp.  The z loads were issued half a chunk
-  // earlier; one wait for all of them here (for the compiler, a wait for a
-  // load issued after a store would also wait for that store).
+  // after the chunk's last barrier: the row sums over the waves (in wave
+  // order), then y of chunk c as 16-bit values in yp.  The z loads were
+  // issued half a chunk earlier; one wait for all of them here (for the
+  // compiler, a wait for a load issued after a store would also wait for
+  // that store).
   auto gate_finish = [&](int c) {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     // this lane's 4 rows of z per (tile, row block): keep one half of each
@@ -1150,9 +1329,9 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
     for (int t = 0; t < RT; ++t)
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        const uint4 v = zl[t][p];
-        const uint2 keep = godd ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y);
-        const uint2 send = godd ? make_uint2(v.x, v.y) : make_uint2(v.z, v.w);
+        const uint4 vz = zl[t][p];
+        const uint2 keep = godd ? make_uint2(vz.z, vz.w) : make_uint2(vz.x, vz.y);
+        const uint2 send = godd ? make_uint2(vz.x, vz.y) : make_uint2(vz.z, vz.w);
         const uint2 recv = make_uint2(__shfl_xor(send.x, 16, 64), __shfl_xor(send.y, 16, 64));
         zr[t][2 * p] = godd ? recv : keep;
         zr[t][2 * p + 1] = godd ? keep : recv;
@@ -1211,7 +1390,7 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
   if constexpr (GATE) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   lds_barrier();
   for (int c = c_begin; c < c_end; ++c) {
-    compute(c, [&] {
+    compute_a(c, [&] {
       if constexpr (GATE) {
         __builtin_amdgcn_sched_barrier(0);
         if (c > c_begin) gate_emit(c - 1);
@@ -1219,11 +1398,12 @@ __global__ __launch_bounds__(64 * (NW + LW), 1) void chunk_seq_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     });
-    if constexpr (GATE)
-      gate_partials(c);
-    else
-      store_o(c);
-    lds_barrier();
+    lds_barrier();   // B1: every wave's P blocks of chunk c are in LDS; V of chunk c has been read
+    compute_b(c, [&](int R) {
+      if constexpr (!GATE) store_o(c, R);
+    });
+    if constexpr (GATE) gate_partials(c);
+    lds_barrier();   // B2
     if constexpr (GATE) gate_finish(c);
   }
   if constexpr (GATE) gate_emit(c_end - 1);
@@ -1293,16 +1473,16 @@ hipError_t launch_order(const Shape &sh, void *ws, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename TQ, typename TG, int NW, int RT, bool KDA, int LW, bool CONV = false, bool GATE = false,
+template <typename TQ, typename TG, int NW, int RT, bool KDA, bool CONV = false, bool GATE = false,
           bool ND = false>
 hipError_t launch_seq(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
                       const void *beta, const uint4 *TPws, const float *S0, float *o, float *ST,
                       int nchunks, int c_begin, int c_end, hipStream_t st, const ConvIn &cv = ConvIn{},
                       const GateArgs &ga = GateArgs{}) {
-  using Cfg = SeqCfg<NW, RT, KDA, LW>;
+  using Cfg = SeqCfg<NW, RT, KDA, CONV>;
   constexpr int smem = GATE ? Cfg::SMEM_GATE : Cfg::SMEM;
   static_assert(smem <= 160 * 1024, "LDS");
-  auto kern = chunk_seq_kernel<TQ, TG, NW, RT, KDA, LW, CONV, GATE, ND>;
+  auto kern = chunk_seq_kernel<TQ, TG, NW, RT, KDA, CONV, GATE, ND>;
   hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   if (e != hipSuccess) return e;
   const int ntasks = sh.B * sh.Hv * Cfg::NS;
@@ -1435,26 +1615,26 @@ hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v
   auto seq = [&](int cb, int ce, const float *s0, hipStream_t s) {
     if constexpr (CONV)
       if (gate)
-        return launch_seq<TQ, TG, 4, 2, false, 4, CONV, true>(sh, qs, ks, v, g, beta, TPws, s0, nullptr, ST,
+        return launch_seq<TQ, TG, 4, 2, false, CONV, true>(sh, qs, ks, v, g, beta, TPws, s0, nullptr, ST,
                                                               nchunks, cb, ce, s, cv, *gate);
     if constexpr (!CONV)
       if (sh.no_delta) {
         if (heads > 128)
-          return launch_seq<TQ, TG, 4, 2, false, 4, false, false, true>(sh, qs, ks, v, g, beta, TPws, s0, o, ST,
+          return launch_seq<TQ, TG, 4, 2, false, false, false, true>(sh, qs, ks, v, g, beta, TPws, s0, o, ST,
                                                                         nchunks, cb, ce, s, cv);
         if (heads > 64)
-          return launch_seq<TQ, TG, 4, 1, false, 4, false, false, true>(sh, qs, ks, v, g, beta, TPws, s0, o, ST,
+          return launch_seq<TQ, TG, 4, 1, false, false, false, true>(sh, qs, ks, v, g, beta, TPws, s0, o, ST,
                                                                         nchunks, cb, ce, s, cv);
-        return launch_seq<TQ, TG, 2, 1, false, 4, false, false, true>(sh, qs, ks, v, g, beta, TPws, s0, o, ST,
+        return launch_seq<TQ, TG, 2, 1, false, false, false, true>(sh, qs, ks, v, g, beta, TPws, s0, o, ST,
                                                                       nchunks, cb, ce, s, cv);
       }
     if (heads > 128)
-      return launch_seq<TQ, TG, 4, 2, false, 4, CONV>(sh, qs, ks, v, g, beta, TPws, s0, o, ST, nchunks, cb,
+      return launch_seq<TQ, TG, 4, 2, false, CONV>(sh, qs, ks, v, g, beta, TPws, s0, o, ST, nchunks, cb,
                                                       ce, s, cv);
     if (heads > 64)
-      return launch_seq<TQ, TG, 4, 1, false, 4, CONV>(sh, qs, ks, v, g, beta, TPws, s0, o, ST, nchunks, cb,
+      return launch_seq<TQ, TG, 4, 1, false, CONV>(sh, qs, ks, v, g, beta, TPws, s0, o, ST, nchunks, cb,
                                                       ce, s, cv);
-    return launch_seq<TQ, TG, 2, 1, false, 4, CONV>(sh, qs, ks, v, g, beta, TPws, s0, o, ST, nchunks, cb,
+    return launch_seq<TQ, TG, 2, 1, false, CONV>(sh, qs, ks, v, g, beta, TPws, s0, o, ST, nchunks, cb,
                                                     ce, s, cv);
   };
   if ((e = launch_order(sh, ws, st)) != hipSuccess) return e;
@@ -1728,7 +1908,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(
     sP[rr * CST + 16 + cc] = (_Float16)0.f;
     sP[(32 + rr) * CST + 48 + cc] = (_Float16)0.f;
   }
-  invert_store(sAd, sAo, sT, sP, wc, w, l);
+  invert_store<true>(sAd, sAo, sT, sP, wc, w, l);
 }
 
 template <typename TQ, typename TG>
@@ -1753,14 +1933,14 @@ hipError_t launch_kda_t(const Shape &sh, const void *q, const void *k, const voi
   auto seq = [&](int cb, int ce, const float *s0, hipStream_t s) {
     if (sh.no_delta) {
       if (heads > 64)
-        return launch_seq<TQ, TG, 4, 1, true, 4, false, false, true>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks,
+        return launch_seq<TQ, TG, 4, 1, true, false, false, true>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks,
                                                                      cb, ce, s);
-      return launch_seq<TQ, TG, 2, 1, true, 4, false, false, true>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks,
+      return launch_seq<TQ, TG, 2, 1, true, false, false, true>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks,
                                                                    cb, ce, s);
     }
     if (heads > 64)
-      return launch_seq<TQ, TG, 4, 1, true, 4>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks, cb, ce, s);
-    return launch_seq<TQ, TG, 2, 1, true, 4>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks, cb, ce, s);
+      return launch_seq<TQ, TG, 4, 1, true>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks, cb, ce, s);
+    return launch_seq<TQ, TG, 2, 1, true>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks, cb, ce, s);
   };
   if ((e = launch_order(sh, ws, st)) != hipSuccess) return e;
   return pipelined(nchunks, !sh.packed && seq_overlap(heads), S0, ST, st, prep, seq);
@@ -1811,11 +1991,7 @@ hipError_t launch_chunk_mfma_conv(const Shape &sh, const void *xq, const void *x
   cv.q = base + chunk_mfma_workspace(sh);
   cv.k = (char *)cv.q + nqk * 2;
   cv.eps = eps;
-  if (sh.qkv == DType::BF16)
-    return sh.gate_t == DType::F32
-               ? launch_t<bf16_t, float, true>(sh, nullptr, nullptr, nullptr, g, beta, S0, o, ST, ws, st, cv, gate)
-               : launch_t<bf16_t, bf16_t, true>(sh, nullptr, nullptr, nullptr, g, beta, S0, o, ST, ws, st, cv,
-                                                gate);
+  if (sh.qkv != DType::F16) return hipErrorInvalidValue;   // q, k after the prologue are fp16 here
   return sh.gate_t == DType::F32
              ? launch_t<f16_t, float, true>(sh, nullptr, nullptr, nullptr, g, beta, S0, o, ST, ws, st, cv, gate)
              : launch_t<f16_t, bf16_t, true>(sh, nullptr, nullptr, nullptr, g, beta, S0, o, ST, ws, st, cv, gate);

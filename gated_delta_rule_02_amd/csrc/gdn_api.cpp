@@ -318,11 +318,12 @@ gdn_status check_prologue_args(const gdn_desc *d, int32_t x_dtype, float eps) {
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// The convolution runs inside the chunked kernels for bf16 raw inputs on
-// the matrix-core path with the per-head gate; otherwise the prologue
-// writes q, k, v into the workspace first.
+// The convolution runs inside the chunked kernels for bf16 raw inputs and
+// fp16 q, k (the prologue's output type) on the matrix-core path with the
+// per-head gate and the delta rule; otherwise the prologue writes q, k, v
+// into the workspace first.
 bool conv_fused(const gdn_desc *d, const gdn::Shape &sh, bool use_mfma, int32_t x_dtype) {
-  return use_mfma && !sh.key_gate && !sh.no_delta && x_dtype == GDN_BF16;
+  return use_mfma && !sh.key_gate && !sh.no_delta && x_dtype == GDN_BF16 && d->qkv_dtype == GDN_F16;
 }
 
 size_t conv_workspace(const gdn_desc *d, const gdn::Shape &sh, bool use_mfma, int32_t x_dtype) {

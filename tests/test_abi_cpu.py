@@ -107,10 +107,10 @@ def test_prologue_rejects(L):
 
 
 def test_workspace_query(L):
-    # matrix-core path: 13568 bytes per (batch, value head, 64-token chunk),
+    # matrix-core path: 7424 bytes per (batch, value head, 64-token chunk),
     # 62208 with the key-channel gate
-    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc())) == 2 * 6 * 2 * 13568
-    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(T=1))) == 2 * 6 * 1 * 13568
+    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc())) == 2 * 6 * 2 * 7424
+    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(T=1))) == 2 * 6 * 1 * 7424
     assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(gate=gdn.GATE_KEY_CHANNEL))) == 2 * 6 * 2 * 62208
     assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(gate=gdn.GATE_KEY_CHANNEL, dk=64, dv=64))) == 0
     assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(qkv_dtype=gdn.F32, gate_dtype=gdn.F32, chunk=32))) == 0
@@ -136,15 +136,16 @@ def test_null_desc(L):
 
 
 def test_conv_workspace_query(L):
-    d = desc()                       # B 2, 6 value heads, 2 chunks, matrix-core path
+    d = desc(qkv_dtype=gdn.F16)      # B 2, 6 value heads, 2 chunks, matrix-core path
     ws = L.gdn_fwd_workspace_bytes(ctypes.byref(d))
     B, T, Hk, Hv = d.B, d.T, d.Hk, d.Hv
-    # fused (bf16 raw inputs): the chunk matrices, then q and k after the prologue
+    # fused (bf16 raw inputs, fp16 q and k): the chunk matrices, then q and k after the prologue
     assert L.gdn_fwd_conv_workspace_bytes(ctypes.byref(d), gdn.BF16) == ws + 2 * B * T * Hk * 128 * 2
-    # fp32 raw inputs: q, k, v buffers (256-byte rounded) and the chunk matrices
+    # fp32 raw inputs, or bf16 q, k, v: q, k, v buffers (256-byte rounded) and the chunk matrices
     r = lambda x: (x + 255) // 256 * 256
     nqk, nv = B * T * Hk * 128 * 2, B * T * Hv * 128 * 2
     assert L.gdn_fwd_conv_workspace_bytes(ctypes.byref(d), gdn.F32) == 2 * r(nqk) + r(nv) + ws
+    assert L.gdn_fwd_conv_workspace_bytes(ctypes.byref(desc()), gdn.BF16) == 2 * r(nqk) + r(nv) + ws
     assert L.gdn_fwd_conv_workspace_bytes(ctypes.byref(d), gdn.F16) == 0    # raw fp16 is not supported
     assert L.gdn_fwd_conv_workspace_bytes(ctypes.byref(desc(Hv=5)), gdn.BF16) == 0
 
@@ -177,9 +178,9 @@ def test_gated_workspace_query(L):
     conv = L.gdn_fwd_conv_workspace_bytes(ctypes.byref(d), gdn.BF16)
     o_bytes = d.B * d.T * d.Hv * 128 * 4
     assert L.gdn_fwd_gated_workspace_bytes(ctypes.byref(d), gdn.BF16, gdn.BF16) == r(conv) + o_bytes
-    # B * Hv = 192 > 128 with bf16 raw inputs and 16-bit y: the gate runs
-    # inside the sequential pass
-    d = desc(B=4, Hk=16, Hv=48)
+    # B * Hv = 192 > 128 with bf16 raw inputs, fp16 q and k and 16-bit y:
+    # the gate runs inside the sequential pass
+    d = desc(B=4, Hk=16, Hv=48, qkv_dtype=gdn.F16)
     inside = L.gdn_fwd_conv_workspace_bytes(ctypes.byref(d), gdn.BF16)
     assert L.gdn_fwd_gated_workspace_bytes(ctypes.byref(d), gdn.BF16, gdn.BF16) == inside
     assert L.gdn_fwd_gated_workspace_bytes(ctypes.byref(d), gdn.BF16, gdn.F16) == inside
@@ -250,7 +251,7 @@ def test_varlen_checks(L):
     cu = P(FAKE + 11 * (1 << 36))
     need = L.gdn_fwd_varlen_workspace_bytes(ctypes.byref(d))
     # matrix-core path: chunk slots per value head = T / 64 + B = 20
-    assert need == 6 * (1000 // 64 + 5) * 13568 + 256   # and the sequence order (5 ints, in 256 bytes)
+    assert need == 6 * (1000 // 64 + 5) * 7424 + 256   # and the sequence order (5 ints, in 256 bytes)
     assert L.gdn_fwd_varlen_workspace_bytes(ctypes.byref(desc(B=5, T=1000, Hv=5))) == 0
     call = lambda dd, cu_, ptrs=p, ws=p[10], nbytes=need: L.gdn_fwd_chunked_varlen(
         ctypes.byref(dd), cu_, *ptrs[:5], None, *ptrs[5:7], ws, nbytes, None)
@@ -262,8 +263,11 @@ def test_varlen_checks(L):
     assert call(d, cu, bad) == 1
     assert call(desc(B=5, T=1000, dk=64), cu) == 3
     # the conv form and the prologue
+    d16 = desc(B=5, T=1000, qkv_dtype=gdn.F16)
+    assert L.gdn_fwd_varlen_workspace_bytes(ctypes.byref(d16)) == need
+    assert L.gdn_fwd_conv_varlen_workspace_bytes(ctypes.byref(d16), gdn.BF16) == \
+        need + 2 * 1000 * 2 * 128 * 2                    # plus q and k after the prologue
     cneed = L.gdn_fwd_conv_varlen_workspace_bytes(ctypes.byref(d), gdn.BF16)
-    assert cneed == need + 2 * 1000 * 2 * 128 * 2        # plus q and k after the prologue
     assert L.gdn_fwd_chunked_conv_varlen(ctypes.byref(d), None, gdn.BF16, *p[:4], 1e-6, *p[4:6], None,
                                          *p[6:8], p[10], cneed, None) == 1
     assert L.gdn_prologue_varlen(ctypes.byref(d), cu, gdn.BF16, *p[:4], 1e-6, P(cu.value), *p[5:7],

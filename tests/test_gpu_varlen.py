@@ -102,9 +102,13 @@ def test_varlen_conv_vs_oracle_and_two_calls():
     q, k, v = gdn.prologue_varlen(*xs, w, cut)
     o2, S2 = gdn.fwd_chunked_varlen(q, k, v, g, beta, cut, S0=to_torch(S0))
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2) and torch.equal(S1, S2), "conv inside differs from prologue + forward"
     o_ref, S_ref = oracle_per_sequence(inp, cu, S0, conv=True)
-    check("bf16", o1.cpu().numpy(), o_ref, S1.cpu().numpy(), S_ref, "varlen conv")
+    # the fused kernels keep v at fp32 where the prologue stores fp16: the
+    # two forms are each checked against the oracle and against each other
+    check("bf16", o1.cpu().numpy(), o_ref, S1.cpu().numpy(), S_ref, "varlen conv inside")
+    check("bf16", o2.cpu().numpy(), o_ref, S2.cpu().numpy(), S_ref, "varlen conv two calls")
+    check("bf16", o1.cpu().numpy(), o2.cpu().numpy(), S1.cpu().numpy(), S2.cpu().numpy(),
+          "varlen conv inside vs two calls")
 
 
 def test_prologue_varlen_resets_history():
