@@ -33,6 +33,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # one built with host AddressSanitizer and UBSan)
 LIB_PATH = os.environ.get("GDN_LIBRARY") or os.path.join(HERE, "libgdn.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "gdn.h")
+NOALLOC_SCRATCH_BYTES = 128 << 20   # GDN_NOALLOC_SCRATCH_BYTES
 
 F32, BF16, F16 = 0, 1, 2
 GATE_HEAD, GATE_KEY_CHANNEL = 0, 1
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.gdn_fwd_workspace_bytes.restype = S
         L.gdn_fwd_chunked.argtypes = [D, P, P, P, P, P, P, P, P, P, S, P]
         L.gdn_fwd_chunked.restype = I
+        L.gdn_fwd_chunked_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P]
+        L.gdn_fwd_chunked_noalloc.restype = I
         L.gdn_fwd_conv_workspace_bytes.argtypes = [D, I]
         L.gdn_fwd_conv_workspace_bytes.restype = S
         L.gdn_fwd_chunked_conv.argtypes = [D, I, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, S, P]
@@ -209,6 +212,27 @@ def fwd_chunked(q, k, v, g, beta, S0=None, chunk=64, o=None, S_T=None, stream=No
     g [B,T,Hv] or [B,T,Hv,dk]; beta [B,T,Hv]; S0 fp32 [B,Hv,dv,dk] or None.
     Returns (o fp32 [B,T,Hv,dv], S_T fp32 [B,Hv,dv,dk]); S_T may be S0.
     delta=False: the update without the delta correction."""
+    d, o, S_T = _chunked_args(q, k, v, g, beta, S0, chunk, o, S_T, delta)
+    L = lib()
+    ws_bytes = L.gdn_fwd_workspace_bytes(ctypes.byref(d))
+    ws = _workspace(ws_bytes, q.device)
+    check(L.gdn_fwd_chunked(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                            _ptr(S0), _ptr(o), _ptr(S_T), _ptr(ws), ws_bytes, _stream(stream)))
+    return o, S_T
+
+
+def fwd_chunked_noalloc(q, k, v, g, beta, S0=None, chunk=64, o=None, S_T=None, stream=None, delta=True):
+    """fwd_chunked through gdn_fwd_chunked_noalloc: no workspace argument (the
+    library's per-device scratch, GDN_NOALLOC_SCRATCH_BYTES, holds the chunk
+    matrices).  With o and S_T given, nothing is allocated."""
+    d, o, S_T = _chunked_args(q, k, v, g, beta, S0, chunk, o, S_T, delta)
+    check(lib().gdn_fwd_chunked_noalloc(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                        _ptr(S0), _ptr(o), _ptr(S_T), _stream(stream)))
+    return o, S_T
+
+
+def _chunked_args(q, k, v, g, beta, S0, chunk, o, S_T, delta):
+    """Checks of the chunked forward's tensors; the description and the outputs."""
     B, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
     _dev("q", q)
@@ -226,12 +250,7 @@ def fwd_chunked(q, k, v, g, beta, S0=None, chunk=64, o=None, S_T=None, stream=No
     _dev("S_T", S_T, (B, Hv, dv, dk), (torch.float32,))
     d = make_desc(B, T, Hk, Hv, dk, dv, chunk, _DTYPE_CODE[q.dtype], _DTYPE_CODE[g.dtype], gate,
                   RULE_DELTA if delta else RULE_NO_DELTA)
-    L = lib()
-    ws_bytes = L.gdn_fwd_workspace_bytes(ctypes.byref(d))
-    ws = _workspace(ws_bytes, q.device)
-    check(L.gdn_fwd_chunked(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                            _ptr(S0), _ptr(o), _ptr(S_T), _ptr(ws), ws_bytes, _stream(stream)))
-    return o, S_T
+    return d, o, S_T
 
 
 def fwd_chunked_conv(xq, xk, xv, conv_w, g, beta, S0=None, qkv_dtype=torch.float16, eps=1e-6,

@@ -1638,7 +1638,8 @@ hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v
                                                     ce, s, cv);
   };
   if ((e = launch_order(sh, ws, st)) != hipSuccess) return e;
-  return pipelined(nchunks, !sh.packed && seq_overlap(heads), S0, ST, st, prep, seq);
+  const bool overlap = !sh.packed && !sh.single_stream && seq_overlap(heads);
+  return pipelined(nchunks, overlap, S0, ST, st, prep, seq);
 }
 
 // ============================================================================
@@ -1943,7 +1944,8 @@ hipError_t launch_kda_t(const Shape &sh, const void *q, const void *k, const voi
     return launch_seq<TQ, TG, 2, 1, true>(sh, q, k, v, g, beta, wsu, s0, o, ST, nchunks, cb, ce, s);
   };
   if ((e = launch_order(sh, ws, st)) != hipSuccess) return e;
-  return pipelined(nchunks, !sh.packed && seq_overlap(heads), S0, ST, st, prep, seq);
+  const bool overlap = !sh.packed && !sh.single_stream && seq_overlap(heads);
+  return pipelined(nchunks, overlap, S0, ST, st, prep, seq);
 }
 
 }  // namespace

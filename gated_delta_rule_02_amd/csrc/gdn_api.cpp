@@ -7,6 +7,7 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <string>
 
 #include "gdn_launch.h"
@@ -384,10 +385,40 @@ gdn_status check_gate_args(const gdn_desc *d, int32_t z_dtype, int32_t y_dtype, 
 
 namespace {
 
+// The workspace of gdn_fwd_chunked_noalloc: one copy per device, held by the
+// code object from the time it is loaded on that device.  In host code
+// `scratch` names a host-side stand-in, not device memory: its device address
+// comes from hipGetSymbolAddress, looked up once per device and kept.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// The scratch's device address on the current device.  Two threads that
+// race the first lookup on a device store the same address.
+gdn_status scratch_address(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GDN_E_HIP, "no current device: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(GDN_E_UNSUPPORTED, "device %d: the scratch is kept for devices 0..%d", dev, kMaxDevices - 1);
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(GDN_E_HIP, "scratch address on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return GDN_OK;
+}
+
 // gdn_fwd_chunked and its packed-sequence form (cu: device offsets, or null).
+// noalloc: the workspace is the library's scratch (the workspace arguments
+// are ignored) and every launch goes on the caller's stream.
 gdn_status chunked_impl(const gdn_desc *d, const int32_t *cu, const void *q, const void *k, const void *v,
                         const void *g, const void *beta, const float *S0, float *o, float *S_T,
-                        void *workspace, size_t workspace_bytes, void *stream) {
+                        void *workspace, size_t workspace_bytes, void *stream, bool noalloc = false) {
   const bool packed = cu != nullptr;
   gdn::Shape sh;
   bool use_mfma = false;
@@ -402,6 +433,18 @@ gdn_status chunked_impl(const gdn_desc *d, const int32_t *cu, const void *q, con
   const int nins = packed ? 4 : 3;
   if ((st = check_chunked_ptrs(d, sh, ins, nins, g, beta, S0, o, S_T)) != GDN_OK) return st;
   const size_t need = use_mfma ? gdn::chunk_mfma_workspace(sh) : 0;
+  if (noalloc) {
+    if (need > GDN_NOALLOC_SCRATCH_BYTES)
+      return fail(GDN_E_WORKSPACE, "the problem needs %zu bytes of workspace; the no-allocation form "
+                  "holds %zu", need, (size_t)GDN_NOALLOC_SCRATCH_BYTES);
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (need > 0) {
+      if ((st = scratch_address(&workspace)) != GDN_OK) return st;
+      workspace_bytes = GDN_NOALLOC_SCRATCH_BYTES;
+    }
+    sh.single_stream = true;
+  }
   if ((st = check_workspace(d, workspace, workspace_bytes, need, ins, nins, g, beta, S0, o, S_T,
                             sh.key_gate, 0, packed)) != GDN_OK)
     return st;
@@ -452,6 +495,12 @@ gdn_status gdn_fwd_chunked(const gdn_desc *d, const void *q, const void *k, cons
                            const void *g, const void *beta, const float *S0, float *o, float *S_T,
                            void *workspace, size_t workspace_bytes, void *stream) {
   return chunked_impl(d, nullptr, q, k, v, g, beta, S0, o, S_T, workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_fwd_chunked_noalloc(const gdn_desc *d, const void *q, const void *k, const void *v,
+                                   const void *g, const void *beta, const float *S0, float *o,
+                                   float *S_T, void *stream) {
+  return chunked_impl(d, nullptr, q, k, v, g, beta, S0, o, S_T, nullptr, 0, stream, true);
 }
 
 gdn_status gdn_fwd_chunked_varlen(const gdn_desc *d, const int32_t *cu_seqlens, const void *q,

@@ -20,6 +20,7 @@ struct Shape {
   bool packed = false;
   const int *cu = nullptr;
   bool no_delta = false;   // the update without the delta correction
+  bool single_stream = false;   // all work on the caller's stream (no side stream)
 };
 
 // The gate's arguments for the chunked forward with the prologue inside,

@@ -175,15 +175,46 @@ gdn_status gdn_fwd_chunked(const gdn_desc *d, const void *q, const void *k,
                            void *stream);
 
 /*
+ * gdn_fwd_chunked_noalloc -- gdn_fwd_chunked without a workspace argument and
+ * without any allocation, for callers that cannot allocate device memory
+ * (code under stream capture, tight serving loops, hosts that forbid it).
+ *
+ * The chunk matrices live in a scratch array that the library's code object
+ * holds on each device, GDN_NOALLOC_SCRATCH_BYTES bytes, made when the
+ * library is loaded on that device and kept until the process ends.  The
+ * call allocates nothing (no device memory, no streams or events: all work
+ * runs on `stream`), and gives bit for bit the results of gdn_fwd_chunked
+ * with the same arguments.
+ *
+ *   d, q, k, v, g, beta, S0, o, S_T, stream   as for gdn_fwd_chunked
+ * Errors: as gdn_fwd_chunked; GDN_E_WORKSPACE when gdn_fwd_workspace_bytes(d)
+ * exceeds GDN_NOALLOC_SCRATCH_BYTES (head gate: at most 18078 (batch, value
+ * head, 64-token chunk) triples, e.g. B 4, Hv 48, T 4096; key-channel gate:
+ * at most 2157); GDN_E_HIP when the scratch address cannot be obtained on
+ * the current device.  Nothing in the scratch needs to start at zero.
+ * Every call on one device shares that device's scratch: calls that overlap
+ * in time on one device (on different streams, or from several threads
+ * without ordering) race and give wrong results.  Calls on one stream are
+ * ordered and safe.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+gdn_status gdn_fwd_chunked_noalloc(const gdn_desc *d, const void *q, const void *k,
+                                   const void *v, const void *g, const void *beta,
+                                   const float *S0, float *o, float *S_T, void *stream);
+
+/*
  * gdn_fwd_chunked_conv -- the prologue and the chunked forward in one call:
- * the same results as gdn_prologue(d, x_dtype, xq, xk, xv, conv_w, eps) into
- * q, k, v of d->qkv_dtype followed by gdn_fwd_chunked(d, q, k, v, g, beta,
- * S0) (the same arithmetic and roundings), without q, k, v as arguments.
- * For bf16 raw inputs on the matrix-core path with the per-head gate the
- * convolution runs inside the chunked kernels: q and k are made once per
- * (chunk, key head) and kept in the workspace, v is made as the sequential
- * pass loads it, so v never goes through memory.  Any other supported
- * combination runs the prologue into the workspace first.
+ * what gdn_prologue(d, x_dtype, xq, xk, xv, conv_w, eps) into q, k, v of
+ * d->qkv_dtype followed by gdn_fwd_chunked(d, q, k, v, g, beta, S0) computes,
+ * without q, k, v as arguments.
+ * For bf16 raw inputs, fp16 d->qkv_dtype, the per-head gate and the delta
+ * rule on the matrix-core path the convolution runs inside the chunked
+ * kernels: q and k are made once per (chunk, key head), rounded to fp16 and
+ * kept in the workspace; v is made as the sequential pass loads it and stays
+ * fp32 (it is not rounded to fp16 and never goes through memory), so this
+ * form is slightly more accurate than the two calls and not bit-identical to
+ * them.  Any other supported combination runs the prologue into the
+ * workspace first and gives the two calls' results bit for bit.
  *
  *   x_dtype, xq, xk, xv, conv_w, eps   as for gdn_prologue
  *   g, beta, S0, o, S_T                as for gdn_fwd_chunked
@@ -269,7 +300,7 @@ gdn_status gdn_output_gate(const gdn_desc *d, const float *o, int32_t z_dtype,
  *     gdn_fwd_chunked_conv(d, x_dtype, xq, xk, xv, conv_w, eps, g, beta, S0, o, S_T)
  *     gdn_output_gate(d, o, x_dtype, z, gain, norm_eps, y_dtype, y).
  * When the convolution runs inside the chunked kernels (bf16 raw inputs,
- * matrix-core path, per-head gate), B * Hv > 128 (a workgroup of the
+ * fp16 d->qkv_dtype, matrix-core path, per-head gate), B * Hv > 128 (a workgroup of the
  * sequential pass then holds a whole value head) and y is 16-bit, the gate
  * is applied there and o never goes through memory; otherwise o is kept in
  * the workspace and the gate runs after the forward.

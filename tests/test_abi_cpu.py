@@ -74,6 +74,45 @@ def test_fwd_rejects_null_and_misaligned(L):
     assert fwd(L, desc(), p, S0=FAKE + 7 * (1 << 32) + 4) == 4
 
 
+def noalloc(L, d, ptrs=None):
+    p = [FAKE + i * (1 << 32) for i in range(7)] if ptrs is None else ptrs
+    P = ctypes.c_void_p
+    return L.gdn_fwd_chunked_noalloc(ctypes.byref(d), *[P(x) for x in p[:5]], None, P(p[5]), P(p[6]), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 1), (dict(gate=3), 1), (dict(Hv=5), 2), (dict(dk=64), 3),
+    (dict(B=8, T=4096, Hk=16, Hv=48), 5),                 # 174 MiB of chunk matrices > 128 MiB
+    (dict(B=2, T=4096, Hk=32, Hv=32, gate=gdn.GATE_KEY_CHANNEL), 5),   # 4096 x 62208 B
+])
+def test_noalloc_rejects(L, kw, status):
+    d = desc(**kw)
+    assert noalloc(L, d) == status
+    assert L.gdn_last_error()
+    if status == 5:
+        assert b"no-allocation" in L.gdn_last_error()
+        assert L.gdn_fwd_workspace_bytes(ctypes.byref(d)) > gdn.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_scratch_size_matches_header(L):
+    text = open(gdn.HEADER).read()
+    assert "#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)" in text
+    assert gdn.NOALLOC_SCRATCH_BYTES == 128 << 20
+    # the largest problems the scratch holds: B4 Hv48 T4096 (head gate), B1 H32 T4096 (key gate)
+    for d in (desc(B=4, T=4096, Hk=16, Hv=48), desc(B=1, T=4096, Hk=32, Hv=32, gate=gdn.GATE_KEY_CHANNEL)):
+        assert 0 < L.gdn_fwd_workspace_bytes(ctypes.byref(d)) <= gdn.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_rejects_null_and_misaligned(L):
+    p = [FAKE + i * (1 << 32) for i in range(7)]
+    for i in range(7):
+        bad = list(p)
+        bad[i] = 0
+        assert noalloc(L, desc(), bad) == 1
+        bad[i] = p[i] + 8
+        assert noalloc(L, desc(), bad) == 4
+
+
 def test_fwd_rejects_overlaps(L):
     p = [FAKE + i * (1 << 32) for i in range(7)]
     o_on_v = list(p)
