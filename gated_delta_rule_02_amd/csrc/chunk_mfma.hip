@@ -507,21 +507,21 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
 // loads at all (their only memory traffic is LDS reads and the output
 // stores, and a wait for a load never waits for stores).
 //
-// Two barriers per chunk c.  Before the first (B1) the loading waves form
-// the chunk's P (the decayed masked Q K^T) from its K and Q and the compute
-// waves read the chunk's V; after it the compute waves read P, and the
-// loading waves write V of chunk c + 1 (before the second barrier, B2), so
-// V and P need one LDS buffer each.  K, Q, T and the per-token scalars of chunk c + 1
-// are written during chunk c into the other of two buffers and are complete
-// at B2.
+// Two barriers per chunk c.  Before the first (B1) the compute waves read the
+// chunk's V and form its P (the decayed masked Q K^T) from the K and Q
+// fragments they read for K S^T and S Q^T; after B1 they read P for the
+// output product while the loading waves write V of chunk c + 1 (complete at
+// the second barrier, B2), so V and P need one LDS buffer each.  K, Q, T and
+// the per-token scalars of chunk c + 1 are written during chunk c into the
+// other of two buffers and are complete at B2.
 //
 // Precision: X, N (as the operand of the output product) and P are each
 // split into an fp16 high part and an fp16 low part (x = hi + lo with
 // |lo| <= 2^-11 |x|), and their products take the three terms
-// hi*hi + lo*hi + hi*lo; with the prologue inside, v keeps its fp32 value the
-// same way (high and low parts in LDS).  An fp16 operand alone rounds each of
-// these to 11 bits, which on the conv-prefill workload costs up to 2e-2 of
-// rms(o) over a whole output tensor; the splits bring that to about 6e-3.
+// hi*hi + lo*hi + hi*lo; with the prologue inside, v stays fp32 (V^T in LDS)
+// up to X.  An fp16 operand alone rounds each of these to 11 bits, which on
+// the conv-prefill workload costs up to 2e-2 of
+// rms(o) over a whole output tensor; the splits bring that below 1e-2.
 template <int NW, int RT, bool KDA, bool VLO>
 struct SeqCfg {
   static constexpr int LW = 4;                 // loading waves
