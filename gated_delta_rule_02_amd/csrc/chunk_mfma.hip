@@ -98,6 +98,11 @@ __device__ __forceinline__ half8 to_half8(uint4 u, bf16_t) {
   return h;
 }
 __device__ __forceinline__ half8 to_half8(uint4 u, f16_t) { return __builtin_bit_cast(half8, u); }
+__device__ __forceinline__ half4 to_half4(uint2 u, bf16_t) {
+  return half4{(_Float16)__uint_as_float(u.x << 16), (_Float16)__uint_as_float(u.x & 0xFFFF0000u),
+               (_Float16)__uint_as_float(u.y << 16), (_Float16)__uint_as_float(u.y & 0xFFFF0000u)};
+}
+__device__ __forceinline__ half4 to_half4(uint2 u, f16_t) { return __builtin_bit_cast(half4, u); }
 
 // Eight fp32 values narrowed to a 16-bit type, as stored to memory.
 __device__ __forceinline__ uint4 pack8(const float (&x)[8], f16_t) {
@@ -1654,8 +1659,7 @@ hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v
 // a reference token, on the matrix cores (details where A and P are formed).
 constexpr int GST = DK + 4;                              // gamma row stride (fp32)
 constexpr int KP_OFF_K = 0;                              // [C][KST] fp16
-constexpr int KP_OFF_Q = KP_OFF_K + C * KST * 2;         // [C][KST] fp16
-constexpr int KP_OFF_G = KP_OFF_Q + C * KST * 2;         // [C][GST] fp32 (g, then gamma)
+constexpr int KP_OFF_G = KP_OFF_K + C * KST * 2;         // [C][GST] fp32 (g, then gamma)
 constexpr int KP_OFF_B = KP_OFF_G + C * GST * 4;         // beta [C] fp32
 constexpr int KP_SMEM = KP_OFF_B + C * 4;
 // once A and P are in registers, the matrices of the inverse reuse K and Q
@@ -1663,7 +1667,9 @@ constexpr int KP_OFF_T = 0;
 constexpr int KP_OFF_P = KP_OFF_T + C * CST * 2;
 constexpr int KP_OFF_AO = KP_OFF_P + C * CST * 2;
 constexpr int KP_OFF_AD = KP_OFF_AO + C * CST * 2;
-static_assert(KP_OFF_AD + 4 * 16 * DST * 4 <= KP_OFF_G, "inverse matrices overlap gamma");
+static_assert(KP_OFF_AD + 4 * 16 * DST * 4 <= KP_OFF_B, "inverse matrices overlap beta");
+// three workgroups per compute unit
+static_assert(3 * KP_SMEM <= 160 * 1024, "LDS");
 
 // Eight consecutive channels of row `row` at kset(g4, kk) of a row-major fp32 matrix.
 __device__ __forceinline__ void perm_row_f32(const float *M, int st, int row, int kk, int g4, float (&x)[8]) {
@@ -1674,13 +1680,12 @@ __device__ __forceinline__ void perm_row_f32(const float *M, int st, int row, in
 }
 
 template <typename TQ, typename TG>
-__global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(
+__global__ __launch_bounds__(kThreads, 3) void kda_prep_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TG *__restrict__ g,
     const TG *__restrict__ beta, uint4 *__restrict__ ws, int Tall, int Hk, int Hv, int nchunks, int c0,
     Seqs sq) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   _Float16 *sK = reinterpret_cast<_Float16 *>(smem + KP_OFF_K);
-  _Float16 *sQ = reinterpret_cast<_Float16 *>(smem + KP_OFF_Q);
   float *sG = reinterpret_cast<float *>(smem + KP_OFF_G);
   float *sB = reinterpret_cast<float *>(smem + KP_OFF_B);
   _Float16 *sT = reinterpret_cast<_Float16 *>(smem + KP_OFF_T);
@@ -1706,7 +1711,12 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(
   const size_t bt0 = (size_t)start + t0;
   uint4 *wc = ws + (ws_chain(sq, b, h, Hv, nchunks, start) + c) * KDA_CHUNK_U4;
 
-  // K, Q, g and beta of the chunk; rows past the end are zero (so gamma stays flat there)
+  // K, g and beta of the chunk into LDS; rows past the end are zero (so gamma
+  // stays flat there).  Q stays in registers: qh holds the rows this thread
+  // loaded (for Q o e^gamma), qd the rows of the wave's block row (for the
+  // diagonal tile of P).
+  half8 qh[4];
+  uint2 qd[8];
   {
     constexpr int GW = sizeof(TG) == 4 ? 2 : 1;  // 16-byte pieces per 8 gate values
     uint4 uk[4], uq[4], ug[4][GW];
@@ -1721,6 +1731,15 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(
       for (int u = 0; u < GW; ++u) ug[it][u] = *reinterpret_cast<const uint4 *>(g + goff + 4 * u);
     }
     const TG braw = beta[(bt0 + min(tid & 63, n - 1)) * Hv + h];
+    // Q of the wave's block row, rows 16 w + ln at the channels kset(g4, kk)
+    {
+      const TQ *qp = q + ((bt0 + min(16 * w + ln, n - 1)) * Hk + kh) * DK + 4 * g4;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        qd[2 * kk] = *reinterpret_cast<const uint2 *>(qp + 32 * kk);
+        qd[2 * kk + 1] = *reinterpret_cast<const uint2 *>(qp + 32 * kk + 16);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
     const half8 hz = {};
 #pragma unroll
@@ -1728,7 +1747,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(
       const int row = (tid >> 4) + 16 * it;
       const bool ok = row < n;
       *reinterpret_cast<half8 *>(sK + row * KST + (tid & 15) * 8) = ok ? to_half8(uk[it], TQ{}) : hz;
-      *reinterpret_cast<half8 *>(sQ + row * KST + (tid & 15) * 8) = ok ? to_half8(uq[it], TQ{}) : hz;
+      qh[it] = ok ? to_half8(uq[it], TQ{}) : hz;
       float gv[8];
       if constexpr (sizeof(TG) == 4) {
         const float4 a = __builtin_bit_cast(float4, ug[it][0]), bq = __builtin_bit_cast(float4, ug[it][1]);
@@ -1778,7 +1797,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(
       const int e = tid + kThreads * it;
       const int row = e >> 4, c8 = (e & 15) * 8;
       const half8 kv = *reinterpret_cast<const half8 *>(sK + row * KST + c8);
-      const half8 qv = *reinterpret_cast<const half8 *>(sQ + row * KST + c8);
+      const half8 qv = qh[it];
       half8 kg, qg, kd;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -1821,7 +1840,9 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(
         perm_row_f32(sG, GST, 16 * R + ln, kk, g4, gr);
         perm_row_f32(sG, GST, p, kk, g4, gp);
         const half8 kv = perm_row(sK, KST, 16 * R + ln, kk, g4);
-        const half8 qv = perm_row(sQ, KST, 16 * R + ln, kk, g4);
+        const half4 qa = to_half4(qd[2 * kk], TQ{}), qb = to_half4(qd[2 * kk + 1], TQ{});
+        const half8 qv = 16 * R + ln < n ? half8{qa[0], qa[1], qa[2], qa[3], qb[0], qb[1], qb[2], qb[3]}
+                                         : half8{};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float f = __expf(gr[e] - gp[e]), fi = __expf(gp[e] - gr[e]);
@@ -1840,11 +1861,13 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(
           const int r = 16 * R + 4 * g4 + ii, s_ = 16 * R + ln;
           float a = 0.f, pp = 0.f;
           if (s_ <= r) {
+            const TQ *qr = q + ((bt0 + min(r, n - 1)) * Hk + kh) * DK;
             for (int j = 0; j < DK; ++j) {
               const float e = __expf(sG[r * GST + j] - sG[s_ * GST + j]);
               const float ks = (float)sK[s_ * KST + j];
+              const float qv = r < n ? (float)(_Float16)to_f32(qr[j]) : 0.f;
               a += (float)sK[r * KST + j] * ks * e;
-              pp += (float)sQ[r * KST + j] * ks * e;
+              pp += qv * ks * e;
             }
           }
           ad[ii] = a;
@@ -1880,7 +1903,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prep_kernel(
       }
     }
   }
-  lds_barrier();  // K and Q are no longer read: T, P, A take their place
+  lds_barrier();  // K and gamma are no longer read: T, P, A take their place
 
   // A (diagonal blocks fp32 strictly lower, blocks below fp16) and P (lower incl. diagonal)
   {
