@@ -179,8 +179,21 @@ __device__ __forceinline__ void chunk_scalars(float g, float beta, float *sc, in
   sc[4 * C + lane] = __expf(gC - x);
 }
 
+// fp16 high and low parts of x: x = hi + lo to about 22 bits.
+// The low part is x - hi (exact in fp32) rounded to fp16 by one mixed-precision
+// fma (hi read as fp16, -1 and x as fp32), written out as the instruction:
+// the compiler otherwise widens hi, subtracts and narrows again.
+__device__ __forceinline__ void split16(float x, _Float16 &hi, _Float16 &lo) {
+  hi = (_Float16)x;
+  const uint32_t h = __builtin_bit_cast(uint16_t, hi);
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
+  lo = __builtin_bit_cast(_Float16, (uint16_t)r);
+}
+
 // T = (I + A)^{-1} for a 64 x 64 unit lower-triangular I + A, then T (and,
-// WITH_P, P after it) stored as fragments at dst.  On entry the strictly
+// NP >= 1, P after it; NP = 2, P as high part sP and low part sPl) stored as
+// fragments at dst.  On entry the strictly
 // lower 16 x 16 diagonal blocks of A are in sAd (fp32), its blocks below the
 // diagonal in sAo (fp16), and sT (and sP) have zero blocks (0,1) and (2,3)
 // (the fragments read them).  Called by all 256 threads; wave w owns block
@@ -188,9 +201,10 @@ __device__ __forceinline__ void chunk_scalars(float g, float beta, float *sc, in
 //
 // Diagonal blocks: forward substitution in fp32 (wave w -> block w).  Blocks
 // below: column by column, T_RS = -T_RR sum_M A_RM T_MS, on 16x16x16 MFMAs.
-template <bool WITH_P>
+template <int NP>
 __device__ __forceinline__ void invert_store(const float *sAd, const _Float16 *sAo, _Float16 *sT,
-                                             const _Float16 *sP, uint4 *__restrict__ dst, int w, int l) {
+                                             const _Float16 *sP, const _Float16 *sPl, uint4 *__restrict__ dst,
+                                             int w, int l) {
   const int g4 = l >> 4, ln = l & 15;
   lds_barrier();
   // diagonal blocks of T by forward substitution (wave w -> block w):
@@ -254,9 +268,12 @@ __device__ __forceinline__ void invert_store(const float *sAd, const _Float16 *s
     for (int kk = 0; kk < 2; ++kk)
       if (kk == 0 || w >= 2) {
         dst[frag_index(w, kk) * 64 + l] = __builtin_bit_cast(uint4, perm_row(sT, CST, 16 * w + ln, kk, g4));
-        if constexpr (WITH_P)
+        if constexpr (NP >= 1)
           dst[(NFRAG + frag_index(w, kk)) * 64 + l] =
               __builtin_bit_cast(uint4, perm_row(sP, CST, 16 * w + ln, kk, g4));
+        if constexpr (NP == 2)
+          dst[(2 * NFRAG + frag_index(w, kk)) * 64 + l] =
+              __builtin_bit_cast(uint4, perm_row(sPl, CST, 16 * w + ln, kk, g4));
       }
   }
 }
@@ -266,10 +283,14 @@ __device__ __forceinline__ void invert_store(const float *sAd, const _Float16 *s
 // K o e^{gamma_n - gamma} (fp16, 64 x 128 row-major, rows past the end of the
 // sequence zero); beta[64] and Gamma_n[128] (fp32).
 // Workspace of the head gate per (batch, value head, chunk): T fragments,
-// then the per-token scalars of chunk_scalars (5 x 64 fp32).  (Its P is
-// formed in the sequential pass.)
+// then the per-token scalars of chunk_scalars (5 x 64 fp32); P is formed in
+// the sequential pass.  With at most 64 chains (the sequential pass then
+// runs two compute waves per workgroup and is bound by its chain of chunks)
+// the prep also forms P and stores its high and low parts after T.
 constexpr int GDN_SC = NFRAG * 64;
 constexpr int GDN_CHUNK_U4 = GDN_SC + 5 * C / 4;
+constexpr int GDN_SC_P = 3 * NFRAG * 64;
+constexpr int GDN_CHUNK_U4_P = GDN_SC_P + 5 * C / 4;
 constexpr int KDA_KG = 2 * NFRAG * 64;
 constexpr int KDA_QG = KDA_KG + C * DK / 8;
 constexpr int KDA_KD = KDA_QG + C * DK / 8;
@@ -294,14 +315,22 @@ constexpr int P_OFF_AD = P_OFF_AO + C * CST * 2;        // [4][16][DST] fp32
 constexpr int P_OFF_GB = P_OFF_Q + C * KST * 2;         // then 2 x grp x C fp32
 constexpr int P_SC_BYTES = 5 * C * 4, P_TAP_BYTES = 2 * DK * 16;
 static_assert(P_OFF_AD + 4 * 16 * DST * 4 <= P_OFF_GB, "per-head matrices overlap the gates");
-inline size_t prep_smem(int grp, bool conv) {
-  return P_OFF_GB + (size_t)2 * grp * C * 4 + (conv ? P_TAP_BYTES : P_SC_BYTES);
+// PW (P to the workspace): its high and low parts after the inverse's
+// matrices (over Q, which is read only before the head loop), and the gates
+// after them
+constexpr int P_OFF_PH = P_OFF_AD + 4 * 16 * DST * 4;   // [C][CST] fp16
+constexpr int P_OFF_PL = P_OFF_PH + C * CST * 2;        // [C][CST] fp16
+constexpr int P_OFF_GB_P = P_OFF_PL + C * CST * 2;
+inline size_t prep_smem(int grp, bool conv, bool pw) {
+  return (pw ? P_OFF_GB_P : P_OFF_GB) + (size_t)2 * grp * C * 4 + (conv ? P_TAP_BYTES : P_SC_BYTES);
 }
 
 // CONV: q and k are computed here from the raw inputs of cv (convolution,
 // SiLU, L2 normalisation) and written to cv.q and cv.k for the sequential
-// pass; the q and k arguments are not read.
-template <typename TQ, typename TG, bool CONV>
+// pass; the q and k arguments are not read.  PW: P = L o Q K^T with the
+// decays too, once per key head as P0 = masked Q K^T, then scaled per value
+// head; its high and low parts go to the workspace after T.
+template <typename TQ, typename TG, bool CONV, bool PW>
 __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
     const TQ *__restrict__ q, const TQ *__restrict__ k, const TG *__restrict__ g,
     const TG *__restrict__ beta, uint4 *__restrict__ Tws, int Tall, int Hk, int Hv, int nchunks, int c0,
@@ -311,7 +340,10 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
   _Float16 *sT = reinterpret_cast<_Float16 *>(smem + P_OFF_T);
   _Float16 *sAo = reinterpret_cast<_Float16 *>(smem + P_OFF_AO);
   float *sAd = reinterpret_cast<float *>(smem + P_OFF_AD);
-  float *sGB = reinterpret_cast<float *>(smem + P_OFF_GB);   // [2][grp][C]: gate, beta per head
+  _Float16 *sQ = reinterpret_cast<_Float16 *>(smem + P_OFF_Q);
+  _Float16 *sPh = reinterpret_cast<_Float16 *>(smem + P_OFF_PH);   // PW: P, high part
+  _Float16 *sPl = reinterpret_cast<_Float16 *>(smem + P_OFF_PL);   // ... and low part
+  float *sGB = reinterpret_cast<float *>(smem + (PW ? P_OFF_GB_P : P_OFF_GB));   // [2][grp][C]: gate, beta per head
   float *sc = sGB + 2 * (Hv / Hk) * C;
   const float *sGam = sc;
   const float *sB = sc + 2 * C;
@@ -345,7 +377,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
   // before the sequence start) at the lane's 8 channels.
   {
     constexpr int NL = CONV ? 7 : 4;
-    uint4 uk[NL], uq[CONV ? NL : 1];
+    uint4 uk[NL], uq[(CONV || PW) ? NL : 1];
     if constexpr (CONV) {
 #pragma unroll
       for (int j = 0; j < 7; ++j) {
@@ -362,6 +394,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
         const int row = (tid >> 4) + 16 * it;
         const size_t off = ((bt0 + min(row, n - 1)) * Hk + kh) * DK + ch;
         uk[it] = *reinterpret_cast<const uint4 *>(k + off);
+        if constexpr (PW) uq[it] = *reinterpret_cast<const uint4 *>(q + off);
       }
     }
     // gate and beta of every value head of the group, [head][token] in LDS
@@ -416,14 +449,17 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
         }
       };
       conv_rows(uk, sTap, sK, ky);
-      // q's rows go to LDS too, where nothing reads them: without these
-      // stores the compiler's schedule of this kernel spills registers
-      conv_rows(uq, sTap + DK, reinterpret_cast<_Float16 *>(smem + P_OFF_Q), qy);
+      // q's rows go to LDS too (without PW nothing reads them there, but
+      // without these stores the compiler's schedule of this kernel spills
+      // registers)
+      conv_rows(uq, sTap + DK, sQ, qy);
     } else {
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const int row = (tid >> 4) + 16 * it;
         *reinterpret_cast<half8 *>(sK + row * KST + ch) = row < n ? to_half8(uk[it], TQ{}) : hz;
+        if constexpr (PW)
+          *reinterpret_cast<half8 *>(sQ + row * KST + ch) = row < n ? to_half8(uq[it], TQ{}) : hz;
       }
     }
   }
@@ -447,6 +483,25 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
       accG[d] = ag;
     }
   }
+  // PW: P0 row w (tiles (w, w - d)) = Q rows 16 w .. times K rows 16 (w - d) ..
+  float4v accP[PW ? 4 : 1];
+  if constexpr (PW) {
+    const _Float16 *qw = sQ + (16 * w + ln) * KST + 8 * g4;
+    const _Float16 *kw = sK + (16 * w + ln) * KST + 8 * g4;
+    half8 aq[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) aq[kk] = *reinterpret_cast<const half8 *>(qw + 32 * kk);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      float4v ap = {0.f, 0.f, 0.f, 0.f};
+      if (d <= w) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          ap = mfma32(aq[kk], *reinterpret_cast<const half8 *>(kw - 16 * d * KST + 32 * kk), ap);
+      }
+      accP[d] = ap;
+    }
+  }
   // All loads so far have landed (nothing is stored yet): said explicitly so
   // that the head loop does not wait on them again behind its own stores.
   // (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15.)
@@ -467,8 +522,8 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
     lds_barrier();  // K, or the previous head's T, has been read out
     if (tid < C) chunk_scalars(sGB[hv * C + tid], sGB[(grp + hv) * C + tid], sc, tid);
     lds_barrier();
-    uint4 *wch = Tws + (ws_chain(sq, b, h, Hv, nchunks, start) + c) * GDN_CHUNK_U4;
-    if (tid < 5 * C / 4) wch[GDN_SC + tid] = reinterpret_cast<const uint4 *>(sc)[tid];
+    uint4 *wch = Tws + (ws_chain(sq, b, h, Hv, nchunks, start) + c) * (PW ? GDN_CHUNK_U4_P : GDN_CHUNK_U4);
+    if (tid < 5 * C / 4) wch[(PW ? GDN_SC_P : GDN_SC) + tid] = reinterpret_cast<const uint4 *>(sc)[tid];
     // A: diagonal blocks fp32 (strictly lower), off-diagonal blocks fp16
     {
       const int r0 = 16 * w + 4 * g4;
@@ -499,8 +554,30 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
       const int rr = tid >> 4, cc = tid & 15;
       sT[rr * CST + 16 + cc] = (_Float16)0.f;
       sT[(32 + rr) * CST + 48 + cc] = (_Float16)0.f;
+      if constexpr (PW) {
+        // P = P0 e^{gamma_r - gamma_s} (s <= r), high and low parts
+        _Float16 *ph = sPh + r0 * CST + 16 * w + ln, *pl = sPl + r0 * CST + 16 * w + ln;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          if (d <= w) {
+            const float gs = sGam[16 * (w - d) + ln];
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+              const bool keep = d > 0 || ln <= 4 * g4 + ii;
+              _Float16 hi, lo;
+              split16(keep ? __expf(gr[ii] - gs) * accP[d][ii] : 0.f, hi, lo);
+              ph[ii * CST - 16 * d] = hi;
+              pl[ii * CST - 16 * d] = lo;
+            }
+          }
+        }
+        sPh[rr * CST + 16 + cc] = (_Float16)0.f;
+        sPh[(32 + rr) * CST + 48 + cc] = (_Float16)0.f;
+        sPl[rr * CST + 16 + cc] = (_Float16)0.f;
+        sPl[(32 + rr) * CST + 48 + cc] = (_Float16)0.f;
+      }
     }
-    invert_store<false>(sAd, sAo, sT, nullptr, wch, w, l);
+    invert_store<PW ? 2 : 0>(sAd, sAo, sT, sPh, sPl, wch, w, l);
   }
 }
 
@@ -538,11 +615,14 @@ struct SeqCfg {
   static constexpr int VST = WGC + 8;          // sV row stride
   static constexpr int NKQ = (C * DK / 8) / LT;     // 16-byte K (and Q) pieces per loading thread
   static constexpr int NV = (C * WGC / 8) / LT;     // 16-byte V pieces per loading thread
-  static constexpr int NFR = KDA ? 2 * NFRAG : NFRAG;   // fragments from the workspace: T (key gate: T, P)
+  // head gate with two compute waves: P (high and low) comes from the workspace
+  static constexpr bool PWS = !KDA && NW == 2;
+  // fragments from the workspace: T (key gate: T, P; PWS: T, P high, P low)
+  static constexpr int NFR = KDA ? 2 * NFRAG : PWS ? 3 * NFRAG : NFRAG;
   static constexpr int NTP = (NFR * 64 + LT - 1) / LT;  // their pieces per loading thread
   static constexpr int NSC = KDA ? C + DK : 5 * C;       // fp32 scalars per chunk
-  static constexpr int SC_U4 = KDA ? KDA_SC : GDN_SC;      // their offset in the chunk's workspace
-  static constexpr int CHUNK_U4 = KDA ? KDA_CHUNK_U4 : GDN_CHUNK_U4;  // workspace per chunk
+  static constexpr int SC_U4 = KDA ? KDA_SC : PWS ? GDN_SC_P : GDN_SC;   // their offset in the chunk's workspace
+  static constexpr int CHUNK_U4 = KDA ? KDA_CHUNK_U4 : PWS ? GDN_CHUNK_U4_P : GDN_CHUNK_U4;   // workspace per chunk
   static constexpr int TPS_U4 = NFR * 64 + NSC / 4;        // fragments, then the scalars (16 B units)
   static constexpr int OFF_K = 0;                          // 2 x [C][KST] fp16
   static constexpr int OFF_Q = OFF_K + 2 * C * KST * 2;    // 2 x [C][KST] fp16
@@ -552,7 +632,7 @@ struct SeqCfg {
   static constexpr int OFF_V = OFF_KD + (KDA ? 2 * C * KST * 2 : 0);
   static constexpr int OFF_TP = OFF_V + (VLO ? WGC * VTS * 4 : C * VST * 2);   // 2 x [TPS_U4] x 16 B
   static constexpr int OFF_P = OFF_TP + 2 * TPS_U4 * 16;   // head gate: P high, then low fragments
-  static constexpr int OFF_W = OFF_P + (KDA ? 0 : 2 * NFRAG * 1024);   // VLO: v taps, [WGC][4] fp32
+  static constexpr int OFF_W = OFF_P + (KDA || PWS ? 0 : 2 * NFRAG * 1024);   // VLO: v taps, [WGC][4] fp32
   static constexpr int SMEM = OFF_W + (VLO ? WGC * 16 : 0);
   // with the output gate: the row sums of squares of two chunks, [2][C][NW] fp32
   static constexpr int OFF_SS = SMEM;
@@ -606,18 +686,6 @@ struct SeqFetch {
   uint4 k[NKQ], q[NKQ], kd[KDA ? Cfg::NKQ : 1], v[CONV ? Cfg::NV + 3 : Cfg::NV], tp[Cfg::NTP], sc;
   int n, t0;
 };
-
-// fp16 high and low parts of x: x = hi + lo to about 22 bits.
-// The low part is x - hi (exact in fp32) rounded to fp16 by one mixed-precision
-// fma (hi read as fp16, -1 and x as fp32), written out as the instruction:
-// the compiler otherwise widens hi, subtracts and narrows again.
-__device__ __forceinline__ void split16(float x, _Float16 &hi, _Float16 &lo) {
-  hi = (_Float16)x;
-  const uint32_t h = __builtin_bit_cast(uint16_t, hi);
-  uint32_t r;
-  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
-  lo = __builtin_bit_cast(_Float16, (uint16_t)r);
-}
 
 // KDA false: head gate; K, Q, V, g, beta are read from the inputs and T from
 // the workspace, P is formed here.  KDA true: key-channel gate; the decayed
@@ -1122,7 +1190,7 @@ __global__ __launch_bounds__(64 * (NW + 4), 1) void chunk_seq_kernel(
         accX[t][R] = ax;
         accO[t][R] = ao;
       }
-      if constexpr (!KDA && !GATE) {
+      if constexpr (!KDA && !GATE && !Cfg::PWS) {
         // virtual wave vw in [0, 4): this wave's own w, and w + 2 with two waves
 #pragma unroll
         for (int vw = 0; vw < 4; ++vw) {
@@ -1266,13 +1334,15 @@ __global__ __launch_bounds__(64 * (NW + 4), 1) void chunk_seq_kernel(
     for (int R = 0; R < 4; ++R) {
       const int r = 16 * R + ln;
       const float er = KDA ? 1.f : sc[C + r];
-      const uint4 *ph = KDA ? cT + NFRAG * 64 : sPh;
+      // P: from the T/P buffer (key gate; PWS with its low part after it) or from the P buffer
+      const uint4 *ph = KDA || Cfg::PWS ? cT + NFRAG * 64 : sPh;
+      const uint4 *pl = Cfg::PWS ? cT + 2 * NFRAG * 64 : sPl;
       const half8 p0h = __builtin_bit_cast(half8, ph[frag_index(R, 0) * 64 + l]);
       const half8 p1h = R >= 2 ? __builtin_bit_cast(half8, ph[frag_index(R, 1) * 64 + l]) : half8{};
       half8 p0l = {}, p1l = {};
       if constexpr (!KDA) {
-        p0l = __builtin_bit_cast(half8, sPl[frag_index(R, 0) * 64 + l]);
-        if (R >= 2) p1l = __builtin_bit_cast(half8, sPl[frag_index(R, 1) * 64 + l]);
+        p0l = __builtin_bit_cast(half8, pl[frag_index(R, 0) * 64 + l]);
+        if (R >= 2) p1l = __builtin_bit_cast(half8, pl[frag_index(R, 1) * 64 + l]);
       }
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
@@ -1463,8 +1533,12 @@ __global__ __launch_bounds__(kOrderBins) void seq_order_kernel(Seqs sq, int Tall
 
 // Bytes of the chunk matrices in the workspace; packed sequences keep their
 // order after them (B ints, rounded up to 256 bytes).
+// The head gate's prep stores P too when the sequential pass runs two
+// compute waves per workgroup: at most 64 chains.
+inline bool p_in_workspace(const Shape &sh) { return !sh.key_gate && (long)sh.B * sh.Hv <= 64; }
 inline size_t chunk_matrix_bytes(const Shape &sh) {
-  const size_t per_chunk = (size_t)(sh.key_gate ? KDA_CHUNK_U4 : GDN_CHUNK_U4) * 16;
+  const size_t per_chunk =
+      (size_t)(sh.key_gate ? KDA_CHUNK_U4 : p_in_workspace(sh) ? GDN_CHUNK_U4_P : GDN_CHUNK_U4) * 16;
   return (size_t)(sh.packed ? 1 : sh.B) * sh.Hv * chunks_per_chain(sh) * per_chunk;
 }
 inline size_t order_bytes(const Shape &sh) { return sh.packed ? ((size_t)sh.B * 4 + 255) / 256 * 256 : 0; }
@@ -1599,8 +1673,9 @@ hipError_t launch_t(const Shape &sh, const void *q, const void *k, const void *v
   // chunks per (sequence, value head), or chunk slots per value head (packed sequences)
   const int nchunks = chunks_per_chain(sh);
   uint4 *TPws = (uint4 *)ws;
-  auto prep_k = chunk_prep_kernel<TQ, TG, CONV>;
-  const size_t smem = prep_smem(sh.Hv / sh.Hk, CONV);
+  const bool pw = p_in_workspace(sh);
+  auto prep_k = pw ? chunk_prep_kernel<TQ, TG, CONV, true> : chunk_prep_kernel<TQ, TG, CONV, false>;
+  const size_t smem = prep_smem(sh.Hv / sh.Hk, CONV, pw);
   if (smem > 160 * 1024) return hipErrorInvalidValue;
   hipError_t e =
       hipFuncSetAttribute((const void *)prep_k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
@@ -1932,7 +2007,7 @@ __global__ __launch_bounds__(kThreads, 3) void kda_prep_kernel(
     sP[rr * CST + 16 + cc] = (_Float16)0.f;
     sP[(32 + rr) * CST + 48 + cc] = (_Float16)0.f;
   }
-  invert_store<true>(sAd, sAo, sT, sP, wc, w, l);
+  invert_store<1>(sAd, sAo, sT, sP, nullptr, wc, w, l);
 }
 
 template <typename TQ, typename TG>

@@ -126,7 +126,9 @@ gdn_status gdn_prologue(const gdn_desc *d, int32_t x_dtype, const void *xq,
  * dk = dv = 128, chunk 64) keeps per (batch, value head, 64-token chunk):
  *   head gate: the triangular inverse (a 64 x 64 lower-triangular fp16
  *     matrix) and five fp32 values per token (cumulative log decay and the
- *     factors made from it): 7424 bytes;
+ *     factors made from it): 7424 bytes; with at most 64 (batch, value
+ *     head) pairs, also the decayed masked q.k products as high and low
+ *     fp16 parts (two more 64 x 64 lower-triangular matrices): 19712 bytes;
  *   key-channel gate: the inverse, the decayed masked q.k products (another
  *     64 x 64 lower-triangular fp16 matrix), the decayed k, q and the
  *     state-update k (64 x 128 fp16 each), beta and the chunk's total decay:
@@ -189,8 +191,9 @@ gdn_status gdn_fwd_chunked(const gdn_desc *d, const void *q, const void *k,
  *   d, q, k, v, g, beta, S0, o, S_T, stream   as for gdn_fwd_chunked
  * Errors: as gdn_fwd_chunked; GDN_E_WORKSPACE when gdn_fwd_workspace_bytes(d)
  * exceeds GDN_NOALLOC_SCRATCH_BYTES (head gate: at most 18078 (batch, value
- * head, 64-token chunk) triples, e.g. B 4, Hv 48, T 4096; key-channel gate:
- * at most 2157); GDN_E_HIP when the scratch address cannot be obtained on
+ * head, 64-token chunk) triples, e.g. B 4, Hv 48, T 4096, and at most 6808
+ * with at most 64 (batch, value head) pairs, e.g. B 1, Hv 48, T 8192;
+ * key-channel gate: at most 2157); GDN_E_HIP when the scratch address cannot be obtained on
  * the current device.  Nothing in the scratch needs to start at zero.
  * Every call on one device shares that device's scratch: calls that overlap
  * in time on one device (on different streams, or from several threads

@@ -146,10 +146,14 @@ def test_prologue_rejects(L):
 
 
 def test_workspace_query(L):
-    # matrix-core path: 7424 bytes per (batch, value head, 64-token chunk),
+    # matrix-core path: 7424 bytes per (batch, value head, 64-token chunk)
+    # above 64 (batch, value head) pairs, 19712 (P's two parts too) up to 64,
     # 62208 with the key-channel gate
-    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc())) == 2 * 6 * 2 * 7424
-    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(T=1))) == 2 * 6 * 1 * 7424
+    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(Hk=16, Hv=48))) == 2 * 48 * 2 * 7424
+    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(B=1, Hk=16, Hv=64))) == 1 * 64 * 2 * 19712
+    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(B=5, Hk=13, Hv=13))) == 5 * 13 * 2 * 7424
+    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc())) == 2 * 6 * 2 * 19712
+    assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(T=1))) == 2 * 6 * 1 * 19712
     assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(gate=gdn.GATE_KEY_CHANNEL))) == 2 * 6 * 2 * 62208
     assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(gate=gdn.GATE_KEY_CHANNEL, dk=64, dv=64))) == 0
     assert L.gdn_fwd_workspace_bytes(ctypes.byref(desc(qkv_dtype=gdn.F32, gate_dtype=gdn.F32, chunk=32))) == 0
@@ -289,8 +293,9 @@ def test_varlen_checks(L):
     p = [P(FAKE + i * (1 << 36)) for i in range(12)]
     cu = P(FAKE + 11 * (1 << 36))
     need = L.gdn_fwd_varlen_workspace_bytes(ctypes.byref(d))
-    # matrix-core path: chunk slots per value head = T / 64 + B = 20
-    assert need == 6 * (1000 // 64 + 5) * 7424 + 256   # and the sequence order (5 ints, in 256 bytes)
+    # matrix-core path: chunk slots per value head = T / 64 + B = 20, 19712
+    # bytes each (30 (sequence, value head) pairs: P's two parts too)
+    assert need == 6 * (1000 // 64 + 5) * 19712 + 256   # and the sequence order (5 ints, in 256 bytes)
     assert L.gdn_fwd_varlen_workspace_bytes(ctypes.byref(desc(B=5, T=1000, Hv=5))) == 0
     call = lambda dd, cu_, ptrs=p, ws=p[10], nbytes=need: L.gdn_fwd_chunked_varlen(
         ctypes.byref(dd), cu_, *ptrs[:5], None, *ptrs[5:7], ws, nbytes, None)
