@@ -446,10 +446,11 @@ def conv_state(xq, xk, xv, cu_seqlens=None, stream=None):
 
 
 def decode_step_conv(xq, xk, xv, conv_w, conv_st, g, beta, S, qkv_dtype=torch.float16, eps=1e-6, o=None,
-                     stream=None):
+                     stream=None, delta=True):
     """One decode step from raw inputs xq, xk [B,Hk,dk], xv [B,Hv,dv] and the
     convolution history conv_st [B,3,channels] (moved on by one token in place);
-    S updated in place.  Returns o fp32 [B,Hv,dv]."""
+    S updated in place.  Returns o fp32 [B,Hv,dv].  delta=False: the update
+    without the delta correction."""
     B, Hk, dk = xq.shape
     Hv, dv = xv.shape[1], xv.shape[2]
     _dev("xq", xq)
@@ -463,7 +464,9 @@ def decode_step_conv(xq, xk, xv, conv_w, conv_st, g, beta, S, qkv_dtype=torch.fl
     _dev("S", S, (B, Hv, dv, dk), (torch.float32,))
     if o is None:
         o = torch.empty((B, Hv, dv), dtype=torch.float32, device=xq.device)
-    d = make_desc(B, 1, Hk, Hv, dk, dv, 64, _DTYPE_CODE[qkv_dtype], _DTYPE_CODE[g.dtype], gate)
+    _dev("o", o, (B, Hv, dv), (torch.float32,))
+    d = make_desc(B, 1, Hk, Hv, dk, dv, 64, _DTYPE_CODE[qkv_dtype], _DTYPE_CODE[g.dtype], gate,
+                  RULE_DELTA if delta else RULE_NO_DELTA)
     L = lib()
     ws_bytes = L.gdn_decode_conv_workspace_bytes(ctypes.byref(d))
     ws = _workspace(ws_bytes, xq.device)

@@ -96,6 +96,35 @@ def test_decode_conv_fp32_inputs():
     assert torch.equal(o1, o2) and torch.equal(S, S2)
 
 
+@pytest.mark.parametrize("d,gate,qkv,delta", [
+    (64, "head", torch.float16, True),      # other head dims: q, k, v through the workspace
+    (32, "key", torch.bfloat16, True),
+    (128, "key", torch.float16, True),      # dk 128: one kernel
+    (128, "head", torch.bfloat16, True),
+    (128, "head", torch.float16, False),    # without the delta correction
+])
+def test_decode_conv_forms(d, gate, qkv, delta):
+    """decode_step_conv against the prologue over the whole sequence followed
+    by decode_step, bit for bit, for each form of the step."""
+    wl = PREFILL_CONV.with_(B=3, T=9, Hk=2, Hv=6, dk=d, dv=d, gate=gate)
+    inp = make_prefill(wl)
+    say("decode from raw inputs: d %d, %s gate, %s, delta %s" % (d, gate, qkv, delta))
+    xs = [to_torch(inp[n]) for n in ("xq", "xk", "xv")]
+    w, g, beta = to_torch(inp["conv_w"]), to_torch(inp["g"]), to_torch(inp["beta"])
+    cs = gdn.conv_state(*(x[:, :8].contiguous() for x in xs))
+    S = torch.randn(3, 6, d, d, device="cuda") * 0.05
+    S2 = S.clone()
+    o1 = gdn.decode_step_conv(*(x[:, 8].contiguous() for x in xs), w, cs, g[:, 8].contiguous(),
+                              beta[:, 8].contiguous(), S, qkv_dtype=qkv, delta=delta)
+    q, k, v = gdn.prologue(*xs, w, out_dtype=qkv)
+    o2 = gdn.decode_step(q[:, 8].contiguous(), k[:, 8].contiguous(), v[:, 8].contiguous(), g[:, 8].contiguous(),
+                         beta[:, 8].contiguous(), S2, delta=delta)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2), "o differs from prologue + decode"
+    assert torch.equal(S, S2), "state differs from prologue + decode"
+    assert torch.equal(cs, channels_history(xs, 9)), "conv_state did not move on"
+
+
 def test_conv_state_packed():
     lens = [1, 5, 0, 70, 2]
     T = sum(lens)
