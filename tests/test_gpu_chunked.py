@@ -245,3 +245,30 @@ def test_graph_capture_segmented():
         torch.cuda.synchronize()
         assert torch.isfinite(junk)
         assert torch.equal(o, o_e) and torch.equal(ST, S_e), "replay %d differs from the eager call" % rep
+
+
+def test_bf16_input_beyond_fp16_range():
+    """The matrix-core path narrows 16-bit inputs to fp16 (gdn.h: a magnitude
+    above 65504 becomes infinite, and the call does not check).  One v entry
+    of 1e5 at (sequence 0, token 70, value head 1, channel 3): rows of the
+    state evolve independently, so only that value row of that chain turns
+    non-finite from that token on (the tokens 64..69 before it in its 16-token
+    block may too: the matrix products multiply the zero upper triangles of T
+    and P by it); every other output equals, bit for bit, the run without it."""
+    wl = SMALL.with_(T=200, s0_std=0.0)
+    inp = make_prefill(wl)
+    say("bf16 v entry of 1e5 (beyond fp16)")
+    args = gpu_inputs(inp)
+    o_ref, S_ref = gdn.fwd_chunked(*args, chunk=wl.chunk)
+    v = args[2].clone()
+    v[0, 70, 1, 3] = 1e5
+    o, S = gdn.fwd_chunked(args[0], args[1], v, args[3], args[4], chunk=wl.chunk)
+    torch.cuda.synchronize()
+    assert not torch.isfinite(o[0, 70:, 1, 3]).any(), "the row past the entry should not be finite"
+    away = torch.ones_like(o, dtype=torch.bool)
+    away[0, 64:, 1, 3] = False
+    assert torch.equal(o[away], o_ref[away]), "outputs away from the entry changed"
+    assert not torch.isfinite(S[0, 1, 3]).any()
+    keep = torch.ones_like(S, dtype=torch.bool)
+    keep[0, 1, 3] = False
+    assert torch.equal(S[keep], S_ref[keep])
