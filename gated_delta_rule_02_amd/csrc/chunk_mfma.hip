@@ -768,6 +768,13 @@ __global__ __launch_bounds__(64 * (NW + 4), 1) void chunk_seq_kernel(
   _Float16 *const sKdb = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_KD);
   _Float16 *const sV = reinterpret_cast<_Float16 *>(smem + Cfg::OFF_V);
   float *const sVt = reinterpret_cast<float *>(smem + Cfg::OFF_V);   // CONV: V^T, fp32
+  // V^T element (value row c, token t) sits at token slot t ^ 4 (c / 8 mod 16):
+  // the loading waves write 4 tokens of 8 rows 8 apart per lane, which with
+  // any 16-byte aligned row stride would all fall on the same banks.  The
+  // swizzle keeps groups of 4 tokens together.
+  auto vt_at = [&](int c, int t) __attribute__((always_inline)) {
+    return sVt + c * Cfg::VTS + (t ^ (4 * ((c >> 3) & 15)));
+  };
   uint4 *const sTPb = reinterpret_cast<uint4 *>(smem + Cfg::OFF_TP);   // buffer b at b TPS_U4
   uint4 *const sPh = reinterpret_cast<uint4 *>(smem + Cfg::OFF_P);     // head gate: P high fragments
   uint4 *const sPl = sPh + NFRAG * 64;                                  // ... and low
@@ -984,7 +991,7 @@ __global__ __launch_bounds__(64 * (NW + 4), 1) void chunk_seq_kernel(
         for (int e = 0; e < 8; ++e) {
           // the LDS address (offset in the workgroup's LDS) of the write
           const uint32_t dst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float *)(
-              sVt + (vch8 * 8 + e) * Cfg::VTS + NV * vrb);
+              vt_at(vch8 * 8 + e, NV * vrb));
           if constexpr (NV == 4) {
             const float4v x = {z[0][e], z[1][e], z[2][e], z[3][e]};
             asm volatile("ds_write_b128 %0, %1" ::"v"(dst), "v"(x));
@@ -1235,7 +1242,7 @@ __global__ __launch_bounds__(64 * (NW + 4), 1) void chunk_seq_kernel(
       for (int t = 0; t < RT; ++t) {
         float vx4[4];
         if constexpr (CONV) {
-          const float4 vv = *reinterpret_cast<const float4 *>(sVt + (ic + 16 * t + ln) * Cfg::VTS + r0);
+          const float4 vv = *reinterpret_cast<const float4 *>(vt_at(ic + 16 * t + ln, r0));
           vx4[0] = vv.x; vx4[1] = vv.y; vx4[2] = vv.z; vx4[3] = vv.w;
         } else {
           const half4 vv = lds_read_tr(sV + vto + 16 * t + 16 * R * VST);
