@@ -1843,6 +1843,9 @@ __global__ __launch_bounds__(kThreads, 3) void kda_prep_kernel(
           gv[2 * i + 1] = __uint_as_float(wd[i] & 0xFFFF0000u);
         }
       }
+      // in base 2: the decays below are all 2^x, one instruction each
+#pragma unroll
+      for (int j = 0; j < 8; ++j) gv[j] *= 1.44269504088896341f;   // log2(e)
       float *gp = sG + row * GST + (tid & 15) * 8;
       *reinterpret_cast<float4 *>(gp) = ok ? make_float4(gv[0], gv[1], gv[2], gv[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
       *reinterpret_cast<float4 *>(gp + 4) = ok ? make_float4(gv[4], gv[5], gv[6], gv[7]) : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1851,7 +1854,8 @@ __global__ __launch_bounds__(kThreads, 3) void kda_prep_kernel(
   }
   lds_barrier();
 
-  // gamma: inclusive prefix over the rows, per channel (two halves of 32 rows)
+  // gamma: inclusive prefix over the rows, per channel (two halves of 32 rows);
+  // held as gamma log2(e), so that every e^{...} below is one 2^x
   {
     const int ch = tid & 127, r0 = (tid >> 7) * 32;
     float x = 0.f;
@@ -1884,7 +1888,7 @@ __global__ __launch_bounds__(kThreads, 3) void kda_prep_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float gam = sG[row * GST + c8 + j];
-        const float eg = __expf(gam), ed = __expf(gl[c8 + j] - gam);
+        const float eg = __builtin_amdgcn_exp2f(gam), ed = __builtin_amdgcn_exp2f(gl[c8 + j] - gam);
         kg[j] = (_Float16)((float)kv[j] * eg);
         qg[j] = (_Float16)((float)qv[j] * eg);
         kd[j] = (_Float16)((float)kv[j] * ed);
@@ -1895,7 +1899,7 @@ __global__ __launch_bounds__(kThreads, 3) void kda_prep_kernel(
     }
     float *wsc = reinterpret_cast<float *>(wc + KDA_SC);
     if (tid < C) wsc[tid] = sB[tid];
-    if (tid < DK) wsc[C + tid] = __expf(gl[tid]);
+    if (tid < DK) wsc[C + tid] = __builtin_amdgcn_exp2f(gl[tid]);
   }
 
   // A and P for block row R = w (tiles S = 0..R), into registers.  Reference
@@ -1927,7 +1931,7 @@ __global__ __launch_bounds__(kThreads, 3) void kda_prep_kernel(
                                          : half8{};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float f = __expf(gr[e] - gp[e]), fi = __expf(gp[e] - gr[e]);
+          const float f = __builtin_amdgcn_exp2f(gr[e] - gp[e]), fi = __builtin_amdgcn_exp2f(gp[e] - gr[e]);
           const float kf = (float)kv[e] * f, qf = (float)qv[e] * f, ki = (float)kv[e] * fi;
           ok = ok && fi <= 1.0e30f;
           kl[kk][e] = (_Float16)kf;
@@ -1945,7 +1949,7 @@ __global__ __launch_bounds__(kThreads, 3) void kda_prep_kernel(
           if (s_ <= r) {
             const TQ *qr = q + ((bt0 + min(r, n - 1)) * Hk + kh) * DK;
             for (int j = 0; j < DK; ++j) {
-              const float e = __expf(sG[r * GST + j] - sG[s_ * GST + j]);
+              const float e = __builtin_amdgcn_exp2f(sG[r * GST + j] - sG[s_ * GST + j]);
               const float ks = (float)sK[s_ * KST + j];
               const float qv = r < n ? (float)(_Float16)to_f32(qr[j]) : 0.f;
               a += (float)sK[r * KST + j] * ks * e;
@@ -1976,7 +1980,7 @@ __global__ __launch_bounds__(kThreads, 3) void kda_prep_kernel(
           const half8 kv = perm_row(sK, KST, 16 * S + ln, kk, g4);
           half8 ks;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ks[e] = (_Float16)((float)kv[e] * __expf(gp[e] - gs[e]));
+          for (int e = 0; e < 8; ++e) ks[e] = (_Float16)((float)kv[e] * __builtin_amdgcn_exp2f(gp[e] - gs[e]));
           aa = mfma32(kl[kk], ks, aa);
           ap = mfma32(ql[kk], ks, ap);
         }
