@@ -1580,10 +1580,13 @@ hipError_t launch_seq(const Shape &sh, const void *q, const void *k, const void 
   return hipGetLastError();
 }
 
+// At most 4 segments: the long prefill (1024 chunks) took 2.49 ms in 4, 2.5-2.64
+// ms in 2, 3, 6, 8 or 16 (the first segment's prep runs alone, each further one
+// adds a launch of the pass).
+constexpr int kMaxSeg = 4;
 // A side stream and events for one pipelined call, taken from a per-device
 // pool and returned when the call has enqueued its work (the pool grows to
 // the number of concurrent calls).  Streams have the default priority.
-constexpr int kMaxSeg = 8;
 struct SideSlot {
   hipStream_t stream = nullptr;
   hipEvent_t ev[kMaxSeg + 1] = {};
