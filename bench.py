@@ -25,8 +25,8 @@ kernels run on):
                 (gdn_fwd_chunked_conv_gated) against the forward followed by
                 gdn_output_gate; the step's 16 384 tokens as 16 packed
                 sequences of mixed lengths (gdn_fwd_chunked_conv_varlen); and
-                the backward of the step's prefill (gdn_bwd, state history in
-                the workspace); the same forward without the delta correction;
+                the backward of the step's prefill (gdn_bwd: chunked, fp32
+                matrix cores); the same forward without the delta correction;
   cpu_baseline  the fp64 oracle on the host cores on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -49,6 +49,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, GB/s
 PEAK_F16_TFLOPS = 2500.0         # MI355X dense fp16/bf16 matrix cores, TFLOP/s
+PEAK_F32_TFLOPS = 157.3          # MI355X fp32 (matrix and vector), TFLOP/s
 FLOPS_PER_TOKEN_HEAD = 180224    # algorithmic prefill flops per (token, value head) at C 64, d 128
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "chunk_fwd_prefill_conv_B4_T4096_pmc.txt")
 # the sources the chunked kernels are compiled from
@@ -422,12 +423,13 @@ def main():
     del vws, vST
 
     # the backward of the step's prefill: q, k, v as the prologue makes them,
-    # a random dO, the state history (B Hv T dv dk fp32) in the workspace
-    log("workload: backward of the prefill (state history %.1f GB)" % (B * Hv * T * dv * dk * 4 / 1e9))
+    # a random dO; per chunk and value head the workspace holds T, P^T, the
+    # state before the chunk, the state gradient after it, U and E (fp32)
     prologue()
     dO = torch.randn((B, T, Hv, dv), device=dev)
     pdesc_bwd = gdn.make_desc(B, T, Hk, Hv, dk, dv, C, gdn.F16, gdn.BF16, gdn.GATE_HEAD)
     bws = torch.empty(L.gdn_bwd_workspace_bytes(pdesc_bwd), dtype=torch.uint8, device=dev)
+    log("workload: backward of the prefill (workspace %.2f GB)" % (bws.numel() / 1e9))
     grads = [torch.empty_like(x, dtype=torch.float32) for x in (q, k, v, g, beta)] + [torch.empty_like(ST)]
 
     def backward():
@@ -435,17 +437,18 @@ def main():
                             *(P(x) for x in grads), P(bws), bws.numel(), s_ptr))
 
     t_bwd = time_events(backward, 2, stream, warm=0)
-    hist_bytes = B * Hv * T * dv * dk * 4
-    io_bytes = 2 * ((2 * B * T * Hk * dk + B * T * Hv * dv) * 2 + 2 * B * T * Hv * 2) + B * T * Hv * dv * 4 \
-        + (2 * B * T * Hk * dk + B * T * Hv * dv + 2 * B * T * Hv) * 4 + B * Hv * dv * dk * 4
+    # matrix products per (chunk, value head), multiply-adds: the two passes
+    # 5 C dv dk + 3 C^2 dv, the gradients 3 C dv dk + 2 C^2 dv + 4 C^2 dk, the
+    # prep C^2 dk (the lower halves of Q K^T and K K^T) + C^3 / 6 (T)
+    units = B * Hv * ((T + C - 1) // C)
+    bwd_flops = 2 * units * (8 * C * dv * dk + 5 * C * C * dv + 5 * C * C * dk + C ** 3 // 6)
     extra["backward"] = {
         "workload": wl.name + ", backward (dq, dk, dv, dg, dbeta, dS0 fp32) from a random dO",
         "us_per_call": t_bwd * 1e6, "tokens_per_s": B * T / t_bwd,
-        "hbm_gbs": (2 * hist_bytes + io_bytes) / t_bwd / 1e9,
-        "hbm_frac": (2 * hist_bytes + io_bytes) / t_bwd / 1e9 / PEAK_HBM_GBS,
-        "bytes": 2 * hist_bytes + io_bytes}
-    log("backward: %.2f ms, %.3e tokens/s, %.0f GB/s (history written and read once)" %
-        (t_bwd * 1e3, B * T / t_bwd, (2 * hist_bytes + io_bytes) / t_bwd / 1e9))
+        "tflops": bwd_flops / t_bwd / 1e12, "mfma_f32_frac": bwd_flops / t_bwd / 1e12 / PEAK_F32_TFLOPS,
+        "workspace_bytes": int(bws.numel())}
+    log("backward: %.2f ms, %.3e tokens/s, %.1f TFLOP/s = %.1f%% of the fp32 matrix cores" %
+        (t_bwd * 1e3, B * T / t_bwd, bwd_flops / t_bwd / 1e12, 100 * bwd_flops / t_bwd / 1e12 / PEAK_F32_TFLOPS))
     del bws, grads, dO
 
     for key, xwl in (("long_prefill", LONG_PREFILL), ("key_gate_prefill", KDA_PREFILL)):

@@ -386,11 +386,20 @@ gdn_status gdn_decode_step_conv(const gdn_desc *d, int32_t x_dtype, const void *
 
 /*
  * gdn_bwd -- the backward of the recurrence: the gradients of
- * L = sum_t <dO_t, o_t> + <dS_T, S_T> with respect to q, k, v, g, beta and S0,
- * by the first-order backward that keeps one complete state history
- * ("Source notes", Linear attention, row kda).  The forward recurrence is run
- * again to store the state before every token (fp32, in the workspace), then
- * the tokens are run backwards; all arithmetic is fp32.
+ * L = sum_t <dO_t, o_t> + <dS_T, S_T> with respect to q, k, v, g, beta and S0
+ * (the first-order backward of "Source notes", Linear attention, row kda).
+ *  - Per-head gate: in chunks of 64 tokens (the exact chunkwise form of the
+ *    "SinkProbe" page).  A forward pass keeps the state before every chunk
+ *    and the chunk's U = (I + A)^-1 X; a backward pass runs the state
+ *    gradient over the chunks in reverse, keeping it after every chunk with
+ *    E = (I + A)^-T dU; the other gradients are then products of these per
+ *    chunk, on the fp32 matrix cores.  The chunked form assumes decays
+ *    (g <= 0): factors e^(gamma_i - gamma_j) with i >= j stay <= 1.
+ *  - Per-key-channel gate: token by token; the forward recurrence is run again
+ *    to keep the state before every fourth token, then the tokens are run
+ *    backwards in blocks of four, the states inside a block recomputed from
+ *    the kept one by the same arithmetic.
+ * All arithmetic is fp32.
  *   q, k, v, g, beta, S0   the forward's inputs, as for gdn_fwd_chunked (S0 NULL: zeros)
  *   dO     device fp32 [B,T,Hv,dv]: the gradient of o
  *   dS_T   device fp32 [B,Hv,dv,dk] or NULL (zeros): the gradient of S_T
@@ -399,8 +408,10 @@ gdn_status gdn_decode_step_conv(const gdn_desc *d, int32_t x_dtype, const void *
  *   dg     device out fp32, g's shape ([B,T,Hv] or [B,T,Hv,dk]), the gradient of g = ln alpha
  *   dbeta  device out fp32 [B,T,Hv]
  *   dS0    device out fp32 [B,Hv,dv,dk]
- *   workspace   device scratch of gdn_bwd_workspace_bytes(d) bytes (the state
- *               history, B Hv T dv dk fp32, and partial sums), 16-byte aligned
+ *   workspace   device scratch of gdn_bwd_workspace_bytes(d) bytes, 16-byte
+ *               aligned.  Per-head gate: per (batch, value head, chunk of 64)
+ *               2 (64 64 + 64 + dv dk + 64 dv) fp32.  Per-key-channel gate:
+ *               the kept states, B Hv ceil(T/4) dv dk fp32, and partial sums.
  * Outputs and workspace must not overlap each other or the inputs.
  * Supported: dk in {32, 64, 128}; dv a multiple of 32, <= 1024; q, k, v fp32,
  * bf16 or fp16; g and beta fp32 or bf16; either gate; d->chunk is not used.

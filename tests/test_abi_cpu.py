@@ -347,9 +347,16 @@ def test_bwd_checks(L):
     p = [P(FAKE + i * (1 << 36)) for i in range(16)]
     d = desc(qkv_dtype=gdn.F32, gate_dtype=gdn.F32)
     need = L.gdn_bwd_workspace_bytes(ctypes.byref(d))
-    # the state history (B Hv T dv dk fp32, 256-byte rounded), then partial sums
-    hist = 2 * 6 * 100 * 128 * 128 * 4
-    assert need == (hist + 255) // 256 * 256 + 2 * 6 * 4 * 100 * (2 * 128 + 2) * 4
+    # head gate, per (batch, value head, chunk of 64): T and P^T [64][64], gamma and
+    # beta [64], the state before the chunk and the state gradient after it [dv][dk],
+    # U and E [64][dv], all fp32
+    assert need == 2 * 6 * 2 * (2 * 64 * 64 + 2 * 64 + 2 * 128 * 128 + 2 * 64 * 128) * 4
+    # key-channel gate: the state before every 4th token (B Hv ceil(T / 4) dv dk fp32,
+    # 256-byte rounded), then the partial sums per 32 state rows and token
+    hist = 2 * 6 * 25 * 128 * 128 * 4
+    dkey = desc(qkv_dtype=gdn.F32, gate_dtype=gdn.F32, gate=gdn.GATE_KEY_CHANNEL)
+    assert L.gdn_bwd_workspace_bytes(ctypes.byref(dkey)) == \
+        (hist + 255) // 256 * 256 + 2 * 6 * 4 * 100 * (3 * 128 + 1) * 4
     assert L.gdn_bwd_workspace_bytes(ctypes.byref(desc(dk=16))) == 0
     assert L.gdn_bwd_workspace_bytes(ctypes.byref(desc(dv=48))) == 0
     # q, k, v, g, beta | S0 | dO | dS_T | dq, dk, dv, dg, dbeta, dS0 | workspace
