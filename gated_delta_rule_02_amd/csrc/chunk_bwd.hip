@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void cb_prep_kernel(CbArgs a) {
   constexpr int LK = DK + 4;
   extern __shared__ float4v smem4[];
   float *smem = reinterpret_cast<float *>(smem4);
-  float *sK = smem, *sQ = sK + C * LK, *sA = sQ + C * LK, *sg = sA + C * LC, *sb = sg + C;
+  float *sK = smem, *sA = sK + C * LK, *sg = sA + C * LC, *sb = sg + C;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 15, g4 = lane >> 4;
   const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int T = a.T, Hk = a.Hk, Hv = a.Hv, kh = h / (Hv / Hk);
@@ -129,7 +129,17 @@ __global__ __launch_bounds__(256) void cb_prep_kernel(CbArgs a) {
   const size_t cn = ((size_t)b * Hv + h) * a.nc + n;
   const size_t row0 = (size_t)b * T + t0;
   load_rows<TQ, DK>(sK, (const TQ *)a.k, row0 * Hk + kh, Hk, len, tid);
-  load_rows<TQ, DK>(sQ, (const TQ *)a.q, row0 * Hk + kh, Hk, len, tid);
+  // the lane's q entries of token 16 w + ln as matrix-core operands (zeros past the end)
+  float4v qa[DK / 16];
+  {
+    const int t = 16 * w + ln;
+#pragma unroll
+    for (int kb = 0; kb < DK / 16; ++kb) {
+      float x[4] = {0.f, 0.f, 0.f, 0.f};
+      if (t < len) load4((const TQ *)a.q + ((row0 + t) * Hk + kh) * DK + 16 * kb + 4 * g4, x);
+      qa[kb] = float4v{x[0], x[1], x[2], x[3]};
+    }
+  }
   if (w == 0) {
     const TG *g = (const TG *)a.g, *be = (const TG *)a.beta;
     const float gt = lane < len ? to_f32(g[(row0 + lane) * Hv + h]) : 0.f;
@@ -149,8 +159,7 @@ __global__ __launch_bounds__(256) void cb_prep_kernel(CbArgs a) {
     if (J <= w) {
       mm<DK>(kk, [&](int k) { return row4(sK + (16 * w + ln) * LK + k); },
              [&](int k) { return row4(sK + (16 * J + ln) * LK + k); }, g4);
-      mm<DK>(qk, [&](int k) { return row4(sQ + (16 * w + ln) * LK + k); },
-             [&](int k) { return row4(sK + (16 * J + ln) * LK + k); }, g4);
+      mm<DK>(qk, [&](int k) { return qa[k >> 4]; }, [&](int k) { return row4(sK + (16 * J + ln) * LK + k); }, g4);
     }
     const int j = 16 * J + ln;
     float4v pt;
@@ -166,13 +175,14 @@ __global__ __launch_bounds__(256) void cb_prep_kernel(CbArgs a) {
   __syncthreads();
   if (w == 0) {
     // column c = lane of T: T[i][c] = [i == c] - sum_{j < i} A[i][j] T[j][c]
+    // (four partial sums, j mod 4, so that only one depends on T[i - 1][c])
     float tc[C];
 #pragma unroll
     for (int i = 0; i < C; ++i) {
-      float s = 0.f;
+      float s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < i; ++j) s = __builtin_fmaf(sA[i * LC + j], tc[j], s);
-      tc[i] = (i == lane ? 1.f : 0.f) - s;
+      for (int j = 0; j < i; ++j) s[j & 3] = __builtin_fmaf(sA[i * LC + j], tc[j], s[j & 3]);
+      tc[i] = (i == lane ? 1.f : 0.f) - ((s[0] + s[1]) + (s[2] + s[3]));
     }
     float *Tg = a.Tm + cn * C * C;
 #pragma unroll
@@ -181,152 +191,309 @@ __global__ __launch_bounds__(256) void cb_prep_kernel(CbArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// forward pass: 32 state rows r0 .. of one (batch, value head) over the
-// chunks in order.  Wave w holds the state tiles of row block w & 1 and
-// column blocks (w >> 1) NCT/2 .. ; of the [32][C] products, row block w & 1
-// and column blocks 2 (w >> 1), 2 (w >> 1) + 1.
+// The two passes.  A workgroup of NW waves holds 32 state rows r0 .. of one
+// (batch, value head), fp32 [32][dk] in matrix-core tiles: wave w the tiles
+// w NS .. w NS + NS - 1 (row block id / NCT, column block id % NCT); of the
+// [32][C] products, the tiles w ZT .. (row block id / 4, column block id % 4).
+// The next chunk's inputs are loaded into registers while the current one is
+// worked on, and staged into LDS at the start of the next.
 template <typename TQ, int DK>
-__global__ __launch_bounds__(256) void cb_fwd_kernel(CbArgs a) {
-  constexpr int LK = DK + 4, NST = DK / 32;
+struct PassCfg {
+  static constexpr int NW = DK == 128 ? 8 : 4, NT = 64 * NW;
+  static constexpr int LK = DK + 16 / (int)sizeof(TQ);   // q, k rows in LDS, input type
+  static constexpr int LS = DK + 4;                        // state rows in LDS, fp32
+  static constexpr int NCT = DK / 16, NS = 2 * NCT / NW, ZT = 8 / NW;
+};
+
+// C rows of DK elements of q or k (zeros past the sequence's end), raw, in
+// 16-byte units spread over the NT threads.
+template <typename TQ, int DK, int NT>
+struct RowsReg {
+  static constexpr int UPR = DK * (int)sizeof(TQ) / 16, NU = C * UPR / NT;
+  uint4 u[NU];
+  __device__ __forceinline__ void load(const TQ *row0, size_t stride, int len, int tid) {
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int x = tid + i * NT, t = x / UPR, cu = x % UPR;
+      u[i] = t < len ? *reinterpret_cast<const uint4 *>(row0 + (size_t)t * stride + cu * (16 / sizeof(TQ)))
+                     : uint4{0u, 0u, 0u, 0u};
+    }
+  }
+  template <int LK>
+  __device__ __forceinline__ void store(TQ *s, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int x = tid + i * NT, t = x / UPR, cu = x % UPR;
+      *reinterpret_cast<uint4 *>(s + t * LK + cu * (16 / sizeof(TQ))) = u[i];
+    }
+  }
+};
+
+// a [C][C] fp32 matrix of the workspace
+template <int NT>
+struct CcReg {
+  static constexpr int NU = C * C / 4 / NT;
+  float4v u[NU];
+  __device__ __forceinline__ void load(const float *src, int tid) {
+#pragma unroll
+    for (int i = 0; i < NU; ++i) u[i] = *reinterpret_cast<const float4v *>(src + 4 * (tid + i * NT));
+  }
+  __device__ __forceinline__ void store(float *s, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int x = tid + i * NT;
+      *reinterpret_cast<float4v *>(s + (x / (C / 4)) * LC + (x % (C / 4)) * 4) = u[i];
+    }
+  }
+};
+
+// four consecutive input elements, raw until used
+template <typename TQ> struct Quad { using type = uint2; };
+template <> struct Quad<float> { using type = float4v; };
+template <typename TQ>
+__device__ __forceinline__ typename Quad<TQ>::type quad_load(const TQ *p) {
+  return *reinterpret_cast<const typename Quad<TQ>::type *>(p);
+}
+__device__ __forceinline__ float4v quad_f32(float4v x) { return x; }
+__device__ __forceinline__ float4v quad_f32(uint2 x, bf16_t) {
+  return float4v{__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xFFFF0000u), __uint_as_float(x.y << 16),
+                 __uint_as_float(x.y & 0xFFFF0000u)};
+}
+__device__ __forceinline__ float4v quad_f32(uint2 x, f16_t) {
+  const half4 h = __builtin_bit_cast(half4, x);
+  return float4v{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+}
+template <typename TQ>
+__device__ __forceinline__ float4v quad_to_f32(typename Quad<TQ>::type x) {
+  if constexpr (sizeof(TQ) == 4) return quad_f32(x);
+  else return quad_f32(x, TQ{});
+}
+
+// LDS reads of input-type rows: four consecutive entries, four rows of a column
+template <typename TQ>
+__device__ __forceinline__ float4v rowq(const TQ *p) {
+  float x[4];
+  load4(p, x);
+  return float4v{x[0], x[1], x[2], x[3]};
+}
+template <typename TQ>
+__device__ __forceinline__ float4v colq(const TQ *p, int ld) {
+  return float4v{to_f32(p[0]), to_f32(p[ld]), to_f32(p[2 * ld]), to_f32(p[3 * ld])};
+}
+
+// the chunk's gate inputs (thread t < C: gamma_t, gamma_C, beta_t), and their LDS form
+struct GateReg {
+  float g, gC, b;
+  __device__ __forceinline__ void load(const CbArgs &a, size_t cn, int tid) {
+    if (tid < C) {
+      g = a.gam[cn * C + tid];
+      gC = a.gam[cn * C + C - 1];
+      b = a.bet[cn * C + tid];
+    }
+  }
+  __device__ __forceinline__ void store(float *sEg, float *sEc, float *sb, int tid) const {
+    if (tid < C) {
+      sEg[tid] = __expf(g);
+      sEc[tid] = __expf(gC - g);
+      sb[tid] = b;
+    }
+  }
+};
+
+// forward pass, over the chunks in order: the state before each chunk and U
+template <typename TQ, int DK>
+__global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_fwd_kernel(CbArgs a) {
+  using P = PassCfg<TQ, DK>;
+  constexpr int LK = P::LK, LS = P::LS, NCT = P::NCT, NS = P::NS, ZT = P::ZT, NT = P::NT;
   extern __shared__ float4v smem4[];
-  float *smem = reinterpret_cast<float *>(smem4);
-  float *sK = smem, *sT = sK + C * LK, *sS = sT + C * LC, *sX = sS + R * LK, *sU = sX + R * LC;
+  TQ *sK = reinterpret_cast<TQ *>(smem4);
+  float *sT = reinterpret_cast<float *>(sK + C * LK);
+  float *sS = sT + C * LC, *sX = sS + R * LS, *sU = sX + R * LC;
   float *sEg = sU + R * LC, *sEc = sEg + C, *sb = sEc + C;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 15, g4 = lane >> 4;
   const int sl = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int T = a.T, Hk = a.Hk, Hv = a.Hv, DV = a.dv_dim, nc = a.nc, kh = h / (Hv / Hk), r0 = sl * R;
-  const int rt = w & 1, ct0 = (w >> 1) * NST, zc0 = (w >> 1) * 2;
   const size_t bh = (size_t)b * Hv + h;
-  const TQ *v = (const TQ *)a.v;
-  float4v S[NST];
+  const TQ *k = (const TQ *)a.k, *v = (const TQ *)a.v;
+  int srt[NS], sct[NS], zrt[ZT], zcc[ZT];
 #pragma unroll
-  for (int s = 0; s < NST; ++s)
+  for (int s = 0; s < NS; ++s) srt[s] = (w * NS + s) / NCT, sct[s] = (w * NS + s) % NCT;
+#pragma unroll
+  for (int z = 0; z < ZT; ++z) zrt[z] = (w * ZT + z) / 4, zcc[z] = (w * ZT + z) % 4;
+  float4v S[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      S[s][e] = a.S0 ? a.S0[(bh * DV + r0 + 16 * rt + 4 * g4 + e) * DK + 16 * (ct0 + s) + ln] : 0.f;
-  for (int n = 0; n < nc; ++n) {
+      S[s][e] = a.S0 ? a.S0[(bh * DV + r0 + 16 * srt[s] + 4 * g4 + e) * DK + 16 * sct[s] + ln] : 0.f;
+  RowsReg<TQ, DK, NT> kr;
+  CcReg<NT> tr;
+  GateReg gr;
+  typename Quad<TQ>::type vq[ZT];
+  auto fetch = [&](int n) {
     const int t0 = n * C, len = min(C, T - t0);
     const size_t cn = bh * nc + n, row0 = (size_t)b * T + t0;
-    load_rows<TQ, DK>(sK, (const TQ *)a.k, row0 * Hk + kh, Hk, len, tid);
-    load_cc(sT, a.Tm + cn * C * C, tid);
-    load_gates(sEg, sEc, sb, a, cn, tid);
+    kr.load(k + (row0 * Hk + kh) * DK, (size_t)Hk * DK, len, tid);
+    tr.load(a.Tm + cn * C * C, tid);
+    gr.load(a, cn, tid);
+#pragma unroll
+    for (int z = 0; z < ZT; ++z) {
+      const int t = 16 * zcc[z] + ln;
+      vq[z] = t < len ? quad_load(v + ((row0 + t) * Hv + h) * DV + r0 + 16 * zrt[z] + 4 * g4)
+                      : typename Quad<TQ>::type{};
+    }
+  };
+  fetch(0);
+  for (int n = 0; n < nc; ++n) {
+    const size_t cn = bh * nc + n;
+    kr.template store<LK>(sK, tid);
+    tr.store(sT, tid);
+    gr.store(sEg, sEc, sb, tid);
+    float4v vx[ZT];
+#pragma unroll
+    for (int z = 0; z < ZT; ++z) vx[z] = quad_to_f32<TQ>(vq[z]);
     float *S0g = a.S0s + (cn * DV + r0) * DK;
 #pragma unroll
-    for (int s = 0; s < NST; ++s)
+    for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rt + 4 * g4 + e, c = 16 * (ct0 + s) + ln;
-        sS[r * LK + c] = S[s][e];
+        const int r = 16 * srt[s] + 4 * g4 + e, c = 16 * sct[s] + ln;
+        sS[r * LS + c] = S[s][e];
         S0g[r * DK + c] = S[s][e];
       }
-    __syncthreads();
+    lds_barrier();
+    if (n + 1 < nc) fetch(n + 1);
     // X^T[r][t] = beta_t (v_t[r] - e^gamma_t (S k_t)[r])
 #pragma unroll
-    for (int z = 0; z < 2; ++z) {
-      const int t = 16 * (zc0 + z) + ln;
+    for (int z = 0; z < ZT; ++z) {
+      const int rt = zrt[z], t = 16 * zcc[z] + ln;
       float4v acc = {0.f, 0.f, 0.f, 0.f};
-      mm<DK>(acc, [&](int k) { return row4(sS + (16 * rt + ln) * LK + k); },
-             [&](int k) { return row4(sK + t * LK + k); }, g4);
-      float vx[4] = {0.f, 0.f, 0.f, 0.f};
-      if (t < len) load4(v + (row0 + t) * Hv * DV + (size_t)h * DV + r0 + 16 * rt + 4 * g4, vx);
+      mm<DK>(acc, [&](int kk) { return row4(sS + (16 * rt + ln) * LS + kk); },
+             [&](int kk) { return rowq(sK + t * LK + kk); }, g4);
       const float eg = sEg[t], bt = sb[t];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sX[(16 * rt + 4 * g4 + e) * LC + t] = bt * (vx[e] - eg * acc[e]);
+      for (int e = 0; e < 4; ++e) sX[(16 * rt + 4 * g4 + e) * LC + t] = bt * (vx[z][e] - eg * acc[e]);
     }
-    __syncthreads();
+    lds_barrier();
     // U^T[r][i] = sum_j X^T[r][j] T[i][j]; U to the workspace, U^T e^(gamma_C - gamma_i) to LDS
 #pragma unroll
-    for (int z = 0; z < 2; ++z) {
-      const int i = 16 * (zc0 + z) + ln;
+    for (int z = 0; z < ZT; ++z) {
+      const int rt = zrt[z], i = 16 * zcc[z] + ln;
       float4v u = {0.f, 0.f, 0.f, 0.f};
-      mm<C>(u, [&](int k) { return row4(sX + (16 * rt + ln) * LC + k); },
-            [&](int k) { return row4(sT + i * LC + k); }, g4);
+      mm<C>(u, [&](int kk) { return row4(sX + (16 * rt + ln) * LC + kk); },
+            [&](int kk) { return row4(sT + i * LC + kk); }, g4);
       *reinterpret_cast<float4v *>(a.Um + (cn * C + i) * DV + r0 + 16 * rt + 4 * g4) = u;
       const float ec = sEc[i];
 #pragma unroll
       for (int e = 0; e < 4; ++e) sU[(16 * rt + 4 * g4 + e) * LC + i] = u[e] * ec;
     }
-    __syncthreads();
+    lds_barrier();
     // S <- e^gamma_C S + sum_j U~^T[r][j] k_j
     const float eC = sEg[C - 1];
 #pragma unroll
-    for (int s = 0; s < NST; ++s) {
-      const int c = 16 * (ct0 + s) + ln;
+    for (int s = 0; s < NS; ++s) {
+      const int rt = srt[s], c = 16 * sct[s] + ln;
       S[s] *= eC;
-      mm<C>(S[s], [&](int k) { return row4(sU + (16 * rt + ln) * LC + k); },
-            [&](int k) { return col4(sK + k * LK + c, LK); }, g4);
+      mm<C>(S[s], [&](int kk) { return row4(sU + (16 * rt + ln) * LC + kk); },
+            [&](int kk) { return colq(sK + kk * LK + c, LK); }, g4);
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
-// ---------------------------------------------------------------------------
-// backward pass: the state gradient of 32 rows r0 .. of one (batch, value
-// head) over the chunks in reverse, with the same tiles as the forward pass.
+// backward pass, over the chunks in reverse: the state gradient after each
+// chunk, E, dv, and dS0 at the end
 template <typename TQ, int DK>
-__global__ __launch_bounds__(256) void cb_bwd_kernel(CbArgs a) {
-  constexpr int LK = DK + 4, NST = DK / 32;
+__global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_bwd_kernel(CbArgs a) {
+  using P = PassCfg<TQ, DK>;
+  constexpr int LK = P::LK, LS = P::LS, NCT = P::NCT, NS = P::NS, ZT = P::ZT, NT = P::NT;
   extern __shared__ float4v smem4[];
-  float *smem = reinterpret_cast<float *>(smem4);
-  float *sK = smem, *sQ = sK + C * LK, *sT = sQ + C * LK, *sP = sT + C * LC, *sO = sP + C * LC;
-  float *sS = sO + C * LR, *sD = sS + R * LK, *sE = sD + R * LC;
+  TQ *sK = reinterpret_cast<TQ *>(smem4), *sQ = sK + C * LK;
+  float *sT = reinterpret_cast<float *>(sQ + C * LK);
+  float *sP = sT + C * LC, *sO = sP + C * LC, *sS = sO + C * LR, *sD = sS + R * LS, *sE = sD + R * LC;
   float *sEg = sE + R * LC, *sEc = sEg + C, *sb = sEc + C;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 15, g4 = lane >> 4;
   const int sl = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int T = a.T, Hk = a.Hk, Hv = a.Hv, DV = a.dv_dim, nc = a.nc, kh = h / (Hv / Hk), r0 = sl * R;
-  const int rt = w & 1, ct0 = (w >> 1) * NST, zc0 = (w >> 1) * 2;
   const size_t bh = (size_t)b * Hv + h;
-  float4v dS[NST];
+  const TQ *k = (const TQ *)a.k, *q = (const TQ *)a.q;
+  int srt[NS], sct[NS], zrt[ZT], zcc[ZT];
 #pragma unroll
-  for (int s = 0; s < NST; ++s)
+  for (int s = 0; s < NS; ++s) srt[s] = (w * NS + s) / NCT, sct[s] = (w * NS + s) % NCT;
+#pragma unroll
+  for (int z = 0; z < ZT; ++z) zrt[z] = (w * ZT + z) / 4, zcc[z] = (w * ZT + z) % 4;
+  float4v dS[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      dS[s][e] = a.dST ? a.dST[(bh * DV + r0 + 16 * rt + 4 * g4 + e) * DK + 16 * (ct0 + s) + ln] : 0.f;
+      dS[s][e] = a.dST ? a.dST[(bh * DV + r0 + 16 * srt[s] + 4 * g4 + e) * DK + 16 * sct[s] + ln] : 0.f;
+  RowsReg<TQ, DK, NT> kr, qr;
+  CcReg<NT> tr, pr;
+  GateReg gr;
+  constexpr int NO = C * R / 4 / NT;   // dO: 16-byte units per thread
+  float4v orr[NO];
+  auto fetch = [&](int n) {
+    const int t0 = n * C, len = min(C, T - t0);
+    const size_t cn = bh * nc + n, row0 = (size_t)b * T + t0;
+    kr.load(k + (row0 * Hk + kh) * DK, (size_t)Hk * DK, len, tid);
+    qr.load(q + (row0 * Hk + kh) * DK, (size_t)Hk * DK, len, tid);
+    tr.load(a.Tm + cn * C * C, tid);
+    pr.load(a.Pt + cn * C * C, tid);
+    gr.load(a, cn, tid);
+#pragma unroll
+    for (int i = 0; i < NO; ++i) {
+      const int x = tid + i * NT, t = x / (R / 4), r = (x % (R / 4)) * 4;
+      orr[i] = t < len ? *reinterpret_cast<const float4v *>(a.dO + ((row0 + t) * Hv + h) * DV + r0 + r)
+                       : float4v{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  fetch(nc - 1);
   for (int n = nc - 1; n >= 0; --n) {
     const int t0 = n * C, len = min(C, T - t0);
     const size_t cn = bh * nc + n, row0 = (size_t)b * T + t0;
-    load_rows<TQ, DK>(sK, (const TQ *)a.k, row0 * Hk + kh, Hk, len, tid);
-    load_rows<TQ, DK>(sQ, (const TQ *)a.q, row0 * Hk + kh, Hk, len, tid);
-    load_cc(sT, a.Tm + cn * C * C, tid);
-    load_cc(sP, a.Pt + cn * C * C, tid);
-    load_gates(sEg, sEc, sb, a, cn, tid);
-    for (int u = tid; u < C * R / 4; u += 256) {
-      const int t = u / (R / 4), r = (u % (R / 4)) * 4;
-      *reinterpret_cast<float4v *>(sO + t * LR + r) =
-          t < len ? *reinterpret_cast<const float4v *>(a.dO + ((row0 + t) * Hv + h) * DV + r0 + r)
-                  : float4v{0.f, 0.f, 0.f, 0.f};
+    kr.template store<LK>(sK, tid);
+    qr.template store<LK>(sQ, tid);
+    tr.store(sT, tid);
+    pr.store(sP, tid);
+    gr.store(sEg, sEc, sb, tid);
+#pragma unroll
+    for (int i = 0; i < NO; ++i) {
+      const int x = tid + i * NT;
+      *reinterpret_cast<float4v *>(sO + (x / (R / 4)) * LR + (x % (R / 4)) * 4) = orr[i];
     }
     float *dSg = a.dSC + (cn * DV + r0) * DK;
 #pragma unroll
-    for (int s = 0; s < NST; ++s)
+    for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rt + 4 * g4 + e, c = 16 * (ct0 + s) + ln;
-        sS[r * LK + c] = dS[s][e];
+        const int r = 16 * srt[s] + 4 * g4 + e, c = 16 * sct[s] + ln;
+        sS[r * LS + c] = dS[s][e];
         dSg[r * DK + c] = dS[s][e];
       }
-    __syncthreads();
+    lds_barrier();
+    if (n > 0) fetch(n - 1);
     // dU^T[r][i] = e^(gamma_C - gamma_i) (dS k_i)[r] + sum_j dO[j][r] P[j][i]
 #pragma unroll
-    for (int z = 0; z < 2; ++z) {
-      const int i = 16 * (zc0 + z) + ln;
+    for (int z = 0; z < ZT; ++z) {
+      const int rt = zrt[z], i = 16 * zcc[z] + ln;
       float4v acc = {0.f, 0.f, 0.f, 0.f};
-      mm<DK>(acc, [&](int k) { return row4(sS + (16 * rt + ln) * LK + k); },
-             [&](int k) { return row4(sK + i * LK + k); }, g4);
+      mm<DK>(acc, [&](int kk) { return row4(sS + (16 * rt + ln) * LS + kk); },
+             [&](int kk) { return rowq(sK + i * LK + kk); }, g4);
       acc *= sEc[i];
-      mm<C>(acc, [&](int k) { return col4(sO + k * LR + 16 * rt + ln, LR); },
-            [&](int k) { return row4(sP + i * LC + k); }, g4);
+      mm<C>(acc, [&](int kk) { return col4(sO + kk * LR + 16 * rt + ln, LR); },
+            [&](int kk) { return row4(sP + i * LC + kk); }, g4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) sD[(16 * rt + 4 * g4 + e) * LC + i] = acc[e];
     }
-    __syncthreads();
+    lds_barrier();
     // E^T[r][i] = sum_j dU^T[r][j] T[j][i]; dv = beta E; -beta e^gamma E^T to LDS
 #pragma unroll
-    for (int z = 0; z < 2; ++z) {
-      const int i = 16 * (zc0 + z) + ln;
+    for (int z = 0; z < ZT; ++z) {
+      const int rt = zrt[z], i = 16 * zcc[z] + ln;
       float4v E = {0.f, 0.f, 0.f, 0.f};
-      mm<C>(E, [&](int k) { return row4(sD + (16 * rt + ln) * LC + k); },
-            [&](int k) { return col4(sT + k * LC + i, LC); }, g4);
+      mm<C>(E, [&](int kk) { return row4(sD + (16 * rt + ln) * LC + kk); },
+            [&](int kk) { return col4(sT + kk * LC + i, LC); }, g4);
       const float bi = sb[i];
       if (i < len)
         *reinterpret_cast<float4v *>(a.dv + ((row0 + i) * Hv + h) * DV + r0 + 16 * rt + 4 * g4) = E * bi;
@@ -335,155 +502,235 @@ __global__ __launch_bounds__(256) void cb_bwd_kernel(CbArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) sE[(16 * rt + 4 * g4 + e) * LC + i] = E[e] * f;
     }
-    __syncthreads();
+    lds_barrier();
     // dS <- e^gamma_C dS + sum_t dO[t][r] e^gamma_t q_t - sum_t beta_t e^gamma_t E[t][r] k_t
     const float eC = sEg[C - 1];
 #pragma unroll
-    for (int s = 0; s < NST; ++s) {
-      const int c = 16 * (ct0 + s) + ln;
+    for (int s = 0; s < NS; ++s) {
+      const int rt = srt[s], c = 16 * sct[s] + ln;
       dS[s] *= eC;
-      mm<C>(dS[s], [&](int k) { return col4(sO + k * LR + 16 * rt + ln, LR) * row4(sEg + k); },
-            [&](int k) { return col4(sQ + k * LK + c, LK); }, g4);
-      mm<C>(dS[s], [&](int k) { return row4(sE + (16 * rt + ln) * LC + k); },
-            [&](int k) { return col4(sK + k * LK + c, LK); }, g4);
+      mm<C>(dS[s], [&](int kk) { return col4(sO + kk * LR + 16 * rt + ln, LR) * row4(sEg + kk); },
+            [&](int kk) { return colq(sQ + kk * LK + c, LK); }, g4);
+      mm<C>(dS[s], [&](int kk) { return row4(sE + (16 * rt + ln) * LC + kk); },
+            [&](int kk) { return colq(sK + kk * LK + c, LK); }, g4);
     }
-    __syncthreads();
+    lds_barrier();
   }
 #pragma unroll
-  for (int s = 0; s < NST; ++s)
+  for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      a.dS0[(bh * DV + r0 + 16 * rt + 4 * g4 + e) * DK + 16 * (ct0 + s) + ln] = dS[s][e];
+      a.dS0[(bh * DV + r0 + 16 * srt[s] + 4 * g4 + e) * DK + 16 * sct[s] + ln] = dS[s][e];
 }
 
 // ---------------------------------------------------------------------------
 // gradients of one (chunk, key head): for each value head of the key head,
 // the products over the value rows in slices of 32 (dP = dO U^T, E U^T,
 // dO S0, E S0, U dS_C), then the products with the masked C x C matrices
-// and the row dots; dq and dk summed over the value heads.  Wave w holds
-// token block w of every [C][.] product.
+// and the row dots; dq and dk summed over the value heads.  Eight waves
+// (four for dk < 128): wave w holds token block w & 3 of every [C][.]
+// product, and half w >> 2 of its column blocks.  The next slice is loaded
+// into registers while the current one is worked on.
+template <typename TQ, int DK>
+struct GradCfg {
+  static constexpr int NW = DK == 128 ? 8 : 4, NT = 64 * NW, NH = NW / 4;   // column halves
+  static constexpr int LK = DK + 4, NCT = DK / 16, HCT = NCT / NH, HJ = 4 / NH;
+  static constexpr int SLICE = 3 * C * LR + 2 * R * LK, MASKS = 2 * C * LC;
+  static constexpr int REGION = SLICE > MASKS ? SLICE : MASKS;
+  static constexpr int NC4 = C * R / 4 / NT, NS4 = R * DK / 4 / NT;   // 16-byte units per thread
+  static constexpr int NV = 8 * C / NT;                                 // (token, 4 rows) units of E . v
+  static constexpr int smem = (2 * C * LK + REGION + (4 + 3 * NH) * C + 4) * 4;
+};
+
+// acc1 += A1 B^T, acc2 += A2 B^T (one read of B)
+template <int K, typename FA1, typename FA2, typename FB>
+__device__ __forceinline__ void mm2(float4v &acc1, float4v &acc2, const FA1 &fa1, const FA2 &fa2, const FB &fb,
+                                    int g4) {
+#pragma unroll
+  for (int k = 0; k < K; k += 16) {
+    const float4v x1 = fa1(k + 4 * g4), x2 = fa2(k + 4 * g4), y = fb(k + 4 * g4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc1 = mma(x1[e], y[e], acc1);
+      acc2 = mma(x2[e], y[e], acc2);
+    }
+  }
+}
+
 template <typename TQ, typename TG, int DK>
-__global__ __launch_bounds__(256) void cb_grads_kernel(CbArgs a) {
-  constexpr int LK = DK + 4, NCT = DK / 16;
-  constexpr int SLICE = 3 * C * LR + 2 * R * LK, MASKS = 2 * C * LC;
-  constexpr int REGION = SLICE > MASKS ? SLICE : MASKS;
+__global__ __launch_bounds__((GradCfg<TQ, DK>::NT)) void cb_grads_kernel(CbArgs a) {
+  using G = GradCfg<TQ, DK>;
+  constexpr int LK = G::LK, NT = G::NT, NH = G::NH, HCT = G::HCT, HJ = G::HJ, NC4 = G::NC4, NS4 = G::NS4;
+  constexpr int NV = G::NV;
   extern __shared__ float4v smem4[];
   float *smem = reinterpret_cast<float *>(smem4);
   float *sK = smem, *sQ = sK + C * LK, *rg = sQ + C * LK;
   float *sO = rg, *sU = sO + C * LR, *sE = sU + C * LR, *sS0 = sE + C * LR, *sdS = sS0 + R * LK;
   float *sdP = rg, *sB = sdP + C * LC;
-  float *sEg = rg + REGION, *sEc = sEg + C, *sb = sEc + C, *sGam = sb + C, *sBet = sGam + C, *sBx = sBet + C;
-  float *sg = sBx + C, *sRed = sg + C;
+  float *sEg = rg + G::REGION, *sEc = sEg + C, *sb = sEc + C, *sg = sb + C;
+  float *sGam = sg + C, *sBet = sGam + NH * C, *sBx = sBet + NH * C, *sRed = sBx + NH * C;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 15, g4 = lane >> 4;
+  const int tw = w & 3, hw = w >> 2, ct0 = hw * HCT, J0 = hw * HJ;
   const int n = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
   const int T = a.T, Hk = a.Hk, Hv = a.Hv, DV = a.dv_dim, nc = a.nc, grp = Hv / Hk;
   const int t0 = n * C, len = min(C, T - t0);
   const size_t row0 = (size_t)b * T + t0;
   const TQ *v = (const TQ *)a.v;
-  load_rows<TQ, DK>(sK, (const TQ *)a.k, row0 * Hk + kh, Hk, len, tid);
-  load_rows<TQ, DK>(sQ, (const TQ *)a.q, row0 * Hk + kh, Hk, len, tid);
-  float4v dQa[NCT], dKa[NCT];
+  for (int u = tid; u < C * DK / 8; u += NT) {
+    const int t = u / (DK / 8), c = (u % (DK / 8)) * 8;
+    float x[8], y[8];
+    if (t < len) {
+      load8((const TQ *)a.k + ((row0 + t) * Hk + kh) * DK + c, x);
+      load8((const TQ *)a.q + ((row0 + t) * Hk + kh) * DK + c, y);
+    } else {
 #pragma unroll
-  for (int c = 0; c < NCT; ++c) dQa[c] = dKa[c] = float4v{0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < 8; ++e) x[e] = y[e] = 0.f;
+    }
+    *reinterpret_cast<float4v *>(sK + t * LK + c) = float4v{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<float4v *>(sK + t * LK + c + 4) = float4v{x[4], x[5], x[6], x[7]};
+    *reinterpret_cast<float4v *>(sQ + t * LK + c) = float4v{y[0], y[1], y[2], y[3]};
+    *reinterpret_cast<float4v *>(sQ + t * LK + c + 4) = float4v{y[4], y[5], y[6], y[7]};
+  }
+  // slice registers: dO, U, E [C][32] and S0, dS_C [32][dk], and v for E . v; the
+  // loads take a uniform base per (head, slice) and 32-bit offsets per thread
+  float4v ro[NC4], ru[NC4], re[NC4], rs[NS4], rd[NS4];
+  typename Quad<TQ>::type rv[NV];
+  // E . v: unit tid + i NT is token (tid + i NT) / 8, rows 4 ((tid + i NT) % 8) ..
+  auto vtok = [&](int i) { return (tid + i * NT) >> 3; };
+  const int vr = (tid & 7) * 4;
+  auto fetch = [&](int h, int r0) {
+    const size_t cn = ((size_t)b * Hv + h) * nc + n;
+    const float *pO = a.dO + (row0 * Hv + h) * DV + r0, *pU = a.Um + cn * C * DV + r0, *pE = a.Em + cn * C * DV + r0;
+    const float *pS = a.S0s + (cn * DV + r0) * DK, *pD = a.dSC + (cn * DV + r0) * DK;
+#pragma unroll
+    for (int i = 0; i < NC4; ++i) {
+      const int x = tid + i * NT, t = x / (R / 4), r = (x % (R / 4)) * 4;
+      ro[i] = t < len ? *reinterpret_cast<const float4v *>(pO + (t * Hv * DV + r)) : float4v{0.f, 0.f, 0.f, 0.f};
+      ru[i] = *reinterpret_cast<const float4v *>(pU + (t * DV + r));
+      re[i] = *reinterpret_cast<const float4v *>(pE + (t * DV + r));
+    }
+#pragma unroll
+    for (int i = 0; i < NS4; ++i) {
+      const int x = tid + i * NT;
+      rs[i] = *reinterpret_cast<const float4v *>(pS + 4 * x);
+      rd[i] = *reinterpret_cast<const float4v *>(pD + 4 * x);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (vtok(i) < len) rv[i] = quad_load(v + (row0 * Hv + h) * DV + r0 + (vtok(i) * Hv * DV + vr));
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < NC4; ++i) {
+      const int x = tid + i * NT, t = x / (R / 4), r = (x % (R / 4)) * 4;
+      *reinterpret_cast<float4v *>(sO + t * LR + r) = ro[i];
+      *reinterpret_cast<float4v *>(sU + t * LR + r) = ru[i];
+      *reinterpret_cast<float4v *>(sE + t * LR + r) = re[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NS4; ++i) {
+      const int x = tid + i * NT, r = x / (DK / 4), c = (x % (DK / 4)) * 4;
+      *reinterpret_cast<float4v *>(sS0 + r * LK + c) = rs[i];
+      *reinterpret_cast<float4v *>(sdS + r * LK + c) = rd[i];
+    }
+  };
+  float4v dQa[HCT], dKa[HCT];
+#pragma unroll
+  for (int c = 0; c < HCT; ++c) dQa[c] = dKa[c] = float4v{0.f, 0.f, 0.f, 0.f};
+  const int nsl = DV / R;
+  fetch(kh * grp, 0);
   for (int hh = 0; hh < grp; ++hh) {
     const int h = kh * grp + hh;
     const size_t cn = ((size_t)b * Hv + h) * nc + n;
-    __syncthreads();   // the previous head's last reads of LDS are done
-    load_gates(sEg, sEc, sb, a, cn, tid, sg);
-    if (tid < 2) sRed[tid] = 0.f;
-    float4v dPa[4], dAa[4], Q1[NCT], ES[NCT], UD[NCT];
+    float4v dPa[HJ], dAa[HJ], Q1[HCT], ES[HCT], UD[HCT];
 #pragma unroll
-    for (int J = 0; J < 4; ++J) dPa[J] = dAa[J] = float4v{0.f, 0.f, 0.f, 0.f};
+    for (int J = 0; J < HJ; ++J) dPa[J] = dAa[J] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < NCT; ++c) Q1[c] = ES[c] = UD[c] = float4v{0.f, 0.f, 0.f, 0.f};
-    float dbx = 0.f, sdot = 0.f;
-    for (int r0 = 0; r0 < DV; r0 += R) {
-      __syncthreads();
-      for (int u = tid; u < C * R / 4; u += 256) {
-        const int t = u / (R / 4), r = (u % (R / 4)) * 4;
-        *reinterpret_cast<float4v *>(sO + t * LR + r) =
-            t < len ? *reinterpret_cast<const float4v *>(a.dO + ((row0 + t) * Hv + h) * DV + r0 + r)
-                    : float4v{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<float4v *>(sU + t * LR + r) =
-            *reinterpret_cast<const float4v *>(a.Um + (cn * C + t) * DV + r0 + r);
-        *reinterpret_cast<float4v *>(sE + t * LR + r) =
-            *reinterpret_cast<const float4v *>(a.Em + (cn * C + t) * DV + r0 + r);
+    for (int c = 0; c < HCT; ++c) Q1[c] = ES[c] = UD[c] = float4v{0.f, 0.f, 0.f, 0.f};
+    float dbx[NV], sdot = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) dbx[i] = 0.f;
+    for (int si = 0; si < nsl; ++si) {
+      lds_barrier();   // the previous slice's (or head's) reads of the region are done
+      stage();
+      float4v vx[NV];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) vx[i] = quad_to_f32<TQ>(rv[i]);
+      if (si == 0) {
+        load_gates(sEg, sEc, sb, a, cn, tid, sg);
+        if (tid < 2) sRed[tid] = 0.f;
       }
-      for (int u = tid; u < R * DK / 4; u += 256) {
-        const int r = u / (DK / 4), c = (u % (DK / 4)) * 4;
-        *reinterpret_cast<float4v *>(sS0 + r * LK + c) =
-            *reinterpret_cast<const float4v *>(a.S0s + (cn * DV + r0 + r) * DK + c);
-        *reinterpret_cast<float4v *>(sdS + r * LK + c) =
-            *reinterpret_cast<const float4v *>(a.dSC + (cn * DV + r0 + r) * DK + c);
-      }
-      __syncthreads();
-      {
-        // E . v over the slice for token tid / 4
-        const int t = tid >> 2, rr = (tid & 3) * 8;
-        if (t < len) {
-          float vx[8];
-          load8(v + ((row0 + t) * Hv + h) * DV + r0 + rr, vx);
+      lds_barrier();
+      // the next slice, or the next head's first
+      if (si + 1 < nsl)
+        fetch(h, (si + 1) * R);
+      else if (hh + 1 < grp)
+        fetch(h + 1, 0);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) dbx = __builtin_fmaf(sE[t * LR + rr + e], vx[e], dbx);
+      for (int i = 0; i < NV; ++i)
+        if (vtok(i) < len) {
+          const float4v ev = row4(sE + vtok(i) * LR + vr);
+          dbx[i] += ev[0] * vx[i][0] + ev[1] * vx[i][1] + ev[2] * vx[i][2] + ev[3] * vx[i][3];
         }
-      }
-      for (int u = tid; u < R * DK; u += 256) {
-        const int r = u / DK, c = u % DK;
-        sdot = __builtin_fmaf(sS0[r * LK + c], sdS[r * LK + c], sdot);
+#pragma unroll
+      for (int i = 0; i < NS4; ++i) {
+        const int x = tid + i * NT, r = x / (DK / 4), c = (x % (DK / 4)) * 4;
+        const float4v p = row4(sS0 + r * LK + c) * row4(sdS + r * LK + c);
+        sdot += (p[0] + p[1]) + (p[2] + p[3]);
       }
 #pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        mm<R>(dPa[J], [&](int k) { return row4(sO + (16 * w + ln) * LR + k); },
-              [&](int k) { return row4(sU + (16 * J + ln) * LR + k); }, g4);
-        mm<R>(dAa[J], [&](int k) { return row4(sE + (16 * w + ln) * LR + k); },
-              [&](int k) { return row4(sU + (16 * J + ln) * LR + k); }, g4);
-      }
+      for (int J = 0; J < HJ; ++J)
+        mm2<R>(dPa[J], dAa[J], [&](int k) { return row4(sO + (16 * tw + ln) * LR + k); },
+               [&](int k) { return row4(sE + (16 * tw + ln) * LR + k); },
+               [&](int k) { return row4(sU + (16 * (J0 + J) + ln) * LR + k); }, g4);
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const int c = 16 * ct + ln;
-        mm<R>(Q1[ct], [&](int k) { return row4(sO + (16 * w + ln) * LR + k); },
-              [&](int k) { return col4(sS0 + k * LK + c, LK); }, g4);
-        mm<R>(ES[ct], [&](int k) { return row4(sE + (16 * w + ln) * LR + k); },
-              [&](int k) { return col4(sS0 + k * LK + c, LK); }, g4);
-        mm<R>(UD[ct], [&](int k) { return row4(sU + (16 * w + ln) * LR + k); },
+      for (int ct = 0; ct < HCT; ++ct) {
+        const int c = 16 * (ct0 + ct) + ln;
+        mm2<R>(Q1[ct], ES[ct], [&](int k) { return row4(sO + (16 * tw + ln) * LR + k); },
+               [&](int k) { return row4(sE + (16 * tw + ln) * LR + k); },
+               [&](int k) { return col4(sS0 + k * LK + c, LK); }, g4);
+        mm<R>(UD[ct], [&](int k) { return row4(sU + (16 * tw + ln) * LR + k); },
               [&](int k) { return col4(sdS + k * LK + c, LK); }, g4);
+        __builtin_amdgcn_sched_barrier(0);   // one tile's operands live at a time
       }
     }
-    __syncthreads();
+    lds_barrier();
     // M o dP and B = M o dA = -(M o E U^T) into LDS (over the slices' space)
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
-      const int j = 16 * J + ln;
+    for (int J = 0; J < HJ; ++J) {
+      const int j = 16 * (J0 + J) + ln;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * w + 4 * g4 + e;
+        const int i = 16 * tw + 4 * g4 + e;
         const float m = i >= j ? __expf(sg[i] - sg[j]) : 0.f;
         sdP[i * LC + j] = m * dPa[J][e];
         sB[i * LC + j] = i > j ? -m * dAa[J][e] : 0.f;
       }
     }
-    // E . v and <dS_C, S0> over the workgroup
-    dbx = group_sum<4>(dbx);
-    if ((tid & 3) == 0) sBx[tid >> 2] = dbx;
+    // E . v (eight threads per token) and <dS_C, S0> over the workgroup
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const float x = group_sum<8>(dbx[i]);
+      if ((tid & 7) == 0) sBx[vtok(i)] = x;
+    }
     sdot = group_sum<64>(sdot);
     if (lane == 0) atomicAdd(&sRed[1], sdot);
-    __syncthreads();
+    lds_barrier();
     float gp[4] = {0.f, 0.f, 0.f, 0.f}, bp[4] = {0.f, 0.f, 0.f, 0.f}, cp = 0.f;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const int c = 16 * ct + ln;
+    for (int ct = 0; ct < HCT; ++ct) {
+      const int c = 16 * (ct0 + ct) + ln;
       float4v q2 = {0.f, 0.f, 0.f, 0.f}, k1 = q2, f1 = q2, f2 = q2;
-      mm<C>(q2, [&](int k) { return row4(sdP + (16 * w + ln) * LC + k); },
-            [&](int k) { return col4(sK + k * LK + c, LK); }, g4);
-      mm<C>(k1, [&](int k) { return col4(sdP + k * LC + 16 * w + ln, LC); },
+      mm2<C>(q2, f1, [&](int k) { return row4(sdP + (16 * tw + ln) * LC + k); },
+             [&](int k) { return row4(sB + (16 * tw + ln) * LC + k); },
+             [&](int k) { return col4(sK + k * LK + c, LK); }, g4);
+      mm<C>(k1, [&](int k) { return col4(sdP + k * LC + 16 * tw + ln, LC); },
             [&](int k) { return col4(sQ + k * LK + c, LK); }, g4);
-      mm<C>(f1, [&](int k) { return row4(sB + (16 * w + ln) * LC + k); },
-            [&](int k) { return col4(sK + k * LK + c, LK); }, g4);
-      mm<C>(f2, [&](int k) { return col4(sB + k * LC + 16 * w + ln, LC) * row4(sb + k); },
+      mm<C>(f2, [&](int k) { return col4(sB + k * LC + 16 * tw + ln, LC) * row4(sb + k); },
             [&](int k) { return col4(sK + k * LK + c, LK); }, g4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int t = 16 * w + 4 * g4 + e;
+        const int t = 16 * tw + 4 * g4 + e;
         const float eg = sEg[t], bt = sb[t];
         const float dq = __builtin_fmaf(eg, Q1[ct][e], q2[e]);
         const float f1m = __builtin_fmaf(-eg, ES[ct][e], f1[e]);   // (B k)_t - e^gamma_t (E S0)_t
@@ -496,6 +743,8 @@ __global__ __launch_bounds__(256) void cb_grads_kernel(CbArgs a) {
         bp[e] += kv * f1m;
         cp = __builtin_fmaf(kv, d4, cp);
       }
+      // the next tile reads its operands again rather than keep them in registers
+      asm volatile("" ::: "memory");
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -505,45 +754,49 @@ __global__ __launch_bounds__(256) void cb_grads_kernel(CbArgs a) {
     if (ln == 0) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sGam[16 * w + 4 * g4 + e] = gp[e];
-        sBet[16 * w + 4 * g4 + e] = bp[e];
+        sGam[hw * C + 16 * tw + 4 * g4 + e] = gp[e];
+        sBet[hw * C + 16 * tw + 4 * g4 + e] = bp[e];
       }
     }
     cp = group_sum<64>(cp);
     if (lane == 0) atomicAdd(&sRed[0], cp);
-    __syncthreads();
+    lds_barrier();
     if (w == 0) {
       // dg_t = sum over the chunk's tokens i >= t of the gradient of gamma_i; the
       // last token also carries <dS_C, S_C> = e^gamma_C <dS_C, S0> + sum_j k_j . dk4_j
       const int t = C - 1 - lane;
-      const float x = sGam[t] + (t == C - 1 ? __builtin_fmaf(sEg[C - 1], sRed[1], sRed[0]) : 0.f);
+      float x = sGam[t], y = sBet[t] + sBx[t];
+#pragma unroll
+      for (int u = 1; u < NH; ++u) x += sGam[u * C + t], y += sBet[u * C + t];
+      if (t == C - 1) x += __builtin_fmaf(sEg[C - 1], sRed[1], sRed[0]);
       const float s = wave_prefix_sum(x);
       if (t < len) {
         a.dg[(row0 + t) * Hv + h] = s;
-        a.dbeta[(row0 + t) * Hv + h] = sBet[t] + sBx[t];
+        a.dbeta[(row0 + t) * Hv + h] = y;
       }
     }
   }
+  float *pq = a.dq + (row0 * Hk + kh) * DK, *pk = a.dk + (row0 * Hk + kh) * DK;
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
+  for (int ct = 0; ct < HCT; ++ct)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int t = 16 * w + 4 * g4 + e;
+      const int t = 16 * tw + 4 * g4 + e, o = t * Hk * DK + 16 * (ct0 + ct) + ln;
       if (t < len) {
-        a.dq[((row0 + t) * Hk + kh) * DK + 16 * ct + ln] = dQa[ct][e];
-        a.dk[((row0 + t) * Hk + kh) * DK + 16 * ct + ln] = dKa[ct][e];
+        pq[o] = dQa[ct][e];
+        pk[o] = dKa[ct][e];
       }
     }
 }
 
-template <int DK>
+template <typename TQ, int DK>
 struct CbSmem {
   static constexpr int LK = DK + 4;
-  static constexpr int prep = (2 * C * LK + C * LC + 2 * C) * 4;
-  static constexpr int fwd = (C * LK + C * LC + R * LK + 2 * R * LC + 3 * C) * 4;
-  static constexpr int bwd = (2 * C * LK + 2 * C * LC + C * LR + R * LK + 2 * R * LC + 3 * C) * 4;
-  static constexpr int slice = 3 * C * LR + 2 * R * LK, masks = 2 * C * LC;
-  static constexpr int grads = (2 * C * LK + (slice > masks ? slice : masks) + 7 * C + 4) * 4;
+  static constexpr int QK = PassCfg<TQ, DK>::LK * (int)sizeof(TQ), LS = DK + 4;
+  static constexpr int fwd = C * QK + (C * LC + R * LS + 2 * R * LC + 3 * C) * 4;
+  static constexpr int bwd = 2 * C * QK + (2 * C * LC + C * LR + R * LS + 2 * R * LC + 3 * C) * 4;
+  static constexpr int prep = (C * LK + C * LC + 2 * C) * 4;
+  static constexpr int grads = GradCfg<TQ, DK>::smem;
 };
 
 template <typename F>
@@ -553,7 +806,8 @@ hipError_t set_smem(F *kern, int bytes) {
 
 template <typename TQ, typename TG, int DK>
 hipError_t launch_cb_t(const Shape &sh, const CbArgs &a, hipStream_t st) {
-  using Sm = CbSmem<DK>;
+  using Sm = CbSmem<TQ, DK>;
+  constexpr int NTP = PassCfg<TQ, DK>::NT;
   static_assert(Sm::bwd <= 160 * 1024 && Sm::grads <= 160 * 1024 && Sm::prep <= 160 * 1024, "LDS");
   hipError_t e;
   if ((e = set_smem(cb_prep_kernel<TQ, TG, DK>, Sm::prep)) != hipSuccess) return e;
@@ -562,11 +816,12 @@ hipError_t launch_cb_t(const Shape &sh, const CbArgs &a, hipStream_t st) {
   if ((e = set_smem(cb_grads_kernel<TQ, TG, DK>, Sm::grads)) != hipSuccess) return e;
   hipLaunchKernelGGL((cb_prep_kernel<TQ, TG, DK>), dim3(a.nc, sh.Hv, sh.B), dim3(256), Sm::prep, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((cb_fwd_kernel<TQ, DK>), dim3(sh.dv / R, sh.Hv, sh.B), dim3(256), Sm::fwd, st, a);
+  hipLaunchKernelGGL((cb_fwd_kernel<TQ, DK>), dim3(sh.dv / R, sh.Hv, sh.B), dim3(NTP), Sm::fwd, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((cb_bwd_kernel<TQ, DK>), dim3(sh.dv / R, sh.Hv, sh.B), dim3(256), Sm::bwd, st, a);
+  hipLaunchKernelGGL((cb_bwd_kernel<TQ, DK>), dim3(sh.dv / R, sh.Hv, sh.B), dim3(NTP), Sm::bwd, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((cb_grads_kernel<TQ, TG, DK>), dim3(a.nc, sh.Hk, sh.B), dim3(256), Sm::grads, st, a);
+  hipLaunchKernelGGL((cb_grads_kernel<TQ, TG, DK>), dim3(a.nc, sh.Hk, sh.B), dim3(GradCfg<TQ, DK>::NT), Sm::grads,
+                     st, a);
   return hipGetLastError();
 }
 
