@@ -21,7 +21,8 @@
 // sum over the chunk's later tokens.
 //
 // Four launches, the three passes after the first working from its output:
-//  - prep, per (chunk, value head): gamma, beta, T and P^T;
+//  - prep, per (chunk, key head) over the key head's value heads: gamma,
+//    beta, T and P^T;
 //  - forward pass, per (batch, value head, 32 state rows), over the chunks in
 //    order: the state before each chunk and U;
 //  - backward pass, per (batch, value head, 32 state rows), over the chunks
@@ -76,20 +77,26 @@ __device__ __forceinline__ void mm(float4v &acc, const FA &fa, const FB &fb, int
 }
 
 // rows of a chunk of q or k (zeros past the sequence's end) into LDS, fp32 [C][DK + 4]
+// (a 256-thread workgroup; every load is issued before the first store)
 template <typename TQ, int DK>
 __device__ __forceinline__ void load_rows(float *dst, const TQ *src, size_t row0, int stride, int len, int tid) {
-  constexpr int LK = DK + 4;
-  for (int u = tid; u < C * DK / 8; u += 256) {
-    const int t = u / (DK / 8), c = (u % (DK / 8)) * 8;
-    float x[8];
+  constexpr int LK = DK + 4, NU = C * DK / 8 / 256;
+  float x[NU][8];
+#pragma unroll
+  for (int i = 0; i < NU; ++i) {
+    const int u = tid + 256 * i, t = u / (DK / 8), c = (u % (DK / 8)) * 8;
     if (t < len) {
-      load8(src + (row0 + (size_t)t * stride) * DK + c, x);
+      load8(src + (row0 + (size_t)t * stride) * DK + c, x[i]);
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+      for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
     }
-    *reinterpret_cast<float4v *>(dst + t * LK + c) = float4v{x[0], x[1], x[2], x[3]};
-    *reinterpret_cast<float4v *>(dst + t * LK + c + 4) = float4v{x[4], x[5], x[6], x[7]};
+  }
+#pragma unroll
+  for (int i = 0; i < NU; ++i) {
+    const int u = tid + 256 * i, t = u / (DK / 8), c = (u % (DK / 8)) * 8;
+    *reinterpret_cast<float4v *>(dst + t * LK + c) = float4v{x[i][0], x[i][1], x[i][2], x[i][3]};
+    *reinterpret_cast<float4v *>(dst + t * LK + c + 4) = float4v{x[i][4], x[i][5], x[i][6], x[i][7]};
   }
 }
 
@@ -115,18 +122,25 @@ __device__ __forceinline__ void load_gates(float *sEg, float *sEc, float *sb, co
 
 // ---------------------------------------------------------------------------
 // prep: gamma (inclusive prefix sum of g over the chunk, zero past the end),
-// beta, P^T and T = (I + A)^-1 by forward substitution.
+// beta, P^T and T = (I + A)^-1 in 16 x 16 blocks: the diagonal blocks by
+// forward substitution (one wave each), then the blocks below them, one block
+// diagonal at a time, as T_IJ = -T_II sum_{J <= K < I} A_IK T_KJ.
+constexpr int LX = 20;   // stride of the prep's 16 x 16 staging tiles
+// the prep's first LDS region: k rows [C][DK + 4], later T [C][LC] and four staging tiles
+__host__ __device__ constexpr int prep_region(int DK) {
+  return C * (DK + 4) > C * LC + 4 * 16 * LX ? C * (DK + 4) : C * LC + 4 * 16 * LX;
+}
+
 template <typename TQ, typename TG, int DK>
 __global__ __launch_bounds__(256) void cb_prep_kernel(CbArgs a) {
   constexpr int LK = DK + 4;
   extern __shared__ float4v smem4[];
   float *smem = reinterpret_cast<float *>(smem4);
-  float *sK = smem, *sA = sK + C * LK, *sg = sA + C * LC, *sb = sg + C;
+  float *sK = smem, *sA = sK + prep_region(DK), *sg = sA + C * LC, *sb = sg + C;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 15, g4 = lane >> 4;
-  const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int T = a.T, Hk = a.Hk, Hv = a.Hv, kh = h / (Hv / Hk);
+  const int n = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
+  const int T = a.T, Hk = a.Hk, Hv = a.Hv, grp = Hv / Hk;
   const int t0 = n * C, len = min(C, T - t0);
-  const size_t cn = ((size_t)b * Hv + h) * a.nc + n;
   const size_t row0 = (size_t)b * T + t0;
   load_rows<TQ, DK>(sK, (const TQ *)a.k, row0 * Hk + kh, Hk, len, tid);
   // the lane's q entries of token 16 w + ln as matrix-core operands (zeros past the end)
@@ -140,53 +154,99 @@ __global__ __launch_bounds__(256) void cb_prep_kernel(CbArgs a) {
       qa[kb] = float4v{x[0], x[1], x[2], x[3]};
     }
   }
-  if (w == 0) {
-    const TG *g = (const TG *)a.g, *be = (const TG *)a.beta;
-    const float gt = lane < len ? to_f32(g[(row0 + lane) * Hv + h]) : 0.f;
-    const float bt = lane < len ? to_f32(be[(row0 + lane) * Hv + h]) : 0.f;
-    const float gm = wave_prefix_sum(gt);
-    sg[lane] = gm;
-    sb[lane] = bt;
-    a.gam[cn * C + lane] = gm;
-    a.bet[cn * C + lane] = bt;
-  }
   __syncthreads();
-  // wave w: block row w (tokens 16 w ..); the lane holds i = 16 w + 4 g4 + e, j = 16 J + ln
-  float *Ptg = a.Pt + cn * C * C;
+  // K K^T and Q K^T of the key head, once for its value heads: wave w holds the
+  // tiles of block row w (tokens 16 w ..) left of and on the diagonal; the lane
+  // holds i = 16 w + 4 g4 + e, j = 16 J + ln
+  float4v kk[4], qk[4];
 #pragma unroll
   for (int J = 0; J < 4; ++J) {
-    float4v kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
+    kk[J] = qk[J] = float4v{0.f, 0.f, 0.f, 0.f};
     if (J <= w) {
-      mm<DK>(kk, [&](int k) { return row4(sK + (16 * w + ln) * LK + k); },
+      mm<DK>(kk[J], [&](int k) { return row4(sK + (16 * w + ln) * LK + k); },
              [&](int k) { return row4(sK + (16 * J + ln) * LK + k); }, g4);
-      mm<DK>(qk, [&](int k) { return qa[k >> 4]; }, [&](int k) { return row4(sK + (16 * J + ln) * LK + k); }, g4);
+      mm<DK>(qk[J], [&](int k) { return qa[k >> 4]; }, [&](int k) { return row4(sK + (16 * J + ln) * LK + k); },
+             g4);
     }
-    const int j = 16 * J + ln;
-    float4v pt;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 16 * w + 4 * g4 + e;
-      const float m = i >= j ? __expf(sg[i] - sg[j]) : 0.f;
-      sA[i * LC + j] = i > j ? sb[i] * m * kk[e] : 0.f;
-      pt[e] = m * qk[e];
-    }
-    *reinterpret_cast<float4v *>(Ptg + j * C + 16 * w + 4 * g4) = pt;   // P^T[j][i]
   }
-  __syncthreads();
-  if (w == 0) {
-    // column c = lane of T: T[i][c] = [i == c] - sum_{j < i} A[i][j] T[j][c]
-    // (four partial sums, j mod 4, so that only one depends on T[i - 1][c])
-    float tc[C];
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-      float s[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < i; ++j) s[j & 3] = __builtin_fmaf(sA[i * LC + j], tc[j], s[j & 3]);
-      tc[i] = (i == lane ? 1.f : 0.f) - ((s[0] + s[1]) + (s[2] + s[3]));
+  // T over the k rows' space; a 16 x 16 staging tile per wave after it
+  float *sT = sK, *sX = sK + C * LC + w * 16 * LX;
+  for (int hh = 0; hh < grp; ++hh) {
+    const int h = kh * grp + hh;
+    const size_t cn = ((size_t)b * Hv + h) * a.nc + n;
+    __syncthreads();   // the k rows (first head) or the previous head's T are read
+    if (w == 0) {
+      const TG *g = (const TG *)a.g, *be = (const TG *)a.beta;
+      const float gt = lane < len ? to_f32(g[(row0 + lane) * Hv + h]) : 0.f;
+      const float bt = lane < len ? to_f32(be[(row0 + lane) * Hv + h]) : 0.f;
+      const float gm = wave_prefix_sum(gt);
+      sg[lane] = gm;
+      sb[lane] = bt;
+      a.gam[cn * C + lane] = gm;
+      a.bet[cn * C + lane] = bt;
     }
-    float *Tg = a.Tm + cn * C * C;
+    __syncthreads();
+    float *Ptg = a.Pt + cn * C * C;
 #pragma unroll
-    for (int i = 0; i < C; ++i) Tg[i * C + lane] = tc[i];
+    for (int J = 0; J < 4; ++J) {
+      const int j = 16 * J + ln;
+      float4v pt;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * w + 4 * g4 + e;
+        const float m = i >= j ? __expf(sg[i] - sg[j]) : 0.f;
+        sA[i * LC + j] = i > j ? sb[i] * m * kk[J][e] : 0.f;
+        pt[e] = m * qk[J][e];
+      }
+      *reinterpret_cast<float4v *>(Ptg + j * C + 16 * w + 4 * g4) = pt;   // P^T[j][i]
+    }
+    __syncthreads();
+    {
+      // diagonal block w: lane (c, q) = (lane / 4, lane % 4) holds T[b + 4 m + q][b + c]
+      // (b = 16 w); T[i][c] = [i == c] - sum_{j < i} A[i][j] T[j][c], the sum over
+      // j = 4 m + q in the lane and over q in the quad (A is zero on and above the diagonal)
+      const int c = lane >> 2, q = lane & 3, bw = 16 * w;
+      float t4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float s = 0.f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) s = __builtin_fmaf(sA[(bw + i) * LC + bw + 4 * m + q], t4[m], s);
+        s = group_sum<4>(s);
+        const float val = (i == c ? 1.f : 0.f) - s;
+        t4[i >> 2] = q == (i & 3) ? val : t4[i >> 2];
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) sT[(bw + 4 * m + q) * LC + bw + c] = t4[m];
+      // blocks above the diagonal are zero
+      for (int J = w + 1; J < 4; ++J)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) sT[(bw + 4 * m + q) * LC + 16 * J + c] = 0.f;
+    }
+#pragma unroll
+    for (int d = 1; d < 4; ++d) {
+      lds_barrier();
+      if (w < 4 - d) {
+        const int I = w + d, J = w;
+        float4v x = {0.f, 0.f, 0.f, 0.f};
+        for (int K = J; K < I; ++K)
+          mm<16>(x, [&](int k) { return row4(sA + (16 * I + ln) * LC + 16 * K + k); },
+                 [&](int k) { return col4(sT + (16 * K + k) * LC + 16 * J + ln, LC); }, g4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sX[(4 * g4 + e) * LX + ln] = x[e];
+        float4v y = {0.f, 0.f, 0.f, 0.f};
+        mm<16>(y, [&](int k) { return row4(sT + (16 * I + ln) * LC + 16 * I + k); },
+               [&](int k) { return col4(sX + k * LX + ln, LX); }, g4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sT[(16 * I + 4 * g4 + e) * LC + 16 * J + ln] = -y[e];
+      }
+    }
+    lds_barrier();
+    float *Tg = a.Tm + cn * C * C;
+    for (int u = tid; u < C * C / 4; u += 256) {
+      const int i = u / (C / 4), j = (u % (C / 4)) * 4;
+      *reinterpret_cast<float4v *>(Tg + i * C + j) = row4(sT + i * LC + j);
+    }
   }
 }
 
@@ -795,7 +855,7 @@ struct CbSmem {
   static constexpr int QK = PassCfg<TQ, DK>::LK * (int)sizeof(TQ), LS = DK + 4;
   static constexpr int fwd = C * QK + (C * LC + R * LS + 2 * R * LC + 3 * C) * 4;
   static constexpr int bwd = 2 * C * QK + (2 * C * LC + C * LR + R * LS + 2 * R * LC + 3 * C) * 4;
-  static constexpr int prep = (C * LK + C * LC + 2 * C) * 4;
+  static constexpr int prep = (prep_region(DK) + C * LC + 2 * C) * 4;
   static constexpr int grads = GradCfg<TQ, DK>::smem;
 };
 
@@ -814,7 +874,7 @@ hipError_t launch_cb_t(const Shape &sh, const CbArgs &a, hipStream_t st) {
   if ((e = set_smem(cb_fwd_kernel<TQ, DK>, Sm::fwd)) != hipSuccess) return e;
   if ((e = set_smem(cb_bwd_kernel<TQ, DK>, Sm::bwd)) != hipSuccess) return e;
   if ((e = set_smem(cb_grads_kernel<TQ, TG, DK>, Sm::grads)) != hipSuccess) return e;
-  hipLaunchKernelGGL((cb_prep_kernel<TQ, TG, DK>), dim3(a.nc, sh.Hv, sh.B), dim3(256), Sm::prep, st, a);
+  hipLaunchKernelGGL((cb_prep_kernel<TQ, TG, DK>), dim3(a.nc, sh.Hk, sh.B), dim3(256), Sm::prep, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((cb_fwd_kernel<TQ, DK>), dim3(sh.dv / R, sh.Hv, sh.B), dim3(NTP), Sm::fwd, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
