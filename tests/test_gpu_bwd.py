@@ -105,3 +105,38 @@ def test_bwd_full_heads_long():
             print("[parity] bwd 16/48 T=1024 key head %d %s rel %.3e (bar 1e-4)" % (kh, n, e),
                   file=sys.stderr, flush=True)
             assert e <= 1e-4, "key head %d: %s error %.3e" % (kh, n, e)
+
+
+def test_bwd_prefill_full_size_sampled():
+    """The backward at the prefill workload's full size (B 4, T 4096, 16 key /
+    48 value heads, d 128, bf16 inputs), in the launch configuration the bench
+    times, every chain on the GPU; the oracle recomputes two sampled (batch,
+    key head) groups over the whole sequence, each with its three value heads."""
+    wl = PREFILL_CONV.with_(conv=False)
+    inp = make_prefill(wl)
+    say("bwd full size: B=%d T=%d Hk=%d Hv=%d d=128 bf16" % (wl.B, wl.T, wl.Hk, wl.Hv))
+    r = np.random.default_rng(4242)
+    S0 = np.ascontiguousarray(r.normal(0, 0.05, (wl.B, wl.Hv, wl.dv, wl.dk)), dtype=np.float32)
+    dO = np.ascontiguousarray(r.standard_normal((wl.B, wl.T, wl.Hv, wl.dv)), dtype=np.float32)
+    dST = np.ascontiguousarray(r.standard_normal((wl.B, wl.Hv, wl.dv, wl.dk)), dtype=np.float32)
+    args = [to_torch(inp[n]) for n in ("q", "k", "v", "g", "beta")]
+    got = gdn.bwd(*args, to_torch(S0), to_torch(dO), to_torch(dST))
+    torch.cuda.synchronize()
+    got = {n: x.cpu().numpy() for n, x in got.items()}
+    del args
+    grp = wl.Hv // wl.Hk
+    x = {n: inp[n].f32() for n in ("q", "k", "v", "g", "beta")}
+    for b, kh in ((0, 0), (3, 15)):
+        hs = slice(kh * grp, (kh + 1) * grp)
+        bs = slice(b, b + 1)
+        ref = oracle.backward(x["q"][bs, :, kh:kh + 1], x["k"][bs, :, kh:kh + 1], x["v"][bs, :, hs],
+                              x["g"][bs, :, hs], x["beta"][bs, :, hs], S0[bs, hs].astype(np.float64), dO[bs, :, hs],
+                              dST[bs, hs])
+        mine = {"dq": got["dq"][bs, :, kh:kh + 1], "dk": got["dk"][bs, :, kh:kh + 1], "dv": got["dv"][bs, :, hs],
+                "dg": got["dg"][bs, :, hs], "dbeta": got["dbeta"][bs, :, hs], "dS0": got["dS0"][bs, hs]}
+        for n in ("dq", "dk", "dv", "dg", "dbeta", "dS0"):
+            assert np.all(np.isfinite(mine[n])), "non-finite %s" % n
+            e = rel_inf(mine[n], ref[n])
+            print("[parity] bwd 4x4096 batch %d key head %d %s rel %.3e (bar 1e-4)" % (b, kh, n, e),
+                  file=sys.stderr, flush=True)
+            assert e <= 1e-4, "batch %d key head %d: %s error %.3e" % (b, kh, n, e)
