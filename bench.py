@@ -442,13 +442,22 @@ def main():
     # prep C^2 dk (the lower halves of Q K^T and K K^T) + C^3 / 6 (T)
     units = B * Hv * ((T + C - 1) // C)
     bwd_flops = 2 * units * (8 * C * dv * dk + 5 * C * C * dv + 5 * C * C * dk + C ** 3 // 6)
+    # the same within a workspace of at most 1 GB (the sequence in segments, a
+    # forward pass more for the segment starts)
+    del bws
+    cap_bytes = L.gdn_bwd_workspace_bytes_within(ctypes.byref(pdesc_bwd), 10 ** 9)
+    bws = torch.empty(cap_bytes, dtype=torch.uint8, device=dev)
+    t_cap = time_events(backward, 2, stream, warm=0)
     extra["backward"] = {
         "workload": wl.name + ", backward (dq, dk, dv, dg, dbeta, dS0 fp32) from a random dO",
         "us_per_call": t_bwd * 1e6, "tokens_per_s": B * T / t_bwd,
         "tflops": bwd_flops / t_bwd / 1e12, "mfma_f32_frac": bwd_flops / t_bwd / 1e12 / PEAK_F32_TFLOPS,
-        "workspace_bytes": int(bws.numel())}
-    log("backward: %.2f ms, %.3e tokens/s, %.1f TFLOP/s = %.1f%% of the fp32 matrix cores" %
-        (t_bwd * 1e3, B * T / t_bwd, bwd_flops / t_bwd / 1e12, 100 * bwd_flops / t_bwd / 1e12 / PEAK_F32_TFLOPS))
+        "workspace_bytes": int(L.gdn_bwd_workspace_bytes(ctypes.byref(pdesc_bwd))),
+        "within_1gb": {"us_per_call": t_cap * 1e6, "workspace_bytes": int(cap_bytes)}}
+    log("backward: %.2f ms, %.3e tokens/s, %.1f TFLOP/s = %.1f%% of the fp32 matrix cores; "
+        "%.2f ms within a %.2f GB workspace" %
+        (t_bwd * 1e3, B * T / t_bwd, bwd_flops / t_bwd / 1e12, 100 * bwd_flops / t_bwd / 1e12 / PEAK_F32_TFLOPS,
+         t_cap * 1e3, cap_bytes / 1e9))
     del bws, grads, dO
 
     for key, xwl in (("long_prefill", LONG_PREFILL), ("key_gate_prefill", KDA_PREFILL)):

@@ -97,6 +97,8 @@ def lib() -> ctypes.CDLL:
         L.gdn_decode_step_conv.restype = I
         L.gdn_bwd_workspace_bytes.argtypes = [D]
         L.gdn_bwd_workspace_bytes.restype = S
+        L.gdn_bwd_workspace_bytes_within.argtypes = [D, S]
+        L.gdn_bwd_workspace_bytes_within.restype = S
         L.gdn_bwd.argtypes = [D] + [P] * 15 + [S, P]
         L.gdn_bwd.restype = I
         L.gdn_output_gate.argtypes = [D, P, I, P, P, ctypes.c_float, I, P, P]
@@ -476,9 +478,10 @@ def decode_step_conv(xq, xk, xv, conv_w, conv_st, g, beta, S, qkv_dtype=torch.fl
     return o
 
 
-def bwd(q, k, v, g, beta, S0, dO, dS_T=None, stream=None):
+def bwd(q, k, v, g, beta, S0, dO, dS_T=None, stream=None, workspace_cap=None):
     """Gradients of sum <dO, o> + <dS_T, S_T> with respect to q, k, v, g, beta,
-    S0 (fp32).  Shapes as for fwd_chunked; dO fp32 [B,T,Hv,dv]."""
+    S0 (fp32).  Shapes as for fwd_chunked; dO fp32 [B,T,Hv,dv].  With
+    workspace_cap (bytes), the workspace of the fastest plan within it."""
     B, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
     _dev("q", q)
@@ -495,7 +498,8 @@ def bwd(q, k, v, g, beta, S0, dO, dS_T=None, stream=None):
            "dS0": f((B, Hv, dv, dk))}
     d = make_desc(B, T, Hk, Hv, dk, dv, 64, _DTYPE_CODE[q.dtype], _DTYPE_CODE[g.dtype], gate)
     L = lib()
-    ws_bytes = L.gdn_bwd_workspace_bytes(ctypes.byref(d))
+    ws_bytes = L.gdn_bwd_workspace_bytes(ctypes.byref(d)) if workspace_cap is None else \
+        L.gdn_bwd_workspace_bytes_within(ctypes.byref(d), int(workspace_cap))
     ws = _workspace(ws_bytes, q.device)
     check(L.gdn_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(dO),
                     _ptr(dS_T), *(_ptr(out[n]) for n in ("dq", "dk", "dv", "dg", "dbeta", "dS0")), _ptr(ws),

@@ -450,8 +450,8 @@ inline size_t history_bytes(const Shape &sh) {
 
 }  // namespace
 
-size_t backward_workspace(const Shape &sh) {
-  if (!sh.key_gate) return chunk_backward_workspace(sh);
+size_t backward_workspace(const Shape &sh, size_t cap) {
+  if (!sh.key_gate) return chunk_backward_workspace(sh, cap);
   const size_t pw = 2 * (size_t)sh.dk + 1 + (sh.key_gate ? sh.dk : 1);
   const size_t part = (size_t)sh.B * sh.Hv * (sh.dv / kSlice) * sh.T * pw * 4;
   return ((history_bytes(sh) + 255) & ~(size_t)255) + part;
@@ -459,9 +459,10 @@ size_t backward_workspace(const Shape &sh) {
 
 hipError_t launch_backward(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
                            const void *beta, const float *S0, const float *dO, const float *dST, float *dq,
-                           float *dk, float *dv, float *dg, float *dbeta, float *dS0, void *ws, hipStream_t st) {
+                           float *dk, float *dv, float *dg, float *dbeta, float *dS0, void *ws, size_t ws_bytes,
+                           hipStream_t st) {
   if (!sh.key_gate)
-    return launch_chunk_backward(sh, q, k, v, g, beta, S0, dO, dST, dq, dk, dv, dg, dbeta, dS0, ws, st);
+    return launch_chunk_backward(sh, q, k, v, g, beta, S0, dO, dST, dq, dk, dv, dg, dbeta, dS0, ws, ws_bytes, st);
   BwdArgs a;
   a.q = q;
   a.k = k;

@@ -32,6 +32,8 @@
 // The two passes are independent of each other.  All arithmetic is fp32.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -43,15 +45,30 @@ constexpr int R = 32;       // state rows of a workgroup in the two passes
 constexpr int LC = C + 4;   // LDS row strides (4 mod 32 floats: conflict-free row and column reads)
 constexpr int LR = R + 4;
 
+// flags of a launch
+constexpr int kPrepT = 1, kPrepP = 2;   // prep: T, gamma, beta; P^T
+constexpr int kStatesOnly = 4;          // forward pass: only the states at segment starts
+
 struct CbArgs {
   const void *q, *k, *v, *g, *beta;
-  const float *S0, *dO, *dST;
+  const float *S0, *dO;
+  const float *dS_in;   // the state gradient after the last chunk of the launch's range (null: zeros)
   float *dq, *dk, *dv, *dg, *dbeta, *dS0;
-  // workspace, per (batch, value head, chunk): T [C][C], P^T [C][C], gamma [C], beta [C],
-  // state before the chunk [dv][dk], state gradient after it [dv][dk], U [C][dv], E [C][dv]
-  float *Tm, *Pt, *gam, *bet, *S0s, *dSC, *Um, *Em;
+  // workspace.  For every (batch, value head, chunk): T [C][C], gamma [C], beta [C].
+  // For the chunks of one segment (ncs of them per (batch, value head), from chunk
+  // sc0): P^T [C][C], the state before the chunk [dv][dk], the state gradient after
+  // it [dv][dk], U [C][dv], E [C][dv].  With several segments, the state before
+  // each segment's first chunk, [B Hv][nseg][dv][dk].
+  float *Tm, *gam, *bet, *Pt, *S0s, *dSC, *Um, *Em, *Sseg;
   int T, Hk, Hv, dv_dim, nc;
+  int c0, c1;         // the launch's chunks
+  int sc0, ncs, nseg;
+  int flags;
 };
+
+// index of (batch-head bh, chunk n) in the all-chunk arrays and in the segment arrays
+__device__ __forceinline__ size_t gch(const CbArgs &a, size_t bh, int n) { return bh * a.nc + n; }
+__device__ __forceinline__ size_t sch(const CbArgs &a, size_t bh, int n) { return bh * a.ncs + (n - a.sc0); }
 
 __device__ __forceinline__ float4v mma(float a, float b, float4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -138,10 +155,11 @@ __global__ __launch_bounds__(256) void cb_prep_kernel(CbArgs a) {
   float *smem = reinterpret_cast<float *>(smem4);
   float *sK = smem, *sA = sK + prep_region(DK), *sg = sA + C * LC, *sb = sg + C;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 15, g4 = lane >> 4;
-  const int n = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
+  const int n = a.c0 + blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
   const int T = a.T, Hk = a.Hk, Hv = a.Hv, grp = Hv / Hk;
   const int t0 = n * C, len = min(C, T - t0);
   const size_t row0 = (size_t)b * T + t0;
+  const bool doT = a.flags & kPrepT, doP = a.flags & kPrepP;
   load_rows<TQ, DK>(sK, (const TQ *)a.k, row0 * Hk + kh, Hk, len, tid);
   // the lane's q entries of token 16 w + ln as matrix-core operands (zeros past the end)
   float4v qa[DK / 16];
@@ -162,18 +180,18 @@ __global__ __launch_bounds__(256) void cb_prep_kernel(CbArgs a) {
 #pragma unroll
   for (int J = 0; J < 4; ++J) {
     kk[J] = qk[J] = float4v{0.f, 0.f, 0.f, 0.f};
-    if (J <= w) {
+    if (J <= w && doT)
       mm<DK>(kk[J], [&](int k) { return row4(sK + (16 * w + ln) * LK + k); },
              [&](int k) { return row4(sK + (16 * J + ln) * LK + k); }, g4);
+    if (J <= w && doP)
       mm<DK>(qk[J], [&](int k) { return qa[k >> 4]; }, [&](int k) { return row4(sK + (16 * J + ln) * LK + k); },
              g4);
-    }
   }
   // T over the k rows' space; a 16 x 16 staging tile per wave after it
   float *sT = sK, *sX = sK + C * LC + w * 16 * LX;
   for (int hh = 0; hh < grp; ++hh) {
     const int h = kh * grp + hh;
-    const size_t cn = ((size_t)b * Hv + h) * a.nc + n;
+    const size_t bh = (size_t)b * Hv + h, cn = gch(a, bh, n);
     __syncthreads();   // the k rows (first head) or the previous head's T are read
     if (w == 0) {
       const TG *g = (const TG *)a.g, *be = (const TG *)a.beta;
@@ -182,11 +200,13 @@ __global__ __launch_bounds__(256) void cb_prep_kernel(CbArgs a) {
       const float gm = wave_prefix_sum(gt);
       sg[lane] = gm;
       sb[lane] = bt;
-      a.gam[cn * C + lane] = gm;
-      a.bet[cn * C + lane] = bt;
+      if (doT) {
+        a.gam[cn * C + lane] = gm;
+        a.bet[cn * C + lane] = bt;
+      }
     }
     __syncthreads();
-    float *Ptg = a.Pt + cn * C * C;
+    float *Ptg = a.Pt + sch(a, bh, n) * C * C;
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
       const int j = 16 * J + ln;
@@ -198,8 +218,9 @@ __global__ __launch_bounds__(256) void cb_prep_kernel(CbArgs a) {
         sA[i * LC + j] = i > j ? sb[i] * m * kk[J][e] : 0.f;
         pt[e] = m * qk[J][e];
       }
-      *reinterpret_cast<float4v *>(Ptg + j * C + 16 * w + 4 * g4) = pt;   // P^T[j][i]
+      if (doP) *reinterpret_cast<float4v *>(Ptg + j * C + 16 * w + 4 * g4) = pt;   // P^T[j][i]
     }
+    if (!doT) continue;
     __syncthreads();
     {
       // diagonal block w: lane (c, q) = (lane / 4, lane % 4) holds T[b + 4 m + q][b + c]
@@ -372,7 +393,7 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_fwd_kernel(CbArgs a)
   float *sEg = sU + R * LC, *sEc = sEg + C, *sb = sEc + C;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 15, g4 = lane >> 4;
   const int sl = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int T = a.T, Hk = a.Hk, Hv = a.Hv, DV = a.dv_dim, nc = a.nc, kh = h / (Hv / Hk), r0 = sl * R;
+  const int T = a.T, Hk = a.Hk, Hv = a.Hv, DV = a.dv_dim, kh = h / (Hv / Hk), r0 = sl * R;
   const size_t bh = (size_t)b * Hv + h;
   const TQ *k = (const TQ *)a.k, *v = (const TQ *)a.v;
   int srt[NS], sct[NS], zrt[ZT], zcc[ZT];
@@ -380,19 +401,30 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_fwd_kernel(CbArgs a)
   for (int s = 0; s < NS; ++s) srt[s] = (w * NS + s) / NCT, sct[s] = (w * NS + s) % NCT;
 #pragma unroll
   for (int z = 0; z < ZT; ++z) zrt[z] = (w * ZT + z) / 4, zcc[z] = (w * ZT + z) % 4;
+  const bool so = a.flags & kStatesOnly;
+  // the state before the range: S0, or the kept state of the segment that starts it
+  const float *Sin = a.c0 == 0 ? a.S0 : a.Sseg + (bh * a.nseg + a.c0 / a.ncs) * DV * DK;
   float4v S[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      S[s][e] = a.S0 ? a.S0[(bh * DV + r0 + 16 * srt[s] + 4 * g4 + e) * DK + 16 * sct[s] + ln] : 0.f;
+      S[s][e] = Sin ? Sin[(r0 + 16 * srt[s] + 4 * g4 + e) * DK + 16 * sct[s] + ln + (a.c0 == 0 ? bh * DV * DK : 0)]
+                    : 0.f;
+  auto keep_state = [&](int sg) {   // the state before segment sg's first chunk
+    float *Sg = a.Sseg + (bh * a.nseg + sg) * DV * DK;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Sg[(r0 + 16 * srt[s] + 4 * g4 + e) * DK + 16 * sct[s] + ln] = S[s][e];
+  };
   RowsReg<TQ, DK, NT> kr;
   CcReg<NT> tr;
   GateReg gr;
   typename Quad<TQ>::type vq[ZT];
   auto fetch = [&](int n) {
     const int t0 = n * C, len = min(C, T - t0);
-    const size_t cn = bh * nc + n, row0 = (size_t)b * T + t0;
+    const size_t cn = gch(a, bh, n), row0 = (size_t)b * T + t0;
     kr.load(k + (row0 * Hk + kh) * DK, (size_t)Hk * DK, len, tid);
     tr.load(a.Tm + cn * C * C, tid);
     gr.load(a, cn, tid);
@@ -403,26 +435,26 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_fwd_kernel(CbArgs a)
                       : typename Quad<TQ>::type{};
     }
   };
-  fetch(0);
-  for (int n = 0; n < nc; ++n) {
-    const size_t cn = bh * nc + n;
+  fetch(a.c0);
+  for (int n = a.c0; n < a.c1; ++n) {
     kr.template store<LK>(sK, tid);
     tr.store(sT, tid);
     gr.store(sEg, sEc, sb, tid);
     float4v vx[ZT];
 #pragma unroll
     for (int z = 0; z < ZT; ++z) vx[z] = quad_to_f32<TQ>(vq[z]);
-    float *S0g = a.S0s + (cn * DV + r0) * DK;
+    if (so && n > 0 && n % a.ncs == 0) keep_state(n / a.ncs);
+    float *S0g = a.S0s + (sch(a, bh, n) * DV + r0) * DK;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * srt[s] + 4 * g4 + e, c = 16 * sct[s] + ln;
         sS[r * LS + c] = S[s][e];
-        S0g[r * DK + c] = S[s][e];
+        if (!so) S0g[r * DK + c] = S[s][e];
       }
     lds_barrier();
-    if (n + 1 < nc) fetch(n + 1);
+    if (n + 1 < a.c1) fetch(n + 1);
     // X^T[r][t] = beta_t (v_t[r] - e^gamma_t (S k_t)[r])
 #pragma unroll
     for (int z = 0; z < ZT; ++z) {
@@ -442,7 +474,7 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_fwd_kernel(CbArgs a)
       float4v u = {0.f, 0.f, 0.f, 0.f};
       mm<C>(u, [&](int kk) { return row4(sX + (16 * rt + ln) * LC + kk); },
             [&](int kk) { return row4(sT + i * LC + kk); }, g4);
-      *reinterpret_cast<float4v *>(a.Um + (cn * C + i) * DV + r0 + 16 * rt + 4 * g4) = u;
+      if (!so) *reinterpret_cast<float4v *>(a.Um + (sch(a, bh, n) * C + i) * DV + r0 + 16 * rt + 4 * g4) = u;
       const float ec = sEc[i];
 #pragma unroll
       for (int e = 0; e < 4; ++e) sU[(16 * rt + 4 * g4 + e) * LC + i] = u[e] * ec;
@@ -459,6 +491,7 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_fwd_kernel(CbArgs a)
     }
     lds_barrier();
   }
+  if (so) keep_state(a.c1 / a.ncs);
 }
 
 // backward pass, over the chunks in reverse: the state gradient after each
@@ -474,7 +507,7 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_bwd_kernel(CbArgs a)
   float *sEg = sE + R * LC, *sEc = sEg + C, *sb = sEc + C;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 15, g4 = lane >> 4;
   const int sl = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int T = a.T, Hk = a.Hk, Hv = a.Hv, DV = a.dv_dim, nc = a.nc, kh = h / (Hv / Hk), r0 = sl * R;
+  const int T = a.T, Hk = a.Hk, Hv = a.Hv, DV = a.dv_dim, kh = h / (Hv / Hk), r0 = sl * R;
   const size_t bh = (size_t)b * Hv + h;
   const TQ *k = (const TQ *)a.k, *q = (const TQ *)a.q;
   int srt[NS], sct[NS], zrt[ZT], zcc[ZT];
@@ -487,7 +520,7 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_bwd_kernel(CbArgs a)
   for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      dS[s][e] = a.dST ? a.dST[(bh * DV + r0 + 16 * srt[s] + 4 * g4 + e) * DK + 16 * sct[s] + ln] : 0.f;
+      dS[s][e] = a.dS_in ? a.dS_in[(bh * DV + r0 + 16 * srt[s] + 4 * g4 + e) * DK + 16 * sct[s] + ln] : 0.f;
   RowsReg<TQ, DK, NT> kr, qr;
   CcReg<NT> tr, pr;
   GateReg gr;
@@ -495,11 +528,11 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_bwd_kernel(CbArgs a)
   float4v orr[NO];
   auto fetch = [&](int n) {
     const int t0 = n * C, len = min(C, T - t0);
-    const size_t cn = bh * nc + n, row0 = (size_t)b * T + t0;
+    const size_t cn = gch(a, bh, n), row0 = (size_t)b * T + t0;
     kr.load(k + (row0 * Hk + kh) * DK, (size_t)Hk * DK, len, tid);
     qr.load(q + (row0 * Hk + kh) * DK, (size_t)Hk * DK, len, tid);
     tr.load(a.Tm + cn * C * C, tid);
-    pr.load(a.Pt + cn * C * C, tid);
+    pr.load(a.Pt + sch(a, bh, n) * C * C, tid);
     gr.load(a, cn, tid);
 #pragma unroll
     for (int i = 0; i < NO; ++i) {
@@ -508,10 +541,10 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_bwd_kernel(CbArgs a)
                        : float4v{0.f, 0.f, 0.f, 0.f};
     }
   };
-  fetch(nc - 1);
-  for (int n = nc - 1; n >= 0; --n) {
+  fetch(a.c1 - 1);
+  for (int n = a.c1 - 1; n >= a.c0; --n) {
     const int t0 = n * C, len = min(C, T - t0);
-    const size_t cn = bh * nc + n, row0 = (size_t)b * T + t0;
+    const size_t cn = sch(a, bh, n), row0 = (size_t)b * T + t0;
     kr.template store<LK>(sK, tid);
     qr.template store<LK>(sQ, tid);
     tr.store(sT, tid);
@@ -532,7 +565,7 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_bwd_kernel(CbArgs a)
         dSg[r * DK + c] = dS[s][e];
       }
     lds_barrier();
-    if (n > 0) fetch(n - 1);
+    if (n > a.c0) fetch(n - 1);
     // dU^T[r][i] = e^(gamma_C - gamma_i) (dS k_i)[r] + sum_j dO[j][r] P[j][i]
 #pragma unroll
     for (int z = 0; z < ZT; ++z) {
@@ -599,7 +632,7 @@ struct GradCfg {
   static constexpr int REGION = SLICE > MASKS ? SLICE : MASKS;
   static constexpr int NC4 = C * R / 4 / NT, NS4 = R * DK / 4 / NT;   // 16-byte units per thread
   static constexpr int NV = 8 * C / NT;                                 // (token, 4 rows) units of E . v
-  static constexpr int smem = (2 * C * LK + REGION + (4 + 3 * NH) * C + 4) * 4;
+  static constexpr int smem = (2 * C * LK + REGION + (4 + 3 * NH) * C + 2 * NW) * 4;
 };
 
 // acc1 += A1 B^T, acc2 += A2 B^T (one read of B)
@@ -631,8 +664,8 @@ __global__ __launch_bounds__((GradCfg<TQ, DK>::NT)) void cb_grads_kernel(CbArgs 
   float *sGam = sg + C, *sBet = sGam + NH * C, *sBx = sBet + NH * C, *sRed = sBx + NH * C;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 15, g4 = lane >> 4;
   const int tw = w & 3, hw = w >> 2, ct0 = hw * HCT, J0 = hw * HJ;
-  const int n = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
-  const int T = a.T, Hk = a.Hk, Hv = a.Hv, DV = a.dv_dim, nc = a.nc, grp = Hv / Hk;
+  const int n = a.c0 + blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
+  const int T = a.T, Hk = a.Hk, Hv = a.Hv, DV = a.dv_dim, grp = Hv / Hk;
   const int t0 = n * C, len = min(C, T - t0);
   const size_t row0 = (size_t)b * T + t0;
   const TQ *v = (const TQ *)a.v;
@@ -659,7 +692,7 @@ __global__ __launch_bounds__((GradCfg<TQ, DK>::NT)) void cb_grads_kernel(CbArgs 
   auto vtok = [&](int i) { return (tid + i * NT) >> 3; };
   const int vr = (tid & 7) * 4;
   auto fetch = [&](int h, int r0) {
-    const size_t cn = ((size_t)b * Hv + h) * nc + n;
+    const size_t cn = sch(a, (size_t)b * Hv + h, n);
     const float *pO = a.dO + (row0 * Hv + h) * DV + r0, *pU = a.Um + cn * C * DV + r0, *pE = a.Em + cn * C * DV + r0;
     const float *pS = a.S0s + (cn * DV + r0) * DK, *pD = a.dSC + (cn * DV + r0) * DK;
 #pragma unroll
@@ -701,7 +734,7 @@ __global__ __launch_bounds__((GradCfg<TQ, DK>::NT)) void cb_grads_kernel(CbArgs 
   fetch(kh * grp, 0);
   for (int hh = 0; hh < grp; ++hh) {
     const int h = kh * grp + hh;
-    const size_t cn = ((size_t)b * Hv + h) * nc + n;
+    const size_t cn = gch(a, (size_t)b * Hv + h, n);
     float4v dPa[HJ], dAa[HJ], Q1[HCT], ES[HCT], UD[HCT];
 #pragma unroll
     for (int J = 0; J < HJ; ++J) dPa[J] = dAa[J] = float4v{0.f, 0.f, 0.f, 0.f};
@@ -718,7 +751,6 @@ __global__ __launch_bounds__((GradCfg<TQ, DK>::NT)) void cb_grads_kernel(CbArgs 
       for (int i = 0; i < NV; ++i) vx[i] = quad_to_f32<TQ>(rv[i]);
       if (si == 0) {
         load_gates(sEg, sEc, sb, a, cn, tid, sg);
-        if (tid < 2) sRed[tid] = 0.f;
       }
       lds_barrier();
       // the next slice, or the next head's first
@@ -774,7 +806,7 @@ __global__ __launch_bounds__((GradCfg<TQ, DK>::NT)) void cb_grads_kernel(CbArgs 
       if ((tid & 7) == 0) sBx[vtok(i)] = x;
     }
     sdot = group_sum<64>(sdot);
-    if (lane == 0) atomicAdd(&sRed[1], sdot);
+    if (lane == 0) sRed[G::NW + w] = sdot;   // one slot per wave: a fixed order of the sum
     lds_barrier();
     float gp[4] = {0.f, 0.f, 0.f, 0.f}, bp[4] = {0.f, 0.f, 0.f, 0.f}, cp = 0.f;
 #pragma unroll
@@ -819,7 +851,7 @@ __global__ __launch_bounds__((GradCfg<TQ, DK>::NT)) void cb_grads_kernel(CbArgs 
       }
     }
     cp = group_sum<64>(cp);
-    if (lane == 0) atomicAdd(&sRed[0], cp);
+    if (lane == 0) sRed[w] = cp;
     lds_barrier();
     if (w == 0) {
       // dg_t = sum over the chunk's tokens i >= t of the gradient of gamma_i; the
@@ -828,7 +860,12 @@ __global__ __launch_bounds__((GradCfg<TQ, DK>::NT)) void cb_grads_kernel(CbArgs 
       float x = sGam[t], y = sBet[t] + sBx[t];
 #pragma unroll
       for (int u = 1; u < NH; ++u) x += sGam[u * C + t], y += sBet[u * C + t];
-      if (t == C - 1) x += __builtin_fmaf(sEg[C - 1], sRed[1], sRed[0]);
+      if (t == C - 1) {
+        float c4 = 0.f, sd = 0.f;
+#pragma unroll
+        for (int u = 0; u < G::NW; ++u) c4 += sRed[u], sd += sRed[G::NW + u];
+        x += __builtin_fmaf(sEg[C - 1], sd, c4);
+      }
       const float s = wave_prefix_sum(x);
       if (t < len) {
         a.dg[(row0 + t) * Hv + h] = s;
@@ -864,56 +901,126 @@ hipError_t set_smem(F *kern, int bytes) {
   return hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
+// The workspace of one call: how many segments, and where each array starts.
+// Floats per (batch, value head): T, gamma, beta for every chunk; P^T, S0,
+// dS_C, U, E for the chunks of one segment.  One segment is the fastest; with
+// more, a forward pass over the chunks before the last segment first keeps
+// the states at the segment starts, and each segment then runs its own
+// forward pass.
+
+struct CbPlan {
+  int nc, nseg, ncs;
+  size_t units, sunits;   // (batch, value head, chunk) for all chunks and for one segment
+  size_t f_T, f_g, f_b, f_Sseg, f_P, f_S0, f_dS, f_U, f_E, floats;
+  CbPlan(const Shape &sh, int want) {
+    nc = (sh.T + C - 1) / C;
+    ncs = (nc + want - 1) / want;
+    nseg = (nc + ncs - 1) / ncs;
+    const size_t bh = (size_t)sh.B * sh.Hv, st = (size_t)sh.dv * sh.dk, cv = (size_t)C * sh.dv;
+    units = bh * nc;
+    sunits = bh * ncs;
+    size_t o = 0;
+    f_T = o, o += units * C * C;
+    f_g = o, o += units * C;
+    f_b = o, o += units * C;
+    f_Sseg = o, o += nseg > 1 ? bh * nseg * st : 0;
+    f_P = o, o += sunits * C * C;
+    f_S0 = o, o += sunits * st;
+    f_dS = o, o += sunits * st;
+    f_U = o, o += sunits * cv;
+    f_E = o, o += sunits * cv;
+    floats = o;
+  }
+  size_t bytes() const { return floats * 4; }
+};
+
+// the plan with the fewest segments whose workspace fits in `bytes`, else the
+// plan with the smallest workspace (more segments keep more segment-start
+// states, so the smallest is not the one with the most segments)
+inline CbPlan plan_for(const Shape &sh, size_t bytes) {
+  const int nc = (sh.T + C - 1) / C;
+  CbPlan best(sh, 1);
+  for (int want = 1; want <= nc; ++want) {
+    CbPlan p(sh, want);
+    if (p.bytes() <= bytes) return p;
+    if (p.bytes() < best.bytes()) best = p;
+  }
+  return best;
+}
+
 template <typename TQ, typename TG, int DK>
-hipError_t launch_cb_t(const Shape &sh, const CbArgs &a, hipStream_t st) {
+hipError_t launch_cb_t(const Shape &sh, const CbPlan &pl, CbArgs a, const float *dST, hipStream_t st) {
   using Sm = CbSmem<TQ, DK>;
-  constexpr int NTP = PassCfg<TQ, DK>::NT;
+  constexpr int NTP = PassCfg<TQ, DK>::NT, NTG = GradCfg<TQ, DK>::NT;
   static_assert(Sm::bwd <= 160 * 1024 && Sm::grads <= 160 * 1024 && Sm::prep <= 160 * 1024, "LDS");
   hipError_t e;
   if ((e = set_smem(cb_prep_kernel<TQ, TG, DK>, Sm::prep)) != hipSuccess) return e;
   if ((e = set_smem(cb_fwd_kernel<TQ, DK>, Sm::fwd)) != hipSuccess) return e;
   if ((e = set_smem(cb_bwd_kernel<TQ, DK>, Sm::bwd)) != hipSuccess) return e;
   if ((e = set_smem(cb_grads_kernel<TQ, TG, DK>, Sm::grads)) != hipSuccess) return e;
-  hipLaunchKernelGGL((cb_prep_kernel<TQ, TG, DK>), dim3(a.nc, sh.Hk, sh.B), dim3(256), Sm::prep, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((cb_fwd_kernel<TQ, DK>), dim3(sh.dv / R, sh.Hv, sh.B), dim3(NTP), Sm::fwd, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((cb_bwd_kernel<TQ, DK>), dim3(sh.dv / R, sh.Hv, sh.B), dim3(NTP), Sm::bwd, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((cb_grads_kernel<TQ, TG, DK>), dim3(a.nc, sh.Hk, sh.B), dim3(GradCfg<TQ, DK>::NT), Sm::grads,
-                     st, a);
-  return hipGetLastError();
+  const dim3 pass(sh.dv / R, sh.Hv, sh.B);
+  auto prep = [&](int flags) {
+    a.flags = flags;
+    hipLaunchKernelGGL((cb_prep_kernel<TQ, TG, DK>), dim3(a.c1 - a.c0, sh.Hk, sh.B), dim3(256), Sm::prep, st, a);
+    return hipGetLastError();
+  };
+  auto fwd = [&](int flags) {
+    a.flags = flags;
+    hipLaunchKernelGGL((cb_fwd_kernel<TQ, DK>), pass, dim3(NTP), Sm::fwd, st, a);
+    return hipGetLastError();
+  };
+  auto segment = [&]() {   // the chunks [c0, c1) of one segment, from their P^T to their gradients
+    hipError_t r = fwd(0);
+    if (r != hipSuccess) return r;
+    hipLaunchKernelGGL((cb_bwd_kernel<TQ, DK>), pass, dim3(NTP), Sm::bwd, st, a);
+    if ((r = hipGetLastError()) != hipSuccess) return r;
+    hipLaunchKernelGGL((cb_grads_kernel<TQ, TG, DK>), dim3(a.c1 - a.c0, sh.Hk, sh.B), dim3(NTG), Sm::grads, st, a);
+    return hipGetLastError();
+  };
+  a.nseg = pl.nseg;
+  a.ncs = pl.ncs;
+  if (pl.nseg == 1) {
+    a.c0 = a.sc0 = 0, a.c1 = pl.nc;
+    a.dS_in = dST;
+    if ((e = prep(kPrepT | kPrepP)) != hipSuccess) return e;
+    return segment();
+  }
+  // T, gamma, beta of every chunk; the states at the segment starts; then the
+  // segments from the last, the state gradient carried in dS0
+  a.c0 = a.sc0 = 0, a.c1 = pl.nc;
+  if ((e = prep(kPrepT)) != hipSuccess) return e;
+  a.c1 = (pl.nseg - 1) * pl.ncs;
+  if ((e = fwd(kStatesOnly)) != hipSuccess) return e;
+  for (int sg = pl.nseg - 1; sg >= 0; --sg) {
+    a.c0 = a.sc0 = sg * pl.ncs;
+    a.c1 = std::min(pl.nc, a.c0 + pl.ncs);
+    a.dS_in = sg == pl.nseg - 1 ? dST : a.dS0;
+    if ((e = prep(kPrepP)) != hipSuccess) return e;
+    if ((e = segment()) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <typename TQ, typename TG>
-hipError_t launch_cb_d(const Shape &sh, const CbArgs &a, hipStream_t st) {
+hipError_t launch_cb_d(const Shape &sh, const CbPlan &pl, const CbArgs &a, const float *dST, hipStream_t st) {
   switch (sh.dk) {
-    case 32: return launch_cb_t<TQ, TG, 32>(sh, a, st);
-    case 64: return launch_cb_t<TQ, TG, 64>(sh, a, st);
-    case 128: return launch_cb_t<TQ, TG, 128>(sh, a, st);
+    case 32: return launch_cb_t<TQ, TG, 32>(sh, pl, a, dST, st);
+    case 64: return launch_cb_t<TQ, TG, 64>(sh, pl, a, dST, st);
+    case 128: return launch_cb_t<TQ, TG, 128>(sh, pl, a, dST, st);
   }
   return hipErrorInvalidValue;
 }
 
-// floats of each workspace array per (batch, value head, chunk)
-struct CbSizes {
-  size_t cc, c, st, cv;
-  explicit CbSizes(const Shape &sh) : cc((size_t)C * C), c(C), st((size_t)sh.dv * sh.dk), cv((size_t)C * sh.dv) {}
-  size_t per_chunk() const { return 2 * cc + 2 * c + 2 * st + 2 * cv; }
-};
-
 }  // namespace
 
-size_t chunk_backward_workspace(const Shape &sh) {
-  const size_t nc = (size_t)(sh.T + C - 1) / C;
-  return (size_t)sh.B * sh.Hv * nc * CbSizes(sh).per_chunk() * 4;
-}
+size_t chunk_backward_workspace(const Shape &sh, size_t cap) { return plan_for(sh, cap).bytes(); }
 
 hipError_t launch_chunk_backward(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
                                  const void *beta, const float *S0, const float *dO, const float *dST, float *dq,
                                  float *dk, float *dv, float *dg, float *dbeta, float *dS0, void *ws,
-                                 hipStream_t st) {
-  CbArgs a;
+                                 size_t ws_bytes, hipStream_t st) {
+  const CbPlan pl = plan_for(sh, ws_bytes);
+  CbArgs a = {};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -921,7 +1028,6 @@ hipError_t launch_chunk_backward(const Shape &sh, const void *q, const void *k, 
   a.beta = beta;
   a.S0 = S0;
   a.dO = dO;
-  a.dST = dST;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
@@ -932,30 +1038,25 @@ hipError_t launch_chunk_backward(const Shape &sh, const void *q, const void *k, 
   a.Hk = sh.Hk;
   a.Hv = sh.Hv;
   a.dv_dim = sh.dv;
-  a.nc = (sh.T + C - 1) / C;
-  const size_t units = (size_t)sh.B * sh.Hv * a.nc;
-  const CbSizes z(sh);
-  float *p = (float *)ws;
-  a.Tm = p;
-  p += units * z.cc;
-  a.Pt = p;
-  p += units * z.cc;
-  a.gam = p;
-  p += units * z.c;
-  a.bet = p;
-  p += units * z.c;
-  a.S0s = p;
-  p += units * z.st;
-  a.dSC = p;
-  p += units * z.st;
-  a.Um = p;
-  p += units * z.cv;
-  a.Em = p;
+  a.nc = pl.nc;
+  float *w = (float *)ws;
+  a.Tm = w + pl.f_T;
+  a.gam = w + pl.f_g;
+  a.bet = w + pl.f_b;
+  a.Sseg = w + pl.f_Sseg;
+  a.Pt = w + pl.f_P;
+  a.S0s = w + pl.f_S0;
+  a.dSC = w + pl.f_dS;
+  a.Um = w + pl.f_U;
+  a.Em = w + pl.f_E;
   if (sh.qkv == DType::F32)
-    return sh.gate_t == DType::F32 ? launch_cb_d<float, float>(sh, a, st) : launch_cb_d<float, bf16_t>(sh, a, st);
+    return sh.gate_t == DType::F32 ? launch_cb_d<float, float>(sh, pl, a, dST, st)
+                                   : launch_cb_d<float, bf16_t>(sh, pl, a, dST, st);
   if (sh.qkv == DType::BF16)
-    return sh.gate_t == DType::F32 ? launch_cb_d<bf16_t, float>(sh, a, st) : launch_cb_d<bf16_t, bf16_t>(sh, a, st);
-  return sh.gate_t == DType::F32 ? launch_cb_d<f16_t, float>(sh, a, st) : launch_cb_d<f16_t, bf16_t>(sh, a, st);
+    return sh.gate_t == DType::F32 ? launch_cb_d<bf16_t, float>(sh, pl, a, dST, st)
+                                   : launch_cb_d<bf16_t, bf16_t>(sh, pl, a, dST, st);
+  return sh.gate_t == DType::F32 ? launch_cb_d<f16_t, float>(sh, pl, a, dST, st)
+                                 : launch_cb_d<f16_t, bf16_t>(sh, pl, a, dST, st);
 }
 
 }  // namespace gdn

@@ -651,6 +651,14 @@ size_t gdn_bwd_workspace_bytes(const gdn_desc *d) {
   return st == GDN_OK ? gdn::backward_workspace(sh) : 0;
 }
 
+size_t gdn_bwd_workspace_bytes_within(const gdn_desc *d, size_t cap) {
+  gdn::Shape sh;
+  const std::string saved = g_last_error;
+  const gdn_status st = check_bwd(d, &sh);
+  g_last_error = saved;
+  return st == GDN_OK ? gdn::backward_workspace(sh, cap) : 0;
+}
+
 gdn_status gdn_bwd(const gdn_desc *d, const void *q, const void *k, const void *v, const void *g,
                    const void *beta, const float *S0, const float *dO, const float *dS_T, float *dq,
                    float *dk, float *dv, float *dg, float *dbeta, float *dS0, void *workspace,
@@ -663,9 +671,10 @@ gdn_status gdn_bwd(const gdn_desc *d, const void *q, const void *k, const void *
   if ((st = check_ptrs(names, ptrs, 13)) != GDN_OK) return st;
   if ((S0 && !aligned16(S0)) || (dS_T && !aligned16(dS_T)))
     return fail(GDN_E_ALIGN, "S0 and dS_T must be 16-byte aligned");
-  const size_t need = gdn::backward_workspace(sh);
+  // the fastest plan that fits in the workspace given; below the smallest plan it is too small
+  const size_t need = gdn::backward_workspace(sh, workspace_bytes);
   if (workspace_bytes < need)
-    return fail(GDN_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    return fail(GDN_E_WORKSPACE, "workspace needs at least %zu bytes, got %zu", need, workspace_bytes);
   const size_t bt = (size_t)d->B * d->T, qs = dsize(d->qkv_dtype), gs = dsize(d->gate_dtype);
   const size_t gdim = sh.key_gate ? d->dk : 1, sb = (size_t)d->B * d->Hv * d->dv * d->dk * 4;
   const Range ins[] = {range(q, bt * d->Hk * d->dk * qs), range(k, bt * d->Hk * d->dk * qs),
@@ -682,7 +691,7 @@ gdn_status gdn_bwd(const gdn_desc *d, const void *q, const void *k, const void *
       if (overlap(outs[i], outs[j])) return fail(GDN_E_ARG, "outputs and workspace must not overlap each other");
   }
   return launched(gdn::launch_backward(sh, q, k, v, g, beta, S0, dO, dS_T, dq, dk, dv, dg, dbeta, dS0, workspace,
-                                       (hipStream_t)stream),
+                                       workspace_bytes, (hipStream_t)stream),
                   "backward launch");
 }
 

@@ -351,6 +351,25 @@ def test_bwd_checks(L):
     # beta [64], the state before the chunk and the state gradient after it [dv][dk],
     # U and E [64][dv], all fp32
     assert need == 2 * 6 * 2 * (2 * 64 * 64 + 2 * 64 + 2 * 128 * 128 + 2 * 64 * 128) * 4
+    # at the prefill workload's size: one segment takes 2.8 GB; within 1 GB, four segments
+    # of 16 chunks: T, gamma, beta for all 64 chunks, the states at the 4 segment starts,
+    # P^T, S0, dS_C, U, E for one segment's 16 chunks (B 4, 48 value heads)
+    dbig = desc(B=4, T=4096, Hk=16, Hv=48)
+    per_chunk = 2 * 64 * 64 + 2 * 64 + 2 * 128 * 128 + 2 * 64 * 128
+    assert L.gdn_bwd_workspace_bytes(ctypes.byref(dbig)) == 4 * 48 * 64 * per_chunk * 4
+    assert L.gdn_bwd_workspace_bytes_within(ctypes.byref(dbig), 1 << 62) == 4 * 48 * 64 * per_chunk * 4
+    units, sunits = 4 * 48 * 64, 4 * 48 * 16
+    four = 4 * (units * (64 * 64 + 2 * 64) + 4 * 48 * 4 * 128 * 128
+                + sunits * (64 * 64 + 2 * 128 * 128 + 2 * 64 * 128))
+    assert four == 912261120
+    assert L.gdn_bwd_workspace_bytes_within(ctypes.byref(dbig), 10 ** 9) == four
+    # three segments (22, 22 and 20 chunks) need 1.145 GB
+    three = 4 * (units * (64 * 64 + 2 * 64) + 4 * 48 * 3 * 128 * 128
+                 + 4 * 48 * 22 * (64 * 64 + 2 * 128 * 128 + 2 * 64 * 128))
+    assert L.gdn_bwd_workspace_bytes_within(ctypes.byref(dbig), three) == three
+    # below the smallest plan (one chunk per segment) the call is refused
+    smallest = L.gdn_bwd_workspace_bytes_within(ctypes.byref(dbig), 0)
+    assert 0 < smallest < four
     # key-channel gate: the state before every 4th token (B Hv ceil(T / 4) dv dk fp32,
     # 256-byte rounded), then the partial sums per 32 state rows and token
     hist = 2 * 6 * 25 * 128 * 128 * 4
@@ -363,7 +382,8 @@ def test_bwd_checks(L):
     call = lambda dd, ptrs=p, nbytes=need: L.gdn_bwd(ctypes.byref(dd), *ptrs[:5], None, ptrs[6], None,
                                                      *ptrs[8:14], ptrs[14], nbytes, None)
     assert call(desc(gate_dtype=gdn.F16)) == 3
-    assert call(d, nbytes=need - 1) == 5
+    assert call(d, nbytes=L.gdn_bwd_workspace_bytes_within(ctypes.byref(d), 0) - 1) == 5
+    assert call(dkey, nbytes=L.gdn_bwd_workspace_bytes(ctypes.byref(dkey)) - 1) == 5
     bad = list(p)
     bad[8] = None
     assert call(d, bad) == 1                             # dq missing

@@ -5,6 +5,7 @@ Bar: the fp32-mode bar of the forward, max|x - x_ref| / max|x_ref| <= 1e-4 for
 every gradient: the backward computes in fp32 from the stored input values,
 as the forward's fp32 mode does.
 """
+import ctypes
 import sys
 
 import numpy as np
@@ -107,11 +108,39 @@ def test_bwd_full_heads_long():
             assert e <= 1e-4, "key head %d: %s error %.3e" % (kh, n, e)
 
 
+def test_bwd_segments_ragged():
+    """Per-head gate with a workspace too small for one segment: the sequence
+    runs in segments (here 1000 tokens, a ragged last chunk), which must give
+    the one-segment result bit for bit, and the oracle's gradients."""
+    wl = PREFILL_CONV.with_(B=2, T=1000, Hk=2, Hv=6, conv=False)
+    inp = make_prefill(wl)
+    r = np.random.default_rng(909)
+    S0 = np.ascontiguousarray(r.normal(0, 0.05, (wl.B, wl.Hv, wl.dv, wl.dk)), dtype=np.float32)
+    dO = np.ascontiguousarray(r.standard_normal((wl.B, wl.T, wl.Hv, wl.dv)), dtype=np.float32)
+    dST = np.ascontiguousarray(r.standard_normal((wl.B, wl.Hv, wl.dv, wl.dk)), dtype=np.float32)
+    args = [to_torch(inp[n]) for n in ("q", "k", "v", "g", "beta")] + [to_torch(S0), to_torch(dO), to_torch(dST)]
+    one = gdn.bwd(*args)
+    full = gdn.lib().gdn_bwd_workspace_bytes(ctypes.byref(gdn.make_desc(
+        wl.B, wl.T, wl.Hk, wl.Hv, wl.dk, wl.dv, 64, gdn.BF16, gdn.BF16, gdn.GATE_HEAD)))
+    for cap in (full // 2, full // 5, 0):
+        say("bwd segments: workspace cap %d of %d bytes" % (cap, full))
+        seg = gdn.bwd(*args, workspace_cap=cap)
+        torch.cuda.synchronize()
+        for n in one:
+            assert torch.equal(one[n], seg[n]), "cap %d: %s differs from one segment" % (cap, n)
+    ref = oracle.backward(*(inp[n].f32() for n in ("q", "k", "v", "g", "beta")), S0.astype(np.float64), dO, dST)
+    for n in ("dq", "dk", "dv", "dg", "dbeta", "dS0"):
+        e = rel_inf(seg[n].cpu().numpy(), ref[n])
+        print("[parity] bwd segments %s rel %.3e (bar 1e-4)" % (n, e), file=sys.stderr, flush=True)
+        assert e <= 1e-4, "%s error %.3e" % (n, e)
+
+
 def test_bwd_prefill_full_size_sampled():
     """The backward at the prefill workload's full size (B 4, T 4096, 16 key /
-    48 value heads, d 128, bf16 inputs), in the launch configuration the bench
-    times, every chain on the GPU; the oracle recomputes two sampled (batch,
-    key head) groups over the whole sequence, each with its three value heads."""
+    48 value heads, d 128, bf16 inputs), every chain on the GPU, in one segment
+    and within a 1 GB workspace (four segments): the two agree bit for bit,
+    and the oracle recomputes two sampled (batch, key head) groups over the
+    whole sequence, each with its three value heads."""
     wl = PREFILL_CONV.with_(conv=False)
     inp = make_prefill(wl)
     say("bwd full size: B=%d T=%d Hk=%d Hv=%d d=128 bf16" % (wl.B, wl.T, wl.Hk, wl.Hv))
@@ -121,7 +150,11 @@ def test_bwd_prefill_full_size_sampled():
     dST = np.ascontiguousarray(r.standard_normal((wl.B, wl.Hv, wl.dv, wl.dk)), dtype=np.float32)
     args = [to_torch(inp[n]) for n in ("q", "k", "v", "g", "beta")]
     got = gdn.bwd(*args, to_torch(S0), to_torch(dO), to_torch(dST))
+    capped = gdn.bwd(*args, to_torch(S0), to_torch(dO), to_torch(dST), workspace_cap=10 ** 9)
     torch.cuda.synchronize()
+    for n in got:
+        assert torch.equal(got[n], capped[n]), "%s: the 1 GB workspace differs from one segment" % n
+    del capped
     got = {n: x.cpu().numpy() for n, x in got.items()}
     del args
     grp = wl.Hv // wl.Hk
