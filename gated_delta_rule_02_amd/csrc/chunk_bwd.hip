@@ -33,6 +33,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "gdn_device.h"
 #include "gdn_launch.h"
@@ -635,6 +636,36 @@ struct GradCfg {
   static constexpr int smem = (2 * C * LK + REGION + (4 + 3 * NH) * C + 2 * NW) * 4;
 };
 
+// as mm, over the k blocks lo <= k / 16 < hi only (the rest of A or B is zero)
+template <int K, typename FA, typename FB>
+__device__ __forceinline__ void mmr(float4v &acc, const FA &fa, const FB &fb, int g4, int lo, int hi) {
+#pragma unroll
+  for (int k = 0; k < K; k += 16) {
+    if (k / 16 < lo || k / 16 >= hi) continue;
+    const float4v x = fa(k + 4 * g4), y = fb(k + 4 * g4);
+    acc = mma(x[0], y[0], acc);
+    acc = mma(x[1], y[1], acc);
+    acc = mma(x[2], y[2], acc);
+    acc = mma(x[3], y[3], acc);
+  }
+}
+
+// acc1 += A1 B^T, acc2 += A2 B^T (one read of B), over the k blocks lo <= k / 16 < hi
+template <int K, typename FA1, typename FA2, typename FB>
+__device__ __forceinline__ void mm2r(float4v &acc1, float4v &acc2, const FA1 &fa1, const FA2 &fa2, const FB &fb,
+                                     int g4, int lo, int hi) {
+#pragma unroll
+  for (int k = 0; k < K; k += 16) {
+    if (k / 16 < lo || k / 16 >= hi) continue;
+    const float4v x1 = fa1(k + 4 * g4), x2 = fa2(k + 4 * g4), y = fb(k + 4 * g4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc1 = mma(x1[e], y[e], acc1);
+      acc2 = mma(x2[e], y[e], acc2);
+    }
+  }
+}
+
 // acc1 += A1 B^T, acc2 += A2 B^T (one read of B)
 template <int K, typename FA1, typename FA2, typename FB>
 __device__ __forceinline__ void mm2(float4v &acc1, float4v &acc2, const FA1 &fa1, const FA2 &fa2, const FB &fb,
@@ -809,34 +840,47 @@ __global__ __launch_bounds__((GradCfg<TQ, DK>::NT)) void cb_grads_kernel(CbArgs 
     if (lane == 0) sRed[G::NW + w] = sdot;   // one slot per wave: a fixed order of the sum
     lds_barrier();
     float gp[4] = {0.f, 0.f, 0.f, 0.f}, bp[4] = {0.f, 0.f, 0.f, 0.f}, cp = 0.f;
+    // M o dP and B are zero above the diagonal (B on it too): token block TW's rows
+    // need the key blocks up to TW, its columns the token blocks from TW (the tiles
+    // above the diagonal are never read).  One copy of the products per TW, so
+    // that every range is fixed at compile time.
+    auto products = [&](auto TWc) {
+      constexpr int TW = decltype(TWc)::value;
 #pragma unroll
-    for (int ct = 0; ct < HCT; ++ct) {
-      const int c = 16 * (ct0 + ct) + ln;
-      float4v q2 = {0.f, 0.f, 0.f, 0.f}, k1 = q2, f1 = q2, f2 = q2;
-      mm2<C>(q2, f1, [&](int k) { return row4(sdP + (16 * tw + ln) * LC + k); },
-             [&](int k) { return row4(sB + (16 * tw + ln) * LC + k); },
-             [&](int k) { return col4(sK + k * LK + c, LK); }, g4);
-      mm<C>(k1, [&](int k) { return col4(sdP + k * LC + 16 * tw + ln, LC); },
-            [&](int k) { return col4(sQ + k * LK + c, LK); }, g4);
-      mm<C>(f2, [&](int k) { return col4(sB + k * LC + 16 * tw + ln, LC) * row4(sb + k); },
-            [&](int k) { return col4(sK + k * LK + c, LK); }, g4);
+      for (int ct = 0; ct < HCT; ++ct) {
+        const int c = 16 * (ct0 + ct) + ln;
+        float4v q2 = {0.f, 0.f, 0.f, 0.f}, k1 = q2, f1 = q2, f2 = q2;
+        mm2r<C>(q2, f1, [&](int k) { return row4(sdP + (16 * TW + ln) * LC + k); },
+                [&](int k) { return row4(sB + (16 * TW + ln) * LC + k); },
+                [&](int k) { return col4(sK + k * LK + c, LK); }, g4, 0, TW + 1);
+        mmr<C>(k1, [&](int k) { return col4(sdP + k * LC + 16 * TW + ln, LC); },
+               [&](int k) { return col4(sQ + k * LK + c, LK); }, g4, TW, 4);
+        mmr<C>(f2, [&](int k) { return col4(sB + k * LC + 16 * TW + ln, LC) * row4(sb + k); },
+               [&](int k) { return col4(sK + k * LK + c, LK); }, g4, TW, 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * tw + 4 * g4 + e;
-        const float eg = sEg[t], bt = sb[t];
-        const float dq = __builtin_fmaf(eg, Q1[ct][e], q2[e]);
-        const float f1m = __builtin_fmaf(-eg, ES[ct][e], f1[e]);   // (B k)_t - e^gamma_t (E S0)_t
-        const float d4 = sEc[t] * UD[ct][e];
-        const float g1 = k1[e] + d4 + f2[e];
-        dQa[ct][e] += dq;
-        dKa[ct][e] += __builtin_fmaf(bt, f1m, g1);
-        const float qv = sQ[t * LK + c], kv = sK[t * LK + c];
-        gp[e] += qv * dq - kv * g1 + kv * bt * f1m;
-        bp[e] += kv * f1m;
-        cp = __builtin_fmaf(kv, d4, cp);
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * TW + 4 * g4 + e;
+          const float eg = sEg[t], bt = sb[t];
+          const float dq = __builtin_fmaf(eg, Q1[ct][e], q2[e]);
+          const float f1m = __builtin_fmaf(-eg, ES[ct][e], f1[e]);   // (B k)_t - e^gamma_t (E S0)_t
+          const float d4 = sEc[t] * UD[ct][e];
+          const float g1 = k1[e] + d4 + f2[e];
+          dQa[ct][e] += dq;
+          dKa[ct][e] += __builtin_fmaf(bt, f1m, g1);
+          const float qv = sQ[t * LK + c], kv = sK[t * LK + c];
+          gp[e] += qv * dq - kv * g1 + kv * bt * f1m;
+          bp[e] += kv * f1m;
+          cp = __builtin_fmaf(kv, d4, cp);
+        }
+        // the next tile reads its operands again rather than keep them in registers
+        asm volatile("" ::: "memory");
       }
-      // the next tile reads its operands again rather than keep them in registers
-      asm volatile("" ::: "memory");
+    };
+    switch (tw) {
+      case 0: products(std::integral_constant<int, 0>{}); break;
+      case 1: products(std::integral_constant<int, 1>{}); break;
+      case 2: products(std::integral_constant<int, 2>{}); break;
+      default: products(std::integral_constant<int, 3>{}); break;
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
