@@ -287,6 +287,43 @@ struct PassCfg {
   static constexpr int NCT = DK / 16, NS = 2 * NCT / NW, ZT = 8 / NW;
 };
 
+// f(std::integral_constant<int, zc>) for a 16-token block zc in 0..3 known only
+// at run time: one copy of f per block, so that ranges depending on it are
+// fixed at compile time
+template <typename F>
+__device__ __forceinline__ void with_block(int zc, F &&f) {
+  switch (zc) {
+    case 0: f(std::integral_constant<int, 0>{}); break;
+    case 1: f(std::integral_constant<int, 1>{}); break;
+    case 2: f(std::integral_constant<int, 2>{}); break;
+    default: f(std::integral_constant<int, 3>{}); break;
+  }
+}
+
+// as mm, over the k blocks lo <= k / 16 < hi only (the rest of A or B is zero)
+template <int K, typename FA, typename FB>
+__device__ __forceinline__ void mmr(float4v &acc, const FA &fa, const FB &fb, int g4, int lo, int hi) {
+#pragma unroll
+  for (int k = 0; k < K; k += 16) {
+    if (k / 16 < lo || k / 16 >= hi) continue;
+    const float4v x = fa(k + 4 * g4), y = fb(k + 4 * g4);
+    acc = mma(x[0], y[0], acc);
+    acc = mma(x[1], y[1], acc);
+    acc = mma(x[2], y[2], acc);
+    acc = mma(x[3], y[3], acc);
+  }
+}
+
+// the column block of [32][C] tile z of wave w (row block (w ZT + z) / 4): blocks
+// zc and 3 - zc go to waves that share a SIMD (eight waves) or to one wave (four),
+// so products over the triangular T and P^T weigh the same on every SIMD
+template <int NW, int ZT>
+__device__ __forceinline__ int pass_block(int w, int z) {
+  const int id = w * ZT + z, rt = id / 4, p = id % 4;
+  if constexpr (NW == 8) return rt == 0 ? p : 3 - p;
+  else return p == 0 ? 0 : p == 1 ? 3 : p == 2 ? 1 : 2;
+}
+
 // C rows of DK elements of q or k (zeros past the sequence's end), raw, in
 // 16-byte units spread over the NT threads.
 template <typename TQ, int DK, int NT>
@@ -401,7 +438,7 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_fwd_kernel(CbArgs a)
 #pragma unroll
   for (int s = 0; s < NS; ++s) srt[s] = (w * NS + s) / NCT, sct[s] = (w * NS + s) % NCT;
 #pragma unroll
-  for (int z = 0; z < ZT; ++z) zrt[z] = (w * ZT + z) / 4, zcc[z] = (w * ZT + z) % 4;
+  for (int z = 0; z < ZT; ++z) zrt[z] = (w * ZT + z) / 4, zcc[z] = pass_block<P::NW, ZT>(w, z);
   const bool so = a.flags & kStatesOnly;
   // the state before the range: S0, or the kept state of the segment that starts it
   const float *Sin = a.c0 == 0 ? a.S0 : a.Sseg + (bh * a.nseg + a.c0 / a.ncs) * DV * DK;
@@ -473,8 +510,11 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_fwd_kernel(CbArgs a)
     for (int z = 0; z < ZT; ++z) {
       const int rt = zrt[z], i = 16 * zcc[z] + ln;
       float4v u = {0.f, 0.f, 0.f, 0.f};
-      mm<C>(u, [&](int kk) { return row4(sX + (16 * rt + ln) * LC + kk); },
-            [&](int kk) { return row4(sT + i * LC + kk); }, g4);
+      // T[i][j] is zero for j > i: key blocks up to i's
+      with_block(zcc[z], [&](auto ZC) {
+        mmr<C>(u, [&](int kk) { return row4(sX + (16 * rt + ln) * LC + kk); },
+               [&](int kk) { return row4(sT + i * LC + kk); }, g4, 0, decltype(ZC)::value + 1);
+      });
       if (!so) *reinterpret_cast<float4v *>(a.Um + (sch(a, bh, n) * C + i) * DV + r0 + 16 * rt + 4 * g4) = u;
       const float ec = sEc[i];
 #pragma unroll
@@ -515,7 +555,7 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_bwd_kernel(CbArgs a)
 #pragma unroll
   for (int s = 0; s < NS; ++s) srt[s] = (w * NS + s) / NCT, sct[s] = (w * NS + s) % NCT;
 #pragma unroll
-  for (int z = 0; z < ZT; ++z) zrt[z] = (w * ZT + z) / 4, zcc[z] = (w * ZT + z) % 4;
+  for (int z = 0; z < ZT; ++z) zrt[z] = (w * ZT + z) / 4, zcc[z] = pass_block<P::NW, ZT>(w, z);
   float4v dS[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s)
@@ -575,8 +615,11 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_bwd_kernel(CbArgs a)
       mm<DK>(acc, [&](int kk) { return row4(sS + (16 * rt + ln) * LS + kk); },
              [&](int kk) { return rowq(sK + i * LK + kk); }, g4);
       acc *= sEc[i];
-      mm<C>(acc, [&](int kk) { return col4(sO + kk * LR + 16 * rt + ln, LR); },
-            [&](int kk) { return row4(sP + i * LC + kk); }, g4);
+      // P[j][i] is zero for j < i: token blocks from i's
+      with_block(zcc[z], [&](auto ZC) {
+        mmr<C>(acc, [&](int kk) { return col4(sO + kk * LR + 16 * rt + ln, LR); },
+               [&](int kk) { return row4(sP + i * LC + kk); }, g4, decltype(ZC)::value, 4);
+      });
 #pragma unroll
       for (int e = 0; e < 4; ++e) sD[(16 * rt + 4 * g4 + e) * LC + i] = acc[e];
     }
@@ -586,8 +629,11 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_bwd_kernel(CbArgs a)
     for (int z = 0; z < ZT; ++z) {
       const int rt = zrt[z], i = 16 * zcc[z] + ln;
       float4v E = {0.f, 0.f, 0.f, 0.f};
-      mm<C>(E, [&](int kk) { return row4(sD + (16 * rt + ln) * LC + kk); },
-            [&](int kk) { return col4(sT + kk * LC + i, LC); }, g4);
+      // T[j][i] is zero for j < i: token blocks from i's
+      with_block(zcc[z], [&](auto ZC) {
+        mmr<C>(E, [&](int kk) { return row4(sD + (16 * rt + ln) * LC + kk); },
+               [&](int kk) { return col4(sT + kk * LC + i, LC); }, g4, decltype(ZC)::value, 4);
+      });
       const float bi = sb[i];
       if (i < len)
         *reinterpret_cast<float4v *>(a.dv + ((row0 + i) * Hv + h) * DV + r0 + 16 * rt + 4 * g4) = E * bi;
@@ -635,20 +681,6 @@ struct GradCfg {
   static constexpr int NV = 8 * C / NT;                                 // (token, 4 rows) units of E . v
   static constexpr int smem = (2 * C * LK + REGION + (4 + 3 * NH) * C + 2 * NW) * 4;
 };
-
-// as mm, over the k blocks lo <= k / 16 < hi only (the rest of A or B is zero)
-template <int K, typename FA, typename FB>
-__device__ __forceinline__ void mmr(float4v &acc, const FA &fa, const FB &fb, int g4, int lo, int hi) {
-#pragma unroll
-  for (int k = 0; k < K; k += 16) {
-    if (k / 16 < lo || k / 16 >= hi) continue;
-    const float4v x = fa(k + 4 * g4), y = fb(k + 4 * g4);
-    acc = mma(x[0], y[0], acc);
-    acc = mma(x[1], y[1], acc);
-    acc = mma(x[2], y[2], acc);
-    acc = mma(x[3], y[3], acc);
-  }
-}
 
 // acc1 += A1 B^T, acc2 += A2 B^T (one read of B), over the k blocks lo <= k / 16 < hi
 template <int K, typename FA1, typename FA2, typename FB>
