@@ -17,8 +17,9 @@
 //   dk = (M o dP)^T Q + Kt-weighted U dS_C - beta Gam E S0 + beta (B K) + (beta B)^T K,  B = M o dA,
 //   dbeta = rows of E . (V - Gam K S0^T) + rows of K . (B K),
 // and the gradient of each gamma_i collects the same products as row dots
-// with q_i and k_i (plus <dS_C, S_C> at the chunk's last token); dg is its
-// sum over the chunk's later tokens.
+// with q_i and k_i (plus <dS_C, S_C> at the chunk's last token); dg_t is the
+// sum of those over the chunk's tokens i >= t.  The gate is taken to decay
+// (g <= 0), so every factor e^(gamma_i - gamma_j) with i >= j is at most 1.
 //
 // Four launches, the three passes after the first working from its output:
 //  - prep, per (chunk, key head) over the key head's value heads: gamma,
@@ -30,6 +31,12 @@
 //  - gradients, per (chunk, key head) over the key head's value heads: dq,
 //    dk (summed over the value heads), dg, dbeta.
 // The two passes are independent of each other.  All arithmetic is fp32.
+// With a workspace too small for every chunk's arrays, the sequence runs in
+// segments of consecutive chunks, last first: T, gamma, beta are made for
+// all chunks, a forward pass keeps only the states at the segment starts,
+// and each segment then runs P^T, its forward pass, its backward pass (the
+// state gradient carried in dS0) and its gradients; the results are the same
+// bits as with one segment.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
