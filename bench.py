@@ -485,6 +485,25 @@ def main():
                       "hbm_gbs_algorithmic": xbytes / tx / 1e9,
                       "hbm_frac_algorithmic": xbytes / tx / 1e9 / PEAK_HBM_GBS}
         log("%s: %.1f us, %.3e tokens/s, %.1f TFLOP/s" % (key, tx * 1e6, ntok / tx, xfl / tx / 1e12))
+        if xwl.gate == "key":
+            # the backward of the key-gate prefill (token by token over the state
+            # kept before every 4th token)
+            xdO = torch.randn((xwl.B, xwl.T, xwl.Hv, xwl.dv), device=dev)
+            xgr = [torch.empty(x.shape, dtype=torch.float32, device=dev) for x in
+                   (xi["q"], xi["k"], xi["v"], xi["g"], xi["beta"])] + [torch.empty_like(xst)]
+            del xws
+            xws = torch.empty(L.gdn_bwd_workspace_bytes(ctypes.byref(xd)), dtype=torch.uint8, device=dev)
+
+            def xback(xi=xi, xd=xd, xws=xws, xgr=xgr, xdO=xdO):
+                gdn.check(L.gdn_bwd(ctypes.byref(xd), P(xi["q"]), P(xi["k"]), P(xi["v"]), P(xi["g"]),
+                                    P(xi["beta"]), None if xi["S0"] is None else P(xi["S0"]), P(xdO), None,
+                                    *(P(x) for x in xgr), P(xws), xws.numel(), s_ptr))
+
+            tb = time_events(xback, 2, stream, warm=0)
+            extra[key]["backward_us_per_call"] = tb * 1e6
+            extra[key]["backward_workspace_bytes"] = int(xws.numel())
+            log("%s backward: %.2f ms (token by token, workspace %.2f GB)" % (key, tb * 1e3, xws.numel() / 1e9))
+            del xdO, xgr
         del xi, xo, xst, xws
 
     # ------------------------------------------------------------------ CPU baseline (oracle)

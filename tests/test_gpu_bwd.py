@@ -173,3 +173,10 @@ def test_bwd_prefill_full_size_sampled():
             print("[parity] bwd 4x4096 batch %d key head %d %s rel %.3e (bar 1e-4)" % (b, kh, n, e),
                   file=sys.stderr, flush=True)
             assert e <= 1e-4, "batch %d key head %d: %s error %.3e" % (b, kh, n, e)
+
+
+@pytest.mark.parametrize("T", [1, 64, 65])
+def test_bwd_chunk_edges(T):
+    """One token, exactly one chunk, one chunk and a token: the chunked
+    backward's padding and its single-chunk case, one key and one value head."""
+    run_case(PREFILL_CONV.with_(B=2, T=T, Hk=1, Hv=1, conv=False), "bwd T=%d" % T, seed=T)
