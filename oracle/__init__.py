@@ -200,12 +200,14 @@ def output_gate(o, z, gain, eps):
     return y
 
 
-def backward(q, k, v, g, beta, S0, dO, dST=None):
+def backward(q, k, v, g, beta, S0, dO, dST=None, delta=True):
     """Gradients of L = sum <dO, o> + <dST, S_T> with respect to q, k, v, g,
     beta and S0 (fp64, reverse mode over the stored state history).
 
     Shapes as for recurrent(); dO [B,T,Hv,dv]; dST [B,Hv,dv,dk] or None; S0
-    [B,Hv,dv,dk] or None.  Returns a dict dq, dk, dv, dg, dbeta, dS0 (float64).
+    [B,Hv,dv,dk] or None; delta=False: the update without the delta
+    correction, as for recurrent().  Returns a dict dq, dk, dv, dg, dbeta, dS0
+    (float64).
     """
     lib = _load()
     q, k, v, g, beta = (_f32(a) for a in (q, k, v, g, beta))
@@ -218,7 +220,8 @@ def backward(q, k, v, g, beta, S0, dO, dST=None):
         raise ValueError("dO must be [B,T,Hv,dv]")
     out = {"dq": np.empty(q.shape), "dk": np.empty(k.shape), "dv": np.empty(v.shape),
            "dg": np.empty(g.shape), "dbeta": np.empty(beta.shape), "dS0": np.empty((B, Hv, dv, dk))}
-    rc = lib.gdnref_backward(B, T, Hk, Hv, dk, dv, per_channel, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+    rc = lib.gdnref_backward(B, T, Hk, Hv, dk, dv, per_channel | (0 if delta else 2), _ptr(q), _ptr(k), _ptr(v),
+                             _ptr(g), _ptr(beta),
                              _ptr(S0), _ptr(dO), _ptr(dST), *(_ptr(out[n]) for n in
                                                              ("dq", "dk", "dv", "dg", "dbeta", "dS0")))
     if rc != 0:

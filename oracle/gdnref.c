@@ -278,16 +278,20 @@ int gdnref_output_gate(long rows, int d, const double *o, const float *z,
  *   dg_t = <dD, D>  (per-key-channel gate: column sums of dD o D)
  *   G <- alpha dD  (per-key-channel gate: dD diag(alpha)), the gradient for S_{t-1}
  * and dS0 = G after token 0.  dq and dk of a key head add up over its value
- * heads.  Inputs as for gdnref_recurrent (S0 double or NULL); dO [B,T,Hv,dv],
+ * heads.  Without the delta correction (bit 1 of gate_flags, as for
+ * gdnref_recurrent) a = 0: u = beta v, so the terms in beta du drop out of dk
+ * and dD, and dbeta_t = du . v.
+ * Inputs as for gdnref_recurrent (S0 double or NULL); dO [B,T,Hv,dv],
  * dST [B,Hv,dv,dk] or NULL; outputs double: dq, dk [B,T,Hk,dk], dv
  * [B,T,Hv,dv], dg like g, dbeta [B,T,Hv], dS0 [B,Hv,dv,dk].
  */
-int gdnref_backward(int B, int T, int Hk, int Hv, int dk, int dv, int per_channel_gate,
+int gdnref_backward(int B, int T, int Hk, int Hv, int dk, int dv, int gate_flags,
                     const float *q, const float *k, const float *v, const float *g,
                     const float *beta, const double *S0, const double *dO, const double *dST,
                     double *dq, double *dkk, double *dvv, double *dg, double *dbeta,
                     double *dS0) {
   int b, h, t, i, j;
+  const int per_channel_gate = gate_flags & 1, no_delta = (gate_flags >> 1) & 1;
   if (B <= 0 || T < 0 || Hk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || Hv % Hk != 0) return -1;
   if (!q || !k || !v || !g || !beta || !dO || !dq || !dkk || !dvv || !dg || !dbeta || !dS0) return -1;
   const size_t ss = (size_t)dv * dk;
@@ -322,7 +326,8 @@ int gdnref_backward(int B, int T, int Hk, int Hv, int dk, int dv, int per_channe
           al[j] = exp((double)(per_channel_gate ? g[(bt * Hv + h) * dk + j] : g[bt * Hv + h]));
         for (i = 0; i < dv; ++i) {
           double p = 0.0;
-          for (j = 0; j < dk; ++j) p += P[(size_t)i * dk + j] * al[j] * (double)kt[j];
+          if (!no_delta)
+            for (j = 0; j < dk; ++j) p += P[(size_t)i * dk + j] * al[j] * (double)kt[j];
           const double uu = bet * ((double)vt[i] - p);
           for (j = 0; j < dk; ++j) N[(size_t)i * dk + j] = P[(size_t)i * dk + j] * al[j] + uu * (double)kt[j];
         }
@@ -346,8 +351,8 @@ int gdnref_backward(int B, int T, int Hk, int Hv, int dk, int dv, int per_channe
             D[(size_t)i * dk + j] = P[(size_t)i * dk + j] * al[j];
             p += D[(size_t)i * dk + j] * (double)kt[j];
           }
-          a[i] = p;
-          u[i] = bet * ((double)vt[i] - p);
+          a[i] = no_delta ? 0.0 : p;
+          u[i] = bet * ((double)vt[i] - a[i]);
           for (j = 0; j < dk; ++j) St[(size_t)i * dk + j] = D[(size_t)i * dk + j] + u[i] * (double)kt[j];
         }
         /* o_t = S_t q */
@@ -371,7 +376,8 @@ int gdnref_backward(int B, int T, int Hk, int Hv, int dk, int dv, int per_channe
         dbeta[bt * Hv + h] = db;
         for (j = 0; j < dk; ++j) {
           double s = 0.0;
-          for (i = 0; i < dv; ++i) s += G[(size_t)i * dk + j] * u[i] - bet * du[i] * D[(size_t)i * dk + j];
+          for (i = 0; i < dv; ++i)
+            s += G[(size_t)i * dk + j] * u[i] - (no_delta ? 0.0 : bet * du[i] * D[(size_t)i * dk + j]);
           dkt[j] += s;
         }
         /* dD, the decay's gradient, then the gradient for S_{t-1} */
@@ -379,7 +385,7 @@ int gdnref_backward(int B, int T, int Hk, int Hv, int dk, int dv, int per_channe
         for (j = 0; j < dk; ++j) {
           double colsum = 0.0;
           for (i = 0; i < dv; ++i) {
-            const double dd = G[(size_t)i * dk + j] - bet * du[i] * (double)kt[j];
+            const double dd = G[(size_t)i * dk + j] - (no_delta ? 0.0 : bet * du[i] * (double)kt[j]);
             colsum += dd * D[(size_t)i * dk + j];
             G[(size_t)i * dk + j] = dd * al[j];
           }

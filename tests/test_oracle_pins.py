@@ -379,19 +379,20 @@ def test_output_gate_rejects_bad_shapes():
 # --------------------------------------------------------------------------
 # Backward: central finite differences of the forward oracle, every input
 # --------------------------------------------------------------------------
-def _loss(q, k, v, g, beta, S0, dO, dST):
-    o, ST = oracle.recurrent_full(q, k, v, g, beta, S0)
+def _loss(q, k, v, g, beta, S0, dO, dST, delta=True):
+    o, ST = oracle.recurrent_full(q, k, v, g, beta, S0, delta=delta)
     return float(np.sum(o * dO) + np.sum(ST * dST))
 
 
-@pytest.mark.parametrize("gate", ["head", "key"])
-def test_backward_matches_finite_differences(gate):
-    # grouped heads (2 value heads per key head), S0 given, dS_T given
+@pytest.mark.parametrize("gate,delta", [("head", True), ("key", True), ("head", False), ("key", False)])
+def test_backward_matches_finite_differences(gate, delta):
+    # grouped heads (2 value heads per key head), S0 given, dS_T given; with and
+    # without the delta correction (the forward oracle of each is pinned above)
     q, k, v, g, beta, S0 = rand_problem(31, B=1, T=5, Hk=1, Hv=2, dk=3, dv=2, gate=gate)
     r = np.random.default_rng(32)
     dO = r.standard_normal(v.shape)
     dST = r.standard_normal(S0.shape)
-    grads = oracle.backward(q, k, v, g, beta, S0, dO, dST)
+    grads = oracle.backward(q, k, v, g, beta, S0, dO, dST, delta=delta)
     inputs = {"q": q, "k": k, "v": v, "g": g, "beta": beta, "S0": S0}
     for name, x in inputs.items():
         fd = np.zeros(x.shape)
@@ -405,9 +406,9 @@ def test_backward_matches_finite_differences(gate):
                 xm[idx] = np.float32(x[idx] - 1e-3)
             args = dict(inputs)
             args[name] = xp
-            lp = _loss(args["q"], args["k"], args["v"], args["g"], args["beta"], args["S0"], dO, dST)
+            lp = _loss(args["q"], args["k"], args["v"], args["g"], args["beta"], args["S0"], dO, dST, delta)
             args[name] = xm
-            lm = _loss(args["q"], args["k"], args["v"], args["g"], args["beta"], args["S0"], dO, dST)
+            lm = _loss(args["q"], args["k"], args["v"], args["g"], args["beta"], args["S0"], dO, dST, delta)
             fd[idx] = (lp - lm) / (xp[idx] - xm[idx])
         np.testing.assert_allclose(grads["d" + name], fd, rtol=2e-5, atol=2e-6, err_msg=name)
 
