@@ -478,10 +478,11 @@ def decode_step_conv(xq, xk, xv, conv_w, conv_st, g, beta, S, qkv_dtype=torch.fl
     return o
 
 
-def bwd(q, k, v, g, beta, S0, dO, dS_T=None, stream=None, workspace_cap=None):
+def bwd(q, k, v, g, beta, S0, dO, dS_T=None, stream=None, workspace_cap=None, delta=True):
     """Gradients of sum <dO, o> + <dS_T, S_T> with respect to q, k, v, g, beta,
     S0 (fp32).  Shapes as for fwd_chunked; dO fp32 [B,T,Hv,dv].  With
-    workspace_cap (bytes), the workspace of the fastest plan within it."""
+    workspace_cap (bytes), the workspace of the fastest plan within it;
+    delta=False: the update without the delta correction (per-head gate)."""
     B, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
     _dev("q", q)
@@ -496,7 +497,8 @@ def bwd(q, k, v, g, beta, S0, dO, dS_T=None, stream=None, workspace_cap=None):
     f = lambda shape: torch.empty(shape, dtype=torch.float32, device=q.device)
     out = {"dq": f(q.shape), "dk": f(q.shape), "dv": f(v.shape), "dg": f(g.shape), "dbeta": f(beta.shape),
            "dS0": f((B, Hv, dv, dk))}
-    d = make_desc(B, T, Hk, Hv, dk, dv, 64, _DTYPE_CODE[q.dtype], _DTYPE_CODE[g.dtype], gate)
+    d = make_desc(B, T, Hk, Hv, dk, dv, 64, _DTYPE_CODE[q.dtype], _DTYPE_CODE[g.dtype], gate,
+                  RULE_DELTA if delta else RULE_NO_DELTA)
     L = lib()
     ws_bytes = L.gdn_bwd_workspace_bytes(ctypes.byref(d)) if workspace_cap is None else \
         L.gdn_bwd_workspace_bytes_within(ctypes.byref(d), int(workspace_cap))

@@ -72,6 +72,7 @@ struct CbArgs {
   int c0, c1;         // the launch's chunks
   int sc0, ncs, nseg;
   int flags;
+  int nd;             // the update without the delta correction: A = 0 (T = I), X = beta V
 };
 
 // index of (batch-head bh, chunk n) in the all-chunk arrays and in the segment arrays
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(256) void cb_prep_kernel(CbArgs a) {
 #pragma unroll
   for (int J = 0; J < 4; ++J) {
     kk[J] = qk[J] = float4v{0.f, 0.f, 0.f, 0.f};
-    if (J <= w && doT)
+    if (J <= w && doT && !a.nd)   // without the delta correction A = 0, so T = I
       mm<DK>(kk[J], [&](int k) { return row4(sK + (16 * w + ln) * LK + k); },
              [&](int k) { return row4(sK + (16 * J + ln) * LK + k); }, g4);
     if (J <= w && doP)
@@ -505,8 +506,9 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_fwd_kernel(CbArgs a)
     for (int z = 0; z < ZT; ++z) {
       const int rt = zrt[z], t = 16 * zcc[z] + ln;
       float4v acc = {0.f, 0.f, 0.f, 0.f};
-      mm<DK>(acc, [&](int kk) { return row4(sS + (16 * rt + ln) * LS + kk); },
-             [&](int kk) { return rowq(sK + t * LK + kk); }, g4);
+      if (!a.nd)
+        mm<DK>(acc, [&](int kk) { return row4(sS + (16 * rt + ln) * LS + kk); },
+               [&](int kk) { return rowq(sK + t * LK + kk); }, g4);
       const float eg = sEg[t], bt = sb[t];
 #pragma unroll
       for (int e = 0; e < 4; ++e) sX[(16 * rt + 4 * g4 + e) * LC + t] = bt * (vx[z][e] - eg * acc[e]);
@@ -658,8 +660,9 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_bwd_kernel(CbArgs a)
       dS[s] *= eC;
       mm<C>(dS[s], [&](int kk) { return col4(sO + kk * LR + 16 * rt + ln, LR) * row4(sEg + kk); },
             [&](int kk) { return colq(sQ + kk * LK + c, LK); }, g4);
-      mm<C>(dS[s], [&](int kk) { return row4(sE + (16 * rt + ln) * LC + kk); },
-            [&](int kk) { return colq(sK + kk * LK + c, LK); }, g4);
+      if (!a.nd)   // X = beta V does not depend on the state without the delta correction
+        mm<C>(dS[s], [&](int kk) { return row4(sE + (16 * rt + ln) * LC + kk); },
+              [&](int kk) { return colq(sK + kk * LK + c, LK); }, g4);
     }
     lds_barrier();
   }
@@ -720,7 +723,7 @@ __device__ __forceinline__ void mm2(float4v &acc1, float4v &acc2, const FA1 &fa1
   }
 }
 
-template <typename TQ, typename TG, int DK>
+template <typename TQ, typename TG, int DK, bool ND>
 __global__ __launch_bounds__((GradCfg<TQ, DK>::NT)) void cb_grads_kernel(CbArgs a) {
   using G = GradCfg<TQ, DK>;
   constexpr int LK = G::LK, NT = G::NT, NH = G::NH, HCT = G::HCT, HJ = G::HJ, NC4 = G::NC4, NS4 = G::NS4;
@@ -840,17 +843,27 @@ __global__ __launch_bounds__((GradCfg<TQ, DK>::NT)) void cb_grads_kernel(CbArgs 
         const float4v p = row4(sS0 + r * LK + c) * row4(sdS + r * LK + c);
         sdot += (p[0] + p[1]) + (p[2] + p[3]);
       }
+      // without the delta correction A and X do not depend on k or the state: no E U^T, no E S0
 #pragma unroll
-      for (int J = 0; J < HJ; ++J)
-        mm2<R>(dPa[J], dAa[J], [&](int k) { return row4(sO + (16 * tw + ln) * LR + k); },
-               [&](int k) { return row4(sE + (16 * tw + ln) * LR + k); },
-               [&](int k) { return row4(sU + (16 * (J0 + J) + ln) * LR + k); }, g4);
+      for (int J = 0; J < HJ; ++J) {
+        if constexpr (ND)
+          mm<R>(dPa[J], [&](int k) { return row4(sO + (16 * tw + ln) * LR + k); },
+                [&](int k) { return row4(sU + (16 * (J0 + J) + ln) * LR + k); }, g4);
+        else
+          mm2<R>(dPa[J], dAa[J], [&](int k) { return row4(sO + (16 * tw + ln) * LR + k); },
+                 [&](int k) { return row4(sE + (16 * tw + ln) * LR + k); },
+                 [&](int k) { return row4(sU + (16 * (J0 + J) + ln) * LR + k); }, g4);
+      }
 #pragma unroll
       for (int ct = 0; ct < HCT; ++ct) {
         const int c = 16 * (ct0 + ct) + ln;
-        mm2<R>(Q1[ct], ES[ct], [&](int k) { return row4(sO + (16 * tw + ln) * LR + k); },
-               [&](int k) { return row4(sE + (16 * tw + ln) * LR + k); },
-               [&](int k) { return col4(sS0 + k * LK + c, LK); }, g4);
+        if constexpr (ND)
+          mm<R>(Q1[ct], [&](int k) { return row4(sO + (16 * tw + ln) * LR + k); },
+                [&](int k) { return col4(sS0 + k * LK + c, LK); }, g4);
+        else
+          mm2<R>(Q1[ct], ES[ct], [&](int k) { return row4(sO + (16 * tw + ln) * LR + k); },
+                 [&](int k) { return row4(sE + (16 * tw + ln) * LR + k); },
+                 [&](int k) { return col4(sS0 + k * LK + c, LK); }, g4);
         mm<R>(UD[ct], [&](int k) { return row4(sU + (16 * tw + ln) * LR + k); },
               [&](int k) { return col4(sdS + k * LK + c, LK); }, g4);
         __builtin_amdgcn_sched_barrier(0);   // one tile's operands live at a time
@@ -889,13 +902,19 @@ __global__ __launch_bounds__((GradCfg<TQ, DK>::NT)) void cb_grads_kernel(CbArgs 
       for (int ct = 0; ct < HCT; ++ct) {
         const int c = 16 * (ct0 + ct) + ln;
         float4v q2 = {0.f, 0.f, 0.f, 0.f}, k1 = q2, f1 = q2, f2 = q2;
-        mm2r<C>(q2, f1, [&](int k) { return row4(sdP + (16 * TW + ln) * LC + k); },
-                [&](int k) { return row4(sB + (16 * TW + ln) * LC + k); },
-                [&](int k) { return col4(sK + k * LK + c, LK); }, g4, 0, TW + 1);
+        if constexpr (ND) {   // B = 0 without the delta correction
+          mmr<C>(q2, [&](int k) { return row4(sdP + (16 * TW + ln) * LC + k); },
+                 [&](int k) { return col4(sK + k * LK + c, LK); }, g4, 0, TW + 1);
+        } else {
+          mm2r<C>(q2, f1, [&](int k) { return row4(sdP + (16 * TW + ln) * LC + k); },
+                  [&](int k) { return row4(sB + (16 * TW + ln) * LC + k); },
+                  [&](int k) { return col4(sK + k * LK + c, LK); }, g4, 0, TW + 1);
+        }
         mmr<C>(k1, [&](int k) { return col4(sdP + k * LC + 16 * TW + ln, LC); },
                [&](int k) { return col4(sQ + k * LK + c, LK); }, g4, TW, 4);
-        mmr<C>(f2, [&](int k) { return col4(sB + k * LC + 16 * TW + ln, LC) * row4(sb + k); },
-               [&](int k) { return col4(sK + k * LK + c, LK); }, g4, TW, 4);
+        if constexpr (!ND)
+          mmr<C>(f2, [&](int k) { return col4(sB + k * LC + 16 * TW + ln, LC) * row4(sb + k); },
+                 [&](int k) { return col4(sK + k * LK + c, LK); }, g4, TW, 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 16 * TW + 4 * g4 + e;
@@ -1040,7 +1059,8 @@ hipError_t launch_cb_t(const Shape &sh, const CbPlan &pl, CbArgs a, const float 
   if ((e = set_smem(cb_prep_kernel<TQ, TG, DK>, Sm::prep)) != hipSuccess) return e;
   if ((e = set_smem(cb_fwd_kernel<TQ, DK>, Sm::fwd)) != hipSuccess) return e;
   if ((e = set_smem(cb_bwd_kernel<TQ, DK>, Sm::bwd)) != hipSuccess) return e;
-  if ((e = set_smem(cb_grads_kernel<TQ, TG, DK>, Sm::grads)) != hipSuccess) return e;
+  if ((e = set_smem(cb_grads_kernel<TQ, TG, DK, false>, Sm::grads)) != hipSuccess) return e;
+  if ((e = set_smem(cb_grads_kernel<TQ, TG, DK, true>, Sm::grads)) != hipSuccess) return e;
   const dim3 pass(sh.dv / R, sh.Hv, sh.B);
   auto prep = [&](int flags) {
     a.flags = flags;
@@ -1057,7 +1077,12 @@ hipError_t launch_cb_t(const Shape &sh, const CbPlan &pl, CbArgs a, const float 
     if (r != hipSuccess) return r;
     hipLaunchKernelGGL((cb_bwd_kernel<TQ, DK>), pass, dim3(NTP), Sm::bwd, st, a);
     if ((r = hipGetLastError()) != hipSuccess) return r;
-    hipLaunchKernelGGL((cb_grads_kernel<TQ, TG, DK>), dim3(a.c1 - a.c0, sh.Hk, sh.B), dim3(NTG), Sm::grads, st, a);
+    if (a.nd)
+      hipLaunchKernelGGL((cb_grads_kernel<TQ, TG, DK, true>), dim3(a.c1 - a.c0, sh.Hk, sh.B), dim3(NTG), Sm::grads, st,
+                         a);
+    else
+      hipLaunchKernelGGL((cb_grads_kernel<TQ, TG, DK, false>), dim3(a.c1 - a.c0, sh.Hk, sh.B), dim3(NTG), Sm::grads,
+                         st, a);
     return hipGetLastError();
   };
   a.nseg = pl.nseg;
@@ -1122,6 +1147,7 @@ hipError_t launch_chunk_backward(const Shape &sh, const void *q, const void *k, 
   a.Hv = sh.Hv;
   a.dv_dim = sh.dv;
   a.nc = pl.nc;
+  a.nd = sh.no_delta ? 1 : 0;
   float *w = (float *)ws;
   a.Tm = w + pl.f_T;
   a.gam = w + pl.f_g;

@@ -30,7 +30,7 @@ def gpu():
     gdn.lib()
 
 
-def run_case(wl, label, s0=True, dst=True, seed=0):
+def run_case(wl, label, s0=True, dst=True, seed=0, delta=True, workspace_cap=None):
     inp = make_prefill(wl.with_(s0_std=0.0))
     say("%s: B=%d T=%d Hk=%d Hv=%d d=%d/%d %s gate=%s" % (label, wl.B, wl.T, wl.Hk, wl.Hv, wl.dk, wl.dv,
                                                           wl.dtype, wl.gate))
@@ -40,10 +40,10 @@ def run_case(wl, label, s0=True, dst=True, seed=0):
     dST = np.ascontiguousarray(r.standard_normal((wl.B, wl.Hv, wl.dv, wl.dk)), dtype=np.float32) if dst else None
     args = [to_torch(inp[n]) for n in ("q", "k", "v", "g", "beta")]
     got = gdn.bwd(*args, None if S0 is None else to_torch(S0), to_torch(dO),
-                  None if dST is None else to_torch(dST))
+                  None if dST is None else to_torch(dST), delta=delta, workspace_cap=workspace_cap)
     torch.cuda.synchronize()
     ref = oracle.backward(*(inp[n].f32() for n in ("q", "k", "v", "g", "beta")),
-                          None if S0 is None else S0.astype(np.float64), dO, dST)
+                          None if S0 is None else S0.astype(np.float64), dO, dST, delta=delta)
     for n in ("dq", "dk", "dv", "dg", "dbeta", "dS0"):
         x = got[n].cpu().numpy()
         assert np.all(np.isfinite(x)), "%s: non-finite %s" % (label, n)
@@ -180,3 +180,13 @@ def test_bwd_chunk_edges(T):
     """One token, exactly one chunk, one chunk and a token: the chunked
     backward's padding and its single-chunk case, one key and one value head."""
     run_case(PREFILL_CONV.with_(B=2, T=T, Hk=1, Hv=1, conv=False), "bwd T=%d" % T, seed=T)
+
+
+def test_bwd_without_delta_correction():
+    """The update without the delta correction (per-head gate): fp32 at small
+    head dims, and bf16 grouped heads over several chunks, one segment and
+    several (the smallest workspace)."""
+    run_case(TINY_F32.with_(B=2, T=70, Hk=1, Hv=2, dk=32, dv=64), "bwd no-delta fp32", delta=False)
+    wl = PREFILL_CONV.with_(B=1, T=300, Hk=2, Hv=6, conv=False)
+    run_case(wl, "bwd no-delta bf16", delta=False, seed=3)
+    run_case(wl, "bwd no-delta bf16 segments", delta=False, seed=3, workspace_cap=0)
