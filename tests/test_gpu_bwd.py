@@ -190,3 +190,38 @@ def test_bwd_without_delta_correction():
     wl = PREFILL_CONV.with_(B=1, T=300, Hk=2, Hv=6, conv=False)
     run_case(wl, "bwd no-delta bf16", delta=False, seed=3)
     run_case(wl, "bwd no-delta bf16 segments", delta=False, seed=3, workspace_cap=0)
+
+
+@pytest.mark.parametrize("cap", [None, 0])
+def test_bwd_graph_capture(cap):
+    """The backward captured into a graph (one segment, and the smallest
+    workspace's several) and replayed three times with eager work between the
+    replays: every replay equals the eager call bit for bit."""
+    wl = PREFILL_CONV.with_(B=1, T=300, Hk=2, Hv=6, conv=False)
+    inp = make_prefill(wl)
+    say("bwd graph capture, workspace cap %s" % cap)
+    r = np.random.default_rng(77)
+    S0 = to_torch(np.ascontiguousarray(r.normal(0, 0.05, (wl.B, wl.Hv, wl.dv, wl.dk)), dtype=np.float32))
+    dO = to_torch(np.ascontiguousarray(r.standard_normal((wl.B, wl.T, wl.Hv, wl.dv)), dtype=np.float32))
+    dST = to_torch(np.ascontiguousarray(r.standard_normal((wl.B, wl.Hv, wl.dv, wl.dk)), dtype=np.float32))
+    args = [to_torch(inp[n]) for n in ("q", "k", "v", "g", "beta")] + [S0, dO, dST]
+    eager = gdn.bwd(*args, workspace_cap=cap)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):           # warm the allocator outside the capture
+        gdn.bwd(*args, workspace_cap=cap)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        got = gdn.bwd(*args, workspace_cap=cap)
+    for rep in range(3):
+        for x in got.values():
+            x.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda").sum()   # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        for n in eager:
+            assert torch.equal(got[n], eager[n]), "replay %d: %s differs from the eager call" % (rep, n)
