@@ -1,5 +1,6 @@
-// chunk_bwd.hip -- the backward of the gated delta rule with the per-head
-// gate, in chunks of C = 64 tokens on the fp32 matrix cores (16x16x4).
+// chunk_bwd.hip -- the backward of the gated delta rule, per-head and
+// per-key-channel gates, in chunks of C = 64 tokens on the fp32 matrix cores
+// (16x16x4).
 // ("Source notes", Linear attention, row kda: the first-order backward; the
 // "SinkProbe" page: the exact chunkwise form of the recurrence.)
 //
@@ -21,9 +22,21 @@
 // sum of those over the chunk's tokens i >= t.  The gate is taken to decay
 // (g <= 0), so every factor e^(gamma_i - gamma_j) with i >= j is at most 1.
 //
+// Per-key-channel gate: gamma_i is a vector over the key channels and every
+// decay acts channel by channel: A_ij = beta_i sum_c k_ic k_jc e^(gamma_ic -
+// gamma_jc) and P likewise with q_i; X = beta (V - (K o e^gamma) S0^T);
+// S_C = S0 diag(e^gamma_C) + U^T (K o e^(gamma_C - gamma)); dU takes
+// K o e^(gamma_C - gamma) and dS0 = dS_C diag(e^gamma_C) + dO^T (Q o e^gamma)
+// - (beta E)^T (K o e^gamma).  The masked products, (M o dP) K and the like,
+// become sums over j of dP_ij k_j o e^(gamma_i - gamma_j): in 16-token blocks,
+// off the diagonal through a reference token between i and j (both factors
+// at most 1), on the diagonal term by term.  The gradient of gamma, and dg,
+// are per channel.
+//
 // Four launches, the three passes after the first working from its output:
 //  - prep, per (chunk, key head) over the key head's value heads: gamma,
-//    beta, T and P^T;
+//    beta, T and P^T (per-key-channel gate: also K o e^gamma, Q o e^gamma
+//    and K o e^(gamma_C - gamma), for the passes);
 //  - forward pass, per (batch, value head, 32 state rows), over the chunks in
 //    order: the state before each chunk and U;
 //  - backward pass, per (batch, value head, 32 state rows), over the chunks
@@ -68,6 +81,9 @@ struct CbArgs {
   // it [dv][dk], U [C][dv], E [C][dv].  With several segments, the state before
   // each segment's first chunk, [B Hv][nseg][dv][dk].
   float *Tm, *gam, *bet, *Pt, *S0s, *dSC, *Um, *Em, *Sseg;
+  // per-key-channel gate, for every chunk: gamma is [C][dk], and the decayed
+  // operands K o e^gamma, Q o e^gamma, K o e^(gamma_C - gamma), [C][dk] each
+  float *Kh, *Qh, *Kt;
   int T, Hk, Hv, dv_dim, nc;
   int c0, c1;         // the launch's chunks
   int sc0, ncs, nseg;
@@ -157,6 +173,60 @@ __host__ __device__ constexpr int prep_region(int DK) {
   return C * (DK + 4) > C * LC + 4 * 16 * LX ? C * (DK + 4) : C * LC + 4 * 16 * LX;
 }
 
+// T = (I + A)^-1 for the strictly lower A in LDS [C][LC], into sT [C][LC] and
+// Tg [C][C]: the 16 x 16 diagonal blocks by forward substitution (wave w the
+// block w), then the blocks below them one block diagonal at a time as
+// T_IJ = -T_II sum_{J <= K < I} A_IK T_KJ (sX: the wave's 16 x 16 staging
+// tile).  The caller has synchronised the workgroup after writing A.
+__device__ __forceinline__ void solve_T(const float *sA, float *sT, float *sX, float *Tg, int tid) {
+  const int w = tid >> 6, lane = tid & 63, ln = lane & 15, g4 = lane >> 4;
+  {
+    // diagonal block w: lane (c, q) = (lane / 4, lane % 4) holds T[b + 4 m + q][b + c]
+    // (b = 16 w); T[i][c] = [i == c] - sum_{j < i} A[i][j] T[j][c], the sum over
+    // j = 4 m + q in the lane and over q in the quad (A is zero on and above the diagonal)
+    const int c = lane >> 2, q = lane & 3, bw = 16 * w;
+    float t4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float s = 0.f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) s = __builtin_fmaf(sA[(bw + i) * LC + bw + 4 * m + q], t4[m], s);
+      s = group_sum<4>(s);
+      const float val = (i == c ? 1.f : 0.f) - s;
+      t4[i >> 2] = q == (i & 3) ? val : t4[i >> 2];
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) sT[(bw + 4 * m + q) * LC + bw + c] = t4[m];
+    // blocks above the diagonal are zero
+    for (int J = w + 1; J < 4; ++J)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) sT[(bw + 4 * m + q) * LC + 16 * J + c] = 0.f;
+  }
+#pragma unroll
+  for (int d = 1; d < 4; ++d) {
+    lds_barrier();
+    if (w < 4 - d) {
+      const int I = w + d, J = w;
+      float4v x = {0.f, 0.f, 0.f, 0.f};
+      for (int K = J; K < I; ++K)
+        mm<16>(x, [&](int k) { return row4(sA + (16 * I + ln) * LC + 16 * K + k); },
+               [&](int k) { return col4(sT + (16 * K + k) * LC + 16 * J + ln, LC); }, g4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sX[(4 * g4 + e) * LX + ln] = x[e];
+      float4v y = {0.f, 0.f, 0.f, 0.f};
+      mm<16>(y, [&](int k) { return row4(sT + (16 * I + ln) * LC + 16 * I + k); },
+             [&](int k) { return col4(sX + k * LX + ln, LX); }, g4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sT[(16 * I + 4 * g4 + e) * LC + 16 * J + ln] = -y[e];
+    }
+  }
+  lds_barrier();
+  for (int u = tid; u < C * C / 4; u += 256) {
+    const int i = u / (C / 4), j = (u % (C / 4)) * 4;
+    *reinterpret_cast<float4v *>(Tg + i * C + j) = row4(sT + i * LC + j);
+  }
+}
+
 template <typename TQ, typename TG, int DK>
 __global__ __launch_bounds__(256) void cb_prep_kernel(CbArgs a) {
   constexpr int LK = DK + 4;
@@ -231,52 +301,117 @@ __global__ __launch_bounds__(256) void cb_prep_kernel(CbArgs a) {
     }
     if (!doT) continue;
     __syncthreads();
-    {
-      // diagonal block w: lane (c, q) = (lane / 4, lane % 4) holds T[b + 4 m + q][b + c]
-      // (b = 16 w); T[i][c] = [i == c] - sum_{j < i} A[i][j] T[j][c], the sum over
-      // j = 4 m + q in the lane and over q in the quad (A is zero on and above the diagonal)
-      const int c = lane >> 2, q = lane & 3, bw = 16 * w;
-      float t4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float s = 0.f;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) s = __builtin_fmaf(sA[(bw + i) * LC + bw + 4 * m + q], t4[m], s);
-        s = group_sum<4>(s);
-        const float val = (i == c ? 1.f : 0.f) - s;
-        t4[i >> 2] = q == (i & 3) ? val : t4[i >> 2];
+    solve_T(sA, sT, sX, a.Tm + cn * C * C, tid);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// prep, per-key-channel gate: per (chunk, key head), for each value head of
+// the key head: gamma [C][dk] (the prefix sums of g over the chunk, channel by
+// channel), beta, the decayed operands K o e^gamma, Q o e^gamma and
+// K o e^(gamma_C - gamma), A and P, P^T and T.  A_ij = beta_i sum_c k_ic k_jc
+// e^(gamma_ic - gamma_jc) and P_ij = sum_c q_ic k_jc e^(...): below the
+// diagonal 16 x 16 blocks, about the row block's first token p, as products
+// of (k_i o e^(gamma_i - gamma_p)) and (k_j o e^(gamma_p - gamma_j)), both
+// factors at most 1 (j < p <= i); the diagonal blocks term by term, each
+// factor e^(gamma_ic - gamma_jc) at most 1, so no decay overflows.
+template <typename TQ, typename TG, int DK>
+__global__ __launch_bounds__(256) void cb_prep_key_kernel(CbArgs a) {
+  constexpr int LK = DK + 4;
+  extern __shared__ float4v smem4[];
+  float *smem = reinterpret_cast<float *>(smem4);
+  float *sK = smem, *sQ = sK + C * LK, *sG = sQ + C * LK, *sA = sG + C * LK, *sT = sA + C * LC;
+  float *sb = sT + C * LC;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 15, g4 = lane >> 4;
+  float *sX = sb + C + w * 16 * LX;
+  const int n = a.c0 + blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
+  const int T = a.T, Hk = a.Hk, Hv = a.Hv, grp = Hv / Hk;
+  const int t0 = n * C, len = min(C, T - t0);
+  const size_t row0 = (size_t)b * T + t0;
+  const bool doT = a.flags & kPrepT, doP = a.flags & kPrepP;
+  load_rows<TQ, DK>(sK, (const TQ *)a.k, row0 * Hk + kh, Hk, len, tid);
+  load_rows<TQ, DK>(sQ, (const TQ *)a.q, row0 * Hk + kh, Hk, len, tid);
+  const TG *g = (const TG *)a.g, *be = (const TG *)a.beta;
+  for (int hh = 0; hh < grp; ++hh) {
+    const int h = kh * grp + hh;
+    const size_t bh = (size_t)b * Hv + h, cn = gch(a, bh, n);
+    __syncthreads();   // the rows are loaded, or the previous head's reads are done
+    if (tid < DK) {
+      // gamma_tc = sum_{s <= t} g_sc over the chunk (zero past the end)
+      float sum = 0.f;
+#pragma unroll 8
+      for (int t = 0; t < C; ++t) {
+        sum += t < len ? to_f32(g[((row0 + t) * Hv + h) * DK + tid]) : 0.f;
+        sG[t * LK + tid] = sum;
       }
-#pragma unroll
-      for (int m = 0; m < 4; ++m) sT[(bw + 4 * m + q) * LC + bw + c] = t4[m];
-      // blocks above the diagonal are zero
-      for (int J = w + 1; J < 4; ++J)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) sT[(bw + 4 * m + q) * LC + 16 * J + c] = 0.f;
     }
+    if (tid < C) sb[tid] = tid < len ? to_f32(be[(row0 + tid) * Hv + h]) : 0.f;
+    __syncthreads();
+    if (doT) {
+      float *gg = a.gam + cn * C * DK, *kh_ = a.Kh + cn * C * DK, *qh_ = a.Qh + cn * C * DK, *kt_ = a.Kt + cn * C * DK;
+      for (int u = tid; u < C * DK / 4; u += 256) {
+        const int t = u / (DK / 4), c = (u % (DK / 4)) * 4;
+        const float4v gm = row4(sG + t * LK + c), gC = row4(sG + (C - 1) * LK + c);
+        const float4v kv = row4(sK + t * LK + c), qv = row4(sQ + t * LK + c);
+        float4v e1, e2;
 #pragma unroll
-    for (int d = 1; d < 4; ++d) {
-      lds_barrier();
-      if (w < 4 - d) {
-        const int I = w + d, J = w;
-        float4v x = {0.f, 0.f, 0.f, 0.f};
-        for (int K = J; K < I; ++K)
-          mm<16>(x, [&](int k) { return row4(sA + (16 * I + ln) * LC + 16 * K + k); },
-                 [&](int k) { return col4(sT + (16 * K + k) * LC + 16 * J + ln, LC); }, g4);
+        for (int e = 0; e < 4; ++e) e1[e] = __expf(gm[e]), e2[e] = __expf(gC[e] - gm[e]);
+        *reinterpret_cast<float4v *>(gg + t * DK + c) = gm;
+        *reinterpret_cast<float4v *>(kh_ + t * DK + c) = kv * e1;
+        *reinterpret_cast<float4v *>(qh_ + t * DK + c) = qv * e1;
+        *reinterpret_cast<float4v *>(kt_ + t * DK + c) = kv * e2;
+      }
+      if (tid < C) a.bet[cn * C + tid] = sb[tid];
+    }
+    float *Ptg = a.Pt + sch(a, bh, n) * C * C;
+    // blocks (w, J < w): about token p = 16 w; the lane holds i = 16 w + 4 g4 + e, j = 16 J + ln
+    const int p = 16 * w;
+    for (int J = 0; J < 4; ++J) {
+      const int j = 16 * J + ln;
+      float4v kk = {0.f, 0.f, 0.f, 0.f}, qk = kk;
+      if (J < w) {
+        for (int k = 0; k < DK; k += 16) {
+          const int kb = k + 4 * g4;
+          const float4v gi = row4(sG + (16 * w + ln) * LK + kb), gp = row4(sG + p * LK + kb);
+          const float4v gj = row4(sG + j * LK + kb);
+          const float4v ki = row4(sK + (16 * w + ln) * LK + kb), qi = row4(sQ + (16 * w + ln) * LK + kb);
+          const float4v kj = row4(sK + j * LK + kb);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sX[(4 * g4 + e) * LX + ln] = x[e];
-        float4v y = {0.f, 0.f, 0.f, 0.f};
-        mm<16>(y, [&](int k) { return row4(sT + (16 * I + ln) * LC + 16 * I + k); },
-               [&](int k) { return col4(sX + k * LX + ln, LX); }, g4);
+          for (int e = 0; e < 4; ++e) {
+            const float fi = __expf(gi[e] - gp[e]), y = kj[e] * __expf(gp[e] - gj[e]);
+            kk = mma(ki[e] * fi, y, kk);
+            qk = mma(qi[e] * fi, y, qk);
+          }
+        }
+      }
+      if (J != w) {   // the diagonal block is written below
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sT[(16 * I + 4 * g4 + e) * LC + 16 * J + ln] = -y[e];
+        for (int e = 0; e < 4; ++e) sA[(16 * w + 4 * g4 + e) * LC + j] = J < w ? sb[16 * w + 4 * g4 + e] * kk[e] : 0.f;
+        if (doP) *reinterpret_cast<float4v *>(Ptg + j * C + 16 * w + 4 * g4) = qk;   // P^T[j][i]; zero above
       }
     }
-    lds_barrier();
-    float *Tg = a.Tm + cn * C * C;
-    for (int u = tid; u < C * C / 4; u += 256) {
-      const int i = u / (C / 4), j = (u % (C / 4)) * 4;
-      *reinterpret_cast<float4v *>(Tg + i * C + j) = row4(sT + i * LC + j);
+    // diagonal block w, term by term: pair m = (i, j) of the block, four per lane
+    for (int m = lane; m < 256; m += 64) {
+      const int il = m >> 4, jl = m & 15, i = 16 * w + il, j = 16 * w + jl;
+      float av = 0.f, pv = 0.f;
+      if (jl <= il) {
+        for (int c = 0; c < DK; c += 4) {
+          const float4v gi = row4(sG + i * LK + c), gj = row4(sG + j * LK + c);
+          const float4v ki = row4(sK + i * LK + c), qi = row4(sQ + i * LK + c), kj = row4(sK + j * LK + c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float f = kj[e] * __expf(gi[e] - gj[e]);
+            av = __builtin_fmaf(ki[e], f, av);
+            pv = __builtin_fmaf(qi[e], f, pv);
+          }
+        }
+      }
+      sA[i * LC + j] = jl < il ? sb[i] * av : 0.f;
+      if (doP) Ptg[j * C + i] = pv;
     }
+    if (!doT) continue;
+    __syncthreads();
+    solve_T(sA, sT, sX, a.Tm + cn * C * C, tid);
   }
 }
 
@@ -427,16 +562,52 @@ struct GateReg {
   }
 };
 
-// forward pass, over the chunks in order: the state before each chunk and U
-template <typename TQ, int DK>
+// a [C][DK] fp32 matrix of the workspace (the key gate's decayed operands), into
+// LDS rows of DK + 4
+template <int DK, int NT>
+struct CkReg {
+  static constexpr int NU = C * DK / 4 / NT;
+  float4v u[NU];
+  __device__ __forceinline__ void load(const float *src, int tid) {
+#pragma unroll
+    for (int i = 0; i < NU; ++i) u[i] = *reinterpret_cast<const float4v *>(src + 4 * (tid + i * NT));
+  }
+  __device__ __forceinline__ void store(float *s, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int x = tid + i * NT;
+      *reinterpret_cast<float4v *>(s + (x / (DK / 4)) * (DK + 4) + (x % (DK / 4)) * 4) = u[i];
+    }
+  }
+};
+
+// the key gate's chunk scalars: beta_t (thread t < C) and e^gamma_C per channel (thread c < DK)
+template <int DK>
+struct KeyGateReg {
+  float b, gC;
+  __device__ __forceinline__ void load(const CbArgs &a, size_t cn, int tid) {
+    if (tid < C) b = a.bet[cn * C + tid];
+    if (tid < DK) gC = a.gam[(cn * C + C - 1) * DK + tid];
+  }
+  __device__ __forceinline__ void store(float *sb, float *sEC, int tid) const {
+    if (tid < C) sb[tid] = b;
+    if (tid < DK) sEC[tid] = __expf(gC);
+  }
+};
+
+// forward pass, over the chunks in order: the state before each chunk and U.
+// Key gate (KEY): K o e^gamma and K o e^(gamma_C - gamma) from the prep in
+// place of k, and the state's columns decay by e^gamma_C,c.
+template <typename TQ, int DK, bool KEY>
 __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_fwd_kernel(CbArgs a) {
   using P = PassCfg<TQ, DK>;
   constexpr int LK = P::LK, LS = P::LS, NCT = P::NCT, NS = P::NS, ZT = P::ZT, NT = P::NT;
   extern __shared__ float4v smem4[];
   TQ *sK = reinterpret_cast<TQ *>(smem4);
-  float *sT = reinterpret_cast<float *>(sK + C * LK);
+  float *sKh = reinterpret_cast<float *>(smem4), *sKt = sKh + C * LS;   // key gate
+  float *sT = KEY ? sKt + C * LS : reinterpret_cast<float *>(sK + C * LK);
   float *sS = sT + C * LC, *sX = sS + R * LS, *sU = sX + R * LC;
-  float *sEg = sU + R * LC, *sEc = sEg + C, *sb = sEc + C;
+  float *sEg = sU + R * LC, *sEc = sEg + C, *sb = sEc + C, *sEC = sb + C;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 15, g4 = lane >> 4;
   const int sl = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int T = a.T, Hk = a.Hk, Hv = a.Hv, DV = a.dv_dim, kh = h / (Hv / Hk), r0 = sl * R;
@@ -465,15 +636,23 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_fwd_kernel(CbArgs a)
       for (int e = 0; e < 4; ++e) Sg[(r0 + 16 * srt[s] + 4 * g4 + e) * DK + 16 * sct[s] + ln] = S[s][e];
   };
   RowsReg<TQ, DK, NT> kr;
+  CkReg<DK, NT> khr, ktr;
   CcReg<NT> tr;
   GateReg gr;
+  KeyGateReg<DK> kgr;
   typename Quad<TQ>::type vq[ZT];
   auto fetch = [&](int n) {
     const int t0 = n * C, len = min(C, T - t0);
     const size_t cn = gch(a, bh, n), row0 = (size_t)b * T + t0;
-    kr.load(k + (row0 * Hk + kh) * DK, (size_t)Hk * DK, len, tid);
+    if constexpr (KEY) {
+      khr.load(a.Kh + cn * C * DK, tid);
+      ktr.load(a.Kt + cn * C * DK, tid);
+      kgr.load(a, cn, tid);
+    } else {
+      kr.load(k + (row0 * Hk + kh) * DK, (size_t)Hk * DK, len, tid);
+      gr.load(a, cn, tid);
+    }
     tr.load(a.Tm + cn * C * C, tid);
-    gr.load(a, cn, tid);
 #pragma unroll
     for (int z = 0; z < ZT; ++z) {
       const int t = 16 * zcc[z] + ln;
@@ -483,9 +662,15 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_fwd_kernel(CbArgs a)
   };
   fetch(a.c0);
   for (int n = a.c0; n < a.c1; ++n) {
-    kr.template store<LK>(sK, tid);
+    if constexpr (KEY) {
+      khr.store(sKh, tid);
+      ktr.store(sKt, tid);
+      kgr.store(sb, sEC, tid);
+    } else {
+      kr.template store<LK>(sK, tid);
+      gr.store(sEg, sEc, sb, tid);
+    }
     tr.store(sT, tid);
-    gr.store(sEg, sEc, sb, tid);
     float4v vx[ZT];
 #pragma unroll
     for (int z = 0; z < ZT; ++z) vx[z] = quad_to_f32<TQ>(vq[z]);
@@ -508,8 +693,11 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_fwd_kernel(CbArgs a)
       float4v acc = {0.f, 0.f, 0.f, 0.f};
       if (!a.nd)
         mm<DK>(acc, [&](int kk) { return row4(sS + (16 * rt + ln) * LS + kk); },
-               [&](int kk) { return rowq(sK + t * LK + kk); }, g4);
-      const float eg = sEg[t], bt = sb[t];
+               [&](int kk) {
+                 if constexpr (KEY) return row4(sKh + t * LS + kk);   // (k o e^gamma)_t
+                 else return rowq(sK + t * LK + kk);
+               }, g4);
+      const float eg = KEY ? 1.f : sEg[t], bt = sb[t];
 #pragma unroll
       for (int e = 0; e < 4; ++e) sX[(16 * rt + 4 * g4 + e) * LC + t] = bt * (vx[z][e] - eg * acc[e]);
     }
@@ -525,19 +713,21 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_fwd_kernel(CbArgs a)
                [&](int kk) { return row4(sT + i * LC + kk); }, g4, 0, decltype(ZC)::value + 1);
       });
       if (!so) *reinterpret_cast<float4v *>(a.Um + (sch(a, bh, n) * C + i) * DV + r0 + 16 * rt + 4 * g4) = u;
-      const float ec = sEc[i];
+      const float ec = KEY ? 1.f : sEc[i];   // the key gate's decay is in K o e^(gamma_C - gamma)
 #pragma unroll
       for (int e = 0; e < 4; ++e) sU[(16 * rt + 4 * g4 + e) * LC + i] = u[e] * ec;
     }
     lds_barrier();
-    // S <- e^gamma_C S + sum_j U~^T[r][j] k_j
-    const float eC = sEg[C - 1];
+    // S <- e^gamma_C S + sum_j U~^T[r][j] k_j (key gate: S diag(e^gamma_C) + U^T (K o e^(gamma_C - gamma)))
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int rt = srt[s], c = 16 * sct[s] + ln;
-      S[s] *= eC;
+      S[s] *= KEY ? sEC[c] : sEg[C - 1];
       mm<C>(S[s], [&](int kk) { return row4(sU + (16 * rt + ln) * LC + kk); },
-            [&](int kk) { return colq(sK + kk * LK + c, LK); }, g4);
+            [&](int kk) {
+              if constexpr (KEY) return col4(sKt + kk * LS + c, LS);
+              else return colq(sK + kk * LK + c, LK);
+            }, g4);
     }
     lds_barrier();
   }
@@ -545,16 +735,21 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_fwd_kernel(CbArgs a)
 }
 
 // backward pass, over the chunks in reverse: the state gradient after each
-// chunk, E, dv, and dS0 at the end
-template <typename TQ, int DK>
+// chunk, E, dv, and dS0 at the end.  Key gate (KEY): K o e^(gamma_C - gamma)
+// in place of the decayed k of dU, K o e^gamma and Q o e^gamma in place of
+// the decayed k and q of the state gradient's update; K o e^(gamma_C - gamma)
+// is read only before the first barrier of a chunk, so Q o e^gamma is written
+// over it after that barrier (and its next chunk loaded after that).
+template <typename TQ, int DK, bool KEY>
 __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_bwd_kernel(CbArgs a) {
   using P = PassCfg<TQ, DK>;
   constexpr int LK = P::LK, LS = P::LS, NCT = P::NCT, NS = P::NS, ZT = P::ZT, NT = P::NT;
   extern __shared__ float4v smem4[];
   TQ *sK = reinterpret_cast<TQ *>(smem4), *sQ = sK + C * LK;
-  float *sT = reinterpret_cast<float *>(sQ + C * LK);
+  float *sKtQ = reinterpret_cast<float *>(smem4), *sKh = sKtQ + C * LS;   // key gate
+  float *sT = KEY ? sKh + C * LS : reinterpret_cast<float *>(sQ + C * LK);
   float *sP = sT + C * LC, *sO = sP + C * LC, *sS = sO + C * LR, *sD = sS + R * LS, *sE = sD + R * LC;
-  float *sEg = sE + R * LC, *sEc = sEg + C, *sb = sEc + C;
+  float *sEg = sE + R * LC, *sEc = sEg + C, *sb = sEc + C, *sEC = sb + C;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 15, g4 = lane >> 4;
   const int sl = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int T = a.T, Hk = a.Hk, Hv = a.Hv, DV = a.dv_dim, kh = h / (Hv / Hk), r0 = sl * R;
@@ -572,18 +767,26 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_bwd_kernel(CbArgs a)
     for (int e = 0; e < 4; ++e)
       dS[s][e] = a.dS_in ? a.dS_in[(bh * DV + r0 + 16 * srt[s] + 4 * g4 + e) * DK + 16 * sct[s] + ln] : 0.f;
   RowsReg<TQ, DK, NT> kr, qr;
+  CkReg<DK, NT> ktr, khr, qhr;
   CcReg<NT> tr, pr;
   GateReg gr;
+  KeyGateReg<DK> kgr;
   constexpr int NO = C * R / 4 / NT;   // dO: 16-byte units per thread
   float4v orr[NO];
-  auto fetch = [&](int n) {
+  auto fetch = [&](int n) {   // all but the key gate's Q o e^gamma
     const int t0 = n * C, len = min(C, T - t0);
     const size_t cn = gch(a, bh, n), row0 = (size_t)b * T + t0;
-    kr.load(k + (row0 * Hk + kh) * DK, (size_t)Hk * DK, len, tid);
-    qr.load(q + (row0 * Hk + kh) * DK, (size_t)Hk * DK, len, tid);
+    if constexpr (KEY) {
+      ktr.load(a.Kt + cn * C * DK, tid);
+      khr.load(a.Kh + cn * C * DK, tid);
+      kgr.load(a, cn, tid);
+    } else {
+      kr.load(k + (row0 * Hk + kh) * DK, (size_t)Hk * DK, len, tid);
+      qr.load(q + (row0 * Hk + kh) * DK, (size_t)Hk * DK, len, tid);
+      gr.load(a, cn, tid);
+    }
     tr.load(a.Tm + cn * C * C, tid);
     pr.load(a.Pt + sch(a, bh, n) * C * C, tid);
-    gr.load(a, cn, tid);
 #pragma unroll
     for (int i = 0; i < NO; ++i) {
       const int x = tid + i * NT, t = x / (R / 4), r = (x % (R / 4)) * 4;
@@ -592,14 +795,21 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_bwd_kernel(CbArgs a)
     }
   };
   fetch(a.c1 - 1);
+  if constexpr (KEY) qhr.load(a.Qh + gch(a, bh, a.c1 - 1) * C * DK, tid);
   for (int n = a.c1 - 1; n >= a.c0; --n) {
     const int t0 = n * C, len = min(C, T - t0);
     const size_t cn = sch(a, bh, n), row0 = (size_t)b * T + t0;
-    kr.template store<LK>(sK, tid);
-    qr.template store<LK>(sQ, tid);
+    if constexpr (KEY) {
+      ktr.store(sKtQ, tid);
+      khr.store(sKh, tid);
+      kgr.store(sb, sEC, tid);
+    } else {
+      kr.template store<LK>(sK, tid);
+      qr.template store<LK>(sQ, tid);
+      gr.store(sEg, sEc, sb, tid);
+    }
     tr.store(sT, tid);
     pr.store(sP, tid);
-    gr.store(sEg, sEc, sb, tid);
 #pragma unroll
     for (int i = 0; i < NO; ++i) {
       const int x = tid + i * NT;
@@ -622,8 +832,11 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_bwd_kernel(CbArgs a)
       const int rt = zrt[z], i = 16 * zcc[z] + ln;
       float4v acc = {0.f, 0.f, 0.f, 0.f};
       mm<DK>(acc, [&](int kk) { return row4(sS + (16 * rt + ln) * LS + kk); },
-             [&](int kk) { return rowq(sK + i * LK + kk); }, g4);
-      acc *= sEc[i];
+             [&](int kk) {
+               if constexpr (KEY) return row4(sKtQ + i * LS + kk);   // (k o e^(gamma_C - gamma))_i
+               else return rowq(sK + i * LK + kk);
+             }, g4);
+      if constexpr (!KEY) acc *= sEc[i];
       // P[j][i] is zero for j < i: token blocks from i's
       with_block(zcc[z], [&](auto ZC) {
         mmr<C>(acc, [&](int kk) { return col4(sO + kk * LR + 16 * rt + ln, LR); },
@@ -633,6 +846,10 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_bwd_kernel(CbArgs a)
       for (int e = 0; e < 4; ++e) sD[(16 * rt + 4 * g4 + e) * LC + i] = acc[e];
     }
     lds_barrier();
+    if constexpr (KEY) {   // Q o e^gamma over K o e^(gamma_C - gamma), then the next chunk's
+      qhr.store(sKtQ, tid);
+      if (n > a.c0) qhr.load(a.Qh + gch(a, bh, n - 1) * C * DK, tid);
+    }
     // E^T[r][i] = sum_j dU^T[r][j] T[j][i]; dv = beta E; -beta e^gamma E^T to LDS
 #pragma unroll
     for (int z = 0; z < ZT; ++z) {
@@ -647,22 +864,30 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_bwd_kernel(CbArgs a)
       if (i < len)
         *reinterpret_cast<float4v *>(a.dv + ((row0 + i) * Hv + h) * DV + r0 + 16 * rt + 4 * g4) = E * bi;
       *reinterpret_cast<float4v *>(a.Em + (cn * C + i) * DV + r0 + 16 * rt + 4 * g4) = E;
-      const float f = -bi * sEg[i];
+      const float f = KEY ? -bi : -bi * sEg[i];
 #pragma unroll
       for (int e = 0; e < 4; ++e) sE[(16 * rt + 4 * g4 + e) * LC + i] = E[e] * f;
     }
     lds_barrier();
     // dS <- e^gamma_C dS + sum_t dO[t][r] e^gamma_t q_t - sum_t beta_t e^gamma_t E[t][r] k_t
-    const float eC = sEg[C - 1];
+    // (key gate: dS diag(e^gamma_C) + dO^T (Q o e^gamma) - (beta E)^T (K o e^gamma))
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int rt = srt[s], c = 16 * sct[s] + ln;
-      dS[s] *= eC;
-      mm<C>(dS[s], [&](int kk) { return col4(sO + kk * LR + 16 * rt + ln, LR) * row4(sEg + kk); },
-            [&](int kk) { return colq(sQ + kk * LK + c, LK); }, g4);
-      if (!a.nd)   // X = beta V does not depend on the state without the delta correction
+      if constexpr (KEY) {
+        dS[s] *= sEC[c];
+        mm<C>(dS[s], [&](int kk) { return col4(sO + kk * LR + 16 * rt + ln, LR); },
+              [&](int kk) { return col4(sKtQ + kk * LS + c, LS); }, g4);
         mm<C>(dS[s], [&](int kk) { return row4(sE + (16 * rt + ln) * LC + kk); },
-              [&](int kk) { return colq(sK + kk * LK + c, LK); }, g4);
+              [&](int kk) { return col4(sKh + kk * LS + c, LS); }, g4);
+      } else {
+        dS[s] *= sEg[C - 1];
+        mm<C>(dS[s], [&](int kk) { return col4(sO + kk * LR + 16 * rt + ln, LR) * row4(sEg + kk); },
+              [&](int kk) { return colq(sQ + kk * LK + c, LK); }, g4);
+        if (!a.nd)   // X = beta V does not depend on the state without the delta correction
+          mm<C>(dS[s], [&](int kk) { return row4(sE + (16 * rt + ln) * LC + kk); },
+                [&](int kk) { return colq(sK + kk * LK + c, LK); }, g4);
+      }
     }
     lds_barrier();
   }
@@ -681,15 +906,16 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_bwd_kernel(CbArgs a)
 // (four for dk < 128): wave w holds token block w & 3 of every [C][.]
 // product, and half w >> 2 of its column blocks.  The next slice is loaded
 // into registers while the current one is worked on.
-template <typename TQ, int DK>
+template <typename TQ, int DK, bool KEY = false>
 struct GradCfg {
   static constexpr int NW = DK == 128 ? 8 : 4, NT = 64 * NW, NH = NW / 4;   // column halves
   static constexpr int LK = DK + 4, NCT = DK / 16, HCT = NCT / NH, HJ = 4 / NH;
-  static constexpr int SLICE = 3 * C * LR + 2 * R * LK, MASKS = 2 * C * LC;
+  // the key gate keeps gamma [C][dk] after the two masked matrices
+  static constexpr int SLICE = 3 * C * LR + 2 * R * LK, MASKS = 2 * C * LC + (KEY ? C * LK : 0);
   static constexpr int REGION = SLICE > MASKS ? SLICE : MASKS;
   static constexpr int NC4 = C * R / 4 / NT, NS4 = R * DK / 4 / NT;   // 16-byte units per thread
   static constexpr int NV = 8 * C / NT;                                 // (token, 4 rows) units of E . v
-  static constexpr int smem = (2 * C * LK + REGION + (4 + 3 * NH) * C + 2 * NW) * 4;
+  static constexpr int smem = (2 * C * LK + REGION + (4 + 3 * NH) * C + 2 * NW + (KEY ? (NW + 4) * DK : 0)) * 4;
 };
 
 // acc1 += A1 B^T, acc2 += A2 B^T (one read of B), over the k blocks lo <= k / 16 < hi
@@ -723,9 +949,9 @@ __device__ __forceinline__ void mm2(float4v &acc1, float4v &acc2, const FA1 &fa1
   }
 }
 
-template <typename TQ, typename TG, int DK, bool ND>
-__global__ __launch_bounds__((GradCfg<TQ, DK>::NT)) void cb_grads_kernel(CbArgs a) {
-  using G = GradCfg<TQ, DK>;
+template <typename TQ, typename TG, int DK, bool ND, bool KEY>
+__global__ __launch_bounds__((GradCfg<TQ, DK, KEY>::NT)) void cb_grads_kernel(CbArgs a) {
+  using G = GradCfg<TQ, DK, KEY>;
   constexpr int LK = G::LK, NT = G::NT, NH = G::NH, HCT = G::HCT, HJ = G::HJ, NC4 = G::NC4, NS4 = G::NS4;
   constexpr int NV = G::NV;
   extern __shared__ float4v smem4[];
@@ -735,6 +961,9 @@ __global__ __launch_bounds__((GradCfg<TQ, DK>::NT)) void cb_grads_kernel(CbArgs 
   float *sdP = rg, *sB = sdP + C * LC;
   float *sEg = rg + G::REGION, *sEc = sEg + C, *sb = sEc + C, *sg = sb + C;
   float *sGam = sg + C, *sBet = sGam + NH * C, *sBx = sBet + NH * C, *sRed = sBx + NH * C;
+  // key gate: gamma [C][dk] after the masked matrices, and the per-channel gradient of
+  // gamma over them once they are read; per-wave channel sums of dS_C o S0 and of k o dk4
+  float *sG = sB + C * LC, *sGp = rg, *sSd = sRed + 2 * G::NW, *sKd = sSd + G::NW * DK;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 15, g4 = lane >> 4;
   const int tw = w & 3, hw = w >> 2, ct0 = hw * HCT, J0 = hw * HJ;
   const int n = a.c0 + blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
@@ -814,6 +1043,7 @@ __global__ __launch_bounds__((GradCfg<TQ, DK>::NT)) void cb_grads_kernel(CbArgs 
 #pragma unroll
     for (int c = 0; c < HCT; ++c) Q1[c] = ES[c] = UD[c] = float4v{0.f, 0.f, 0.f, 0.f};
     float dbx[NV], sdot = 0.f;
+    float4v sd4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NV; ++i) dbx[i] = 0.f;
     for (int si = 0; si < nsl; ++si) {
@@ -823,7 +1053,11 @@ __global__ __launch_bounds__((GradCfg<TQ, DK>::NT)) void cb_grads_kernel(CbArgs 
 #pragma unroll
       for (int i = 0; i < NV; ++i) vx[i] = quad_to_f32<TQ>(rv[i]);
       if (si == 0) {
-        load_gates(sEg, sEc, sb, a, cn, tid, sg);
+        if constexpr (KEY) {
+          if (tid < C) sb[tid] = a.bet[cn * C + tid];
+        } else {
+          load_gates(sEg, sEc, sb, a, cn, tid, sg);
+        }
       }
       lds_barrier();
       // the next slice, or the next head's first
@@ -841,7 +1075,8 @@ __global__ __launch_bounds__((GradCfg<TQ, DK>::NT)) void cb_grads_kernel(CbArgs 
       for (int i = 0; i < NS4; ++i) {
         const int x = tid + i * NT, r = x / (DK / 4), c = (x % (DK / 4)) * 4;
         const float4v p = row4(sS0 + r * LK + c) * row4(sdS + r * LK + c);
-        sdot += (p[0] + p[1]) + (p[2] + p[3]);
+        if constexpr (KEY) sd4 += p;   // the thread's channels are the same in every unit
+        else sdot += (p[0] + p[1]) + (p[2] + p[3]);
       }
       // without the delta correction A and X do not depend on k or the state: no E U^T, no E S0
 #pragma unroll
@@ -869,109 +1104,289 @@ __global__ __launch_bounds__((GradCfg<TQ, DK>::NT)) void cb_grads_kernel(CbArgs 
         __builtin_amdgcn_sched_barrier(0);   // one tile's operands live at a time
       }
     }
-    lds_barrier();
-    // M o dP and B = M o dA = -(M o E U^T) into LDS (over the slices' space)
+    if constexpr (KEY) {
+      lds_barrier();
+      // dP and B = dA = -E U^T, masked only: the decay is per channel, in the
+      // products below; gamma [C][dk] of the head after them
 #pragma unroll
-    for (int J = 0; J < HJ; ++J) {
-      const int j = 16 * (J0 + J) + ln;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 16 * tw + 4 * g4 + e;
-        const float m = i >= j ? __expf(sg[i] - sg[j]) : 0.f;
-        sdP[i * LC + j] = m * dPa[J][e];
-        sB[i * LC + j] = i > j ? -m * dAa[J][e] : 0.f;
-      }
-    }
-    // E . v (eight threads per token) and <dS_C, S0> over the workgroup
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const float x = group_sum<8>(dbx[i]);
-      if ((tid & 7) == 0) sBx[vtok(i)] = x;
-    }
-    sdot = group_sum<64>(sdot);
-    if (lane == 0) sRed[G::NW + w] = sdot;   // one slot per wave: a fixed order of the sum
-    lds_barrier();
-    float gp[4] = {0.f, 0.f, 0.f, 0.f}, bp[4] = {0.f, 0.f, 0.f, 0.f}, cp = 0.f;
-    // M o dP and B are zero above the diagonal (B on it too): token block TW's rows
-    // need the key blocks up to TW, its columns the token blocks from TW (the tiles
-    // above the diagonal are never read).  One copy of the products per TW, so
-    // that every range is fixed at compile time.
-    auto products = [&](auto TWc) {
-      constexpr int TW = decltype(TWc)::value;
-#pragma unroll
-      for (int ct = 0; ct < HCT; ++ct) {
-        const int c = 16 * (ct0 + ct) + ln;
-        float4v q2 = {0.f, 0.f, 0.f, 0.f}, k1 = q2, f1 = q2, f2 = q2;
-        if constexpr (ND) {   // B = 0 without the delta correction
-          mmr<C>(q2, [&](int k) { return row4(sdP + (16 * TW + ln) * LC + k); },
-                 [&](int k) { return col4(sK + k * LK + c, LK); }, g4, 0, TW + 1);
-        } else {
-          mm2r<C>(q2, f1, [&](int k) { return row4(sdP + (16 * TW + ln) * LC + k); },
-                  [&](int k) { return row4(sB + (16 * TW + ln) * LC + k); },
-                  [&](int k) { return col4(sK + k * LK + c, LK); }, g4, 0, TW + 1);
-        }
-        mmr<C>(k1, [&](int k) { return col4(sdP + k * LC + 16 * TW + ln, LC); },
-               [&](int k) { return col4(sQ + k * LK + c, LK); }, g4, TW, 4);
-        if constexpr (!ND)
-          mmr<C>(f2, [&](int k) { return col4(sB + k * LC + 16 * TW + ln, LC) * row4(sb + k); },
-                 [&](int k) { return col4(sK + k * LK + c, LK); }, g4, TW, 4);
+      for (int J = 0; J < HJ; ++J) {
+        const int j = 16 * (J0 + J) + ln;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int t = 16 * TW + 4 * g4 + e;
-          const float eg = sEg[t], bt = sb[t];
-          const float dq = __builtin_fmaf(eg, Q1[ct][e], q2[e]);
-          const float f1m = __builtin_fmaf(-eg, ES[ct][e], f1[e]);   // (B k)_t - e^gamma_t (E S0)_t
-          const float d4 = sEc[t] * UD[ct][e];
-          const float g1 = k1[e] + d4 + f2[e];
-          dQa[ct][e] += dq;
-          dKa[ct][e] += __builtin_fmaf(bt, f1m, g1);
-          const float qv = sQ[t * LK + c], kv = sK[t * LK + c];
-          gp[e] += qv * dq - kv * g1 + kv * bt * f1m;
-          bp[e] += kv * f1m;
-          cp = __builtin_fmaf(kv, d4, cp);
+          const int i = 16 * tw + 4 * g4 + e;
+          sdP[i * LC + j] = i >= j ? dPa[J][e] : 0.f;
+          sB[i * LC + j] = i > j ? -dAa[J][e] : 0.f;
         }
-        // the next tile reads its operands again rather than keep them in registers
-        asm volatile("" ::: "memory");
       }
-    };
-    switch (tw) {
-      case 0: products(std::integral_constant<int, 0>{}); break;
-      case 1: products(std::integral_constant<int, 1>{}); break;
-      case 2: products(std::integral_constant<int, 2>{}); break;
-      default: products(std::integral_constant<int, 3>{}); break;
-    }
+      for (int u = tid; u < C * DK / 4; u += NT)
+        *reinterpret_cast<float4v *>(sG + (u / (DK / 4)) * LK + (u % (DK / 4)) * 4) =
+            *reinterpret_cast<const float4v *>(a.gam + cn * C * DK + 4 * u);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      gp[e] = group_sum<16>(gp[e]);
-      bp[e] = group_sum<16>(bp[e]);
-    }
-    if (ln == 0) {
+      for (int i = 0; i < NV; ++i) {
+        const float x = group_sum<8>(dbx[i]);
+        if ((tid & 7) == 0) sBx[vtok(i)] = x;
+      }
+      // <dS_C, S0> per channel: lanes of one lane % (dk / 4) hold the same four channels
+#pragma unroll
+      for (int m = DK / 4; m < 64; m <<= 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sd4[e] += __shfl_xor(sd4[e], m, 64);
+      if (lane < DK / 4) *reinterpret_cast<float4v *>(sSd + w * DK + 4 * lane) = sd4;
+      lds_barrier();
+      float bp[4] = {0.f, 0.f, 0.f, 0.f}, gpk[HCT][4], kdx[HCT];
+      // token block TW of the rows (q2, f1: sums over keys j <= i) and of the columns
+      // (k1, f2: sums over rows i >= j).  The blocks off the diagonal go through the
+      // matrix cores about a reference token: the rows' first token p for the keys
+      // before the block, the columns' last token pe for the rows after it, so that
+      // both factors of e^(gamma_i - gamma_j) = e^(gamma_i - gamma_ref) e^(gamma_ref -
+      // gamma_j) are at most 1; the diagonal block term by term.
+      auto products = [&](auto TWc) {
+        constexpr int TW = decltype(TWc)::value, p = 16 * TW, pe = p + 15;
+#pragma unroll
+        for (int ct = 0; ct < HCT; ++ct) {
+          const int c = 16 * (ct0 + ct) + ln;
+          const float gp = sG[p * LK + c], gl = sG[pe * LK + c], gC = sG[(C - 1) * LK + c];
+          float gi[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) gi[e] = sG[(p + 4 * g4 + e) * LK + c];
+          float4v q2 = {0.f, 0.f, 0.f, 0.f}, f1 = q2, k1 = q2, f2 = q2;
+          if constexpr (TW > 0) {
+            mm2r<C>(q2, f1, [&](int k) { return row4(sdP + (p + ln) * LC + k); },
+                    [&](int k) { return row4(sB + (p + ln) * LC + k); },
+                    [&](int k) {
+                      const float4v kv = col4(sK + k * LK + c, LK), gv = col4(sG + k * LK + c, LK);
+                      return float4v{kv[0] * __expf(gp - gv[0]), kv[1] * __expf(gp - gv[1]),
+                                     kv[2] * __expf(gp - gv[2]), kv[3] * __expf(gp - gv[3])};
+                    },
+                    g4, 0, TW);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float f = __expf(gi[e] - gp);
+              q2[e] *= f;
+              f1[e] *= f;
+            }
+          }
+          if constexpr (TW < 3) {
+#pragma unroll
+            for (int k0 = 16 * (TW + 1); k0 < C; k0 += 16) {
+              const int k = k0 + 4 * g4;
+              const float4v gv = col4(sG + k * LK + c, LK), qv = col4(sQ + k * LK + c, LK);
+              const float4v kv = col4(sK + k * LK + c, LK) * row4(sb + k);
+              const float4v x1 = col4(sdP + k * LC + p + ln, LC), x2 = col4(sB + k * LC + p + ln, LC);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float f = __expf(gv[e] - gl);
+                k1 = mma(x1[e], qv[e] * f, k1);
+                f2 = mma(x2[e], kv[e] * f, f2);
+              }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float f = __expf(gl - gi[e]);
+              k1[e] *= f;
+              f2[e] *= f;
+            }
+          }
+          // the diagonal block: masked entries are zero, and their factor is clamped to 1
+#pragma unroll
+          for (int jq = 0; jq < 16; jq += 4) {
+            float4v xp[4], xb[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              xp[e] = row4(sdP + (p + 4 * g4 + e) * LC + p + jq);
+              xb[e] = row4(sB + (p + 4 * g4 + e) * LC + p + jq);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const float kj = sK[(p + jq + u) * LK + c], gj = sG[(p + jq + u) * LK + c];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float f = kj * __expf(fminf(gi[e] - gj, 0.f));
+                q2[e] = __builtin_fmaf(xp[e][u], f, q2[e]);
+                f1[e] = __builtin_fmaf(xb[e][u], f, f1[e]);
+              }
+            }
+          }
+#pragma unroll
+          for (int ii = 0; ii < 16; ++ii) {
+            const int i = p + ii;
+            const float qi = sQ[i * LK + c], ki = sK[i * LK + c] * sb[i], gv = sG[i * LK + c];
+            const float4v xp = row4(sdP + i * LC + p + 4 * g4), xb = row4(sB + i * LC + p + 4 * g4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float f = __expf(fminf(gv - gi[e], 0.f));
+              k1[e] = __builtin_fmaf(xp[e], qi * f, k1[e]);
+              f2[e] = __builtin_fmaf(xb[e], ki * f, f2[e]);
+            }
+          }
+          float kd = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = p + 4 * g4 + e;
+            const float eg = __expf(gi[e]), bt = sb[t];
+            const float dq = __builtin_fmaf(eg, Q1[ct][e], q2[e]);
+            const float f1m = __builtin_fmaf(-eg, ES[ct][e], f1[e]);   // (B k)_t - e^gamma_t o (E S0)_t
+            const float d4 = __expf(gC - gi[e]) * UD[ct][e];
+            const float g1 = k1[e] + d4 + f2[e];
+            dQa[ct][e] += dq;
+            dKa[ct][e] += __builtin_fmaf(bt, f1m, g1);
+            const float qv = sQ[t * LK + c], kv = sK[t * LK + c];
+            gpk[ct][e] = qv * dq - kv * g1 + kv * bt * f1m;
+            bp[e] += kv * f1m;
+            kd = __builtin_fmaf(kv, d4, kd);
+          }
+          kdx[ct] = kd;
+          asm volatile("" ::: "memory");
+        }
+      };
+      switch (tw) {
+        case 0: products(std::integral_constant<int, 0>{}); break;
+        case 1: products(std::integral_constant<int, 1>{}); break;
+        case 2: products(std::integral_constant<int, 2>{}); break;
+        default: products(std::integral_constant<int, 3>{}); break;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bp[e] = group_sum<16>(bp[e]);
+      if (ln == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sBet[hw * C + 16 * tw + 4 * g4 + e] = bp[e];
+      }
+#pragma unroll
+      for (int ct = 0; ct < HCT; ++ct) {   // sum of k o dk4 over the wave's tokens, per channel
+        float x = kdx[ct];
+        x += __shfl_xor(x, 16, 64);
+        x += __shfl_xor(x, 32, 64);
+        if (g4 == 0) sKd[tw * DK + 16 * (ct0 + ct) + ln] = x;
+      }
+      lds_barrier();   // the products' reads of the masked matrices are done
+#pragma unroll
+      for (int ct = 0; ct < HCT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sGp[(16 * tw + 4 * g4 + e) * LK + 16 * (ct0 + ct) + ln] = gpk[ct][e];
+      lds_barrier();
+      // dg_tc = sum over the chunk's tokens s >= t of the gradient of gamma_sc; the last
+      // token also carries <dS_C, S_C>_c = e^gamma_Cc <dS_C, S0>_c + sum_j k_jc dk4_jc
+      for (int c = tid; c < DK; c += NT) {
+        float sd = 0.f, kd = 0.f;
+        for (int u = 0; u < G::NW; ++u) sd += sSd[u * DK + c];
+        for (int u = 0; u < 4; ++u) kd += sKd[u * DK + c];
+        float s = __builtin_fmaf(__expf(sG[(C - 1) * LK + c]), sd, kd);
+        for (int t = C - 1; t >= 0; --t) {
+          s += sGp[t * LK + c];
+          if (t < len) a.dg[((row0 + t) * Hv + h) * DK + c] = s;
+        }
+      }
+      if (w == G::NW - 1) {
+        float y = sBet[lane] + sBx[lane];
+#pragma unroll
+        for (int u = 1; u < NH; ++u) y += sBet[u * C + lane];
+        if (lane < len) a.dbeta[(row0 + lane) * Hv + h] = y;
+      }
+    } else {
+      lds_barrier();
+      // M o dP and B = M o dA = -(M o E U^T) into LDS (over the slices' space)
+#pragma unroll
+      for (int J = 0; J < HJ; ++J) {
+        const int j = 16 * (J0 + J) + ln;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * tw + 4 * g4 + e;
+          const float m = i >= j ? __expf(sg[i] - sg[j]) : 0.f;
+          sdP[i * LC + j] = m * dPa[J][e];
+          sB[i * LC + j] = i > j ? -m * dAa[J][e] : 0.f;
+        }
+      }
+      // E . v (eight threads per token) and <dS_C, S0> over the workgroup
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const float x = group_sum<8>(dbx[i]);
+        if ((tid & 7) == 0) sBx[vtok(i)] = x;
+      }
+      sdot = group_sum<64>(sdot);
+      if (lane == 0) sRed[G::NW + w] = sdot;   // one slot per wave: a fixed order of the sum
+      lds_barrier();
+      float gp[4] = {0.f, 0.f, 0.f, 0.f}, bp[4] = {0.f, 0.f, 0.f, 0.f}, cp = 0.f;
+      // M o dP and B are zero above the diagonal (B on it too): token block TW's rows
+      // need the key blocks up to TW, its columns the token blocks from TW (the tiles
+      // above the diagonal are never read).  One copy of the products per TW, so
+      // that every range is fixed at compile time.
+      auto products = [&](auto TWc) {
+        constexpr int TW = decltype(TWc)::value;
+#pragma unroll
+        for (int ct = 0; ct < HCT; ++ct) {
+          const int c = 16 * (ct0 + ct) + ln;
+          float4v q2 = {0.f, 0.f, 0.f, 0.f}, k1 = q2, f1 = q2, f2 = q2;
+          if constexpr (ND) {   // B = 0 without the delta correction
+            mmr<C>(q2, [&](int k) { return row4(sdP + (16 * TW + ln) * LC + k); },
+                   [&](int k) { return col4(sK + k * LK + c, LK); }, g4, 0, TW + 1);
+          } else {
+            mm2r<C>(q2, f1, [&](int k) { return row4(sdP + (16 * TW + ln) * LC + k); },
+                    [&](int k) { return row4(sB + (16 * TW + ln) * LC + k); },
+                    [&](int k) { return col4(sK + k * LK + c, LK); }, g4, 0, TW + 1);
+          }
+          mmr<C>(k1, [&](int k) { return col4(sdP + k * LC + 16 * TW + ln, LC); },
+                 [&](int k) { return col4(sQ + k * LK + c, LK); }, g4, TW, 4);
+          if constexpr (!ND)
+            mmr<C>(f2, [&](int k) { return col4(sB + k * LC + 16 * TW + ln, LC) * row4(sb + k); },
+                   [&](int k) { return col4(sK + k * LK + c, LK); }, g4, TW, 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = 16 * TW + 4 * g4 + e;
+            const float eg = sEg[t], bt = sb[t];
+            const float dq = __builtin_fmaf(eg, Q1[ct][e], q2[e]);
+            const float f1m = __builtin_fmaf(-eg, ES[ct][e], f1[e]);   // (B k)_t - e^gamma_t (E S0)_t
+            const float d4 = sEc[t] * UD[ct][e];
+            const float g1 = k1[e] + d4 + f2[e];
+            dQa[ct][e] += dq;
+            dKa[ct][e] += __builtin_fmaf(bt, f1m, g1);
+            const float qv = sQ[t * LK + c], kv = sK[t * LK + c];
+            gp[e] += qv * dq - kv * g1 + kv * bt * f1m;
+            bp[e] += kv * f1m;
+            cp = __builtin_fmaf(kv, d4, cp);
+          }
+          // the next tile reads its operands again rather than keep them in registers
+          asm volatile("" ::: "memory");
+        }
+      };
+      switch (tw) {
+        case 0: products(std::integral_constant<int, 0>{}); break;
+        case 1: products(std::integral_constant<int, 1>{}); break;
+        case 2: products(std::integral_constant<int, 2>{}); break;
+        default: products(std::integral_constant<int, 3>{}); break;
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sGam[hw * C + 16 * tw + 4 * g4 + e] = gp[e];
-        sBet[hw * C + 16 * tw + 4 * g4 + e] = bp[e];
+        gp[e] = group_sum<16>(gp[e]);
+        bp[e] = group_sum<16>(bp[e]);
       }
-    }
-    cp = group_sum<64>(cp);
-    if (lane == 0) sRed[w] = cp;
-    lds_barrier();
-    if (w == 0) {
-      // dg_t = sum over the chunk's tokens i >= t of the gradient of gamma_i; the
-      // last token also carries <dS_C, S_C> = e^gamma_C <dS_C, S0> + sum_j k_j . dk4_j
-      const int t = C - 1 - lane;
-      float x = sGam[t], y = sBet[t] + sBx[t];
+      if (ln == 0) {
 #pragma unroll
-      for (int u = 1; u < NH; ++u) x += sGam[u * C + t], y += sBet[u * C + t];
-      if (t == C - 1) {
-        float c4 = 0.f, sd = 0.f;
-#pragma unroll
-        for (int u = 0; u < G::NW; ++u) c4 += sRed[u], sd += sRed[G::NW + u];
-        x += __builtin_fmaf(sEg[C - 1], sd, c4);
+        for (int e = 0; e < 4; ++e) {
+          sGam[hw * C + 16 * tw + 4 * g4 + e] = gp[e];
+          sBet[hw * C + 16 * tw + 4 * g4 + e] = bp[e];
+        }
       }
-      const float s = wave_prefix_sum(x);
-      if (t < len) {
-        a.dg[(row0 + t) * Hv + h] = s;
-        a.dbeta[(row0 + t) * Hv + h] = y;
+      cp = group_sum<64>(cp);
+      if (lane == 0) sRed[w] = cp;
+      lds_barrier();
+      if (w == 0) {
+        // dg_t = sum over the chunk's tokens i >= t of the gradient of gamma_i; the
+        // last token also carries <dS_C, S_C> = e^gamma_C <dS_C, S0> + sum_j k_j . dk4_j
+        const int t = C - 1 - lane;
+        float x = sGam[t], y = sBet[t] + sBx[t];
+#pragma unroll
+        for (int u = 1; u < NH; ++u) x += sGam[u * C + t], y += sBet[u * C + t];
+        if (t == C - 1) {
+          float c4 = 0.f, sd = 0.f;
+#pragma unroll
+          for (int u = 0; u < G::NW; ++u) c4 += sRed[u], sd += sRed[G::NW + u];
+          x += __builtin_fmaf(sEg[C - 1], sd, c4);
+        }
+        const float s = wave_prefix_sum(x);
+        if (t < len) {
+          a.dg[(row0 + t) * Hv + h] = s;
+          a.dbeta[(row0 + t) * Hv + h] = y;
+        }
       }
     }
   }
@@ -988,14 +1403,19 @@ __global__ __launch_bounds__((GradCfg<TQ, DK>::NT)) void cb_grads_kernel(CbArgs 
     }
 }
 
-template <typename TQ, int DK>
+template <typename TQ, int DK, bool KEY>
 struct CbSmem {
   static constexpr int LK = DK + 4;
   static constexpr int QK = PassCfg<TQ, DK>::LK * (int)sizeof(TQ), LS = DK + 4;
-  static constexpr int fwd = C * QK + (C * LC + R * LS + 2 * R * LC + 3 * C) * 4;
-  static constexpr int bwd = 2 * C * QK + (2 * C * LC + C * LR + R * LS + 2 * R * LC + 3 * C) * 4;
-  static constexpr int prep = (prep_region(DK) + C * LC + 2 * C) * 4;
-  static constexpr int grads = GradCfg<TQ, DK>::smem;
+  // the key gate's passes hold two fp32 [C][dk] operands in place of the rows of k
+  // (and q), and e^gamma_C per channel
+  static constexpr int OP1 = KEY ? 2 * C * LS * 4 : C * QK, OP2 = KEY ? 2 * C * LS * 4 : 2 * C * QK;
+  static constexpr int EC = KEY ? DK : 0;
+  static constexpr int fwd = OP1 + (C * LC + R * LS + 2 * R * LC + 3 * C + EC) * 4;
+  static constexpr int bwd = OP2 + (2 * C * LC + C * LR + R * LS + 2 * R * LC + 3 * C + EC) * 4;
+  static constexpr int prep = KEY ? (3 * C * LK + 2 * C * LC + C + 4 * 16 * LX) * 4
+                                  : (prep_region(DK) + C * LC + 2 * C) * 4;
+  static constexpr int grads = GradCfg<TQ, DK, KEY>::smem;
 };
 
 template <typename F>
@@ -1004,8 +1424,9 @@ hipError_t set_smem(F *kern, int bytes) {
 }
 
 // The workspace of one call: how many segments, and where each array starts.
-// Floats per (batch, value head): T, gamma, beta for every chunk; P^T, S0,
-// dS_C, U, E for the chunks of one segment.  One segment is the fastest; with
+// Floats per (batch, value head): T, gamma, beta for every chunk (the key
+// gate: gamma [C][dk], and K o e^gamma, Q o e^gamma, K o e^(gamma_C - gamma)
+// too); P^T, S0, dS_C, U, E for the chunks of one segment.  One segment is the fastest; with
 // more, a forward pass over the chunks before the last segment first keeps
 // the states at the segment starts, and each segment then runs its own
 // forward pass.
@@ -1013,7 +1434,7 @@ hipError_t set_smem(F *kern, int bytes) {
 struct CbPlan {
   int nc, nseg, ncs;
   size_t units, sunits;   // (batch, value head, chunk) for all chunks and for one segment
-  size_t f_T, f_g, f_b, f_Sseg, f_P, f_S0, f_dS, f_U, f_E, floats;
+  size_t f_T, f_g, f_b, f_Kh, f_Qh, f_Kt, f_Sseg, f_P, f_S0, f_dS, f_U, f_E, floats;
   CbPlan(const Shape &sh, int want) {
     nc = (sh.T + C - 1) / C;
     ncs = (nc + want - 1) / want;
@@ -1021,10 +1442,14 @@ struct CbPlan {
     const size_t bh = (size_t)sh.B * sh.Hv, st = (size_t)sh.dv * sh.dk, cv = (size_t)C * sh.dv;
     units = bh * nc;
     sunits = bh * ncs;
+    const size_t ck = sh.key_gate ? (size_t)C * sh.dk : 0;   // a key gate's [C][dk] arrays
     size_t o = 0;
     f_T = o, o += units * C * C;
-    f_g = o, o += units * C;
+    f_g = o, o += sh.key_gate ? units * ck : units * C;
     f_b = o, o += units * C;
+    f_Kh = o, o += units * ck;
+    f_Qh = o, o += units * ck;
+    f_Kt = o, o += units * ck;
     f_Sseg = o, o += nseg > 1 ? bh * nseg * st : 0;
     f_P = o, o += sunits * C * C;
     f_S0 = o, o += sunits * st;
@@ -1050,39 +1475,44 @@ inline CbPlan plan_for(const Shape &sh, size_t bytes) {
   return best;
 }
 
-template <typename TQ, typename TG, int DK>
+template <typename TQ, typename TG, int DK, bool KEY>
 hipError_t launch_cb_t(const Shape &sh, const CbPlan &pl, CbArgs a, const float *dST, hipStream_t st) {
-  using Sm = CbSmem<TQ, DK>;
-  constexpr int NTP = PassCfg<TQ, DK>::NT, NTG = GradCfg<TQ, DK>::NT;
-  static_assert(Sm::bwd <= 160 * 1024 && Sm::grads <= 160 * 1024 && Sm::prep <= 160 * 1024, "LDS");
+  using Sm = CbSmem<TQ, DK, KEY>;
+  constexpr int NTP = PassCfg<TQ, DK>::NT, NTG = GradCfg<TQ, DK, KEY>::NT;
+  static_assert(Sm::fwd <= 160 * 1024 && Sm::bwd <= 160 * 1024 && Sm::grads <= 160 * 1024 &&
+                    Sm::prep <= 160 * 1024,
+                "LDS");
+  constexpr auto prep_k = KEY ? cb_prep_key_kernel<TQ, TG, DK> : cb_prep_kernel<TQ, TG, DK>;
   hipError_t e;
-  if ((e = set_smem(cb_prep_kernel<TQ, TG, DK>, Sm::prep)) != hipSuccess) return e;
-  if ((e = set_smem(cb_fwd_kernel<TQ, DK>, Sm::fwd)) != hipSuccess) return e;
-  if ((e = set_smem(cb_bwd_kernel<TQ, DK>, Sm::bwd)) != hipSuccess) return e;
-  if ((e = set_smem(cb_grads_kernel<TQ, TG, DK, false>, Sm::grads)) != hipSuccess) return e;
-  if ((e = set_smem(cb_grads_kernel<TQ, TG, DK, true>, Sm::grads)) != hipSuccess) return e;
+  if ((e = set_smem(prep_k, Sm::prep)) != hipSuccess) return e;
+  if ((e = set_smem(cb_fwd_kernel<TQ, DK, KEY>, Sm::fwd)) != hipSuccess) return e;
+  if ((e = set_smem(cb_bwd_kernel<TQ, DK, KEY>, Sm::bwd)) != hipSuccess) return e;
+  if ((e = set_smem(cb_grads_kernel<TQ, TG, DK, false, KEY>, Sm::grads)) != hipSuccess) return e;
+  if constexpr (!KEY)
+    if ((e = set_smem(cb_grads_kernel<TQ, TG, DK, true, false>, Sm::grads)) != hipSuccess) return e;
   const dim3 pass(sh.dv / R, sh.Hv, sh.B);
   auto prep = [&](int flags) {
     a.flags = flags;
-    hipLaunchKernelGGL((cb_prep_kernel<TQ, TG, DK>), dim3(a.c1 - a.c0, sh.Hk, sh.B), dim3(256), Sm::prep, st, a);
+    hipLaunchKernelGGL(prep_k, dim3(a.c1 - a.c0, sh.Hk, sh.B), dim3(256), Sm::prep, st, a);
     return hipGetLastError();
   };
   auto fwd = [&](int flags) {
     a.flags = flags;
-    hipLaunchKernelGGL((cb_fwd_kernel<TQ, DK>), pass, dim3(NTP), Sm::fwd, st, a);
+    hipLaunchKernelGGL((cb_fwd_kernel<TQ, DK, KEY>), pass, dim3(NTP), Sm::fwd, st, a);
     return hipGetLastError();
   };
   auto segment = [&]() {   // the chunks [c0, c1) of one segment, from their P^T to their gradients
     hipError_t r = fwd(0);
     if (r != hipSuccess) return r;
-    hipLaunchKernelGGL((cb_bwd_kernel<TQ, DK>), pass, dim3(NTP), Sm::bwd, st, a);
+    hipLaunchKernelGGL((cb_bwd_kernel<TQ, DK, KEY>), pass, dim3(NTP), Sm::bwd, st, a);
     if ((r = hipGetLastError()) != hipSuccess) return r;
-    if (a.nd)
-      hipLaunchKernelGGL((cb_grads_kernel<TQ, TG, DK, true>), dim3(a.c1 - a.c0, sh.Hk, sh.B), dim3(NTG), Sm::grads, st,
-                         a);
+    const dim3 grid(a.c1 - a.c0, sh.Hk, sh.B);
+    if constexpr (KEY)
+      hipLaunchKernelGGL((cb_grads_kernel<TQ, TG, DK, false, true>), grid, dim3(NTG), Sm::grads, st, a);
+    else if (a.nd)
+      hipLaunchKernelGGL((cb_grads_kernel<TQ, TG, DK, true, false>), grid, dim3(NTG), Sm::grads, st, a);
     else
-      hipLaunchKernelGGL((cb_grads_kernel<TQ, TG, DK, false>), dim3(a.c1 - a.c0, sh.Hk, sh.B), dim3(NTG), Sm::grads,
-                         st, a);
+      hipLaunchKernelGGL((cb_grads_kernel<TQ, TG, DK, false, false>), grid, dim3(NTG), Sm::grads, st, a);
     return hipGetLastError();
   };
   a.nseg = pl.nseg;
@@ -1111,22 +1541,29 @@ hipError_t launch_cb_t(const Shape &sh, const CbPlan &pl, CbArgs a, const float 
 
 template <typename TQ, typename TG>
 hipError_t launch_cb_d(const Shape &sh, const CbPlan &pl, const CbArgs &a, const float *dST, hipStream_t st) {
+  const bool key = sh.key_gate;
   switch (sh.dk) {
-    case 32: return launch_cb_t<TQ, TG, 32>(sh, pl, a, dST, st);
-    case 64: return launch_cb_t<TQ, TG, 64>(sh, pl, a, dST, st);
-    case 128: return launch_cb_t<TQ, TG, 128>(sh, pl, a, dST, st);
+    case 32:
+      return key ? launch_cb_t<TQ, TG, 32, true>(sh, pl, a, dST, st)
+                 : launch_cb_t<TQ, TG, 32, false>(sh, pl, a, dST, st);
+    case 64:
+      return key ? launch_cb_t<TQ, TG, 64, true>(sh, pl, a, dST, st)
+                 : launch_cb_t<TQ, TG, 64, false>(sh, pl, a, dST, st);
+    case 128:
+      return key ? launch_cb_t<TQ, TG, 128, true>(sh, pl, a, dST, st)
+                 : launch_cb_t<TQ, TG, 128, false>(sh, pl, a, dST, st);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-size_t chunk_backward_workspace(const Shape &sh, size_t cap) { return plan_for(sh, cap).bytes(); }
+size_t backward_workspace(const Shape &sh, size_t cap) { return plan_for(sh, cap).bytes(); }
 
-hipError_t launch_chunk_backward(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
-                                 const void *beta, const float *S0, const float *dO, const float *dST, float *dq,
-                                 float *dk, float *dv, float *dg, float *dbeta, float *dS0, void *ws,
-                                 size_t ws_bytes, hipStream_t st) {
+hipError_t launch_backward(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
+                           const void *beta, const float *S0, const float *dO, const float *dST, float *dq,
+                           float *dk, float *dv, float *dg, float *dbeta, float *dS0, void *ws, size_t ws_bytes,
+                           hipStream_t st) {
   const CbPlan pl = plan_for(sh, ws_bytes);
   CbArgs a = {};
   a.q = q;
@@ -1158,6 +1595,9 @@ hipError_t launch_chunk_backward(const Shape &sh, const void *q, const void *k, 
   a.dSC = w + pl.f_dS;
   a.Um = w + pl.f_U;
   a.Em = w + pl.f_E;
+  a.Kh = w + pl.f_Kh;
+  a.Qh = w + pl.f_Qh;
+  a.Kt = w + pl.f_Kt;
   if (sh.qkv == DType::F32)
     return sh.gate_t == DType::F32 ? launch_cb_d<float, float>(sh, pl, a, dST, st)
                                    : launch_cb_d<float, bf16_t>(sh, pl, a, dST, st);

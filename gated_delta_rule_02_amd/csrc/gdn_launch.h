@@ -86,25 +86,18 @@ hipError_t launch_output_gate(const float *o, const void *z, DType zt, const flo
 
 // Backward of the recurrence: dq, dk, dv, dg, dbeta, dS0 (fp32) from dO
 // [B,T,Hv,dv] and dST (or null).  dk in {32, 64, 128}, dv a multiple of 32.
-// The head gate takes the chunked backward (launch_chunk_backward), the
-// key-channel gate the token-by-token backward over kept states.
-// backward_workspace(sh, cap): the bytes of the fastest plan whose workspace
-// fits in cap (for the head gate, the fewest segments; the smallest plan if
-// none fits; the key-channel gate has one size).  launch_backward runs the
-// fastest plan that fits in ws_bytes.
+// Chunked, both gates: per chunk of 64 tokens, the state before it and the
+// state gradient after it, U and E, T and P^T (the key-channel gate: also
+// gamma [C][dk] and the decayed k and q) in the workspace, for the whole
+// sequence or one segment of it at a time.  backward_workspace(sh, cap): the
+// bytes of the fastest plan whose workspace fits in cap (the fewest segments;
+// the smallest plan if none fits).  launch_backward runs the fastest plan
+// that fits in ws_bytes.
 size_t backward_workspace(const Shape &sh, size_t cap = ~(size_t)0);
 hipError_t launch_backward(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
                            const void *beta, const float *S0, const float *dO, const float *dST, float *dq,
                            float *dk, float *dv, float *dg, float *dbeta, float *dS0, void *ws, size_t ws_bytes,
                            hipStream_t st);
-// The chunked backward (head gate): per chunk of 64 tokens, the state before
-// it and the state gradient after it, U and E, T and P^T in the workspace,
-// for the whole sequence or one segment of it at a time.
-size_t chunk_backward_workspace(const Shape &sh, size_t cap);
-hipError_t launch_chunk_backward(const Shape &sh, const void *q, const void *k, const void *v, const void *g,
-                                 const void *beta, const float *S0, const float *dO, const float *dST, float *dq,
-                                 float *dk, float *dv, float *dg, float *dbeta, float *dS0, void *ws,
-                                 size_t ws_bytes, hipStream_t st);
 
 // Internal chunk length the fp32 kernels use for a requested chunk and dk.
 int chunk_f32_internal(int chunk, int dk);

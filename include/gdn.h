@@ -389,18 +389,17 @@ gdn_status gdn_decode_step_conv(const gdn_desc *d, int32_t x_dtype, const void *
  * gdn_bwd -- the backward of the recurrence: the gradients of
  * L = sum_t <dO_t, o_t> + <dS_T, S_T> with respect to q, k, v, g, beta and S0
  * (the first-order backward of "Source notes", Linear attention, row kda).
- *  - Per-head gate: in chunks of 64 tokens (the exact chunkwise form of the
- *    "SinkProbe" page).  A forward pass keeps the state before every chunk
- *    and the chunk's U = (I + A)^-1 X; a backward pass runs the state
- *    gradient over the chunks in reverse, keeping it after every chunk with
- *    E = (I + A)^-T dU; the other gradients are then products of these per
- *    chunk, on the fp32 matrix cores.  The chunked form assumes decays
- *    (g <= 0): factors e^(gamma_i - gamma_j) with i >= j stay <= 1.
- *  - Per-key-channel gate: token by token; the forward recurrence is run again
- *    to keep the state before every fourth token, then the tokens are run
- *    backwards in blocks of four, the states inside a block recomputed from
- *    the kept one by the same arithmetic.
- * All arithmetic is fp32.
+ * In chunks of 64 tokens (the exact chunkwise form of the "SinkProbe" page),
+ * both gates.  A forward pass keeps the state before every chunk and the
+ * chunk's U = (I + A)^-1 X; a backward pass runs the state gradient over the
+ * chunks in reverse, keeping it after every chunk with E = (I + A)^-T dU; the
+ * other gradients are then products of these per chunk, on the fp32 matrix
+ * cores.  The chunked form assumes decays (g <= 0): factors e^(gamma_i -
+ * gamma_j) with i >= j stay <= 1.  With the per-key-channel gate every decay
+ * acts channel by channel; the masked products over a chunk's tokens are
+ * taken in 16-token blocks, through a reference token between the two off
+ * the diagonal and term by term on it, so no factor exceeds 1 however strong
+ * the decay.  All arithmetic is fp32.
  *   q, k, v, g, beta, S0   the forward's inputs, as for gdn_fwd_chunked (S0 NULL: zeros)
  *   dO     device fp32 [B,T,Hv,dv]: the gradient of o
  *   dS_T   device fp32 [B,Hv,dv,dk] or NULL (zeros): the gradient of S_T
@@ -410,14 +409,15 @@ gdn_status gdn_decode_step_conv(const gdn_desc *d, int32_t x_dtype, const void *
  *   dbeta  device out fp32 [B,T,Hv]
  *   dS0    device out fp32 [B,Hv,dv,dk]
  *   workspace   device scratch, 16-byte aligned, of workspace_bytes bytes.
- *     Per-key-channel gate: gdn_bwd_workspace_bytes(d) bytes (the kept states,
- *     B Hv ceil(T/4) dv dk fp32, and partial sums).
- *     Per-head gate: the call runs the fastest plan whose workspace fits in
- *     workspace_bytes.  gdn_bwd_workspace_bytes(d) is the fastest plan's
- *     (one segment): per (batch, value head, chunk of 64) 2 (64 64 + 64 +
- *     dv dk + 64 dv) fp32.  With less, the sequence runs in segments of
- *     consecutive chunks, last segment first: T, gamma and beta are kept for
- *     every chunk (64 64 + 2 64 fp32 per (batch, value head, chunk)), the
+ *     The call runs the fastest plan whose workspace fits in workspace_bytes.
+ *     gdn_bwd_workspace_bytes(d) is the fastest plan's (one segment): per
+ *     (batch, value head, chunk of 64) 2 (64 64 + 64 + dv dk + 64 dv) fp32
+ *     with the per-head gate; the per-key-channel gate keeps gamma as
+ *     [64][dk] in place of [64], and K o e^gamma, Q o e^gamma and
+ *     K o e^(gamma_C - gamma), [64][dk] each, too.  With less, the sequence
+ *     runs in segments of consecutive chunks, last segment first: T, gamma
+ *     and beta (and the decayed k and q) are kept for every chunk (64 64 +
+ *     2 64 fp32 per (batch, value head, chunk) with the per-head gate), the
  *     other arrays (64 64 + 2 dv dk + 2 64 dv fp32) for one segment's chunks,
  *     and the state at each segment start (B Hv dv dk fp32 per segment).  A
  *     forward pass over the chunks before the last segment keeps those

@@ -370,12 +370,11 @@ def test_bwd_checks(L):
     # below the smallest plan (one chunk per segment) the call is refused
     smallest = L.gdn_bwd_workspace_bytes_within(ctypes.byref(dbig), 0)
     assert 0 < smallest < four
-    # key-channel gate: the state before every 4th token (B Hv ceil(T / 4) dv dk fp32,
-    # 256-byte rounded), then the partial sums per 32 state rows and token
-    hist = 2 * 6 * 25 * 128 * 128 * 4
+    # key-channel gate: as the head gate, with gamma [64][dk] per chunk in place of [64],
+    # and K o e^gamma, Q o e^gamma, K o e^(gamma_C - gamma), [64][dk] each, per chunk
     dkey = desc(qkv_dtype=gdn.F32, gate_dtype=gdn.F32, gate=gdn.GATE_KEY_CHANNEL)
-    assert L.gdn_bwd_workspace_bytes(ctypes.byref(dkey)) == \
-        (hist + 255) // 256 * 256 + 2 * 6 * 4 * 100 * (3 * 128 + 1) * 4
+    assert L.gdn_bwd_workspace_bytes(ctypes.byref(dkey)) == 2 * 6 * 2 * (per_chunk - 64 + 4 * 64 * 128) * 4
+    assert L.gdn_bwd_workspace_bytes_within(ctypes.byref(dkey), 0) < L.gdn_bwd_workspace_bytes(ctypes.byref(dkey))
     assert L.gdn_bwd_workspace_bytes(ctypes.byref(desc(dk=16))) == 0
     assert L.gdn_bwd_workspace_bytes(ctypes.byref(desc(dv=48))) == 0
     # q, k, v, g, beta | S0 | dO | dS_T | dq, dk, dv, dg, dbeta, dS0 | workspace
@@ -389,7 +388,7 @@ def test_bwd_checks(L):
     assert L.gdn_bwd_workspace_bytes(ctypes.byref(knd)) == 0
     assert call(knd, nbytes=1 << 40) == 3
     assert call(d, nbytes=L.gdn_bwd_workspace_bytes_within(ctypes.byref(d), 0) - 1) == 5
-    assert call(dkey, nbytes=L.gdn_bwd_workspace_bytes(ctypes.byref(dkey)) - 1) == 5
+    assert call(dkey, nbytes=L.gdn_bwd_workspace_bytes_within(ctypes.byref(dkey), 0) - 1) == 5
     bad = list(p)
     bad[8] = None
     assert call(d, bad) == 1                             # dq missing

@@ -75,6 +75,84 @@ def test_bwd_bf16_key_gate():
     run_case(KDA_PREFILL.with_(B=1, T=100, Hk=2, Hv=2), "bwd bf16 key gate")
 
 
+@pytest.mark.parametrize("dk,dv,grp", [(32, 64, 2), (64, 32, 1), (128, 96, 3)])
+def test_bwd_key_gate_shapes(dk, dv, grp):
+    """Per-key-channel gate, fp32, each head dim, with one to three value
+    heads per key head, over several chunks and a ragged last one."""
+    run_case(TINY_F32.with_(B=2, T=150, Hk=2, Hv=2 * grp, dk=dk, dv=dv, gate="key"),
+             "bwd key gate d %d/%d groups of %d" % (dk, dv, grp), seed=dk + grp)
+
+
+def test_bwd_key_gate_strong_decay():
+    """Per-key-channel gate with g = logsigmoid(N(-4, 1)), about -4 per token
+    and channel: the decay between two tokens of one 16-token block reaches
+    e^-60 and more, far past fp32's range, so every decay factor must be
+    formed between tokens in order (each at most 1)."""
+    run_case(KDA_PREFILL.with_(B=1, T=200, Hk=2, Hv=2, g_mu=-4.0), "bwd key gate strong decay", seed=11)
+
+
+@pytest.mark.parametrize("T", [1, 64, 65])
+def test_bwd_key_gate_chunk_edges(T):
+    """Per-key-channel gate: one token, exactly one chunk, one chunk and a token."""
+    run_case(KDA_PREFILL.with_(B=2, T=T, Hk=1, Hv=1), "bwd key gate T=%d" % T, seed=T)
+
+
+def test_bwd_key_gate_segments():
+    """Per-key-channel gate with workspaces too small for one segment: the
+    segments give the one-segment result bit for bit, and the oracle's."""
+    wl = KDA_PREFILL.with_(B=2, T=700, Hk=2, Hv=4)
+    inp = make_prefill(wl)
+    r = np.random.default_rng(919)
+    S0 = np.ascontiguousarray(r.normal(0, 0.05, (wl.B, wl.Hv, wl.dv, wl.dk)), dtype=np.float32)
+    dO = np.ascontiguousarray(r.standard_normal((wl.B, wl.T, wl.Hv, wl.dv)), dtype=np.float32)
+    dST = np.ascontiguousarray(r.standard_normal((wl.B, wl.Hv, wl.dv, wl.dk)), dtype=np.float32)
+    args = [to_torch(inp[n]) for n in ("q", "k", "v", "g", "beta")] + [to_torch(S0), to_torch(dO), to_torch(dST)]
+    one = gdn.bwd(*args)
+    full = gdn.lib().gdn_bwd_workspace_bytes(ctypes.byref(gdn.make_desc(
+        wl.B, wl.T, wl.Hk, wl.Hv, wl.dk, wl.dv, 64, gdn.BF16, gdn.BF16, gdn.GATE_KEY_CHANNEL)))
+    for cap in (full // 2, 0):
+        say("bwd key gate segments: workspace cap %d of %d bytes" % (cap, full))
+        seg = gdn.bwd(*args, workspace_cap=cap)
+        torch.cuda.synchronize()
+        for n in one:
+            assert torch.equal(one[n], seg[n]), "cap %d: %s differs from one segment" % (cap, n)
+    ref = oracle.backward(*(inp[n].f32() for n in ("q", "k", "v", "g", "beta")), S0.astype(np.float64), dO, dST)
+    for n in ("dq", "dk", "dv", "dg", "dbeta", "dS0"):
+        e = rel_inf(seg[n].cpu().numpy(), ref[n])
+        print("[parity] bwd key gate segments %s rel %.3e (bar 1e-4)" % (n, e), file=sys.stderr, flush=True)
+        assert e <= 1e-4, "%s error %.3e" % (n, e)
+
+
+def test_bwd_key_gate_full_size_sampled():
+    """Per-key-channel gate at its prefill workload's full size (B 2, T 8192,
+    32 heads, d 128, bf16 inputs), every chain on the GPU; the oracle
+    recomputes two sampled (batch, head) chains over the whole sequence."""
+    wl = KDA_PREFILL
+    inp = make_prefill(wl)
+    say("bwd key gate full size: B=%d T=%d H=%d d=128 bf16" % (wl.B, wl.T, wl.Hv))
+    r = np.random.default_rng(4343)
+    S0 = np.ascontiguousarray(r.normal(0, 0.05, (wl.B, wl.Hv, wl.dv, wl.dk)), dtype=np.float32)
+    dO = np.ascontiguousarray(r.standard_normal((wl.B, wl.T, wl.Hv, wl.dv)), dtype=np.float32)
+    dST = np.ascontiguousarray(r.standard_normal((wl.B, wl.Hv, wl.dv, wl.dk)), dtype=np.float32)
+    args = [to_torch(inp[n]) for n in ("q", "k", "v", "g", "beta")]
+    got = gdn.bwd(*args, to_torch(S0), to_torch(dO), to_torch(dST))
+    torch.cuda.synchronize()
+    got = {n: x.cpu().numpy() for n, x in got.items()}
+    del args
+    x = {n: inp[n].f32() for n in ("q", "k", "v", "g", "beta")}
+    for b, h in ((0, 0), (1, 31)):
+        bs, hs = slice(b, b + 1), slice(h, h + 1)
+        ref = oracle.backward(x["q"][bs, :, hs], x["k"][bs, :, hs], x["v"][bs, :, hs], x["g"][bs, :, hs],
+                              x["beta"][bs, :, hs], S0[bs, hs].astype(np.float64), dO[bs, :, hs], dST[bs, hs])
+        for n in ("dq", "dk", "dv", "dg", "dbeta", "dS0"):
+            mine = got[n][bs, hs] if n == "dS0" else got[n][bs, :, hs]
+            assert np.all(np.isfinite(mine)), "non-finite %s" % n
+            e = rel_inf(mine, ref[n])
+            print("[parity] bwd key gate 2x8192 batch %d head %d %s rel %.3e (bar 1e-4)" % (b, h, n, e),
+                  file=sys.stderr, flush=True)
+            assert e <= 1e-4, "batch %d head %d: %s error %.3e" % (b, h, n, e)
+
+
 def test_bwd_full_heads_long():
     """The backward at the prefill workload's head shape (16 key / 48 value
     heads, d 128, bf16 inputs) over T = 1024 tokens, on the GPU for every
