@@ -69,6 +69,12 @@ constexpr int LR = R + 4;
 // flags of a launch
 constexpr int kPrepT = 1, kPrepP = 2;   // prep: T, gamma, beta; P^T
 constexpr int kStatesOnly = 4;          // forward pass: only the states at segment starts
+// Per-key-channel gate: a 16-token block whose decay over its tokens, gamma at
+// its first token minus gamma at its last, is at most kWide in every channel
+// goes through the matrix cores with one reference token for the whole block
+// (one factor at most 1, the other at most e^kWide, finite however the
+// products are masked); a wider block is summed term by term.
+constexpr float kWide = 60.f;
 
 struct CbArgs {
   const void *q, *k, *v, *g, *beta;
@@ -118,27 +124,49 @@ __device__ __forceinline__ void mm(float4v &acc, const FA &fa, const FB &fb, int
   }
 }
 
+// Four consecutive input values as raw bits, and as fp32.
+template <typename TQ> struct Quad { using type = uint2; };
+template <> struct Quad<float> { using type = float4v; };
+template <typename TQ>
+__device__ __forceinline__ typename Quad<TQ>::type quad_load(const TQ *p) {
+  return *reinterpret_cast<const typename Quad<TQ>::type *>(p);
+}
+__device__ __forceinline__ float4v quad_f32(float4v x) { return x; }
+__device__ __forceinline__ float4v quad_f32(uint2 x, bf16_t) {
+  return float4v{__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xFFFF0000u), __uint_as_float(x.y << 16),
+                 __uint_as_float(x.y & 0xFFFF0000u)};
+}
+__device__ __forceinline__ float4v quad_f32(uint2 x, f16_t) {
+  const half4 h = __builtin_bit_cast(half4, x);
+  return float4v{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+}
+template <typename TQ>
+__device__ __forceinline__ float4v quad_to_f32(typename Quad<TQ>::type x) {
+  if constexpr (sizeof(TQ) == 4) return quad_f32(x);
+  else return quad_f32(x, TQ{});
+}
+
 // rows of a chunk of q or k (zeros past the sequence's end) into LDS, fp32 [C][DK + 4]
-// (a 256-thread workgroup; every load is issued before the first store)
+// (a 256-thread workgroup).  Every load is issued before the first is used: a row
+// past the end reads the chunk's last row in its place and is zeroed after, so that
+// no load sits in a branch of its own and waits there.
 template <typename TQ, int DK>
 __device__ __forceinline__ void load_rows(float *dst, const TQ *src, size_t row0, int stride, int len, int tid) {
   constexpr int LK = DK + 4, NU = C * DK / 8 / 256;
-  float x[NU][8];
+  typename Quad<TQ>::type x[NU][2];
 #pragma unroll
   for (int i = 0; i < NU; ++i) {
-    const int u = tid + 256 * i, t = u / (DK / 8), c = (u % (DK / 8)) * 8;
-    if (t < len) {
-      load8(src + (row0 + (size_t)t * stride) * DK + c, x[i]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
-    }
+    const int u = tid + 256 * i, t = min(u / (DK / 8), len - 1), c = (u % (DK / 8)) * 8;
+    const TQ *p = src + (row0 + (size_t)t * stride) * DK + c;
+    x[i][0] = quad_load(p);
+    x[i][1] = quad_load(p + 4);
   }
 #pragma unroll
   for (int i = 0; i < NU; ++i) {
     const int u = tid + 256 * i, t = u / (DK / 8), c = (u % (DK / 8)) * 8;
-    *reinterpret_cast<float4v *>(dst + t * LK + c) = float4v{x[i][0], x[i][1], x[i][2], x[i][3]};
-    *reinterpret_cast<float4v *>(dst + t * LK + c + 4) = float4v{x[i][4], x[i][5], x[i][6], x[i][7]};
+    const float4v z = {0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<float4v *>(dst + t * LK + c) = t < len ? quad_to_f32<TQ>(x[i][0]) : z;
+    *reinterpret_cast<float4v *>(dst + t * LK + c + 4) = t < len ? quad_to_f32<TQ>(x[i][1]) : z;
   }
 }
 
@@ -243,13 +271,12 @@ __global__ __launch_bounds__(256) void cb_prep_kernel(CbArgs a) {
   // the lane's q entries of token 16 w + ln as matrix-core operands (zeros past the end)
   float4v qa[DK / 16];
   {
-    const int t = 16 * w + ln;
+    const int t = 16 * w + ln, tc = min(t, len - 1);   // past the end: the last row, zeroed
+    typename Quad<TQ>::type qr[DK / 16];
 #pragma unroll
-    for (int kb = 0; kb < DK / 16; ++kb) {
-      float x[4] = {0.f, 0.f, 0.f, 0.f};
-      if (t < len) load4((const TQ *)a.q + ((row0 + t) * Hk + kh) * DK + 16 * kb + 4 * g4, x);
-      qa[kb] = float4v{x[0], x[1], x[2], x[3]};
-    }
+    for (int kb = 0; kb < DK / 16; ++kb) qr[kb] = quad_load((const TQ *)a.q + ((row0 + tc) * Hk + kh) * DK + 16 * kb + 4 * g4);
+#pragma unroll
+    for (int kb = 0; kb < DK / 16; ++kb) qa[kb] = t < len ? quad_to_f32<TQ>(qr[kb]) : float4v{0.f, 0.f, 0.f, 0.f};
   }
   __syncthreads();
   // K K^T and Q K^T of the key head, once for its value heads: wave w holds the
@@ -274,8 +301,9 @@ __global__ __launch_bounds__(256) void cb_prep_kernel(CbArgs a) {
     __syncthreads();   // the k rows (first head) or the previous head's T are read
     if (w == 0) {
       const TG *g = (const TG *)a.g, *be = (const TG *)a.beta;
-      const float gt = lane < len ? to_f32(g[(row0 + lane) * Hv + h]) : 0.f;
-      const float bt = lane < len ? to_f32(be[(row0 + lane) * Hv + h]) : 0.f;
+      const int tl = min(lane, len - 1);   // past the end: the last token's, zeroed
+      const TG gr = g[(row0 + tl) * Hv + h], br = be[(row0 + tl) * Hv + h];
+      const float gt = lane < len ? to_f32(gr) : 0.f, bt = lane < len ? to_f32(br) : 0.f;
       const float gm = wave_prefix_sum(gt);
       sg[lane] = gm;
       sb[lane] = bt;
@@ -310,11 +338,12 @@ __global__ __launch_bounds__(256) void cb_prep_kernel(CbArgs a) {
 // the key head: gamma [C][dk] (the prefix sums of g over the chunk, channel by
 // channel), beta, the decayed operands K o e^gamma, Q o e^gamma and
 // K o e^(gamma_C - gamma), A and P, P^T and T.  A_ij = beta_i sum_c k_ic k_jc
-// e^(gamma_ic - gamma_jc) and P_ij = sum_c q_ic k_jc e^(...): below the
-// diagonal 16 x 16 blocks, about the row block's first token p, as products
-// of (k_i o e^(gamma_i - gamma_p)) and (k_j o e^(gamma_p - gamma_j)), both
-// factors at most 1 (j < p <= i); the diagonal blocks term by term, each
-// factor e^(gamma_ic - gamma_jc) at most 1, so no decay overflows.
+// e^(gamma_ic - gamma_jc) and P_ij = sum_c q_ic k_jc e^(...): in 16 x 16
+// blocks about the row block's first token p, as products of
+// (k_i o e^(gamma_i - gamma_p)) and (k_j o e^(gamma_p - gamma_j)), both
+// factors at most 1 below the diagonal (j < p <= i) and the second at most
+// e^kWide on it; a diagonal block whose decay is wider in some channel is
+// summed term by term, each factor e^(gamma_ic - gamma_jc) at most 1.
 template <typename TQ, typename TG, int DK>
 __global__ __launch_bounds__(256) void cb_prep_key_kernel(CbArgs a) {
   constexpr int LK = DK + 4;
@@ -337,15 +366,22 @@ __global__ __launch_bounds__(256) void cb_prep_key_kernel(CbArgs a) {
     const size_t bh = (size_t)b * Hv + h, cn = gch(a, bh, n);
     __syncthreads();   // the rows are loaded, or the previous head's reads are done
     if (tid < DK) {
-      // gamma_tc = sum_{s <= t} g_sc over the chunk (zero past the end)
+      // gamma_tc = sum_{s <= t} g_sc over the chunk (zero past the end): every
+      // token's g requested first (past the end the last token's), then summed
+      TG x[C];
+#pragma unroll
+      for (int t = 0; t < C; ++t) x[t] = g[((row0 + min(t, len - 1)) * Hv + h) * DK + tid];
       float sum = 0.f;
-#pragma unroll 8
+#pragma unroll
       for (int t = 0; t < C; ++t) {
-        sum += t < len ? to_f32(g[((row0 + t) * Hv + h) * DK + tid]) : 0.f;
+        sum += t < len ? to_f32(x[t]) : 0.f;
         sG[t * LK + tid] = sum;
       }
     }
-    if (tid < C) sb[tid] = tid < len ? to_f32(be[(row0 + tid) * Hv + h]) : 0.f;
+    if (tid < C) {
+      const TG bx = be[(row0 + min(tid, len - 1)) * Hv + h];
+      sb[tid] = tid < len ? to_f32(bx) : 0.f;
+    }
     __syncthreads();
     if (doT) {
       float *gg = a.gam + cn * C * DK, *kh_ = a.Kh + cn * C * DK, *qh_ = a.Qh + cn * C * DK, *kt_ = a.Kt + cn * C * DK;
@@ -364,50 +400,74 @@ __global__ __launch_bounds__(256) void cb_prep_key_kernel(CbArgs a) {
       if (tid < C) a.bet[cn * C + tid] = sb[tid];
     }
     float *Ptg = a.Pt + sch(a, bh, n) * C * C;
-    // blocks (w, J < w): about token p = 16 w; the lane holds i = 16 w + 4 g4 + e, j = 16 J + ln
+    // blocks (w, J <= w): about token p = 16 w; the lane holds i = 16 w + 4 g4 + e, j = 16 J + ln.
+    // The diagonal block too unless its decay is wide in some channel.  Channels outer,
+    // so that the row side k_i o e^(gamma_i - gamma_p) is formed once for all J.
     const int p = 16 * w;
-    for (int J = 0; J < 4; ++J) {
-      const int j = 16 * J + ln;
-      float4v kk = {0.f, 0.f, 0.f, 0.f}, qk = kk;
-      if (J < w) {
-        for (int k = 0; k < DK; k += 16) {
-          const int kb = k + 4 * g4;
-          const float4v gi = row4(sG + (16 * w + ln) * LK + kb), gp = row4(sG + p * LK + kb);
-          const float4v gj = row4(sG + j * LK + kb);
-          const float4v ki = row4(sK + (16 * w + ln) * LK + kb), qi = row4(sQ + (16 * w + ln) * LK + kb);
-          const float4v kj = row4(sK + j * LK + kb);
+    float rng = 0.f;
+    for (int c = lane; c < DK; c += 64) rng = fmaxf(rng, sG[p * LK + c] - sG[(p + 15) * LK + c]);
+    const bool wide = __any(rng > kWide);
+    const int nb = wide ? w : w + 1;   // the blocks J < nb go through the matrix cores
+    float4v kk[4], qk[4];
+#pragma unroll
+    for (int J = 0; J < 4; ++J) kk[J] = qk[J] = float4v{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < DK; k += 16) {
+      const int kb = k + 4 * g4;
+      const float4v gi = row4(sG + (16 * w + ln) * LK + kb), gp = row4(sG + p * LK + kb);
+      const float4v ki = row4(sK + (16 * w + ln) * LK + kb), qi = row4(sQ + (16 * w + ln) * LK + kb);
+      float4v xk, xq;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float fi = __expf(gi[e] - gp[e]);
+        xk[e] = ki[e] * fi;
+        xq[e] = qi[e] * fi;
+      }
+#pragma unroll
+      for (int J = 0; J < 4; ++J)
+        if (J < nb) {
+          const int j = 16 * J + ln;
+          const float4v gj = row4(sG + j * LK + kb), kj = row4(sK + j * LK + kb);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float fi = __expf(gi[e] - gp[e]), y = kj[e] * __expf(gp[e] - gj[e]);
-            kk = mma(ki[e] * fi, y, kk);
-            qk = mma(qi[e] * fi, y, qk);
+            const float y = kj[e] * __expf(gp[e] - gj[e]);
+            kk[J] = mma(xk[e], y, kk[J]);
+            qk[J] = mma(xq[e], y, qk[J]);
           }
         }
-      }
-      if (J != w) {   // the diagonal block is written below
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sA[(16 * w + 4 * g4 + e) * LC + j] = J < w ? sb[16 * w + 4 * g4 + e] * kk[e] : 0.f;
-        if (doP) *reinterpret_cast<float4v *>(Ptg + j * C + 16 * w + 4 * g4) = qk;   // P^T[j][i]; zero above
-      }
     }
-    // diagonal block w, term by term: pair m = (i, j) of the block, four per lane
-    for (int m = lane; m < 256; m += 64) {
-      const int il = m >> 4, jl = m & 15, i = 16 * w + il, j = 16 * w + jl;
-      float av = 0.f, pv = 0.f;
-      if (jl <= il) {
-        for (int c = 0; c < DK; c += 4) {
-          const float4v gi = row4(sG + i * LK + c), gj = row4(sG + j * LK + c);
-          const float4v ki = row4(sK + i * LK + c), qi = row4(sQ + i * LK + c), kj = row4(sK + j * LK + c);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float f = kj[e] * __expf(gi[e] - gj[e]);
-            av = __builtin_fmaf(ki[e], f, av);
-            pv = __builtin_fmaf(qi[e], f, pv);
+    for (int J = 0; J < 4; ++J) {
+      if (J == w && wide) continue;   // a wide diagonal block is written below
+      const int j = 16 * J + ln;
+      float4v pt;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * w + 4 * g4 + e;
+        sA[i * LC + j] = i > j ? sb[i] * kk[J][e] : 0.f;
+        pt[e] = i >= j ? qk[J][e] : 0.f;
+      }
+      if (doP) *reinterpret_cast<float4v *>(Ptg + j * C + 16 * w + 4 * g4) = pt;   // P^T[j][i]; zero above
+    }
+    // a wide diagonal block w, term by term: pair m = (i, j) of the block, four per lane
+    if (wide) {
+      for (int m = lane; m < 256; m += 64) {
+        const int il = m >> 4, jl = m & 15, i = 16 * w + il, j = 16 * w + jl;
+        float av = 0.f, pv = 0.f;
+        if (jl <= il) {
+          for (int c = 0; c < DK; c += 4) {
+            const float4v gi = row4(sG + i * LK + c), gj = row4(sG + j * LK + c);
+            const float4v ki = row4(sK + i * LK + c), qi = row4(sQ + i * LK + c), kj = row4(sK + j * LK + c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float f = kj[e] * __expf(gi[e] - gj[e]);
+              av = __builtin_fmaf(ki[e], f, av);
+              pv = __builtin_fmaf(qi[e], f, pv);
+            }
           }
         }
+        sA[i * LC + j] = jl < il ? sb[i] * av : 0.f;
+        if (doP) Ptg[j * C + i] = pv;
       }
-      sA[i * LC + j] = jl < il ? sb[i] * av : 0.f;
-      if (doP) Ptg[j * C + i] = pv;
     }
     if (!doT) continue;
     __syncthreads();
@@ -510,27 +570,6 @@ struct CcReg {
 };
 
 // four consecutive input elements, raw until used
-template <typename TQ> struct Quad { using type = uint2; };
-template <> struct Quad<float> { using type = float4v; };
-template <typename TQ>
-__device__ __forceinline__ typename Quad<TQ>::type quad_load(const TQ *p) {
-  return *reinterpret_cast<const typename Quad<TQ>::type *>(p);
-}
-__device__ __forceinline__ float4v quad_f32(float4v x) { return x; }
-__device__ __forceinline__ float4v quad_f32(uint2 x, bf16_t) {
-  return float4v{__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xFFFF0000u), __uint_as_float(x.y << 16),
-                 __uint_as_float(x.y & 0xFFFF0000u)};
-}
-__device__ __forceinline__ float4v quad_f32(uint2 x, f16_t) {
-  const half4 h = __builtin_bit_cast(half4, x);
-  return float4v{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
-}
-template <typename TQ>
-__device__ __forceinline__ float4v quad_to_f32(typename Quad<TQ>::type x) {
-  if constexpr (sizeof(TQ) == 4) return quad_f32(x);
-  else return quad_f32(x, TQ{});
-}
-
 // LDS reads of input-type rows: four consecutive entries, four rows of a column
 template <typename TQ>
 __device__ __forceinline__ float4v rowq(const TQ *p) {
@@ -949,6 +988,46 @@ __device__ __forceinline__ void mm2(float4v &acc1, float4v &acc2, const FA1 &fa1
   }
 }
 
+// The masked products of a diagonal 16-token block p .. p + 15 in channel c, term
+// by term (each factor e^(gamma_i - gamma_j), i >= j, at most 1; masked entries
+// are zero and their factor is clamped to 1): rows p + 4 g4 + e of
+// sum_j dP_ij k_j e^.., sum_j B_ij k_j e^.., and of the transposed sums with q_i
+// and beta_i k_i.  Out of line: only blocks whose decay is too wide for the
+// matrix-core form take it.
+struct Diag4 {
+  float4v q2, f1, k1, f2;
+};
+template <int LK>
+__device__ __noinline__ Diag4 wide_diagonal(const float *sdP, const float *sB, const float *sK, const float *sQ,
+                                            const float *sG, const float *sb, int p, int c, int g4) {
+  float gi[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) gi[e] = sG[(p + 4 * g4 + e) * LK + c];
+  Diag4 d;
+  d.q2 = d.f1 = d.k1 = d.f2 = float4v{0.f, 0.f, 0.f, 0.f};
+  for (int j = p; j < p + 16; ++j) {
+    const float kj = sK[j * LK + c], gj = sG[j * LK + c];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = p + 4 * g4 + e;
+      const float f = kj * __expf(fminf(gi[e] - gj, 0.f));
+      d.q2[e] = __builtin_fmaf(sdP[i * LC + j], f, d.q2[e]);
+      d.f1[e] = __builtin_fmaf(sB[i * LC + j], f, d.f1[e]);
+    }
+  }
+  for (int i = p; i < p + 16; ++i) {
+    const float qi = sQ[i * LK + c], ki = sK[i * LK + c] * sb[i], gv = sG[i * LK + c];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = p + 4 * g4 + e;
+      const float f = __expf(fminf(gv - gi[e], 0.f));
+      d.k1[e] = __builtin_fmaf(sdP[i * LC + j], qi * f, d.k1[e]);
+      d.f2[e] = __builtin_fmaf(sB[i * LC + j], ki * f, d.f2[e]);
+    }
+  }
+  return d;
+}
+
 template <typename TQ, typename TG, int DK, bool ND, bool KEY>
 __global__ __launch_bounds__((GradCfg<TQ, DK, KEY>::NT)) void cb_grads_kernel(CbArgs a) {
   using G = GradCfg<TQ, DK, KEY>;
@@ -971,20 +1050,28 @@ __global__ __launch_bounds__((GradCfg<TQ, DK, KEY>::NT)) void cb_grads_kernel(Cb
   const int t0 = n * C, len = min(C, T - t0);
   const size_t row0 = (size_t)b * T + t0;
   const TQ *v = (const TQ *)a.v;
-  for (int u = tid; u < C * DK / 8; u += NT) {
-    const int t = u / (DK / 8), c = (u % (DK / 8)) * 8;
-    float x[8], y[8];
-    if (t < len) {
-      load8((const TQ *)a.k + ((row0 + t) * Hk + kh) * DK + c, x);
-      load8((const TQ *)a.q + ((row0 + t) * Hk + kh) * DK + c, y);
-    } else {
+  {   // k and q rows, fp32; every load issued first (past the end the last row's, zeroed)
+    constexpr int NU = C * DK / 8 / NT;
+    static_assert(C * DK / 8 % NT == 0, "whole units per thread");
+    typename Quad<TQ>::type x[NU][4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = y[e] = 0.f;
+    for (int i = 0; i < NU; ++i) {
+      const int u = tid + i * NT, t = min(u / (DK / 8), len - 1), c = (u % (DK / 8)) * 8;
+      const size_t o = ((row0 + t) * Hk + kh) * DK + c;
+      x[i][0] = quad_load((const TQ *)a.k + o);
+      x[i][1] = quad_load((const TQ *)a.k + o + 4);
+      x[i][2] = quad_load((const TQ *)a.q + o);
+      x[i][3] = quad_load((const TQ *)a.q + o + 4);
     }
-    *reinterpret_cast<float4v *>(sK + t * LK + c) = float4v{x[0], x[1], x[2], x[3]};
-    *reinterpret_cast<float4v *>(sK + t * LK + c + 4) = float4v{x[4], x[5], x[6], x[7]};
-    *reinterpret_cast<float4v *>(sQ + t * LK + c) = float4v{y[0], y[1], y[2], y[3]};
-    *reinterpret_cast<float4v *>(sQ + t * LK + c + 4) = float4v{y[4], y[5], y[6], y[7]};
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int u = tid + i * NT, t = u / (DK / 8), c = (u % (DK / 8)) * 8;
+      const float4v z = {0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<float4v *>(sK + t * LK + c) = t < len ? quad_to_f32<TQ>(x[i][0]) : z;
+      *reinterpret_cast<float4v *>(sK + t * LK + c + 4) = t < len ? quad_to_f32<TQ>(x[i][1]) : z;
+      *reinterpret_cast<float4v *>(sQ + t * LK + c) = t < len ? quad_to_f32<TQ>(x[i][2]) : z;
+      *reinterpret_cast<float4v *>(sQ + t * LK + c + 4) = t < len ? quad_to_f32<TQ>(x[i][3]) : z;
+    }
   }
   // slice registers: dO, U, E [C][32] and S0, dS_C [32][dk], and v for E . v; the
   // loads take a uniform base per (head, slice) and 32-bit offsets per thread
@@ -1106,14 +1193,16 @@ __global__ __launch_bounds__((GradCfg<TQ, DK, KEY>::NT)) void cb_grads_kernel(Cb
     }
     if constexpr (KEY) {
       lds_barrier();
+      int kln = ln, kg4 = g4;   // opaque per head: no lane address is hoisted out of the head loop
+      asm volatile("" : "+v"(kln), "+v"(kg4));
       // dP and B = dA = -E U^T, masked only: the decay is per channel, in the
       // products below; gamma [C][dk] of the head after them
 #pragma unroll
       for (int J = 0; J < HJ; ++J) {
-        const int j = 16 * (J0 + J) + ln;
+        const int j = 16 * (J0 + J) + kln;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int i = 16 * tw + 4 * g4 + e;
+          const int i = 16 * tw + 4 * kg4 + e;
           sdP[i * LC + j] = i >= j ? dPa[J][e] : 0.f;
           sB[i * LC + j] = i > j ? -dAa[J][e] : 0.f;
         }
@@ -1133,109 +1222,124 @@ __global__ __launch_bounds__((GradCfg<TQ, DK, KEY>::NT)) void cb_grads_kernel(Cb
         for (int e = 0; e < 4; ++e) sd4[e] += __shfl_xor(sd4[e], m, 64);
       if (lane < DK / 4) *reinterpret_cast<float4v *>(sSd + w * DK + 4 * lane) = sd4;
       lds_barrier();
+      // the slice products' shares of dq, dk, the gradient of gamma and dbeta, with
+      // their per-channel factors, so that they are not held through the products:
+      // dq = e^gamma o (dO S0) + q2, dk = g1 + beta f1m with f1m = f1 - e^gamma o (E S0)
+      // and g1 = k1 + f2 + dk4, dk4 = e^(gamma_C - gamma) o (U dS_C)
       float bp[4] = {0.f, 0.f, 0.f, 0.f}, gpk[HCT][4], kdx[HCT];
+#pragma unroll
+      for (int ct = 0; ct < HCT; ++ct) {
+        const int c = 16 * (ct0 + ct) + kln;
+        const float gC = sG[(C - 1) * LK + c];
+        float kd = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * tw + 4 * kg4 + e;
+          const float gt = sG[t * LK + c], eg = __expf(gt), bt = sb[t];
+          const float dq1 = eg * Q1[ct][e], x1 = -eg * ES[ct][e], d4 = __expf(gC - gt) * UD[ct][e];
+          const float qv = sQ[t * LK + c], kv = sK[t * LK + c];
+          dQa[ct][e] += dq1;
+          dKa[ct][e] += __builtin_fmaf(bt, x1, d4);
+          gpk[ct][e] = qv * dq1 - kv * d4 + kv * bt * x1;
+          bp[e] += kv * x1;
+          kd = __builtin_fmaf(kv, d4, kd);
+        }
+        kdx[ct] = kd;
+      }
       // token block TW of the rows (q2, f1: sums over keys j <= i) and of the columns
-      // (k1, f2: sums over rows i >= j).  The blocks off the diagonal go through the
-      // matrix cores about a reference token: the rows' first token p for the keys
-      // before the block, the columns' last token pe for the rows after it, so that
-      // both factors of e^(gamma_i - gamma_j) = e^(gamma_i - gamma_ref) e^(gamma_ref -
-      // gamma_j) are at most 1; the diagonal block term by term.
+      // (k1, f2: sums over rows i >= j).  The blocks go through the matrix cores
+      // about a reference token: the rows' first token p for the keys up to the
+      // block, the columns' last token pe for the rows from it, so that both
+      // factors of e^(gamma_i - gamma_j) = e^(gamma_i - gamma_ref) e^(gamma_ref -
+      // gamma_j) are at most 1 off the diagonal and one at most e^kWide on it; a
+      // diagonal block whose decay is wider in the wave's channels term by term.
+      // adds a tile's masked products to dq, dk, the gradient of gamma and dbeta
+      auto combine = [&](int ct, const float4v &q2, const float4v &f1, const float4v &k1, const float4v &f2) {
+        const int c = 16 * (ct0 + ct) + kln;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * tw + 4 * kg4 + e;
+          const float bt = sb[t], qv = sQ[t * LK + c], kv = sK[t * LK + c];
+          const float g1 = k1[e] + f2[e];
+          dQa[ct][e] += q2[e];
+          dKa[ct][e] += __builtin_fmaf(bt, f1[e], g1);
+          gpk[ct][e] += qv * q2[e] - kv * g1 + kv * bt * f1[e];
+          bp[e] += kv * f1[e];
+        }
+      };
+      unsigned wmask = 0;   // the wave's column tiles whose diagonal block is wide
       auto products = [&](auto TWc) {
         constexpr int TW = decltype(TWc)::value, p = 16 * TW, pe = p + 15;
 #pragma unroll
         for (int ct = 0; ct < HCT; ++ct) {
-          const int c = 16 * (ct0 + ct) + ln;
-          const float gp = sG[p * LK + c], gl = sG[pe * LK + c], gC = sG[(C - 1) * LK + c];
+          const int c = 16 * (ct0 + ct) + kln;
+          const float gp = sG[p * LK + c], gl = sG[pe * LK + c];
           float gi[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) gi[e] = sG[(p + 4 * g4 + e) * LK + c];
+          for (int e = 0; e < 4; ++e) gi[e] = sG[(p + 4 * kg4 + e) * LK + c];
           float4v q2 = {0.f, 0.f, 0.f, 0.f}, f1 = q2, k1 = q2, f2 = q2;
-          if constexpr (TW > 0) {
-            mm2r<C>(q2, f1, [&](int k) { return row4(sdP + (p + ln) * LC + k); },
-                    [&](int k) { return row4(sB + (p + ln) * LC + k); },
-                    [&](int k) {
-                      const float4v kv = col4(sK + k * LK + c, LK), gv = col4(sG + k * LK + c, LK);
-                      return float4v{kv[0] * __expf(gp - gv[0]), kv[1] * __expf(gp - gv[1]),
-                                     kv[2] * __expf(gp - gv[2]), kv[3] * __expf(gp - gv[3])};
-                    },
-                    g4, 0, TW);
+          // the decay over the block in the wave's channels decides whether the
+          // diagonal block joins the matrix-core products
+          const bool wide = __any(gp - gl > kWide);
+          // the keys of the blocks [LO, HI) about token p (into q2, f1), the rows of the
+          // blocks [LO, HI) about token pe (into k1, f2); one block's operands at a time
+          auto rows = [&](auto LO, auto HI, float4v &acc1, float4v &acc2, float cap) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float f = __expf(gi[e] - gp);
-              q2[e] *= f;
-              f1[e] *= f;
+            for (int k0 = 16 * decltype(LO)::value; k0 < 16 * decltype(HI)::value; k0 += 16) {
+              const int k = k0 + 4 * kg4;
+              const float4v kv = col4(sK + k * LK + c, LK), gv = col4(sG + k * LK + c, LK);
+              const float4v x1 = row4(sdP + (p + kln) * LC + k), x2 = row4(sB + (p + kln) * LC + k);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float y = kv[e] * __expf(fminf(gp - gv[e], cap));
+                acc1 = mma(x1[e], y, acc1);
+                acc2 = mma(x2[e], y, acc2);
+              }
+              __builtin_amdgcn_sched_barrier(0);
             }
-          }
-          if constexpr (TW < 3) {
+          };
+          auto cols = [&](auto LO, auto HI, float4v &acc1, float4v &acc2, float cap) {
 #pragma unroll
-            for (int k0 = 16 * (TW + 1); k0 < C; k0 += 16) {
-              const int k = k0 + 4 * g4;
+            for (int k0 = 16 * decltype(LO)::value; k0 < 16 * decltype(HI)::value; k0 += 16) {
+              const int k = k0 + 4 * kg4;
               const float4v gv = col4(sG + k * LK + c, LK), qv = col4(sQ + k * LK + c, LK);
               const float4v kv = col4(sK + k * LK + c, LK) * row4(sb + k);
-              const float4v x1 = col4(sdP + k * LC + p + ln, LC), x2 = col4(sB + k * LC + p + ln, LC);
+              const float4v x1 = col4(sdP + k * LC + p + kln, LC), x2 = col4(sB + k * LC + p + kln, LC);
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                const float f = __expf(gv[e] - gl);
-                k1 = mma(x1[e], qv[e] * f, k1);
-                f2 = mma(x2[e], kv[e] * f, f2);
+                const float f = __expf(fminf(gv[e] - gl, cap));
+                acc1 = mma(x1[e], qv[e] * f, acc1);
+                acc2 = mma(x2[e], kv[e] * f, acc2);
               }
+              __builtin_amdgcn_sched_barrier(0);
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float f = __expf(gl - gi[e]);
-              k1[e] *= f;
-              f2[e] *= f;
-            }
+          };
+          using I0 = std::integral_constant<int, 0>;
+          using IT = std::integral_constant<int, TW>;
+          using IT1 = std::integral_constant<int, TW + 1>;
+          using I4 = std::integral_constant<int, 4>;
+          rows(I0{}, IT{}, q2, f1, 0.f);
+          cols(IT1{}, I4{}, k1, f2, 0.f);
+          {   // the diagonal block (masked entries are zero); a wide one's finite values are dropped
+            float4v d1 = {0.f, 0.f, 0.f, 0.f}, d2 = d1, d3 = d1, d4 = d1;
+            rows(IT{}, IT1{}, d1, d2, kWide);
+            cols(IT{}, IT1{}, d3, d4, kWide);
+            const float keep = wide ? 0.f : 1.f;
+            q2 += d1 * keep;
+            f1 += d2 * keep;
+            k1 += d3 * keep;
+            f2 += d4 * keep;
+            if (wide) wmask |= 1u << ct;
           }
-          // the diagonal block: masked entries are zero, and their factor is clamped to 1
-#pragma unroll
-          for (int jq = 0; jq < 16; jq += 4) {
-            float4v xp[4], xb[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              xp[e] = row4(sdP + (p + 4 * g4 + e) * LC + p + jq);
-              xb[e] = row4(sB + (p + 4 * g4 + e) * LC + p + jq);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const float kj = sK[(p + jq + u) * LK + c], gj = sG[(p + jq + u) * LK + c];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float f = kj * __expf(fminf(gi[e] - gj, 0.f));
-                q2[e] = __builtin_fmaf(xp[e][u], f, q2[e]);
-                f1[e] = __builtin_fmaf(xb[e][u], f, f1[e]);
-              }
-            }
-          }
-#pragma unroll
-          for (int ii = 0; ii < 16; ++ii) {
-            const int i = p + ii;
-            const float qi = sQ[i * LK + c], ki = sK[i * LK + c] * sb[i], gv = sG[i * LK + c];
-            const float4v xp = row4(sdP + i * LC + p + 4 * g4), xb = row4(sB + i * LC + p + 4 * g4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float f = __expf(fminf(gv - gi[e], 0.f));
-              k1[e] = __builtin_fmaf(xp[e], qi * f, k1[e]);
-              f2[e] = __builtin_fmaf(xb[e], ki * f, f2[e]);
-            }
-          }
-          float kd = 0.f;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int t = p + 4 * g4 + e;
-            const float eg = __expf(gi[e]), bt = sb[t];
-            const float dq = __builtin_fmaf(eg, Q1[ct][e], q2[e]);
-            const float f1m = __builtin_fmaf(-eg, ES[ct][e], f1[e]);   // (B k)_t - e^gamma_t o (E S0)_t
-            const float d4 = __expf(gC - gi[e]) * UD[ct][e];
-            const float g1 = k1[e] + d4 + f2[e];
-            dQa[ct][e] += dq;
-            dKa[ct][e] += __builtin_fmaf(bt, f1m, g1);
-            const float qv = sQ[t * LK + c], kv = sK[t * LK + c];
-            gpk[ct][e] = qv * dq - kv * g1 + kv * bt * f1m;
-            bp[e] += kv * f1m;
-            kd = __builtin_fmaf(kv, d4, kd);
+            const float fr = __expf(gi[e] - gp), fc = __expf(gl - gi[e]);
+            q2[e] *= fr;
+            f1[e] *= fr;
+            k1[e] *= fc;
+            f2[e] *= fc;
           }
-          kdx[ct] = kd;
+          combine(ct, q2, f1, k1, f2);
           asm volatile("" ::: "memory");
         }
       };
@@ -1245,24 +1349,34 @@ __global__ __launch_bounds__((GradCfg<TQ, DK, KEY>::NT)) void cb_grads_kernel(Cb
         case 2: products(std::integral_constant<int, 2>{}); break;
         default: products(std::integral_constant<int, 3>{}); break;
       }
+      // wide diagonal blocks, term by term (each factor e^(gamma_i - gamma_j), i >= j,
+      // at most 1; masked entries are zero and their factor is clamped to 1)
+      if (wmask) {
+#pragma unroll
+        for (int ct = 0; ct < HCT; ++ct)
+          if (wmask & (1u << ct)) {
+            const Diag4 d = wide_diagonal<LK>(sdP, sB, sK, sQ, sG, sb, 16 * tw, 16 * (ct0 + ct) + kln, kg4);
+            combine(ct, d.q2, d.f1, d.k1, d.f2);
+          }
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) bp[e] = group_sum<16>(bp[e]);
-      if (ln == 0) {
+      if (kln == 0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sBet[hw * C + 16 * tw + 4 * g4 + e] = bp[e];
+        for (int e = 0; e < 4; ++e) sBet[hw * C + 16 * tw + 4 * kg4 + e] = bp[e];
       }
 #pragma unroll
       for (int ct = 0; ct < HCT; ++ct) {   // sum of k o dk4 over the wave's tokens, per channel
         float x = kdx[ct];
         x += __shfl_xor(x, 16, 64);
         x += __shfl_xor(x, 32, 64);
-        if (g4 == 0) sKd[tw * DK + 16 * (ct0 + ct) + ln] = x;
+        if (kg4 == 0) sKd[tw * DK + 16 * (ct0 + ct) + kln] = x;
       }
       lds_barrier();   // the products' reads of the masked matrices are done
 #pragma unroll
       for (int ct = 0; ct < HCT; ++ct)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sGp[(16 * tw + 4 * g4 + e) * LK + 16 * (ct0 + ct) + ln] = gpk[ct][e];
+        for (int e = 0; e < 4; ++e) sGp[(16 * tw + 4 * kg4 + e) * LK + 16 * (ct0 + ct) + kln] = gpk[ct][e];
       lds_barrier();
       // dg_tc = sum over the chunk's tokens s >= t of the gradient of gamma_sc; the last
       // token also carries <dS_C, S_C>_c = e^gamma_Cc <dS_C, S0>_c + sum_j k_jc dk4_jc
