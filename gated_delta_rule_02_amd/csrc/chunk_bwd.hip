@@ -430,7 +430,7 @@ __global__ __launch_bounds__(256) void cb_prep_key_kernel(CbArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float y = kj[e] * __expf(gp[e] - gj[e]);
-            kk[J] = mma(xk[e], y, kk[J]);
+            if (!a.nd) kk[J] = mma(xk[e], y, kk[J]);   // without the delta correction A = 0, so T = I
             qk[J] = mma(xq[e], y, qk[J]);
           }
         }
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(256) void cb_prep_key_kernel(CbArgs a) {
             }
           }
         }
-        sA[i * LC + j] = jl < il ? sb[i] * av : 0.f;
+        sA[i * LC + j] = jl < il && !a.nd ? sb[i] * av : 0.f;
         if (doP) Ptg[j * C + i] = pv;
       }
     }
@@ -917,8 +917,9 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_bwd_kernel(CbArgs a)
         dS[s] *= sEC[c];
         mm<C>(dS[s], [&](int kk) { return col4(sO + kk * LR + 16 * rt + ln, LR); },
               [&](int kk) { return col4(sKtQ + kk * LS + c, LS); }, g4);
-        mm<C>(dS[s], [&](int kk) { return row4(sE + (16 * rt + ln) * LC + kk); },
-              [&](int kk) { return col4(sKh + kk * LS + c, LS); }, g4);
+        if (!a.nd)
+          mm<C>(dS[s], [&](int kk) { return row4(sE + (16 * rt + ln) * LC + kk); },
+                [&](int kk) { return col4(sKh + kk * LS + c, LS); }, g4);
       } else {
         dS[s] *= sEg[C - 1];
         mm<C>(dS[s], [&](int kk) { return col4(sO + kk * LR + 16 * rt + ln, LR) * row4(sEg + kk); },
@@ -1293,7 +1294,7 @@ __global__ __launch_bounds__((GradCfg<TQ, DK, KEY>::NT)) void cb_grads_kernel(Cb
               for (int e = 0; e < 4; ++e) {
                 const float y = kv[e] * __expf(fminf(gp - gv[e], cap));
                 acc1 = mma(x1[e], y, acc1);
-                acc2 = mma(x2[e], y, acc2);
+                if constexpr (!ND) acc2 = mma(x2[e], y, acc2);   // B = 0 without the delta correction
               }
               __builtin_amdgcn_sched_barrier(0);
             }
@@ -1309,7 +1310,7 @@ __global__ __launch_bounds__((GradCfg<TQ, DK, KEY>::NT)) void cb_grads_kernel(Cb
               for (int e = 0; e < 4; ++e) {
                 const float f = __expf(fminf(gv[e] - gl, cap));
                 acc1 = mma(x1[e], qv[e] * f, acc1);
-                acc2 = mma(x2[e], kv[e] * f, acc2);
+                if constexpr (!ND) acc2 = mma(x2[e], kv[e] * f, acc2);
               }
               __builtin_amdgcn_sched_barrier(0);
             }
@@ -1602,8 +1603,7 @@ hipError_t launch_cb_t(const Shape &sh, const CbPlan &pl, CbArgs a, const float 
   if ((e = set_smem(cb_fwd_kernel<TQ, DK, KEY>, Sm::fwd)) != hipSuccess) return e;
   if ((e = set_smem(cb_bwd_kernel<TQ, DK, KEY>, Sm::bwd)) != hipSuccess) return e;
   if ((e = set_smem(cb_grads_kernel<TQ, TG, DK, false, KEY>, Sm::grads)) != hipSuccess) return e;
-  if constexpr (!KEY)
-    if ((e = set_smem(cb_grads_kernel<TQ, TG, DK, true, false>, Sm::grads)) != hipSuccess) return e;
+  if ((e = set_smem(cb_grads_kernel<TQ, TG, DK, true, KEY>, Sm::grads)) != hipSuccess) return e;
   const dim3 pass(sh.dv / R, sh.Hv, sh.B);
   auto prep = [&](int flags) {
     a.flags = flags;
@@ -1621,12 +1621,10 @@ hipError_t launch_cb_t(const Shape &sh, const CbPlan &pl, CbArgs a, const float 
     hipLaunchKernelGGL((cb_bwd_kernel<TQ, DK, KEY>), pass, dim3(NTP), Sm::bwd, st, a);
     if ((r = hipGetLastError()) != hipSuccess) return r;
     const dim3 grid(a.c1 - a.c0, sh.Hk, sh.B);
-    if constexpr (KEY)
-      hipLaunchKernelGGL((cb_grads_kernel<TQ, TG, DK, false, true>), grid, dim3(NTG), Sm::grads, st, a);
-    else if (a.nd)
-      hipLaunchKernelGGL((cb_grads_kernel<TQ, TG, DK, true, false>), grid, dim3(NTG), Sm::grads, st, a);
+    if (a.nd)
+      hipLaunchKernelGGL((cb_grads_kernel<TQ, TG, DK, true, KEY>), grid, dim3(NTG), Sm::grads, st, a);
     else
-      hipLaunchKernelGGL((cb_grads_kernel<TQ, TG, DK, false, false>), grid, dim3(NTG), Sm::grads, st, a);
+      hipLaunchKernelGGL((cb_grads_kernel<TQ, TG, DK, false, KEY>), grid, dim3(NTG), Sm::grads, st, a);
     return hipGetLastError();
   };
   a.nseg = pl.nseg;

@@ -638,8 +638,6 @@ gdn_status check_bwd(const gdn_desc *d, gdn::Shape *sh) {
   if (d->dv % 32 != 0 || d->dv > 1024)
     return fail(GDN_E_UNSUPPORTED, "the backward supports dv a multiple of 32, <= 1024 (got %d)", d->dv);
   if (d->gate_dtype == GDN_F16) return fail(GDN_E_UNSUPPORTED, "the backward's gates must be fp32 or bf16");
-  if (d->rule != GDN_RULE_DELTA && sh->key_gate)
-    return fail(GDN_E_UNSUPPORTED, "the backward of the per-key-channel gate is built for the delta rule only");
   return GDN_OK;
 }
 }  // namespace

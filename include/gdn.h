@@ -76,8 +76,7 @@ typedef enum {
   GDN_RULE_NO_DELTA = 1 /* without the delta correction: S_t = alpha_t S_{t-1} + beta_t v_t k_t^T
                            (per-key-channel gate: S_{t-1} diag(alpha_t)); the "SinkProbe" page's
                            hybrid_nodelta layer, the "Source notes" gla row's update.  Supported by
-                           the forward and decode entry points, and by gdn_bwd with the
-                           per-head gate. */
+                           the forward, decode and backward entry points, either gate. */
 } gdn_rule;
 
 /* Problem description shared by all entry points. */
@@ -430,8 +429,8 @@ gdn_status gdn_decode_step_conv(const gdn_desc *d, int32_t x_dtype, const void *
  * Outputs and workspace must not overlap each other or the inputs.
  * Supported: dk in {32, 64, 128}; dv a multiple of 32, <= 1024; q, k, v fp32,
  * bf16 or fp16; g and beta fp32 or bf16; either gate; d->chunk is not used;
- * d->rule either rule with the per-head gate (without the delta correction A
- * = 0, so T = I and X = beta V), the delta rule with the per-key-channel gate.
+ * d->rule either rule (without the delta correction A = 0, so T = I and
+ * X = beta V).
  */
 size_t gdn_bwd_workspace_bytes(const gdn_desc *d);
 size_t gdn_bwd_workspace_bytes_within(const gdn_desc *d, size_t cap);

@@ -381,12 +381,11 @@ def test_bwd_checks(L):
     call = lambda dd, ptrs=p, nbytes=need: L.gdn_bwd(ctypes.byref(dd), *ptrs[:5], None, ptrs[6], None,
                                                      *ptrs[8:14], ptrs[14], nbytes, None)
     assert call(desc(gate_dtype=gdn.F16)) == 3
-    # without the delta correction: the per-head gate only (same workspace)
+    # without the delta correction: either gate, the same workspace as the delta rule
     dnd = desc(qkv_dtype=gdn.F32, gate_dtype=gdn.F32, rule=gdn.RULE_NO_DELTA)
     assert L.gdn_bwd_workspace_bytes(ctypes.byref(dnd)) == need
     knd = desc(qkv_dtype=gdn.F32, gate_dtype=gdn.F32, gate=gdn.GATE_KEY_CHANNEL, rule=gdn.RULE_NO_DELTA)
-    assert L.gdn_bwd_workspace_bytes(ctypes.byref(knd)) == 0
-    assert call(knd, nbytes=1 << 40) == 3
+    assert L.gdn_bwd_workspace_bytes(ctypes.byref(knd)) == L.gdn_bwd_workspace_bytes(ctypes.byref(dkey))
     assert call(d, nbytes=L.gdn_bwd_workspace_bytes_within(ctypes.byref(d), 0) - 1) == 5
     assert call(dkey, nbytes=L.gdn_bwd_workspace_bytes_within(ctypes.byref(dkey), 0) - 1) == 5
     bad = list(p)

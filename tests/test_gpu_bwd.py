@@ -270,6 +270,17 @@ def test_bwd_without_delta_correction():
     run_case(wl, "bwd no-delta bf16 segments", delta=False, seed=3, workspace_cap=0)
 
 
+def test_bwd_key_gate_without_delta_correction():
+    """The update without the delta correction with the per-key-channel gate:
+    fp32 at small head dims with grouped heads, and bf16 at d 128 over several
+    chunks, one segment and several (the smallest workspace)."""
+    run_case(TINY_F32.with_(B=2, T=150, Hk=1, Hv=2, dk=64, dv=32, gate="key"), "bwd key gate no-delta fp32",
+             delta=False, seed=5)
+    wl = KDA_PREFILL.with_(B=1, T=300, Hk=2, Hv=4)
+    run_case(wl, "bwd key gate no-delta bf16", delta=False, seed=6)
+    run_case(wl, "bwd key gate no-delta bf16 segments", delta=False, seed=6, workspace_cap=0)
+
+
 @pytest.mark.parametrize("cap", [None, 0])
 def test_bwd_graph_capture(cap):
     """The backward captured into a graph (one segment, and the smallest
