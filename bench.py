@@ -127,12 +127,24 @@ def time_events(fn, reps, stream, repeats=3, warm=0.05):
 
 
 def git_sha():
-    """The commit of the working tree, or None where there is no git history."""
+    """The commit of the working tree; where there is no git history, the
+    commit the library was built from (recorded by the build next to it), or
+    None."""
     import subprocess
     try:
         r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=10)
-        return r.stdout.strip() or None if r.returncode == 0 else None
+        if r.returncode == 0 and r.stdout.strip():
+            return r.stdout.strip()
     except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open(os.path.join(ROOT, "gated_delta_rule_02_amd", "build_info.json")) as f:
+            info = json.load(f)
+        sha = info.get("git_sha")
+        if sha and info.get("sources_modified_since_commit"):
+            sha += "+modified"
+        return sha
+    except (OSError, ValueError):
         return None
 
 

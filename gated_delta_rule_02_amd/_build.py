@@ -53,7 +53,27 @@ def build(jobs: int = 8) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s" % r.stderr)
     os.replace(tmp, LIB)
+    _write_build_info()
     return LIB
+
+
+BUILD_INFO = os.path.join(HERE, "build_info.json")
+
+
+def _write_build_info() -> None:
+    """Record the commit the library was built from next to it (the built
+    library travels without the git history)."""
+    import json
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=10)
+        sha = r.stdout.strip() if r.returncode == 0 else None
+        r = subprocess.run(["git", "-C", ROOT, "status", "--porcelain", "--", "gated_delta_rule_02_amd/csrc",
+                            "include"], capture_output=True, text=True, timeout=10)
+        dirty = bool(r.stdout.strip()) if r.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError):
+        sha, dirty = None, None
+    with open(BUILD_INFO, "w") as f:
+        json.dump({"git_sha": sha, "sources_modified_since_commit": dirty}, f)
 
 
 # Host-side sanitizers for the C ABI's validation code: AddressSanitizer and
