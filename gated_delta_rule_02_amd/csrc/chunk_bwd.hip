@@ -517,6 +517,22 @@ __device__ __forceinline__ void mmr(float4v &acc, const FA &fa, const FB &fb, in
   }
 }
 
+// The task (row slice, value head, batch) of a pass's workgroup.  Workgroups
+// go round-robin over the 8 XCDs by their linear index; the row slices of
+// one (batch, value head) read the same per-chunk matrices and inputs, so
+// each XCD takes a contiguous range of tasks and the slices of a head share
+// its L2 (numbered as the grid, x fastest, they would sit on four XCDs and
+// fetch those matrices from HBM once each).
+__device__ __forceinline__ void pass_task(int &sl, int &h, int &b) {
+  const int ns = gridDim.x, nh = gridDim.y, total = ns * nh * gridDim.z;
+  const int lin = blockIdx.x + ns * (blockIdx.y + nh * blockIdx.z);
+  const int xcd = lin & 7, idx = lin >> 3, per = total >> 3, rem = total & 7;
+  const int task = xcd * per + min(xcd, rem) + idx;
+  sl = task % ns;
+  h = task / ns % nh;
+  b = task / ns / nh;
+}
+
 // the column block of [32][C] tile z of wave w (row block (w ZT + z) / 4): blocks
 // zc and 3 - zc go to waves that share a SIMD (eight waves) or to one wave (four),
 // so products over the triangular T and P^T weigh the same on every SIMD
@@ -648,7 +664,8 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_fwd_kernel(CbArgs a)
   float *sS = sT + C * LC, *sX = sS + R * LS, *sU = sX + R * LC;
   float *sEg = sU + R * LC, *sEc = sEg + C, *sb = sEc + C, *sEC = sb + C;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 15, g4 = lane >> 4;
-  const int sl = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int sl, h, b;
+  pass_task(sl, h, b);
   const int T = a.T, Hk = a.Hk, Hv = a.Hv, DV = a.dv_dim, kh = h / (Hv / Hk), r0 = sl * R;
   const size_t bh = (size_t)b * Hv + h;
   const TQ *k = (const TQ *)a.k, *v = (const TQ *)a.v;
@@ -790,7 +807,8 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_bwd_kernel(CbArgs a)
   float *sP = sT + C * LC, *sO = sP + C * LC, *sS = sO + C * LR, *sD = sS + R * LS, *sE = sD + R * LC;
   float *sEg = sE + R * LC, *sEc = sEg + C, *sb = sEc + C, *sEC = sb + C;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 15, g4 = lane >> 4;
-  const int sl = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int sl, h, b;
+  pass_task(sl, h, b);
   const int T = a.T, Hk = a.Hk, Hv = a.Hv, DV = a.dv_dim, kh = h / (Hv / Hk), r0 = sl * R;
   const size_t bh = (size_t)b * Hv + h;
   const TQ *k = (const TQ *)a.k, *q = (const TQ *)a.q;
