@@ -961,12 +961,15 @@ __global__ __launch_bounds__((PassCfg<TQ, DK>::NT)) void cb_bwd_kernel(CbArgs a)
 // the products over the value rows in slices of 32 (dP = dO U^T, E U^T,
 // dO S0, E S0, U dS_C), then the products with the masked C x C matrices
 // and the row dots; dq and dk summed over the value heads.  Eight waves
-// (four for dk < 128): wave w holds token block w & 3 of every [C][.]
+// (four for dk < 128 and for the key gate): wave w holds token block w & 3 of every [C][.]
 // product, and half w >> 2 of its column blocks.  The next slice is loaded
 // into registers while the current one is worked on.
 template <typename TQ, int DK, bool KEY = false>
 struct GradCfg {
-  static constexpr int NW = DK == 128 ? 8 : 4, NT = 64 * NW, NH = NW / 4;   // column halves
+  // the key gate runs four waves at dk 128 too, one per SIMD, so that each
+  // has the whole register file: its per-channel terms spill 352 bytes per
+  // lane with four waves against 448 with eight (backward 4.42 vs 4.49 ms)
+  static constexpr int NW = DK == 128 && !KEY ? 8 : 4, NT = 64 * NW, NH = NW / 4;   // column halves
   static constexpr int LK = DK + 4, NCT = DK / 16, HCT = NCT / NH, HJ = 4 / NH;
   // the key gate keeps gamma [C][dk] after the two masked matrices
   static constexpr int SLICE = 3 * C * LR + 2 * R * LK, MASKS = 2 * C * LC + (KEY ? C * LK : 0);
