@@ -1337,38 +1337,84 @@ __global__ __launch_bounds__(64 * (NW + 4), 1) void chunk_seq_kernel(
     const int buf = (c - c_begin) & 1;
     const uint4 *cT = sTPb + buf * TPS_U4;
     const float *sc = reinterpret_cast<const float *>(cT + SC_AT);
-#pragma unroll
-    for (int R = 0; R < 4; ++R) {
-      const int r = 16 * R + ln;
-      const float er = KDA ? 1.f : sc[C + r];
-      // P: from the T/P buffer (key gate; PWS with its low part after it) or from the P buffer
+    if constexpr (RT == 1) {
+      // One row tile per wave (32- and 64-row workgroups): the four row
+      // blocks' accumulators take each term in turn, so that four
+      // independent products are in flight where one chain of up to six
+      // dependent ones was (long prefill 2.49 -> 2.35 ms); each accumulator
+      // still takes its terms in the same order.  With two row tiles the
+      // per-block order below keeps fewer fragments live and is faster.
       const uint4 *ph = KDA || Cfg::PWS ? cT + NFRAG * 64 : sPh;
       const uint4 *pl = Cfg::PWS ? cT + 2 * NFRAG * 64 : sPl;
-      const half8 p0h = __builtin_bit_cast(half8, ph[frag_index(R, 0) * 64 + l]);
-      const half8 p1h = R >= 2 ? __builtin_bit_cast(half8, ph[frag_index(R, 1) * 64 + l]) : half8{};
-      half8 p0l = {}, p1l = {};
-      if constexpr (!KDA) {
-        p0l = __builtin_bit_cast(half8, pl[frag_index(R, 0) * 64 + l]);
-        if (R >= 2) p1l = __builtin_bit_cast(half8, pl[frag_index(R, 1) * 64 + l]);
-      }
+      half8 p0h[4], p1h[4], p0l[4], p1l[4];
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        float4v acc = accO[t][R];
+      for (int R = 0; R < 4; ++R) {
+        p0h[R] = __builtin_bit_cast(half8, ph[frag_index(R, 0) * 64 + l]);
+        p1h[R] = R >= 2 ? __builtin_bit_cast(half8, ph[frag_index(R, 1) * 64 + l]) : half8{};
+        p0l[R] = half8{};
+        p1l[R] = half8{};
         if constexpr (!KDA) {
+          p0l[R] = __builtin_bit_cast(half8, pl[frag_index(R, 0) * 64 + l]);
+          if (R >= 2) p1l[R] = __builtin_bit_cast(half8, pl[frag_index(R, 1) * 64 + l]);
+          const float er = sc[C + 16 * R + ln];
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) acc[ii] *= er;
+          for (int ii = 0; ii < 4; ++ii) accO[0][R][ii] *= er;
         }
-        acc = mfma32(nh[t][0], p0h, acc);
-        acc = mfma32(nl[t][0], p0h, acc);
-        if constexpr (!KDA) acc = mfma32(nh[t][0], p0l, acc);
-        if (R >= 2) {
-          acc = mfma32(nh[t][1], p1h, acc);
-          acc = mfma32(nl[t][1], p1h, acc);
-          if constexpr (!KDA) acc = mfma32(nh[t][1], p1l, acc);
-        }
-        accO[t][R] = acc;
       }
-      emit(R);
+#pragma unroll
+      for (int R = 0; R < 4; ++R) accO[0][R] = mfma32(nh[0][0], p0h[R], accO[0][R]);
+#pragma unroll
+      for (int R = 0; R < 4; ++R) accO[0][R] = mfma32(nl[0][0], p0h[R], accO[0][R]);
+      if constexpr (!KDA) {
+#pragma unroll
+        for (int R = 0; R < 4; ++R) accO[0][R] = mfma32(nh[0][0], p0l[R], accO[0][R]);
+      }
+      emit(0);
+      emit(1);
+#pragma unroll
+      for (int R = 2; R < 4; ++R) accO[0][R] = mfma32(nh[0][1], p1h[R], accO[0][R]);
+#pragma unroll
+      for (int R = 2; R < 4; ++R) accO[0][R] = mfma32(nl[0][1], p1h[R], accO[0][R]);
+      if constexpr (!KDA) {
+#pragma unroll
+        for (int R = 2; R < 4; ++R) accO[0][R] = mfma32(nh[0][1], p1l[R], accO[0][R]);
+      }
+      emit(2);
+      emit(3);
+    } else {
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        const int r = 16 * R + ln;
+        const float er = KDA ? 1.f : sc[C + r];
+        // P: from the T/P buffer (key gate; PWS with its low part after it) or from the P buffer
+        const uint4 *ph = KDA || Cfg::PWS ? cT + NFRAG * 64 : sPh;
+        const uint4 *pl = Cfg::PWS ? cT + 2 * NFRAG * 64 : sPl;
+        const half8 p0h = __builtin_bit_cast(half8, ph[frag_index(R, 0) * 64 + l]);
+        const half8 p1h = R >= 2 ? __builtin_bit_cast(half8, ph[frag_index(R, 1) * 64 + l]) : half8{};
+        half8 p0l = {}, p1l = {};
+        if constexpr (!KDA) {
+          p0l = __builtin_bit_cast(half8, pl[frag_index(R, 0) * 64 + l]);
+          if (R >= 2) p1l = __builtin_bit_cast(half8, pl[frag_index(R, 1) * 64 + l]);
+        }
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          float4v acc = accO[t][R];
+          if constexpr (!KDA) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) acc[ii] *= er;
+          }
+          acc = mfma32(nh[t][0], p0h, acc);
+          acc = mfma32(nl[t][0], p0h, acc);
+          if constexpr (!KDA) acc = mfma32(nh[t][0], p0l, acc);
+          if (R >= 2) {
+            acc = mfma32(nh[t][1], p1h, acc);
+            acc = mfma32(nl[t][1], p1h, acc);
+            if constexpr (!KDA) acc = mfma32(nh[t][1], p1l, acc);
+          }
+          accO[t][R] = acc;
+        }
+        emit(R);
+      }
     }
   };
   // the outputs of row block R of chunk c (issued as soon as they are made,
