@@ -1224,6 +1224,17 @@ __global__ __launch_bounds__(64 * (NW + 4), 1) void chunk_seq_kernel(
       }
     }
 
+    if constexpr (RT == 1 && !ND && (KDA || Cfg::PWS)) {
+      // the K and Q fragments of row block R + 1 are read while the eight
+      // products of block R run
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
     mid();
 
     // X = beta V - beta Gamma (K S^T) as fp32 (V rows 16 R + 4 g4 .. + 3 at
