@@ -204,12 +204,20 @@ def test_full_prefill_conv_fused_seeds(seed):
     check("bf16", o, o_ref, ST, S_ref, "prefill+conv fused seed %d whole tensor" % seed)
 
 
-def test_full_long_prefill():
-    whole(LONG_PREFILL, "long prefill")
+@pytest.mark.parametrize("seed", [None, 201])
+def test_full_long_prefill(seed):
+    """The long prefill at full size over the whole output tensor, at the
+    workload's own seed and one more."""
+    wl = LONG_PREFILL if seed is None else LONG_PREFILL.with_(seed=seed)
+    whole(wl, "long prefill seed %d" % wl.seed)
 
 
-def test_full_key_gate():
-    whole(KDA_PREFILL, "key gate")
+@pytest.mark.parametrize("seed", [None, 401])
+def test_full_key_gate(seed):
+    """The per-key-channel gate at full size over the whole output tensor,
+    at the workload's own seed and one more."""
+    wl = KDA_PREFILL if seed is None else KDA_PREFILL.with_(seed=seed)
+    whole(wl, "key gate seed %d" % wl.seed)
 
 
 # ---------------------------------------------------------------- stream capture
