@@ -158,6 +158,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=0)
+    ap.add_argument("--profile-workload", choices=["step", "long", "key"], default="step",
+                    help="with --profile-steps: the bench step, the long prefill or the key-gate prefill")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the forward pass here runs on a single MI355X "
@@ -231,11 +233,28 @@ def main():
         fused()
         decode()
 
+    def chunked_call(xwl):
+        """One gdn_fwd_chunked call of workload xwl on device-drawn inputs."""
+        xi = prefill_device(xwl, dev)
+        xo = torch.empty((xwl.B, xwl.T, xwl.Hv, xwl.dv), dtype=torch.float32, device=dev)
+        xst = torch.empty((xwl.B, xwl.Hv, xwl.dv, xwl.dk), dtype=torch.float32, device=dev)
+        gate = gdn.GATE_HEAD if xwl.gate == "head" else gdn.GATE_KEY_CHANNEL
+        xd = gdn.make_desc(xwl.B, xwl.T, xwl.Hk, xwl.Hv, xwl.dk, xwl.dv, xwl.chunk, gdn.BF16, gdn.BF16, gate)
+        xws = torch.empty(L.gdn_fwd_workspace_bytes(xd), dtype=torch.uint8, device=dev)
+
+        def xrun():
+            gdn.check(L.gdn_fwd_chunked(ctypes.byref(xd), P(xi["q"]), P(xi["k"]), P(xi["v"]), P(xi["g"]),
+                                        P(xi["beta"]), None if xi["S0"] is None else P(xi["S0"]),
+                                        P(xo), P(xst), P(xws), xws.numel(), s_ptr))
+        return xrun, xi, xo, xst, xd, xws
+
     if args.profile_steps > 0:
+        fn = step if args.profile_workload == "step" else \
+            chunked_call(LONG_PREFILL if args.profile_workload == "long" else KDA_PREFILL)[0]
         for _ in range(args.profile_steps):
-            step()
+            fn()
         torch.cuda.synchronize()
-        log("%d profile steps done" % args.profile_steps)
+        log("%d profile steps done (%s)" % (args.profile_steps, args.profile_workload))
         return
 
     # ------------------------------------------------------------------ timed steps
@@ -474,18 +493,7 @@ def main():
 
     for key, xwl in (("long_prefill", LONG_PREFILL), ("key_gate_prefill", KDA_PREFILL)):
         log("workload: %s" % xwl.name)
-        xi = prefill_device(xwl, dev)
-        xo = torch.empty((xwl.B, xwl.T, xwl.Hv, xwl.dv), dtype=torch.float32, device=dev)
-        xst = torch.empty((xwl.B, xwl.Hv, xwl.dv, xwl.dk), dtype=torch.float32, device=dev)
-        gate = gdn.GATE_HEAD if xwl.gate == "head" else gdn.GATE_KEY_CHANNEL
-        xd = gdn.make_desc(xwl.B, xwl.T, xwl.Hk, xwl.Hv, xwl.dk, xwl.dv, xwl.chunk, gdn.BF16, gdn.BF16, gate)
-        xws = torch.empty(L.gdn_fwd_workspace_bytes(xd), dtype=torch.uint8, device=dev)
-
-        def xrun(xi=xi, xd=xd, xo=xo, xst=xst, xws=xws):
-            gdn.check(L.gdn_fwd_chunked(ctypes.byref(xd), P(xi["q"]), P(xi["k"]), P(xi["v"]), P(xi["g"]),
-                                        P(xi["beta"]), None if xi["S0"] is None else P(xi["S0"]),
-                                        P(xo), P(xst), P(xws), xws.numel(), s_ptr))
-
+        xrun, xi, xo, xst, xd, xws = chunked_call(xwl)
         tx = time_events(xrun, 10, stream)
         ntok = xwl.B * xwl.T
         gdim = xwl.dk if xwl.gate == "key" else 1
